@@ -1,0 +1,264 @@
+/*
+ * pmn.h -- C ABI of the quantized MoE expert layer on AMD Instinct MI355X (gfx950).
+ *
+ * The hot path of an MoE expert layer trained with a 4-bit forward and an 8-bit backward:
+ * NVFP4 quantization (FP4 E2M1 values, an E4M3 scale per 16 values, an fp32 outer scale per
+ * token or per weight matrix, 4/6 scale choice for activations), the NVFP4 grouped expert GEMM,
+ * the backward operand preparation (dequantize, transpose, stochastically re-quantize to MXFP8)
+ * feeding MXFP8 dgrad/wgrad GEMMs, and the combine-side 32-point randomized Hadamard transform
+ * with S2F6 block quantization.
+ *
+ * Pages cited (by title and section heading):
+ *   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+ *          贯穿预训练到最后一次 RL rollout", sections
+ *            "更少的比特换更快的算术,量化误差是代价"   (formats and bits per value)
+ *            "只把专家层的前向传播降到 4-bit"           (NVFP4 forward, MXFP8 backward)
+ *            "转置打散分组,随机舍入保住期望值"           (blocks, transpose, SR requant)
+ *            "计算提速后,NVLink 通信成了新瓶颈"          (dispatch in NVFP4, RHT + S2F6 combine)
+ *            "配方的代价:预训练约 2% 的计算效率"         (4/6, outer scales per expert / token)
+ *   [LHC]  lhc.media note "Le calcul en 4 bits dès le préentraînement d'Inkling 2 Small".
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host). The caller owns and allocates every
+ *     buffer; no call allocates, frees or keeps a pointer after it returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream) and never
+ *     synchronize the device. Outputs are valid once the stream reaches the call.
+ *   - Arguments are checked on the host before any launch. On a bad argument the call returns
+ *     a negative PMN_E* code, launches nothing and writes nothing. pmn_strerror() names it.
+ *   - Results are deterministic: the same inputs, seed and RNG stream give the same bits,
+ *     whatever the stream, launch order or launch configuration. Random bits are keyed by the
+ *     element's index in the logical source matrix, never by thread or block id.
+ *   - bf16 data is passed as `const void*` (raw 16-bit bf16 words).
+ *
+ * Formats:
+ *   NVFP4 matrix [R x C] (C % 16 == 0):
+ *     codes  uint8 [R x C/2]  element 2j in the low nibble of byte j, 2j+1 in the high nibble;
+ *                             nibble = sign bit 3 | magnitude index into {0,.5,1,1.5,2,3,4,6}
+ *     scales uint8 [R x C/16] E4M3 (OCP E4M3FN) block scale of each 16 consecutive values
+ *     outer  fp32  [R / rows_per_outer] second-level scale of each group of rows
+ *     value(r, c) = fp4(code) * ( e4m3(scale) * outer[r / rows_per_outer] )
+ *   MXFP8 matrix with blocks of 32 along its rows: E4M3 bytes + E8M0 bytes (2^(b-127)) per 32.
+ *   S2F6: int8 code c, value c/64, plus an E8M0 scale per 32 values.
+ *   Grouped, padded transposed layout (requant, column-wise MXFP8): a logical source of M slots
+ *   split into G groups by offsets [G+1] becomes [cols x ld] where group g occupies columns
+ *   [po_g, po_g + P_g), P_g = m_g rounded up to 32, po_g = sum_{h<g} P_h; columns of a group past
+ *   m_g are zero; E8M0 scales are [cols x ld/32]. ld >= sum_g P_g is the caller's; when offsets
+ *   are only on the device, pmn_padded_bound(M, G) is always enough. Columns past sum_g P_g are
+ *   not written.
+ */
+#ifndef PMN_H
+#define PMN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* pmn_stream_t; /* hipStream_t */
+
+/* Status codes. */
+#define PMN_OK          0
+#define PMN_EINVAL     -1  /* null pointer, bad enum, bad seed/stream argument */
+#define PMN_ESHAPE     -2  /* a size is negative, not a multiple of the block, or inconsistent */
+#define PMN_EALIGN     -3  /* a pointer is not aligned as the call requires (16 bytes) */
+#define PMN_EWORKSPACE -4  /* the workspace is missing or smaller than *_workspace_size() */
+#define PMN_ELAUNCH    -5  /* the HIP runtime refused a launch (hipGetLastError after launch) */
+
+/* Text for a status code (static storage, never NULL). */
+const char* pmn_strerror(int status);
+
+/* ABI version: 100 * major + minor. */
+int pmn_version(void);
+
+/* Padded column count that is always enough for M slots in G groups: round32(M) + 32 * G. */
+int64_t pmn_padded_bound(int64_t M, int G);
+
+/* ------------------------------------------------------------------------------------------ */
+/* NVFP4 quantization   [AREX] "转置打散分组,随机舍入保住期望值" (16-value blocks, E4M3 scales, */
+/* the block max maps to the top of the grid) and "配方的代价:预训练约 2% 的计算效率" (4/6 for     */
+/* activations only; outer scale per expert for weights, per token for activations).           */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PMN_NVFP4_WEIGHT 0 /* one scale candidate (the block max maps to 6) */
+#define PMN_NVFP4_ACT    1 /* 4/6: candidates 6 and 4, the smaller squared error is kept (ties: 6) */
+
+/*
+ * x: bf16 [rows x cols], cols % 16 == 0, 16-byte aligned.
+ * rows_per_outer: rows sharing one outer scale (1 = per token; N = one weight matrix of N rows);
+ *   rows % rows_per_outer == 0.
+ * outer_in: NULL, or fp32 [rows / rows_per_outer] outer scales to use instead of computing them.
+ * Per group of rows: s_o = amax / 2688 (amax = max |x| over the group; 1 if amax == 0).
+ * Per block of 16 and candidate c: t = (amax_b / c) / s_o; scale = E4M3(t) (RNE, saturating at
+ *   448); d = scale * s_o; r = 1/d (0 if d == 0); code_i = FP4(x_i * r) (RNE, saturating at 6).
+ * Outputs: codes [rows x cols/2], scales [rows x cols/16] (16-byte aligned), outer_out fp32
+ *   [rows / rows_per_outer] (the outer scales used). For 4/6 the squared error of a candidate
+ *   is accumulated as e = fma(delta_i, delta_i, e) over i = 0..15 with delta_i =
+ *   fma(-fp4(code_i), d, x_i).
+ */
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int mode, int64_t rows_per_outer,
+                   const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out,
+                   pmn_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Backward operand preparation   [AREX] "转置打散分组,随机舍入保住期望值"; [LHC] (dequantize,   */
+/* transpose in higher precision, re-quantize to MXFP8 with stochastic rounding; the           */
+/* expectation of the re-quantized value is the forward value).                                */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PMN_TARGET_E4M3 0 /* MXFP8 elements (one byte each) */
+#define PMN_TARGET_E2M1 1 /* FP4 elements, one nibble per output byte (the pages' worked example) */
+
+/*
+ * Source: the NVFP4 matrix (codes, scales, outer, rows_per_outer) of src_rows x cols.
+ * Slots: M logical rows; slot s reads source row gather[s] (gather: int32 [M], or NULL for
+ *   slot s = row s, then M <= src_rows). Groups: offsets int64 [G+1] (device, offsets[0] = 0,
+ *   offsets[G] = M), or NULL with G = 0 for one group of M slots.
+ * For every output row c and 32-block of a group's slots:
+ *   v = value(source(slot), c) computed as fp4(code) * RN(e4m3(scale) * outer) in fp32, 0 for
+ *       padding; e = smallest e in [-127, 127] with max|v| <= Mx * 2^e (Mx = 448 for E4M3, 6 for
+ *       E2M1), so no element saturates; y = v * 2^-e; code = SR(y): with lo <= |y| < hi its grid
+ *       neighbours and f = (|y| - lo) / (hi - lo), round up iff r16 < floor(f * 2^16), where r16
+ *       is the 16-bit slice (i & 7) of Philox4x32-10(key = seed, counter = (i / 8, rng_stream, 0))
+ *       for i = slot * cols + c (low half for even i).
+ * Outputs: out [cols x ld_out] (uint8 codes), out_e8m0 [cols x ld_out/32] (biased exponent
+ *   e + 127), ld_out % 32 == 0, ld_out >= sum of padded group sizes; padded_offsets (nullable)
+ *   int64 [G+1] (or [2] when G = 0) receives po_g.
+ */
+int requant_transpose_sr_mxfp8(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                               int64_t src_rows, int64_t cols, int64_t rows_per_outer,
+                               const int32_t* gather, int64_t M, const int64_t* offsets, int G,
+                               int target, uint64_t seed, uint32_t rng_stream, uint8_t* out,
+                               uint8_t* out_e8m0, int64_t ld_out, int64_t* padded_offsets,
+                               pmn_stream_t stream);
+
+/*
+ * MXFP8 quantization of a bf16 gradient x [M x N] (N % 32 == 0), [AREX]
+ * "只把专家层的前向传播降到 4-bit" (gradients are computed with MXFP8 matmuls).
+ * layout PMN_ROWWISE: blocks of 32 along each row -> out [M x N], out_e8m0 [M x N/32]
+ *   (ld_out ignored).
+ * layout PMN_COLWISE: the grouped, padded transposed layout -> out [N x ld_out],
+ *   out_e8m0 [N x ld_out/32] (offsets/G as for the requant; padded_offsets as there).
+ * Scale rule as the requant (Mx = 448); rounding PMN_RNE (default for gradients) or PMN_SR
+ * (then r16 comes from index i = row * N + col of x, with seed and rng_stream).
+ */
+#define PMN_ROWWISE 0
+#define PMN_COLWISE 1
+#define PMN_RNE 0
+#define PMN_SR  1
+int mxfp8_quantize(const void* x, int64_t M, int64_t N, int layout, const int64_t* offsets, int G,
+                   int rounding, uint64_t seed, uint32_t rng_stream, uint8_t* out,
+                   uint8_t* out_e8m0, int64_t ld_out, int64_t* padded_offsets,
+                   pmn_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Combine-side RHT + S2F6   [AREX] "计算提速后,NVLink 通信成了新瓶颈" (a 32-point randomized   */
+/* Hadamard transform spreads outliers, is orthogonal and exactly invertible; then S2F6 block  */
+/* quantization with one scale per 32 values: 16 -> 8.25 bits per value); [LHC].               */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PMN_DTYPE_BF16 0
+#define PMN_DTYPE_F32  1
+
+/*
+ * x: [rows x cols] bf16 or fp32 (cols % 32 == 0). For each aligned 32-chunk y of a row:
+ *   y'_j = -y_j if bit j of sign_mask else y_j; z = H_32 y' (butterflies h = 1, 2, 4, 8, 16:
+ *   (a, b) -> (a + b, a - b), fp32, no 1/sqrt(32)); e = smallest e with max|z| <= (127/64) 2^e;
+ *   code_j = round-half-even(z_j * 2^(6 - e)) in [-127, 127].
+ * Outputs: codes int8 [rows x cols], scales_e8m0 uint8 [rows x cols/32] (e + 127).
+ * Decode: x = D H (code * 2^(e - 6)) / 32.
+ */
+int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask,
+                        int8_t* codes, uint8_t* scales_e8m0, pmn_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Grouped expert GEMMs   [AREX] "只把专家层的前向传播降到 4-bit" (NVFP4 expert forward with     */
+/* dedicated kernels; MXFP8 backward) and "计算提速后,NVLink 通信成了新瓶颈" (RHT + quantization */
+/* fused into the end of the w2 matmul).                                                       */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PMN_EPI_F32        0 /* out fp32 [M x N] */
+#define PMN_EPI_BF16       1 /* out bf16 [M x N] (round to nearest even) */
+#define PMN_EPI_SWIGLU     2 /* N = 2F: rows 0..F-1 of each expert are w1, F..2F-1 are w3;
+                                out bf16 [M x F] = silu(h1) * h3; out_aux (nullable) bf16 [M x N]
+                                receives h1 | h3 for the backward */
+#define PMN_EPI_RHT32_S2F6 3 /* out int8 [M x N] S2F6 codes, out_e8m0 [M x N/32], the transform
+                                of rht32_s2f6_quantize applied to the fp32 result (no bf16 step) */
+
+/*
+ * Y[s, n] = (sum_k a(row_s, k) b(g*N + n, k)) * RN(a_outer(row_s) * b_outer(g*N + n)), where the
+ * sum runs over exact products of dequantized values fp4 * e4m3 scale (fp32 accumulation), s is
+ * a slot of group g (offsets, device int64 [G+1], offsets[G] = M) and row_s = gather[s] (or s).
+ * A: NVFP4 [a_rows x K] with a_rows_per_outer; B: NVFP4 [G*N x K] with b_rows_per_outer.
+ * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (for SWIGLU also F % b_rows_per_outer == 0
+ * or b_rows_per_outer % N == 0, so w1 and w3 rows keep their own outer scales). M is the number of
+ * slots (host value). Codes and scales 16-byte aligned.
+ */
+int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                         int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather,
+                         const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                         int64_t b_rows_per_outer, const int64_t* offsets, int G, int64_t M,
+                         int64_t N, int64_t K, int epilogue, uint32_t rht_sign_mask, void* out,
+                         uint8_t* out_e8m0, void* out_aux, pmn_stream_t stream);
+
+#define PMN_BWD_DGRAD 1
+#define PMN_BWD_WGRAD 2
+
+/*
+ * Workspace bytes moe_grouped_gemm_bwd needs for these sizes and flags (host call).
+ */
+size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t K, int flags);
+
+/*
+ * Backward of Y = A W^T for one grouped layer, from the saved NVFP4 operands ([AREX]: the
+ * backward reuses the forward's quantized activations; both are requantized to MXFP8 by SR):
+ *   dgrad (flags & PMN_BWD_DGRAD): da[s, k] = sum_n dY[s, n] W_g[n, k], with dY quantized
+ *     row-wise to MXFP8 (dy_rounding) and W_g^T requantized (seed, rng_stream_b).
+ *   wgrad (flags & PMN_BWD_WGRAD): db[g*N + n, k] = sum_{s in g} dY[s, n] A[row_s, k], with dY
+ *     quantized column-wise per group and A^T requantized (seed, rng_stream_a), contraction over
+ *     the zero-padded slot dimension.
+ * dy: bf16 [M x N]; a_*: NVFP4 [a_rows x K] (+ gather); b_*: NVFP4 [G*N x K]; offsets device
+ * int64 [G+1]. N % 256 == 0, K % 256 == 0. Outputs fp32: da [M x K], db [G*N x K].
+ * dY quantized with SR uses rng_stream_dy (row-wise) and rng_stream_dy + 1 (column-wise).
+ * Workspace (16-byte aligned, >= moe_grouped_gemm_bwd_workspace_size) holds, in order, each
+ * part rounded up to 256 bytes: dY row-wise codes [M x N] and E8M0 [M x N/32]; W^T codes
+ * [K x G*N] and E8M0 [K x G*N/32]; dY^T codes [N x Pb] and E8M0 [N x Pb/32]; A^T codes [K x Pb]
+ * and E8M0 [K x Pb/32]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M, G); the
+ * parts of a gradient not requested are still reserved.
+ */
+int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,
+                         const int32_t* gather, const uint8_t* b_codes, const uint8_t* b_scales,
+                         const float* b_outer, int64_t b_rows_per_outer, const int64_t* offsets,
+                         int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
+                         uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b,
+                         uint32_t rng_stream_dy, float* da, float* db, void* workspace,
+                         size_t workspace_bytes, pmn_stream_t stream);
+
+/*
+ * SwiGLU backward (the layer's activation between w1/w3 and w2): da fp32 [M x F] and the saved
+ * h13 bf16 [M x 2F] (h1 | h3) give dh13 bf16 [M x 2F]: dh1 = da h3 silu'(h1), dh3 = da silu(h1).
+ */
+int swiglu_bwd(const float* da, const void* h13, int64_t M, int64_t F, void* dh13,
+               pmn_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Routing into expert groups   [AREX] "计算提速后,NVLink 通信成了新瓶颈" (the router picks each */
+/* token's experts; tokens are dispatched to them and combined back).                          */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * logits fp32 [T x E] (E <= 1024, 1 <= k <= min(E, 16)) -> ids int32 [T x k] (top-k by logit,
+ * descending, equal logits: lower expert first), gates fp32 [T x k] (softmax probability of
+ * each chosen expert, not renormalized), offsets int64 [E+1], gather_token int32 [T*k] (token
+ * of each slot) and slot_of int32 [T*k] (slot of (t, j)); slots are ordered by (expert, token).
+ */
+int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
+                   int64_t* offsets, int32_t* gather_token, int32_t* slot_of, pmn_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PMN_H */

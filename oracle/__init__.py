@@ -93,6 +93,7 @@ def _declare(L):
         "orc_e4m3_encode_array": (None, [P, I64, I32, P, P]),
         "orc_fp4_encode_array": (None, [P, I64, I32, P, P]),
         "orc_rand16_array": (None, [U64, U32, P, I64, P]),
+        "orc_requant_window": (None, [P, P, P, I64, I64, I64, I64, I64, I32, U64, U32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -229,6 +230,20 @@ def requant_transpose_sr(q, gather=None, offsets=None, M=None, target=TARGET_E4M
     oe = np.zeros((cols, Ptot // 32), np.uint8)
     lib().orc_requant_transpose_sr(_p(codes), _p(scales), _p(outer), cols, q["rows_per_outer"],
                                    _p(g), _p(o), G, M, target, seed, stream, _p(out), _p(oe))
+    return out, oe
+
+
+def requant_window(q, s_begin, count, target=TARGET_E4M3, seed=0, stream=0):
+    """Requantized output columns for slots [s_begin, s_begin + count) of an ungrouped source."""
+    codes, scales = np.ascontiguousarray(q["codes"]), np.ascontiguousarray(q["scales"])
+    outer = np.ascontiguousarray(q["outer"], np.float32)
+    R, half = codes.shape
+    cols = half * 2
+    Pw = (count + 31) // 32 * 32
+    out = np.zeros((cols, Pw), np.uint8)
+    oe = np.zeros((cols, Pw // 32), np.uint8)
+    lib().orc_requant_window(_p(codes), _p(scales), _p(outer), cols, q["rows_per_outer"], s_begin, count, R,
+                             target, seed, stream, _p(out), _p(oe))
     return out, oe
 
 

@@ -784,3 +784,41 @@ void orc_rand16_array(uint64_t seed, uint32_t stream, const uint64_t* idx, int64
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; i++) out[i] = orc_rand16(seed, stream, idx[i]);
 }
+
+/*
+ * The requantization of slots [s_begin, s_begin + count) of an ungrouped, ungathered source
+ * (s_begin % 32 == 0), for checking windows of a large output one by one: the same computation
+ * as orc_requant_transpose_sr, with the random bits of slot s drawn at index s * cols + c.
+ * out [cols x round32(count)], out_e8m0 [cols x round32(count)/32].
+ */
+void orc_requant_window(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                        int64_t cols, int64_t rows_per_outer, int64_t s_begin, int64_t count,
+                        int64_t M, int target, uint64_t seed, uint32_t stream, uint8_t* out,
+                        uint8_t* out_e8m0)
+{
+    int64_t P = (count + 31) / 32 * 32;
+    double Mmax = (target == ORC_TARGET_E4M3) ? 448.0 : 6.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < cols; c++)
+        for (int64_t jb = 0; jb < P; jb += 32) {
+            float v[32], amax = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                int64_t s = s_begin + jb + j;
+                v[j] = (jb + j < count && s < M)
+                           ? orc_nvfp4_dequant_elem(codes, scales, outer, cols, rows_per_outer, s, c) : 0.0f;
+                if (fabsf(v[j]) > amax) amax = fabsf(v[j]);
+            }
+            int e = orc_e8m0_exponent(amax, Mmax);
+            out_e8m0[c * (P / 32) + jb / 32] = (uint8_t)(e + 127);
+            for (int j = 0; j < 32; j++) {
+                int64_t s = s_begin + jb + j;
+                uint8_t code = 0;
+                if (jb + j < count && s < M) {
+                    float y = ldexpf(v[j], -e);
+                    uint32_t r16 = orc_rand16(seed, stream, (uint64_t)s * (uint64_t)cols + (uint64_t)c);
+                    code = (target == ORC_TARGET_E4M3) ? orc_e4m3_encode(y, ORC_SR, r16) : orc_fp4_encode(y, ORC_SR, r16);
+                }
+                out[c * P + jb + j] = code;
+            }
+        }
+}

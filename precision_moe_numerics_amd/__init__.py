@@ -1,0 +1,273 @@
+"""Quantized MoE expert layer for AMD Instinct MI355X (gfx950).
+
+Python binding of the C ABI in include/pmn.h (libpmn.so, built by ``build.py``). The functions
+below have the ABI's names and only marshal arguments: they allocate outputs with torch on the
+current device, pass raw pointers and torch's current HIP stream, and check the status code.
+Every step of the computation runs in the library's HIP kernels; if the library is not built
+the import fails.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpmn.so")
+
+P, I64, I32, U32, U64, SZ = C.c_void_p, C.c_int64, C.c_int, C.c_uint32, C.c_uint64, C.c_size_t
+
+_SIGS = {
+    "pmn_strerror": (C.c_char_p, [I32]),
+    "pmn_version": (I32, []),
+    "pmn_padded_bound": (I64, [I64, I32]),
+    "nvfp4_quantize": (I32, [P, I64, I64, I32, I64, P, P, P, P, P]),
+    "requant_transpose_sr_mxfp8": (I32, [P, P, P, I64, I64, I64, P, I64, P, I32, I32, U64, U32, P, P, I64, P, P]),
+    "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, I32, U64, U32, P, P, I64, P, P]),
+    "rht32_s2f6_quantize": (I32, [P, I32, I64, I64, U32, P, P, P]),
+    "moe_grouped_gemm_fwd": (I32, [P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, U32, P, P, P, P]),
+    "moe_grouped_gemm_bwd_workspace_size": (SZ, [I64, I32, I64, I64, I32]),
+    "moe_grouped_gemm_bwd": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32, U64,
+                                   U32, U32, U32, P, P, P, SZ, P]),
+    "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
+    "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
+}
+
+ABI_FUNCTIONS = tuple(n for n in _SIGS if not n.startswith("pmn_"))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGS.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+# ---- constants of include/pmn.h -------------------------------------------------------------
+NVFP4_WEIGHT, NVFP4_ACT = 0, 1
+TARGET_E4M3, TARGET_E2M1 = 0, 1
+ROWWISE, COLWISE = 0, 1
+RNE, SR = 0, 1
+DTYPE_BF16, DTYPE_F32 = 0, 1
+EPI_F32, EPI_BF16, EPI_SWIGLU, EPI_RHT32_S2F6 = 0, 1, 2, 3
+BWD_DGRAD, BWD_WGRAD = 1, 2
+
+
+class PmnError(RuntimeError):
+    pass
+
+
+def _check(st: int, what: str):
+    if st != 0:
+        raise PmnError(f"{what}: {_lib.pmn_strerror(st).decode()} (status {st})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise PmnError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise PmnError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def version() -> int:
+    return _lib.pmn_version()
+
+
+def padded_bound(M: int, G: int) -> int:
+    return _lib.pmn_padded_bound(M, G)
+
+
+@dataclass
+class NVFP4:
+    """An NVFP4 matrix [rows x cols]: codes u8 [rows, cols/2], scales u8 (E4M3) [rows, cols/16],
+    outer fp32 [rows / rows_per_outer]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    outer: torch.Tensor
+    rows_per_outer: int
+
+    @property
+    def rows(self) -> int:
+        return self.codes.shape[0]
+
+    @property
+    def cols(self) -> int:
+        return self.codes.shape[1] * 2
+
+
+def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int = 1,
+                   outer_in: Optional[torch.Tensor] = None) -> NVFP4:
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    R, Cc = x.shape
+    dev = x.device
+    codes = torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev)
+    outer = torch.empty((max(R // max(rows_per_outer, 1), 0),), dtype=torch.float32, device=dev)
+    _check(_lib.nvfp4_quantize(_ptr(x), R, Cc, mode, rows_per_outer, _ptr(outer_in), _ptr(codes), _ptr(scales),
+                               _ptr(outer), _stream()), "nvfp4_quantize")
+    return NVFP4(codes, scales, outer, rows_per_outer)
+
+
+def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
+                               offsets: Optional[torch.Tensor] = None, M: Optional[int] = None,
+                               target: int = TARGET_E4M3, seed: int = 0, rng_stream: int = 0,
+                               ld: Optional[int] = None, want_padded_offsets: bool = False):
+    """Returns (out [cols, ld] u8, out_e8m0 [cols, ld/32] u8, padded_offsets or None)."""
+    if M is None:
+        M = gather.numel() if gather is not None else q.rows
+    G = 0 if offsets is None else offsets.numel() - 1
+    if ld is None:
+        ld = padded_bound(M, G)
+    dev = q.codes.device
+    out = torch.zeros((q.cols, ld), dtype=torch.uint8, device=dev)
+    oe = torch.zeros((q.cols, ld // 32), dtype=torch.uint8, device=dev)
+    po = torch.zeros((max(G, 1) + 1,), dtype=torch.int64, device=dev) if want_padded_offsets else None
+    _check(_lib.requant_transpose_sr_mxfp8(_ptr(q.codes), _ptr(q.scales), _ptr(q.outer), q.rows, q.cols,
+                                           q.rows_per_outer, _ptr(gather), M, _ptr(offsets), G, target, seed,
+                                           rng_stream, _ptr(out), _ptr(oe), ld, _ptr(po), _stream()),
+           "requant_transpose_sr_mxfp8")
+    return out, oe, po
+
+
+def mxfp8_quantize(x: torch.Tensor, layout: int = ROWWISE, offsets: Optional[torch.Tensor] = None,
+                   rounding: int = RNE, seed: int = 0, rng_stream: int = 0, ld: Optional[int] = None,
+                   want_padded_offsets: bool = False):
+    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    M, N = x.shape
+    dev = x.device
+    G = 0 if offsets is None else offsets.numel() - 1
+    po = None
+    if layout == ROWWISE:
+        out = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        oe = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+        ld = N
+    else:
+        if ld is None:
+            ld = padded_bound(M, G)
+        out = torch.zeros((N, ld), dtype=torch.uint8, device=dev)
+        oe = torch.zeros((N, ld // 32), dtype=torch.uint8, device=dev)
+        po = torch.zeros((max(G, 1) + 1,), dtype=torch.int64, device=dev) if want_padded_offsets else None
+    _check(_lib.mxfp8_quantize(_ptr(x), M, N, layout, _ptr(offsets), G, rounding, seed, rng_stream, _ptr(out),
+                               _ptr(oe), ld, _ptr(po), _stream()), "mxfp8_quantize")
+    return out, oe, po
+
+
+def rht32_s2f6_quantize(x: torch.Tensor, sign_mask: int):
+    assert x.dim() == 2 and x.dtype in (torch.bfloat16, torch.float32)
+    R, Cc = x.shape
+    codes = torch.empty((R, Cc), dtype=torch.int8, device=x.device)
+    e = torch.empty((R, Cc // 32), dtype=torch.uint8, device=x.device)
+    _check(_lib.rht32_s2f6_quantize(_ptr(x), DTYPE_F32 if x.dtype == torch.float32 else DTYPE_BF16, R, Cc,
+                                    sign_mask & 0xFFFFFFFF, _ptr(codes), _ptr(e), _stream()), "rht32_s2f6_quantize")
+    return codes, e
+
+
+def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N: int,
+                         epilogue: int = EPI_F32, gather: Optional[torch.Tensor] = None,
+                         rht_sign_mask: int = 0, save_h13: bool = False, out=None, out_e8m0=None,
+                         out_aux=None):
+    """Y = grouped NVFP4 product; returns the epilogue's outputs (see include/pmn.h)."""
+    K = xq.cols
+    G = offsets.numel() - 1
+    dev = xq.codes.device
+    if out is None:
+        if epilogue == EPI_F32:
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        elif epilogue == EPI_BF16:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        elif epilogue == EPI_SWIGLU:
+            out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty((M, N), dtype=torch.int8, device=dev)
+    if epilogue == EPI_RHT32_S2F6 and out_e8m0 is None:
+        out_e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    if epilogue == EPI_SWIGLU and save_h13 and out_aux is None:
+        out_aux = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(_lib.moe_grouped_gemm_fwd(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows, xq.rows_per_outer,
+                                     _ptr(gather), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer),
+                                     wq.rows_per_outer, _ptr(offsets), G, M, N, K, epilogue,
+                                     rht_sign_mask & 0xFFFFFFFF, _ptr(out), _ptr(out_e8m0), _ptr(out_aux), _stream()),
+           "moe_grouped_gemm_fwd")
+    if epilogue == EPI_RHT32_S2F6:
+        return out, out_e8m0
+    if epilogue == EPI_SWIGLU:
+        return out, out_aux
+    return out
+
+
+def moe_grouped_gemm_bwd_workspace_size(M: int, G: int, N: int, K: int, flags: int) -> int:
+    return _lib.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
+
+
+def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N: int,
+                         flags: int = BWD_DGRAD | BWD_WGRAD, gather: Optional[torch.Tensor] = None,
+                         dy_rounding: int = RNE, seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
+                         rng_stream_dy: int = 3, workspace: Optional[torch.Tensor] = None, da=None, db=None):
+    """Returns (da [M, K] fp32 or None, db [G*N, K] fp32 or None, workspace)."""
+    K = xq.cols
+    G = offsets.numel() - 1
+    dev = dy.device
+    ws_bytes = moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
+    if workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    if da is None and flags & BWD_DGRAD:
+        da = torch.empty((M, K), dtype=torch.float32, device=dev)
+    if db is None and flags & BWD_WGRAD:
+        db = torch.empty((G * N, K), dtype=torch.float32, device=dev)
+    _check(_lib.moe_grouped_gemm_bwd(_ptr(dy), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows,
+                                     xq.rows_per_outer, _ptr(gather), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer),
+                                     wq.rows_per_outer, _ptr(offsets), G, M, N, K, flags, dy_rounding, seed,
+                                     rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da), _ptr(db),
+                                     _ptr(workspace), workspace.numel(), _stream()), "moe_grouped_gemm_bwd")
+    return da, db, workspace
+
+
+def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int):
+    """Views of the backward workspace parts, in the order include/pmn.h documents them."""
+    Pb = padded_bound(M, G)
+    sizes = [("dq", M * N, (M, N)), ("de", M * N // 32, (M, N // 32)), ("wt", K * G * N, (K, G * N)),
+             ("wte", K * G * N // 32, (K, G * N // 32)), ("dt", N * Pb, (N, Pb)), ("dte", N * Pb // 32, (N, Pb // 32)),
+             ("xt", K * Pb, (K, Pb)), ("xte", K * Pb // 32, (K, Pb // 32)), ("po", (G + 1) * 8, None)]
+    off, views = 0, {}
+    for name, nbytes, shape in sizes:
+        part = workspace[off:off + nbytes]
+        views[name] = part.view(torch.int64) if shape is None else part.view(*shape)
+        off += (nbytes + 255) // 256 * 256
+    return views
+
+
+def swiglu_bwd(da: torch.Tensor, h13: torch.Tensor) -> torch.Tensor:
+    M, F = da.shape
+    out = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=da.device)
+    _check(_lib.swiglu_bwd(_ptr(da), _ptr(h13), M, F, _ptr(out), _stream()), "swiglu_bwd")
+    return out
+
+
+def moe_route_topk(logits: torch.Tensor, k: int):
+    """Returns dict(ids, gates, offsets, gather, slot_of) on the device."""
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    offsets = torch.empty((E + 1,), dtype=torch.int64, device=dev)
+    gather = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    slot_of = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    _check(_lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(gates), _ptr(offsets), _ptr(gather),
+                               _ptr(slot_of), _stream()), "moe_route_topk")
+    return dict(ids=ids, gates=gates, offsets=offsets, gather=gather, slot_of=slot_of)

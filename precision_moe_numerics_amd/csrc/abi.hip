@@ -1,0 +1,235 @@
+// abi.hip -- the C ABI of include/pmn.h: host-side argument checks, workspace layout and the
+// launch sequence of each call. No call allocates, frees or synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmn.h"
+#include "pmn_kernels.hpp"
+
+namespace {
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+inline int status(hipError_t e) { return e == hipSuccess ? PMN_OK : PMN_ELAUNCH; }
+inline hipStream_t hs(pmn_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+struct BwdLayout {
+    size_t dq, de, wt, wte, dt, dte, xt, xte, po, total;
+    int64_t Pb;
+};
+
+BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K)
+{
+    BwdLayout L{};
+    L.Pb = pmn_padded_bound(M, G);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
+    L.dq = take((size_t)(M * N));
+    L.de = take((size_t)(M * N / 32));
+    L.wt = take((size_t)(K * G * N));
+    L.wte = take((size_t)(K * G * N / 32));
+    L.dt = take((size_t)(N * L.Pb));
+    L.dte = take((size_t)(N * L.Pb / 32));
+    L.xt = take((size_t)(K * L.Pb));
+    L.xte = take((size_t)(K * L.Pb / 32));
+    L.po = take((size_t)(G + 1) * sizeof(int64_t));
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pmn_strerror(int s)
+{
+    switch (s) {
+    case PMN_OK: return "ok";
+    case PMN_EINVAL: return "invalid argument (null pointer or bad enum)";
+    case PMN_ESHAPE: return "bad shape (negative, not a block multiple, or inconsistent)";
+    case PMN_EALIGN: return "pointer not aligned as required";
+    case PMN_EWORKSPACE: return "workspace missing or too small";
+    case PMN_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int pmn_version(void) { return 100; }
+
+int64_t pmn_padded_bound(int64_t M, int G) { return ((M + 31) & ~(int64_t)31) + 32 * (int64_t)(G > 0 ? G : 0); }
+
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int mode, int64_t rows_per_outer,
+                   const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out,
+                   pmn_stream_t stream)
+{
+    if (mode != PMN_NVFP4_WEIGHT && mode != PMN_NVFP4_ACT) return PMN_EINVAL;
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows_per_outer < 1 || rows % rows_per_outer != 0)
+        return PMN_ESHAPE;
+    if (rows == 0) return PMN_OK;
+    if (!x || !codes || !scales || !outer_out) return PMN_EINVAL;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(outer_out, 4) || (outer_in && !aligned(outer_in, 4)))
+        return PMN_EALIGN;
+    return status(pmn::launch_nvfp4_quantize(static_cast<const uint16_t*>(x), rows, cols,
+                                             mode == PMN_NVFP4_ACT, rows_per_outer, outer_in, codes,
+                                             scales, outer_out, hs(stream)));
+}
+
+static int check_groups(int64_t M, const int64_t* offsets, int G, int64_t ld)
+{
+    if (M < 0 || G < 0 || (offsets == nullptr) != (G == 0)) return PMN_ESHAPE;
+    if (ld % 32 != 0 || ld < pmn_padded_bound(M, G)) return PMN_ESHAPE;
+    return PMN_OK;
+}
+
+int requant_transpose_sr_mxfp8(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                               int64_t src_rows, int64_t cols, int64_t rows_per_outer,
+                               const int32_t* gather, int64_t M, const int64_t* offsets, int G,
+                               int target, uint64_t seed, uint32_t rng_stream, uint8_t* out,
+                               uint8_t* out_e8m0, int64_t ld_out, int64_t* padded_offsets,
+                               pmn_stream_t stream)
+{
+    if (target != PMN_TARGET_E4M3 && target != PMN_TARGET_E2M1) return PMN_EINVAL;
+    if (src_rows < 0 || cols <= 0 || cols % 16 != 0 || rows_per_outer < 1) return PMN_ESHAPE;
+    if (!gather && M > src_rows) return PMN_ESHAPE;
+    int st = check_groups(M, offsets, G, ld_out);
+    if (st != PMN_OK) return st;
+    if (M == 0 && !padded_offsets) return PMN_OK;
+    if ((M > 0 && (!codes || !scales || !outer)) || !out || !out_e8m0) return PMN_EINVAL;
+    if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(outer, 4)) return PMN_EALIGN;
+    return status(pmn::launch_requant(codes, scales, outer, cols, rows_per_outer, gather, M, offsets, G,
+                                      target, seed, rng_stream, out, out_e8m0, ld_out, padded_offsets,
+                                      hs(stream)));
+}
+
+int mxfp8_quantize(const void* x, int64_t M, int64_t N, int layout, const int64_t* offsets, int G,
+                   int rounding, uint64_t seed, uint32_t rng_stream, uint8_t* out,
+                   uint8_t* out_e8m0, int64_t ld_out, int64_t* padded_offsets, pmn_stream_t stream)
+{
+    if ((layout != PMN_ROWWISE && layout != PMN_COLWISE) || (rounding != PMN_RNE && rounding != PMN_SR))
+        return PMN_EINVAL;
+    if (M < 0 || N <= 0 || N % 32 != 0) return PMN_ESHAPE;
+    if (!x || !out || !out_e8m0) return M == 0 && layout == PMN_ROWWISE ? PMN_OK : PMN_EINVAL;
+    if (!aligned(x, 16) || !aligned(out, 16)) return PMN_EALIGN;
+    if (layout == PMN_ROWWISE)
+        return status(pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(x), M, N, rounding == PMN_SR, seed,
+                                             rng_stream, out, out_e8m0, hs(stream)));
+    int st = check_groups(M, offsets, G, ld_out);
+    if (st != PMN_OK) return st;
+    return status(pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(x), M, N, offsets, G, rounding == PMN_SR,
+                                         seed, rng_stream, out, out_e8m0, ld_out, padded_offsets, hs(stream)));
+}
+
+int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask,
+                        int8_t* codes, uint8_t* scales_e8m0, pmn_stream_t stream)
+{
+    if (dtype != PMN_DTYPE_BF16 && dtype != PMN_DTYPE_F32) return PMN_EINVAL;
+    if (rows < 0 || cols <= 0 || cols % 32 != 0) return PMN_ESHAPE;
+    if (rows == 0) return PMN_OK;
+    if (!x || !codes || !scales_e8m0) return PMN_EINVAL;
+    if (!aligned(x, 16) || !aligned(codes, 16)) return PMN_EALIGN;
+    return status(pmn::launch_rht32_s2f6(x, dtype == PMN_DTYPE_F32, rows, cols, sign_mask, codes, scales_e8m0,
+                                         hs(stream)));
+}
+
+int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                         int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather,
+                         const uint8_t* b_codes, const uint8_t* b_scales, const float* b_outer,
+                         int64_t b_rows_per_outer, const int64_t* offsets, int G, int64_t M,
+                         int64_t N, int64_t K, int epilogue, uint32_t rht_sign_mask, void* out,
+                         uint8_t* out_e8m0, void* out_aux, pmn_stream_t stream)
+{
+    if (epilogue < PMN_EPI_F32 || epilogue > PMN_EPI_RHT32_S2F6) return PMN_EINVAL;
+    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 64 != 0) return PMN_ESHAPE;
+    if (a_rows_per_outer < 1 || b_rows_per_outer < 32 || b_rows_per_outer % 32 != 0) return PMN_ESHAPE;
+    if (!gather && M > a_rows) return PMN_ESHAPE;
+    if (!offsets || !a_codes || !a_scales || !a_outer || !b_codes || !b_scales || !b_outer || !out)
+        return PMN_EINVAL;
+    if (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0) return PMN_EINVAL;
+    if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
+        !aligned(out, 16) || (out_aux && !aligned(out_aux, 16)))
+        return PMN_EALIGN;
+    if (M == 0) return PMN_OK;
+    return status(pmn::launch_gemm_fwd(a_codes, a_scales, a_outer, a_rows_per_outer, gather, b_codes, b_scales,
+                                       b_outer, b_rows_per_outer, offsets, G, M, N, K, epilogue, rht_sign_mask,
+                                       out, out_e8m0, epilogue == PMN_EPI_SWIGLU ? out_aux : nullptr,
+                                       hs(stream)));
+}
+
+size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t K, int flags)
+{
+    (void)flags;
+    if (M < 0 || G < 1 || N <= 0 || K <= 0) return 0;
+    return bwd_layout(M, G, N, K).total;
+}
+
+int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
+                         const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,
+                         const int32_t* gather, const uint8_t* b_codes, const uint8_t* b_scales,
+                         const float* b_outer, int64_t b_rows_per_outer, const int64_t* offsets,
+                         int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
+                         uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b,
+                         uint32_t rng_stream_dy, float* da, float* db, void* workspace,
+                         size_t workspace_bytes, pmn_stream_t stream)
+{
+    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD)) != 0 || flags == 0) return PMN_EINVAL;
+    if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
+    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
+    if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
+    if (!gather && M > a_rows) return PMN_ESHAPE;
+    if (!offsets || !dy) return PMN_EINVAL;
+    const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
+    if (dgrad && (!b_codes || !b_scales || !b_outer || !da)) return PMN_EINVAL;
+    if (wgrad && (!a_codes || !a_scales || !a_outer || !db)) return PMN_EINVAL;
+    const BwdLayout L = bwd_layout(M, G, N, K);
+    if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
+    if (!aligned(workspace, 16) || !aligned(dy, 16) || (da && !aligned(da, 16)) || (db && !aligned(db, 16)) ||
+        (a_codes && !aligned(a_codes, 16)) || (b_codes && !aligned(b_codes, 16)))
+        return PMN_EALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const hipStream_t s = hs(stream);
+    const bool sr = dy_rounding == PMN_SR;
+    hipError_t e = hipSuccess;
+    if (dgrad) {
+        e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
+                                   ws + L.de, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
+                                0, PMN_TARGET_E4M3, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N,
+                                nullptr, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, G, M, N, K, da, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+    }
+    if (wgrad) {
+        int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
+        e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
+                                   ws + L.dt, ws + L.dte, L.Pb, po, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G,
+                                PMN_TARGET_E4M3, seed, rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, nullptr, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+    }
+    return PMN_OK;
+}
+
+int swiglu_bwd(const float* da, const void* h13, int64_t M, int64_t F, void* dh13, pmn_stream_t stream)
+{
+    if (M < 0 || F <= 0 || F % 8 != 0) return PMN_ESHAPE;
+    if (M == 0) return PMN_OK;
+    if (!da || !h13 || !dh13) return PMN_EINVAL;
+    if (!aligned(da, 16) || !aligned(h13, 16) || !aligned(dh13, 16)) return PMN_EALIGN;
+    return status(pmn::launch_swiglu_bwd(da, static_cast<const uint16_t*>(h13), M, F, static_cast<uint16_t*>(dh13),
+                                         hs(stream)));
+}
+
+int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
+                   int64_t* offsets, int32_t* gather_token, int32_t* slot_of, pmn_stream_t stream)
+{
+    if (T < 0 || E < 1 || E > 1024 || k < 1 || k > 16 || k > E) return PMN_ESHAPE;
+    if (!offsets || (T > 0 && (!logits || !ids || !gates || !gather_token || !slot_of))) return PMN_EINVAL;
+    return status(pmn::launch_route(logits, T, E, k, ids, gates, offsets, gather_token, slot_of, hs(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// gemm_bwd.hip -- MXFP8 grouped GEMMs of the expert-layer backward (dgrad, wgrad) and the
+// SwiGLU backward.
+//
+// Pages cited (by title and section heading):
+//   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+//          贯穿预训练到最后一次 RL rollout":
+//            "只把专家层的前向传播降到 4-bit" -- the backward pass runs in MXFP8;
+//            "转置打散分组,随机舍入保住期望值" -- weights and activations are re-quantized to
+//              MXFP8 with stochastic rounding and the gradients use MXFP8 matmuls.
+//
+// Both GEMMs are D[r, c] = sum_k A[r, k] B[c, k] over E4M3 operands with one E8M0 scale per 32
+// consecutive k, which is exactly the operand format of gfx950's block-scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3). Its lane layout, measured on the device:
+// lane l supplies row l % 32; with h = l / 32 its bytes 0..15 are k = 16h .. 16h+15 and bytes
+// 16..31 are k = 32+16h .. 32+16h+15 of the 64-k step, and its scale operand is the E8M0 scale
+// of k-block h of that row (k-block b of the step = k in [32b, 32b+32)).
+//
+// Tiling: 256 x 256 output tile per workgroup of 4 wavefronts (128 x 128 each, 4 x 4 MFMA
+// blocks), K stages of 128 bytes staged through LDS (rows padded to 144 bytes), two stages.
+#include "pmn_dev.hpp"
+#include "pmn_kernels.hpp"
+
+namespace pmn {
+
+namespace bwd {
+constexpr int BT = 256;
+constexpr int BK = 128;                 // k per stage (bytes per row)
+constexpr int ROWB = 144;
+constexpr int TILEB = BT * ROWB;        // one operand's codes
+constexpr int SCB = BT * 4;             // one operand's 4 scale bytes per row
+constexpr int STAGEB = 2 * TILEB + 2 * SCB;
+constexpr int LDSB = 2 * STAGEB;
+}  // namespace bwd
+
+enum { MODE_DGRAD = 0, MODE_WGRAD = 1 };
+
+struct Mx8Args {
+    // dgrad: A = dY row-wise [M x Nf] (lda = Nf), B = W^T [Kf x G*Nf] (ldb = G*Nf, group g at
+    //        column g*Nf), contraction Nf, output dX [M x Kf].
+    // wgrad: A = dY^T [Nf x ld] , B = X^T [Kf x ld], contraction over the padded slots of group
+    //        g (columns po[g] .. po[g+1]), output dW [G*Nf x Kf].
+    const uint8_t* a;
+    const uint8_t* ae;
+    int64_t lda;
+    const uint8_t* b;
+    const uint8_t* be;
+    int64_t ldb;
+    const int64_t* offsets;
+    const int64_t* po;        // padded offsets (wgrad)
+    int G;
+    int64_t Nf, Kf;
+    float* out;
+};
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
+{
+    using namespace bwd;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wr = wave >> 1, wc = wave & 1;
+
+    int g = -1;
+    int64_t r0 = 0, rvalid = BT, c0 = 0, kbeg = 0, klen = 0;
+    const uint8_t *abase, *aebase, *bbase, *bebase;
+    int64_t ldo;
+    float* obase;
+    if (MODE == MODE_DGRAD) {
+        int64_t t = blockIdx.y, cum = 0;
+        for (int gg = 0; gg < p.G; gg++) {
+            const int64_t s0 = p.offsets[gg], s1 = p.offsets[gg + 1];
+            const int64_t tiles = (s1 - s0 + BT - 1) / BT;
+            if (t < cum + tiles) {
+                g = gg;
+                r0 = s0 + (t - cum) * BT;
+                rvalid = s1 - r0 < BT ? s1 - r0 : BT;
+                break;
+            }
+            cum += tiles;
+        }
+        if (g < 0) return;
+        c0 = (int64_t)blockIdx.x * BT;
+        kbeg = 0;
+        klen = p.Nf;
+        abase = p.a; aebase = p.ae;
+        bbase = p.b + (int64_t)g * p.Nf; bebase = p.be + (int64_t)g * (p.Nf / 32);
+        ldo = p.Kf;
+        obase = p.out;
+    } else {
+        g = blockIdx.z;
+        r0 = (int64_t)blockIdx.y * BT;
+        rvalid = BT;
+        c0 = (int64_t)blockIdx.x * BT;
+        kbeg = p.po[g];
+        klen = p.po[g + 1] - kbeg;
+        abase = p.a + kbeg; aebase = p.ae + kbeg / 32;
+        bbase = p.b + kbeg; bebase = p.be + kbeg / 32;
+        ldo = p.Kf;
+        obase = p.out + (int64_t)g * p.Nf * p.Kf;
+    }
+
+    // staging rows of this thread
+    const bool arow_ok = tid < rvalid;
+    const uint8_t* ap = abase + (arow_ok ? (r0 + tid) : 0) * p.lda;
+    const uint8_t* aep = aebase + (arow_ok ? (r0 + tid) : 0) * (p.lda / 32);
+    const uint8_t* bp = bbase + (c0 + tid) * p.ldb;
+    const uint8_t* bep = bebase + (c0 + tid) * (p.ldb / 32);
+
+    uint4 av[8], bv[8];
+    uint32_t as, bs;
+    auto load_stage = [&](int kt) {
+        const int64_t k0 = (int64_t)kt * BK;
+        const int64_t rem = klen - k0;            // bytes of this stage that exist (>= 32)
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            const bool ok = arow_ok && (q * 16 < rem);
+            av[q] = ok ? reinterpret_cast<const uint4*>(ap + k0)[q] : make_uint4(0u, 0u, 0u, 0u);
+            bv[q] = (q * 16 < rem) ? reinterpret_cast<const uint4*>(bp + k0)[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        // scale bytes (one per 32): missing blocks get 127 (2^0) with zero data
+        as = 0x7F7F7F7Fu;
+        bs = 0x7F7F7F7Fu;
+        uint32_t sa = 0u, sbb = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const bool ok = q * 32 < rem;
+            uint32_t x = ok && arow_ok ? (uint32_t)aep[k0 / 32 + q] : 127u;
+            uint32_t y = ok ? (uint32_t)bep[k0 / 32 + q] : 127u;
+            sa |= x << (8 * q);
+            sbb |= y << (8 * q);
+        }
+        as = sa;
+        bs = sbb;
+    };
+    auto store_stage = [&](int buf) {
+        uint8_t* base = lds + buf * STAGEB;
+        uint4* pa = reinterpret_cast<uint4*>(base + tid * ROWB);
+        uint4* pb = reinterpret_cast<uint4*>(base + TILEB + tid * ROWB);
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            pa[q] = av[q];
+            pb[q] = bv[q];
+        }
+        reinterpret_cast<uint32_t*>(base + 2 * TILEB)[tid] = as;
+        reinterpret_cast<uint32_t*>(base + 2 * TILEB + SCB)[tid] = bs;
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+    const int KT = (int)((klen + BK - 1) / BK);
+    if (KT > 0) {
+        load_stage(0);
+        store_stage(0);
+    }
+    __syncthreads();
+    const int lrow = lane & 31, hh = lane >> 5;
+    for (int kt = 0; kt < KT; kt++) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load_stage(kt + 1);
+        const uint8_t* base = lds + buf * STAGEB;
+        const uint32_t* sca = reinterpret_cast<const uint32_t*>(base + 2 * TILEB);
+        const uint32_t* scb = reinterpret_cast<const uint32_t*>(base + 2 * TILEB + SCB);
+#pragma unroll
+        for (int ks = 0; ks < BK / 64; ks++) {
+            i32x8 af[4], bf[4];
+            int sa[4], sb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int row = wr * 128 + i * 32 + lrow;
+                const uint8_t* src = base + row * ROWB + ks * 64 + hh * 16;
+                uint4 lo = *reinterpret_cast<const uint4*>(src);
+                uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
+                af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sa[i] = (int)((sca[row] >> (8 * (2 * ks + hh))) & 0xFFu);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int row = wc * 128 + j * 32 + lrow;
+                const uint8_t* src = base + TILEB + row * ROWB + ks * 64 + hh * 16;
+                uint4 lo = *reinterpret_cast<const uint4*>(src);
+                uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
+                bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                sb[j] = (int)((scb[row] >> (8 * (2 * ks + hh))) & 0xFFu);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+        }
+        if (kt + 1 < KT) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: block (i, j): lane holds column c = c0 + wc*128 + j*32 + lane%32 and rows
+    // r = r0 + wr*128 + i*32 + (v/4)*8 + hh*4 + v%4
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int64_t col = c0 + wc * 128 + j * 32 + lrow;
+#pragma unroll
+            for (int v = 0; v < 16; v++) {
+                const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                if (rl < rvalid) obase[(r0 + rl) * ldo + col] = acc[i][j][v];
+            }
+        }
+}
+
+hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
+                              const uint8_t* wte, const int64_t* offsets, int G, int64_t M,
+                              int64_t Nf, int64_t Kf, float* dx, hipStream_t stream)
+{
+    if (M == 0 || G == 0) return hipSuccess;
+    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, nullptr, G, Nf, Kf, dx};
+    dim3 grid((unsigned)(Kf / bwd::BT), (unsigned)((M + bwd::BT - 1) / bwd::BT + G));
+    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
+                              const uint8_t* xte, int64_t ld, const int64_t* po, int G,
+                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream)
+{
+    if (G == 0) return hipSuccess;
+    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, G, Nf, Kf, dw};
+    dim3 grid((unsigned)(Kf / bwd::BT), (unsigned)(Nf / bwd::BT), (unsigned)G);
+    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// SwiGLU backward (elementwise): dh1 = da * h3 * silu'(h1), dh3 = da * silu(h1),
+// silu'(h) = s (1 + h (1 - s)), s = sigmoid(h). Eight elements per thread.
+// ------------------------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ da, const uint16_t* __restrict__ h13,
+                                                    int64_t M, int64_t F, uint16_t* __restrict__ dh13)
+{
+    const int64_t per_row = F / 8;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * per_row) return;
+    const int64_t m = i / per_row, j0 = (i - m * per_row) * 8;
+    const float4* pd = reinterpret_cast<const float4*>(da + m * F + j0);
+    float4 d0 = pd[0], d1 = pd[1];
+    float d[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+    uint4 w1 = *reinterpret_cast<const uint4*>(h13 + m * 2 * F + j0);
+    uint4 w3 = *reinterpret_cast<const uint4*>(h13 + m * 2 * F + F + j0);
+    uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w}, a3[4] = {w3.x, w3.y, w3.z, w3.w};
+    uint32_t o1[4], o3[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint32_t r1[2], r3[2];
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            float h1 = u ? bf16_hi(a1[q]) : bf16_lo(a1[q]);
+            float h3 = u ? bf16_hi(a3[q]) : bf16_lo(a3[q]);
+            float s = 1.0f / (1.0f + expf(-h1));
+            float g = d[2 * q + u];
+            r1[u] = f32_to_bf16_bits(g * h3 * (s * (1.0f + h1 * (1.0f - s))));
+            r3[u] = f32_to_bf16_bits(g * h1 * s);
+        }
+        o1[q] = r1[0] | (r1[1] << 16);
+        o3[q] = r3[0] | (r3[1] << 16);
+    }
+    *reinterpret_cast<uint4*>(dh13 + m * 2 * F + j0) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+    *reinterpret_cast<uint4*>(dh13 + m * 2 * F + F + j0) = make_uint4(o3[0], o3[1], o3[2], o3[3]);
+}
+
+hipError_t launch_swiglu_bwd(const float* da, const uint16_t* h13, int64_t M, int64_t F,
+                             uint16_t* dh13, hipStream_t stream)
+{
+    const int64_t n = M * (F / 8);
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_swiglu_bwd, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, da, h13, M, F, dh13);
+    return hipGetLastError();
+}
+
+}  // namespace pmn

@@ -1,0 +1,352 @@
+// gemm_fwd.hip -- NVFP4 grouped expert GEMM (forward) with bf16/fp32, SwiGLU and RHT32 + S2F6
+// epilogues.
+//
+// Pages cited (by title and section heading):
+//   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+//          贯穿预训练到最后一次 RL rollout":
+//            "只把专家层的前向传播降到 4-bit" -- the expert layers' forward runs in NVFP4 with
+//              dedicated kernels;
+//            "计算提速后,NVLink 通信成了新瓶颈" -- the RHT and the S2F6 quantization are fused
+//              into the end of the w2 matmul, so the combine payload leaves the GEMM at 8.25
+//              bits per value.
+//
+// Arithmetic. Every NVFP4 value is fp4 * e4m3 (the outer scales are applied in the epilogue).
+// That product has at most 6 significant bits and lies in [2^-10, 2688], so it is exact in
+// fp16; products of two such values are exact in fp32. The kernel dequantizes FP4 codes with
+// the gfx950 FP4->fp16 converter and one packed fp16 multiply by the block scale, then runs
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation. gfx950's block-scaled MFMA only takes E8M0
+// scales per 32 values, which cannot carry an E4M3 scale per 16, so the exact path is the fp16
+// one.
+//
+// Tiling. A workgroup of 4 wavefronts computes a 256 (weight rows n) x 256 (slots m) tile of
+// D = W X^T, i.e. Y^T, as 2 x 2 wavefront tiles of 128 x 128 (4 x 4 MFMA blocks). K advances in
+// stages of 64: each thread loads 32 code bytes and 4 scale bytes of one weight row and one
+// (gathered) activation row, dequantizes them and writes 128 bytes of fp16 per operand to LDS
+// (rows padded to 144 bytes, so fragment reads are bank-conflict free); two LDS stages
+// alternate with one barrier per stage while the next stage's codes are in flight.
+// Groups (experts) are ragged: workgroup y walks the device offsets to find its (expert,
+// slot tile), so no host synchronization is needed.
+#include "pmn_dev.hpp"
+#include "pmn_kernels.hpp"
+
+namespace pmn {
+
+namespace fwd {
+constexpr int BT = 256;                       // rows per operand tile
+constexpr int BK = 64;                        // K per stage
+constexpr int ROWB = 144;                     // LDS bytes per row: 64 fp16 + 16 pad
+constexpr int TILEB = BT * ROWB;              // one operand tile
+constexpr int STAGEB = 2 * TILEB;             // weights + activations
+constexpr int LDSB = 2 * STAGEB;              // two stages
+}  // namespace fwd
+
+struct FwdArgs {
+    const uint8_t* a_codes;   // activations NVFP4 [a_rows x K]
+    const uint8_t* a_scales;
+    const float* a_outer;
+    int64_t a_rpo;
+    const int32_t* gather;
+    const uint8_t* b_codes;   // weights NVFP4 [G*N x K]
+    const uint8_t* b_scales;
+    const float* b_outer;
+    int64_t b_rpo;
+    const int64_t* offsets;
+    int G;
+    int64_t N, K;
+    uint32_t rht_mask;
+    void* out;
+    uint8_t* out_e8m0;
+    void* out_aux;
+};
+
+// Dequantize one row's stage: 8 code words (64 FP4 values) and 4 E4M3 scale bytes -> 64 fp16
+// written as 8 x 16 bytes to LDS.
+PMN_DEV void dequant_row_to_lds(const uint4 (&cw)[2], uint32_t sc, uint8_t* dst)
+{
+    uint32_t w[8] = {cw[0].x, cw[0].y, cw[0].z, cw[0].w, cw[1].x, cw[1].y, cw[1].z, cw[1].w};
+#pragma unroll
+    for (int blk = 0; blk < 4; blk++) {
+        const _Float16 s = (_Float16)e4m3_value((sc >> (8 * blk)) & 0xFFu);
+        const f16x2 ss = {s, s};
+#pragma unroll
+        for (int h = 0; h < 2; h++) {
+            const uint32_t word = w[2 * blk + h];
+            f16x2 p0 = PMN_FP4_TO_F16(word, 0) * ss;
+            f16x2 p1 = PMN_FP4_TO_F16(word, 1) * ss;
+            f16x2 p2 = PMN_FP4_TO_F16(word, 2) * ss;
+            f16x2 p3 = PMN_FP4_TO_F16(word, 3) * ss;
+            uint4 v;
+            __builtin_memcpy(&v.x, &p0, 4);
+            __builtin_memcpy(&v.y, &p1, 4);
+            __builtin_memcpy(&v.z, &p2, 4);
+            __builtin_memcpy(&v.w, &p3, 4);
+            *reinterpret_cast<uint4*>(dst + 16 * (2 * blk + h)) = v;
+        }
+    }
+}
+
+PMN_DEV float silu(float h) { return h / (1.0f + expf(-h)); }
+
+// RHT32 + S2F6 on one 32 x 32 accumulator block whose 32 rows (n) are one aligned chunk:
+// lane l holds column m = l % 32 and rows i = (v/4)*8 + (l/32)*4 + v%4. Butterfly stages
+// h = 1, 2, 4, 8, 16 in that order: h = 1, 2, 8, 16 pair registers of one lane, h = 4 pairs the
+// two lane halves.
+PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_chunk, uint8_t* e8m0_ptr)
+{
+    const int hh = lane >> 5;
+    float t[16];
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+        const int i = (v >> 2) * 8 + hh * 4 + (v & 3);
+        t[v] = __uint_as_float(__float_as_uint(z[v]) ^ (((mask >> i) & 1u) << 31));
+    }
+    // h = 1 (v ^ 1), h = 2 (v ^ 2)
+#pragma unroll
+    for (int hb = 1; hb <= 2; hb <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            if ((v & hb) == 0) {
+                float a = t[v], b = t[v + hb];
+                t[v] = a + b;
+                t[v + hb] = a - b;
+            }
+        }
+    }
+    // h = 4: across lane halves
+#pragma unroll
+    for (int v = 0; v < 16; v++) {
+        float p = __shfl_xor(t[v], 32, 64);
+        t[v] = hh == 0 ? t[v] + p : p - t[v];
+    }
+    // h = 8 (v ^ 4), h = 16 (v ^ 8)
+#pragma unroll
+    for (int hb = 4; hb <= 8; hb <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+            if ((v & hb) == 0) {
+                float a = t[v], b = t[v + hb];
+                t[v] = a + b;
+                t[v + hb] = a - b;
+            }
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(t[v]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    const int e = e8m0_exponent<E8M0_S2F6>(amax);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int c = (int)__builtin_rintf(__builtin_ldexpf(t[4 * q + j], 6 - e));
+            w |= ((uint32_t)c & 0xFFu) << (8 * j);
+        }
+        *reinterpret_cast<uint32_t*>(out_row_chunk + q * 8 + hh * 4) = w;
+    }
+    if (hh == 0) *e8m0_ptr = (uint8_t)(e + 127);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
+{
+    using namespace fwd;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wn = wave >> 1, wm = wave & 1;
+
+    // ---- which (expert, slot tile, weight tile)
+    int g = -1;
+    int64_t m0 = 0, mvalid = 0;
+    {
+        int64_t t = blockIdx.y, cum = 0;
+        for (int gg = 0; gg < p.G; gg++) {
+            const int64_t a = p.offsets[gg], b = p.offsets[gg + 1];
+            const int64_t tiles = (b - a + BT - 1) / BT;
+            if (t < cum + tiles) {
+                g = gg;
+                m0 = a + (t - cum) * BT;
+                mvalid = b - m0 < BT ? b - m0 : BT;
+                break;
+            }
+            cum += tiles;
+        }
+    }
+    if (g < 0) return;
+    const int64_t N = p.N, K = p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
+
+    // ---- global rows this thread stages
+    int64_t wrow;   // weight row
+    if (EPI == PMN_EPI_SWIGLU) {
+        const int F = (int)(N >> 1);
+        const int twn = tid >> 7, trb = (tid & 127) >> 5, tr = tid & 31;
+        wrow = (int64_t)g * N + (trb < 2 ? 0 : F) + n0 + twn * 64 + (trb & 1) * 32 + tr;
+    } else {
+        wrow = (int64_t)g * N + n0 + tid;
+    }
+    const bool xvalid = tid < mvalid;
+    const int64_t xrow = xvalid ? (p.gather ? (int64_t)p.gather[m0 + tid] : m0 + tid) : 0;
+    const uint8_t* wc = p.b_codes + wrow * (K >> 1);
+    const uint8_t* ws = p.b_scales + wrow * (K >> 4);
+    const uint8_t* xc = p.a_codes + xrow * (K >> 1);
+    const uint8_t* xs = p.a_scales + xrow * (K >> 4);
+
+    uint4 wcw[2], xcw[2];
+    uint32_t wsc, xsc;
+    auto load_stage = [&](int kt) {
+        const uint4* pw = reinterpret_cast<const uint4*>(wc + kt * (BK / 2));
+        wcw[0] = pw[0];
+        wcw[1] = pw[1];
+        wsc = *reinterpret_cast<const uint32_t*>(ws + kt * (BK / 16));
+        if (xvalid) {
+            const uint4* px = reinterpret_cast<const uint4*>(xc + kt * (BK / 2));
+            xcw[0] = px[0];
+            xcw[1] = px[1];
+            xsc = *reinterpret_cast<const uint32_t*>(xs + kt * (BK / 16));
+        } else {
+            xcw[0] = xcw[1] = make_uint4(0u, 0u, 0u, 0u);
+            xsc = 0u;
+        }
+    };
+    auto store_stage = [&](int buf) {
+        uint8_t* base = lds + buf * STAGEB;
+        dequant_row_to_lds(wcw, wsc, base + tid * ROWB);
+        dequant_row_to_lds(xcw, xsc, base + TILEB + tid * ROWB);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+    const int KT = (int)(K / BK);
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    const int lrow = lane & 31, lk = (lane >> 5) * 16;
+    for (int kt = 0; kt < KT; kt++) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) load_stage(kt + 1);
+        const uint8_t* wb = lds + buf * STAGEB + (wn * 128 + lrow) * ROWB + lk;
+        const uint8_t* xb = lds + buf * STAGEB + TILEB + (wm * 128 + lrow) * ROWB + lk;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ks++) {
+            f16x8 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) af[i] = *reinterpret_cast<const f16x8*>(wb + i * 32 * ROWB + ks * 32);
+#pragma unroll
+            for (int j = 0; j < 4; j++) bf[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT) store_stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds slot m = (wm*128 + j*32 + lane%32), weight rows of block i
+    const int hh = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int64_t ml = wm * 128 + j * 32 + (lane & 31);
+        const bool mok = ml < mvalid;
+        const int64_t m = m0 + ml;
+        const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
+        const float sx = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
+        if (EPI == PMN_EPI_SWIGLU) {
+            const int64_t F = N >> 1;
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const int64_t jbase = n0 + wn * 64 + i * 32;         // A column of row 0 of block
+                const float s1 = sx * p.b_outer[((int64_t)g * N + jbase) / p.b_rpo];
+                const float s3 = sx * p.b_outer[((int64_t)g * N + F + jbase) / p.b_rpo];
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    float h1[4], h3[4];
+                    uint32_t ab[4], b1[4], b3[4];
+#pragma unroll
+                    for (int u = 0; u < 4; u++) {
+                        h1[u] = acc[i][j][4 * q + u] * s1;
+                        h3[u] = acc[i + 2][j][4 * q + u] * s3;
+                        ab[u] = f32_to_bf16_bits(silu(h1[u]) * h3[u]);
+                        b1[u] = f32_to_bf16_bits(h1[u]);
+                        b3[u] = f32_to_bf16_bits(h3[u]);
+                    }
+                    if (mok) {
+                        const int64_t col = jbase + q * 8 + hh * 4;
+                        uint16_t* A = reinterpret_cast<uint16_t*>(p.out) + m * F + col;
+                        *reinterpret_cast<uint2*>(A) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                        if (p.out_aux) {
+                            uint16_t* H = reinterpret_cast<uint16_t*>(p.out_aux) + m * N;
+                            *reinterpret_cast<uint2*>(H + col) = make_uint2(b1[0] | (b1[1] << 16), b1[2] | (b1[3] << 16));
+                            *reinterpret_cast<uint2*>(H + F + col) = make_uint2(b3[0] | (b3[1] << 16), b3[2] | (b3[3] << 16));
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int64_t nb = n0 + wn * 128 + i * 32;           // first weight row of block
+                const float s = sx * p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
+                if (EPI == PMN_EPI_RHT32_S2F6) {
+                    f32x16 z;
+#pragma unroll
+                    for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * s;
+                    // lanes l and l ^ 32 hold the same slot, so a masked slot masks both halves of
+                    // the butterfly exchange together
+                    if (mok)
+                        rht_block_store(z, p.rht_mask, lane, reinterpret_cast<int8_t*>(p.out) + m * N + nb,
+                                        p.out_e8m0 + m * (N >> 5) + (nb >> 5));
+                } else if (mok) {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const int64_t col = nb + q * 8 + hh * 4;
+                        float y0 = acc[i][j][4 * q] * s, y1 = acc[i][j][4 * q + 1] * s;
+                        float y2 = acc[i][j][4 * q + 2] * s, y3 = acc[i][j][4 * q + 3] * s;
+                        if (EPI == PMN_EPI_F32) {
+                            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
+                        } else {
+                            uint2 v = make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
+                                                 f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
+                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + m * N + col) = v;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                           int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
+                           const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
+                           const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
+                           int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
+                           void* out_aux, hipStream_t stream)
+{
+    FwdArgs p{a_codes, a_scales, a_outer, a_rpo, gather, b_codes, b_scales, b_outer, b_rpo,
+              offsets, G, N, K, rht_mask, out, out_e8m0, out_aux};
+    if (M == 0 || G == 0) return hipSuccess;
+    const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;   // bound on sum of ceil(m_g / 256)
+    const int64_t ntiles = N / fwd::BT;   // SWIGLU: each tile covers 128 w1 and 128 w3 rows
+    dim3 grid((unsigned)ntiles, (unsigned)mtiles);
+    switch (epilogue) {
+    case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32>), grid, dim3(256), 0, stream, p); break;
+    case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16>), grid, dim3(256), 0, stream, p); break;
+    case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU>), grid, dim3(256), 0, stream, p); break;
+    default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6>), grid, dim3(256), 0, stream, p); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pmn

@@ -1,0 +1,194 @@
+// pmn_dev.hpp -- device helpers shared by the HIP kernels of the quantized MoE expert layer.
+//
+// Pages cited (by title and section heading):
+//   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+//          贯穿预训练到最后一次 RL rollout"; sections cited by heading below.
+//
+// Number formats used here (the pages name them; bit layouts are the OCP definitions):
+//   FP4 E2M1 nibble: sign bit 3 | index into {0, .5, 1, 1.5, 2, 3, 4, 6}  ([AREX]
+//     "转置打散分组,随机舍入保住期望值" lists exactly these sixteen values).
+//   E4M3 byte (OCP E4M3FN): bias 7, max 448, subnormal step 2^-9.
+//   E8M0 byte b: 2^(b - 127).
+//
+// gfx950 conversion instructions used, each checked on the device against the CPU oracle:
+//   v_cvt_scalef32_pk_fp4_f32 with scale 1.0: round-to-nearest-even onto the FP4 grid,
+//     saturating at 6, first operand in the low nibble (the scale only contributes its
+//     power-of-two exponent, so it is kept at 1.0 and the block reciprocal is applied first).
+//   v_cvt_scalef32_pk_f16_fp4 / _pk_f32_fp4 with scale 1.0: exact FP4 values.
+//   v_cvt_pk_fp8_f32: round-to-nearest-even E4M3 for |x| <= 448 (NaN above: inputs are clamped).
+//   v_cvt_sr_fp8_f32: stochastic E4M3 rounding that adds the top 20 bits of its random operand
+//     to the 20 discarded mantissa bits; feeding (0xFFFF - r16) << 16 makes it round up exactly
+//     when r16 < floor(f * 2^16), f being the position of |y| between its two grid neighbours.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pmn {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+#define PMN_DEV __device__ __forceinline__
+
+// ---- bf16 ---------------------------------------------------------------------------------
+
+PMN_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+PMN_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+PMN_DEV uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---- E4M3 ---------------------------------------------------------------------------------
+
+// Value of an E4M3 byte (finite codes).
+PMN_DEV float e4m3_value(uint32_t c)
+{
+    uint32_t mag = c & 0x7Fu;
+    float v = (mag < 8u) ? (float)mag * 0x1p-9f : __uint_as_float((mag << 20) + (120u << 23));
+    return (c & 0x80u) ? -v : v;
+}
+
+// Non-negative t -> E4M3 byte, round to nearest even, saturating at 448.
+PMN_DEV uint32_t e4m3_rne_sat(float t)
+{
+    t = fminf(t, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;
+}
+
+// ---- FP4 ----------------------------------------------------------------------------------
+
+// Two fp32 values -> one byte of two FP4 nibbles (a low, b high), placed at byte `sel` of old.
+#define PMN_CVT_FP4(old, a, b, sel) __builtin_amdgcn_cvt_scalef32_pk_fp4_f32((old), (a), (b), 1.0f, (sel))
+
+// Byte `sel` of w (two FP4 nibbles) -> two fp32 values (low nibble first).
+#define PMN_FP4_TO_F32(w, sel) __builtin_amdgcn_cvt_scalef32_pk_f32_fp4((w), 1.0f, (sel))
+
+// Byte `sel` of w -> two fp16 values (low nibble first).
+#define PMN_FP4_TO_F16(w, sel) __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), 1.0f, (sel))
+
+// The 8 FP4 values of a code word (element 0 in the low nibble of byte 0) as fp32.
+PMN_DEV void fp4x8_to_f32(uint32_t w, float (&q)[8])
+{
+    const f32x2 a = PMN_FP4_TO_F32(w, 0), b = PMN_FP4_TO_F32(w, 1);
+    const f32x2 c = PMN_FP4_TO_F32(w, 2), d = PMN_FP4_TO_F32(w, 3);
+    q[0] = a.x; q[1] = a.y; q[2] = b.x; q[3] = b.y;
+    q[4] = c.x; q[5] = c.y; q[6] = d.x; q[7] = d.y;
+}
+
+// ---- E8M0 block exponent ----------------------------------------------------------------
+//
+// Smallest e in [-127, 127] with amax <= M * 2^e, for M = 448 (E4M3 elements), 6 (E2M1) and
+// 127/64 (S2F6). With amax = m * 2^E (m in [1, 2)) and M = mM * 2^EM, e = E - EM + [m > mM].
+// [AREX] "转置打散分组,随机舍入保住期望值": the backward must not be biased, so no element of a
+// block may saturate; this rule guarantees that.
+enum { E8M0_E4M3 = 0, E8M0_E2M1 = 1, E8M0_S2F6 = 2 };
+
+template <int KIND>
+PMN_DEV int e8m0_exponent(float amax)
+{
+    constexpr int EM = KIND == E8M0_E4M3 ? 8 : (KIND == E8M0_E2M1 ? 2 : 0);
+    constexpr uint32_t MANT = KIND == E8M0_E4M3 ? 0x600000u : (KIND == E8M0_E2M1 ? 0x400000u : 0x7E0000u);
+    uint32_t u = __float_as_uint(amax);
+    if (u == 0u) return -127;
+    int E;
+    uint32_t m;
+    uint32_t ef = u >> 23;
+    if (ef != 0u) {
+        E = (int)ef - 127;
+        m = u & 0x7FFFFFu;
+    } else {                              // fp32 subnormal: normalize
+        int lz = __builtin_clz(u) - 8;    // u < 2^23
+        E = -126 - lz;
+        m = (u << lz) & 0x7FFFFFu;
+    }
+    int e = E - EM + (m > MANT ? 1 : 0);
+    e = e < -127 ? -127 : e;
+    e = e > 127 ? 127 : e;
+    return e;
+}
+
+// ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------------------------
+
+PMN_DEV void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; r++) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        c[1] = (uint32_t)p1;
+        c[3] = (uint32_t)p0;
+        c[0] = n0;
+        c[2] = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+// The 8 random 16-bit values of elements 8*blk .. 8*blk+7 under (seed, stream), returned as
+// four words: element 8*blk + j uses half (j & 1) of word j >> 1 (low half first).
+PMN_DEV void rand16x8(uint64_t seed, uint32_t stream, uint64_t blk, uint32_t w[4])
+{
+    w[0] = (uint32_t)blk;
+    w[1] = (uint32_t)(blk >> 32);
+    w[2] = stream;
+    w[3] = 0u;
+    philox4x32_10(w, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+// SR operand of the hardware converter for the element that owns 16-bit half `hi` of word w.
+PMN_DEV uint32_t sr_operand(uint32_t w, int hi)
+{
+    uint32_t r16 = hi ? (w >> 16) : (w & 0xFFFFu);
+    return (0xFFFFu - r16) << 16;
+}
+
+// y (|y| <= 448) -> E4M3 byte by stochastic rounding with the given SR operand.
+PMN_DEV uint32_t e4m3_sr(float y, uint32_t rng)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_sr_fp8_f32(y, (int)rng, 0, 0) & 0xFFu;
+}
+
+// y (|y| <= 448) -> E4M3 byte, round to nearest even.
+PMN_DEV uint32_t e4m3_rne(float y)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
+}
+
+// y (|y| <= 6) -> FP4 nibble by stochastic rounding with 16 random bits (the E2M1 requant
+// target, used for the pages' worked example): up iff r16 < floor(f * 2^16).
+PMN_DEV uint32_t fp4_sr(float y, uint32_t r16)
+{
+    float a = fabsf(y);
+    uint32_t base, scale_shift;
+    if (a < 2.0f) { base = 0u; scale_shift = 17; }        // step 0.5: n = 2a
+    else if (a < 4.0f) { base = 2u; scale_shift = 16; }   // step 1:   n = a, index = 2 + n
+    else { base = 4u; scale_shift = 15; }                 // step 2:   n = a/2, index = 4 + n
+    uint32_t N = (uint32_t)(a * __uint_as_float((127u + scale_shift) << 23));
+    uint32_t L = N >> 16, f16 = N & 0xFFFFu;
+    uint32_t idx = base + L + (r16 < f16 ? 1u : 0u);
+    idx = idx > 7u ? 7u : idx;
+    return idx | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// ---- wave reductions ------------------------------------------------------------------------
+
+PMN_DEV float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+}  // namespace pmn

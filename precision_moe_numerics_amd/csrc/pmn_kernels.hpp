@@ -1,0 +1,55 @@
+// pmn_kernels.hpp -- launchers of the HIP kernels (internal to the library; the public
+// interface is include/pmn.h). Every launcher only enqueues work on `stream` and returns
+// hipGetLastError(); arguments are validated by the C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmn.h"
+
+namespace pmn {
+
+hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
+                                 int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
+                                 uint8_t* scales, float* outer_out, hipStream_t stream);
+
+hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
+                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, hipStream_t stream);
+
+hipError_t launch_rht32_s2f6(const void* x, bool f32, int64_t rows, int64_t cols, uint32_t mask,
+                             int8_t* codes, uint8_t* e8m0, hipStream_t stream);
+
+hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                          int64_t cols, int64_t rows_per_outer, const int32_t* gather, int64_t M,
+                          const int64_t* offsets, int G, int target, uint64_t seed,
+                          uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, int64_t ld,
+                          int64_t* padded_offsets, hipStream_t stream);
+
+hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                             int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
+                             uint8_t* out_e8m0, int64_t ld, int64_t* padded_offsets,
+                             hipStream_t stream);
+
+hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                           int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
+                           const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
+                           const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
+                           int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
+                           void* out_aux, hipStream_t stream);
+
+hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
+                              const uint8_t* wte, const int64_t* offsets, int G, int64_t M,
+                              int64_t Nf, int64_t Kf, float* dx, hipStream_t stream);
+
+hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
+                              const uint8_t* xte, int64_t ld, const int64_t* po, int G,
+                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream);
+
+hipError_t launch_swiglu_bwd(const float* da, const uint16_t* h13, int64_t M, int64_t F,
+                             uint16_t* dh13, hipStream_t stream);
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
+                        int64_t* offsets, int32_t* gather_token, int32_t* slot_of, hipStream_t stream);
+
+}  // namespace pmn

@@ -1,0 +1,412 @@
+// quant.hip -- NVFP4 quantization, MXFP8 row-wise gradient quantization and the standalone
+// RHT32 + S2F6 combine quantizer.
+//
+// Pages cited (by title and section heading):
+//   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+//          贯穿预训练到最后一次 RL rollout".
+//
+// All three kernels stream HBM once: each element is read once and its codes written once; the
+// per-token outer scale is reduced across a wavefront while the row sits in registers.
+#include "pmn_dev.hpp"
+#include "pmn_kernels.hpp"
+
+namespace pmn {
+
+// ------------------------------------------------------------------------------------------
+// NVFP4 block quantization  [AREX] "转置打散分组,随机舍入保住期望值": 16 consecutive values share
+// an E4M3 scale chosen so that the block max lands on the top of the FP4 grid.
+// [AREX] "配方的代价:预训练约 2% 的计算效率": activations pick the better of two scale factors
+// (here: the block max mapped to 6 or to 4, the smaller squared error wins, ties keep 6).
+// ------------------------------------------------------------------------------------------
+
+struct Block16 {
+    float x[16];
+};
+
+PMN_DEV void load_block(const uint4* p, Block16& b)
+{
+    uint4 lo = p[0], hi = p[1];
+    uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        b.x[2 * i] = bf16_lo(w[i]);
+        b.x[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+PMN_DEV float block_absmax(const Block16& b)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) m = fmaxf(m, fabsf(b.x[i]));
+    return m;
+}
+
+// One candidate: scale byte, 16 nibbles (2 words) and the effective scale d.
+template <int CAND>
+PMN_DEV void quant_candidate(const Block16& b, float ab, float s_o, uint32_t& sb, uint32_t& w0,
+                             uint32_t& w1, float& d)
+{
+    float t = (ab / (float)CAND) / s_o;
+    sb = e4m3_rne_sat(t);
+    d = e4m3_value(sb) * s_o;
+    float r = (d != 0.0f) ? fminf(1.0f / d, 3.402823466e38f) : 0.0f;
+    w0 = 0u;
+    w1 = 0u;
+    w0 = PMN_CVT_FP4(w0, b.x[0] * r, b.x[1] * r, 0);
+    w0 = PMN_CVT_FP4(w0, b.x[2] * r, b.x[3] * r, 1);
+    w0 = PMN_CVT_FP4(w0, b.x[4] * r, b.x[5] * r, 2);
+    w0 = PMN_CVT_FP4(w0, b.x[6] * r, b.x[7] * r, 3);
+    w1 = PMN_CVT_FP4(w1, b.x[8] * r, b.x[9] * r, 0);
+    w1 = PMN_CVT_FP4(w1, b.x[10] * r, b.x[11] * r, 1);
+    w1 = PMN_CVT_FP4(w1, b.x[12] * r, b.x[13] * r, 2);
+    w1 = PMN_CVT_FP4(w1, b.x[14] * r, b.x[15] * r, 3);
+}
+
+// Squared error e = fma(delta_i, delta_i, e) over i = 0..15, delta_i = fma(-q_i, d, x_i).
+PMN_DEV float candidate_error(const Block16& b, uint32_t w0, uint32_t w1, float d)
+{
+    float q[16];
+    float (&q0)[8] = *reinterpret_cast<float(*)[8]>(&q[0]);
+    float (&q1)[8] = *reinterpret_cast<float(*)[8]>(&q[8]);
+    fp4x8_to_f32(w0, q0);
+    fp4x8_to_f32(w1, q1);
+    float e = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        const float delta = __builtin_fmaf(-q[i], d, b.x[i]);
+        e = __builtin_fmaf(delta, delta, e);
+    }
+    return e;
+}
+
+template <bool FOUR_SIX>
+PMN_DEV void quant_block(const Block16& b, float s_o, uint32_t& sb, uint2& q)
+{
+    float ab = block_absmax(b);
+    uint32_t sb6, a0, a1;
+    float d6;
+    quant_candidate<6>(b, ab, s_o, sb6, a0, a1, d6);
+    sb = sb6;
+    q = make_uint2(a0, a1);
+    if (FOUR_SIX) {
+        uint32_t sb4, c0, c1;
+        float d4;
+        quant_candidate<4>(b, ab, s_o, sb4, c0, c1, d4);
+        float e6 = candidate_error(b, a0, a1, d6);
+        float e4 = candidate_error(b, c0, c1, d4);
+        if (e4 < e6) {
+            sb = sb4;
+            q = make_uint2(c0, c1);
+        }
+    }
+}
+
+PMN_DEV float outer_from_amax(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
+
+// One wavefront per row; the row stays in registers (NBL blocks of 16 per lane) while its
+// amax is reduced, then every block is quantized. Rows of up to 64 * 16 * NBL values.
+template <int NBL, bool FOUR_SIX>
+__global__ __launch_bounds__(256) void k_nvfp4_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                    int64_t cols, uint8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ scales,
+                                                    float* __restrict__ outer_out)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows) return;
+    const int nb = (int)(cols >> 4);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + r * cols);
+    Block16 blk[NBL];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBL; j++) {
+        int b = lane + 64 * j;
+        if (b < nb) {
+            load_block(xr + 2 * b, blk[j]);
+            amax = fmaxf(amax, block_absmax(blk[j]));
+        }
+    }
+    amax = wave_max(amax);
+    const float s_o = outer_from_amax(amax);
+    if (lane == 0) outer_out[r] = s_o;
+    uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
+    uint8_t* sr = scales + r * nb;
+#pragma unroll
+    for (int j = 0; j < NBL; j++) {
+        int b = lane + 64 * j;
+        if (b < nb) {
+            uint32_t sb;
+            uint2 q;
+            quant_block<FOUR_SIX>(blk[j], s_o, sb, q);
+            cr[b] = q;
+            sr[b] = (uint8_t)sb;
+        }
+    }
+}
+
+// One thread per block of 16 with the outer scales already known (weights after the group
+// amax pass, caller-provided outer scales, or rows too long for k_nvfp4_rows).
+template <bool FOUR_SIX>
+__global__ __launch_bounds__(256) void k_nvfp4_given(const uint16_t* __restrict__ x, int64_t rows,
+                                                     int64_t cols, int64_t rows_per_outer,
+                                                     const float* __restrict__ outer,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales)
+{
+    const int64_t nb = cols >> 4;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= rows * nb) return;
+    const int64_t r = i / nb;
+    Block16 blk;
+    load_block(reinterpret_cast<const uint4*>(x) + 2 * i, blk);
+    uint32_t sb;
+    uint2 q;
+    quant_block<FOUR_SIX>(blk, outer[r / rows_per_outer], sb, q);
+    reinterpret_cast<uint2*>(codes)[i] = q;
+    scales[i] = (uint8_t)sb;
+}
+
+// Group amax: max |x| over each group of rows_per_outer rows, as fp32 bits folded with an
+// integer atomic max (order-independent and exact, so the result is deterministic).
+__global__ __launch_bounds__(256) void k_group_amax(const uint16_t* __restrict__ x, int64_t group_elems,
+                                                    uint32_t* __restrict__ amax_bits)
+{
+    const int64_t g = blockIdx.y;
+    const uint4* xg = reinterpret_cast<const uint4*>(x + g * group_elems);
+    const int64_t n16 = group_elems >> 3;
+    float m = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (int64_t)gridDim.x * blockDim.x) {
+        uint4 v = xg[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.x)), fabsf(bf16_hi(v.x))), fmaxf(fabsf(bf16_lo(v.y)), fabsf(bf16_hi(v.y)))));
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(bf16_lo(v.z)), fabsf(bf16_hi(v.z))), fmaxf(fabsf(bf16_lo(v.w)), fabsf(bf16_hi(v.w)))));
+    }
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(amax_bits + g, __float_as_uint(m));
+}
+
+__global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+__global__ void k_outer_from_amax(float* outer, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) outer[i] = outer_from_amax(outer[i]);   // outer[i] holds the amax bits
+}
+
+__global__ void k_copy_f32(const float* __restrict__ a, float* __restrict__ b, int64_t n)
+{
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) b[i] = a[i];
+}
+
+hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
+                                 int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
+                                 uint8_t* scales, float* outer_out, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    const int64_t nb = cols / 16;
+    const int64_t ngroups = rows / rows_per_outer;
+    if (outer_in == nullptr && rows_per_outer == 1 && nb <= 64 * 8) {
+        const int64_t grid = (rows + 3) / 4;
+        int nbl = nb <= 64 ? 1 : (nb <= 128 ? 2 : (nb <= 256 ? 4 : 8));
+#define PMN_ROWS(N)                                                                                       \
+    if (four_six) hipLaunchKernelGGL((k_nvfp4_rows<N, true>), dim3(grid), dim3(256), 0, stream, x, rows, cols, codes, scales, outer_out); \
+    else hipLaunchKernelGGL((k_nvfp4_rows<N, false>), dim3(grid), dim3(256), 0, stream, x, rows, cols, codes, scales, outer_out);
+        switch (nbl) {
+        case 1: PMN_ROWS(1) break;
+        case 2: PMN_ROWS(2) break;
+        case 4: PMN_ROWS(4) break;
+        default: PMN_ROWS(8) break;
+        }
+#undef PMN_ROWS
+        return hipGetLastError();
+    }
+    if (outer_in != nullptr) {
+        hipLaunchKernelGGL(k_copy_f32, dim3((ngroups + 255) / 256), dim3(256), 0, stream, outer_in, outer_out, ngroups);
+    } else {
+        uint32_t* amax = reinterpret_cast<uint32_t*>(outer_out);
+        hipLaunchKernelGGL(k_fill_u32, dim3((ngroups + 255) / 256), dim3(256), 0, stream, amax, ngroups, 0u);
+        const int64_t group_elems = rows_per_outer * cols;
+        int64_t gx = (group_elems / 8 + 255) / 256;
+        gx = gx > 512 ? 512 : (gx < 1 ? 1 : gx);
+        hipLaunchKernelGGL(k_group_amax, dim3((unsigned)gx, (unsigned)ngroups), dim3(256), 0, stream, x, group_elems, amax);
+        hipLaunchKernelGGL(k_outer_from_amax, dim3((ngroups + 255) / 256), dim3(256), 0, stream, outer_out, ngroups);
+    }
+    const int64_t nblocks = rows * nb;
+    const int64_t grid = (nblocks + 255) / 256;
+    if (four_six)
+        hipLaunchKernelGGL((k_nvfp4_given<true>), dim3(grid), dim3(256), 0, stream, x, rows, cols, rows_per_outer, outer_out, codes, scales);
+    else
+        hipLaunchKernelGGL((k_nvfp4_given<false>), dim3(grid), dim3(256), 0, stream, x, rows, cols, rows_per_outer, outer_out, codes, scales);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// MXFP8 row-wise quantization of gradients  [AREX] "只把专家层的前向传播降到 4-bit" (gradients
+// go through MXFP8 matmuls). One thread per block of 32: e from the block amax, y = x * 2^-e,
+// E4M3 by round-to-nearest-even or by stochastic rounding.
+// ------------------------------------------------------------------------------------------
+
+template <bool SR>
+__global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t M,
+                                                    int64_t N, uint64_t seed, uint32_t stream_id,
+                                                    uint8_t* __restrict__ out,
+                                                    uint8_t* __restrict__ out_e8m0)
+{
+    const int64_t nb = N >> 5;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * nb) return;
+    const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * i;
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint4 v = p[q];
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+    const int e = e8m0_exponent<E8M0_E4M3>(amax);
+    out_e8m0[i] = (uint8_t)(e + 127);
+    uint32_t o[8];
+    if (SR) {
+        const int64_t r = i / nb;
+        const int64_t c0 = (i - r * nb) * 32;
+        const uint64_t idx0 = (uint64_t)r * (uint64_t)N + (uint64_t)c0;   // multiple of 8
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t rw[4];
+            rand16x8(seed, stream_id, (idx0 >> 3) + q, rw);
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                uint32_t word = w[4 * q + j / 2];
+                float v = (j & 1) ? bf16_hi(word) : bf16_lo(word);
+                uint32_t c = e4m3_sr(__builtin_ldexpf(v, -e), sr_operand(rw[j >> 1], j & 1));
+                if (j < 4) lo |= c << (8 * j); else hi |= c << (8 * (j - 4));
+            }
+            o[2 * q] = lo;
+            o[2 * q + 1] = hi;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            float v0 = __builtin_ldexpf(bf16_lo(w[2 * q]), -e), v1 = __builtin_ldexpf(bf16_hi(w[2 * q]), -e);
+            float v2 = __builtin_ldexpf(bf16_lo(w[2 * q + 1]), -e), v3 = __builtin_ldexpf(bf16_hi(w[2 * q + 1]), -e);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+            o[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
+        }
+    }
+    uint4* po = reinterpret_cast<uint4*>(out) + 2 * i;
+    po[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
+                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, hipStream_t stream)
+{
+    const int64_t n = M * (N / 32);
+    if (n == 0) return hipSuccess;
+    const int64_t grid = (n + 255) / 256;
+    if (sr)
+        hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out, out_e8m0);
+    else
+        hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out, out_e8m0);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------
+// RHT32 + S2F6  [AREX] "计算提速后,NVLink 通信成了新瓶颈": a 32-point randomized Hadamard
+// transform (orthogonal, exactly invertible) spreads outliers, then S2F6 codes (2-bit signed
+// integer part, 6-bit fraction: -128/64 .. 127/64) with one scale per 32 values.
+// One thread per 32-chunk: the whole butterfly network runs in registers.
+// ------------------------------------------------------------------------------------------
+
+PMN_DEV void rht32_s2f6_chunk(float (&t)[32], uint32_t mask, uint32_t (&o)[8], uint32_t& e8m0)
+{
+#pragma unroll
+    for (int j = 0; j < 32; j++) t[j] = __uint_as_float(__float_as_uint(t[j]) ^ (((mask >> j) & 1u) << 31));
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; i++) {
+            if ((i & h) == 0) {
+                float a = t[i], b = t[i + h];
+                t[i] = a + b;
+                t[i + h] = a - b;
+            }
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) amax = fmaxf(amax, fabsf(t[j]));
+    const int e = e8m0_exponent<E8M0_S2F6>(amax);
+    e8m0 = (uint32_t)(e + 127);
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        uint32_t w = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            int c = (int)__builtin_rintf(__builtin_ldexpf(t[4 * q + j], 6 - e));
+            w |= ((uint32_t)c & 0xFFu) << (8 * j);
+        }
+        o[q] = w;
+    }
+}
+
+template <bool F32>
+__global__ __launch_bounds__(256) void k_rht32_s2f6(const void* __restrict__ x, int64_t rows,
+                                                    int64_t cols, uint32_t mask,
+                                                    int8_t* __restrict__ codes,
+                                                    uint8_t* __restrict__ e8m0)
+{
+    const int64_t n = rows * (cols >> 5);
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    float t[32];
+    if (F32) {
+        const float4* p = reinterpret_cast<const float4*>(x) + 8 * i;
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            float4 v = p[q];
+            t[4 * q] = v.x; t[4 * q + 1] = v.y; t[4 * q + 2] = v.z; t[4 * q + 3] = v.w;
+        }
+    } else {
+        const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * i;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint4 v = p[q];
+            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                t[8 * q + 2 * j] = bf16_lo(w[j]);
+                t[8 * q + 2 * j + 1] = bf16_hi(w[j]);
+            }
+        }
+    }
+    uint32_t o[8], e;
+    rht32_s2f6_chunk(t, mask, o, e);
+    uint4* po = reinterpret_cast<uint4*>(codes) + 2 * i;
+    po[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    e8m0[i] = (uint8_t)e;
+}
+
+hipError_t launch_rht32_s2f6(const void* x, bool f32, int64_t rows, int64_t cols, uint32_t mask,
+                             int8_t* codes, uint8_t* e8m0, hipStream_t stream)
+{
+    const int64_t n = rows * (cols / 32);
+    if (n == 0) return hipSuccess;
+    const int64_t grid = (n + 255) / 256;
+    if (f32)
+        hipLaunchKernelGGL((k_rht32_s2f6<true>), dim3(grid), dim3(256), 0, stream, x, rows, cols, mask, codes, e8m0);
+    else
+        hipLaunchKernelGGL((k_rht32_s2f6<false>), dim3(grid), dim3(256), 0, stream, x, rows, cols, mask, codes, e8m0);
+    return hipGetLastError();
+}
+
+}  // namespace pmn

@@ -1,0 +1,248 @@
+// requant.hip -- backward operand preparation: dequantize the saved NVFP4 tensor, transpose it
+// and re-quantize it to MXFP8 with stochastic rounding; and the column-wise (transposed,
+// grouped) MXFP8 quantization of bf16 gradients, which shares the same output layout.
+//
+// Pages cited (by title and section heading):
+//   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
+//          贯穿预训练到最后一次 RL rollout", section "转置打散分组,随机舍入保住期望值": the backward
+//          needs the forward tensors transposed; blocks then run the other way, so the saved
+//          tensor is dequantized to high precision, transposed and re-quantized with stochastic
+//          rounding, keeping the expectation equal to the forward value; MXFP8 is the chosen
+//          re-quantization precision.
+//
+// Work split. A wavefront owns one 32-slot block of the padded output (one E8M0 scale per
+// output row) and 64 groups of 8 consecutive source columns; each lane owns 8 columns. The 8
+// columns of a lane are 8 consecutive element indices of one source row, which is exactly one
+// Philox4x32-10 call (16 random bits per element), so every random bit is drawn once. Pass 1
+// reduces the per-column amax over the 32 slots with the codes kept in registers; pass 2
+// converts and writes 16 bytes per column every 16 slots.
+#include "pmn_dev.hpp"
+#include "pmn_kernels.hpp"
+
+namespace pmn {
+
+struct GroupBlock {
+    int64_t s0;   // first slot of the block
+    int valid;    // slots of the block that exist (the rest is zero padding)
+    bool live;    // the block lies inside the padded output
+};
+
+// Map padded block pb (32 output columns) to its slots: walk the groups, each padded to 32.
+PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t M)
+{
+    GroupBlock r;
+    const int64_t col = pb * 32;
+    if (offsets == nullptr) {
+        r.s0 = col;
+        r.live = col < M;
+        int64_t v = M - col;
+        r.valid = (int)(v > 32 ? 32 : (v < 0 ? 0 : v));
+        return r;
+    }
+    int64_t po = 0;
+    for (int g = 0; g < G; g++) {
+        int64_t a = offsets[g], b = offsets[g + 1];
+        int64_t P = (b - a + 31) & ~(int64_t)31;
+        if (col < po + P) {
+            r.s0 = a + (col - po);
+            int64_t v = (b < M ? b : M) - r.s0;     // never past the last slot
+            v = v < 0 ? 0 : v;
+            r.valid = (int)(v > 32 ? 32 : v);
+            r.live = true;
+            return r;
+        }
+        po += P;
+    }
+    r.s0 = 0;
+    r.valid = 0;
+    r.live = false;
+    return r;
+}
+
+__global__ void k_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* po)
+{
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    if (offsets == nullptr) {
+        po[0] = 0;
+        po[1] = (M + 31) & ~(int64_t)31;
+        return;
+    }
+    int64_t p = 0;
+    po[0] = 0;
+    for (int g = 0; g < G; g++) {
+        p += (offsets[g + 1] - offsets[g] + 31) & ~(int64_t)31;
+        po[g + 1] = p;
+    }
+}
+
+enum { SRC_NVFP4 = 0, SRC_BF16 = 1 };
+
+struct TransposeArgs {
+    // source
+    const uint8_t* codes;     // NVFP4 codes [src_rows x cols/2]    (SRC_NVFP4)
+    const uint8_t* scales;    // E4M3 [src_rows x cols/16]
+    const float* outer;       // [src_rows / rows_per_outer]
+    int64_t rows_per_outer;
+    const uint16_t* x;        // bf16 [M x cols]                    (SRC_BF16)
+    int64_t cols;
+    const int32_t* gather;    // slot -> source row (nullable)
+    int64_t M;
+    const int64_t* offsets;   // [G+1] (nullable)
+    int G;
+    uint64_t seed;
+    uint32_t stream_id;
+    uint8_t* out;             // [cols x ld]
+    uint8_t* out_e8m0;        // [cols x ld/32]
+    int64_t ld;
+};
+
+// Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
+PMN_DEV void deq8(uint32_t cw, float d, float (&v)[8])
+{
+    float q[8];
+    fp4x8_to_f32(cw, q);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = q[i] * d;
+}
+
+PMN_DEV void bf8(uint4 w, float (&v)[8])
+{
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (nibble/byte).
+template <int SRC, int ROUND, int TARGET>
+__global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t pb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t cg = (int64_t)blockIdx.y * 64 + lane;   // column group of 8
+    const int64_t c0 = cg * 8;
+    GroupBlock blk = find_block(pb, a.offsets, a.G, a.M);
+    if (!blk.live || c0 >= a.cols) return;
+
+    // ---- pass 1: load the 32 slots of this column group, per-column amax
+    uint32_t cw[32];      // NVFP4: code words; BF16: unused
+    float dsc[32];        // NVFP4: effective block scale per slot
+    uint4 xw[32];         // BF16: raw values
+    float amax[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) amax[c] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j++) {
+        float v[8];
+        if (j < blk.valid) {
+            const int64_t s = blk.s0 + j;
+            if (SRC == SRC_NVFP4) {
+                const int64_t r = a.gather ? (int64_t)a.gather[s] : s;
+                cw[j] = *reinterpret_cast<const uint32_t*>(a.codes + ((r * a.cols + c0) >> 1));
+                float sb = e4m3_value(a.scales[(r * a.cols + c0) >> 4]);
+                dsc[j] = sb * a.outer[r / a.rows_per_outer];
+                deq8(cw[j], dsc[j], v);
+            } else {
+                xw[j] = *reinterpret_cast<const uint4*>(a.x + s * a.cols + c0);
+                bf8(xw[j], v);
+            }
+#pragma unroll
+            for (int c = 0; c < 8; c++) amax[c] = fmaxf(amax[c], fabsf(v[c]));
+        } else {
+            if (SRC == SRC_NVFP4) { cw[j] = 0u; dsc[j] = 0.0f; }
+            else xw[j] = make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+    int e[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        e[c] = TARGET == 0 ? e8m0_exponent<E8M0_E4M3>(amax[c]) : e8m0_exponent<E8M0_E2M1>(amax[c]);
+        a.out_e8m0[(c0 + c) * (a.ld >> 5) + pb] = (uint8_t)(e[c] + 127);
+    }
+
+    // ---- pass 2: convert, 16 slots at a time (4 words per column), write 16 bytes per column
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+        uint32_t o[8][4];
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) o[c][q] = 0u;
+#pragma unroll
+        for (int jj = 0; jj < 16; jj++) {
+            const int j = half * 16 + jj;
+            if (j < blk.valid) {
+                const int64_t s = blk.s0 + j;
+                float v[8];
+                if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
+                else bf8(xw[j], v);
+                uint32_t rw[4] = {0u, 0u, 0u, 0u};
+                if (ROUND == 1) rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                    const float y = __builtin_ldexpf(v[c], -e[c]);
+                    uint32_t code;
+                    if (TARGET == 0) {
+                        code = ROUND == 1 ? e4m3_sr(y, sr_operand(rw[c >> 1], c & 1)) : e4m3_rne(y);
+                    } else {
+                        uint32_t word = rw[c >> 1];
+                        code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
+                    }
+                    o[c][jj >> 2] |= code << (8 * (jj & 3));
+                }
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            uint4* dst = reinterpret_cast<uint4*>(a.out + (c0 + c) * a.ld + pb * 32 + half * 16);
+            *dst = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+        }
+    }
+}
+
+static hipError_t launch_transpose(const TransposeArgs& a, int src, int round, int target,
+                                   int64_t* padded_offsets, hipStream_t stream)
+{
+    if (padded_offsets)
+        hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, a.offsets, a.G, a.M, padded_offsets);
+    const int64_t nblk = a.ld / 32;
+    if (nblk == 0 || a.cols == 0) return hipGetLastError();
+    dim3 grid((unsigned)((nblk + 3) / 4), (unsigned)((a.cols / 8 + 63) / 64));
+    if (src == SRC_NVFP4) {
+        if (target == 0) {
+            if (round == 1) hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 1, 0>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 0, 0>), grid, dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 1, 1>), grid, dim3(256), 0, stream, a);
+        }
+    } else {
+        if (round == 1) hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 1, 0>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 0, 0>), grid, dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const float* outer,
+                          int64_t cols, int64_t rows_per_outer, const int32_t* gather, int64_t M,
+                          const int64_t* offsets, int G, int target, uint64_t seed,
+                          uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, int64_t ld,
+                          int64_t* padded_offsets, hipStream_t stream)
+{
+    TransposeArgs a{};
+    a.codes = codes; a.scales = scales; a.outer = outer; a.rows_per_outer = rows_per_outer;
+    a.x = nullptr; a.cols = cols; a.gather = gather; a.M = M; a.offsets = offsets; a.G = G;
+    a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
+    return launch_transpose(a, SRC_NVFP4, 1, target, padded_offsets, stream);
+}
+
+hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                             int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
+                             uint8_t* out_e8m0, int64_t ld, int64_t* padded_offsets,
+                             hipStream_t stream)
+{
+    TransposeArgs a{};
+    a.codes = nullptr; a.scales = nullptr; a.outer = nullptr; a.rows_per_outer = 1;
+    a.x = x; a.cols = N; a.gather = nullptr; a.M = M; a.offsets = offsets; a.G = G;
+    a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
+    return launch_transpose(a, SRC_BF16, sr ? 1 : 0, 0, padded_offsets, stream);
+}
+
+}  // namespace pmn

@@ -1,0 +1,89 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry point
+that include/pmn.h declares, and rejects bad arguments before launching anything."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pmn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_five_hot_path_calls():
+    names = declared_functions()
+    for n in ("nvfp4_quantize", "requant_transpose_sr_mxfp8", "moe_grouped_gemm_fwd", "moe_grouped_gemm_bwd",
+              "rht32_s2f6_quantize"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import precision_moe_numerics_amd as P
+    lib = C.CDLL(P.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(P.ABI_FUNCTIONS) <= set(declared_functions())
+
+
+def test_library_has_gfx950_code_only():
+    import precision_moe_numerics_amd as P
+    data = open(P.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in data
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import precision_moe_numerics_amd as P
+    return P._lib
+
+
+def test_argument_errors_without_launch(lib):
+    fake = C.c_void_p(0x1000)     # never dereferenced: every call below fails its host checks
+    # bad shapes
+    assert lib.nvfp4_quantize(fake, 4, 15, 1, 1, None, fake, fake, fake, None) == -2
+    assert lib.nvfp4_quantize(fake, 6, 32, 1, 4, None, fake, fake, fake, None) == -2
+    assert lib.nvfp4_quantize(fake, 4, 32, 7, 1, None, fake, fake, fake, None) == -1
+    assert lib.nvfp4_quantize(None, 4, 32, 1, 1, None, fake, fake, fake, None) == -1
+    assert lib.nvfp4_quantize(C.c_void_p(0x1001), 4, 32, 1, 1, None, fake, fake, fake, None) == -3
+    # requant: ld too small for the groups, offsets/G mismatch
+    assert lib.requant_transpose_sr_mxfp8(fake, fake, fake, 64, 32, 1, None, 64, fake, 2, 0, 0, 0, fake, fake,
+                                          64, None, None) == -2
+    assert lib.requant_transpose_sr_mxfp8(fake, fake, fake, 64, 32, 1, None, 64, None, 2, 0, 0, 0, fake, fake,
+                                          256, None, None) == -2
+    assert lib.requant_transpose_sr_mxfp8(fake, fake, fake, 64, 32, 1, None, 64, None, 0, 5, 0, 0, fake, fake,
+                                          64, None, None) == -1
+    # rht: cols not a multiple of 32
+    assert lib.rht32_s2f6_quantize(fake, 0, 2, 48, 0, fake, fake, None) == -2
+    # gemm fwd: N not a multiple of 256, K not a multiple of 64
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 128, 64, 0,
+                                    0, fake, None, None, None) == -2
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 256, 96, 0,
+                                    0, fake, None, None, None) == -2
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 256, 64, 3,
+                                    0, fake, None, None, None) == -1
+    # gemm bwd: workspace too small
+    ws = lib.moe_grouped_gemm_bwd_workspace_size(64, 1, 256, 256, 3)
+    assert ws > 0
+    assert lib.moe_grouped_gemm_bwd(fake, fake, fake, fake, 64, 1, None, fake, fake, fake, 256, fake, 1, 64, 256, 256,
+                                    3, 0, 0, 1, 2, 3, fake, fake, fake, ws - 1, None) == -4
+    assert lib.moe_grouped_gemm_bwd(fake, fake, fake, fake, 64, 1, None, fake, fake, fake, 256, fake, 1, 64, 256, 256,
+                                    0, 0, 0, 1, 2, 3, fake, fake, fake, ws, None) == -1
+    # routing: k > E
+    assert lib.moe_route_topk(fake, 4, 4, 8, fake, fake, fake, fake, fake, None) == -2
+    assert lib.pmn_strerror(-4) == b"workspace missing or too small"
+    assert lib.pmn_padded_bound(33, 2) == 64 + 64
+
+
+def test_zero_size_calls_are_no_ops(lib):
+    assert lib.nvfp4_quantize(None, 0, 32, 1, 1, None, None, None, None, None) == 0
+    assert lib.rht32_s2f6_quantize(None, 0, 0, 64, 0, None, None, None) == 0

@@ -1,0 +1,346 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bit-exact for every code, scale byte, index and integer output; GEMM outputs within 2e-3
+relative Frobenius error of the oracle on identical quantized operands. Inputs are seeded
+synthetic tensors from precision_moe_numerics_amd.inputs (or seeded numpy draws), sized so the
+oracle finishes in seconds while the kernels still see several tiles and ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def P():
+    import precision_moe_numerics_amd as P
+    return P
+
+
+@pytest.fixture(scope="module")
+def I():
+    from precision_moe_numerics_amd import inputs as I
+    return I
+
+
+def npy(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def bf16_np(a):
+    return torch.tensor(np.asarray(a, np.float32)).to(torch.bfloat16)
+
+
+def rel_fro(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return np.linalg.norm(np.asarray(got, np.float64) - ref) / max(np.linalg.norm(ref), 1e-300)
+
+
+def assert_nvfp4_equal(q, ref, rows=None):
+    codes, scales, outer = npy(q.codes), npy(q.scales), npy(q.outer)
+    if rows is not None:
+        codes, scales = codes[rows], scales[rows]
+    assert np.array_equal(scales, ref["scales"]), "scale bytes differ"
+    assert np.array_equal(codes, ref["codes"]), "codes differ"
+    if rows is None:
+        assert np.array_equal(outer, ref["outer"]), "outer scales differ"
+
+
+# ------------------------------------------------------------------------------------------
+# NVFP4 quantization
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,nu", [(256, 512, 0), (300, 7168, 3), (130, 1536, 4), (67, 16, 3),
+                                          (33, 8208, 3), (5, 4096, 0)])
+@pytest.mark.parametrize("four_six", [True, False])
+def test_nvfp4_quantize_rows(P, I, rows, cols, nu, four_six):
+    x = I.student_t((rows, cols), nu, 0.5, 11) if nu else I.normal((rows, cols), 1.0, 12)
+    q = P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT if four_six else P.NVFP4_WEIGHT)
+    ref = O.nvfp4_quantize(x, 1, four_six)
+    assert_nvfp4_equal(q, ref)
+
+
+@pytest.mark.parametrize("rpo", [256, 512, 32])
+def test_nvfp4_quantize_weight_groups(P, I, rpo):
+    w = I.normal((4 * 256 + 512, 512), 0.02, 13)[: (4 * 256 + 512) // rpo * rpo]
+    q = P.nvfp4_quantize(w.to(DEV), P.NVFP4_WEIGHT, rows_per_outer=rpo)
+    ref = O.nvfp4_quantize(w, rpo, False)
+    assert_nvfp4_equal(q, ref)
+
+
+def test_nvfp4_worked_example_with_outer_hook(P):
+    x = np.zeros((1, 16), np.float32)
+    x[0, :5] = [-54.0, 5.4, 1.0, -2.0, 0.3]
+    q = P.nvfp4_quantize(bf16_np(x).to(DEV), P.NVFP4_WEIGHT, outer_in=torch.ones(1, device=DEV))
+    assert npy(q.scales)[0, 0] == 0x51
+    c = npy(q.codes)[0]
+    assert c[0] & 15 == 0xF and (c[0] >> 4) == 0x1        # -6 and 0.5
+
+
+def test_nvfp4_edge_values(P):
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    x[0] = 0.0                                  # all-zero row: outer 1, zero codes
+    x[1, :16] = 1e-38                           # tiny values
+    x[2, 16:32] = -0.0
+    x[3] *= 1e30                                # large values
+    x[4, ::16] = 3e38                           # bf16 near max
+    x[5, :] = 6.0
+    xb = bf16_np(x)
+    for four_six in (True, False):
+        q = P.nvfp4_quantize(xb.to(DEV), P.NVFP4_ACT if four_six else P.NVFP4_WEIGHT)
+        assert_nvfp4_equal(q, O.nvfp4_quantize(xb, 1, four_six))
+
+
+def test_nvfp4_empty(P):
+    q = P.nvfp4_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV))
+    assert q.codes.shape == (0, 32)
+
+
+def test_nvfp4_full_size_quantizer_workload_sampled_rows(P, I):
+    """8192 x 7168 Student-t(3) * 0.5, ACT mode with 4/6: sampled rows checked bit for bit."""
+    x = I.quantizer(DEV)["x"]
+    q = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    rows = np.sort(np.random.default_rng(5).choice(8192, 48, replace=False))
+    ref = O.nvfp4_quantize(x[torch.as_tensor(rows, device=DEV)].cpu(), 1, True)
+    assert_nvfp4_equal(q, ref, rows=rows)
+    assert np.array_equal(npy(q.outer)[rows], ref["outer"])
+    # the same call twice gives the same bits
+    q2 = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    assert torch.equal(q.codes, q2.codes) and torch.equal(q.scales, q2.scales)
+
+
+# ------------------------------------------------------------------------------------------
+# Requantization (dequant -> transpose -> SR) and MXFP8 gradients
+# ------------------------------------------------------------------------------------------
+
+def _ref_q(q):
+    return dict(codes=npy(q.codes), scales=npy(q.scales), outer=npy(q.outer), rows_per_outer=q.rows_per_outer)
+
+
+@pytest.mark.parametrize("rows,cols", [(256, 512), (97, 4096), (64, 16), (1, 32)])
+def test_requant_ungrouped(P, I, rows, cols):
+    x = I.student_t((rows, cols), 3, 0.5, 21)
+    q = P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT)
+    out, oe, po = P.requant_transpose_sr_mxfp8(q, seed=7, rng_stream=3, want_padded_offsets=True)
+    ro, roe = O.requant_transpose_sr(_ref_q(q), seed=7, stream=3)
+    Pt = ro.shape[1]
+    assert np.array_equal(npy(out)[:, :Pt], ro) and np.array_equal(npy(oe)[:, :Pt // 32], roe)
+    assert list(npy(po)) == [0, Pt]
+
+
+def test_requant_grouped_gathered_ragged(P, I):
+    rng = np.random.default_rng(22)
+    x = I.student_t((300, 1536), 4, 1.0, 23)
+    q = P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT)
+    counts = [37, 0, 300, 1, 64, 298]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    gather = rng.integers(0, 300, offsets[-1]).astype(np.int32)
+    out, oe, po = P.requant_transpose_sr_mxfp8(q, gather=torch.as_tensor(gather, device=DEV),
+                                               offsets=torch.as_tensor(offsets, device=DEV), seed=11,
+                                               rng_stream=5, want_padded_offsets=True)
+    ro, roe = O.requant_transpose_sr(_ref_q(q), gather=gather, offsets=offsets, seed=11, stream=5)
+    Pt = ro.shape[1]
+    assert np.array_equal(npy(out)[:, :Pt], ro) and np.array_equal(npy(oe)[:, :Pt // 32], roe)
+    assert list(npy(po)) == list(np.concatenate([[0], np.cumsum([(c + 31) // 32 * 32 for c in counts])]))
+
+
+def test_requant_weights(P, I):
+    w = I.normal((3 * 256, 512), 0.02, 24)
+    q = P.nvfp4_quantize(w.to(DEV), P.NVFP4_WEIGHT, rows_per_outer=256)
+    out, oe, _ = P.requant_transpose_sr_mxfp8(q, seed=2, rng_stream=1, ld=768)
+    ro, roe = O.requant_transpose_sr(_ref_q(q), seed=2, stream=1)
+    assert np.array_equal(npy(out), ro) and np.array_equal(npy(oe), roe)
+
+
+def test_requant_e2m1_worked_example(P):
+    rows = 64
+    x = np.zeros((rows, 16), np.float32)
+    x[:, 0] = -54.0
+    x[:, 1] = 5.4
+    x[3, 1] = 9.0
+    q = P.nvfp4_quantize(bf16_np(x).to(DEV), P.NVFP4_WEIGHT, outer_in=torch.ones(rows, device=DEV))
+    out, oe, _ = P.requant_transpose_sr_mxfp8(q, target=P.TARGET_E2M1, seed=5, rng_stream=3)
+    ro, roe = O.requant_transpose_sr(_ref_q(q), target=O.TARGET_E2M1, seed=5, stream=3)
+    assert np.array_equal(npy(out)[:, :64], ro) and np.array_equal(npy(oe)[:, :2], roe)
+    # column 1, block 0 has max 9 -> E8M0 scale 2; every 4.5 (rows other than 3) became 2 or 3
+    assert npy(oe)[1, 0] == 128
+    vals = {O.fp4_value(int(c)) for j, c in enumerate(npy(out)[1, :32]) if j != 3}
+    assert vals <= {2.0, 3.0}
+
+
+def test_requant_full_size_windows_and_unbiased(P, I):
+    """Requant of the 8192 x 7168 quantizer workload (seed 1, stream 0): windows of 32-slot
+    blocks bit for bit, and the SR mean over the whole tensor unbiased against the dequantized
+    forward values."""
+    data = I.quantizer(DEV)
+    q = P.nvfp4_quantize(data["x"], P.NVFP4_ACT)
+    out, oe, _ = P.requant_transpose_sr_mxfp8(q, seed=data["seed"], rng_stream=data["stream"])
+    ref_q = _ref_q(q)
+    for s0 in (0, 4096, 8160):
+        ro, roe = O.requant_window(ref_q, s0, 32, seed=data["seed"], stream=data["stream"])
+        assert np.array_equal(npy(out[:, s0:s0 + 32]), ro)
+        assert np.array_equal(npy(oe[:, s0 // 32:s0 // 32 + 1]), roe)
+    # unbiasedness on sampled columns: the mean of (requant - forward value) over many
+    # elements is within a few standard errors of zero
+    cols = torch.arange(0, 7168, 97, device=DEV)
+    e4 = torch.tensor([O.e4m3_value(c) if (c & 0x7F) != 0x7F else 0.0 for c in range(256)], dtype=torch.float64,
+                      device=DEV)
+    got = e4[out[cols].long()] * torch.pow(2.0, oe[cols].double() - 127).repeat_interleave(32, dim=1)
+    deq = torch.from_numpy(O.nvfp4_dequantize(dict(codes=ref_q["codes"][:, :], scales=ref_q["scales"],
+                                                   outer=ref_q["outer"], rows_per_outer=1))).to(DEV).double()
+    fwd = deq[:, cols].t()
+    d = (got[:, :8192] - fwd)
+    spacing = torch.pow(2.0, torch.floor(torch.log2(fwd.abs().clamp_min(1e-30))) - 3)
+    z = d.sum() / torch.sqrt((spacing ** 2 / 4).sum())
+    assert abs(z.item()) < 5
+
+
+@pytest.mark.parametrize("sr", [False, True])
+def test_mxfp8_quantize_rows_and_cols(P, I, sr):
+    dy = I.normal((600, 512), 1e-3, 31)
+    rnd = P.SR if sr else P.RNE
+    q, e, _ = P.mxfp8_quantize(dy.to(DEV), P.ROWWISE, rounding=rnd, seed=3, rng_stream=9)
+    rq, re = O.mxfp8_quantize_rows(dy, sr=sr, seed=3, stream=9)
+    assert np.array_equal(npy(q), rq) and np.array_equal(npy(e), re)
+    offsets = np.array([0, 100, 100, 433, 600], np.int64)
+    t, te, _ = P.mxfp8_quantize(dy.to(DEV), P.COLWISE, offsets=torch.as_tensor(offsets, device=DEV), rounding=rnd,
+                                seed=3, rng_stream=9)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=offsets, sr=sr, seed=3, stream=9)
+    Pt = rt.shape[1]
+    assert np.array_equal(npy(t)[:, :Pt], rt) and np.array_equal(npy(te)[:, :Pt // 32], rte)
+
+
+# ------------------------------------------------------------------------------------------
+# RHT32 + S2F6
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rht32_s2f6(P, I, dtype):
+    x = I.student_t((333, 1024), 3, 1.0, 41).to(dtype)
+    x[0, :32] = 0
+    mask = I.sign_mask(3)
+    c, e = P.rht32_s2f6_quantize(x.to(DEV), mask)
+    rc, re = O.rht32_s2f6_quantize(x.float().numpy(), mask)
+    assert np.array_equal(npy(c), rc) and np.array_equal(npy(e), re)
+    xh = O.rht32_s2f6_decode(npy(c), npy(e), mask)
+    assert rel_fro(xh, x.float().numpy()) < 0.02
+
+
+# ------------------------------------------------------------------------------------------
+# Grouped GEMMs
+# ------------------------------------------------------------------------------------------
+
+def _moe_small(P, I, counts, N, K, gather_rows=None, seed=50):
+    rng = np.random.default_rng(seed)
+    G = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    M = int(offsets[-1])
+    T = gather_rows or M
+    x = I.student_t((T, K), 4, 1.0, seed + 1)
+    w = I.normal((G * N, K), 0.02, seed + 2)
+    gather = rng.integers(0, T, M).astype(np.int32) if gather_rows else None
+    xq = P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT)
+    wq = P.nvfp4_quantize(w.to(DEV), P.NVFP4_WEIGHT, rows_per_outer=N // 2 if N % 64 == 0 else N)
+    return dict(offsets=offsets, M=M, x=x, w=w, gather=gather, xq=xq, wq=wq,
+                goff=torch.as_tensor(offsets, device=DEV),
+                ggather=None if gather is None else torch.as_tensor(gather, device=DEV))
+
+
+@pytest.mark.parametrize("counts,N,K,gather_rows", [([300], 256, 192, None), ([10, 0, 300, 77], 512, 256, 200),
+                                                    ([256, 513], 256, 1024, 1000)])
+def test_gemm_fwd_f32_bf16(P, I, counts, N, K, gather_rows):
+    d = _moe_small(P, I, counts, N, K, gather_rows)
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_F32, gather=d["ggather"])
+    ref = O.gemm_nvfp4_grouped(_ref_q(d["xq"]), _ref_q(d["wq"]), d["offsets"], N, K, gather=d["gather"])
+    assert rel_fro(npy(y), ref) <= 2e-3
+    assert rel_fro(npy(y), ref) <= 1e-5          # exact products, fp32 accumulation
+    yb = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_BF16, gather=d["ggather"])
+    assert torch.equal(yb, y.to(torch.bfloat16))
+
+
+def test_gemm_fwd_swiglu(P, I):
+    counts, F, K = [130, 0, 301], 128, 256
+    d = _moe_small(P, I, counts, 2 * F, K, gather_rows=250, seed=60)
+    a, h13 = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], 2 * F, P.EPI_SWIGLU, gather=d["ggather"],
+                                    save_h13=True)
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], 2 * F, P.EPI_F32, gather=d["ggather"])
+    ref = O.gemm_nvfp4_grouped(_ref_q(d["xq"]), _ref_q(d["wq"]), d["offsets"], 2 * F, K, gather=d["gather"])
+    aref = O.swiglu(ref, F)
+    assert rel_fro(npy(a.float()), aref) <= 2e-3
+    assert torch.equal(h13, y.to(torch.bfloat16))
+
+
+def test_gemm_fwd_rht_epilogue_bit_exact(P, I):
+    counts, N, K = [70, 256, 3], 512, 192
+    d = _moe_small(P, I, counts, N, K, gather_rows=120, seed=70)
+    mask = I.sign_mask(3)
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_F32, gather=d["ggather"])
+    c, e = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_RHT32_S2F6, gather=d["ggather"],
+                                  rht_sign_mask=mask)
+    rc, re = O.rht32_s2f6_quantize(npy(y), mask)
+    assert np.array_equal(npy(c), rc) and np.array_equal(npy(e), re)
+    ref = O.gemm_nvfp4_grouped(_ref_q(d["xq"]), _ref_q(d["wq"]), d["offsets"], N, K, gather=d["gather"])
+    assert rel_fro(O.rht32_s2f6_decode(npy(c), npy(e), mask), ref) < 0.02
+
+
+def test_gemm_bwd_intermediates_and_gradients(P, I):
+    counts, N, K = [40, 0, 333, 227], 256, 512
+    d = _moe_small(P, I, counts, N, K, gather_rows=400, seed=80)
+    M, G = d["M"], len(counts)
+    dy = I.normal((M, N), 1e-3, 81)
+    da, db, ws = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
+                                        seed=9, rng_stream_a=4, rng_stream_b=1, rng_stream_dy=6)
+    v = P.bwd_workspace_views(ws, M, G, N, K)
+    rq, re = O.mxfp8_quantize_rows(dy)
+    assert np.array_equal(npy(v["dq"]), rq) and np.array_equal(npy(v["de"]), re)
+    rwt, rwte = O.requant_transpose_sr(_ref_q(d["wq"]), seed=9, stream=1)
+    assert np.array_equal(npy(v["wt"]), rwt) and np.array_equal(npy(v["wte"]), rwte)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], stream=7)
+    Pt = rt.shape[1]
+    assert np.array_equal(npy(v["dt"])[:, :Pt], rt) and np.array_equal(npy(v["dte"])[:, :Pt // 32], rte)
+    rxt, rxte = O.requant_transpose_sr(_ref_q(d["xq"]), gather=d["gather"], offsets=d["offsets"], seed=9, stream=4)
+    assert np.array_equal(npy(v["xt"])[:, :Pt], rxt) and np.array_equal(npy(v["xte"])[:, :Pt // 32], rxte)
+    da_ref = O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K)
+    db_ref = O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K)
+    assert rel_fro(npy(da), da_ref) <= 2e-3
+    assert rel_fro(npy(db), db_ref) <= 2e-3
+    assert np.all(npy(db)[N:2 * N] == 0)          # the empty expert gets a zero gradient
+
+
+def test_gemm_bwd_sr_gradients_deterministic(P, I):
+    counts, N, K = [200, 56], 256, 256
+    d = _moe_small(P, I, counts, N, K, seed=90)
+    dy = I.normal((d["M"], N), 1e-3, 91).to(DEV)
+    a1 = P.moe_grouped_gemm_bwd(dy, d["xq"], d["wq"], d["goff"], d["M"], N, dy_rounding=P.SR, seed=3)
+    a2 = P.moe_grouped_gemm_bwd(dy, d["xq"], d["wq"], d["goff"], d["M"], N, dy_rounding=P.SR, seed=3)
+    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+
+
+def test_swiglu_bwd(P, I):
+    M, F = 300, 256
+    da = I.normal((M, F), 1.0, 95, dtype=torch.float32)
+    h13 = I.normal((M, 2 * F), 2.0, 96)
+    g = P.swiglu_bwd(da.to(DEV), h13.to(DEV))
+    ref = O.swiglu_bwd(da.numpy(), h13, F)
+    assert rel_fro(npy(g.float()), ref) <= 2e-3
+
+
+# ------------------------------------------------------------------------------------------
+# Routing
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k", [(1000, 32, 8), (257, 48, 8), (3, 8, 8), (50, 384, 8)])
+def test_route_topk(P, I, T, E, k):
+    logits = torch.randn((T, E), generator=torch.Generator().manual_seed(T + E), dtype=torch.float32)
+    r = P.moe_route_topk(logits.to(DEV), k)
+    ref = O.route_topk(logits.numpy(), k)
+    for key in ("ids", "offsets", "gather", "slot_of"):
+        assert np.array_equal(npy(r[key]), ref[key]), key
+    assert np.allclose(npy(r["gates"]), ref["gates"], rtol=1e-5, atol=1e-7)

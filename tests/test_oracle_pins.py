@@ -628,3 +628,13 @@ def test_philox_vs_rocrand_header(tmp_path):
     for row, line in zip(vecs, out):
         want = O.philox4x32_10(row[:4], row[4:])
         assert line == " ".join(f"{int(w):08x}" for w in want)
+
+
+def test_requant_window_matches_full_output():
+    rng = np.random.default_rng(20)
+    q = O.nvfp4_quantize(bf16(rng.standard_t(3, size=(200, 64))), four_six=True)
+    full, fe = O.requant_transpose_sr(q, seed=4, stream=2)
+    w, we = O.requant_window(q, 64, 96, seed=4, stream=2)
+    assert np.array_equal(w, full[:, 64:160]) and np.array_equal(we, fe[:, 2:5])
+    tail, te = O.requant_window(q, 192, 8, seed=4, stream=2)
+    assert np.array_equal(tail, full[:, 192:224]) and np.array_equal(te, fe[:, 6:7])
