@@ -1,0 +1,313 @@
+"""Benchmark of the quantized MoE expert layer on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input, by default the
+one-GPU expert share (48 local experts, 65536 routed slots with Zipf(1.1) loads, hidden 7168,
+FFN 2048, SwiGLU):
+  weights:  NVFP4 quantization of w13 and w2 (one outer scale per expert and matrix)
+  forward:  NVFP4 quantization of X (per-token outer scale, 4/6) -> grouped GEMM w13 with the
+            SwiGLU epilogue (h13 saved) -> NVFP4 quantization of A -> grouped GEMM w2 with the
+            fused RHT32 + S2F6 epilogue (the combine payload)
+  backward: w2 backward (dY MXFP8 row/column quantization, SR requantization of W2^T and A^T,
+            MXFP8 dgrad and wgrad) -> SwiGLU backward -> w13 backward (same steps with X^T, W13^T)
+Inputs are generated on the GPU from fixed seeds before the timed region and stay resident in
+HBM. Per-call device time comes from HIP events on the stream the kernels run on.
+
+Also reported: the memory-bound quantizer workload (8192 x 7168 activations, 0.5 * StudentT(3)):
+nvfp4_quantize with 4/6 and requant_transpose_sr_mxfp8 of its output, each timed over rotating
+input buffers larger than the 256 MB Infinity Cache, as GB/s of algorithmic bytes.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ep48|moe32]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4/MXFP8-SR quantize GB/s + MoE grouped GEMM TFLOPS, % of MI355X roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
+PEAK_F16_TFLOPS = 2500.0       # MI355X dense MFMA fp16/bf16
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense MFMA fp8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ep48", choices=["ep48", "moe32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--quant-iters", type=int, default=20)
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events around each ABI call on torch's current stream (the calls' stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.events = []
+
+    def run(self, name, fn, *a, **k):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn(*a, **k)
+        e1.record()
+        self.events.append((name, e0, e1))
+        return r
+
+    def collect(self):
+        out = {}
+        for name, e0, e1 in self.events:
+            ms = e0.elapsed_time(e1)
+            s = out.setdefault(name, [0.0, 0])
+            s[0] += ms
+            s[1] += 1
+        self.events = []
+        return {k: v[0] / v[1] for k, v in out.items()}
+
+
+class Layer:
+    def __init__(self, P, I, torch, shape, dev):
+        self.P, self.torch = P, torch
+        self.shape = shape
+        E, H, F = shape.experts, shape.hidden, shape.ffn
+        self.E, self.H, self.F = E, H, F
+        if shape.tokens:        # routed workload: route on the device, activations gathered
+            logits = I.moe_logits(shape, dev)
+            r = P.moe_route_topk(logits, shape.top_k)
+            torch.cuda.synchronize()
+            self.offsets = r["offsets"]
+            self.gather = r["gather"]
+            self.M = shape.tokens * shape.top_k
+            self.x = I.moe_activations(shape, dev)
+        else:
+            counts = I.moe_loads(shape)
+            self.offsets = I.offsets_from_counts(counts, dev)
+            self.gather = None
+            self.M = sum(counts)
+            self.x = I.moe_activations(shape, dev)
+        w13, w2 = I.moe_weights(shape, dev)
+        self.w13 = w13.view(E * 2 * F, H)
+        self.w2 = w2.view(E * H, F)
+        self.dy = I.moe_grad(shape, self.M, dev)
+        self.mask = I.sign_mask(shape.seeds["rht"])
+        self.seed = shape.seeds["sr"]
+        M = self.M
+        self.ws13 = torch.empty(P.moe_grouped_gemm_bwd_workspace_size(M, E, 2 * F, H, 3), dtype=torch.uint8, device=dev)
+        self.ws2 = torch.empty(P.moe_grouped_gemm_bwd_workspace_size(M, E, H, F, 3), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def flops(self):
+        M, H, F = self.M, self.H, self.F
+        fwd13 = 2.0 * M * 2 * F * H
+        fwd2 = 2.0 * M * H * F
+        return dict(fwd13=fwd13, fwd2=fwd2, fwd=fwd13 + fwd2, bwd=2 * (fwd13 + fwd2), step=3 * (fwd13 + fwd2))
+
+    def step(self, T):
+        P = self.P
+        E, H, F, M = self.E, self.H, self.F, self.M
+        w13q = T.run("nvfp4_quantize[w13]", P.nvfp4_quantize, self.w13, P.NVFP4_WEIGHT, F)
+        w2q = T.run("nvfp4_quantize[w2]", P.nvfp4_quantize, self.w2, P.NVFP4_WEIGHT, H)
+        xq = T.run("nvfp4_quantize[x]", P.nvfp4_quantize, self.x, P.NVFP4_ACT)
+        a, h13 = T.run("moe_grouped_gemm_fwd[w13+swiglu]", P.moe_grouped_gemm_fwd, xq, w13q, self.offsets, M, 2 * F,
+                       P.EPI_SWIGLU, gather=self.gather, save_h13=True)
+        aq = T.run("nvfp4_quantize[a]", P.nvfp4_quantize, a, P.NVFP4_ACT)
+        yc, ye = T.run("moe_grouped_gemm_fwd[w2+rht32_s2f6]", P.moe_grouped_gemm_fwd, aq, w2q, self.offsets, M, H,
+                       P.EPI_RHT32_S2F6, rht_sign_mask=self.mask)
+        da, dw2, _ = T.run("moe_grouped_gemm_bwd[w2]", P.moe_grouped_gemm_bwd, self.dy, aq, w2q, self.offsets, M, H,
+                           seed=self.seed, rng_stream_a=5, rng_stream_b=3, rng_stream_dy=6, workspace=self.ws2)
+        dh13 = T.run("swiglu_bwd", P.swiglu_bwd, da, h13)
+        dx, dw13, _ = T.run("moe_grouped_gemm_bwd[w13]", P.moe_grouped_gemm_bwd, dh13, xq, w13q, self.offsets, M,
+                            2 * F, gather=self.gather, seed=self.seed, rng_stream_a=4, rng_stream_b=1,
+                            rng_stream_dy=8, workspace=self.ws13)
+        return yc, dx, dw13, dw2
+
+
+def quantizer_workload(P, I, torch, dev, iters):
+    """GB/s of nvfp4_quantize (4/6, per-token outer) and requant_transpose_sr_mxfp8 on the
+    8192 x 7168 activation workload, rotating inputs so the Infinity Cache cannot serve them."""
+    R, Cc = 8192, 7168
+    base = I.quantizer(dev)
+    nbuf = 4
+    xs = [base["x"]] + [base["x"].roll(shifts=97 * i, dims=1).contiguous() for i in range(1, nbuf)]
+    qs = [P.nvfp4_quantize(x, P.NVFP4_ACT) for x in xs]
+    nq = 12
+    qs = [qs[i % nbuf] for i in range(nq)]
+    qbuf = []
+    for i in range(nq):     # distinct copies of the quantized tensors (> 256 MB in total)
+        q = qs[i]
+        qbuf.append(P.NVFP4(q.codes.clone(), q.scales.clone(), q.outer.clone(), q.rows_per_outer))
+    ld = P.padded_bound(R, 0)
+    out = torch.empty((Cc, ld), dtype=torch.uint8, device=dev)
+    oe = torch.empty((Cc, ld // 32), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    res = {}
+    # nvfp4_quantize
+    for i in range(3):
+        P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = R * Cc * (2 + 0.5 + 1 / 16) + R * 4
+    res["nvfp4_quantize"] = dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+    # requant
+    def rq(q):
+        P.requant_transpose_sr_mxfp8(q, seed=base["seed"], rng_stream=base["stream"], ld=ld, out=out, out_e8m0=oe)
+
+    for i in range(3):
+        rq(qbuf[i])
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        rq(qbuf[i % nq])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    nbytes = R * Cc * (0.5 + 1 / 16 + 1 + 1 / 32) + R * 4
+    res["requant_transpose_sr_mxfp8"] = dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
+    # measured copy bandwidth (device-to-device copy of 1 GiB, read + write)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    res["hbm_copy_gbs"] = 2 * (1 << 30) / (ms * 1e-3) / 1e9
+    del src, dst
+    return res
+
+
+def cpu_baseline(I, shape):
+    """The CPU oracle (as it stands) on a bounded sample of the same step: 32 slots of one expert
+    through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
+    import numpy as np
+    import torch
+
+    import oracle as O
+    S, H, F = 32, shape.hidden, shape.ffn
+    x = I.moe_activations(shape, "cpu", rows=S)
+    w13 = I.normal((2 * F, H), 0.02, shape.seeds["w"])
+    w2 = I.normal((H, F), 0.02, shape.seeds["w"] + 1000)
+    dy = I.moe_grad(shape, S, "cpu")
+    mask = I.sign_mask(shape.seeds["rht"])
+    off = [0, S]
+    t0 = time.perf_counter()
+    xq = O.nvfp4_quantize(x, 1, True)
+    w13q = O.nvfp4_quantize(w13, F, False)
+    w2q = O.nvfp4_quantize(w2, H, False)
+    h13 = O.gemm_nvfp4_grouped(xq, w13q, off, 2 * F, H)
+    a = torch.from_numpy(O.swiglu(h13, F)).to(torch.bfloat16)
+    aq = O.nvfp4_quantize(a, 1, True)
+    y = O.gemm_nvfp4_grouped(aq, w2q, off, H, F)
+    O.rht32_s2f6_quantize(y, mask)
+    dq, de = O.mxfp8_quantize_rows(dy)
+    w2t, w2te = O.requant_transpose_sr(w2q, seed=5, stream=3)
+    da = O.gemm_mxfp8_dgrad(dq, de, w2t, w2te, off, H, F)
+    dt, dte = O.mxfp8_quantize_cols(dy, offsets=off)
+    at, ate = O.requant_transpose_sr(aq, offsets=off, seed=5, stream=5)
+    O.gemm_mxfp8_wgrad(dt, dte, at, ate, off, H, F)
+    h13b = torch.from_numpy(h13).to(torch.bfloat16)
+    dh = torch.from_numpy(O.swiglu_bwd(da, h13b, F)).to(torch.bfloat16)
+    gq, ge = O.mxfp8_quantize_rows(dh)
+    w13t, w13te = O.requant_transpose_sr(w13q, seed=5, stream=1)
+    O.gemm_mxfp8_dgrad(gq, ge, w13t, w13te, off, 2 * F, H)
+    gt, gte = O.mxfp8_quantize_cols(dh, offsets=off)
+    xt, xte = O.requant_transpose_sr(xq, offsets=off, seed=5, stream=4)
+    O.gemm_mxfp8_wgrad(gt, gte, xt, xte, off, 2 * F, H)
+    dt_s = time.perf_counter() - t0
+    flops = 3 * 2.0 * S * (2 * F * H + H * F)
+    return dict(value=flops / dt_s / 1e12, unit="TFLOP/s", cores=O.threads(), kind="oracle", seconds=dt_s,
+                sample=f"{S} routed slots of one expert through the whole layer (NVFP4 quantize of X, w13, w2; "
+                       f"w13 GEMM + SwiGLU; A quantize; w2 GEMM; RHT32+S2F6; MXFP8 dY quantize; SR requant of "
+                       f"W2^T, A^T, W13^T, X^T; dgrad and wgrad of both GEMMs), H={H}, F={F}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    import precision_moe_numerics_amd as P
+    from precision_moe_numerics_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    shape = I.EP48 if args.workload == "ep48" else I.MOE32
+    layer = Layer(P, I, torch, shape, dev)
+    T = Timer(torch)
+    for _ in range(args.warmup):
+        layer.step(T)
+    torch.cuda.synchronize()
+    T.collect()
+    t0 = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        layer.step(T)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = T.collect()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    fl = layer.flops()
+    value = fl["step"] / (ms_step * 1e-3) / 1e12
+
+    k13 = per_call["moe_grouped_gemm_fwd[w13+swiglu]"]
+    k2 = per_call["moe_grouped_gemm_fwd[w2+rht32_s2f6]"]
+    ach = fl["fwd13"] / (k13 * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": "k_nvfp4_grouped_gemm<SWIGLU> (w13 forward, fp16 MFMA after exact "
+                                           "NVFP4 dequant)",
+                "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_F16_TFLOPS,
+                "traffic": None, "flops_per_launch": fl["fwd13"], "ms_per_launch": k13}
+    kernels = {name: {"ms": ms} for name, ms in per_call.items()}
+    kernels["moe_grouped_gemm_fwd[w13+swiglu]"].update(tflops=ach, frac_f16_peak=ach / PEAK_F16_TFLOPS)
+    a2 = fl["fwd2"] / (k2 * 1e-3) / 1e12
+    kernels["moe_grouped_gemm_fwd[w2+rht32_s2f6]"].update(tflops=a2, frac_f16_peak=a2 / PEAK_F16_TFLOPS)
+    for nm, f in (("moe_grouped_gemm_bwd[w2]", 2 * fl["fwd2"]), ("moe_grouped_gemm_bwd[w13]", 2 * fl["fwd13"])):
+        t = f / (per_call[nm] * 1e-3) / 1e12
+        kernels[nm].update(tflops_incl_quant=t, frac_fp8_peak=t / PEAK_FP8_TFLOPS)
+
+    quant = quantizer_workload(P, I, torch, dev, args.quant_iters)
+    for k in ("nvfp4_quantize", "requant_transpose_sr_mxfp8"):
+        quant[k]["frac_of_8TBs"] = quant[k]["gbs"] / PEAK_HBM_GBS
+        quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(I, shape)
+
+    cfg = {"workload": (f"{shape.name}: {shape.experts} local experts, {layer.M} routed slots"
+                        + (f" (top-{shape.top_k} of {shape.tokens} tokens)" if shape.tokens else
+                           f" with Zipf({shape.zipf_s}) loads")
+                        + f", hidden {shape.hidden}, FFN {shape.ffn}, SwiGLU, forward + backward"),
+           "experts": shape.experts, "slots": layer.M, "hidden": shape.hidden, "ffn": shape.ffn,
+           "step_tflop": fl["step"] / 1e12}
+    line = {"metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
+            "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
+            "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant,
+            "wall_s_timed": wall}
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -127,16 +127,18 @@ def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int =
 def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
                                offsets: Optional[torch.Tensor] = None, M: Optional[int] = None,
                                target: int = TARGET_E4M3, seed: int = 0, rng_stream: int = 0,
-                               ld: Optional[int] = None, want_padded_offsets: bool = False):
-    """Returns (out [cols, ld] u8, out_e8m0 [cols, ld/32] u8, padded_offsets or None)."""
+                               ld: Optional[int] = None, want_padded_offsets: bool = False,
+                               out: Optional[torch.Tensor] = None, out_e8m0: Optional[torch.Tensor] = None):
+    """Returns (out [cols, ld] u8, out_e8m0 [cols, ld/32] u8, padded_offsets or None); columns
+    past the padded total are not written."""
     if M is None:
         M = gather.numel() if gather is not None else q.rows
     G = 0 if offsets is None else offsets.numel() - 1
     if ld is None:
         ld = padded_bound(M, G)
     dev = q.codes.device
-    out = torch.zeros((q.cols, ld), dtype=torch.uint8, device=dev)
-    oe = torch.zeros((q.cols, ld // 32), dtype=torch.uint8, device=dev)
+    out = torch.empty((q.cols, ld), dtype=torch.uint8, device=dev) if out is None else out
+    oe = torch.empty((q.cols, ld // 32), dtype=torch.uint8, device=dev) if out_e8m0 is None else out_e8m0
     po = torch.zeros((max(G, 1) + 1,), dtype=torch.int64, device=dev) if want_padded_offsets else None
     _check(_lib.requant_transpose_sr_mxfp8(_ptr(q.codes), _ptr(q.scales), _ptr(q.outer), q.rows, q.cols,
                                            q.rows_per_outer, _ptr(gather), M, _ptr(offsets), G, target, seed,
@@ -160,8 +162,8 @@ def mxfp8_quantize(x: torch.Tensor, layout: int = ROWWISE, offsets: Optional[tor
     else:
         if ld is None:
             ld = padded_bound(M, G)
-        out = torch.zeros((N, ld), dtype=torch.uint8, device=dev)
-        oe = torch.zeros((N, ld // 32), dtype=torch.uint8, device=dev)
+        out = torch.empty((N, ld), dtype=torch.uint8, device=dev)
+        oe = torch.empty((N, ld // 32), dtype=torch.uint8, device=dev)
         po = torch.zeros((max(G, 1) + 1,), dtype=torch.int64, device=dev) if want_padded_offsets else None
     _check(_lib.mxfp8_quantize(_ptr(x), M, N, layout, _ptr(offsets), G, rounding, seed, rng_stream, _ptr(out),
                                _ptr(oe), ld, _ptr(po), _stream()), "mxfp8_quantize")

@@ -101,47 +101,59 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
         obase = p.out + (int64_t)g * p.Nf * p.Kf;
     }
 
-    // staging rows of this thread
-    const bool arow_ok = tid < rvalid;
-    const uint8_t* ap = abase + (arow_ok ? (r0 + tid) : 0) * p.lda;
-    const uint8_t* aep = aebase + (arow_ok ? (r0 + tid) : 0) * (p.lda / 32);
-    const uint8_t* bp = bbase + (c0 + tid) * p.ldb;
+    // Staging: per stage each operand tile is 256 rows x 128 bytes = 2048 chunks of 16 bytes;
+    // thread t stages chunks q = 256 k + t (row q / 8, part q % 8), so 8 lanes cover one row and a
+    // wavefront reads 8 whole 128-byte row segments per instruction. Loads are branch-free: a
+    // chunk outside the tile reads a valid address and is replaced by zeros.
+    const int prow = tid >> 3, part = tid & 7;
+    const uint8_t* arow[8];
+    bool arow_ok[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int row = k * 32 + prow;
+        arow_ok[k] = row < rvalid;
+        arow[k] = abase + (r0 + (arow_ok[k] ? row : 0)) * p.lda + part * 16;
+    }
+    const uint8_t* brow0 = bbase + (c0 + prow) * p.ldb + part * 16;
+    const bool srow_ok = tid < rvalid;
+    const uint8_t* aep = aebase + (r0 + (srow_ok ? tid : 0)) * (p.lda / 32);
     const uint8_t* bep = bebase + (c0 + tid) * (p.ldb / 32);
+    const int64_t kblocks = klen / 32;
 
     uint4 av[8], bv[8];
     uint32_t as, bs;
     auto load_stage = [&](int kt) {
         const int64_t k0 = (int64_t)kt * BK;
-        const int64_t rem = klen - k0;            // bytes of this stage that exist (>= 32)
+        const bool kok = k0 + part * 16 < klen;
+        const int64_t koff = kok ? k0 : 0;
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            const bool ok = arow_ok && (q * 16 < rem);
-            av[q] = ok ? reinterpret_cast<const uint4*>(ap + k0)[q] : make_uint4(0u, 0u, 0u, 0u);
-            bv[q] = (q * 16 < rem) ? reinterpret_cast<const uint4*>(bp + k0)[q] : make_uint4(0u, 0u, 0u, 0u);
+        for (int k = 0; k < 8; k++) {
+            uint4 a = *reinterpret_cast<const uint4*>(arow[k] + koff);
+            uint4 b = *reinterpret_cast<const uint4*>(brow0 + (int64_t)k * 32 * p.ldb + koff);
+            const bool aok = kok && arow_ok[k];
+            av[k] = aok ? a : make_uint4(0u, 0u, 0u, 0u);
+            bv[k] = kok ? b : make_uint4(0u, 0u, 0u, 0u);
         }
-        // scale bytes (one per 32): missing blocks get 127 (2^0) with zero data
-        as = 0x7F7F7F7Fu;
-        bs = 0x7F7F7F7Fu;
         uint32_t sa = 0u, sbb = 0u;
 #pragma unroll
         for (int q = 0; q < 4; q++) {
-            const bool ok = q * 32 < rem;
-            uint32_t x = ok && arow_ok ? (uint32_t)aep[k0 / 32 + q] : 127u;
-            uint32_t y = ok ? (uint32_t)bep[k0 / 32 + q] : 127u;
-            sa |= x << (8 * q);
-            sbb |= y << (8 * q);
+            const int64_t kb = k0 / 32 + q;
+            const bool ok = kb < kblocks;
+            const int64_t ki = ok ? kb : 0;
+            const uint32_t x = aep[ki], y = bep[ki];
+            sa |= ((ok && srow_ok) ? x : 127u) << (8 * q);
+            sbb |= (ok ? y : 127u) << (8 * q);
         }
         as = sa;
         bs = sbb;
     };
     auto store_stage = [&](int buf) {
         uint8_t* base = lds + buf * STAGEB;
-        uint4* pa = reinterpret_cast<uint4*>(base + tid * ROWB);
-        uint4* pb = reinterpret_cast<uint4*>(base + TILEB + tid * ROWB);
 #pragma unroll
-        for (int q = 0; q < 8; q++) {
-            pa[q] = av[q];
-            pb[q] = bv[q];
+        for (int k = 0; k < 8; k++) {
+            const int row = k * 32 + prow;
+            *reinterpret_cast<uint4*>(base + row * ROWB + part * 16) = av[k];
+            *reinterpret_cast<uint4*>(base + TILEB + row * ROWB + part * 16) = bv[k];
         }
         reinterpret_cast<uint32_t*>(base + 2 * TILEB)[tid] = as;
         reinterpret_cast<uint32_t*>(base + 2 * TILEB + SCB)[tid] = bs;
@@ -196,6 +208,8 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
                 for (int j = 0; j < 4; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
         }
+        // keep the next stage's LDS writes (which wait for its global loads) after the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
         if (kt + 1 < KT) store_stage(buf ^ 1);
         __syncthreads();
     }

@@ -111,89 +111,150 @@ PMN_DEV void bf8(uint4 w, float (&v)[8])
     v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
 
+// Output tile of a workgroup: 512 output rows (source columns) x 128 padded slots (4 blocks),
+// assembled in LDS so that global stores write whole 128-byte row segments.
+// Rows are 128 bytes (8 chunks of 16); chunk p of row r sits at position p ^ ((r / 8) % 8), so
+// the transposed writes (lane l -> rows 8l .. 8l+7) and the row-wise reads both spread over the
+// LDS banks.
+constexpr int TQ_ROWS = 512;
+constexpr int TQ_RS = 128;
+
+PMN_DEV int tile_chunk(int row, int chunk) { return row * TQ_RS + ((chunk ^ ((row >> 3) & 7)) << 4); }
+
 // SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (nibble/byte).
 template <int SRC, int ROUND, int TARGET>
 __global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
 {
+    __shared__ __attribute__((aligned(16))) uint8_t tile[TQ_ROWS * TQ_RS];
+    __shared__ uint8_t tile_e[TQ_ROWS * 4];
+    __shared__ int block_live[4];
     const int lane = threadIdx.x & 63;
-    const int64_t pb = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wavefront-uniform
+    const int64_t pb = (int64_t)blockIdx.x * 4 + w;
     const int64_t cg = (int64_t)blockIdx.y * 64 + lane;   // column group of 8
     const int64_t c0 = cg * 8;
-    GroupBlock blk = find_block(pb, a.offsets, a.G, a.M);
-    if (!blk.live || c0 >= a.cols) return;
+    const GroupBlock blk = find_block(pb, a.offsets, a.G, a.M);
+    if (lane == 0) block_live[w] = blk.live ? 1 : 0;
+    const bool active = blk.live && c0 < a.cols;
+    // lane j (mod 32) fetches slot j's source row and outer scale with one vector load each;
+    // readlane later hands every slot's values to the whole wavefront, so every lane of a live
+    // block computes them, whatever its columns
+    const int last = blk.valid - 1;
+    int rl = 0;
+    float ol = 0.0f;
+    if (SRC == SRC_NVFP4 && blk.live) {
+        const int jl = lane & 31;
+        const int64_t sl = blk.s0 + (jl < last ? jl : last);
+        rl = a.gather ? a.gather[sl] : (int)sl;
+        ol = a.outer[rl / a.rows_per_outer];
+    }
 
-    // ---- pass 1: load the 32 slots of this column group, per-column amax
-    uint32_t cw[32];      // NVFP4: code words; BF16: unused
-    float dsc[32];        // NVFP4: effective block scale per slot
-    uint4 xw[32];         // BF16: raw values
-    float amax[8];
+    if (active) {
+        // ---- pass 1: every load of the 32 slots is issued before any is used (slots past the
+        // group's end re-read its last slot and get a zero scale), then per-column amax
+        uint32_t cw[32];      // NVFP4: code words
+        float dsc[32];        // NVFP4: effective block scale per slot
+        uint4 xw[32];         // BF16: raw values
+        if (SRC == SRC_NVFP4) {
+            uint32_t sbyte[32];
+            float so[32];
 #pragma unroll
-    for (int c = 0; c < 8; c++) amax[c] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 32; j++) {
-        float v[8];
-        if (j < blk.valid) {
-            const int64_t s = blk.s0 + j;
-            if (SRC == SRC_NVFP4) {
-                const int64_t r = a.gather ? (int64_t)a.gather[s] : s;
+            for (int j = 0; j < 32; j++) {
+                const int64_t r = __builtin_amdgcn_readlane(rl, j);
+                so[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ol), j));
                 cw[j] = *reinterpret_cast<const uint32_t*>(a.codes + ((r * a.cols + c0) >> 1));
-                float sb = e4m3_value(a.scales[(r * a.cols + c0) >> 4]);
-                dsc[j] = sb * a.outer[r / a.rows_per_outer];
-                deq8(cw[j], dsc[j], v);
-            } else {
-                xw[j] = *reinterpret_cast<const uint4*>(a.x + s * a.cols + c0);
-                bf8(xw[j], v);
+                sbyte[j] = a.scales[(r * a.cols + c0) >> 4];
             }
+#pragma unroll
+            for (int j = 0; j < 32; j++) dsc[j] = j <= last ? e4m3_value(sbyte[j]) * so[j] : 0.0f;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 32; j++) {
+                const uint4 v = *reinterpret_cast<const uint4*>(a.x + (blk.s0 + (j < last ? j : last)) * a.cols + c0);
+                xw[j] = j <= last ? v : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        float amax[8];
+#pragma unroll
+        for (int c = 0; c < 8; c++) amax[c] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            float v[8];
+            if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
+            else bf8(xw[j], v);
 #pragma unroll
             for (int c = 0; c < 8; c++) amax[c] = fmaxf(amax[c], fabsf(v[c]));
-        } else {
-            if (SRC == SRC_NVFP4) { cw[j] = 0u; dsc[j] = 0.0f; }
-            else xw[j] = make_uint4(0u, 0u, 0u, 0u);
         }
-    }
-    int e[8];
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-        e[c] = TARGET == 0 ? e8m0_exponent<E8M0_E4M3>(amax[c]) : e8m0_exponent<E8M0_E2M1>(amax[c]);
-        a.out_e8m0[(c0 + c) * (a.ld >> 5) + pb] = (uint8_t)(e[c] + 127);
-    }
-
-    // ---- pass 2: convert, 16 slots at a time (4 words per column), write 16 bytes per column
-#pragma unroll
-    for (int half = 0; half < 2; half++) {
-        uint32_t o[8][4];
-#pragma unroll
-        for (int c = 0; c < 8; c++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) o[c][q] = 0u;
-#pragma unroll
-        for (int jj = 0; jj < 16; jj++) {
-            const int j = half * 16 + jj;
-            if (j < blk.valid) {
-                const int64_t s = blk.s0 + j;
-                float v[8];
-                if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
-                else bf8(xw[j], v);
-                uint32_t rw[4] = {0u, 0u, 0u, 0u};
-                if (ROUND == 1) rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
-#pragma unroll
-                for (int c = 0; c < 8; c++) {
-                    const float y = __builtin_ldexpf(v[c], -e[c]);
-                    uint32_t code;
-                    if (TARGET == 0) {
-                        code = ROUND == 1 ? e4m3_sr(y, sr_operand(rw[c >> 1], c & 1)) : e4m3_rne(y);
-                    } else {
-                        uint32_t word = rw[c >> 1];
-                        code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
-                    }
-                    o[c][jj >> 2] |= code << (8 * (jj & 3));
-                }
-            }
-        }
+        int e[8];
 #pragma unroll
         for (int c = 0; c < 8; c++) {
-            uint4* dst = reinterpret_cast<uint4*>(a.out + (c0 + c) * a.ld + pb * 32 + half * 16);
-            *dst = make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+            e[c] = TARGET == 0 ? e8m0_exponent<E8M0_E4M3>(amax[c]) : e8m0_exponent<E8M0_E2M1>(amax[c]);
+            tile_e[(lane * 8 + c) * 4 + w] = (uint8_t)(e[c] + 127);
+        }
+
+        // ---- pass 2: convert 16 slots at a time (4 words per column) into the LDS tile
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            uint32_t o[8][4];
+#pragma unroll
+            for (int c = 0; c < 8; c++)
+#pragma unroll
+                for (int q = 0; q < 4; q++) o[c][q] = 0u;
+#pragma unroll
+            for (int jj = 0; jj < 16; jj++) {
+                const int j = half * 16 + jj;
+                if (j < blk.valid) {
+                    const int64_t s = blk.s0 + j;
+                    float v[8];
+                    if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
+                    else bf8(xw[j], v);
+                    uint32_t rw[4] = {0u, 0u, 0u, 0u};
+                    if (ROUND == 1) rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+#pragma unroll
+                    for (int c = 0; c < 8; c++) {
+                        const float y = __builtin_ldexpf(v[c], -e[c]);
+                        uint32_t code;
+                        if (TARGET == 0) {
+                            code = ROUND == 1 ? e4m3_sr(y, sr_operand(rw[c >> 1], c & 1)) : e4m3_rne(y);
+                        } else {
+                            const uint32_t word = rw[c >> 1];
+                            code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
+                        }
+                        o[c][jj >> 2] |= code << (8 * (jj & 3));
+                    }
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 8; c++) {
+                const int row = lane * 8 + c;
+                *reinterpret_cast<uint4*>(tile + tile_chunk(row, w * 2 + half)) =
+                    make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- store: 512 rows x 8 chunks of 16 bytes; a chunk is written if its column exists and its
+    // 32-slot block lies inside the padded output.
+    const int64_t col_base = (int64_t)blockIdx.y * 512;
+#pragma unroll 4
+    for (int k = 0; k < 16; k++) {
+        const int q = k * 256 + threadIdx.x;
+        const int row = q >> 3, chunk = q & 7;
+        const int64_t col = col_base + row;
+        if (col < a.cols && block_live[chunk >> 1]) {
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, chunk));
+            *reinterpret_cast<uint4*>(a.out + col * a.ld + (int64_t)blockIdx.x * 128 + chunk * 16) = v;
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; k++) {
+        const int row = k * 256 + threadIdx.x;
+        const int64_t col = col_base + row;
+        if (col < a.cols) {
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                if (block_live[b]) a.out_e8m0[col * (a.ld >> 5) + (int64_t)blockIdx.x * 4 + b] = tile_e[row * 4 + b];
         }
     }
 }
