@@ -195,13 +195,13 @@ def quantizer_workload(P, I, torch, dev, iters):
 
 
 def cpu_baseline(I, shape):
-    """The CPU oracle (as it stands) on a bounded sample of the same step: 32 slots of one expert
+    """The CPU oracle (as it stands) on a bounded sample of the same step: 16 slots of one expert
     through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
     import numpy as np
     import torch
 
     import oracle as O
-    S, H, F = 32, shape.hidden, shape.ffn
+    S, H, F = 16, shape.hidden, shape.ffn
     x = I.moe_activations(shape, "cpu", rows=S)
     w13 = I.normal((2 * F, H), 0.02, shape.seeds["w"])
     w2 = I.normal((H, F), 0.02, shape.seeds["w"] + 1000)
@@ -237,6 +237,21 @@ def cpu_baseline(I, shape):
                 sample=f"{S} routed slots of one expert through the whole layer (NVFP4 quantize of X, w13, w2; "
                        f"w13 GEMM + SwiGLU; A quantize; w2 GEMM; RHT32+S2F6; MXFP8 dY quantize; SR requant of "
                        f"W2^T, A^T, W13^T, X^T; dgrad and wgrad of both GEMMs), H={H}, F={F}")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the w13 forward GEMM from the committed PMC profile (FETCH_SIZE and
+    WRITE_SIZE runs, scaled by the copy-kernel calibration), or None when the kernel's source has
+    changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_gemm_fwd.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["sources"])).hexdigest()
+    if h != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def main():
@@ -276,7 +291,8 @@ def main():
     roofline = {"bound": "mfma", "kernel": "k_nvfp4_grouped_gemm<SWIGLU> (w13 forward, fp16 MFMA after exact "
                                            "NVFP4 dequant)",
                 "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_F16_TFLOPS,
-                "traffic": None, "flops_per_launch": fl["fwd13"], "ms_per_launch": k13}
+                "traffic": measured_traffic() if args.workload == "ep48" else None,
+                "flops_per_launch": fl["fwd13"], "ms_per_launch": k13}
     kernels = {name: {"ms": ms} for name, ms in per_call.items()}
     kernels["moe_grouped_gemm_fwd[w13+swiglu]"].update(tflops=ach, frac_f16_peak=ach / PEAK_F16_TFLOPS)
     a2 = fl["fwd2"] / (k2 * 1e-3) / 1e12
