@@ -15,8 +15,9 @@
 // 16..31 are k = 32+16h .. 32+16h+15 of the 64-k step, and its scale operand is the E8M0 scale
 // of k-block h of that row (k-block b of the step = k in [32b, 32b+32)).
 //
-// Tiling: 256 x 256 output tile per workgroup of 4 wavefronts (128 x 128 each, 4 x 4 MFMA
-// blocks), K stages of 128 bytes staged through LDS (rows padded to 144 bytes), two stages.
+// Tiling: 256 x 256 output tile per workgroup of 8 wavefronts (128 x 64 each, 4 x 2 MFMA
+// blocks, two wavefronts per SIMD to hide latency), K stages of 64 bytes (one MFMA k-step)
+// staged through LDS (rows padded to 80 bytes), two stages.
 #include "pmn_dev.hpp"
 #include "pmn_kernels.hpp"
 
@@ -24,12 +25,14 @@ namespace pmn {
 
 namespace bwd {
 constexpr int BT = 256;
-constexpr int BK = 128;                 // k per stage (bytes per row)
-constexpr int ROWB = 144;
+constexpr int BK = 64;                  // k per stage (bytes per row) = one MFMA k-step
+constexpr int ROWB = 80;                // 64 + 16 pad: 16 consecutive rows hit 16 distinct 16-byte bank groups
 constexpr int TILEB = BT * ROWB;        // one operand's codes
-constexpr int SCB = BT * 4;             // one operand's 4 scale bytes per row
+constexpr int SCB = BT * 4;             // one operand's scale bytes per row (2 used: 2 blocks of 32)
 constexpr int STAGEB = 2 * TILEB + 2 * SCB;
 constexpr int LDSB = 2 * STAGEB;
+constexpr int THREADS = 512;            // 8 wavefronts: 2 along output rows x 4 along columns
+static_assert(THREADS == 2 * BT, "one staging thread per row of each operand tile");
 }  // namespace bwd
 
 enum { MODE_DGRAD = 0, MODE_WGRAD = 1 };
@@ -50,25 +53,40 @@ struct Mx8Args {
     int G;
     int64_t Nf, Kf;
     float* out;
+    int64_t rtiles, ctiles;   // tile grid (dgrad: slot-tile bound x Kf/256; wgrad: Nf/256 x Kf/256)
+    int SM, SN;
 };
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
+__global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
 {
     using namespace bwd;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
+    const int wr = wave >> 2, wc = wave & 3;    // 2 wavefronts along output rows, 4 along columns
 
     int g = -1;
     int64_t r0 = 0, rvalid = BT, c0 = 0, kbeg = 0, klen = 0;
     const uint8_t *abase, *aebase, *bbase, *bebase;
     int64_t ldo;
     float* obase;
+    TileXY tile;
+    int64_t L = blockIdx.x, batch = 0;
+    if (MODE == MODE_WGRAD) {
+        // super-tiles of expert g are numbered after those of experts 0 .. g-1
+        const int64_t nsuper = ((p.rtiles + p.SM - 1) / p.SM) * ((p.ctiles + p.SN - 1) / p.SN);
+        const int64_t s = ((L >> 3) >> 5) * 8 + (L & 7);
+        batch = s / nsuper;
+        if (batch >= p.G) return;
+        const int64_t s_in = s - batch * nsuper;
+        const int64_t j = ((s_in >> 3) << 5) + ((L >> 3) & 31);
+        L = (j << 3) | (s_in & 7);
+    }
+    if (!xcd_tile(L, p.rtiles, p.ctiles, p.SM, p.SN, tile)) return;
     if (MODE == MODE_DGRAD) {
-        int64_t t = blockIdx.y, cum = 0;
+        int64_t t = tile.row, cum = 0;
         for (int gg = 0; gg < p.G; gg++) {
             const int64_t s0 = p.offsets[gg], s1 = p.offsets[gg + 1];
             const int64_t tiles = (s1 - s0 + BT - 1) / BT;
@@ -81,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
             cum += tiles;
         }
         if (g < 0) return;
-        c0 = (int64_t)blockIdx.x * BT;
+        c0 = tile.col * BT;
         kbeg = 0;
         klen = p.Nf;
         abase = p.a; aebase = p.ae;
@@ -89,10 +107,10 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
         ldo = p.Kf;
         obase = p.out;
     } else {
-        g = blockIdx.z;
-        r0 = (int64_t)blockIdx.y * BT;
+        g = (int)batch;
+        r0 = tile.row * BT;
         rvalid = BT;
-        c0 = (int64_t)blockIdx.x * BT;
+        c0 = tile.col * BT;
         kbeg = p.po[g];
         klen = p.po[g + 1] - kbeg;
         abase = p.a + kbeg; aebase = p.ae + kbeg / 32;
@@ -101,69 +119,63 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
         obase = p.out + (int64_t)g * p.Nf * p.Kf;
     }
 
-    // Staging: per stage each operand tile is 256 rows x 128 bytes = 2048 chunks of 16 bytes;
-    // thread t stages chunks q = 256 k + t (row q / 8, part q % 8), so 8 lanes cover one row and a
-    // wavefront reads 8 whole 128-byte row segments per instruction. Loads are branch-free: a
-    // chunk outside the tile reads a valid address and is replaced by zeros.
-    const int prow = tid >> 3, part = tid & 7;
-    const uint8_t* arow[8];
-    bool arow_ok[8];
+    // Staging: per stage each operand tile is 256 rows x 64 bytes = 1024 chunks of 16 bytes.
+    // Threads 0..255 stage A and threads 256..511 stage B (wavefront-uniform); thread t stages
+    // chunks q = 256 k + (t % 256) (row q / 4, part q % 4), so 4 lanes cover one row segment,
+    // plus the 2 scale bytes of row t % 256. Loads are branch-free: a chunk outside the tile
+    // reads a valid address and is replaced by zeros (scale 127).
+    const bool stage_a = tid < BT;
+    const int st = tid & (BT - 1);
+    const int prow = st >> 2, part = st & 3;
+    const uint8_t* srow[4];
+    bool srow_ok[4];
 #pragma unroll
-    for (int k = 0; k < 8; k++) {
-        const int row = k * 32 + prow;
-        arow_ok[k] = row < rvalid;
-        arow[k] = abase + (r0 + (arow_ok[k] ? row : 0)) * p.lda + part * 16;
+    for (int k = 0; k < 4; k++) {
+        const int row = k * 64 + prow;
+        srow_ok[k] = stage_a ? row < rvalid : true;
+        srow[k] = stage_a ? abase + (r0 + (srow_ok[k] ? row : 0)) * p.lda + part * 16
+                          : bbase + (c0 + row) * p.ldb + part * 16;
     }
-    const uint8_t* brow0 = bbase + (c0 + prow) * p.ldb + part * 16;
-    const bool srow_ok = tid < rvalid;
-    const uint8_t* aep = aebase + (r0 + (srow_ok ? tid : 0)) * (p.lda / 32);
-    const uint8_t* bep = bebase + (c0 + tid) * (p.ldb / 32);
+    const bool scrow_ok = stage_a ? st < rvalid : true;
+    const uint8_t* sep = stage_a ? aebase + (r0 + (scrow_ok ? st : 0)) * (p.lda / 32)
+                                 : bebase + (c0 + st) * (p.ldb / 32);
     const int64_t kblocks = klen / 32;
+    uint8_t* const lds_tile = lds + (stage_a ? 0 : TILEB);
+    uint32_t* const lds_sc = reinterpret_cast<uint32_t*>(lds + 2 * TILEB + (stage_a ? 0 : SCB));
 
-    uint4 av[8], bv[8];
-    uint32_t as, bs;
+    uint4 sv[4];
+    uint32_t ss;
     auto load_stage = [&](int kt) {
         const int64_t k0 = (int64_t)kt * BK;
         const bool kok = k0 + part * 16 < klen;
         const int64_t koff = kok ? k0 : 0;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            uint4 a = *reinterpret_cast<const uint4*>(arow[k] + koff);
-            uint4 b = *reinterpret_cast<const uint4*>(brow0 + (int64_t)k * 32 * p.ldb + koff);
-            const bool aok = kok && arow_ok[k];
-            av[k] = aok ? a : make_uint4(0u, 0u, 0u, 0u);
-            bv[k] = kok ? b : make_uint4(0u, 0u, 0u, 0u);
+        for (int k = 0; k < 4; k++) {
+            const uint4 v = *reinterpret_cast<const uint4*>(srow[k] + koff);
+            sv[k] = (kok && srow_ok[k]) ? v : make_uint4(0u, 0u, 0u, 0u);
         }
-        uint32_t sa = 0u, sbb = 0u;
+        uint32_t sc = 0u;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
+        for (int q = 0; q < 2; q++) {
             const int64_t kb = k0 / 32 + q;
             const bool ok = kb < kblocks;
-            const int64_t ki = ok ? kb : 0;
-            const uint32_t x = aep[ki], y = bep[ki];
-            sa |= ((ok && srow_ok) ? x : 127u) << (8 * q);
-            sbb |= (ok ? y : 127u) << (8 * q);
+            const uint32_t x = sep[ok ? kb : 0];
+            sc |= ((ok && scrow_ok) ? x : 127u) << (8 * q);
         }
-        as = sa;
-        bs = sbb;
+        ss = sc;
     };
     auto store_stage = [&](int buf) {
-        uint8_t* base = lds + buf * STAGEB;
+        uint8_t* base = lds_tile + buf * STAGEB;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const int row = k * 32 + prow;
-            *reinterpret_cast<uint4*>(base + row * ROWB + part * 16) = av[k];
-            *reinterpret_cast<uint4*>(base + TILEB + row * ROWB + part * 16) = bv[k];
-        }
-        reinterpret_cast<uint32_t*>(base + 2 * TILEB)[tid] = as;
-        reinterpret_cast<uint32_t*>(base + 2 * TILEB + SCB)[tid] = bs;
+        for (int k = 0; k < 4; k++) *reinterpret_cast<uint4*>(base + (k * 64 + prow) * ROWB + part * 16) = sv[k];
+        lds_sc[buf * (STAGEB / 4) + st] = ss;
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
@@ -182,8 +194,8 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
         const uint32_t* scb = reinterpret_cast<const uint32_t*>(base + 2 * TILEB + SCB);
 #pragma unroll
         for (int ks = 0; ks < BK / 64; ks++) {
-            i32x8 af[4], bf[4];
-            int sa[4], sb[4];
+            i32x8 af[4], bf[2];
+            int sa[4], sb[2];
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const int row = wr * 128 + i * 32 + lrow;
@@ -194,8 +206,8 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
                 sa[i] = (int)((sca[row] >> (8 * (2 * ks + hh))) & 0xFFu);
             }
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                const int row = wc * 128 + j * 32 + lrow;
+            for (int j = 0; j < 2; j++) {
+                const int row = wc * 64 + j * 32 + lrow;
                 const uint8_t* src = base + TILEB + row * ROWB + ks * 64 + hh * 16;
                 uint4 lo = *reinterpret_cast<const uint4*>(src);
                 uint4 hi = *reinterpret_cast<const uint4*>(src + 32);
@@ -205,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < 2; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
         }
         // keep the next stage's LDS writes (which wait for its global loads) after the MFMAs
@@ -214,13 +226,13 @@ __global__ __launch_bounds__(256, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
         __syncthreads();
     }
 
-    // epilogue: block (i, j): lane holds column c = c0 + wc*128 + j*32 + lane%32 and rows
+    // epilogue: block (i, j): lane holds column c = c0 + wc*64 + j*32 + lane%32 and rows
     // r = r0 + wr*128 + i*32 + (v/4)*8 + hh*4 + v%4
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t col = c0 + wc * 128 + j * 32 + lrow;
+        for (int j = 0; j < 2; j++) {
+            const int64_t col = c0 + wc * 64 + j * 32 + lrow;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
@@ -234,9 +246,12 @@ hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_
                               int64_t Nf, int64_t Kf, float* dx, hipStream_t stream)
 {
     if (M == 0 || G == 0) return hipSuccess;
-    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, nullptr, G, Nf, Kf, dx};
-    dim3 grid((unsigned)(Kf / bwd::BT), (unsigned)((M + bwd::BT - 1) / bwd::BT + G));
-    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(256), 0, stream, p);
+    const int64_t rt = (M + bwd::BT - 1) / bwd::BT + G, ct = Kf / bwd::BT;
+    int SM, SN;
+    xcd_shape(rt, ct, SM, SN);
+    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, nullptr, G, Nf, Kf, dx, rt, ct, SM, SN};
+    dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
+    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -245,9 +260,12 @@ hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8
                               int64_t Nf, int64_t Kf, float* dw, hipStream_t stream)
 {
     if (G == 0) return hipSuccess;
-    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, G, Nf, Kf, dw};
-    dim3 grid((unsigned)(Kf / bwd::BT), (unsigned)(Nf / bwd::BT), (unsigned)G);
-    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(256), 0, stream, p);
+    const int64_t rt = Nf / bwd::BT, ct = Kf / bwd::BT;
+    int SM, SN;
+    xcd_shape(rt, ct, SM, SN);
+    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, G, Nf, Kf, dw, rt, ct, SM, SN};
+    dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN, G));
+    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -38,6 +38,8 @@ constexpr int ROWB = 144;                     // LDS bytes per row: 64 fp16 + 16
 constexpr int TILEB = BT * ROWB;              // one operand tile
 constexpr int STAGEB = 2 * TILEB;             // weights + activations
 constexpr int LDSB = 2 * STAGEB;              // two stages
+constexpr int THREADS = 512;                  // 8 wavefronts: 2 along weight rows x 4 along slots
+static_assert(THREADS == 2 * BT, "one staging thread per row of each operand tile");
 }  // namespace fwd
 
 struct FwdArgs {
@@ -57,6 +59,8 @@ struct FwdArgs {
     void* out;
     uint8_t* out_e8m0;
     void* out_aux;
+    int64_t mtiles, ntiles;   // slot-tile bound and weight tiles
+    int SM, SN;               // super-tile shape
 };
 
 // Dequantize one row's stage: 8 code words (64 FP4 values) and 4 E4M3 scale bytes -> 64 fp16
@@ -149,20 +153,22 @@ PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
+__global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
 {
     using namespace fwd;
     __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wn = wave >> 1, wm = wave & 1;
+    const int wn = wave >> 2, wm = wave & 3;    // 2 wavefronts along weight rows, 4 along slots
 
-    // ---- which (expert, slot tile, weight tile)
+    // ---- which (expert, slot tile, weight tile): XCD-aware order over slot tiles x weight tiles
+    TileXY tile;
+    if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
     int g = -1;
     int64_t m0 = 0, mvalid = 0;
     {
-        int64_t t = blockIdx.y, cum = 0;
+        int64_t t = tile.row, cum = 0;
         for (int gg = 0; gg < p.G; gg++) {
             const int64_t a = p.offsets[gg], b = p.offsets[gg + 1];
             const int64_t tiles = (b - a + BT - 1) / BT;
@@ -177,52 +183,50 @@ __global__ __launch_bounds__(256, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
     }
     if (g < 0) return;
     const int64_t N = p.N, K = p.K;
-    const int64_t n0 = (int64_t)blockIdx.x * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
+    const int64_t n0 = tile.col * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
 
-    // ---- global rows this thread stages
-    int64_t wrow;   // weight row
-    if (EPI == PMN_EPI_SWIGLU) {
-        const int F = (int)(N >> 1);
-        const int twn = tid >> 7, trb = (tid & 127) >> 5, tr = tid & 31;
-        wrow = (int64_t)g * N + (trb < 2 ? 0 : F) + n0 + twn * 64 + (trb & 1) * 32 + tr;
-    } else {
-        wrow = (int64_t)g * N + n0 + tid;
-    }
-    const bool xvalid = tid < mvalid;
-    const int64_t xrow = xvalid ? (p.gather ? (int64_t)p.gather[m0 + tid] : m0 + tid) : 0;
-    const uint8_t* wc = p.b_codes + wrow * (K >> 1);
-    const uint8_t* ws = p.b_scales + wrow * (K >> 4);
-    const uint8_t* xc = p.a_codes + xrow * (K >> 1);
-    const uint8_t* xs = p.a_scales + xrow * (K >> 4);
-
-    uint4 wcw[2], xcw[2];
-    uint32_t wsc, xsc;
-    auto load_stage = [&](int kt) {
-        const uint4* pw = reinterpret_cast<const uint4*>(wc + kt * (BK / 2));
-        wcw[0] = pw[0];
-        wcw[1] = pw[1];
-        wsc = *reinterpret_cast<const uint32_t*>(ws + kt * (BK / 16));
-        if (xvalid) {
-            const uint4* px = reinterpret_cast<const uint4*>(xc + kt * (BK / 2));
-            xcw[0] = px[0];
-            xcw[1] = px[1];
-            xsc = *reinterpret_cast<const uint32_t*>(xs + kt * (BK / 16));
+    // ---- staging: threads 0..255 stage weight row t, threads 256..511 activation row t - 256
+    const bool stage_w = tid < BT;                  // wavefront-uniform
+    const int srow = tid & (BT - 1);
+    const uint8_t* sc_codes;
+    const uint8_t* sc_scales;
+    bool svalid = true;
+    if (stage_w) {
+        int64_t wrow;
+        if (EPI == PMN_EPI_SWIGLU) {
+            const int F = (int)(N >> 1);
+            const int twn = srow >> 7, trb = (srow & 127) >> 5, tr = srow & 31;
+            wrow = (int64_t)g * N + (trb < 2 ? 0 : F) + n0 + twn * 64 + (trb & 1) * 32 + tr;
         } else {
-            xcw[0] = xcw[1] = make_uint4(0u, 0u, 0u, 0u);
-            xsc = 0u;
+            wrow = (int64_t)g * N + n0 + srow;
         }
-    };
-    auto store_stage = [&](int buf) {
-        uint8_t* base = lds + buf * STAGEB;
-        dequant_row_to_lds(wcw, wsc, base + tid * ROWB);
-        dequant_row_to_lds(xcw, xsc, base + TILEB + tid * ROWB);
-    };
+        sc_codes = p.b_codes + wrow * (K >> 1);
+        sc_scales = p.b_scales + wrow * (K >> 4);
+    } else {
+        svalid = srow < mvalid;
+        const int64_t xrow = svalid ? (p.gather ? (int64_t)p.gather[m0 + srow] : m0 + srow) : 0;
+        sc_codes = p.a_codes + xrow * (K >> 1);
+        sc_scales = p.a_scales + xrow * (K >> 4);
+    }
+    uint8_t* const lds_row = lds + (stage_w ? 0 : TILEB) + srow * ROWB;
 
-    f32x16 acc[4][4];
+    uint4 cw[2];
+    uint32_t sc;
+    auto load_stage = [&](int kt) {
+        const uint4* pc = reinterpret_cast<const uint4*>(sc_codes + kt * (BK / 2));
+        const uint4 c0 = pc[0], c1 = pc[1];
+        const uint32_t s = *reinterpret_cast<const uint32_t*>(sc_scales + kt * (BK / 16));
+        cw[0] = svalid ? c0 : make_uint4(0u, 0u, 0u, 0u);
+        cw[1] = svalid ? c1 : make_uint4(0u, 0u, 0u, 0u);
+        sc = svalid ? s : 0u;
+    };
+    auto store_stage = [&](int buf) { dequant_row_to_lds(cw, sc, lds_row + buf * STAGEB); };
+
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
@@ -235,29 +239,29 @@ __global__ __launch_bounds__(256, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
         const int buf = kt & 1;
         if (kt + 1 < KT) load_stage(kt + 1);
         const uint8_t* wb = lds + buf * STAGEB + (wn * 128 + lrow) * ROWB + lk;
-        const uint8_t* xb = lds + buf * STAGEB + TILEB + (wm * 128 + lrow) * ROWB + lk;
+        const uint8_t* xb = lds + buf * STAGEB + TILEB + (wm * 64 + lrow) * ROWB + lk;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ks++) {
-            f16x8 af[4], bf[4];
+            f16x8 af[4], bf[2];
 #pragma unroll
             for (int i = 0; i < 4; i++) af[i] = *reinterpret_cast<const f16x8*>(wb + i * 32 * ROWB + ks * 32);
 #pragma unroll
-            for (int j = 0; j < 4; j++) bf[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
+            for (int j = 0; j < 2; j++) bf[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 4; j++)
+                for (int j = 0; j < 2; j++)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < KT) store_stage(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- epilogue: lane holds slot m = (wm*128 + j*32 + lane%32), weight rows of block i
+    // ---- epilogue: lane holds slot m = (wm*64 + j*32 + lane%32), weight rows of block i
     const int hh = lane >> 5;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int64_t ml = wm * 128 + j * 32 + (lane & 31);
+    for (int j = 0; j < 2; j++) {
+        const int64_t ml = wm * 64 + j * 32 + (lane & 31);
         const bool mok = ml < mvalid;
         const int64_t m = m0 + ml;
         const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
@@ -334,17 +338,19 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
                            void* out_aux, hipStream_t stream)
 {
-    FwdArgs p{a_codes, a_scales, a_outer, a_rpo, gather, b_codes, b_scales, b_outer, b_rpo,
-              offsets, G, N, K, rht_mask, out, out_e8m0, out_aux};
     if (M == 0 || G == 0) return hipSuccess;
     const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;   // bound on sum of ceil(m_g / 256)
     const int64_t ntiles = N / fwd::BT;   // SWIGLU: each tile covers 128 w1 and 128 w3 rows
-    dim3 grid((unsigned)ntiles, (unsigned)mtiles);
+    int SM, SN;
+    xcd_shape(mtiles, ntiles, SM, SN);
+    FwdArgs p{a_codes, a_scales, a_outer, a_rpo, gather, b_codes, b_scales, b_outer, b_rpo,
+              offsets, G, N, K, rht_mask, out, out_e8m0, out_aux, mtiles, ntiles, SM, SN};
+    dim3 grid((unsigned)xcd_grid(mtiles, ntiles, SM, SN));
     switch (epilogue) {
-    case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32>), grid, dim3(256), 0, stream, p); break;
-    case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16>), grid, dim3(256), 0, stream, p); break;
-    case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU>), grid, dim3(256), 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6>), grid, dim3(256), 0, stream, p); break;
+    case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32>), grid, dim3(fwd::THREADS), 0, stream, p); break;
+    case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16>), grid, dim3(fwd::THREADS), 0, stream, p); break;
+    case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU>), grid, dim3(fwd::THREADS), 0, stream, p); break;
+    default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6>), grid, dim3(fwd::THREADS), 0, stream, p); break;
     }
     return hipGetLastError();
 }

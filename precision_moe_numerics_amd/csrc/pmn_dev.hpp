@@ -182,6 +182,49 @@ PMN_DEV uint32_t fp4_sr(float y, uint32_t r16)
     return idx | ((__float_as_uint(y) >> 28) & 8u);
 }
 
+// ---- XCD-aware tile order for the GEMMs ----------------------------------------------------
+//
+// MI355X has 8 XCDs, each with its own L2; workgroup L of a 1-D grid runs on XCD L % 8, and the
+// 32 CUs of an XCD run about 32 workgroups at a time. Tiles are grouped in "super-tiles" of
+// SM row tiles x SN column tiles (SM * SN = 32): the j-th workgroup of XCD x takes position
+// j % 32 of super-tile (j / 32) * 8 + x, so the workgroups an XCD runs together share SM A tiles
+// and SN B tiles in its L2. Super-tiles are numbered row-major over a grid of
+// ceil(rows / SM) x ceil(cols / SN); positions outside the tile grid return false.
+struct TileXY {
+    int64_t row, col, super_id;
+};
+
+PMN_DEV bool xcd_tile(int64_t L, int64_t row_tiles, int64_t col_tiles, int SM, int SN, TileXY& t)
+{
+    const int64_t x = L & 7, j = L >> 3;
+    const int64_t s = (j >> 5) * 8 + x;
+    const int p = (int)(j & 31);
+    const int64_t scols = (col_tiles + SN - 1) / SN;
+    const int64_t srow = s / scols, scol = s - srow * scols;
+    t.super_id = s;
+    t.row = srow * SM + p / SN;
+    t.col = scol * SN + p % SN;
+    return t.row < row_tiles && t.col < col_tiles;
+}
+
+// Grid size covering every super-tile of a rows x cols tile grid.
+inline int64_t xcd_grid(int64_t row_tiles, int64_t col_tiles, int SM, int SN, int64_t batches = 1)
+{
+    const int64_t nsuper = ((row_tiles + SM - 1) / SM) * ((col_tiles + SN - 1) / SN) * batches;
+    return 8 * 32 * ((nsuper + 7) / 8);
+}
+
+// SM x SN with SM * SN = 32 that wastes the fewest positions on a rows x cols tile grid.
+inline void xcd_shape(int64_t row_tiles, int64_t col_tiles, int& SM, int& SN)
+{
+    const int cand[2][2] = {{8, 4}, {4, 8}};
+    int64_t best = -1;
+    for (auto& c : cand) {
+        const int64_t n = ((row_tiles + c[0] - 1) / c[0]) * ((col_tiles + c[1] - 1) / c[1]);
+        if (best < 0 || n < best) { best = n; SM = c[0]; SN = c[1]; }
+    }
+}
+
 // ---- wave reductions ------------------------------------------------------------------------
 
 PMN_DEV float wave_max(float v)

@@ -168,33 +168,41 @@ __global__ __launch_bounds__(256) void k_nvfp4_given(const uint16_t* __restrict_
 }
 
 // Group amax: max |x| over each group of rows_per_outer rows, as fp32 bits folded with an
-// integer atomic max (order-independent and exact, so the result is deterministic). Each
-// workgroup reduces 4096 consecutive 16-byte chunks of its group with 16 independent loads per
-// thread; indices past the group end re-read its last chunk, which leaves a max unchanged.
+// integer atomic max (order-independent and exact, so the result is deterministic). At most
+// AMAX_BLOCKS workgroups per group, each looping over the group with 16 independent 16-byte
+// loads per thread per step (indices past the group end re-read its last chunk, which leaves a
+// max unchanged), reduce in LDS and issue one atomic, so no address sees many atomics.
 constexpr int AMAX_CHUNKS_PER_THREAD = 16;
+constexpr int AMAX_BLOCKS = 32;
 
 __global__ __launch_bounds__(256) void k_group_amax(const uint16_t* __restrict__ x, int64_t group_elems,
                                                     uint32_t* __restrict__ amax_bits)
 {
+    __shared__ float wmax[4];
     const int64_t g = blockIdx.y;
     const uint4* xg = reinterpret_cast<const uint4*>(x + g * group_elems);
     const int64_t n16 = group_elems >> 3;
-    const int64_t base = (int64_t)blockIdx.x * 256 * AMAX_CHUNKS_PER_THREAD + threadIdx.x;
-    uint4 v[AMAX_CHUNKS_PER_THREAD];
-#pragma unroll
-    for (int u = 0; u < AMAX_CHUNKS_PER_THREAD; u++) {
-        const int64_t i = base + u * 256;
-        v[u] = xg[i < n16 ? i : n16 - 1];
-    }
+    const int64_t step = (int64_t)gridDim.x * 256 * AMAX_CHUNKS_PER_THREAD;
     float m = 0.0f;
+    for (int64_t base = (int64_t)blockIdx.x * 256 * AMAX_CHUNKS_PER_THREAD + threadIdx.x; base < n16; base += step) {
+        uint4 v[AMAX_CHUNKS_PER_THREAD];
 #pragma unroll
-    for (int u = 0; u < AMAX_CHUNKS_PER_THREAD; u++) {
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        for (int u = 0; u < AMAX_CHUNKS_PER_THREAD; u++) {
+            const int64_t i = base + u * 256;
+            v[u] = xg[i < n16 ? i : n16 - 1];
+        }
 #pragma unroll
-        for (int q = 0; q < 4; q++) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
+        for (int u = 0; u < AMAX_CHUNKS_PER_THREAD; u++) {
+            const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; q++) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[q])), fabsf(bf16_hi(w[q]))));
+        }
     }
     m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) atomicMax(amax_bits + g, __float_as_uint(m));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(amax_bits + g, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 __global__ void k_fill_u32(uint32_t* p, int64_t n, uint32_t v)
@@ -244,7 +252,8 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
         hipLaunchKernelGGL(k_fill_u32, dim3((ngroups + 255) / 256), dim3(256), 0, stream, amax, ngroups, 0u);
         const int64_t group_elems = rows_per_outer * cols;
         const int64_t per_block = 256 * AMAX_CHUNKS_PER_THREAD;
-        const int64_t gx = (group_elems / 8 + per_block - 1) / per_block;
+        int64_t gx = (group_elems / 8 + per_block - 1) / per_block;
+        gx = gx > AMAX_BLOCKS ? AMAX_BLOCKS : gx;
         hipLaunchKernelGGL(k_group_amax, dim3((unsigned)gx, (unsigned)ngroups), dim3(256), 0, stream, x, group_elems, amax);
         hipLaunchKernelGGL(k_outer_from_amax, dim3((ngroups + 255) / 256), dim3(256), 0, stream, outer_out, ngroups);
     }
