@@ -222,10 +222,12 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * int64 [G+1]. N % 256 == 0, K % 256 == 0. Outputs fp32: da [M x K], db [G*N x K].
  * dY quantized with SR uses rng_stream_dy (row-wise) and rng_stream_dy + 1 (column-wise).
  * Workspace (16-byte aligned, >= moe_grouped_gemm_bwd_workspace_size) holds, in order, each
- * part rounded up to 256 bytes: dY row-wise codes [M x N] and E8M0 [M x N/32]; W^T codes
- * [K x G*N] and E8M0 [K x G*N/32]; dY^T codes [N x Pb] and E8M0 [N x Pb/32]; A^T codes [K x Pb]
- * and E8M0 [K x Pb/32]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M, G); the
- * parts of a gradient not requested are still reserved.
+ * part rounded up to 256 bytes: dY row-wise codes [M x N] and E8M0 [N/32 x Pb]; W^T codes
+ * [K x G*N] and E8M0 [G*N/32 x K]; dY^T codes [N x Pb] and E8M0 [Pb/32 x N]; A^T codes [K x Pb]
+ * and E8M0 [Pb/32 x K]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M, G). The
+ * E8M0 parts are k-block-major (entry [b, r] is the scale of k-block b of row r); the row-wise
+ * dY scales of slot s of group g sit at column padded_offsets[g] + s - offsets[g]. The parts of
+ * a gradient not requested are still reserved.
  */
 int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,

@@ -243,9 +243,9 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
 def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int):
     """Views of the backward workspace parts, in the order include/pmn.h documents them."""
     Pb = padded_bound(M, G)
-    sizes = [("dq", M * N, (M, N)), ("de", M * N // 32, (M, N // 32)), ("wt", K * G * N, (K, G * N)),
-             ("wte", K * G * N // 32, (K, G * N // 32)), ("dt", N * Pb, (N, Pb)), ("dte", N * Pb // 32, (N, Pb // 32)),
-             ("xt", K * Pb, (K, Pb)), ("xte", K * Pb // 32, (K, Pb // 32)), ("po", (G + 1) * 8, None)]
+    sizes = [("dq", M * N, (M, N)), ("de", N // 32 * Pb, (N // 32, Pb)), ("wt", K * G * N, (K, G * N)),
+             ("wte", K * G * N // 32, (G * N // 32, K)), ("dt", N * Pb, (N, Pb)), ("dte", N * Pb // 32, (Pb // 32, N)),
+             ("xt", K * Pb, (K, Pb)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
     off, views = 0, {}
     for name, nbytes, shape in sizes:
         part = workspace[off:off + nbytes]

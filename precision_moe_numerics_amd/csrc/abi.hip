@@ -25,7 +25,7 @@ BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K)
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
     L.dq = take((size_t)(M * N));
-    L.de = take((size_t)(M * N / 32));
+    L.de = take((size_t)(N / 32 * L.Pb));
     L.wt = take((size_t)(K * G * N));
     L.wte = take((size_t)(K * G * N / 32));
     L.dt = take((size_t)(N * L.Pb));
@@ -97,8 +97,8 @@ int requant_transpose_sr_mxfp8(const uint8_t* codes, const uint8_t* scales, cons
     if ((M > 0 && (!codes || !scales || !outer)) || !out || !out_e8m0) return PMN_EINVAL;
     if (!aligned(codes, 16) || !aligned(out, 16) || !aligned(outer, 4)) return PMN_EALIGN;
     return status(pmn::launch_requant(codes, scales, outer, cols, rows_per_outer, gather, M, offsets, G,
-                                      target, seed, rng_stream, out, out_e8m0, ld_out, padded_offsets,
-                                      hs(stream)));
+                                      target, seed, rng_stream, out, out_e8m0, ld_out, false,
+                                      padded_offsets, hs(stream)));
 }
 
 int mxfp8_quantize(const void* x, int64_t M, int64_t N, int layout, const int64_t* offsets, int G,
@@ -112,11 +112,12 @@ int mxfp8_quantize(const void* x, int64_t M, int64_t N, int layout, const int64_
     if (!aligned(x, 16) || !aligned(out, 16)) return PMN_EALIGN;
     if (layout == PMN_ROWWISE)
         return status(pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(x), M, N, rounding == PMN_SR, seed,
-                                             rng_stream, out, out_e8m0, hs(stream)));
+                                             rng_stream, out, out_e8m0, nullptr, 0, nullptr, 0, hs(stream)));
     int st = check_groups(M, offsets, G, ld_out);
     if (st != PMN_OK) return st;
     return status(pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(x), M, N, offsets, G, rounding == PMN_SR,
-                                         seed, rng_stream, out, out_e8m0, ld_out, padded_offsets, hs(stream)));
+                                         seed, rng_stream, out, out_e8m0, ld_out, false, padded_offsets,
+                                         hs(stream)));
 }
 
 int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, uint32_t sign_mask,
@@ -188,25 +189,27 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t s = hs(stream);
     const bool sr = dy_rounding == PMN_SR;
-    hipError_t e = hipSuccess;
+    int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
+    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s);
+    if (e != hipSuccess) return PMN_ELAUNCH;
     if (dgrad) {
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
-                                   ws + L.de, s);
+                                   ws + L.de, offsets, G, po, L.Pb, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
                                 0, PMN_TARGET_E4M3, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N,
-                                nullptr, s);
+                                true, nullptr, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, G, M, N, K, da, s);
+        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
+                                    s);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (wgrad) {
-        int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
         e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
-                                   ws + L.dt, ws + L.dte, L.Pb, po, s);
+                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G,
-                                PMN_TARGET_E4M3, seed, rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, nullptr, s);
+                                PMN_TARGET_E4M3, seed, rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s);
         if (e != hipSuccess) return PMN_ELAUNCH;

@@ -14,8 +14,17 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
                                  uint8_t* scales, float* outer_out, hipStream_t stream);
 
+// Row-wise MXFP8. With padded_offsets null the E8M0 scales are row-major [M x N/32]; otherwise
+// they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column
+// padded_offsets[g] + s - offsets[g] (the layout the grouped dgrad GEMM streams).
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
-                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, hipStream_t stream);
+                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
+                             const int64_t* offsets, int G, const int64_t* padded_offsets,
+                             int64_t ld_e8m0, hipStream_t stream);
+
+// Padded group offsets (each group rounded up to 32 slots) into padded_offsets [G+1].
+hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
+                                 hipStream_t stream);
 
 hipError_t launch_rht32_s2f6(const void* x, bool f32, int64_t rows, int64_t cols, uint32_t mask,
                              int8_t* codes, uint8_t* e8m0, hipStream_t stream);
@@ -24,12 +33,12 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t cols, int64_t rows_per_outer, const int32_t* gather, int64_t M,
                           const int64_t* offsets, int G, int target, uint64_t seed,
                           uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, int64_t ld,
-                          int64_t* padded_offsets, hipStream_t stream);
+                          bool e8m0_kb_major, int64_t* padded_offsets, hipStream_t stream);
 
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
-                             uint8_t* out_e8m0, int64_t ld, int64_t* padded_offsets,
-                             hipStream_t stream);
+                             uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,
+                             int64_t* padded_offsets, hipStream_t stream);
 
 hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                            int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
@@ -38,9 +47,12 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
                            void* out_aux, hipStream_t stream);
 
+// Grouped MXFP8 GEMMs. All E8M0 operands are k-block-major: de [Nf/32 x Pb] (padded slot
+// columns, po), wte [G*Nf/32 x Kf], dte [Pb/32 x Nf], xte [Pb/32 x Kf].
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
-                              const uint8_t* wte, const int64_t* offsets, int G, int64_t M,
-                              int64_t Nf, int64_t Kf, float* dx, hipStream_t stream);
+                              const uint8_t* wte, const int64_t* offsets, const int64_t* po,
+                              int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
+                              hipStream_t stream);
 
 hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
                               const uint8_t* xte, int64_t ld, const int64_t* po, int G,

@@ -276,7 +276,9 @@ template <bool SR>
 __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t M,
                                                     int64_t N, uint64_t seed, uint32_t stream_id,
                                                     uint8_t* __restrict__ out,
-                                                    uint8_t* __restrict__ out_e8m0)
+                                                    uint8_t* __restrict__ out_e8m0,
+                                                    const int64_t* __restrict__ offsets, int G,
+                                                    const int64_t* __restrict__ pad_off, int64_t ld_e8m0)
 {
     const int64_t nb = N >> 5;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -292,7 +294,18 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
     const int e = e8m0_exponent<E8M0_E4M3>(amax);
-    out_e8m0[i] = (uint8_t)(e + 127);
+    if (pad_off == nullptr) {
+        out_e8m0[i] = (uint8_t)(e + 127);
+    } else {
+        // group of slot r: the largest g with offsets[g] <= r (empty groups are skipped)
+        const int64_t r = i / nb, kb = i - r * nb;
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        out_e8m0[kb * ld_e8m0 + pad_off[lo] + (r - offsets[lo])] = (uint8_t)(e + 127);
+    }
     uint32_t o[8];
     if (SR) {
         const int64_t r = i / nb;
@@ -328,15 +341,19 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 }
 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
-                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, hipStream_t stream)
+                             uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
+                             const int64_t* offsets, int G, const int64_t* padded_offsets,
+                             int64_t ld_e8m0, hipStream_t stream)
 {
     const int64_t n = M * (N / 32);
     if (n == 0) return hipSuccess;
     const int64_t grid = (n + 255) / 256;
     if (sr)
-        hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out, out_e8m0);
+        hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+                           out_e8m0, offsets, G, padded_offsets, ld_e8m0);
     else
-        hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out, out_e8m0);
+        hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+                           out_e8m0, offsets, G, padded_offsets, ld_e8m0);
     return hipGetLastError();
 }
 

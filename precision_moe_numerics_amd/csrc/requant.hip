@@ -92,8 +92,9 @@ struct TransposeArgs {
     uint64_t seed;
     uint32_t stream_id;
     uint8_t* out;             // [cols x ld]
-    uint8_t* out_e8m0;        // [cols x ld/32]
+    uint8_t* out_e8m0;        // [cols x ld/32], or k-block-major [ld/32 x cols] when e8m0_kb_major
     int64_t ld;
+    bool e8m0_kb_major;
 };
 
 // Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
@@ -254,9 +255,19 @@ __global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
         if (col < a.cols) {
 #pragma unroll
             for (int b = 0; b < 4; b++)
-                if (block_live[b]) a.out_e8m0[col * (a.ld >> 5) + (int64_t)blockIdx.x * 4 + b] = tile_e[row * 4 + b];
+                if (block_live[b]) {
+                    const int64_t kb = (int64_t)blockIdx.x * 4 + b;
+                    a.out_e8m0[a.e8m0_kb_major ? kb * a.cols + col : col * (a.ld >> 5) + kb] = tile_e[row * 4 + b];
+                }
         }
     }
+}
+
+hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
+                                 hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, offsets, G, M, padded_offsets);
+    return hipGetLastError();
 }
 
 static hipError_t launch_transpose(const TransposeArgs& a, int src, int round, int target,
@@ -285,9 +296,10 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t cols, int64_t rows_per_outer, const int32_t* gather, int64_t M,
                           const int64_t* offsets, int G, int target, uint64_t seed,
                           uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, int64_t ld,
-                          int64_t* padded_offsets, hipStream_t stream)
+                          bool e8m0_kb_major, int64_t* padded_offsets, hipStream_t stream)
 {
     TransposeArgs a{};
+    a.e8m0_kb_major = e8m0_kb_major;
     a.codes = codes; a.scales = scales; a.outer = outer; a.rows_per_outer = rows_per_outer;
     a.x = nullptr; a.cols = cols; a.gather = gather; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
@@ -296,10 +308,11 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
-                             uint8_t* out_e8m0, int64_t ld, int64_t* padded_offsets,
-                             hipStream_t stream)
+                             uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,
+                             int64_t* padded_offsets, hipStream_t stream)
 {
     TransposeArgs a{};
+    a.e8m0_kb_major = e8m0_kb_major;
     a.codes = nullptr; a.scales = nullptr; a.outer = nullptr; a.rows_per_outer = 1;
     a.x = x; a.cols = N; a.gather = nullptr; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;

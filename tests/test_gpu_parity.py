@@ -298,15 +298,21 @@ def test_gemm_bwd_intermediates_and_gradients(P, I):
     da, db, ws = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
                                         seed=9, rng_stream_a=4, rng_stream_b=1, rng_stream_dy=6)
     v = P.bwd_workspace_views(ws, M, G, N, K)
+    # E8M0 parts are k-block-major; the row-wise dY scales sit at padded slot columns
+    off = np.asarray(d["offsets"], dtype=np.int64)
+    po = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
+    assert np.array_equal(npy(v["po"]), po)
+    grp = np.searchsorted(off, np.arange(M), side="right") - 1
+    pcol = po[grp] + np.arange(M) - off[grp]
     rq, re = O.mxfp8_quantize_rows(dy)
-    assert np.array_equal(npy(v["dq"]), rq) and np.array_equal(npy(v["de"]), re)
+    assert np.array_equal(npy(v["dq"]), rq) and np.array_equal(npy(v["de"])[:, pcol].T, re)
     rwt, rwte = O.requant_transpose_sr(_ref_q(d["wq"]), seed=9, stream=1)
-    assert np.array_equal(npy(v["wt"]), rwt) and np.array_equal(npy(v["wte"]), rwte)
+    assert np.array_equal(npy(v["wt"]), rwt) and np.array_equal(npy(v["wte"]).T, rwte)
     rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], stream=7)
     Pt = rt.shape[1]
-    assert np.array_equal(npy(v["dt"])[:, :Pt], rt) and np.array_equal(npy(v["dte"])[:, :Pt // 32], rte)
+    assert np.array_equal(npy(v["dt"])[:, :Pt], rt) and np.array_equal(npy(v["dte"]).T[:, :Pt // 32], rte)
     rxt, rxte = O.requant_transpose_sr(_ref_q(d["xq"]), gather=d["gather"], offsets=d["offsets"], seed=9, stream=4)
-    assert np.array_equal(npy(v["xt"])[:, :Pt], rxt) and np.array_equal(npy(v["xte"])[:, :Pt // 32], rxte)
+    assert np.array_equal(npy(v["xt"])[:, :Pt], rxt) and np.array_equal(npy(v["xte"]).T[:, :Pt // 32], rxte)
     da_ref = O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K)
     db_ref = O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K)
     assert rel_fro(npy(da), da_ref) <= 2e-3
