@@ -18,12 +18,13 @@
 // scales per 32 values, which cannot carry an E4M3 scale per 16, so the exact path is the fp16
 // one.
 //
-// Tiling. A workgroup of 4 wavefronts computes a 256 (weight rows n) x 256 (slots m) tile of
-// D = W X^T, i.e. Y^T, as 2 x 2 wavefront tiles of 128 x 128 (4 x 4 MFMA blocks). K advances in
-// stages of 64: each thread loads 32 code bytes and 4 scale bytes of one weight row and one
-// (gathered) activation row, dequantizes them and writes 128 bytes of fp16 per operand to LDS
-// (rows padded to 144 bytes, so fragment reads are bank-conflict free); two LDS stages
-// alternate with one barrier per stage while the next stage's codes are in flight.
+// Tiling. A workgroup of 8 wavefronts computes a 256 (weight rows n) x 256 (slots m) tile of
+// D = W X^T, i.e. Y^T, as 2 x 4 wavefront tiles of 128 x 64 (4 x 2 MFMA blocks), two wavefronts
+// per SIMD. K advances in stages of 64: each thread owns one weight row or one (gathered)
+// activation row, fetches its 32 code bytes and 4 scale bytes two stages ahead into registers,
+// and dequantizes them into 128 bytes of fp16 in LDS (rows padded to 144 bytes, so fragment
+// reads are bank-conflict free) between the MFMAs of the current stage; two LDS stages
+// alternate with one barrier per stage.
 // Groups (experts) are ragged: workgroup y walks the device offsets to find its (expert,
 // slot tile), so no host synchronization is needed.
 #include "pmn_dev.hpp"
@@ -63,29 +64,34 @@ struct FwdArgs {
     int SM, SN;               // super-tile shape
 };
 
-// Dequantize one row's stage: 8 code words (64 FP4 values) and 4 E4M3 scale bytes -> 64 fp16
-// written as 8 x 16 bytes to LDS.
-PMN_DEV void dequant_row_to_lds(const uint4 (&cw)[2], uint32_t sc, uint8_t* dst)
+// Dequantize block blk (16 FP4 values, two code words, one E4M3 scale byte) of one row's stage
+// to 16 fp16 values written as 2 x 16 bytes to LDS.
+struct RawStage {
+    uint4 c0, c1;   // 32 code bytes = 64 FP4 values
+    uint32_t s;     // 4 E4M3 block scales
+};
+
+template <int BLK>
+PMN_DEV void dequant_block_to_lds(const RawStage& r, uint8_t* dst)
 {
-    uint32_t w[8] = {cw[0].x, cw[0].y, cw[0].z, cw[0].w, cw[1].x, cw[1].y, cw[1].z, cw[1].w};
+    const uint32_t w0 = BLK == 0 ? r.c0.x : BLK == 1 ? r.c0.z : BLK == 2 ? r.c1.x : r.c1.z;
+    const uint32_t w1 = BLK == 0 ? r.c0.y : BLK == 1 ? r.c0.w : BLK == 2 ? r.c1.y : r.c1.w;
+    // E4M3 (OCP, bias 7) byte -> fp32 by the hardware converter (exact, subnormals included)
+    const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.s, BLK);
+    const f16x2 ss = {s, s};
 #pragma unroll
-    for (int blk = 0; blk < 4; blk++) {
-        const _Float16 s = (_Float16)e4m3_value((sc >> (8 * blk)) & 0xFFu);
-        const f16x2 ss = {s, s};
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-            const uint32_t word = w[2 * blk + h];
-            f16x2 p0 = PMN_FP4_TO_F16(word, 0) * ss;
-            f16x2 p1 = PMN_FP4_TO_F16(word, 1) * ss;
-            f16x2 p2 = PMN_FP4_TO_F16(word, 2) * ss;
-            f16x2 p3 = PMN_FP4_TO_F16(word, 3) * ss;
-            uint4 v;
-            __builtin_memcpy(&v.x, &p0, 4);
-            __builtin_memcpy(&v.y, &p1, 4);
-            __builtin_memcpy(&v.z, &p2, 4);
-            __builtin_memcpy(&v.w, &p3, 4);
-            *reinterpret_cast<uint4*>(dst + 16 * (2 * blk + h)) = v;
-        }
+    for (int h = 0; h < 2; h++) {
+        const uint32_t word = h ? w1 : w0;
+        f16x2 p0 = PMN_FP4_TO_F16(word, 0) * ss;
+        f16x2 p1 = PMN_FP4_TO_F16(word, 1) * ss;
+        f16x2 p2 = PMN_FP4_TO_F16(word, 2) * ss;
+        f16x2 p3 = PMN_FP4_TO_F16(word, 3) * ss;
+        uint4 v;
+        __builtin_memcpy(&v.x, &p0, 4);
+        __builtin_memcpy(&v.y, &p1, 4);
+        __builtin_memcpy(&v.z, &p2, 4);
+        __builtin_memcpy(&v.w, &p3, 4);
+        *reinterpret_cast<uint4*>(dst + 16 * (2 * BLK + h)) = v;
     }
 }
 
@@ -210,17 +216,18 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     }
     uint8_t* const lds_row = lds + (stage_w ? 0 : TILEB) + srow * ROWB;
 
-    uint4 cw[2];
-    uint32_t sc;
-    auto load_stage = [&](int kt) {
-        const uint4* pc = reinterpret_cast<const uint4*>(sc_codes + kt * (BK / 2));
-        const uint4 c0 = pc[0], c1 = pc[1];
-        const uint32_t s = *reinterpret_cast<const uint32_t*>(sc_scales + kt * (BK / 16));
-        cw[0] = svalid ? c0 : make_uint4(0u, 0u, 0u, 0u);
-        cw[1] = svalid ? c1 : make_uint4(0u, 0u, 0u, 0u);
-        sc = svalid ? s : 0u;
+    // Raw stages are fetched into registers two iterations ahead of their dequantization: three
+    // register sets rotate over an unrolled-by-3 loop. Fetches past the last stage re-read it, so
+    // every iteration issues the same loads and the compiler's load counting stays exact.
+    // A slot row past the tile's end reads activation row 0 instead: its products land only in
+    // output columns that are never stored, so the loaded values need no masking (masking them
+    // here would make every fetch wait for its data at once).
+    auto load_raw = [&](int kt, RawStage& r) {
+        const uint4* pc = reinterpret_cast<const uint4*>(sc_codes + (int64_t)kt * (BK / 2));
+        r.c0 = pc[0];
+        r.c1 = pc[1];
+        r.s = *reinterpret_cast<const uint32_t*>(sc_scales + (int64_t)kt * (BK / 16));
     };
-    auto store_stage = [&](int buf) { dequant_row_to_lds(cw, sc, lds_row + buf * STAGEB); };
 
     f32x16 acc[4][2];
 #pragma unroll
@@ -231,31 +238,60 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
     const int KT = (int)(K / BK);
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
     const int lrow = lane & 31, lk = (lane >> 5) * 16;
-    for (int kt = 0; kt < KT; kt++) {
+    // one iteration: MFMAs on LDS stage kt % 2 while stage kt + 1 (registers `nxt`) is
+    // dequantized into the other LDS stage, one 16-value block per k-substep, and stage kt + 3 is
+    // fetched into `fut` (whose stage kt was dequantized in the previous iteration)
+    // The last iteration dequantizes a repeated stage into the LDS stage nobody reads again, so
+    // the body has no conditional work and the compiler's wait counts stay exact.
+    auto step = [&](int kt, const RawStage& nxt, RawStage& fut) {
         const int buf = kt & 1;
-        if (kt + 1 < KT) load_stage(kt + 1);
+        load_raw(kt + 3 < KT ? kt + 3 : KT - 1, fut);
+        uint8_t* const dst = lds_row + (buf ^ 1) * STAGEB;
         const uint8_t* wb = lds + buf * STAGEB + (wn * 128 + lrow) * ROWB + lk;
         const uint8_t* xb = lds + buf * STAGEB + TILEB + (wm * 64 + lrow) * ROWB + lk;
+        // fragments of k-substep ks + 1 are read while the MFMAs of ks run
+        f16x8 af[2][4], bf[2][2];
+        auto read_frags = [&](int ks, f16x8 (&a)[4], f16x8 (&b)[2]) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const f16x8*>(wb + i * 32 * ROWB + ks * 32);
+#pragma unroll
+            for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
+        };
+        read_frags(0, af[0], bf[0]);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ks++) {
-            f16x8 af[4], bf[2];
-#pragma unroll
-            for (int i = 0; i < 4; i++) af[i] = *reinterpret_cast<const f16x8*>(wb + i * 32 * ROWB + ks * 32);
-#pragma unroll
-            for (int j = 0; j < 2; j++) bf[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
+            if (ks + 1 < BK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
+            if (ks == 0) dequant_block_to_lds<0>(nxt, dst);
+            if (ks == 1) dequant_block_to_lds<1>(nxt, dst);
+            if (ks == 2) dequant_block_to_lds<2>(nxt, dst);
+            if (ks == 3) dequant_block_to_lds<3>(nxt, dst);
         }
-        if (kt + 1 < KT) store_stage(buf ^ 1);
         __syncthreads();
+    };
+
+    RawStage r0, r1, r2;
+    load_raw(0, r0);
+    load_raw(KT > 1 ? 1 : 0, r1);
+    load_raw(KT > 2 ? 2 : KT - 1, r2);
+    dequant_block_to_lds<0>(r0, lds_row);
+    dequant_block_to_lds<1>(r0, lds_row);
+    dequant_block_to_lds<2>(r0, lds_row);
+    dequant_block_to_lds<3>(r0, lds_row);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 2 < KT; kt += 3) {
+        step(kt, r1, r0);
+        step(kt + 1, r2, r1);
+        step(kt + 2, r0, r2);
     }
+    if (kt < KT) step(kt, r1, r0);
+    if (kt + 1 < KT) step(kt + 1, r2, r1);
 
     // ---- epilogue: lane holds slot m = (wm*64 + j*32 + lane%32), weight rows of block i
     const int hh = lane >> 5;
