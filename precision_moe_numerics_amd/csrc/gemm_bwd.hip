@@ -15,12 +15,14 @@
 // 16..31 are k = 32+16h .. 32+16h+15 of the 64-k step, and its scale operand is the E8M0 scale
 // of k-block h of that row (k-block b of the step = k in [32b, 32b+32)).
 //
-// Tiling: 256 x 256 output tile per workgroup of 8 wavefronts (128 x 64 each, 4 x 2 MFMA
-// blocks, two wavefronts per SIMD). Operands stream through a ring of 4 LDS stages of 64 k
-// (one MFMA k-step) filled by global_load_lds (global -> LDS without registers), so three
-// stages are in flight while one is multiplied. Every wavefront issues the same 5 loads per
-// stage (4 x 1 KB of codes, 1 x 128 B of scales), so "stage kt has landed" is the per-wave
-// condition vmcnt <= 5 x (stages issued after kt), followed by a barrier.
+// Tiling: 256 x 256 output tile per workgroup of 4 wavefronts, one per SIMD, each computing a
+// 128 x 128 quarter (4 x 4 MFMA blocks, accumulators in AGPRs). Operands stream through a ring
+// of 4 LDS stages of 64 k (one MFMA k-step) filled by global_load_lds (global -> LDS without
+// registers). A wavefront reads the fragments of stage kt + 1 from LDS while the MFMAs of stage
+// kt run from registers, so the matrix cores never wait for LDS after a barrier; three further
+// stages are in flight. Every wavefront issues the same 9 loads per stage (8 x 1 KB of codes,
+// 1 x 256 B of scales), so "stage s has landed" is the per-wave condition vmcnt <= 9 x (stages
+// issued after s), followed by a barrier.
 //
 // LDS stage: A codes [256 rows x 64 B], B codes [256 x 64 B], A scales [2 k-blocks x 256 rows],
 // B scales [2 x 256]. Chunk c (16 B) of row r sits at slot c ^ ((r / 4) % 4): the 16 rows a
@@ -40,9 +42,9 @@ constexpr int TILEB = BT * BK;          // one operand's codes per stage
 constexpr int SCB = 2 * BT;             // one operand's scales per stage
 constexpr int STAGEB = 2 * TILEB + 2 * SCB;
 constexpr int LDSB = NSTAGE * STAGEB;
-constexpr int THREADS = 512;            // 8 wavefronts: 2 along output rows x 4 along columns
-constexpr int LOADS_PER_STAGE = 5;      // per wavefront
-static_assert(THREADS == 512 && BT == 256 && BK == 64, "the load assignment below assumes these sizes");
+constexpr int THREADS = 256;            // 4 wavefronts: 2 along output rows x 2 along columns
+constexpr int LOADS_PER_STAGE = 9;      // per wavefront
+static_assert(THREADS == 256 && BT == 256 && BK == 64 && NSTAGE == 4, "the load schedule below assumes these");
 }  // namespace bwd
 
 // Asynchronous global -> LDS copies. The LDS destination of lane l is m0 + 16 l (dwordx4) or
@@ -56,12 +58,14 @@ PMN_DEV void dma4(const void* src, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
+// Wait for this wavefront's LDS reads and until at most N of its loads are outstanding, then
+// barrier: afterwards the stage those loads waited for is visible to the workgroup and every
+// wavefront has finished reading the stages it read before.
 template <int N>
 PMN_DEV void wait_loads_and_barrier()
 {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-
 enum { MODE_DGRAD = 0, MODE_WGRAD = 1 };
 
 struct Mx8Args {
@@ -87,15 +91,24 @@ struct Mx8Args {
     int SM, SN;
 };
 
+// MFMA operands of one k-step for a wavefront's 128 x 128 quarter
+struct Mx8Frags {
+    i32x8 a[4], b[4];
+    int sa[4], sb[4];
+};
+
 template <int MODE>
 __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
 {
     using namespace bwd;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
+    // An AGPR operand marks the kernel as using AGPRs, so the compiler keeps the 256 accumulator
+    // registers in AGPRs (MFMA accumulator form) instead of arch VGPRs.
+    asm volatile("; agpr in use %0" ::"a"(0));
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave >> 2, wc = wave & 3;    // 2 wavefronts along output rows, 4 along columns
+    const int wr = wave >> 1, wc = wave & 1;    // 2 wavefronts along output rows, 2 along columns
 
     int g = -1;
     int64_t r0 = 0, rvalid = BT, c0 = 0, klen = 0;
@@ -154,124 +167,159 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
     }
 
-    // Load assignment. Wavefronts 0-3 load A, 4-7 load B. Codes: wavefront w issues the 1 KB
-    // pieces 4 (w % 4) .. 4 (w % 4) + 3 of its operand (16 rows each); lane l of a piece lands at
+    // Load schedule. Wavefronts 0-1 load A, 2-3 load B. Codes: wavefront w issues the 1 KB
+    // pieces 8 (w % 2) .. 8 (w % 2) + 7 of its operand (16 rows each); lane l of piece n lands at
     // row 16 n + l / 4, slot l % 4, and so fetches chunk (l % 4) ^ ((l / 16) % 4). Rows outside the
     // tile (dgrad's last tile of a group) fetch row 0 instead: their outputs are never stored.
-    // Scales: wavefront w covers k-block (w / 2) % 2 of the stage, rows 128 (w % 2) .. +127, four
-    // per lane over lanes 0-31.
-    const int op = wave >> 2;
+    // Scales: wavefront w loads k-block w % 2 of the stage, rows 4 l .. 4 l + 3 in lane l.
+    const int op = wave >> 1, half = wave & 1;
     const uint8_t* cbase = op ? bcode : acode;
     const int64_t cld = op ? p.ldb : p.lda;
-    const int64_t crows = op ? (int64_t)BT : rvalid;
+    const int crows = (int)(op ? (int64_t)BT : rvalid);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    const uint8_t* cptr[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int row = ((wave & 3) * 4 + i) * 16 + (lane >> 2);
-        cptr[i] = cbase + (int64_t)(row < crows ? row : 0) * cld + chunk * 16;
-    }
-    const int kbsel = (wave >> 1) & 1;
-    const int srow = ((wave & 1) * 32 + lane) * 4;
     const uint8_t* sbase = op ? bsc : asc;
     const int64_t sld = op ? bsld : asld;
     const int64_t srows = op ? (int64_t)BT : asrows;
-    const uint8_t* sptr = sbase + (srow < srows ? srow : 0);
+    const uint8_t* sptr = sbase + (4 * lane < srows ? 4 * lane : 0);
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);   // LDS offset
-    const uint32_t cdst = lds0 + op * TILEB + (wave & 3) * 4096;
-    const uint32_t sdst = lds0 + 2 * TILEB + op * SCB + kbsel * 256 + (wave & 1) * 128;
+    const uint32_t cdst = lds0 + op * TILEB + half * 8192;
+    const uint32_t sdst = lds0 + 2 * TILEB + op * SCB + half * BT;
 
     const int64_t kblocks = klen / 32;
     const int KT = (int)((klen + BK - 1) / BK);
     const bool half_tail = (klen & (BK - 1)) != 0;   // last stage holds one k-block (wgrad)
     const int tail_back = chunk >= 2 ? 32 : 0;        // that stage's missing chunks re-read valid k
 
-    auto issue = [&](int kt) {
+    // Steps v = 0 .. KV-1 walk the stages; when KT is odd a leading step (v = 0) re-reads stage 0
+    // with every scale forced to 2^-127 on both operands, so it adds nothing and the step count
+    // is even. Step v multiplies stage v - pre and uses LDS slot v % NSTAGE.
+    const int pre = KT & 1;
+    const int KV = KT + pre;
+    auto stage_of = [&](int v) { const int st = v - pre; return st < 0 ? 0 : (st < KT ? st : KT - 1); };
+    // the loads of step v: 8 code pieces and one scale line
+    struct IssueAt {
+        int64_t kc, kb;
+        uint32_t so;
+    };
+    auto issue_at = [&](int v) {
+        const int kt = stage_of(v);
         const int64_t k0 = (int64_t)kt * BK;
-        const int64_t kc = (half_tail && kt == KT - 1) ? k0 - tail_back : k0;
-        const uint32_t so = (uint32_t)(kt % NSTAGE) * STAGEB;
+        IssueAt r;
+        r.kc = ((half_tail && kt == KT - 1) ? k0 - tail_back : k0) + chunk * 16;
+        r.kb = (k0 >> 5) + half;
+        r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
+        r.so = (uint32_t)(v % NSTAGE) * STAGEB;
+        return r;
+    };
+    auto issue_piece = [&](const IssueAt& r, int i) {
+        const int row = (half * 8 + i) * 16 + (lane >> 2);
+        dma16(cbase + (int64_t)(row < crows ? row : 0) * cld + r.kc, cdst + r.so + i * 1024);
+    };
+    auto issue_scales = [&](const IssueAt& r) { dma4(sptr + r.kb * sld, sdst + r.so); };
+    auto issue = [&](int v) {
+        const IssueAt r = issue_at(v);
 #pragma unroll
-        for (int i = 0; i < 4; i++) dma16(cptr[i] + kc, cdst + so + i * 1024);
-        int64_t kb = (k0 >> 5) + kbsel;
-        kb = kb < kblocks ? kb : kblocks - 1;
-        const uint32_t sd = sdst + so;
-        if (lane < 32) dma4(sptr + kb * sld, sd);
+        for (int i = 0; i < 8; i++) issue_piece(r, i);
+        issue_scales(r);
     };
 
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
-
-    if (KT > 0) issue(0);
-    if (KT > 1) issue(1);
-    if (KT > 2) issue(2);
     const int lrow = lane & 31, hh = lane >> 5;
     const int swz = (lrow >> 2) & 3;
     const int off_lo = ((hh ^ swz) << 4), off_hi = (((2 + hh) ^ swz) << 4);
-    for (int kt = 0; kt < KT; kt++) {
-        // stage kt has landed once at most 5 x (stages issued after it) loads are outstanding
-        const int later = KT - 1 - kt;
-        if (later >= 2) wait_loads_and_barrier<2 * LOADS_PER_STAGE>();
-        else if (later == 1) wait_loads_and_barrier<LOADS_PER_STAGE>();
-        else wait_loads_and_barrier<0>();
-        // the barrier also ends every wavefront's reads of stage kt - 1, whose slot is refilled here
-        if (kt + 3 < KT) issue(kt + 3);
+    // Fragments of step v: lane l supplies row l % 32 of each 32-row block with bytes 0..15 =
+    // k 16h .. 16h+15 and bytes 16..31 = k 32+16h .. (h = l / 32), and the scale of k-block h.
+    // In a half-full last stage, k-block 1 holds re-read (finite) codes; both operands give it
+    // the E8M0 scale 2^-127, so its products are scaled by 2^-254 and vanish in fp32 (as does
+    // the whole leading step).
+    auto frag_mask = [&](int v) {
+        const int kt = v - pre;
+        return (kt < 0 || (half_tail && kt == KT - 1 && hh)) ? 0 : 0xFF;
+    };
+    // (the scale mask is applied when the MFMA is issued, one step after the read: applying it at
+    // the read would make the wavefront wait for the LDS byte right away)
+    auto read_frag = [&](const uint8_t* base, int opb, int row, i32x8& f, int& sc) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_lo);
+        const uint4 hi = *reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_hi);
+        sc = (int)base[2 * TILEB + opb * SCB + hh * BT + row];
+        f = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
+    auto read_frags = [&](int v, Mx8Frags& f) {
+        const uint8_t* base = lds + (v % NSTAGE) * STAGEB;
+#pragma unroll
+        for (int i = 0; i < 4; i++) read_frag(base, 0, wr * 128 + i * 32 + lrow, f.a[i], f.sa[i]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) read_frag(base, 1, wc * 128 + j * 32 + lrow, f.b[j], f.sb[j]);
+    };
 
-        const uint8_t* base = lds + (kt % NSTAGE) * STAGEB;
-        const uint8_t* sca = base + 2 * TILEB + hh * BT;
-        const uint8_t* scb = base + 2 * TILEB + SCB + hh * BT;
-        const bool tail = half_tail && kt == KT - 1;
-        i32x8 af[4], bf[2];
-        int sa[4], sb[2];
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+    // One step: once slot v + 1 has landed (and every wavefront is done reading slot v, which is
+    // refilled), read its fragments while the MFMAs of step v (already in registers) run. With
+    // one wavefront per SIMD the wavefront itself must keep the matrix core fed, so each of the
+    // 16 MFMAs is followed by one piece of the next step's work (a load or a fragment read) and
+    // the compiler may not regroup them. Every step is identical: the refill loads step
+    // min(v + 4, KV - 1) (near the end this re-loads the last stage, into a free slot or over
+    // identical bytes) and the fragment read re-reads the last step once past it, so each step
+    // waits for exactly two younger slots and no value is live only on some paths.
+    auto step = [&](int v, const Mx8Frags& cur, Mx8Frags& nxt) {
+        wait_loads_and_barrier<2 * LOADS_PER_STAGE>();
+        const IssueAt r = issue_at(v + NSTAGE < KV ? v + NSTAGE : KV - 1);
+        const int vr = v + 1 < KV ? v + 1 : v;
+        const uint8_t* rbase = lds + (vr % NSTAGE) * STAGEB;
+        const int smask = frag_mask(v);
+        int sa[4], sb[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int row = wr * 128 + i * 32 + lrow;
-            const uint4 lo = *reinterpret_cast<const uint4*>(base + row * BK + off_lo);
-            uint4 hi = *reinterpret_cast<const uint4*>(base + row * BK + off_hi);
-            int sc = sca[row];
-            if (tail) {
-                hi = make_uint4(0u, 0u, 0u, 0u);
-                sc = hh ? 127 : sc;
-            }
-            af[i] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sa[i] = sc;
+            sa[i] = cur.sa[i] & smask;
+            sb[i] = cur.sb[i] & smask;
         }
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int row = wc * 64 + j * 32 + lrow;
-            const uint4 lo = *reinterpret_cast<const uint4*>(base + TILEB + row * BK + off_lo);
-            uint4 hi = *reinterpret_cast<const uint4*>(base + TILEB + row * BK + off_hi);
-            int sc = scb[row];
-            if (tail) {
-                hi = make_uint4(0u, 0u, 0u, 0u);
-                sc = hh ? 127 : sc;
-            }
-            bf[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-            sb[j] = sc;
+        for (int q = 0; q < 16; q++) {
+            const int i = q >> 2, j = q & 3;
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
+                                                                       sa[i], 0, sb[j]);
+            if (q < 8) issue_piece(r, q);
+            if (q == 8) issue_scales(r);
+            if (q >= 8 && q < 12) read_frag(rbase, 0, wr * 128 + (q - 8) * 32 + lrow, nxt.a[q - 8], nxt.sa[q - 8]);
+            if (q >= 12) read_frag(rbase, 1, wc * 128 + (q - 12) * 32 + lrow, nxt.b[q - 12], nxt.sb[q - 12]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+
+    if (KT > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
+        for (int v = 0; v < NSTAGE; v++) issue(v < KV ? v : KV - 1);
+        Mx8Frags f0, f1;
+        wait_loads_and_barrier<3 * LOADS_PER_STAGE>();
+        read_frags(0, f0);
+        for (int v = 0; v < KV; v += 2) {
+            step(v, f0, f1);
+            step(v + 1, f1, f0);
+        }
+        // no LDS copy may still be in flight when the workgroup's LDS is released
+        wait_loads_and_barrier<0>();
     }
 
-    // epilogue: block (i, j): lane holds column c = c0 + wc*64 + j*32 + lane%32 and tile rows
+    // epilogue: block (i, j): lane holds column c = c0 + wc*128 + j*32 + lane%32 and tile rows
     // wr*128 + i*32 + (v/4)*8 + hh*4 + v%4
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t col = c0 + wc * 64 + j * 32 + lrow;
+        for (int j = 0; j < 4; j++) {
+            const int64_t col = c0 + wc * 128 + j * 32 + lrow;
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
                 if (rl < rvalid) obase[rl * p.Kf + col] = acc[i][j][v];
             }
+            // one block at a time: keeps the accumulators in AGPRs until they are stored
+            __builtin_amdgcn_sched_barrier(0);
         }
 }
 
