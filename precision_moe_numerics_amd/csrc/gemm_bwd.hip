@@ -130,20 +130,12 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     if (!xcd_tile(L, p.rtiles, p.ctiles, p.SM, p.SN, tile)) return;
     c0 = tile.col * BT;
     if (MODE == MODE_DGRAD) {
-        int64_t t = tile.row, cum = 0, p0 = 0;
-        for (int gg = 0; gg < p.G; gg++) {
-            const int64_t s0 = p.offsets[gg], s1 = p.offsets[gg + 1];
-            const int64_t tiles = (s1 - s0 + BT - 1) / BT;
-            if (t < cum + tiles) {
-                g = gg;
-                r0 = s0 + (t - cum) * BT;
-                p0 = p.po[gg] + (t - cum) * BT;
-                rvalid = s1 - r0 < BT ? s1 - r0 : BT;
-                break;
-            }
-            cum += tiles;
-        }
-        if (g < 0) return;
+        const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, BT);
+        if (u.g < 0) return;
+        g = u.g;
+        r0 = u.s0 + u.index * BT;
+        const int64_t p0 = p.po[g] + u.index * BT;
+        rvalid = u.s1 - r0 < BT ? u.s1 - r0 : BT;
         klen = p.Nf;
         acode = p.a + r0 * p.lda;
         asc = p.ae + p0;

@@ -171,23 +171,11 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     // ---- which (expert, slot tile, weight tile): XCD-aware order over slot tiles x weight tiles
     TileXY tile;
     if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
-    int g = -1;
-    int64_t m0 = 0, mvalid = 0;
-    {
-        int64_t t = tile.row, cum = 0;
-        for (int gg = 0; gg < p.G; gg++) {
-            const int64_t a = p.offsets[gg], b = p.offsets[gg + 1];
-            const int64_t tiles = (b - a + BT - 1) / BT;
-            if (t < cum + tiles) {
-                g = gg;
-                m0 = a + (t - cum) * BT;
-                mvalid = b - m0 < BT ? b - m0 : BT;
-                break;
-            }
-            cum += tiles;
-        }
-    }
-    if (g < 0) return;
+    const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, BT);
+    if (u.g < 0) return;
+    const int g = u.g;
+    const int64_t m0 = u.s0 + u.index * BT;
+    const int64_t mvalid = u.s1 - m0 < BT ? u.s1 - m0 : BT;
     const int64_t N = p.N, K = p.K;
     const int64_t n0 = tile.col * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
 

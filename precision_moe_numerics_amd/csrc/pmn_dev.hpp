@@ -234,4 +234,46 @@ PMN_DEV float wave_max(float v)
     return v;
 }
 
+// ---- ragged groups --------------------------------------------------------------------------
+
+// Unit t of the concatenation of per-group unit lists, where group g (slots offsets[g] ..
+// offsets[g+1]) holds ceil(size / unit) units: its group, its index inside the group and the
+// group's slot range. Wavefront-parallel (lane l reads group 64c + l, a prefix sum over the lanes
+// and a ballot pick the group), so the cost does not grow with the group index. Every lane of
+// the wavefront must call it; the result is wavefront-uniform. g = -1 when t is past the end.
+struct GroupUnit {
+    int g;
+    int64_t index;      // unit index inside the group
+    int64_t s0, s1;     // the group's slots
+};
+
+PMN_DEV GroupUnit locate_group_unit(const int64_t* offsets, int G, int64_t t, int64_t unit)
+{
+    const int lane = threadIdx.x & 63;
+    int64_t before = 0;   // units of the groups of earlier chunks
+    for (int c0 = 0; c0 < G; c0 += 64) {
+        const int gl = c0 + lane;
+        const int64_t a = gl < G ? offsets[gl] : 0, b = gl < G ? offsets[gl + 1] : 0;
+        const int64_t n = (b - a + unit - 1) / unit;
+        int64_t cum = n;   // inclusive prefix over the lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t y = __shfl_up(cum, d, 64);
+            if (lane >= d) cum += y;
+        }
+        const uint64_t hit = __ballot(before + cum > t);
+        if (hit) {
+            const int lg = __builtin_ctzll(hit);
+            GroupUnit r;
+            r.g = c0 + lg;
+            r.index = t - (before + __shfl(cum, lg, 64) - __shfl(n, lg, 64));
+            r.s0 = __shfl(a, lg, 64);
+            r.s1 = __shfl(b, lg, 64);
+            return r;
+        }
+        before += __shfl(cum, 63, 64);
+    }
+    return GroupUnit{-1, 0, 0, 0};
+}
+
 }  // namespace pmn
