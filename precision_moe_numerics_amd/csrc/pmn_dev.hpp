@@ -51,11 +51,11 @@ PMN_DEV uint32_t f32_to_bf16_bits(float f)
 // ---- E4M3 ---------------------------------------------------------------------------------
 
 // Value of an E4M3 byte (finite codes).
+// E4M3 (OCP, bias 7, no infinities) byte -> fp32 by the hardware converter: exact for every
+// finite code, subnormals included; 0x7F / 0xFF (NaN) decode to NaN.
 PMN_DEV float e4m3_value(uint32_t c)
 {
-    uint32_t mag = c & 0x7Fu;
-    float v = (mag < 8u) ? (float)mag * 0x1p-9f : __uint_as_float((mag << 20) + (120u << 23));
-    return (c & 0x80u) ? -v : v;
+    return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
 }
 
 // Non-negative t -> E4M3 byte, round to nearest even, saturating at 448.

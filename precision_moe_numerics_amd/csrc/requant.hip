@@ -97,6 +97,29 @@ struct TransposeArgs {
     bool e8m0_kb_major;
 };
 
+// E4M3 code of v / scale (scale a power of two) by stochastic rounding with the given SR operand,
+// written into byte `sel` (0..3) of `word`.
+PMN_DEV uint32_t e4m3_sr_scaled_into(uint32_t word, float v, uint32_t rng, float scale, int sel)
+{
+    switch (sel) {
+    case 0: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 0);
+    case 1: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 1);
+    case 2: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 2);
+    default: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 3);
+    }
+}
+
+// E4M3 codes of a / scale and b / scale (scale a power of two), round to nearest even, written
+// into the low (hi = false) or high 16 bits of `word`.
+PMN_DEV uint32_t e4m3_rne_pair_scaled_into(uint32_t word, float a, float b, float scale, bool hi)
+{
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    const v2i16 old = __builtin_bit_cast(v2i16, word);
+    const v2i16 r = hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, scale, true)
+                       : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(old, a, b, scale, false);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
 PMN_DEV void deq8(uint32_t cw, float d, float (&v)[8])
 {
@@ -124,7 +147,7 @@ PMN_DEV int tile_chunk(int row, int chunk) { return row * TQ_RS + ((chunk ^ ((ro
 
 // SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (nibble/byte).
 template <int SRC, int ROUND, int TARGET>
-__global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
+__global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tile[TQ_ROWS * TQ_RS];
     __shared__ uint8_t tile_e[TQ_ROWS * 4];
@@ -159,15 +182,23 @@ __global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
         if (SRC == SRC_NVFP4) {
             uint32_t sbyte[32];
             float so[32];
+            // row bases are wavefront-uniform (scalar registers); each lane adds a 32-bit offset
+            const uint32_t coff = (uint32_t)(c0 >> 1), soff = (uint32_t)(c0 >> 4);
 #pragma unroll
             for (int j = 0; j < 32; j++) {
                 const int64_t r = __builtin_amdgcn_readlane(rl, j);
                 so[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ol), j));
-                cw[j] = *reinterpret_cast<const uint32_t*>(a.codes + ((r * a.cols + c0) >> 1));
-                sbyte[j] = a.scales[(r * a.cols + c0) >> 4];
+                const uint8_t* crow = a.codes + r * (a.cols >> 1);
+                const uint8_t* srow = a.scales + r * (a.cols >> 4);
+                cw[j] = *reinterpret_cast<const uint32_t*>(crow + coff);
+                sbyte[j] = srow[soff];
             }
+            // slots past the group's end become +0 (code word 0, scale 0), so they need no branch
 #pragma unroll
-            for (int j = 0; j < 32; j++) dsc[j] = j <= last ? e4m3_value(sbyte[j]) * so[j] : 0.0f;
+            for (int j = 0; j < 32; j++) {
+                dsc[j] = j <= last ? e4m3_value(sbyte[j]) * so[j] : 0.0f;
+                cw[j] = j <= last ? cw[j] : 0u;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < 32; j++) {
@@ -179,17 +210,24 @@ __global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
 #pragma unroll
         for (int c = 0; c < 8; c++) amax[c] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; j++) {
-            float v[8];
-            if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
-            else bf8(xw[j], v);
+        for (int j = 0; j < 32; j += 2) {
+            float v0[8], v1[8];
+            if (SRC == SRC_NVFP4) {
+                deq8(cw[j], dsc[j], v0);
+                deq8(cw[j + 1], dsc[j + 1], v1);
+            } else {
+                bf8(xw[j], v0);
+                bf8(xw[j + 1], v1);
+            }
 #pragma unroll
-            for (int c = 0; c < 8; c++) amax[c] = fmaxf(amax[c], fabsf(v[c]));
+            for (int c = 0; c < 8; c++) amax[c] = fmaxf(amax[c], fmaxf(fabsf(v0[c]), fabsf(v1[c])));
         }
         int e[8];
+        float escale[8];   // 2^e: the scaled converter divides by it exactly
 #pragma unroll
         for (int c = 0; c < 8; c++) {
             e[c] = TARGET == 0 ? e8m0_exponent<E8M0_E4M3>(amax[c]) : e8m0_exponent<E8M0_E2M1>(amax[c]);
+            escale[c] = __builtin_ldexpf(1.0f, e[c]);
             tile_e[(lane * 8 + c) * 4 + w] = (uint8_t)(e[c] + 127);
         }
 
@@ -201,27 +239,66 @@ __global__ __launch_bounds__(256) void k_transpose_quant(TransposeArgs a)
             for (int c = 0; c < 8; c++)
 #pragma unroll
                 for (int q = 0; q < 4; q++) o[c][q] = 0u;
+            if (TARGET == 0) {
+                // E4M3 target: every slot runs (padding slots are +0 and convert to 0 whatever the
+                // random bits). The scaled converters compute the conversion of v / 2^e exactly and
+                // write their bytes straight into the packed word: SR one value at a time, RNE two
+                // slots of a column at a time.
 #pragma unroll
-            for (int jj = 0; jj < 16; jj++) {
-                const int j = half * 16 + jj;
-                if (j < blk.valid) {
-                    const int64_t s = blk.s0 + j;
-                    float v[8];
-                    if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
-                    else bf8(xw[j], v);
-                    uint32_t rw[4] = {0u, 0u, 0u, 0u};
-                    if (ROUND == 1) rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+                for (int jj = 0; jj < 16; jj += 2) {
+                    float v[2][8];
 #pragma unroll
-                    for (int c = 0; c < 8; c++) {
-                        const float y = __builtin_ldexpf(v[c], -e[c]);
-                        uint32_t code;
-                        if (TARGET == 0) {
-                            code = ROUND == 1 ? e4m3_sr(y, sr_operand(rw[c >> 1], c & 1)) : e4m3_rne(y);
+                    for (int u = 0; u < 2; u++) {
+                        const int j = half * 16 + jj + u;
+                        // recompute the values instead of keeping the amax pass's 256 values alive
+                        // (the empty asm hides that they are equal)
+                        if (SRC == SRC_NVFP4) {
+                            uint32_t cwj = cw[j];
+                            asm volatile("" : "+v"(cwj));
+                            deq8(cwj, dsc[j], v[u]);
                         } else {
-                            const uint32_t word = rw[c >> 1];
-                            code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
+                            uint4 xj = xw[j];
+                            asm volatile("" : "+v"(xj.x), "+v"(xj.y), "+v"(xj.z), "+v"(xj.w));
+                            bf8(xj, v[u]);
                         }
-                        o[c][jj >> 2] |= code << (8 * (jj & 3));
+                    }
+                    if (ROUND == 1) {
+#pragma unroll
+                        for (int u = 0; u < 2; u++) {
+                            const int64_t s = blk.s0 + half * 16 + jj + u;
+                            uint32_t rw[4];
+                            rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+#pragma unroll
+                            for (int c = 0; c < 8; c++)
+                                o[c][jj >> 2] = e4m3_sr_scaled_into(o[c][jj >> 2], v[u][c], sr_operand(rw[c >> 1], c & 1),
+                                                                    escale[c], (jj + u) & 3);
+                            // one slot at a time: interleaving Philox evaluations only adds live registers
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < 8; c++) o[c][jj >> 2] = e4m3_rne_pair_scaled_into(o[c][jj >> 2], v[0][c], v[1][c], escale[c], (jj & 2) != 0);
+                    }
+                }
+            } else {
+                // E2M1 target (the pages' worked example): SR onto the FP4 grid
+#pragma unroll
+                for (int jj = 0; jj < 16; jj++) {
+                    const int j = half * 16 + jj;
+                    if (j < blk.valid) {
+                        const int64_t s = blk.s0 + j;
+                        float v[8];
+                        if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
+                        else bf8(xw[j], v);
+                        uint32_t rw[4];
+                        rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+#pragma unroll
+                        for (int c = 0; c < 8; c++) {
+                            const float y = __builtin_ldexpf(v[c], -e[c]);
+                            const uint32_t word = rw[c >> 1];
+                            const uint32_t code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
+                            o[c][jj >> 2] |= code << (8 * (jj & 3));
+                        }
                     }
                 }
             }
