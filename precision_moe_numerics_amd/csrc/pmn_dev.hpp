@@ -125,8 +125,9 @@ PMN_DEV void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1)
     for (int r = 0; r < 10; r++) {
         uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
         uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
-        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        // three-way xor in one gfx950 v_bitop3_b32 (truth table 0x96)
+        uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
+        uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
         c[1] = (uint32_t)p1;
         c[3] = (uint32_t)p0;
         c[0] = n0;
