@@ -272,8 +272,6 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                             for (int c = 0; c < 8; c++)
                                 o[c][jj >> 2] = e4m3_sr_scaled_into(o[c][jj >> 2], v[u][c], sr_operand(rw[c >> 1], c & 1),
                                                                     escale[c], (jj + u) & 3);
-                            // one slot at a time: interleaving Philox evaluations only adds live registers
-                            __builtin_amdgcn_sched_barrier(0);
                         }
                     } else {
 #pragma unroll
@@ -288,8 +286,13 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                     if (j < blk.valid) {
                         const int64_t s = blk.s0 + j;
                         float v[8];
-                        if (SRC == SRC_NVFP4) deq8(cw[j], dsc[j], v);
-                        else bf8(xw[j], v);
+                        if (SRC == SRC_NVFP4) {
+                            uint32_t cwj = cw[j];
+                            asm volatile("" : "+v"(cwj));   // recompute rather than keep the amax pass's values
+                            deq8(cwj, dsc[j], v);
+                        } else {
+                            bf8(xw[j], v);
+                        }
                         uint32_t rw[4];
                         rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
 #pragma unroll
