@@ -350,3 +350,21 @@ def test_route_topk(P, I, T, E, k):
     for key in ("ids", "offsets", "gather", "slot_of"):
         assert np.array_equal(npy(r[key]), ref[key]), key
     assert np.allclose(npy(r["gates"]), ref["gates"], rtol=1e-5, atol=1e-7)
+
+
+def test_gemm_bwd_odd_stage_counts_and_half_stages(P, I):
+    """wgrad groups whose padded slot count gives an odd number of 64-slot stages, a half-full
+    last stage, or both (150 -> 160 slots: 3 stages, the last half full; 1 -> 32: 1 half stage;
+    95 -> 96: 2 stages, the last half full; 33 -> 64: 1 full stage)."""
+    counts, N, K = [150, 1, 95, 33], 256, 256
+    d = _moe_small(P, I, counts, N, K, gather_rows=300, seed=95)
+    M = d["M"]
+    dy = I.normal((M, N), 1e-3, 96)
+    da, db, _ = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
+                                       seed=4, rng_stream_a=2, rng_stream_b=3, rng_stream_dy=5)
+    rq, re = O.mxfp8_quantize_rows(dy)
+    rwt, rwte = O.requant_transpose_sr(_ref_q(d["wq"]), seed=4, stream=3)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], stream=6)
+    rxt, rxte = O.requant_transpose_sr(_ref_q(d["xq"]), gather=d["gather"], offsets=d["offsets"], seed=4, stream=2)
+    assert rel_fro(npy(da), O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K)) <= 2e-3
+    assert rel_fro(npy(db), O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K)) <= 2e-3
