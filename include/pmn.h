@@ -193,7 +193,8 @@ int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, ui
  * A: NVFP4 [a_rows x K] with a_rows_per_outer; B: NVFP4 [G*N x K] with b_rows_per_outer.
  * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (for SWIGLU also F % b_rows_per_outer == 0
  * or b_rows_per_outer % N == 0, so w1 and w3 rows keep their own outer scales). M is the number of
- * slots (host value). Codes and scales 16-byte aligned.
+ * slots (host value). Codes, out and out_aux 16-byte aligned, scales 4-byte aligned, out_e8m0
+ * (RHT32_S2F6) 8-byte aligned; PMN_EALIGN otherwise.
  */
 int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                          int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather,

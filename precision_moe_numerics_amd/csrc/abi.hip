@@ -147,7 +147,8 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const 
         return PMN_EINVAL;
     if (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0) return PMN_EINVAL;
     if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
-        !aligned(out, 16) || (out_aux && !aligned(out_aux, 16)))
+        !aligned(out, 16) || (out_aux && !aligned(out_aux, 16)) ||
+        (epilogue == PMN_EPI_RHT32_S2F6 && !aligned(out_e8m0, 8)))
         return PMN_EALIGN;
     if (M == 0) return PMN_OK;
     return status(pmn::launch_gemm_fwd(a_codes, a_scales, a_outer, a_rows_per_outer, gather, b_codes, b_scales,

@@ -41,6 +41,12 @@ constexpr int STAGEB = 2 * TILEB;             // weights + activations
 constexpr int LDSB = 2 * STAGEB;              // two stages
 constexpr int THREADS = 512;                  // 8 wavefronts: 2 along weight rows x 4 along slots
 static_assert(THREADS == 2 * BT, "one staging thread per row of each operand tile");
+// Epilogue: the LDS holds output tiles of 256 slots x 256 bytes (row pitch 272, so the
+// transposed fragment writes of 32 slots fall on 16 distinct bank groups), written out as whole
+// row segments.
+constexpr int OPITCH = 272;
+constexpr int OTILE = BT * OPITCH;
+static_assert(2 * OTILE + BT * 8 <= LDSB, "two output tiles and the E8M0 tile fit in the LDS");
 }  // namespace fwd
 
 struct FwdArgs {
@@ -98,7 +104,8 @@ PMN_DEV void dequant_block_to_lds(const RawStage& r, uint8_t* dst)
 PMN_DEV float silu(float h) { return h / (1.0f + expf(-h)); }
 
 // RHT32 + S2F6 on one 32 x 32 accumulator block whose 32 rows (n) are one aligned chunk:
-// lane l holds column m = l % 32 and rows i = (v/4)*8 + (l/32)*4 + v%4. Butterfly stages
+// lane l holds column m = l % 32 and rows i = (v/4)*8 + (l/32)*4 + v%4. The 32 codes of slot m
+// go to out_row_chunk (the epilogue's LDS tile), its E8M0 byte to e8m0_ptr. Butterfly stages
 // h = 1, 2, 4, 8, 16 in that order: h = 1, 2, 8, 16 pair registers of one lane, h = 4 pairs the
 // two lane halves.
 PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_chunk, uint8_t* e8m0_ptr)
@@ -283,6 +290,101 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
 
     // ---- epilogue: lane holds slot m = (wm*64 + j*32 + lane%32), weight rows of block i
     const int hh = lane >> 5;
+    // copy rows [0, mvalid) of an output tile (256 bytes per slot) to dst + (m0 + row) * pitch
+    auto store_tile = [&](const uint8_t* src, uint8_t* dst, int64_t pitch) {
+#pragma unroll
+        for (int k = 0; k < (BT * 16) / THREADS; k++) {
+            const int q = k * THREADS + tid;
+            const int row = q >> 4, c = q & 15;
+            if (row < mvalid)
+                *reinterpret_cast<uint4*>(dst + (m0 + row) * pitch + c * 16) =
+                    *reinterpret_cast<const uint4*>(src + row * OPITCH + c * 16);
+        }
+    };
+    if (EPI == PMN_EPI_SWIGLU || EPI == PMN_EPI_RHT32_S2F6) {
+        __syncthreads();   // every fragment read of the main loop is done: the LDS holds output tiles
+        uint8_t* const t0 = lds;
+        uint8_t* const t1 = lds + OTILE;
+        uint8_t* const te = lds + 2 * OTILE;
+        float sxs[2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int64_t ml = wm * 64 + j * 32 + (lane & 31);
+            const bool mok = ml < mvalid;
+            const int64_t m = m0 + ml;
+            const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
+            sxs[j] = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
+        }
+        if (EPI == PMN_EPI_SWIGLU) {
+            // tile 0: A = silu(h1) h3 (128 features), tile 1: h1; then tile 0 again: h3
+            const int64_t F = N >> 1;
+            const bool aux = p.out_aux != nullptr;
+#pragma unroll
+            for (int phase = 0; phase < 2; phase++) {
+                if (phase == 1 && !aux) break;
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    const int ml = wm * 64 + j * 32 + (lane & 31);
+#pragma unroll
+                    for (int i = 0; i < 2; i++) {
+                        const int64_t jbase = n0 + wn * 64 + i * 32;       // A column of row 0 of block
+                        const float s1 = sxs[j] * p.b_outer[((int64_t)g * N + jbase) / p.b_rpo];
+                        const float s3 = sxs[j] * p.b_outer[((int64_t)g * N + F + jbase) / p.b_rpo];
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            uint32_t ab[4], b1[4], b3[4];
+#pragma unroll
+                            for (int u = 0; u < 4; u++) {
+                                const float h1 = acc[i][j][4 * q + u] * s1;
+                                const float h3 = acc[i + 2][j][4 * q + u] * s3;
+                                ab[u] = f32_to_bf16_bits(silu(h1) * h3);
+                                b1[u] = f32_to_bf16_bits(h1);
+                                b3[u] = f32_to_bf16_bits(h3);
+                            }
+                            const int off = ml * OPITCH + 2 * (wn * 64 + i * 32 + q * 8 + hh * 4);
+                            if (phase == 0) {
+                                *reinterpret_cast<uint2*>(t0 + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
+                                if (aux) *reinterpret_cast<uint2*>(t1 + off) = make_uint2(b1[0] | (b1[1] << 16), b1[2] | (b1[3] << 16));
+                            } else {
+                                *reinterpret_cast<uint2*>(t0 + off) = make_uint2(b3[0] | (b3[1] << 16), b3[2] | (b3[3] << 16));
+                            }
+                        }
+                    }
+                }
+                __syncthreads();
+                uint8_t* const H = reinterpret_cast<uint8_t*>(p.out_aux);
+                if (phase == 0) {
+                    store_tile(t0, reinterpret_cast<uint8_t*>(p.out) + n0 * 2, F * 2);
+                    if (aux) store_tile(t1, H + n0 * 2, N * 2);
+                } else {
+                    store_tile(t0, H + (F + n0) * 2, N * 2);
+                }
+                if (phase == 0 && aux) __syncthreads();   // tile 0 is rewritten with h3
+            }
+        } else {
+            // RHT32 + S2F6: codes into tile 0 (256 columns of int8), E8M0 into the E8M0 tile
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int ml = wm * 64 + j * 32 + (lane & 31);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int nl = wn * 128 + i * 32;                  // tile column of row 0 of block
+                    const float s = sxs[j] * p.b_outer[((int64_t)g * N + n0 + nl) / p.b_rpo];
+                    f32x16 z;
+#pragma unroll
+                    for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * s;
+                    rht_block_store(z, p.rht_mask, lane, reinterpret_cast<int8_t*>(t0 + ml * OPITCH + nl),
+                                    te + ml * 8 + (nl >> 5));
+                }
+            }
+            __syncthreads();
+            store_tile(t0, reinterpret_cast<uint8_t*>(p.out) + n0, N);
+            if (tid < mvalid)
+                *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + tid) * (N >> 5) + (n0 >> 5)) =
+                    *reinterpret_cast<const uint2*>(te + tid * 8);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; j++) {
         const int64_t ml = wm * 64 + j * 32 + (lane & 31);
@@ -290,64 +392,22 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
         const int64_t m = m0 + ml;
         const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
         const float sx = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
-        if (EPI == PMN_EPI_SWIGLU) {
-            const int64_t F = N >> 1;
 #pragma unroll
-            for (int i = 0; i < 2; i++) {
-                const int64_t jbase = n0 + wn * 64 + i * 32;         // A column of row 0 of block
-                const float s1 = sx * p.b_outer[((int64_t)g * N + jbase) / p.b_rpo];
-                const float s3 = sx * p.b_outer[((int64_t)g * N + F + jbase) / p.b_rpo];
+        for (int i = 0; i < 4; i++) {
+            const int64_t nb = n0 + wn * 128 + i * 32;           // first weight row of block
+            const float s = sx * p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
+            if (mok) {
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    float h1[4], h3[4];
-                    uint32_t ab[4], b1[4], b3[4];
-#pragma unroll
-                    for (int u = 0; u < 4; u++) {
-                        h1[u] = acc[i][j][4 * q + u] * s1;
-                        h3[u] = acc[i + 2][j][4 * q + u] * s3;
-                        ab[u] = f32_to_bf16_bits(silu(h1[u]) * h3[u]);
-                        b1[u] = f32_to_bf16_bits(h1[u]);
-                        b3[u] = f32_to_bf16_bits(h3[u]);
-                    }
-                    if (mok) {
-                        const int64_t col = jbase + q * 8 + hh * 4;
-                        uint16_t* A = reinterpret_cast<uint16_t*>(p.out) + m * F + col;
-                        *reinterpret_cast<uint2*>(A) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                        if (p.out_aux) {
-                            uint16_t* H = reinterpret_cast<uint16_t*>(p.out_aux) + m * N;
-                            *reinterpret_cast<uint2*>(H + col) = make_uint2(b1[0] | (b1[1] << 16), b1[2] | (b1[3] << 16));
-                            *reinterpret_cast<uint2*>(H + F + col) = make_uint2(b3[0] | (b3[1] << 16), b3[2] | (b3[3] << 16));
-                        }
-                    }
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t nb = n0 + wn * 128 + i * 32;           // first weight row of block
-                const float s = sx * p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
-                if (EPI == PMN_EPI_RHT32_S2F6) {
-                    f32x16 z;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * s;
-                    // lanes l and l ^ 32 hold the same slot, so a masked slot masks both halves of
-                    // the butterfly exchange together
-                    if (mok)
-                        rht_block_store(z, p.rht_mask, lane, reinterpret_cast<int8_t*>(p.out) + m * N + nb,
-                                        p.out_e8m0 + m * (N >> 5) + (nb >> 5));
-                } else if (mok) {
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const int64_t col = nb + q * 8 + hh * 4;
-                        float y0 = acc[i][j][4 * q] * s, y1 = acc[i][j][4 * q + 1] * s;
-                        float y2 = acc[i][j][4 * q + 2] * s, y3 = acc[i][j][4 * q + 3] * s;
-                        if (EPI == PMN_EPI_F32) {
-                            *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
-                        } else {
-                            uint2 v = make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
-                                                 f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
-                            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + m * N + col) = v;
-                        }
+                    const int64_t col = nb + q * 8 + hh * 4;
+                    float y0 = acc[i][j][4 * q] * s, y1 = acc[i][j][4 * q + 1] * s;
+                    float y2 = acc[i][j][4 * q + 2] * s, y3 = acc[i][j][4 * q + 3] * s;
+                    if (EPI == PMN_EPI_F32) {
+                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
+                    } else {
+                        uint2 v = make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
+                                             f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
+                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + m * N + col) = v;
                     }
                 }
             }
