@@ -85,6 +85,7 @@ def _declare(L):
         "orc_gemm_nvfp4_grouped": (None, [P, P, P, I64, P, P, P, P, I64, P, I32, I64, I64, P]),
         "orc_gemm_nvfp4_elem": (C.c_double, [P, P, P, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I64]),
         "orc_mxfp8_dot": (C.c_double, [P, P, I64, P, P, I64, I64, I64, I64, I64]),
+        "orc_moe_combine_s2f6": (None, [P, P, I64, I64, U32, P, P, I64, I32, P]),
         "orc_gemm_mxfp8_dgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_gemm_mxfp8_wgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_swiglu": (None, [P, I64, I64, P]),
@@ -298,6 +299,19 @@ def rht32_s2f6_decode(codes, e8m0, mask: int):
     R, Cc = codes.shape
     out = np.zeros((R, Cc), np.float64)
     lib().orc_rht32_s2f6_decode(_p(codes), _p(e8m0), R, Cc, mask, _p(out))
+    return out
+
+
+def moe_combine_s2f6(codes, e8m0, mask: int, slot_of, gates):
+    """Receiver side of the combine: out[t] = sum_i gates[t, i] * decode(codes[slot_of[t, i]]), fp64."""
+    codes = np.ascontiguousarray(codes, np.int8)
+    e8m0 = np.ascontiguousarray(e8m0, np.uint8)
+    so = np.ascontiguousarray(slot_of, np.int32)
+    g = np.ascontiguousarray(gates, np.float32)
+    M, H = codes.shape
+    T, k = so.shape
+    out = np.zeros((T, H), np.float64)
+    lib().orc_moe_combine_s2f6(_p(codes), _p(e8m0), M, H, mask, _p(so), _p(g), T, k, _p(out))
     return out
 
 

@@ -571,6 +571,34 @@ void orc_rht32_s2f6_decode(const int8_t* codes, const uint8_t* e8m0, int64_t row
         }
 }
 
+/*
+ * Combine, receiver side ([AREX S4]: the w2 outputs travel back as RHT32 + S2F6 codes; the
+ * receiver inverts the transform exactly and forms each token's output as the gate-weighted sum
+ * of its routed slots' outputs). For token t and its k choices i: slot slot_of[t*k + i] with gate
+ * gates[t*k + i];  out[t, :] = sum_i gates[t*k+i] * decode(row slot_of[t*k+i]), in fp64, decode
+ * as orc_rht32_s2f6_decode (z^ = c * 2^(e - 127 - 6), x^ = D H z^ / 32).
+ */
+void orc_moe_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t mask,
+                          const int32_t* slot_of, const float* gates, int64_t T, int k, double* out)
+{
+    (void)M;
+#pragma omp parallel
+    {
+        double* row = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+        for (int64_t t = 0; t < T; t++) {
+            for (int64_t c = 0; c < H; c++) out[t * H + c] = 0.0;
+            for (int i = 0; i < k; i++) {
+                const int64_t s = slot_of[t * k + i];
+                orc_rht32_s2f6_decode(codes + s * H, e8m0 + s * (H / 32), 1, H, mask, row);
+                const double g = (double)gates[t * k + i];
+                for (int64_t c = 0; c < H; c++) out[t * H + c] += g * row[c];
+            }
+        }
+        free(row);
+    }
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Grouped GEMMs (fp64 accumulation)  [AREX S2]: expert forward in NVFP4, backward in MXFP8    */
 /* ------------------------------------------------------------------------------------------ */

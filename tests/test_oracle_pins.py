@@ -638,3 +638,49 @@ def test_requant_window_matches_full_output():
     assert np.array_equal(w, full[:, 64:160]) and np.array_equal(we, fe[:, 2:5])
     tail, te = O.requant_window(q, 192, 8, seed=4, stream=2)
     assert np.array_equal(tail, full[:, 192:224]) and np.array_equal(te, fe[:, 6:7])
+
+
+# ------------------------------------------------------------------------------------------
+# combine (receiver side of the w2 output exchange)
+# ------------------------------------------------------------------------------------------
+
+def test_combine_one_hot_code_closed_form():
+    """A chunk whose only nonzero code is c at position 0 decodes to D (c 2^(e-133)) H[:, 0] / 32,
+    and the first Hadamard column is all ones: every value is +-c 2^(e-138), signed by the mask."""
+    H, mask = 64, 0x80000003
+    codes = np.zeros((3, H), np.int8)
+    e8m0 = np.full((3, H // 32), 127, np.uint8)
+    codes[1, 32] = -100
+    e8m0[1, 1] = 130
+    slot_of = np.array([[1]], np.int32)
+    out = O.moe_combine_s2f6(codes, e8m0, mask, slot_of, np.array([[0.75]], np.float32))
+    D = np.array([-1.0 if (mask >> j) & 1 else 1.0 for j in range(32)])
+    assert np.all(out[0, :32] == 0)
+    assert np.array_equal(out[0, 32:], 0.75 * D * (-100.0 * 2.0 ** (130 - 138)))
+
+
+def test_combine_round_trip_and_gate_linearity():
+    """Slots that carry a token's rows scaled by its gates: the combine returns their weighted sum
+    within the S2F6 error bound of each slot; duplicated routes add their gates."""
+    rng = np.random.default_rng(21)
+    T, k, H, mask = 24, 3, 128, 0x13579BDF
+    M = T * k
+    y = (rng.standard_normal((M, H)) * np.exp(rng.uniform(-6, 6, (M, 1)))).astype(np.float32)
+    codes, e = O.rht32_s2f6_quantize(y, mask)
+    perm = rng.permutation(M).astype(np.int32).reshape(T, k)
+    gates = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    out = O.moe_combine_s2f6(codes, e, mask, perm, gates)
+    ref = np.einsum("tk,tkh->th", gates.astype(np.float64), y.astype(np.float64)[perm])
+    # per slot and chunk the decode error is at most 2^(e-127)/128 in the 2-norm
+    bound = (2.0 ** (e.astype(np.float64) - 127) / 128)[perm]                  # [T, k, H/32]
+    err = np.sqrt(((out - ref) ** 2).reshape(T, H // 32, 32).sum(-1))
+    assert np.all(err <= (gates[..., None] * bound).sum(1) * (1 + 1e-6))
+    # two routes to one slot behave as one route with the summed gate
+    dup = np.stack([perm[:, 0], perm[:, 0]], 1)
+    g2 = np.stack([gates[:, 0], gates[:, 1]], 1)
+    one = O.moe_combine_s2f6(codes, e, mask, perm[:, :1], (gates[:, 0] + gates[:, 1])[:, None])
+    assert np.allclose(O.moe_combine_s2f6(codes, e, mask, dup, g2), one, rtol=1e-6, atol=0)
+    # k = 1 with gate 1 is the plain decode, un-permuted
+    dec = O.rht32_s2f6_decode(codes, e, mask)
+    assert np.array_equal(O.moe_combine_s2f6(codes, e, mask, perm[:, :1], np.ones((T, 1), np.float32)),
+                          dec[perm[:, 0]])
