@@ -16,6 +16,9 @@ Also reported: the memory-bound quantizer workload (8192 x 7168 activations, 0.5
 nvfp4_quantize with 4/6 and requant_transpose_sr_mxfp8 of its output, each timed over rotating
 input buffers larger than the 256 MB Infinity Cache, as GB/s of algorithmic bytes.
 
+Also reported: the receiver side of the combine (moe_combine_s2f6) on the routed shape, 16384
+tokens with top-8 of 32 experts gathered back from 131072 S2F6 rows of hidden 4096, as GB/s.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ep48|moe32]
 """
 from __future__ import annotations
@@ -194,6 +197,36 @@ def quantizer_workload(P, I, torch, dev, iters):
     return res
 
 
+def combine_workload(P, I, torch, dev, iters):
+    """GB/s of moe_combine_s2f6 on the routed shape (16384 tokens, top-8 of 32 experts, 131072 slot
+    rows of hidden 4096): routing on the device from the seeded logits, two S2F6 payloads of
+    553 MB each used in turn so the Infinity Cache cannot serve them."""
+    sh = I.MOE32
+    T, k, H = sh.tokens, sh.top_k, sh.hidden
+    M = T * k
+    r = P.moe_route_topk(I.moe_logits(sh, dev), k)
+    so, gates = r["slot_of"], r["gates"]
+    mask = I.sign_mask(sh.seeds["rht"])
+    pay = [I.s2f6_payload(M, H, sh.seeds["payload"] + i, dev) for i in range(2)]
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for i in range(3):
+        P.moe_combine_s2f6(*pay[i % 2], mask, so, gates, out=out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        P.moe_combine_s2f6(*pay[i % 2], mask, so, gates, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    # per token: k rows of H codes + H/32 E8M0 bytes, k slot indices and gates; H bf16 out
+    nbytes = T * (k * (H + H // 32) + 8 * k + 2 * H)
+    del pay
+    return dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, tokens=T, top_k=k, hidden=H,
+                slots=M, frac_of_8TBs=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+
+
 def cpu_baseline(I, shape):
     """The CPU oracle (as it stands) on a bounded sample of the same step: 16 slots of one expert
     through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
@@ -306,6 +339,9 @@ def main():
         quant[k]["frac_of_8TBs"] = quant[k]["gbs"] / PEAK_HBM_GBS
         quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
 
+    comb = combine_workload(P, I, torch, dev, args.quant_iters)
+    comb["frac_of_measured_copy"] = comb["gbs"] / quant["hbm_copy_gbs"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(I, shape)
@@ -320,7 +356,7 @@ def main():
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
             "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
-            "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant,
+            "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant, "combine_workload": comb,
             "wall_s_timed": wall}
     print(json.dumps(line))
 

@@ -260,6 +260,28 @@ int swiglu_bwd(const float* da, const void* h13, int64_t M, int64_t F, void* dh1
 int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
                    int64_t* offsets, int32_t* gather_token, int32_t* slot_of, pmn_stream_t stream);
 
+/* ------------------------------------------------------------------------------------------ */
+/* Combine, receiver side   [AREX] "计算提速后,NVLink 通信成了新瓶颈" (expert outputs return to  */
+/* their tokens as RHT32 + S2F6 rows; the receiver inverts the transform exactly and weights   */
+/* each of a token's k expert outputs by its gate).                                            */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * codes int8 [M x H] and e8m0 uint8 [M x H/32]: the w2 outputs of M routed slots in the form
+ * moe_grouped_gemm_fwd(PMN_EPI_RHT32_S2F6) and rht32_s2f6_quantize write, with the same
+ * rht_sign_mask. slot_of int32 [T x k] names, for token t and its choice j, the slot that holds
+ * its expert output (moe_route_topk's slot_of); gates fp32 [T x k] are the weights.
+ *   out bf16 [T x H]:  out[t, :] = sum_j gates[t, j] * decode(slot_of[t, j]),
+ *   decode(s) per 32-chunk:  D H (codes * 2^(e8m0 - 133)) / 32   (the exact inverse transform).
+ * The sum is taken in fp32 on the scaled codes and transformed once (decode is linear); the
+ * result is rounded once to bf16, nearest even. Values of slot_of outside [0, M) are not read
+ * and add nothing (M = 0 gives zeros). H % 32 == 0 and 1 <= k <= 64 (PMN_ESHAPE); codes and out
+ * 16-byte aligned (PMN_EALIGN). T = 0 launches nothing. All pointers are device pointers.
+ */
+int moe_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t rht_sign_mask,
+                     const int32_t* slot_of, const float* gates, int64_t T, int k, void* out,
+                     pmn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

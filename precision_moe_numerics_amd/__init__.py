@@ -34,6 +34,7 @@ _SIGS = {
                                    U32, U32, U32, P, P, P, SZ, P]),
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
+    "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
 }
 
 ABI_FUNCTIONS = tuple(n for n in _SIGS if not n.startswith("pmn_"))
@@ -273,3 +274,19 @@ def moe_route_topk(logits: torch.Tensor, k: int):
     _check(_lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(gates), _ptr(offsets), _ptr(gather),
                                _ptr(slot_of), _stream()), "moe_route_topk")
     return dict(ids=ids, gates=gates, offsets=offsets, gather=gather, slot_of=slot_of)
+
+
+def moe_combine_s2f6(codes: torch.Tensor, e8m0: torch.Tensor, sign_mask: int, slot_of: torch.Tensor,
+                     gates: torch.Tensor, out=None):
+    """Receiver side of the combine: bf16 [T x H], row t = sum_j gates[t, j] * decode(codes[slot_of[t, j]])."""
+    M, H = codes.shape
+    assert codes.dtype == torch.int8 and e8m0.dtype == torch.uint8 and tuple(e8m0.shape) == (M, H // 32)
+    assert slot_of.dtype == torch.int32 and gates.dtype == torch.float32
+    assert codes.is_contiguous() and e8m0.is_contiguous() and slot_of.is_contiguous() and gates.is_contiguous()
+    T, k = gates.shape
+    assert slot_of.numel() == T * k
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=codes.device)
+    _check(_lib.moe_combine_s2f6(_ptr(codes), _ptr(e8m0), M, H, sign_mask & 0xFFFFFFFF, _ptr(slot_of), _ptr(gates),
+                                 T, k, _ptr(out), _stream()), "moe_combine_s2f6")
+    return out

@@ -236,4 +236,16 @@ int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, f
     return status(pmn::launch_route(logits, T, E, k, ids, gates, offsets, gather_token, slot_of, hs(stream)));
 }
 
+int moe_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t rht_sign_mask,
+                     const int32_t* slot_of, const float* gates, int64_t T, int k, void* out,
+                     pmn_stream_t stream)
+{
+    if (M < 0 || H < 0 || H % 32 != 0 || T < 0 || k < 1 || k > 64) return PMN_ESHAPE;
+    if (T == 0 || H == 0) return PMN_OK;
+    if (!slot_of || !gates || !out || (M > 0 && (!codes || !e8m0))) return PMN_EINVAL;
+    if (!aligned(codes, 16) || !aligned(out, 16)) return PMN_EALIGN;
+    return status(pmn::launch_combine_s2f6(codes, e8m0, M, H, rht_sign_mask, slot_of, gates, T, k,
+                                           static_cast<uint16_t*>(out), hs(stream)));
+}
+
 }  // extern "C"

@@ -14,7 +14,13 @@ Workloads (all synthetic; the pages measure on no dataset):
                   logits); X ~ N(0,1); w1, w3 [F x H], w2 [H x F] ~ N(0, 0.02); dY ~ N(0, 1e-3).
   ep48            48 local experts, 65536 routed slots with Zipf(s = 1.1) loads, H = 7168,
                   F = 2048; X_recv ~ StudentT(nu=4); W ~ N(0, 0.02); dY ~ N(0, 1e-3).
+  combine         the receive side on moe32's routing: 131072 slot rows of S2F6 codes [x 4096]
+                  with one E8M0 byte per 32 codes, gathered back to 16384 tokens by top-8 gates.
 Student-t samples are drawn as Z / sqrt(V / nu) with V a sum of nu squared normals.
+S2F6 payload rows (the w2 outputs after the 32-point transform) are drawn directly as codes:
+c = clamp(round(32 N(0,1)), -127, 127), so a 32-chunk's largest |c| is typically 60..110, near the
+top of the code range as the E8M0 rule places it; E8M0 = 123 + round(2 N(0,1)) per row +
+round(N(0,1)) per chunk, clamped to [100, 150] (values of order 2^-4, spread over rows and chunks).
 """
 from __future__ import annotations
 
@@ -103,7 +109,7 @@ class MoEShape:
 
 
 MOE32 = MoEShape("moe32", experts=32, hidden=4096, ffn=1536, tokens=16384, top_k=8,
-                 seeds=dict(x=300, w=301, logits=302, dy=400, sr=2, rht=3))
+                 seeds=dict(x=300, w=301, logits=302, dy=400, sr=2, rht=3, payload=303))
 EP48 = MoEShape("ep48", experts=48, hidden=7168, ffn=2048, slots=65536, zipf_s=1.1, x_nu=4,
                 seeds=dict(x=500, w=501, dy=502, sr=5, rht=3))
 
@@ -137,3 +143,14 @@ def moe_loads(shape: MoEShape):
 
 def moe_grad(shape: MoEShape, slots: int, device="cpu"):
     return normal((slots, shape.hidden), 1e-3, shape.seeds["dy"], device)
+
+
+def s2f6_payload(rows: int, hidden: int, seed: int, device="cpu"):
+    """int8 codes [rows x hidden] and uint8 E8M0 [rows x hidden/32] of S2F6 payload rows."""
+    g = _gen(seed, device)
+    codes = torch.randn((rows, hidden), generator=g, device=device, dtype=torch.float32).mul_(32.0).round_()
+    codes = codes.clamp_(-127, 127).to(torch.int8)
+    row = torch.randn((rows, 1), generator=g, device=device, dtype=torch.float32).mul_(2.0).round_()
+    chunk = torch.randn((rows, hidden // 32), generator=g, device=device, dtype=torch.float32).round_()
+    e8m0 = (123.0 + row + chunk).clamp_(100, 150).to(torch.uint8)
+    return codes, e8m0
