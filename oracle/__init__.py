@@ -86,6 +86,7 @@ def _declare(L):
         "orc_gemm_nvfp4_elem": (C.c_double, [P, P, P, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I64]),
         "orc_mxfp8_dot": (C.c_double, [P, P, I64, P, P, I64, I64, I64, I64, I64]),
         "orc_moe_combine_s2f6": (None, [P, P, I64, I64, U32, P, P, I64, I32, P]),
+        "orc_s2f6_quantize": (None, [P, I64, I64, P, P]),
         "orc_gemm_mxfp8_dgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_gemm_mxfp8_wgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_swiglu": (None, [P, I64, I64, P]),
@@ -300,6 +301,23 @@ def rht32_s2f6_decode(codes, e8m0, mask: int):
     out = np.zeros((R, Cc), np.float64)
     lib().orc_rht32_s2f6_decode(_p(codes), _p(e8m0), R, Cc, mask, _p(out))
     return out
+
+
+def s2f6_quantize(y):
+    """Plain per-32 S2F6 (no transform): codes int8 [R, C], E8M0 [R, C/32]."""
+    y = np.ascontiguousarray(y, np.float32)
+    R, Cc = y.shape
+    codes = np.zeros((R, Cc), np.int8)
+    e = np.zeros((R, Cc // 32), np.uint8)
+    lib().orc_s2f6_quantize(_p(y), R, Cc, _p(codes), _p(e))
+    return codes, e
+
+
+def s2f6_dequantize(codes, e8m0):
+    """fp64 values c 2^(e - 127 - 6) of plain S2F6 blocks."""
+    c = np.asarray(codes, np.float64)
+    R, Cc = c.shape
+    return (c.reshape(R, Cc // 32, 32) * 2.0 ** (np.asarray(e8m0, np.float64) - 133)[..., None]).reshape(R, Cc)
 
 
 def moe_combine_s2f6(codes, e8m0, mask: int, slot_of, gates):

@@ -552,6 +552,19 @@ void orc_rht32_s2f6_quantize(const float* y, int64_t rows, int64_t cols, uint32_
         }
 }
 
+/*
+ * Plain block-scaled S2F6 without the transform (the ablation of [AREX S4]: outliers are what the
+ * transform is there for): each aligned 32-chunk of y goes through the same block step,
+ * codes c = RNE(y 2^(6 - e)), E8M0 by the smallest-e rule with M = 127/64.
+ */
+void orc_s2f6_quantize(const float* y, int64_t rows, int64_t cols, int8_t* codes, uint8_t* e8m0)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t b = 0; b < cols / 32; b++)
+            orc_s2f6_block(y + r * cols + b * 32, codes + r * cols + b * 32, e8m0 + r * (cols / 32) + b);
+}
+
 /* Decode (receiver side): z^ = c * 2^(e - 6); x^ = D H z^ / 32, in fp64. */
 void orc_rht32_s2f6_decode(const int8_t* codes, const uint8_t* e8m0, int64_t rows, int64_t cols,
                            uint32_t mask, double* out)

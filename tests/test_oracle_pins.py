@@ -684,3 +684,22 @@ def test_combine_round_trip_and_gate_linearity():
     dec = O.rht32_s2f6_decode(codes, e, mask)
     assert np.array_equal(O.moe_combine_s2f6(codes, e, mask, perm[:, :1], np.ones((T, 1), np.float32)),
                           dec[perm[:, 0]])
+
+
+def test_plain_s2f6_grid_values_round_trip_and_bound():
+    """Plain per-32 S2F6: values on the grid (largest |c| in [64, 127]) come back exactly with the
+    scale they were built with; others are within half a step, 2^(e-127)/128."""
+    rng = np.random.default_rng(22)
+    c = rng.integers(-127, 128, (6, 64))
+    c[:, 0] = 127
+    c[:, 32] = -64
+    s = rng.integers(-20, 20, (6, 2))
+    y = (c.reshape(6, 2, 32) / 64.0 * 2.0 ** s[..., None]).reshape(6, 64).astype(np.float32)
+    codes, e = O.s2f6_quantize(y)
+    assert np.array_equal(codes, c) and np.array_equal(e.astype(int), s + 127)
+    assert np.array_equal(O.s2f6_dequantize(codes, e), y.astype(np.float64))
+    y = (rng.standard_t(3, (40, 256)) * np.exp(rng.uniform(-10, 10, (40, 1)))).astype(np.float32)
+    codes, e = O.s2f6_quantize(y)
+    half = np.repeat(2.0 ** (e.astype(np.float64) - 127) / 128, 32, axis=1)
+    assert np.all(np.abs(O.s2f6_dequantize(codes, e) - y) <= half)
+    assert np.all(np.abs(codes.astype(int)).reshape(40, 8, 32).max(-1) >= 64)
