@@ -87,6 +87,7 @@ def _declare(L):
         "orc_mxfp8_dot": (C.c_double, [P, P, I64, P, P, I64, I64, I64, I64, I64]),
         "orc_moe_combine_s2f6": (None, [P, P, I64, I64, U32, P, P, I64, I32, P]),
         "orc_s2f6_quantize": (None, [P, I64, I64, P, P]),
+        "orc_gemm_mxfp8_fwd": (None, [P, P, P, P, P, P, I32, I64, I64, P]),
         "orc_gemm_mxfp8_dgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_gemm_mxfp8_wgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_swiglu": (None, [P, I64, I64, P]),
@@ -359,6 +360,17 @@ def gemm_nvfp4_elems(xq, wq, offsets, N, K, rows, cols, gather=None):
     return np.array([f(_p(arrs[0]), _p(arrs[1]), _p(xo), xq["rows_per_outer"], _p(g), _p(warr[0]), _p(warr[1]),
                        _p(wo), wq["rows_per_outer"], _p(o), len(o) - 1, N, K, int(s), int(n))
                      for s, n in zip(rows, cols)])
+
+
+def gemm_mxfp8_fwd(xq, xe, wq, we, offsets, N, K, gather=None):
+    """MXFP8 grouped forward, fp64: Y[s, n] = sum_k X[gather[s] or s, k] W[g N + n, k]."""
+    o = np.ascontiguousarray(offsets, np.int64)
+    G = len(o) - 1
+    g = None if gather is None else np.ascontiguousarray(gather, np.int32)
+    Y = np.zeros((int(o[-1]), N), np.float64)
+    arrs = [np.ascontiguousarray(a) for a in (xq, xe, wq, we)]
+    lib().orc_gemm_mxfp8_fwd(_p(arrs[0]), _p(arrs[1]), _p(g), _p(arrs[2]), _p(arrs[3]), _p(o), G, N, K, _p(Y))
+    return Y
 
 
 def gemm_mxfp8_dgrad(dq, de, wt, wte, offsets, N, K):

@@ -687,6 +687,26 @@ double orc_mxfp8_dot(const uint8_t* a, const uint8_t* ae, int64_t lda, const uin
 }
 
 /*
+ * MXFP8 forward of one grouped layer ([AREX S5]: the last 16.6% of the layers keep MXFP8 instead
+ * of NVFP4): Y[s, n] = sum_k X[row(s), k] * W_g[n, k] for slot s of group g, with X quantized
+ * row-wise (xq [x_rows x K], xe [x_rows x K/32]), row(s) = gather[s] or s, and W quantized
+ * row-wise (wq [G*N x K], we [G*N x K/32], expert g in rows g*N .. g*N+N-1). fp64 output.
+ */
+void orc_gemm_mxfp8_fwd(const uint8_t* xq, const uint8_t* xe, const int32_t* gather, const uint8_t* wq,
+                        const uint8_t* we, const int64_t* offsets, int G, int64_t N, int64_t K, double* Y)
+{
+    int64_t M = offsets[G];
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t s = 0; s < M; s++) {
+        int g = 0;
+        while (offsets[g + 1] <= s) g++;
+        const int64_t r = gather ? (int64_t)gather[s] : s;
+        for (int64_t n = 0; n < N; n++)
+            Y[s * N + n] = orc_mxfp8_dot(xq, xe, K, wq, we, K, r, (int64_t)g * N + n, 0, K);
+    }
+}
+
+/*
  * dgrad of one grouped layer: dX[s, k] = sum_n dY[s, n] * W_g[n, k], with dY quantized row-wise
  * (dq [M x N], de [M x N/32]) and W_g^T requantized (wt [K x G*N], wte [K x G*N/32]; group g's
  * columns g*N .. g*N+N-1).

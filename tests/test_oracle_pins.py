@@ -703,3 +703,50 @@ def test_plain_s2f6_grid_values_round_trip_and_bound():
     half = np.repeat(2.0 ** (e.astype(np.float64) - 127) / 128, 32, axis=1)
     assert np.all(np.abs(O.s2f6_dequantize(codes, e) - y) <= half)
     assert np.all(np.abs(codes.astype(int)).reshape(40, 8, 32).max(-1) >= 64)
+
+
+def _e4m3_by_torch(codes, e8m0):
+    """MXFP8 values decoded by torch's float8_e4m3fn type (independent of the oracle's decoder)."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    R, Cc = c.shape
+    return (c.reshape(R, Cc // 32, 32) * 2.0 ** (np.asarray(e8m0, np.float64) - 127)[..., None]).reshape(R, Cc)
+
+
+def test_mxfp8_forward_vs_library_decode_and_matmul():
+    """Grouped MXFP8 forward with a gather, an empty group and ragged groups, against torch's E4M3
+    decode and a numpy matmul per group."""
+    rng = np.random.default_rng(23)
+    G, N, K, T = 4, 64, 96, 50
+    offsets = np.array([0, 17, 17, 60, 71], np.int64)
+    M = int(offsets[-1])
+    gather = rng.integers(0, T, M).astype(np.int32)
+    x = bf16(rng.standard_t(4, (T, K)))
+    w = bf16(rng.standard_normal((G * N, K)) * 0.02)
+    xq, xe = O.mxfp8_quantize_rows(x)
+    wq, we = O.mxfp8_quantize_rows(w)
+    Y = O.gemm_mxfp8_fwd(xq, xe, wq, we, offsets, N, K, gather=gather)
+    xv, wv = _e4m3_by_torch(xq, xe), _e4m3_by_torch(wq, we)
+    for g in range(G):
+        s0, s1 = offsets[g], offsets[g + 1]
+        ref = xv[gather[s0:s1]] @ wv[g * N:(g + 1) * N].T
+        assert np.allclose(Y[s0:s1], ref, rtol=1e-12, atol=1e-300)
+    # without a gather the slot is the row (one group of 41 slots)
+    Y2 = O.gemm_mxfp8_fwd(xq[:41], xe[:41], wq, we, [0, 41], N, K)
+    assert np.allclose(Y2, xv[:41] @ wv[:N].T, rtol=1e-12, atol=1e-300)
+
+
+def test_mxfp8_forward_one_hot_closed_form():
+    """X all ones (each quantizes exactly: 1 = 256 * 2^-8) and W rows one-hot with E4M3-exact values:
+    Y[s, n] is the nonzero value of W row g N + n."""
+    G, N, K = 2, 32, 64
+    offsets = np.array([0, 5, 9], np.int64)
+    x = bf16(np.ones((9, K)))
+    vals = np.array([1.5, -0.25, 3.0, -448.0, 0.0078125, 6.0, -1.0, 2.75] * 8)   # 64 rows
+    w = np.zeros((G * N, K))
+    w[np.arange(G * N), np.arange(G * N) % K] = vals
+    xq, xe = O.mxfp8_quantize_rows(x)
+    wq, we = O.mxfp8_quantize_rows(bf16(w))
+    Y = O.gemm_mxfp8_fwd(xq, xe, wq, we, offsets, N, K)
+    for s in range(9):
+        g = 0 if s < 5 else 1
+        assert np.array_equal(Y[s], vals[g * N:(g + 1) * N])
