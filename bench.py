@@ -16,6 +16,9 @@ Also reported: the memory-bound quantizer workload (8192 x 7168 activations, 0.5
 nvfp4_quantize with 4/6 and requant_transpose_sr_mxfp8 of its output, each timed over rotating
 input buffers larger than the 256 MB Infinity Cache, as GB/s of algorithmic bytes.
 
+Also reported: the MXFP8 forward of the layers that keep MXFP8, on the same layer shape (w13 with
+SwiGLU, w2 with RHT32 + S2F6, each call including its MXFP8 quantization), as TFLOP/s.
+
 Also reported: the receiver side of the combine (moe_combine_s2f6) on the routed shape, 16384
 tokens with top-8 of 32 experts gathered back from 131072 S2F6 rows of hidden 4096, as GB/s.
 
@@ -227,6 +230,46 @@ def combine_workload(P, I, torch, dev, iters):
                 slots=M, frac_of_8TBs=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
 
 
+def mxfp8_forward_workload(P, I, torch, layer, iters):
+    """The MXFP8 forward of the layers that keep MXFP8, on the same layer shape: w13 with the
+    SwiGLU epilogue and w2 with the RHT32 + S2F6 epilogue, each call including the row-wise MXFP8
+    quantization of its activations and weights. TFLOP/s of the GEMMs against the fp8 peak."""
+    M, E, H, F = layer.M, layer.E, layer.H, layer.F
+    A = I.student_t((M, F), 4, 0.05, 611, layer.x.device)
+    ws13 = torch.empty((P._lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, E, 2 * F, H),), dtype=torch.uint8,
+                       device=A.device)
+    ws2 = torch.empty((P._lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, E, H, F),), dtype=torch.uint8,
+                      device=A.device)
+    a_out = torch.empty((M, F), dtype=torch.bfloat16, device=A.device)
+    h13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=A.device)
+    c = torch.empty((M, H), dtype=torch.int8, device=A.device)
+    ce = torch.empty((M, H // 32), dtype=torch.uint8, device=A.device)
+
+    def w13():
+        P.moe_grouped_gemm_fwd_mxfp8(layer.x, layer.w13, layer.offsets, M, 2 * F, P.EPI_SWIGLU, gather=layer.gather,
+                                     workspace=ws13, out=a_out, out_aux=h13)
+
+    def w2():
+        P.moe_grouped_gemm_fwd_mxfp8(A, layer.w2, layer.offsets, M, H, P.EPI_RHT32_S2F6, rht_sign_mask=layer.mask,
+                                     workspace=ws2, out=c, out_e8m0=ce)
+    res = {}
+    for name, fn, flops in (("w13+swiglu", w13, 2.0 * M * 2 * F * H), ("w2+rht32_s2f6", w2, 2.0 * M * H * F)):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        t = flops / (ms * 1e-3) / 1e12
+        res[name] = dict(ms_incl_quant=ms, tflops_incl_quant=t, frac_fp8_peak=t / PEAK_FP8_TFLOPS)
+    del ws13, ws2, A
+    return res
+
+
 def cpu_baseline(I, shape):
     """The CPU oracle (as it stands) on a bounded sample of the same step: 16 slots of one expert
     through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
@@ -339,6 +382,7 @@ def main():
         quant[k]["frac_of_8TBs"] = quant[k]["gbs"] / PEAK_HBM_GBS
         quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
 
+    mx8 = mxfp8_forward_workload(P, I, torch, layer, max(args.quant_iters // 4, 3))
     comb = combine_workload(P, I, torch, dev, args.quant_iters)
     comb["frac_of_measured_copy"] = comb["gbs"] / quant["hbm_copy_gbs"]
 
@@ -357,6 +401,7 @@ def main():
             "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
             "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
             "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant, "combine_workload": comb,
+            "mxfp8_forward": mx8,
             "wall_s_timed": wall}
     print(json.dumps(line))
 

@@ -203,6 +203,31 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const 
                          int64_t N, int64_t K, int epilogue, uint32_t rht_sign_mask, void* out,
                          uint8_t* out_e8m0, void* out_aux, pmn_stream_t stream);
 
+/*
+ * Workspace bytes moe_grouped_gemm_fwd_mxfp8 needs for these sizes (host call).
+ */
+size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, int64_t K);
+
+/*
+ * MXFP8 forward of one grouped layer, for the layers that keep MXFP8 instead of NVFP4
+ * ([AREX] "配方的代价:预训练约 2% 的计算效率": the last 16.6% of the layers):
+ *   Y[s, n] = sum_k X8(row_s, k) W8(g*N + n, k)   (fp32 accumulation)
+ * where X8 and W8 are the row-wise MXFP8 quantizations (E4M3 round to nearest even, one E8M0 per
+ * 32 values along K, the smallest scale that does not saturate -- as mxfp8_quantize with
+ * PMN_ROWWISE and PMN_RNE) of x bf16 [x_rows x K] and w bf16 [G*N x K], s a slot of group g
+ * (offsets, device int64 [G+1]) and row_s = gather[s] (or s). The epilogues are those of
+ * moe_grouped_gemm_fwd (SWIGLU: rows 0..F-1 of each expert are w1, F..2F-1 are w3). N % 256 == 0,
+ * K % 32 == 0. x, w, out, out_aux and the workspace 16-byte aligned, out_e8m0 8-byte aligned
+ * (PMN_EALIGN). Workspace (>= moe_grouped_gemm_fwd_mxfp8_workspace_size) holds, in order, each
+ * part rounded up to 256 bytes: X8 codes [M x K] in slot order and E8M0 [K/32 x Pb] (slot s of
+ * group g at column padded_offsets[g] + s - offsets[g]); W8 codes [G*N x K] and E8M0
+ * [K/32 x G*N]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M, G).
+ */
+int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gather, const void* w,
+                               const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int epilogue,
+                               uint32_t rht_sign_mask, void* out, uint8_t* out_e8m0, void* out_aux,
+                               void* workspace, size_t workspace_bytes, pmn_stream_t stream);
+
 #define PMN_BWD_DGRAD 1
 #define PMN_BWD_WGRAD 2
 

@@ -32,6 +32,8 @@ _SIGS = {
     "moe_grouped_gemm_bwd_workspace_size": (SZ, [I64, I32, I64, I64, I32]),
     "moe_grouped_gemm_bwd": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32, U64,
                                    U32, U32, U32, P, P, P, SZ, P]),
+    "moe_grouped_gemm_fwd_mxfp8_workspace_size": (SZ, [I64, I32, I64, I64]),
+    "moe_grouped_gemm_fwd_mxfp8": (I32, [P, I64, P, P, P, I32, I64, I64, I64, I32, U32, P, P, P, P, SZ, P]),
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
     "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
@@ -216,6 +218,43 @@ def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N:
 
 def moe_grouped_gemm_bwd_workspace_size(M: int, G: int, N: int, K: int, flags: int) -> int:
     return _lib.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
+
+
+def moe_grouped_gemm_fwd_mxfp8(x: torch.Tensor, w: torch.Tensor, offsets: torch.Tensor, M: int, N: int,
+                               epilogue: int = EPI_F32, gather: Optional[torch.Tensor] = None,
+                               rht_sign_mask: int = 0, save_h13: bool = False, workspace=None, out=None,
+                               out_e8m0=None, out_aux=None):
+    """MXFP8 forward (row-wise RNE quantization of x and w inside the call); returns the
+    epilogue's outputs as moe_grouped_gemm_fwd does."""
+    assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16
+    K = x.shape[1]
+    G = offsets.numel() - 1
+    dev = w.device
+    if workspace is None:
+        workspace = torch.empty((_lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, G, N, K),), dtype=torch.uint8,
+                                device=dev)
+    if out is None:
+        if epilogue == EPI_F32:
+            out = torch.empty((M, N), dtype=torch.float32, device=dev)
+        elif epilogue == EPI_BF16:
+            out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        elif epilogue == EPI_SWIGLU:
+            out = torch.empty((M, N // 2), dtype=torch.bfloat16, device=dev)
+        else:
+            out = torch.empty((M, N), dtype=torch.int8, device=dev)
+    if epilogue == EPI_RHT32_S2F6 and out_e8m0 is None:
+        out_e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
+    if epilogue == EPI_SWIGLU and save_h13 and out_aux is None:
+        out_aux = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _check(_lib.moe_grouped_gemm_fwd_mxfp8(_ptr(x), x.shape[0], _ptr(gather), _ptr(w), _ptr(offsets), G, M, N, K,
+                                           epilogue, rht_sign_mask & 0xFFFFFFFF, _ptr(out), _ptr(out_e8m0),
+                                           _ptr(out_aux), _ptr(workspace), workspace.numel(), _stream()),
+           "moe_grouped_gemm_fwd_mxfp8")
+    if epilogue == EPI_RHT32_S2F6:
+        return out, out_e8m0
+    if epilogue == EPI_SWIGLU:
+        return out, out_aux
+    return out
 
 
 def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N: int,

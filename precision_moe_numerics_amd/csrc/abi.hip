@@ -37,6 +37,26 @@ BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K)
     return L;
 }
 
+struct FwdMx8Layout {
+    size_t xq, xe, wq, we, po, total;
+    int64_t Pb;
+};
+
+FwdMx8Layout fwd_mx8_layout(int64_t M, int G, int64_t N, int64_t K)
+{
+    FwdMx8Layout L{};
+    L.Pb = pmn_padded_bound(M, G);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
+    L.xq = take((size_t)(M * K));
+    L.xe = take((size_t)(K / 32 * L.Pb));
+    L.wq = take((size_t)((int64_t)G * N * K));
+    L.we = take((size_t)(K / 32 * (int64_t)G * N));
+    L.po = take((size_t)(G + 1) * sizeof(int64_t));
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -216,6 +236,45 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     return PMN_OK;
+}
+
+size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, int64_t K)
+{
+    if (M < 0 || G < 1 || N <= 0 || K <= 0) return 0;
+    return fwd_mx8_layout(M, G, N, K).total;
+}
+
+int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gather, const void* w,
+                               const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int epilogue,
+                               uint32_t rht_sign_mask, void* out, uint8_t* out_e8m0, void* out_aux,
+                               void* workspace, size_t workspace_bytes, pmn_stream_t stream)
+{
+    if (epilogue < PMN_EPI_F32 || epilogue > PMN_EPI_RHT32_S2F6) return PMN_EINVAL;
+    if (G < 1 || M < 0 || x_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 32 != 0) return PMN_ESHAPE;
+    if (!gather && M > x_rows) return PMN_ESHAPE;
+    if (!offsets || !w || !out || (M > 0 && !x)) return PMN_EINVAL;
+    if (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0) return PMN_EINVAL;
+    const FwdMx8Layout L = fwd_mx8_layout(M, G, N, K);
+    if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
+    if (!aligned(workspace, 16) || !aligned(w, 16) || (x && !aligned(x, 16)) || !aligned(out, 16) ||
+        (out_aux && !aligned(out_aux, 16)) || (out_e8m0 && !aligned(out_e8m0, 8)))
+        return PMN_EALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const hipStream_t s = hs(stream);
+    int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
+    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s);
+    if (e != hipSuccess) return PMN_ELAUNCH;
+    // W row-wise (RNE), E8M0 k-block-major [K/32 x G*N]
+    e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(w), (int64_t)G * N, K, false, 0, 0, ws + L.wq,
+                               ws + L.we, nullptr, 0, nullptr, (int64_t)G * N, s);
+    if (e != hipSuccess) return PMN_ELAUNCH;
+    // X in slot order (row s = x[gather[s]]), E8M0 k-block-major at padded slot columns
+    e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(x), M, K, false, 0, 0, ws + L.xq, ws + L.xe, offsets, G,
+                               po, L.Pb, s, gather);
+    if (e != hipSuccess) return PMN_ELAUNCH;
+    e = pmn::launch_mxfp8_fwd(ws + L.wq, ws + L.we, ws + L.xq, ws + L.xe, offsets, po, L.Pb, G, M, N, K, epilogue,
+                              rht_sign_mask, out, out_e8m0, out_aux, s);
+    return e == hipSuccess ? PMN_OK : PMN_ELAUNCH;
 }
 
 int swiglu_bwd(const float* da, const void* h13, int64_t M, int64_t F, void* dh13, pmn_stream_t stream)

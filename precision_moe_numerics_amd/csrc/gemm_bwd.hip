@@ -1,14 +1,16 @@
-// gemm_bwd.hip -- MXFP8 grouped GEMMs of the expert-layer backward (dgrad, wgrad) and the
-// SwiGLU backward.
+// gemm_bwd.hip -- MXFP8 grouped GEMMs: the expert-layer backward (dgrad, wgrad), the MXFP8
+// forward of the layers that keep MXFP8, and the SwiGLU backward.
 //
 // Pages cited (by title and section heading):
 //   [AREX] AREX Feed article "Thinking Machines 发文详解 Inkling 2 Small 训练:原生 4-bit 前向传播
 //          贯穿预训练到最后一次 RL rollout":
 //            "只把专家层的前向传播降到 4-bit" -- the backward pass runs in MXFP8;
 //            "转置打散分组,随机舍入保住期望值" -- weights and activations are re-quantized to
-//              MXFP8 with stochastic rounding and the gradients use MXFP8 matmuls.
+//              MXFP8 with stochastic rounding and the gradients use MXFP8 matmuls;
+//            "配方的代价:预训练约 2% 的计算效率" -- the last 16.6% of the layers compute their
+//              forward in MXFP8 rather than NVFP4.
 //
-// Both GEMMs are D[r, c] = sum_k A[r, k] B[c, k] over E4M3 operands with one E8M0 scale per 32
+// All three are D[r, c] = sum_k A[r, k] B[c, k] over E4M3 operands with one E8M0 scale per 32
 // consecutive k, which is exactly the operand format of gfx950's block-scaled MFMA
 // (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3). Its lane layout, measured on the device:
 // lane l supplies row l % 32; with h = l / 32 its bytes 0..15 are k = 16h .. 16h+15 and bytes
@@ -66,7 +68,7 @@ PMN_DEV void wait_loads_and_barrier()
 {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
-enum { MODE_DGRAD = 0, MODE_WGRAD = 1 };
+enum { MODE_DGRAD = 0, MODE_WGRAD = 1, MODE_FWD = 2 };
 
 struct Mx8Args {
     // dgrad: A = dY row-wise codes [M x Nf] (lda = Nf) with scales de [Nf/32 x Pb] at padded slot
@@ -75,6 +77,12 @@ struct Mx8Args {
     // wgrad: A = dY^T [Nf x Pb], B = X^T [Kf x Pb] (lda = ldb = Pb), scales [Pb/32 x Nf] and
     //        [Pb/32 x Kf]; contraction over the padded slots of group g (po[g] .. po[g+1]),
     //        output dW [G*Nf x Kf].
+    // fwd:   computes Y^T = W X^T so that a lane holds one slot and 16 output features. A = W
+    //        codes [G*Kf x Nf] (lda = Nf; expert g in rows g*Kf ..) with scales [Nf/32 x G*Kf];
+    //        B = X in slot order [M x Nf] (ldb = Nf) with scales [Nf/32 x Pb] at padded slot
+    //        columns; contraction Nf, output Y [M x Kf] through the epilogue. With the SwiGLU
+    //        epilogue (Kf = 2F) a tile's 256 A rows are 128 features of w1 and the same 128 of w3,
+    //        arranged so that blocks i and i + 2 of a wavefront pair h1 and h3.
     const uint8_t* a;
     const uint8_t* ae;
     int64_t lda;
@@ -87,9 +95,22 @@ struct Mx8Args {
     int G;
     int64_t Nf, Kf;
     float* out;
-    int64_t rtiles, ctiles;   // tile grid (dgrad: slot-tile bound x Kf/256; wgrad: Nf/256 x Kf/256)
+    int64_t rtiles, ctiles;   // tile grid (dgrad: slot-tile bound x Kf/256; wgrad: Nf/256 x Kf/256;
+                              // fwd: Kf/256 x slot-tile bound)
     int SM, SN;
+    // fwd epilogue outputs: Y (fp32 / bf16 / A of SwiGLU / S2F6 codes), E8M0 of the codes, h13
+    void* yout;
+    uint8_t* ye8m0;
+    void* yaux;
+    uint32_t mask;
 };
+
+// fwd + SwiGLU: feature row (within the expert's 2F rows) of tile row t of n-tile nt: blocks i of
+// wavefront wr hold w1 (i = 0, 1) and w3 (i = 2, 3) rows of the same 64 features
+PMN_DEV int64_t swiglu_a_row(int t, int64_t nt, int64_t F)
+{
+    return ((t >> 6) & 1) * F + nt * 128 + (t >> 7) * 64 + ((t >> 5) & 1) * 32 + (t & 31);
+}
 
 // MFMA operands of one k-step for a wavefront's 128 x 128 quarter
 struct Mx8Frags {
@@ -97,7 +118,7 @@ struct Mx8Frags {
     int sa[4], sb[4];
 };
 
-template <int MODE>
+template <int MODE, int EPI = PMN_EPI_F32>
 __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
 {
     using namespace bwd;
@@ -111,9 +132,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     const int wr = wave >> 1, wc = wave & 1;    // 2 wavefronts along output rows, 2 along columns
 
     int g = -1;
-    int64_t r0 = 0, rvalid = BT, c0 = 0, klen = 0;
+    int64_t r0 = 0, rvalid = BT, c0 = 0, klen = 0, cvalid = BT;
     const uint8_t *acode, *bcode, *asc, *bsc;
-    int64_t asld, bsld, asrows = BT;
+    int64_t asld, bsld, asrows = BT, bsrows = BT;
     float* obase;
     TileXY tile;
     int64_t L = blockIdx.x, batch = 0;
@@ -129,7 +150,25 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     }
     if (!xcd_tile(L, p.rtiles, p.ctiles, p.SM, p.SN, tile)) return;
     c0 = tile.col * BT;
-    if (MODE == MODE_DGRAD) {
+    if (MODE == MODE_FWD) {
+        const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.col, BT);
+        if (u.g < 0) return;
+        g = u.g;
+        c0 = u.s0 + u.index * BT;                // first slot of the tile
+        const int64_t p0 = p.po[g] + u.index * BT;
+        cvalid = u.s1 - c0 < BT ? u.s1 - c0 : BT;
+        klen = p.Nf;
+        r0 = tile.row * BT;                      // first feature row (plain order)
+        const int64_t wrow0 = (int64_t)g * p.Kf + (EPI == PMN_EPI_SWIGLU ? 0 : r0);
+        acode = p.a + wrow0 * p.lda;
+        asc = p.ae + wrow0;
+        asld = (int64_t)p.G * p.Kf;
+        bcode = p.b + c0 * p.ldb;
+        bsc = p.be + p0;
+        bsld = p.Pb;
+        bsrows = p.Pb - p0;
+        obase = nullptr;
+    } else if (MODE == MODE_DGRAD) {
         const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, BT);
         if (u.g < 0) return;
         g = u.g;
@@ -167,12 +206,15 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     const int op = wave >> 1, half = wave & 1;
     const uint8_t* cbase = op ? bcode : acode;
     const int64_t cld = op ? p.ldb : p.lda;
-    const int crows = (int)(op ? (int64_t)BT : rvalid);
+    const int crows = (int)(op ? cvalid : rvalid);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
     const uint8_t* sbase = op ? bsc : asc;
     const int64_t sld = op ? bsld : asld;
-    const int64_t srows = op ? (int64_t)BT : asrows;
-    const uint8_t* sptr = sbase + (4 * lane < srows ? 4 * lane : 0);
+    const int64_t srows = op ? bsrows : asrows;
+    // the forward's SwiGLU tile takes its A rows (w1 and w3 features) through swiglu_a_row
+    const bool remap = MODE == MODE_FWD && EPI == PMN_EPI_SWIGLU && op == 0;
+    const int64_t Fh = p.Kf >> 1;
+    const uint8_t* sptr = sbase + (remap ? swiglu_a_row(4 * lane, tile.row, Fh) : (4 * lane < srows ? 4 * lane : 0));
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);   // LDS offset
     const uint32_t cdst = lds0 + op * TILEB + half * 8192;
     const uint32_t sdst = lds0 + 2 * TILEB + op * SCB + half * BT;
@@ -205,7 +247,8 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     };
     auto issue_piece = [&](const IssueAt& r, int i) {
         const int row = (half * 8 + i) * 16 + (lane >> 2);
-        dma16(cbase + (int64_t)(row < crows ? row : 0) * cld + r.kc, cdst + r.so + i * 1024);
+        const int64_t src = remap ? swiglu_a_row(row, tile.row, Fh) : (int64_t)(row < crows ? row : 0);
+        dma16(cbase + src * cld + r.kc, cdst + r.so + i * 1024);
     };
     auto issue_scales = [&](const IssueAt& r) { dma4(sptr + r.kb * sld, sdst + r.so); };
     auto issue = [&](int v) {
@@ -298,6 +341,111 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         wait_loads_and_barrier<0>();
     }
 
+    if (MODE == MODE_FWD) {
+        // Y^T tile: block (i, j) of this wavefront holds, in lane l, slot c0 + wc*128 + j*32 + l%32
+        // and the 16 feature rows wr*128 + i*32 + (v/4)*8 + (l/32)*4 + v%4 of the tile.
+        const int64_t Nout = p.Kf;
+        if (EPI == PMN_EPI_F32 || EPI == PMN_EPI_BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int sl = wc * 128 + j * 32 + lrow;
+                if (sl < cvalid) {
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            const int64_t n = r0 + wr * 128 + i * 32 + q * 8 + hh * 4;
+                            const int64_t o = (c0 + sl) * Nout + n;
+                            if (EPI == PMN_EPI_F32) {
+                                *reinterpret_cast<float4*>(static_cast<float*>(p.yout) + o) =
+                                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                acc[i][j][4 * q + 3]);
+                            } else {
+                                const uint32_t lo = f32_to_bf16_bits(acc[i][j][4 * q]) |
+                                                    (f32_to_bf16_bits(acc[i][j][4 * q + 1]) << 16);
+                                const uint32_t hi = f32_to_bf16_bits(acc[i][j][4 * q + 2]) |
+                                                    (f32_to_bf16_bits(acc[i][j][4 * q + 3]) << 16);
+                                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.yout) + o) = make_uint2(lo, hi);
+                            }
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            return;
+        }
+        // SwiGLU and RHT32 + S2F6 stage a 256-slot output tile of 256 bytes per slot in LDS and
+        // write whole 16-byte pieces of each slot's row
+        constexpr int OPITCH = 272;                 // bytes per slot row: conflict-free 8-byte writes
+        uint8_t* const t0 = lds;
+        uint8_t* const te = lds + BT * OPITCH;      // E8M0 tile: 8 bytes per slot
+        auto store_tile = [&](uint8_t* dst, int64_t pitch) {
+#pragma unroll
+            for (int k = 0; k < (BT * 16) / THREADS; k++) {
+                const int q = k * THREADS + tid;
+                const int row = q >> 4, c = q & 15;
+                if (row < cvalid)
+                    *reinterpret_cast<uint4*>(dst + (c0 + row) * pitch + c * 16) =
+                        *reinterpret_cast<const uint4*>(t0 + row * OPITCH + c * 16);
+            }
+        };
+        if (EPI == PMN_EPI_SWIGLU) {
+            // blocks i = 0, 1 hold h1 and i + 2 the matching h3 of features n0 + wr*64 + i*32 + ..
+            const int64_t F = Nout >> 1, n0 = tile.row * 128;
+            uint8_t* const A = static_cast<uint8_t*>(p.yout);
+            uint8_t* const Hs = static_cast<uint8_t*>(p.yaux);
+#pragma unroll
+            for (int phase = 0; phase < 3; phase++) {
+                if (phase > 0 && !Hs) break;
+                if (phase > 0) __syncthreads();     // the previous phase's tile has been stored
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const int sl = wc * 128 + j * 32 + lrow;
+#pragma unroll
+                    for (int i = 0; i < 2; i++) {
+#pragma unroll
+                        for (int q = 0; q < 4; q++) {
+                            uint32_t b[4];
+#pragma unroll
+                            for (int u = 0; u < 4; u++) {
+                                const float h1 = acc[i][j][4 * q + u], h3 = acc[i + 2][j][4 * q + u];
+                                b[u] = f32_to_bf16_bits(phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3));
+                            }
+                            const int off = sl * OPITCH + 2 * (wr * 64 + i * 32 + q * 8 + hh * 4);
+                            *reinterpret_cast<uint2*>(t0 + off) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+                        }
+                        // one block pair at a time: the accumulators stay in AGPRs until used
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+                __syncthreads();
+                if (phase == 0) store_tile(A + n0 * 2, F * 2);
+                else if (phase == 1) store_tile(Hs + n0 * 2, Nout * 2);
+                else store_tile(Hs + (F + n0) * 2, Nout * 2);
+            }
+        } else {
+            // RHT32 + S2F6: each block's 32 feature rows are one aligned chunk of the slot's row
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int sl = wc * 128 + j * 32 + lrow;
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int nl = wr * 128 + i * 32;
+                    rht_block_store(acc[i][j], p.mask, lane, reinterpret_cast<int8_t*>(t0 + sl * OPITCH + nl),
+                                    te + sl * 8 + (nl >> 5));
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+            store_tile(static_cast<uint8_t*>(p.yout) + r0, Nout);
+            if (tid < cvalid)
+                *reinterpret_cast<uint2*>(p.ye8m0 + (c0 + tid) * (Nout >> 5) + (r0 >> 5)) =
+                    *reinterpret_cast<const uint2*>(te + tid * 8);
+        }
+        return;
+    }
+
     // epilogue: block (i, j): lane holds column c = c0 + wc*128 + j*32 + lane%32 and tile rows
     // wr*128 + i*32 + (v/4)*8 + hh*4 + v%4
 #pragma unroll
@@ -324,9 +472,39 @@ hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_
     const int64_t rt = (M + bwd::BT - 1) / bwd::BT + G, ct = Kf / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
-    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN};
+    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN,
+              nullptr, nullptr, nullptr, 0u};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
     hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t* xq, const uint8_t* xe,
+                            const int64_t* offsets, const int64_t* po, int64_t Pb, int G, int64_t M, int64_t N,
+                            int64_t K, int epilogue, uint32_t mask, void* out, uint8_t* out_e8m0, void* out_aux,
+                            hipStream_t stream)
+{
+    if (M == 0 || G == 0) return hipSuccess;
+    const int64_t rt = N / bwd::BT, ct = (M + bwd::BT - 1) / bwd::BT + G;
+    int SM, SN;
+    xcd_shape(rt, ct, SM, SN);
+    Mx8Args p{wq, we, K, xq, xe, K, offsets, po, Pb, G, K, N, nullptr, rt, ct, SM, SN, out, out_e8m0, out_aux, mask};
+    dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
+    switch (epilogue) {
+    case PMN_EPI_F32:
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_FWD, PMN_EPI_F32>), grid, dim3(bwd::THREADS), 0, stream, p);
+        break;
+    case PMN_EPI_BF16:
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_FWD, PMN_EPI_BF16>), grid, dim3(bwd::THREADS), 0, stream, p);
+        break;
+    case PMN_EPI_SWIGLU:
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_FWD, PMN_EPI_SWIGLU>), grid, dim3(bwd::THREADS), 0, stream, p);
+        break;
+    default:
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_FWD, PMN_EPI_RHT32_S2F6>), grid, dim3(bwd::THREADS), 0, stream,
+                           p);
+        break;
+    }
     return hipGetLastError();
 }
 
@@ -338,7 +516,7 @@ hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8
     const int64_t rt = Nf / bwd::BT, ct = Kf / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
-    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, ld, G, Nf, Kf, dw, rt, ct, SM, SN};
+    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, ld, G, Nf, Kf, dw, rt, ct, SM, SN, nullptr, nullptr, nullptr, 0u};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN, G));
     hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
     return hipGetLastError();

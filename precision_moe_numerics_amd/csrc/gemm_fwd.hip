@@ -101,70 +101,6 @@ PMN_DEV void dequant_block_to_lds(const RawStage& r, uint8_t* dst)
     }
 }
 
-PMN_DEV float silu(float h) { return h / (1.0f + expf(-h)); }
-
-// RHT32 + S2F6 on one 32 x 32 accumulator block whose 32 rows (n) are one aligned chunk:
-// lane l holds column m = l % 32 and rows i = (v/4)*8 + (l/32)*4 + v%4. The 32 codes of slot m
-// go to out_row_chunk (the epilogue's LDS tile), its E8M0 byte to e8m0_ptr. Butterfly stages
-// h = 1, 2, 4, 8, 16 in that order: h = 1, 2, 8, 16 pair registers of one lane, h = 4 pairs the
-// two lane halves.
-PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_chunk, uint8_t* e8m0_ptr)
-{
-    const int hh = lane >> 5;
-    float t[16];
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-        const int i = (v >> 2) * 8 + hh * 4 + (v & 3);
-        t[v] = __uint_as_float(__float_as_uint(z[v]) ^ (((mask >> i) & 1u) << 31));
-    }
-    // h = 1 (v ^ 1), h = 2 (v ^ 2)
-#pragma unroll
-    for (int hb = 1; hb <= 2; hb <<= 1) {
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-            if ((v & hb) == 0) {
-                float a = t[v], b = t[v + hb];
-                t[v] = a + b;
-                t[v + hb] = a - b;
-            }
-        }
-    }
-    // h = 4: across lane halves
-#pragma unroll
-    for (int v = 0; v < 16; v++) {
-        float p = __shfl_xor(t[v], 32, 64);
-        t[v] = hh == 0 ? t[v] + p : p - t[v];
-    }
-    // h = 8 (v ^ 4), h = 16 (v ^ 8)
-#pragma unroll
-    for (int hb = 4; hb <= 8; hb <<= 1) {
-#pragma unroll
-        for (int v = 0; v < 16; v++) {
-            if ((v & hb) == 0) {
-                float a = t[v], b = t[v + hb];
-                t[v] = a + b;
-                t[v + hb] = a - b;
-            }
-        }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(t[v]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-    const int e = e8m0_exponent<E8M0_S2F6>(amax);
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        uint32_t w = 0u;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            int c = (int)__builtin_rintf(__builtin_ldexpf(t[4 * q + j], 6 - e));
-            w |= ((uint32_t)c & 0xFFu) << (8 * j);
-        }
-        *reinterpret_cast<uint32_t*>(out_row_chunk + q * 8 + hh * 4) = w;
-    }
-    if (hh == 0) *e8m0_ptr = (uint8_t)(e + 127);
-}
-
 template <int EPI>
 __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
 {

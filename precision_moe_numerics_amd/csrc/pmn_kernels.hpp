@@ -20,7 +20,7 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
-                             int64_t ld_e8m0, hipStream_t stream);
+                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather = nullptr);
 
 // Padded group offsets (each group rounded up to 32 slots) into padded_offsets [G+1].
 hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
@@ -53,6 +53,11 @@ hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
                               hipStream_t stream);
+
+hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t* xq, const uint8_t* xe,
+                            const int64_t* offsets, const int64_t* po, int64_t Pb, int G, int64_t M, int64_t N,
+                            int64_t K, int epilogue, uint32_t mask, void* out, uint8_t* out_e8m0, void* out_aux,
+                            hipStream_t stream);
 
 hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
                               const uint8_t* xte, int64_t ld, const int64_t* po, int G,

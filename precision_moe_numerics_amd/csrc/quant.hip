@@ -267,9 +267,13 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 }
 
 // ------------------------------------------------------------------------------------------
-// MXFP8 row-wise quantization of gradients  [AREX] "只把专家层的前向传播降到 4-bit" (gradients
-// go through MXFP8 matmuls). One thread per block of 32: e from the block amax, y = x * 2^-e,
-// E4M3 by round-to-nearest-even or by stochastic rounding.
+// MXFP8 row-wise quantization  [AREX] "只把专家层的前向传播降到 4-bit" (gradients go through
+// MXFP8 matmuls) and "配方的代价:预训练约 2% 的计算效率" (the last layers' forward stays in
+// MXFP8). One thread per block of 32: e from the block amax, y = x * 2^-e, E4M3 by
+// round-to-nearest-even or by stochastic rounding. Row r reads source row gather[r] (or r).
+// E8M0 layouts: row-major [M x N/32] (ld_e8m0 == 0); k-block-major [N/32 x ld_e8m0] with
+// column r (pad_off == nullptr, ld_e8m0 > 0); or k-block-major at the padded slot column
+// pad_off[g] + r - offsets[g] of r's group g.
 // ------------------------------------------------------------------------------------------
 
 template <bool SR>
@@ -278,12 +282,14 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
                                                     uint8_t* __restrict__ out,
                                                     uint8_t* __restrict__ out_e8m0,
                                                     const int64_t* __restrict__ offsets, int G,
-                                                    const int64_t* __restrict__ pad_off, int64_t ld_e8m0)
+                                                    const int64_t* __restrict__ pad_off, int64_t ld_e8m0,
+                                                    const int32_t* __restrict__ gather)
 {
     const int64_t nb = N >> 5;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= M * nb) return;
-    const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * i;
+    const int64_t src = gather ? (int64_t)gather[i / nb] * nb + (i - (i / nb) * nb) : i;
+    const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * src;
     uint32_t w[16];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -294,8 +300,11 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 #pragma unroll
     for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
     const int e = e8m0_exponent<E8M0_E4M3>(amax);
-    if (pad_off == nullptr) {
+    if (pad_off == nullptr && ld_e8m0 == 0) {
         out_e8m0[i] = (uint8_t)(e + 127);
+    } else if (pad_off == nullptr) {
+        const int64_t r = i / nb, kb = i - r * nb;
+        out_e8m0[kb * ld_e8m0 + r] = (uint8_t)(e + 127);
     } else {
         // group of slot r: the largest g with offsets[g] <= r (empty groups are skipped)
         const int64_t r = i / nb, kb = i - r * nb;
@@ -343,17 +352,17 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
-                             int64_t ld_e8m0, hipStream_t stream)
+                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather)
 {
     const int64_t n = M * (N / 32);
     if (n == 0) return hipSuccess;
     const int64_t grid = (n + 255) / 256;
     if (sr)
         hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
-                           out_e8m0, offsets, G, padded_offsets, ld_e8m0);
+                           out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
     else
         hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
-                           out_e8m0, offsets, G, padded_offsets, ld_e8m0);
+                           out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
     return hipGetLastError();
 }
 
