@@ -276,50 +276,18 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 // pad_off[g] + r - offsets[g] of r's group g.
 // ------------------------------------------------------------------------------------------
 
+// One block of 32 bf16 values (16 words) of row r, k-block kb -> 32 E4M3 codes (8 words, element
+// 0 in the low byte) and the E8M0 exponent e (scale 2^e). SR draws the element index r * N + c.
 template <bool SR>
-__global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t M,
-                                                    int64_t N, uint64_t seed, uint32_t stream_id,
-                                                    uint8_t* __restrict__ out,
-                                                    uint8_t* __restrict__ out_e8m0,
-                                                    const int64_t* __restrict__ offsets, int G,
-                                                    const int64_t* __restrict__ pad_off, int64_t ld_e8m0,
-                                                    const int32_t* __restrict__ gather)
+PMN_DEV int mxfp8_block(const uint32_t (&w)[16], int64_t r, int64_t kb, int64_t N, uint64_t seed,
+                        uint32_t stream_id, uint32_t (&o)[8])
 {
-    const int64_t nb = N >> 5;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= M * nb) return;
-    const int64_t src = gather ? (int64_t)gather[i / nb] * nb + (i - (i / nb) * nb) : i;
-    const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * src;
-    uint32_t w[16];
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        uint4 v = p[q];
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-    }
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
     const int e = e8m0_exponent<E8M0_E4M3>(amax);
-    if (pad_off == nullptr && ld_e8m0 == 0) {
-        out_e8m0[i] = (uint8_t)(e + 127);
-    } else if (pad_off == nullptr) {
-        const int64_t r = i / nb, kb = i - r * nb;
-        out_e8m0[kb * ld_e8m0 + r] = (uint8_t)(e + 127);
-    } else {
-        // group of slot r: the largest g with offsets[g] <= r (empty groups are skipped)
-        const int64_t r = i / nb, kb = i - r * nb;
-        int lo = 0, hi = G - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
-        }
-        out_e8m0[kb * ld_e8m0 + pad_off[lo] + (r - offsets[lo])] = (uint8_t)(e + 127);
-    }
-    uint32_t o[8];
     if (SR) {
-        const int64_t r = i / nb;
-        const int64_t c0 = (i - r * nb) * 32;
-        const uint64_t idx0 = (uint64_t)r * (uint64_t)N + (uint64_t)c0;   // multiple of 8
+        const uint64_t idx0 = (uint64_t)r * (uint64_t)N + (uint64_t)(kb * 32);   // multiple of 8
 #pragma unroll
         for (int q = 0; q < 4; q++) {
             uint32_t rw[4];
@@ -344,9 +312,87 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
             o[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
         }
     }
-    uint4* po = reinterpret_cast<uint4*>(out) + 2 * i;
+    return e;
+}
+
+PMN_DEV void load_block32(const uint16_t* x, int64_t word16, uint32_t (&w)[16])
+{
+    const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * word16;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint4 v = p[q];
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+    }
+}
+
+PMN_DEV void store_block32(uint8_t* out, int64_t block, const uint32_t (&o)[8])
+{
+    uint4* po = reinterpret_cast<uint4*>(out) + 2 * block;
     po[0] = make_uint4(o[0], o[1], o[2], o[3]);
     po[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// Row-major E8M0 [M x N/32]: one thread per block, in row order.
+template <bool SR>
+__global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__ x, int64_t M,
+                                                    int64_t N, uint64_t seed, uint32_t stream_id,
+                                                    uint8_t* __restrict__ out,
+                                                    uint8_t* __restrict__ out_e8m0,
+                                                    const int32_t* __restrict__ gather)
+{
+    const int64_t nb = N >> 5;
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= M * nb) return;
+    const int64_t r = i / nb, kb = i - r * nb;
+    uint32_t w[16], o[8];
+    load_block32(x, (gather ? (int64_t)gather[r] : r) * nb + kb, w);
+    const int e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
+    out_e8m0[i] = (uint8_t)(e + 127);
+    store_block32(out, i, o);
+}
+
+// k-block-major E8M0 [N/32 x ld_e8m0]: a workgroup takes 64 rows x 4 k-blocks (four threads
+// read 256 contiguous bytes of a row), and the scale bytes go through LDS so that each k-block's
+// 64 rows are written as one contiguous run. Column of row r: r (pad_off == nullptr), else
+// pad_off[g] + r - offsets[g] for r's group g.
+template <bool SR>
+__global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restrict__ x, int64_t M,
+                                                        int64_t N, uint64_t seed, uint32_t stream_id,
+                                                        uint8_t* __restrict__ out,
+                                                        uint8_t* __restrict__ out_e8m0,
+                                                        const int64_t* __restrict__ offsets, int G,
+                                                        const int64_t* __restrict__ pad_off, int64_t ld_e8m0,
+                                                        const int32_t* __restrict__ gather)
+{
+    __shared__ uint8_t se[4][64];
+    const int64_t nb = N >> 5;
+    const int t = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * 64, kb0 = (int64_t)blockIdx.y * 4;
+    {
+        const int64_t r = r0 + (t >> 2), kb = kb0 + (t & 3);
+        if (r < M && kb < nb) {
+            uint32_t w[16], o[8];
+            load_block32(x, (gather ? (int64_t)gather[r] : r) * nb + kb, w);
+            const int e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
+            se[t & 3][t >> 2] = (uint8_t)(e + 127);
+            store_block32(out, r * nb + kb, o);
+        }
+    }
+    __syncthreads();
+    const int64_t r = r0 + (t & 63), kb = kb0 + (t >> 6);
+    if (r < M && kb < nb) {
+        int64_t col = r;
+        if (pad_off != nullptr) {
+            // group of slot r: the largest g with offsets[g] <= r (empty groups are skipped)
+            int lo = 0, hi = G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+            }
+            col = pad_off[lo] + (r - offsets[lo]);
+        }
+        out_e8m0[kb * ld_e8m0 + col] = se[t >> 6][t & 63];
+    }
 }
 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
@@ -354,14 +400,24 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
                              int64_t ld_e8m0, hipStream_t stream, const int32_t* gather)
 {
-    const int64_t n = M * (N / 32);
-    if (n == 0) return hipSuccess;
-    const int64_t grid = (n + 255) / 256;
+    const int64_t nb = N / 32;
+    if (M * nb == 0) return hipSuccess;
+    if (padded_offsets == nullptr && ld_e8m0 == 0) {
+        const int64_t grid = (M * nb + 255) / 256;
+        if (sr)
+            hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+                               out_e8m0, gather);
+        else
+            hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+                               out_e8m0, gather);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((nb + 3) / 4));
     if (sr)
-        hipLaunchKernelGGL((k_mxfp8_rows<true>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+        hipLaunchKernelGGL((k_mxfp8_rows_kbm<true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id, out,
                            out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
     else
-        hipLaunchKernelGGL((k_mxfp8_rows<false>), dim3(grid), dim3(256), 0, stream, x, M, N, seed, stream_id, out,
+        hipLaunchKernelGGL((k_mxfp8_rows_kbm<false>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id, out,
                            out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
     return hipGetLastError();
 }
