@@ -88,6 +88,11 @@ def _declare(L):
         "orc_moe_combine_s2f6": (None, [P, P, I64, I64, U32, P, P, I64, I32, P]),
         "orc_s2f6_quantize": (None, [P, I64, I64, P, P]),
         "orc_gemm_mxfp8_fwd": (None, [P, P, P, P, P, P, I32, I64, I64, P]),
+        "orc_mx_quantize_rows": (None, [P, I64, I64, I32, I32, U64, U32, P, P]),
+        "orc_mx_quantize_cols": (None, [P, I64, I64, P, I32, I32, I32, U64, U32, P, P]),
+        "orc_gemm_mx_dgrad": (None, [P, P, P, P, P, I32, I64, I64, I32, P]),
+        "orc_gemm_mx_wgrad": (None, [P, P, P, P, P, I32, I64, I64, I32, P]),
+        "orc_mx_dot": (C.c_double, [P, P, I64, P, P, I64, I64, I64, I64, I64, I32]),
         "orc_gemm_mxfp8_dgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_gemm_mxfp8_wgrad": (None, [P, P, P, P, P, I32, I64, I64, P]),
         "orc_swiglu": (None, [P, I64, I64, P]),
@@ -250,16 +255,17 @@ def requant_window(q, s_begin, count, target=TARGET_E4M3, seed=0, stream=0):
     return out, oe
 
 
-def mxfp8_quantize_rows(x_bf16, sr=False, seed=0, stream=0):
+def mxfp8_quantize_rows(x_bf16, sr=False, seed=0, stream=0, target=TARGET_E4M3):
+    """Row-wise MX quantization: codes [M, N] (E4M3 bytes, or E2M1 one per byte), E8M0 [M, N/32]."""
     x = _u16(x_bf16)
     M, N = x.shape
     out = np.zeros((M, N), np.uint8)
     oe = np.zeros((M, N // 32), np.uint8)
-    lib().orc_mxfp8_quantize_rows(_p(x), M, N, 1 if sr else 0, seed, stream, _p(out), _p(oe))
+    lib().orc_mx_quantize_rows(_p(x), M, N, target, 1 if sr else 0, seed, stream, _p(out), _p(oe))
     return out, oe
 
 
-def mxfp8_quantize_cols(x_bf16, offsets=None, sr=False, seed=0, stream=0):
+def mxfp8_quantize_cols(x_bf16, offsets=None, sr=False, seed=0, stream=0, target=TARGET_E4M3):
     x = _u16(x_bf16)
     M, N = x.shape
     o = None if offsets is None else np.ascontiguousarray(offsets, np.int64)
@@ -267,7 +273,7 @@ def mxfp8_quantize_cols(x_bf16, offsets=None, sr=False, seed=0, stream=0):
     Ptot = padded_total(o, M)
     out = np.zeros((N, Ptot), np.uint8)
     oe = np.zeros((N, Ptot // 32), np.uint8)
-    lib().orc_mxfp8_quantize_cols(_p(x), M, N, _p(o), G, 1 if sr else 0, seed, stream, _p(out), _p(oe))
+    lib().orc_mx_quantize_cols(_p(x), M, N, _p(o), G, target, 1 if sr else 0, seed, stream, _p(out), _p(oe))
     return out, oe
 
 
@@ -373,25 +379,25 @@ def gemm_mxfp8_fwd(xq, xe, wq, we, offsets, N, K, gather=None):
     return Y
 
 
-def gemm_mxfp8_dgrad(dq, de, wt, wte, offsets, N, K):
+def gemm_mxfp8_dgrad(dq, de, wt, wte, offsets, N, K, target=TARGET_E4M3):
     o = np.ascontiguousarray(offsets, np.int64)
     G = len(o) - 1
     dX = np.zeros((int(o[-1]), K), np.float32)
-    lib().orc_gemm_mxfp8_dgrad(*[_p(np.ascontiguousarray(a)) for a in (dq, de, wt, wte, o)], G, N, K, _p(dX))
+    lib().orc_gemm_mx_dgrad(*[_p(np.ascontiguousarray(a)) for a in (dq, de, wt, wte, o)], G, N, K, target, _p(dX))
     return dX
 
 
-def gemm_mxfp8_wgrad(dt, dte, xt, xte, offsets, N, K):
+def gemm_mxfp8_wgrad(dt, dte, xt, xte, offsets, N, K, target=TARGET_E4M3):
     o = np.ascontiguousarray(offsets, np.int64)
     G = len(o) - 1
     dW = np.zeros((G * N, K), np.float32)
-    lib().orc_gemm_mxfp8_wgrad(*[_p(np.ascontiguousarray(a)) for a in (dt, dte, xt, xte, o)], G, N, K, _p(dW))
+    lib().orc_gemm_mx_wgrad(*[_p(np.ascontiguousarray(a)) for a in (dt, dte, xt, xte, o)], G, N, K, target, _p(dW))
     return dW
 
 
-def mxfp8_dot(a, ae, b, be, m, n, k0, kn):
+def mxfp8_dot(a, ae, b, be, m, n, k0, kn, target=TARGET_E4M3):
     a, ae, b, be = (np.ascontiguousarray(t) for t in (a, ae, b, be))
-    return lib().orc_mxfp8_dot(_p(a), _p(ae), a.shape[1], _p(b), _p(be), b.shape[1], m, n, k0, kn)
+    return lib().orc_mx_dot(_p(a), _p(ae), a.shape[1], _p(b), _p(be), b.shape[1], m, n, k0, kn, target)
 
 
 def swiglu(h13, F):

@@ -423,12 +423,16 @@ void orc_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales, const
 
 /*
  * Row-wise: x bf16 [M x N], blocks of 32 along each row (N % 32 == 0).
- *   e = smallest e with max|x| <= 448 * 2^e; y = RN(x * 2^-e); code = E4M3(y), RNE, or SR with
+ *   e = smallest e with max|x| <= Mx * 2^e (Mx = 448 for E4M3, 6 for E2M1); y = RN(x * 2^-e);
+ *   code = E4M3(y) or E2M1(y) (one nibble per byte), RNE, or SR with
  *   r16 = rand16(seed, stream, row * N + col) when sr != 0.
+ * The E2M1 target is the element format of an FP4 backward ([AREX], closing section: FP4 in the
+ * backward pass is the next step; the transpose section's worked example rounds onto that grid).
  */
-void orc_mxfp8_quantize_rows(const uint16_t* x, int64_t M, int64_t N, int sr, uint64_t seed,
-                             uint32_t stream, uint8_t* out, uint8_t* out_e8m0)
+void orc_mx_quantize_rows(const uint16_t* x, int64_t M, int64_t N, int target, int sr, uint64_t seed,
+                          uint32_t stream, uint8_t* out, uint8_t* out_e8m0)
 {
+    const double Mx = target == ORC_TARGET_E4M3 ? 448.0 : 6.0;
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < M; r++)
         for (int64_t b = 0; b < N / 32; b++) {
@@ -437,25 +441,33 @@ void orc_mxfp8_quantize_rows(const uint16_t* x, int64_t M, int64_t N, int sr, ui
                 float m = fabsf(orc_bf16_to_f32(x[r * N + b * 32 + j]));
                 if (m > amax) amax = m;
             }
-            int e = orc_e8m0_exponent(amax, 448.0);
+            int e = orc_e8m0_exponent(amax, Mx);
             out_e8m0[r * (N / 32) + b] = (uint8_t)(e + 127);
             for (int j = 0; j < 32; j++) {
                 int64_t c = b * 32 + j;
                 float y = ldexpf(orc_bf16_to_f32(x[r * N + c]), -e);
                 uint32_t r16 = sr ? orc_rand16(seed, stream, (uint64_t)r * (uint64_t)N + (uint64_t)c) : 0;
-                out[r * N + c] = orc_e4m3_encode(y, sr ? ORC_SR : ORC_RNE, r16);
+                out[r * N + c] = target == ORC_TARGET_E4M3 ? orc_e4m3_encode(y, sr ? ORC_SR : ORC_RNE, r16)
+                                                           : orc_fp4_encode(y, sr ? ORC_SR : ORC_RNE, r16);
             }
         }
+}
+
+void orc_mxfp8_quantize_rows(const uint16_t* x, int64_t M, int64_t N, int sr, uint64_t seed,
+                             uint32_t stream, uint8_t* out, uint8_t* out_e8m0)
+{
+    orc_mx_quantize_rows(x, M, N, ORC_TARGET_E4M3, sr, seed, stream, out, out_e8m0);
 }
 
 /*
  * Column-wise within groups: the transposed, padded layout described above, blocks of 32 along
  * the slots of one group, for x bf16 [M x N] -> out [N x Ptot], out_e8m0 [N x Ptot/32].
  */
-void orc_mxfp8_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
-                             int G, int sr, uint64_t seed, uint32_t stream, uint8_t* out,
-                             uint8_t* out_e8m0)
+void orc_mx_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                          int G, int target, int sr, uint64_t seed, uint32_t stream, uint8_t* out,
+                          uint8_t* out_e8m0)
 {
+    const double Mx = target == ORC_TARGET_E4M3 ? 448.0 : 6.0;
     int64_t Ptot = orc_padded_total(offsets, G, M);
     int ng = offsets ? G : 1;
 #pragma omp parallel for schedule(static)
@@ -471,7 +483,7 @@ void orc_mxfp8_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int6
                     v[j] = (s < s1) ? orc_bf16_to_f32(x[s * N + n]) : 0.0f;
                     if (fabsf(v[j]) > amax) amax = fabsf(v[j]);
                 }
-                int e = orc_e8m0_exponent(amax, 448.0);
+                int e = orc_e8m0_exponent(amax, Mx);
                 out_e8m0[n * (Ptot / 32) + (po + jb) / 32] = (uint8_t)(e + 127);
                 for (int j = 0; j < 32; j++) {
                     int64_t s = s0 + jb + j;
@@ -479,7 +491,8 @@ void orc_mxfp8_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int6
                     if (s < s1) {
                         float y = ldexpf(v[j], -e);
                         uint32_t r16 = sr ? orc_rand16(seed, stream, (uint64_t)s * (uint64_t)N + (uint64_t)n) : 0;
-                        code = orc_e4m3_encode(y, sr ? ORC_SR : ORC_RNE, r16);
+                        code = target == ORC_TARGET_E4M3 ? orc_e4m3_encode(y, sr ? ORC_SR : ORC_RNE, r16)
+                                                         : orc_fp4_encode(y, sr ? ORC_SR : ORC_RNE, r16);
                     }
                     out[n * Ptot + po + jb + j] = code;
                 }
@@ -489,8 +502,19 @@ void orc_mxfp8_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int6
     }
 }
 
-/* Value of an MXFP8 element: value(code) * 2^(e8m0 - 127). */
-double orc_mxfp8_value(uint8_t code, uint8_t e8m0) { return ldexp(orc_e4m3_value(code), (int)e8m0 - 127); }
+void orc_mxfp8_quantize_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                             int G, int sr, uint64_t seed, uint32_t stream, uint8_t* out,
+                             uint8_t* out_e8m0)
+{
+    orc_mx_quantize_cols(x, M, N, offsets, G, ORC_TARGET_E4M3, sr, seed, stream, out, out_e8m0);
+}
+
+/* Value of an MX element: value(code) * 2^(e8m0 - 127), code E4M3 or E2M1 (one per byte). */
+double orc_mx_value(uint8_t code, uint8_t e8m0, int target)
+{
+    return ldexp(target == ORC_TARGET_E4M3 ? orc_e4m3_value(code) : orc_fp4_value(code), (int)e8m0 - 127);
+}
+double orc_mxfp8_value(uint8_t code, uint8_t e8m0) { return orc_mx_value(code, e8m0, ORC_TARGET_E4M3); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* 32-point randomized Hadamard transform + S2F6 block quantization  [AREX S4], [LHC]          */
@@ -676,14 +700,20 @@ double orc_gemm_nvfp4_elem(const uint8_t* xc, const uint8_t* xs, const float* xo
  * dimensions lda / ldb bytes and scale leading dimensions lda/32, ldb/32.
  * Element (m, n) over k in [k0, k0 + kn) (k0, kn multiples of 32), fp64.
  */
-double orc_mxfp8_dot(const uint8_t* a, const uint8_t* ae, int64_t lda, const uint8_t* b,
-                     const uint8_t* be, int64_t ldb, int64_t m, int64_t n, int64_t k0, int64_t kn)
+double orc_mx_dot(const uint8_t* a, const uint8_t* ae, int64_t lda, const uint8_t* b, const uint8_t* be,
+                  int64_t ldb, int64_t m, int64_t n, int64_t k0, int64_t kn, int target)
 {
     double acc = 0.0;
     for (int64_t k = k0; k < k0 + kn; k++)
-        acc += orc_mxfp8_value(a[m * lda + k], ae[m * (lda / 32) + k / 32]) *
-               orc_mxfp8_value(b[n * ldb + k], be[n * (ldb / 32) + k / 32]);
+        acc += orc_mx_value(a[m * lda + k], ae[m * (lda / 32) + k / 32], target) *
+               orc_mx_value(b[n * ldb + k], be[n * (ldb / 32) + k / 32], target);
     return acc;
+}
+
+double orc_mxfp8_dot(const uint8_t* a, const uint8_t* ae, int64_t lda, const uint8_t* b,
+                     const uint8_t* be, int64_t ldb, int64_t m, int64_t n, int64_t k0, int64_t kn)
+{
+    return orc_mx_dot(a, ae, lda, b, be, ldb, m, n, k0, kn, ORC_TARGET_E4M3);
 }
 
 /*
@@ -711,9 +741,8 @@ void orc_gemm_mxfp8_fwd(const uint8_t* xq, const uint8_t* xe, const int32_t* gat
  * (dq [M x N], de [M x N/32]) and W_g^T requantized (wt [K x G*N], wte [K x G*N/32]; group g's
  * columns g*N .. g*N+N-1).
  */
-void orc_gemm_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
-                          const uint8_t* wte, const int64_t* offsets, int G, int64_t N, int64_t K,
-                          float* dX)
+void orc_gemm_mx_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt, const uint8_t* wte,
+                       const int64_t* offsets, int G, int64_t N, int64_t K, int target, float* dX)
 {
     int64_t M = offsets[G];
 #pragma omp parallel for schedule(dynamic, 4)
@@ -723,11 +752,18 @@ void orc_gemm_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* w
         for (int64_t k = 0; k < K; k++) {
             double acc = 0.0;
             for (int64_t n = 0; n < N; n++)
-                acc += orc_mxfp8_value(dq[s * N + n], de[s * (N / 32) + n / 32]) *
-                       orc_mxfp8_value(wt[k * (G * N) + g * N + n], wte[k * (G * N / 32) + (g * N + n) / 32]);
+                acc += orc_mx_value(dq[s * N + n], de[s * (N / 32) + n / 32], target) *
+                       orc_mx_value(wt[k * (G * N) + g * N + n], wte[k * (G * N / 32) + (g * N + n) / 32], target);
             dX[s * K + k] = (float)acc;
         }
     }
+}
+
+void orc_gemm_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
+                          const uint8_t* wte, const int64_t* offsets, int G, int64_t N, int64_t K,
+                          float* dX)
+{
+    orc_gemm_mx_dgrad(dq, de, wt, wte, offsets, G, N, K, ORC_TARGET_E4M3, dX);
 }
 
 /*
@@ -735,9 +771,8 @@ void orc_gemm_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* w
  * quantized dY^T (dt [N x Ptot]) and the requantized X^T (xt [K x Ptot]) in the padded grouped
  * layout (padding is zero and adds nothing).
  */
-void orc_gemm_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
-                          const uint8_t* xte, const int64_t* offsets, int G, int64_t N, int64_t K,
-                          float* dW)
+void orc_gemm_mx_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt, const uint8_t* xte,
+                       const int64_t* offsets, int G, int64_t N, int64_t K, int target, float* dW)
 {
     int64_t Ptot = orc_padded_total(offsets, G, offsets[G]);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -748,8 +783,15 @@ void orc_gemm_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* 
         for (int64_t n = 0; n < N; n++)
             for (int64_t k = 0; k < K; k++)
                 dW[((int64_t)g * N + n) * K + k] =
-                    (float)orc_mxfp8_dot(dt, dte, Ptot, xt, xte, Ptot, n, k, po, P);
+                    (float)orc_mx_dot(dt, dte, Ptot, xt, xte, Ptot, n, k, po, P, target);
     }
+}
+
+void orc_gemm_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
+                          const uint8_t* xte, const int64_t* offsets, int G, int64_t N, int64_t K,
+                          float* dW)
+{
+    orc_gemm_mx_wgrad(dt, dte, xt, xte, offsets, G, N, K, ORC_TARGET_E4M3, dW);
 }
 
 /* ------------------------------------------------------------------------------------------ */

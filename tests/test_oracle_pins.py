@@ -750,3 +750,83 @@ def test_mxfp8_forward_one_hot_closed_form():
     for s in range(9):
         g = 0 if s < 5 else 1
         assert np.array_equal(Y[s], vals[g * N:(g + 1) * N])
+
+
+# ------------------------------------------------------------------------------------------
+# MX with E2M1 elements (the FP4 backward)
+# ------------------------------------------------------------------------------------------
+
+def _fp4_decode(codes, e8m0):
+    """E2M1 codes (one per byte) x 2^(e - 127) from the pages' grid (independent of the oracle)."""
+    grid = np.array(FACTS["fp4_grid"]["magnitudes"])
+    c = np.asarray(codes).astype(int)
+    v = np.where(c & 8, -1.0, 1.0) * grid[c & 7]
+    return v * np.repeat(2.0 ** (np.asarray(e8m0, np.float64) - 127), 32, axis=1)
+
+
+def test_mxfp4_quant_rule_rows_cols_and_nearest():
+    rng = np.random.default_rng(24)
+    x = bf16(rng.standard_t(4, (64, 96)))
+    rq, re = O.mxfp8_quantize_rows(x, target=O.TARGET_E2M1)
+    cq, ce = O.mxfp8_quantize_cols(x.t().contiguous(), target=O.TARGET_E2M1)
+    assert np.array_equal(rq, cq) and np.array_equal(re, ce)
+    assert rq.max() <= 15
+    xf = x.float().numpy().astype(np.float64)
+    # scale rule with M = 6: block amax / 2^e in (3, 6]
+    am = np.abs(xf).reshape(64, 3, 32).max(-1)
+    ratio = am / 2.0 ** (re.astype(int) - 127)
+    assert np.all((ratio > 3) & (ratio <= 6))
+    # RNE: each value is a nearest grid point (brute force over the 15 candidates of its block)
+    v = _fp4_decode(rq, re)
+    grid = np.array(FACTS["fp4_grid"]["magnitudes"])
+    cand = np.concatenate([-grid[::-1], grid])[None, None, :] * np.repeat(2.0 ** (re.astype(int) - 127), 32, 1)[..., None]
+    best = np.abs(cand - xf[..., None]).min(-1)
+    assert np.all(np.abs(v - xf) == best)
+
+
+def test_mxfp4_sr_is_unbiased():
+    rng = np.random.default_rng(25)
+    x = bf16(rng.standard_normal((4, 64)))
+    xf = x.float().numpy().astype(np.float64)
+    acc = np.zeros_like(xf)
+    n = 400
+    for s in range(n):
+        q, e = O.mxfp8_quantize_rows(x, sr=True, seed=s, stream=3, target=O.TARGET_E2M1)
+        acc += _fp4_decode(q, e)
+    mean = acc / n
+    # per element the SR error is at most one grid step (<= 2^(e-127) * 2); z-test on the sum
+    step = np.repeat(2.0 ** (O.mxfp8_quantize_rows(x, target=O.TARGET_E2M1)[1].astype(int) - 127), 32, 1) * 2
+    z = (mean - xf).sum() / np.sqrt((step ** 2 / 4).sum() / n)
+    assert abs(z) < 5
+
+
+def test_mxfp4_gemms_vs_dense_products():
+    """FP4 dgrad and wgrad (the requantized operands on the E2M1 grid) against the pages' grid
+    decode and numpy matmuls."""
+    rng = np.random.default_rng(26)
+    G, N, K = 3, 64, 96
+    offsets = np.array([0, 10, 10, 75], np.int64)
+    M = int(offsets[-1])
+    dy = bf16(rng.standard_normal((M, N)) * 1e-3)
+    w = bf16(rng.standard_normal((G * N, K)) * 0.02)
+    x = bf16(rng.standard_normal((M, K)))
+    wq = O.nvfp4_quantize(w, rows_per_outer=N, four_six=False)
+    xq = O.nvfp4_quantize(x, four_six=True)
+    dq, de = O.mxfp8_quantize_rows(dy, sr=True, seed=4, stream=6, target=O.TARGET_E2M1)
+    wt, wte = O.requant_transpose_sr(wq, offsets=np.arange(G + 1) * N, target=O.TARGET_E2M1, seed=3, stream=1)
+    dX = O.gemm_mxfp8_dgrad(dq, de, wt, wte, offsets, N, K, target=O.TARGET_E2M1)
+    dyv, wtv = _fp4_decode(dq, de), _fp4_decode(wt, wte)
+    for g in range(G):
+        s0, s1 = offsets[g], offsets[g + 1]
+        ref = dyv[s0:s1] @ wtv[:, g * N:(g + 1) * N].T
+        assert np.allclose(dX[s0:s1], ref, rtol=1e-6, atol=1e-12)
+    dt, dte = O.mxfp8_quantize_cols(dy, offsets=offsets, sr=True, seed=4, stream=7, target=O.TARGET_E2M1)
+    xt, xte = O.requant_transpose_sr(xq, offsets=offsets, target=O.TARGET_E2M1, seed=3, stream=2)
+    dW = O.gemm_mxfp8_wgrad(dt, dte, xt, xte, offsets, N, K, target=O.TARGET_E2M1)
+    dtv, xtv = _fp4_decode(dt, dte), _fp4_decode(xt, xte)
+    P, po = [32, 0, 96], [0, 32, 32]
+    for g in range(G):
+        ref = dtv[:, po[g]:po[g] + P[g]] @ xtv[:, po[g]:po[g] + P[g]].T
+        assert np.allclose(dW[g * N:(g + 1) * N], ref, rtol=1e-6, atol=1e-12)
+    # one sampled element through the generic dot
+    assert np.isclose(O.mxfp8_dot(dt, dte, xt, xte, 5, 7, 32, 96, target=O.TARGET_E2M1), dW[2 * N + 5, 7], rtol=1e-6)
