@@ -230,6 +230,7 @@ int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gat
 
 #define PMN_BWD_DGRAD 1
 #define PMN_BWD_WGRAD 2
+#define PMN_BWD_FP4   4  /* with DGRAD and/or WGRAD: the FP4 backward variant (see below) */
 
 /*
  * Workspace bytes moe_grouped_gemm_bwd needs for these sizes and flags (host call).
@@ -254,6 +255,12 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * E8M0 parts are k-block-major (entry [b, r] is the scale of k-block b of row r); the row-wise
  * dY scales of slot s of group g sit at column padded_offsets[g] + s - offsets[g]. The parts of
  * a gradient not requested are still reserved.
+ * PMN_BWD_FP4 ([AREX], closing section: FP4 in the backward pass is the next step; the transpose
+ * section's worked example rounds onto the E2M1 grid by SR): every operand goes to MXFP4 instead
+ * of MXFP8 -- E2M1 codes (W^T, A^T by SR; dY by dy_rounding) with one E8M0 per 32 values chosen
+ * so that nothing saturates (amax <= 6 * 2^e) -- and dgrad / wgrad run on the block-scaled FP4
+ * MFMA. The workspace keeps the same layout; its code parts then hold E2M1 codes packed two per
+ * byte (element 2j in the low nibble), rows of half the bytes.
  */
 int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,

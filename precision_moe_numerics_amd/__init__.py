@@ -62,7 +62,7 @@ ROWWISE, COLWISE = 0, 1
 RNE, SR = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 EPI_F32, EPI_BF16, EPI_SWIGLU, EPI_RHT32_S2F6 = 0, 1, 2, 3
-BWD_DGRAD, BWD_WGRAD = 1, 2
+BWD_DGRAD, BWD_WGRAD, BWD_FP4 = 1, 2, 4
 
 
 class PmnError(RuntimeError):
@@ -280,15 +280,18 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
     return da, db, workspace
 
 
-def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int):
-    """Views of the backward workspace parts, in the order include/pmn.h documents them."""
+def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int, fp4: bool = False):
+    """Views of the backward workspace parts, in the order include/pmn.h documents them (with
+    fp4, the code parts hold E2M1 codes packed two per byte: rows of half the bytes)."""
     Pb = padded_bound(M, G)
-    sizes = [("dq", M * N, (M, N)), ("de", N // 32 * Pb, (N // 32, Pb)), ("wt", K * G * N, (K, G * N)),
-             ("wte", K * G * N // 32, (G * N // 32, K)), ("dt", N * Pb, (N, Pb)), ("dte", N * Pb // 32, (Pb // 32, N)),
-             ("xt", K * Pb, (K, Pb)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
+    h = 2 if fp4 else 1
+    sizes = [("dq", M * N, (M, N // h)), ("de", N // 32 * Pb, (N // 32, Pb)), ("wt", K * G * N, (K, G * N // h)),
+             ("wte", K * G * N // 32, (G * N // 32, K)), ("dt", N * Pb, (N, Pb // h)), ("dte", N * Pb // 32, (Pb // 32, N)),
+             ("xt", K * Pb, (K, Pb // h)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
     off, views = 0, {}
     for name, nbytes, shape in sizes:
-        part = workspace[off:off + nbytes]
+        used = nbytes if shape is None else shape[0] * shape[1]
+        part = workspace[off:off + used]
         views[name] = part.view(torch.int64) if shape is None else part.view(*shape)
         off += (nbytes + 255) // 256 * 256
     return views

@@ -193,7 +193,8 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          uint32_t rng_stream_dy, float* da, float* db, void* workspace,
                          size_t workspace_bytes, pmn_stream_t stream)
 {
-    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD)) != 0 || flags == 0) return PMN_EINVAL;
+    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
+        return PMN_EINVAL;
     if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
     if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
     if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
@@ -210,29 +211,31 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t s = hs(stream);
     const bool sr = dy_rounding == PMN_SR;
+    const bool fp4 = flags & PMN_BWD_FP4;
+    const int target = fp4 ? pmn::TARGET_E2M1_PACKED : PMN_TARGET_E4M3;
     int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
     hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s);
     if (e != hipSuccess) return PMN_ELAUNCH;
     if (dgrad) {
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
-                                   ws + L.de, offsets, G, po, L.Pb, s);
+                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
-                                0, PMN_TARGET_E4M3, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N,
-                                true, nullptr, s);
+                                0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true, nullptr,
+                                s);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
-                                    s);
+                                    s, fp4);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (wgrad) {
         e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
-                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s);
+                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target);
         if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G,
-                                PMN_TARGET_E4M3, seed, rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s);
+        e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G, target, seed,
+                                rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s);
+        e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s, fp4);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     return PMN_OK;

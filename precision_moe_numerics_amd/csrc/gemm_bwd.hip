@@ -117,12 +117,37 @@ struct Mx8Frags {
     i32x8 a[4], b[4];
     int sa[4], sb[4];
 };
+// FP4 (E2M1) operands of one 64-byte stage = two k-steps of 64 values: an E2M1 operand of the
+// block-scaled MFMA is 4 registers (the upper half of the 8-register operand is left undefined)
+struct Mx4Frags {
+    i32x8 a[4], b[4], a2[4], b2[4];
+    int sa[4], sb[4], sa2[4], sb2[4];
+};
+template <bool FP4> struct FragsOf { typedef Mx8Frags type; };
+template <> struct FragsOf<true> { typedef Mx4Frags type; };
 
-template <int MODE, int EPI = PMN_EPI_F32>
+PMN_DEV i32x8 lo4(uint4 x)
+{
+    typedef int i32x4 __attribute__((ext_vector_type(4)));
+    const i32x4 v = {(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+    return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// FP4: the operands are E2M1 codes packed two per byte (k even in the low nibble), lda / ldb in
+// bytes; a stage is still 64 bytes per row, now 128 values = 4 k-blocks = two MFMA k-steps, and
+// each loading wavefront streams two scale lines per stage.
+template <int MODE, int EPI = PMN_EPI_F32, bool FP4 = false>
 __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args p)
 {
     using namespace bwd;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
+    static_assert(!(FP4 && MODE == MODE_FWD), "the FP4 operand format is used by the backward only");
+    constexpr int SCBk = FP4 ? 4 * BT : SCB;        // one operand's scales per stage
+    constexpr int STAGEBk = 2 * TILEB + 2 * SCBk;
+    constexpr int LDSBk = NSTAGE * STAGEBk;
+    constexpr int LPS = FP4 ? LOADS_PER_STAGE + 1 : LOADS_PER_STAGE;
+    constexpr int KS = FP4 ? 2 * BK : BK;           // values (k) per stage
+    typedef typename FragsOf<FP4>::type Frags;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSBk];
     // An AGPR operand marks the kernel as using AGPRs, so the compiler keeps the 256 accumulator
     // registers in AGPRs (MFMA accumulator form) instead of arch VGPRs.
     asm volatile("; agpr in use %0" ::"a"(0));
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         asc = p.ae + p0;
         asld = p.Pb;
         asrows = p.Pb - p0;                      // scale columns of this tile inside the array
-        bcode = p.b + c0 * p.ldb + (int64_t)g * p.Nf;
+        bcode = p.b + c0 * p.ldb + (int64_t)g * (FP4 ? p.Nf / 2 : p.Nf);
         bsc = p.be + (int64_t)g * (p.Nf / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + r0 * p.Kf;
@@ -189,10 +214,10 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         r0 = tile.row * BT;
         const int64_t kbeg = p.po[g];
         klen = p.po[g + 1] - kbeg;
-        acode = p.a + r0 * p.lda + kbeg;
+        acode = p.a + r0 * p.lda + (FP4 ? kbeg / 2 : kbeg);
         asc = p.ae + (kbeg / 32) * p.Nf + r0;
         asld = p.Nf;
-        bcode = p.b + c0 * p.ldb + kbeg;
+        bcode = p.b + c0 * p.ldb + (FP4 ? kbeg / 2 : kbeg);
         bsc = p.be + (kbeg / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
@@ -217,10 +242,10 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     const uint8_t* sptr = sbase + (remap ? swiglu_a_row(4 * lane, tile.row, Fh) : (4 * lane < srows ? 4 * lane : 0));
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);   // LDS offset
     const uint32_t cdst = lds0 + op * TILEB + half * 8192;
-    const uint32_t sdst = lds0 + 2 * TILEB + op * SCB + half * BT;
+    const uint32_t sdst = lds0 + 2 * TILEB + op * SCBk + half * (FP4 ? 2 : 1) * BT;
 
     const int64_t kblocks = klen / 32;
-    const int KT = (int)((klen + BK - 1) / BK);
+    const int KT = (int)((klen + KS - 1) / KS);
     const bool half_tail = (klen & (BK - 1)) != 0;   // last stage holds one k-block (wgrad)
     const int tail_back = chunk >= 2 ? 32 : 0;        // that stage's missing chunks re-read valid k
 
@@ -232,17 +257,29 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     auto stage_of = [&](int v) { const int st = v - pre; return st < 0 ? 0 : (st < KT ? st : KT - 1); };
     // the loads of step v: 8 code pieces and one scale line
     struct IssueAt {
-        int64_t kc, kb;
+        int64_t kc, kb, kb2;
         uint32_t so;
     };
     auto issue_at = [&](int v) {
         const int kt = stage_of(v);
-        const int64_t k0 = (int64_t)kt * BK;
         IssueAt r;
-        r.kc = ((half_tail && kt == KT - 1) ? k0 - tail_back : k0) + chunk * 16;
-        r.kb = (k0 >> 5) + half;
-        r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
-        r.so = (uint32_t)(v % NSTAGE) * STAGEB;
+        if (FP4) {
+            // 16-byte chunk c of a stage row is k-block 4 kt + c; chunks past the last k-block
+            // re-read the last valid one (FP4 codes are always finite; their scale is 2^-127)
+            const int64_t vch = kblocks - 4 * (int64_t)kt;
+            const int64_t cc = chunk < vch ? chunk : vch - 1;
+            r.kc = (int64_t)kt * BK + cc * 16;
+            r.kb = 4 * (int64_t)kt + 2 * half;
+            r.kb2 = r.kb + 1 < kblocks ? r.kb + 1 : kblocks - 1;
+            r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
+        } else {
+            const int64_t k0 = (int64_t)kt * BK;
+            r.kc = ((half_tail && kt == KT - 1) ? k0 - tail_back : k0) + chunk * 16;
+            r.kb = (k0 >> 5) + half;
+            r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
+            r.kb2 = 0;
+        }
+        r.so = (uint32_t)(v % NSTAGE) * STAGEBk;
         return r;
     };
     auto issue_piece = [&](const IssueAt& r, int i) {
@@ -251,11 +288,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         dma16(cbase + src * cld + r.kc, cdst + r.so + i * 1024);
     };
     auto issue_scales = [&](const IssueAt& r) { dma4(sptr + r.kb * sld, sdst + r.so); };
+    auto issue_scales2 = [&](const IssueAt& r) { dma4(sptr + r.kb2 * sld, sdst + r.so + BT); };
     auto issue = [&](int v) {
         const IssueAt r = issue_at(v);
 #pragma unroll
         for (int i = 0; i < 8; i++) issue_piece(r, i);
         issue_scales(r);
+        if (FP4) issue_scales2(r);
     };
 
     const int lrow = lane & 31, hh = lane >> 5;
@@ -270,20 +309,40 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         const int kt = v - pre;
         return (kt < 0 || (half_tail && kt == KT - 1 && hh)) ? 0 : 0xFF;
     };
+    // FP4: k-step s of stage kt uses k-block 4 kt + 2 s + hh
+    auto frag_mask4 = [&](int v, int s) {
+        const int kt = v - pre;
+        return (kt < 0 || 4 * (int64_t)kt + 2 * s + hh >= kblocks) ? 0 : 0xFF;
+    };
     // (the scale mask is applied when the MFMA is issued, one step after the read: applying it at
     // the read would make the wavefront wait for the LDS byte right away)
     auto read_frag = [&](const uint8_t* base, int opb, int row, i32x8& f, int& sc) {
         const uint4 lo = *reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_lo);
         const uint4 hi = *reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_hi);
-        sc = (int)base[2 * TILEB + opb * SCB + hh * BT + row];
+        sc = (int)base[2 * TILEB + opb * SCBk + hh * BT + row];
         f = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
-    auto read_frags = [&](int v, Mx8Frags& f) {
-        const uint8_t* base = lds + (v % NSTAGE) * STAGEB;
+    // FP4: chunk hh is k-block hh of k-step 0 and chunk 2 + hh is k-block hh of k-step 1
+    auto read_frag4 = [&](const uint8_t* base, int opb, int row, i32x8& f0, i32x8& f1, int& s0, int& s1) {
+        f0 = lo4(*reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_lo));
+        f1 = lo4(*reinterpret_cast<const uint4*>(base + opb * TILEB + row * BK + off_hi));
+        s0 = (int)base[2 * TILEB + opb * SCBk + hh * BT + row];
+        s1 = (int)base[2 * TILEB + opb * SCBk + (2 + hh) * BT + row];
+    };
+    auto read_a = [&](const uint8_t* base, int i, Frags& f) {
+        if constexpr (FP4) read_frag4(base, 0, wr * 128 + i * 32 + lrow, f.a[i], f.a2[i], f.sa[i], f.sa2[i]);
+        else read_frag(base, 0, wr * 128 + i * 32 + lrow, f.a[i], f.sa[i]);
+    };
+    auto read_b = [&](const uint8_t* base, int j, Frags& f) {
+        if constexpr (FP4) read_frag4(base, 1, wc * 128 + j * 32 + lrow, f.b[j], f.b2[j], f.sb[j], f.sb2[j]);
+        else read_frag(base, 1, wc * 128 + j * 32 + lrow, f.b[j], f.sb[j]);
+    };
+    auto read_frags = [&](int v, Frags& f) {
+        const uint8_t* base = lds + (v % NSTAGE) * STAGEBk;
 #pragma unroll
-        for (int i = 0; i < 4; i++) read_frag(base, 0, wr * 128 + i * 32 + lrow, f.a[i], f.sa[i]);
+        for (int i = 0; i < 4; i++) read_a(base, i, f);
 #pragma unroll
-        for (int j = 0; j < 4; j++) read_frag(base, 1, wc * 128 + j * 32 + lrow, f.b[j], f.sb[j]);
+        for (int j = 0; j < 4; j++) read_b(base, j, f);
     };
 
     f32x16 acc[4][4];
@@ -302,36 +361,65 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     // min(v + 4, KV - 1) (near the end this re-loads the last stage, into a free slot or over
     // identical bytes) and the fragment read re-reads the last step once past it, so each step
     // waits for exactly two younger slots and no value is live only on some paths.
-    auto step = [&](int v, const Mx8Frags& cur, Mx8Frags& nxt) {
-        wait_loads_and_barrier<2 * LOADS_PER_STAGE>();
+    auto step = [&](int v, const Frags& cur, Frags& nxt) {
+        wait_loads_and_barrier<2 * LPS>();
         const IssueAt r = issue_at(v + NSTAGE < KV ? v + NSTAGE : KV - 1);
         const int vr = v + 1 < KV ? v + 1 : v;
-        const uint8_t* rbase = lds + (vr % NSTAGE) * STAGEB;
-        const int smask = frag_mask(v);
-        int sa[4], sb[4];
+        const uint8_t* rbase = lds + (vr % NSTAGE) * STAGEBk;
+        if constexpr (FP4) {
+            // k-step 0 of all 16 blocks, then k-step 1: an accumulator's two MFMAs are 16 apart
+            const int m0 = frag_mask4(v, 0), m1 = frag_mask4(v, 1);
+            int sa[4], sb[4], sa2[4], sb2[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            sa[i] = cur.sa[i] & smask;
-            sb[i] = cur.sb[i] & smask;
-        }
+            for (int i = 0; i < 4; i++) {
+                sa[i] = cur.sa[i] & m0;
+                sb[i] = cur.sb[i] & m0;
+                sa2[i] = cur.sa2[i] & m1;
+                sb2[i] = cur.sb2[i] & m1;
+            }
 #pragma unroll
-        for (int q = 0; q < 16; q++) {
-            const int i = q >> 2, j = q & 3;
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
-                                                                       sa[i], 0, sb[j]);
-            if (q < 8) issue_piece(r, q);
-            if (q == 8) issue_scales(r);
-            if (q >= 8 && q < 12) read_frag(rbase, 0, wr * 128 + (q - 8) * 32 + lrow, nxt.a[q - 8], nxt.sa[q - 8]);
-            if (q >= 12) read_frag(rbase, 1, wc * 128 + (q - 12) * 32 + lrow, nxt.b[q - 12], nxt.sb[q - 12]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int q = 0; q < 32; q++) {
+                const int i = (q >> 2) & 3, j = q & 3;
+                if (q < 16)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 4, 4, 0,
+                                                                               sa[i], 0, sb[j]);
+                else
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a2[i], cur.b2[j], acc[i][j], 4, 4,
+                                                                               0, sa2[i], 0, sb2[j]);
+                if (q < 8) issue_piece(r, q);
+                if (q == 8) issue_scales(r);
+                if (q == 9) issue_scales2(r);
+                if (q >= 16 && q < 20) read_a(rbase, q - 16, nxt);
+                if (q >= 20 && q < 24) read_b(rbase, q - 20, nxt);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            const int smask = frag_mask(v);
+            int sa[4], sb[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                sa[i] = cur.sa[i] & smask;
+                sb[i] = cur.sb[i] & smask;
+            }
+#pragma unroll
+            for (int q = 0; q < 16; q++) {
+                const int i = q >> 2, j = q & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0,
+                                                                           sa[i], 0, sb[j]);
+                if (q < 8) issue_piece(r, q);
+                if (q == 8) issue_scales(r);
+                if (q >= 8 && q < 12) read_frag(rbase, 0, wr * 128 + (q - 8) * 32 + lrow, nxt.a[q - 8], nxt.sa[q - 8]);
+                if (q >= 12) read_frag(rbase, 1, wc * 128 + (q - 12) * 32 + lrow, nxt.b[q - 12], nxt.sb[q - 12]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
     };
 
     if (KT > 0) {
 #pragma unroll
         for (int v = 0; v < NSTAGE; v++) issue(v < KV ? v : KV - 1);
-        Mx8Frags f0, f1;
-        wait_loads_and_barrier<3 * LOADS_PER_STAGE>();
+        Frags f0, f1;
+        wait_loads_and_barrier<3 * LPS>();
         read_frags(0, f0);
         for (int v = 0; v < KV; v += 2) {
             step(v, f0, f1);
@@ -466,16 +554,20 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
-                              hipStream_t stream)
+                              hipStream_t stream, bool fp4)
 {
     if (M == 0 || G == 0) return hipSuccess;
     const int64_t rt = (M + bwd::BT - 1) / bwd::BT + G, ct = Kf / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
-    Mx8Args p{dq, de, Nf, wt, wte, (int64_t)G * Nf, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN,
+    const int64_t bpv = fp4 ? 2 : 1;   // values per byte
+    Mx8Args p{dq, de, Nf / bpv, wt, wte, (int64_t)G * Nf / bpv, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN,
               nullptr, nullptr, nullptr, 0u};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
-    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
+    if (fp4)
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD, PMN_EPI_F32, true>), grid, dim3(bwd::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -510,15 +602,19 @@ hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t*
 
 hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
                               const uint8_t* xte, int64_t ld, const int64_t* po, int G,
-                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream)
+                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream, bool fp4)
 {
     if (G == 0) return hipSuccess;
     const int64_t rt = Nf / bwd::BT, ct = Kf / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
-    Mx8Args p{dt, dte, ld, xt, xte, ld, nullptr, po, ld, G, Nf, Kf, dw, rt, ct, SM, SN, nullptr, nullptr, nullptr, 0u};
+    const int64_t ldb = fp4 ? ld / 2 : ld;   // code bytes per row
+    Mx8Args p{dt, dte, ldb, xt, xte, ldb, nullptr, po, ld, G, Nf, Kf, dw, rt, ct, SM, SN, nullptr, nullptr, nullptr, 0u};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN, G));
-    hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
+    if (fp4)
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD, PMN_EPI_F32, true>), grid, dim3(bwd::THREADS), 0, stream, p);
+    else
+        hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_WGRAD>), grid, dim3(bwd::THREADS), 0, stream, p);
     return hipGetLastError();
 }
 

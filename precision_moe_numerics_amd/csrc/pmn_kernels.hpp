@@ -10,6 +10,10 @@
 
 namespace pmn {
 
+// requant / column-quantizer target beyond the public PMN_TARGET_* values: E2M1 codes packed two
+// per byte (slot 2j in the low nibble), the operand format of the FP4 backward GEMMs
+constexpr int TARGET_E2M1_PACKED = 2;
+
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
                                  uint8_t* scales, float* outer_out, hipStream_t stream);
@@ -20,7 +24,8 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
-                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather = nullptr);
+                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather = nullptr,
+                             bool fp4 = false);
 
 // Padded group offsets (each group rounded up to 32 slots) into padded_offsets [G+1].
 hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
@@ -38,7 +43,7 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
                              uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,
-                             int64_t* padded_offsets, hipStream_t stream);
+                             int64_t* padded_offsets, hipStream_t stream, int target = 0);
 
 hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                            int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
@@ -52,7 +57,7 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
-                              hipStream_t stream);
+                              hipStream_t stream, bool fp4 = false);
 
 hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t* xq, const uint8_t* xe,
                             const int64_t* offsets, const int64_t* po, int64_t Pb, int G, int64_t M, int64_t N,
@@ -61,7 +66,7 @@ hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t*
 
 hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* xt,
                               const uint8_t* xte, int64_t ld, const int64_t* po, int G,
-                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream);
+                              int64_t Nf, int64_t Kf, float* dw, hipStream_t stream, bool fp4 = false);
 
 hipError_t launch_swiglu_bwd(const float* da, const uint16_t* h13, int64_t M, int64_t F,
                              uint16_t* dh13, hipStream_t stream);

@@ -315,6 +315,35 @@ PMN_DEV int mxfp8_block(const uint32_t (&w)[16], int64_t r, int64_t kb, int64_t 
     return e;
 }
 
+// The same block to E2M1 (the FP4 backward): E8M0 by the smallest scale with amax <= 6 * 2^e,
+// codes packed two per byte (element 2j in the low nibble) into 4 words, RNE or SR.
+template <bool SR>
+PMN_DEV int mxfp4_block(const uint32_t (&w)[16], int64_t r, int64_t kb, int64_t N, uint64_t seed,
+                        uint32_t stream_id, uint32_t (&o)[4])
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+    const int e = e8m0_exponent<E8M0_E2M1>(amax);
+    const uint64_t idx0 = (uint64_t)r * (uint64_t)N + (uint64_t)(kb * 32);   // multiple of 8
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        uint32_t rw[4] = {0u, 0u, 0u, 0u};
+        if (SR) rand16x8(seed, stream_id, (idx0 >> 3) + q, rw);
+        uint32_t word = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            const uint32_t src = w[4 * q + j / 2];
+            const float y = __builtin_ldexpf((j & 1) ? bf16_hi(src) : bf16_lo(src), -e);
+            const uint32_t c = SR ? fp4_sr(y, (j & 1) ? (rw[j >> 1] >> 16) : (rw[j >> 1] & 0xFFFFu))
+                                  : ((uint32_t)PMN_CVT_FP4(0u, y, 0.0f, 0) & 0xFu);
+            word |= c << (4 * j);
+        }
+        o[q] = word;
+    }
+    return e;
+}
+
 PMN_DEV void load_block32(const uint16_t* x, int64_t word16, uint32_t (&w)[16])
 {
     const uint4* p = reinterpret_cast<const uint4*>(x) + 4 * word16;
@@ -354,8 +383,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 // k-block-major E8M0 [N/32 x ld_e8m0]: a workgroup takes 64 rows x 4 k-blocks (four threads
 // read 256 contiguous bytes of a row), and the scale bytes go through LDS so that each k-block's
 // 64 rows are written as one contiguous run. Column of row r: r (pad_off == nullptr), else
-// pad_off[g] + r - offsets[g] for r's group g.
-template <bool SR>
+// pad_off[g] + r - offsets[g] for r's group g. FP4: E2M1 codes packed two per byte, [M x N/2].
+template <bool SR, bool FP4 = false>
 __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restrict__ x, int64_t M,
                                                         int64_t N, uint64_t seed, uint32_t stream_id,
                                                         uint8_t* __restrict__ out,
@@ -371,11 +400,19 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
     {
         const int64_t r = r0 + (t >> 2), kb = kb0 + (t & 3);
         if (r < M && kb < nb) {
-            uint32_t w[16], o[8];
+            uint32_t w[16];
             load_block32(x, (gather ? (int64_t)gather[r] : r) * nb + kb, w);
-            const int e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
+            int e;
+            if (FP4) {
+                uint32_t o[4];
+                e = mxfp4_block<SR>(w, r, kb, N, seed, stream_id, o);
+                reinterpret_cast<uint4*>(out)[r * nb + kb] = make_uint4(o[0], o[1], o[2], o[3]);
+            } else {
+                uint32_t o[8];
+                e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
+                store_block32(out, r * nb + kb, o);
+            }
             se[t & 3][t >> 2] = (uint8_t)(e + 127);
-            store_block32(out, r * nb + kb, o);
         }
     }
     __syncthreads();
@@ -398,10 +435,11 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
-                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather)
+                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather, bool fp4)
 {
     const int64_t nb = N / 32;
     if (M * nb == 0) return hipSuccess;
+    if (fp4 && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
     if (padded_offsets == nullptr && ld_e8m0 == 0) {
         const int64_t grid = (M * nb + 255) / 256;
         if (sr)
@@ -413,6 +451,15 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((nb + 3) / 4));
+    if (fp4) {
+        if (sr)
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<true, true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id,
+                               out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        else
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<false, true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id,
+                               out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        return hipGetLastError();
+    }
     if (sr)
         hipLaunchKernelGGL((k_mxfp8_rows_kbm<true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id, out,
                            out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);

@@ -145,7 +145,8 @@ constexpr int TQ_RS = 128;
 
 PMN_DEV int tile_chunk(int row, int chunk) { return row * TQ_RS + ((chunk ^ ((row >> 3) & 7)) << 4); }
 
-// SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (nibble/byte).
+// SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (one code per
+// byte, SR only), 2 = E2M1 packed two per byte (slot 2j in the low nibble): out [cols x ld/2].
 template <int SRC, int ROUND, int TARGET>
 __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
 {
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                     }
                 }
             } else {
-                // E2M1 target (the pages' worked example): SR onto the FP4 grid
+                // E2M1 target (the pages' worked example and the FP4 backward): SR (or RNE, packed
+                // target only) onto the FP4 grid
 #pragma unroll
                 for (int jj = 0; jj < 16; jj++) {
                     const int j = half * 16 + jj;
@@ -293,14 +295,18 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                         } else {
                             bf8(xw[j], v);
                         }
-                        uint32_t rw[4];
-                        rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+                        uint32_t rw[4] = {0u, 0u, 0u, 0u};
+                        if (ROUND == 1)
+                            rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
 #pragma unroll
                         for (int c = 0; c < 8; c++) {
                             const float y = __builtin_ldexpf(v[c], -e[c]);
                             const uint32_t word = rw[c >> 1];
-                            const uint32_t code = fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
-                            o[c][jj >> 2] |= code << (8 * (jj & 3));
+                            const uint32_t code = (TARGET == 2 && ROUND == 0)
+                                                      ? ((uint32_t)PMN_CVT_FP4(0u, y, 0.0f, 0) & 0xFu)
+                                                      : fp4_sr(y, (c & 1) ? (word >> 16) : (word & 0xFFFFu));
+                            if (TARGET == 1) o[c][jj >> 2] |= code << (8 * (jj & 3));
+                            else o[c][jj >> 3] |= code << (4 * (jj & 7));
                         }
                     }
                 }
@@ -308,8 +314,11 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
 #pragma unroll
             for (int c = 0; c < 8; c++) {
                 const int row = lane * 8 + c;
-                *reinterpret_cast<uint4*>(tile + tile_chunk(row, w * 2 + half)) =
-                    make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
+                if (TARGET == 2)   // 16 slots = 8 bytes: half h of chunk w
+                    *reinterpret_cast<uint2*>(tile + tile_chunk(row, w) + 8 * half) = make_uint2(o[c][0], o[c][1]);
+                else
+                    *reinterpret_cast<uint4*>(tile + tile_chunk(row, w * 2 + half)) =
+                        make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
             }
         }
     }
@@ -318,14 +327,28 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
     // ---- store: 512 rows x 8 chunks of 16 bytes; a chunk is written if its column exists and its
     // 32-slot block lies inside the padded output.
     const int64_t col_base = (int64_t)blockIdx.y * 512;
+    if (TARGET == 2) {
+        // packed: 512 rows x 4 chunks of 16 bytes (one 32-slot block each)
 #pragma unroll 4
-    for (int k = 0; k < 16; k++) {
-        const int q = k * 256 + threadIdx.x;
-        const int row = q >> 3, chunk = q & 7;
-        const int64_t col = col_base + row;
-        if (col < a.cols && block_live[chunk >> 1]) {
-            const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, chunk));
-            *reinterpret_cast<uint4*>(a.out + col * a.ld + (int64_t)blockIdx.x * 128 + chunk * 16) = v;
+        for (int k = 0; k < 8; k++) {
+            const int q = k * 256 + threadIdx.x;
+            const int row = q >> 2, chunk = q & 3;
+            const int64_t col = col_base + row;
+            if (col < a.cols && block_live[chunk]) {
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, chunk));
+                *reinterpret_cast<uint4*>(a.out + col * (a.ld >> 1) + (int64_t)blockIdx.x * 64 + chunk * 16) = v;
+            }
+        }
+    } else {
+#pragma unroll 4
+        for (int k = 0; k < 16; k++) {
+            const int q = k * 256 + threadIdx.x;
+            const int row = q >> 3, chunk = q & 7;
+            const int64_t col = col_base + row;
+            if (col < a.cols && block_live[chunk >> 1]) {
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, chunk));
+                *reinterpret_cast<uint4*>(a.out + col * a.ld + (int64_t)blockIdx.x * 128 + chunk * 16) = v;
+            }
         }
     }
 #pragma unroll
@@ -362,9 +385,14 @@ static hipError_t launch_transpose(const TransposeArgs& a, int src, int round, i
         if (target == 0) {
             if (round == 1) hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 1, 0>), grid, dim3(256), 0, stream, a);
             else hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 0, 0>), grid, dim3(256), 0, stream, a);
-        } else {
+        } else if (target == 1) {
             hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 1, 1>), grid, dim3(256), 0, stream, a);
+        } else {
+            hipLaunchKernelGGL((k_transpose_quant<SRC_NVFP4, 1, 2>), grid, dim3(256), 0, stream, a);
         }
+    } else if (target == 2) {
+        if (round == 1) hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 1, 2>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 0, 2>), grid, dim3(256), 0, stream, a);
     } else {
         if (round == 1) hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 1, 0>), grid, dim3(256), 0, stream, a);
         else hipLaunchKernelGGL((k_transpose_quant<SRC_BF16, 0, 0>), grid, dim3(256), 0, stream, a);
@@ -389,14 +417,14 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
                              uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,
-                             int64_t* padded_offsets, hipStream_t stream)
+                             int64_t* padded_offsets, hipStream_t stream, int target)
 {
     TransposeArgs a{};
     a.e8m0_kb_major = e8m0_kb_major;
     a.codes = nullptr; a.scales = nullptr; a.outer = nullptr; a.rows_per_outer = 1;
     a.x = x; a.cols = N; a.gather = nullptr; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
-    return launch_transpose(a, SRC_BF16, sr ? 1 : 0, 0, padded_offsets, stream);
+    return launch_transpose(a, SRC_BF16, sr ? 1 : 0, target, padded_offsets, stream);
 }
 
 }  // namespace pmn

@@ -1,0 +1,115 @@
+"""Parity of the FP4 backward variant (moe_grouped_gemm_bwd with PMN_BWD_FP4) with the CPU oracle.
+
+Every operand is quantized to MXFP4 (E2M1 codes, one E8M0 per 32 values, no saturation): dY
+row-wise and column-wise per group (round to nearest even or stochastic), W^T and A^T requantized
+from the saved NVFP4 operands by stochastic rounding. The workspace's packed codes and scales are
+compared bit for bit with the oracle's own quantization of the same original inputs (packed two
+per byte by the test); dgrad and wgrad within 2e-3 relative Frobenius error of the oracle's fp64
+products (products of E2M1 values are exact; only the fp32 accumulation rounds).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+E2M1 = O.TARGET_E2M1
+
+
+def npy(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def rel_fro(got, ref):
+    ref = np.asarray(ref, np.float64)
+    return np.linalg.norm(np.asarray(got, np.float64) - ref) / max(np.linalg.norm(ref), 1e-300)
+
+
+def pack(codes):
+    """One E2M1 code per byte -> two per byte, element 2j in the low nibble."""
+    c = np.asarray(codes, np.uint8)
+    return (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+
+
+@pytest.fixture(scope="module")
+def P():
+    import precision_moe_numerics_amd as P
+    return P
+
+
+def _layer(counts, N, K, gather_rows, seed):
+    from precision_moe_numerics_amd import inputs as I
+    import precision_moe_numerics_amd as P
+    rng = np.random.default_rng(seed)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    M, G = int(offsets[-1]), len(counts)
+    T = gather_rows or M
+    x = I.student_t((T, K), 4, 1.0, seed + 1)
+    w = I.normal((G * N, K), 0.02, seed + 2)
+    dy = I.normal((M, N), 1e-3, seed + 3)
+    gather = rng.integers(0, T, M).astype(np.int32) if gather_rows else None
+    rpo = N // 2
+    d = dict(offsets=offsets, M=M, G=G, x=x, w=w, dy=dy, gather=gather,
+             xq=P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT), wq=P.nvfp4_quantize(w.to(DEV), P.NVFP4_WEIGHT, rpo),
+             rxq=O.nvfp4_quantize(x, 1, True), rwq=O.nvfp4_quantize(w, rpo, False),
+             goff=torch.as_tensor(offsets, device=DEV),
+             ggather=None if gather is None else torch.as_tensor(gather, device=DEV))
+    return d
+
+
+@pytest.mark.parametrize("counts,N,K,gather_rows,sr", [([40, 0, 333, 227], 256, 512, 400, False),
+                                                        ([150, 1, 95, 33], 256, 256, 300, True),
+                                                        ([700], 512, 256, None, False)])
+def test_fp4_backward_operands_and_gradients(P, counts, N, K, gather_rows, sr):
+    d = _layer(counts, N, K, gather_rows, seed=300 + len(counts))
+    M, G = d["M"], d["G"]
+    seed, sa, sb, sdy = 11, 4, 1, 6
+    da, db, ws = P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, N,
+                                        flags=P.BWD_DGRAD | P.BWD_WGRAD | P.BWD_FP4, gather=d["ggather"],
+                                        dy_rounding=P.SR if sr else P.RNE, seed=seed, rng_stream_a=sa,
+                                        rng_stream_b=sb, rng_stream_dy=sdy)
+    v = P.bwd_workspace_views(ws, M, G, N, K, fp4=True)
+    off = d["offsets"]
+    po = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
+    grp = np.searchsorted(off, np.arange(M), side="right") - 1
+    pcol = po[grp] + np.arange(M) - off[grp]
+    Pt = int(po[-1])
+    # dY row-wise (the dgrad's A) and column-wise per group (the wgrad's A)
+    rq, re = O.mxfp8_quantize_rows(d["dy"], sr=sr, seed=seed, stream=sdy, target=E2M1)
+    assert np.array_equal(npy(v["dq"]), pack(rq)) and np.array_equal(npy(v["de"])[:, pcol].T, re)
+    rt, rte = O.mxfp8_quantize_cols(d["dy"], offsets=off, sr=sr, seed=seed, stream=sdy + 1, target=E2M1)
+    assert np.array_equal(npy(v["dt"])[:, :Pt // 2], pack(rt)) and np.array_equal(npy(v["dte"]).T[:, :Pt // 32], rte)
+    # W^T and A^T requantized by SR onto the E2M1 grid
+    rwt, rwte = O.requant_transpose_sr(d["rwq"], target=E2M1, seed=seed, stream=sb)
+    assert np.array_equal(npy(v["wt"]), pack(rwt)) and np.array_equal(npy(v["wte"]).T, rwte)
+    rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=off, target=E2M1, seed=seed, stream=sa)
+    assert np.array_equal(npy(v["xt"])[:, :Pt // 2], pack(rxt)) and np.array_equal(npy(v["xte"]).T[:, :Pt // 32], rxte)
+    # gradients on the FP4 MFMA
+    da_ref = O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, off, N, K, target=E2M1)
+    db_ref = O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, off, N, K, target=E2M1)
+    assert rel_fro(npy(da), da_ref) <= 2e-3
+    assert rel_fro(npy(db), db_ref) <= 2e-3
+    for g in range(G):
+        if off[g + 1] == off[g]:
+            assert np.all(npy(db)[g * N:(g + 1) * N] == 0)     # an empty expert gets a zero gradient
+
+
+def test_fp4_backward_deterministic_and_separate_flags(P):
+    d = _layer([200, 56], 256, 256, None, seed=330)
+    M = d["M"]
+    f = P.BWD_DGRAD | P.BWD_WGRAD | P.BWD_FP4
+    a1 = P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256, flags=f, dy_rounding=P.SR, seed=3)
+    a2 = P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256, flags=f, dy_rounding=P.SR, seed=3)
+    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+    only_d = P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256,
+                                    flags=P.BWD_DGRAD | P.BWD_FP4, dy_rounding=P.SR, seed=3)
+    only_w = P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256,
+                                    flags=P.BWD_WGRAD | P.BWD_FP4, dy_rounding=P.SR, seed=3)
+    assert torch.equal(only_d[0], a1[0]) and torch.equal(only_w[1], a1[1])
+    # FP4 alone, without a gradient, is not a request
+    with pytest.raises(P.PmnError):
+        P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256, flags=P.BWD_FP4)
