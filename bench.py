@@ -19,6 +19,9 @@ input buffers larger than the 256 MB Infinity Cache, as GB/s of algorithmic byte
 Also reported: the MXFP8 forward of the layers that keep MXFP8, on the same layer shape (w13 with
 SwiGLU, w2 with RHT32 + S2F6, each call including its MXFP8 quantization), as TFLOP/s.
 
+Also reported: the FP4 backward variant on the same layer (every backward operand in MXFP4, the
+GEMMs on the block-scaled FP4 MFMA), as TFLOP/s.
+
 Also reported: the receiver side of the combine (moe_combine_s2f6) on the routed shape, 16384
 tokens with top-8 of 32 experts gathered back from 131072 S2F6 rows of hidden 4096, as GB/s.
 
@@ -39,6 +42,7 @@ METRIC = "NVFP4/MXFP8-SR quantize GB/s + MoE grouped GEMM TFLOPS, % of MI355X ro
 PEAK_HBM_GBS = 8000.0          # MI355X published HBM3E bandwidth
 PEAK_F16_TFLOPS = 2500.0       # MI355X dense MFMA fp16/bf16
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense MFMA fp8
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MFMA fp4
 
 
 def parse():
@@ -270,6 +274,45 @@ def mxfp8_forward_workload(P, I, torch, layer, iters):
     return res
 
 
+def fp4_backward_workload(P, torch, layer, iters):
+    """The FP4 backward variant on the same layer: w2 and w13 backward with every operand in MXFP4
+    (E2M1 + E8M0/32, SR) and the GEMMs on the block-scaled FP4 MFMA, each call including its
+    quantization and requantization. TFLOP/s of the GEMM work against the FP4 peak."""
+    M, H, F = layer.M, layer.H, layer.F
+    w13q = P.nvfp4_quantize(layer.w13, P.NVFP4_WEIGHT, F)
+    w2q = P.nvfp4_quantize(layer.w2, P.NVFP4_WEIGHT, H)
+    xq = P.nvfp4_quantize(layer.x, P.NVFP4_ACT)
+    a, h13 = P.moe_grouped_gemm_fwd(xq, w13q, layer.offsets, M, 2 * F, P.EPI_SWIGLU, gather=layer.gather,
+                                     save_h13=True)
+    aq = P.nvfp4_quantize(a, P.NVFP4_ACT)
+    dh13 = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=a.device).normal_(0, 1e-3)
+    flags = P.BWD_DGRAD | P.BWD_WGRAD | P.BWD_FP4
+
+    def w2():
+        P.moe_grouped_gemm_bwd(layer.dy, aq, w2q, layer.offsets, M, H, flags=flags, seed=layer.seed, rng_stream_a=5,
+                                rng_stream_b=3, rng_stream_dy=6, workspace=layer.ws2)
+
+    def w13():
+        P.moe_grouped_gemm_bwd(dh13, xq, w13q, layer.offsets, M, 2 * F, flags=flags, gather=layer.gather,
+                                seed=layer.seed, rng_stream_a=4, rng_stream_b=1, rng_stream_dy=8, workspace=layer.ws13)
+    res = {}
+    fl = layer.flops()
+    for name, fn, flops in (("w2", w2, 2 * fl["fwd2"]), ("w13", w13, 2 * fl["fwd13"])):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / iters
+        t = flops / (ms * 1e-3) / 1e12
+        res[name] = dict(ms_incl_quant=ms, tflops_incl_quant=t, frac_fp4_peak=t / PEAK_FP4_TFLOPS)
+    return res
+
+
 def cpu_baseline(I, shape):
     """The CPU oracle (as it stands) on a bounded sample of the same step: 16 slots of one expert
     through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
@@ -383,6 +426,7 @@ def main():
         quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
 
     mx8 = mxfp8_forward_workload(P, I, torch, layer, max(args.quant_iters // 4, 3))
+    fp4b = fp4_backward_workload(P, torch, layer, max(args.quant_iters // 4, 3))
     comb = combine_workload(P, I, torch, dev, args.quant_iters)
     comb["frac_of_measured_copy"] = comb["gbs"] / quant["hbm_copy_gbs"]
 
@@ -401,7 +445,7 @@ def main():
             "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
             "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
             "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant, "combine_workload": comb,
-            "mxfp8_forward": mx8,
+            "mxfp8_forward": mx8, "fp4_backward": fp4b,
             "wall_s_timed": wall}
     print(json.dumps(line))
 

@@ -113,3 +113,52 @@ def test_fp4_backward_deterministic_and_separate_flags(P):
     # FP4 alone, without a gradient, is not a request
     with pytest.raises(P.PmnError):
         P.moe_grouped_gemm_bwd(d["dy"].to(DEV), d["xq"], d["wq"], d["goff"], M, 256, flags=P.BWD_FP4)
+
+
+def test_fp4_backward_full_size_ep48_sampled(P):
+    """The 48-expert layer's w13 backward in FP4, in the launch configuration the bench times:
+    sampled dX and dW values against the oracle's own quantization of the original inputs (W_g^T
+    and X^T windows taken from full-size arrays in which only the sampled rows are filled). dY is
+    rounded to nearest here, so a sampled row or group quantizes on its own; stochastic dY
+    rounding is covered bit for bit by the smaller cases above."""
+    from precision_moe_numerics_amd import inputs as I
+    from fullsize_helpers import oracle_quant_rows, sample_slots as _sample_slots
+    sh = I.EP48
+    E, H, F = sh.experts, sh.hidden, sh.ffn
+    N, K = 2 * F, H
+    off = np.concatenate([[0], np.cumsum(I.moe_loads(sh))]).astype(np.int64)
+    M = int(off[-1])
+    x = I.moe_activations(sh, DEV)
+    w13, _ = I.moe_weights(sh, DEV)
+    xq = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    wq = P.nvfp4_quantize(w13.view(E * N, H), P.NVFP4_WEIGHT, F)
+    dy = I.normal((M, N), 1e-3, 602, DEV)
+    seed = sh.seeds["sr"]
+    da, db, _ = P.moe_grouped_gemm_bwd(dy, xq, wq, torch.as_tensor(off, device=DEV), M, N,
+                                       flags=P.BWD_DGRAD | P.BWD_WGRAD | P.BWD_FP4, dy_rounding=P.RNE, seed=seed,
+                                       rng_stream_a=4, rng_stream_b=1, rng_stream_dy=8)
+    dyh = dy.cpu()
+    rng = np.random.default_rng(41)
+    got, ref = [], []
+    for g in (0, E - 1):
+        wh = oracle_quant_rows(w13[g].cpu(), E * N, g * N, F, False)
+        wt, wte = O.requant_window(wh, g * N, N, target=E2M1, seed=seed, stream=1)
+        for s in _sample_slots(off, [g], 4, rng):
+            dq, de = O.mxfp8_quantize_rows(dyh[int(s):int(s) + 1], target=E2M1)
+            for k in (0, K - 1, int(rng.integers(0, K))):
+                ref.append(O.mxfp8_dot(dq, de, wt, wte, 0, k, 0, N, target=E2M1))
+                got.append(float(da[int(s), k]))
+    assert rel_fro(got, ref) <= 2e-3
+    got, ref = [], []
+    for g in (E - 1, E - 2, 20):
+        a, b = int(off[g]), int(off[g + 1])
+        dt, dte = O.mxfp8_quantize_cols(dyh[a:b], target=E2M1)
+        xh = oracle_quant_rows(x[a:b].cpu(), M, a, 1, True)
+        xt, xte = O.requant_window(xh, a, b - a, target=E2M1, seed=seed, stream=4)
+        Pg = dt.shape[1]
+        for n in (0, N - 1, int(rng.integers(0, N))):
+            for k in (0, K - 1, int(rng.integers(0, K))):
+                ref.append(O.mxfp8_dot(dt, dte, xt, xte, n, k, 0, Pg, target=E2M1))
+                got.append(float(db[g * N + n, k]))
+    assert rel_fro(got, ref) <= 2e-3
+
