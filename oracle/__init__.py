@@ -88,6 +88,7 @@ def _declare(L):
         "orc_moe_combine_s2f6": (None, [P, P, I64, I64, U32, P, P, I64, I32, P]),
         "orc_s2f6_quantize": (None, [P, I64, I64, P, P]),
         "orc_gemm_mxfp8_fwd": (None, [P, P, P, P, P, P, I32, I64, I64, P]),
+        "orc_nvfp4_quantize_2d": (None, [P, I64, I64, I64, P, P, P]),
         "orc_mx_quantize_rows": (None, [P, I64, I64, I32, I32, U64, U32, P, P]),
         "orc_mx_quantize_cols": (None, [P, I64, I64, P, I32, I32, I32, U64, U32, P, P]),
         "orc_gemm_mx_dgrad": (None, [P, P, P, P, P, I32, I64, I64, I32, P]),
@@ -220,6 +221,18 @@ def padded_total(offsets, M: int) -> int:
         return lib().orc_padded_total(None, 0, M)
     o = np.ascontiguousarray(offsets, np.int64)
     return lib().orc_padded_total(_p(o), len(o) - 1, M)
+
+
+def nvfp4_quantize_2d(x_bf16, rows_per_outer: int):
+    """NVFP4 with 16 x 16 blocks: dict(codes, scales [R, C/16] equal within a tile, outer)."""
+    x = _u16(x_bf16)
+    R, Cc = x.shape
+    assert R % 16 == 0 and Cc % 16 == 0 and rows_per_outer % 16 == 0 and R % rows_per_outer == 0
+    codes = np.zeros((R, Cc // 2), np.uint8)
+    scales = np.zeros((R, Cc // 16), np.uint8)
+    outer = np.zeros(R // rows_per_outer, np.float32)
+    lib().orc_nvfp4_quantize_2d(_p(x), R, Cc, rows_per_outer, _p(codes), _p(scales), _p(outer))
+    return dict(codes=codes, scales=scales, outer=outer, rows_per_outer=rows_per_outer)
 
 
 def requant_transpose_sr(q, gather=None, offsets=None, M=None, target=TARGET_E4M3, seed=0, stream=0):

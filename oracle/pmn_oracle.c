@@ -301,6 +301,59 @@ void orc_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t r
     }
 }
 
+/*
+ * NVFP4 with square 16 x 16 blocks ([AREX S3]: the blocking NVIDIA uses so that a tensor and its
+ * transpose quantize bit-identically; the pages reject it because 256 values share one scale).
+ * Tile (I, J) = rows 16I .. 16I+15, columns 16J .. 16J+15 has a_t = max|x| over its 256 values;
+ * every row segment of the tile is quantized as a weight-mode block (candidate 6, no 4/6) whose
+ * amax is a_t: t = RN(RN(a_t / 6) / s_o), sb = E4M3(t) RNE saturating, d = RN(value(sb) s_o),
+ * r = RN(1/d), q = FP4(RN(x r)). Outer scale per group of rows_per_outer rows (a multiple of 16).
+ * The scale is stored once per row segment ([rows x cols/16], the 1D layout, equal within a
+ * tile), so the result is an ordinary NVFP4 matrix.
+ */
+void orc_nvfp4_quantize_2d(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_outer, uint8_t* codes,
+                           uint8_t* scales, float* outer_out)
+{
+    for (int64_t g = 0; g < rows / rows_per_outer; g++) {
+        float A = 0.0f;
+        for (int64_t r = g * rows_per_outer; r < (g + 1) * rows_per_outer; r++)
+            for (int64_t c = 0; c < cols; c++) {
+                float m = fabsf(orc_bf16_to_f32(x[r * cols + c]));
+                if (m > A) A = m;
+            }
+        outer_out[g] = orc_outer_scale(A);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t I = 0; I < rows / 16; I++)
+        for (int64_t J = 0; J < cols / 16; J++) {
+            float at = 0.0f;
+            for (int64_t r = 16 * I; r < 16 * I + 16; r++)
+                for (int64_t c = 16 * J; c < 16 * J + 16; c++) {
+                    float m = fabsf(orc_bf16_to_f32(x[r * cols + c]));
+                    if (m > at) at = m;
+                }
+            const float s_o = outer_out[(16 * I) / rows_per_outer];
+            volatile float t1 = at / 6.0f;
+            volatile float t = t1 / s_o;
+            const uint8_t sb = orc_e4m3_encode(t, ORC_RNE, 0);
+            volatile float d = (float)orc_e4m3_value(sb) * s_o;
+            float rcp = 0.0f;
+            if (d != 0.0f) {
+                volatile float inv = 1.0f / d;
+                rcp = (inv > FLT_MAX) ? FLT_MAX : inv;
+            }
+            for (int64_t r = 16 * I; r < 16 * I + 16; r++) {
+                scales[r * (cols / 16) + J] = sb;
+                for (int i = 0; i < 16; i += 2) {
+                    volatile float y0 = orc_bf16_to_f32(x[r * cols + 16 * J + i]) * rcp;
+                    volatile float y1 = orc_bf16_to_f32(x[r * cols + 16 * J + i + 1]) * rcp;
+                    codes[r * (cols / 2) + 8 * J + i / 2] =
+                        (uint8_t)(orc_fp4_encode(y0, ORC_RNE, 0) | (orc_fp4_encode(y1, ORC_RNE, 0) << 4));
+                }
+            }
+        }
+}
+
 /* Effective scale of block (row r, block b) of an NVFP4 matrix: d = RN(value(sb) * s_o). */
 static float nvfp4_block_scale(const uint8_t* scales, const float* outer, int64_t cols,
                                int64_t rows_per_outer, int64_t r, int64_t b)

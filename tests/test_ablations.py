@@ -84,3 +84,71 @@ if __name__ == "__main__":      # prints the table of errors (run from the repos
     for kind in ("gaussian", "outlier_rows", "chunk_outliers", "student_t3"):
         r = errors(kind)
         print(kind, {k: (round(a, 5), round(b, 5)) for k, (a, b) in r.items()})
+
+
+# ------------------------------------------------------------------------------------------
+# The transpose problem ([AREX] "转置打散分组,随机舍入保住期望值"): zeros after the transpose under
+# outlier rows, for 1D blocks re-quantized by rounding to nearest, 16 x 16 blocks, and the
+# pages' method (dequantize, transpose, stochastic rounding to MXFP8). Workload: X [256 x 512]
+# N(0,1) with two rows x 50 (the single-expert inputs).
+# ------------------------------------------------------------------------------------------
+
+def _fp4_vals(codes):
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    c = np.zeros((codes.shape[0], codes.shape[1] * 2), np.int64)
+    c[:, 0::2], c[:, 1::2] = codes & 15, codes >> 4
+    return np.where(c & 8, -1.0, 1.0) * grid[c & 7]
+
+
+def _nvfp4_values(q):
+    """fp64 values of an NVFP4 matrix (codes x E4M3 scale x outer)."""
+    s = torch.from_numpy(q["scales"]).view(torch.float8_e4m3fn).double().numpy()
+    outer = np.repeat(q["outer"], q["rows_per_outer"])
+    return _fp4_vals(q["codes"]) * np.repeat(s, 16, axis=1) * outer[:, None]
+
+
+def transpose_zero_fractions():
+    from precision_moe_numerics_amd import inputs as I
+    d = I.single_expert("cpu")
+    x, rows = d["x"], d["outlier_rows"]
+    R, C = x.shape
+    fwd = O.nvfp4_quantize(x, 1, True)                         # forward: 1D, per token, 4/6
+    v = _nvfp4_values(fwd)                                      # the saved forward values
+    live = (v != 0)
+    # blocks that hold an outlier-row value after the transpose: every 16-block of columns that
+    # spans one of the outlier rows, i.e. rows (16 * (r // 16)) .. + 15 of each column
+    band = np.zeros((R, C), bool)
+    for r in rows:
+        band[16 * (r // 16):16 * (r // 16) + 16] = True
+    ordinary = band & live & ~np.isin(np.arange(R), rows)[:, None]
+    res = {}
+    # (1) 1D blocks, re-quantized by RTN along the transposed direction (weight mode: no 4/6)
+    vt = torch.tensor(v.T, dtype=torch.float32).to(torch.bfloat16)
+    naive = _nvfp4_values(O.nvfp4_quantize(vt, rows_per_outer=C, four_six=False)).T
+    res["1d_rtn_transposed"] = float((naive[ordinary] == 0).mean())
+    # (2) 16 x 16 blocks: the forward itself already shares the outlier's scale over the tile
+    q2 = O.nvfp4_quantize_2d(x, R)
+    v2 = _nvfp4_values(q2)
+    res["2d_16x16"] = float((v2[ordinary] == 0).mean())
+    # (3) the method: dequantize -> transpose -> SR to MXFP8 (and, for reference, to the E2M1 grid)
+    q = dict(codes=fwd["codes"], scales=fwd["scales"], outer=fwd["outer"], rows_per_outer=1)
+    t8, e8 = O.requant_transpose_sr(q, seed=7, stream=1)
+    m8 = O.mxfp8_dequantize(t8, e8)[:, :R].T
+    res["sr_mxfp8"] = float((m8[ordinary] == 0).mean())
+    t4, e4 = O.requant_transpose_sr(q, target=O.TARGET_E2M1, seed=7, stream=1)
+    m4 = (np.where(t4 & 8, -1.0, 1.0) * np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])[t4 & 7]
+          * np.repeat(2.0 ** (e4.astype(np.float64) - 127), 32, axis=1))[:, :R].T
+    res["sr_e2m1"] = float((m4[ordinary] == 0).mean())
+    res["ordinary_values"] = int(ordinary.sum())
+    res["forward_zero_fraction"] = float((v[band & ~np.isin(np.arange(R), rows)[:, None]] == 0).mean())
+    return res
+
+
+def test_transpose_zero_fractions_under_outlier_rows():
+    """1D blocks re-quantized after the transpose and 16 x 16 blocks both lose most ordinary values
+    of the blocks an outlier row crosses; the method (SR to MXFP8 after dequantizing) keeps them."""
+    r = transpose_zero_fractions()
+    assert r["1d_rtn_transposed"] > 0.5, r
+    assert r["2d_16x16"] > 0.5, r
+    assert r["sr_mxfp8"] < 0.01, r
+    assert r["forward_zero_fraction"] < 0.2, r

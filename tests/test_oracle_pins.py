@@ -830,3 +830,40 @@ def test_mxfp4_gemms_vs_dense_products():
         assert np.allclose(dW[g * N:(g + 1) * N], ref, rtol=1e-6, atol=1e-12)
     # one sampled element through the generic dot
     assert np.isclose(O.mxfp8_dot(dt, dte, xt, xte, 5, 7, 32, 96, target=O.TARGET_E2M1), dW[2 * N + 5, 7], rtol=1e-6)
+
+
+# ------------------------------------------------------------------------------------------
+# 16 x 16 square blocks
+# ------------------------------------------------------------------------------------------
+
+def _nibbles(codes):
+    c = np.asarray(codes)
+    out = np.zeros((c.shape[0], c.shape[1] * 2), np.uint8)
+    out[:, 0::2], out[:, 1::2] = c & 15, c >> 4
+    return out
+
+
+def test_2d_blocks_transpose_bit_identity_and_tile_scales():
+    """Quantizing X^T gives exactly the transpose of X's codes and (tile) scales: a square block
+    is the same set of values either way ([AREX S3])."""
+    rng = np.random.default_rng(27)
+    x = bf16(rng.standard_t(3, (64, 96)))
+    a = O.nvfp4_quantize_2d(x, 64)
+    b = O.nvfp4_quantize_2d(x.t().contiguous(), 96)
+    assert np.array_equal(_nibbles(b["codes"]), _nibbles(a["codes"]).T)
+    assert a["outer"][0] == b["outer"][0]
+    tiles = a["scales"].reshape(4, 16, 6)
+    assert np.all(tiles == tiles[:, :1, :])                   # one scale per tile
+    assert np.array_equal(tiles[:, 0, :].T, b["scales"].reshape(6, 16, 4)[:, 0, :])
+
+
+def test_2d_blocks_reduce_to_1d_when_tile_rows_repeat():
+    """If the 16 rows of every tile are equal, each tile's amax is its rows' block amax and the 2D
+    result equals the 1D weight-mode quantization."""
+    rng = np.random.default_rng(28)
+    base = rng.standard_normal((4, 128)) * np.exp(rng.uniform(-3, 3, (4, 1)))
+    x = bf16(np.repeat(base, 16, axis=0))
+    a = O.nvfp4_quantize_2d(x, 32)
+    b = O.nvfp4_quantize(x, rows_per_outer=32, four_six=False)
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+    assert np.array_equal(a["outer"], b["outer"])
