@@ -425,6 +425,19 @@ def main():
         quant[k]["frac_of_8TBs"] = quant[k]["gbs"] / PEAK_HBM_GBS
         quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
 
+    # 16 x 16 square-block NVFP4 of the w13 weights, beside the 1D weight mode of the same call
+    sq = {}
+    for name, mode in (("weight_1d", P.NVFP4_WEIGHT), ("weight_16x16", P.NVFP4_WEIGHT_2D)):
+        for _ in range(2):
+            P.nvfp4_quantize(layer.w13, mode, layer.F)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            P.nvfp4_quantize(layer.w13, mode, layer.F)
+        e1.record()
+        torch.cuda.synchronize()
+        sq[name] = dict(ms=e0.elapsed_time(e1) / 5)
     mx8 = mxfp8_forward_workload(P, I, torch, layer, max(args.quant_iters // 4, 3))
     fp4b = fp4_backward_workload(P, torch, layer, max(args.quant_iters // 4, 3))
     comb = combine_workload(P, I, torch, dev, args.quant_iters)
@@ -445,7 +458,7 @@ def main():
             "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
             "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
             "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant, "combine_workload": comb,
-            "mxfp8_forward": mx8, "fp4_backward": fp4b,
+            "mxfp8_forward": mx8, "fp4_backward": fp4b, "nvfp4_w13_blocking": sq,
             "wall_s_timed": wall}
     print(json.dumps(line))
 

@@ -83,6 +83,10 @@ int64_t pmn_padded_bound(int64_t M, int G);
 
 #define PMN_NVFP4_WEIGHT 0 /* one scale candidate (the block max maps to 6) */
 #define PMN_NVFP4_ACT    1 /* 4/6: candidates 6 and 4, the smaller squared error is kept (ties: 6) */
+#define PMN_NVFP4_WEIGHT_2D 2 /* 16 x 16 square blocks (the blocking the transpose section of [AREX]
+                                 contrasts with the method): as WEIGHT with each block's amax taken
+                                 over its 16 x 16 tile; the scale byte is stored per row segment
+                                 (equal within a tile). rows and rows_per_outer multiples of 16. */
 
 /*
  * x: bf16 [rows x cols], cols % 16 == 0, 16-byte aligned.

@@ -56,7 +56,7 @@ def _load():
 _lib = _load()
 
 # ---- constants of include/pmn.h -------------------------------------------------------------
-NVFP4_WEIGHT, NVFP4_ACT = 0, 1
+NVFP4_WEIGHT, NVFP4_ACT, NVFP4_WEIGHT_2D = 0, 1, 2
 TARGET_E4M3, TARGET_E2M1 = 0, 1
 ROWWISE, COLWISE = 0, 1
 RNE, SR = 0, 1

@@ -16,7 +16,7 @@ constexpr int TARGET_E2M1_PACKED = 2;
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
-                                 uint8_t* scales, float* outer_out, hipStream_t stream);
+                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square = false);
 
 // Row-wise MXFP8. With padded_offsets null the E8M0 scales are row-major [M x N/32]; otherwise
 // they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column

@@ -167,6 +167,41 @@ __global__ __launch_bounds__(256) void k_nvfp4_given(const uint16_t* __restrict_
     scales[i] = (uint8_t)sb;
 }
 
+// 16 x 16 square blocks ([AREX] "转置打散分组,随机舍入保住期望值": the blocking NVIDIA uses so that
+// a tensor and its transpose quantize bit-identically). A wavefront takes a band of 16 rows x 4
+// tiles; lane l holds row l % 16 of tile l / 16 (16 values) and the tile amax is a 4-step
+// butterfly max over the tile's 16 lanes. Each row segment is then a weight-mode block whose amax
+// is the tile's; the scale byte is stored per row segment (equal within the tile).
+__global__ __launch_bounds__(256) void k_nvfp4_2d(const uint16_t* __restrict__ x, int64_t rows, int64_t cols,
+                                                  int64_t rows_per_outer, const float* __restrict__ outer,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t tiles_c = cols >> 4;
+    const int64_t strips = (tiles_c + 3) >> 2;
+    const int64_t band = wave / strips;
+    if (band >= (rows >> 4)) return;                     // wavefront-uniform
+    const int64_t J = (wave - band * strips) * 4 + (lane >> 4);
+    const int64_t r = band * 16 + (lane & 15);
+    const bool ok = J < tiles_c;
+    Block16 blk;
+    float am = 0.0f;
+    if (ok) {
+        load_block(reinterpret_cast<const uint4*>(x + r * cols + J * 16), blk);
+        am = block_absmax(blk);
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) am = fmaxf(am, __shfl_xor(am, m, 64));
+    if (ok) {
+        uint32_t sb, w0, w1;
+        float d;
+        quant_candidate<6>(blk, am, outer[r / rows_per_outer], sb, w0, w1, d);
+        reinterpret_cast<uint2*>(codes + r * (cols >> 1))[J] = make_uint2(w0, w1);
+        scales[r * tiles_c + J] = (uint8_t)sb;
+    }
+}
+
 // Group amax: max |x| over each group of rows_per_outer rows, as fp32 bits folded with an
 // integer atomic max (order-independent and exact, so the result is deterministic). At most
 // AMAX_BLOCKS workgroups per group, each looping over the group with 16 independent 16-byte
@@ -225,12 +260,12 @@ __global__ void k_copy_f32(const float* __restrict__ a, float* __restrict__ b, i
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
-                                 uint8_t* scales, float* outer_out, hipStream_t stream)
+                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square)
 {
     if (rows == 0) return hipSuccess;
     const int64_t nb = cols / 16;
     const int64_t ngroups = rows / rows_per_outer;
-    if (outer_in == nullptr && rows_per_outer == 1 && nb <= 64 * 8) {
+    if (!square && outer_in == nullptr && rows_per_outer == 1 && nb <= 64 * 8) {
         const int64_t grid = (rows + 3) / 4;
         int nbl = nb <= 64 ? 1 : (nb <= 128 ? 2 : (nb <= 256 ? 4 : 8));
 #define PMN_ROWS(N)                                                                                       \
@@ -256,6 +291,12 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
         gx = gx > AMAX_BLOCKS ? AMAX_BLOCKS : gx;
         hipLaunchKernelGGL(k_group_amax, dim3((unsigned)gx, (unsigned)ngroups), dim3(256), 0, stream, x, group_elems, amax);
         hipLaunchKernelGGL(k_outer_from_amax, dim3((ngroups + 255) / 256), dim3(256), 0, stream, outer_out, ngroups);
+    }
+    if (square) {
+        const int64_t waves = (rows / 16) * ((nb + 3) / 4);
+        hipLaunchKernelGGL(k_nvfp4_2d, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, x, rows, cols,
+                           rows_per_outer, outer_out, codes, scales);
+        return hipGetLastError();
     }
     const int64_t nblocks = rows * nb;
     const int64_t grid = (nblocks + 255) / 256;
