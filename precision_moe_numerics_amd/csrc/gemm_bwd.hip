@@ -544,7 +544,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
 #pragma unroll
             for (int v = 0; v < 16; v++) {
                 const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
-                if (rl < rvalid) obase[rl * p.Kf + col] = acc[i][j][v];
+                // nontemporal: the fp32 gradients are not read again by this pass, and streaming
+                // them past the caches measured faster
+                if (rl < rvalid) __builtin_nontemporal_store(acc[i][j][v], obase + rl * p.Kf + col);
             }
             // one block at a time: keeps the accumulators in AGPRs until they are stored
             __builtin_amdgcn_sched_barrier(0);
