@@ -18,13 +18,21 @@ struct BwdLayout {
     int64_t Pb;
 };
 
-BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K)
+// Bound on the padded slot count when every group is padded to 64 (the blocked operands).
+static int64_t padded_bound64(int64_t M, int G)
+{
+    return ((M + 63) & ~(int64_t)63) + 64 * (int64_t)(G > 0 ? G : 0);
+}
+
+// The E4M3 backward keeps its operands in the blocked layout with groups padded to 64 slots
+// (dY row-wise codes at padded rows); the FP4 backward keeps row-major operands padded to 32.
+BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K, bool fp4 = false)
 {
     BwdLayout L{};
-    L.Pb = pmn_padded_bound(M, G);
+    L.Pb = fp4 ? pmn_padded_bound(M, G) : padded_bound64(M, G);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
-    L.dq = take((size_t)(M * N));
+    L.dq = take((size_t)((fp4 ? M : L.Pb) * N));
     L.de = take((size_t)(N / 32 * L.Pb));
     L.wt = take((size_t)(K * G * N));
     L.wte = take((size_t)(K * G * N / 32));
@@ -180,9 +188,8 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const 
 
 size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t K, int flags)
 {
-    (void)flags;
     if (M < 0 || G < 1 || N <= 0 || K <= 0) return 0;
-    return bwd_layout(M, G, N, K).total;
+    return bwd_layout(M, G, N, K, (flags & PMN_BWD_FP4) != 0).total;
 }
 
 int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
@@ -204,7 +211,8 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
     if (dgrad && (!b_codes || !b_scales || !b_outer || !da)) return PMN_EINVAL;
     if (wgrad && (!a_codes || !a_scales || !a_outer || !db)) return PMN_EINVAL;
-    const BwdLayout L = bwd_layout(M, G, N, K);
+    const bool fp4 = flags & PMN_BWD_FP4;
+    const BwdLayout L = bwd_layout(M, G, N, K, fp4);
     if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
     if (!aligned(workspace, 16) || !aligned(dy, 16) || (da && !aligned(da, 16)) || (db && !aligned(db, 16)) ||
         (a_codes && !aligned(a_codes, 16)) || (b_codes && !aligned(b_codes, 16)))
@@ -212,18 +220,18 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t s = hs(stream);
     const bool sr = dy_rounding == PMN_SR;
-    const bool fp4 = flags & PMN_BWD_FP4;
+    const bool blocked = !fp4;
     const int target = fp4 ? pmn::TARGET_E2M1_PACKED : PMN_TARGET_E4M3;
     int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
-    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s);
+    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, blocked ? pmn::BLOCKED_UNIT : 32);
     if (e != hipSuccess) return PMN_ELAUNCH;
     if (dgrad) {
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
-                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4);
+                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
                                 0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true, nullptr,
-                                s);
+                                s, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
                                     s, fp4);
@@ -231,10 +239,10 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     }
     if (wgrad) {
         e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
-                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target);
+                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G, target, seed,
-                                rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s);
+                                rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s, fp4);
         if (e != hipSuccess) return PMN_ELAUNCH;

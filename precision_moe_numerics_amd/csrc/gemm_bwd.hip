@@ -146,6 +146,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     constexpr int LDSBk = NSTAGE * STAGEBk;
     constexpr int LPS = FP4 ? LOADS_PER_STAGE + 1 : LOADS_PER_STAGE;
     constexpr int KS = FP4 ? 2 * BK : BK;           // values (k) per stage
+    // dgrad and wgrad on E4M3 operands read the blocked layout: a stage piece (16 rows x 64 bytes)
+    // is one contiguous 1 KB block, already in the LDS image's order
+    constexpr bool BLK = MODE != MODE_FWD && !FP4;
     typedef typename FragsOf<FP4>::type Frags;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSBk];
     // An AGPR operand marks the kernel as using AGPRs, so the compiler keeps the 256 accumulator
@@ -201,11 +204,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         const int64_t p0 = p.po[g] + u.index * BT;
         rvalid = u.s1 - r0 < BT ? u.s1 - r0 : BT;
         klen = p.Nf;
-        acode = p.a + r0 * p.lda;
+        // blocked: slot rows sit at their padded positions, whole 1 KB blocks of the stage
+        acode = BLK ? p.a + ((p0 >> 4) * (p.Nf >> 6)) * 1024 : p.a + r0 * p.lda;
         asc = p.ae + p0;
         asld = p.Pb;
         asrows = p.Pb - p0;                      // scale columns of this tile inside the array
-        bcode = p.b + c0 * p.ldb + (int64_t)g * (FP4 ? p.Nf / 2 : p.Nf);
+        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (int64_t)g * (p.Nf >> 6)) * 1024
+                    : p.b + c0 * p.ldb + (int64_t)g * (FP4 ? p.Nf / 2 : p.Nf);
         bsc = p.be + (int64_t)g * (p.Nf / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + r0 * p.Kf;
@@ -214,10 +219,10 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         r0 = tile.row * BT;
         const int64_t kbeg = p.po[g];
         klen = p.po[g + 1] - kbeg;
-        acode = p.a + r0 * p.lda + (FP4 ? kbeg / 2 : kbeg);
+        acode = BLK ? p.a + ((r0 >> 4) * (p.lda >> 6) + (kbeg >> 6)) * 1024 : p.a + r0 * p.lda + (FP4 ? kbeg / 2 : kbeg);
         asc = p.ae + (kbeg / 32) * p.Nf + r0;
         asld = p.Nf;
-        bcode = p.b + c0 * p.ldb + (FP4 ? kbeg / 2 : kbeg);
+        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (kbeg >> 6)) * 1024 : p.b + c0 * p.ldb + (FP4 ? kbeg / 2 : kbeg);
         bsc = p.be + (kbeg / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
@@ -230,7 +235,8 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     // Scales: wavefront w loads k-block w % 2 of the stage, rows 4 l .. 4 l + 3 in lane l.
     const int op = wave >> 1, half = wave & 1;
     const uint8_t* cbase = op ? bcode : acode;
-    const int64_t cld = op ? p.ldb : p.lda;
+    // row stride (row-major) or row-block stride (blocked: 16 rows = ld / 64 blocks of 1 KB)
+    const int64_t cld = BLK ? ((op ? p.ldb : p.lda) >> 6) * 1024 : (op ? p.ldb : p.lda);
     const int crows = (int)(op ? cvalid : rvalid);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
     const uint8_t* sbase = op ? bsc : asc;
@@ -272,6 +278,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
             r.kb = 4 * (int64_t)kt + 2 * half;
             r.kb2 = r.kb + 1 < kblocks ? r.kb + 1 : kblocks - 1;
             r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
+        } else if (BLK) {
+            // stage kt of a piece is block column kt (every k length is a multiple of 64)
+            const int64_t k0 = (int64_t)kt * BK;
+            r.kc = (int64_t)kt * 1024 + lane * 16;
+            r.kb = (k0 >> 5) + half;
+            r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
+            r.kb2 = 0;
         } else {
             const int64_t k0 = (int64_t)kt * BK;
             r.kc = ((half_tail && kt == KT - 1) ? k0 - tail_back : k0) + chunk * 16;
@@ -283,9 +296,16 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         return r;
     };
     auto issue_piece = [&](const IssueAt& r, int i) {
-        const int row = (half * 8 + i) * 16 + (lane >> 2);
-        const int64_t src = remap ? swiglu_a_row(row, tile.row, Fh) : (int64_t)(row < crows ? row : 0);
-        dma16(cbase + src * cld + r.kc, cdst + r.so + i * 1024);
+        if (BLK) {
+            // row block half * 8 + i of the tile; blocks past the tile's valid rows (dgrad's last
+            // tile of a group) re-read its first block: their outputs are never stored
+            const int pb = half * 8 + i;
+            dma16(cbase + (int64_t)(16 * pb < crows ? pb : 0) * cld + r.kc, cdst + r.so + i * 1024);
+        } else {
+            const int row = (half * 8 + i) * 16 + (lane >> 2);
+            const int64_t src = remap ? swiglu_a_row(row, tile.row, Fh) : (int64_t)(row < crows ? row : 0);
+            dma16(cbase + src * cld + r.kc, cdst + r.so + i * 1024);
+        }
     };
     auto issue_scales = [&](const IssueAt& r) { dma4(sptr + r.kb * sld, sdst + r.so); };
     auto issue_scales2 = [&](const IssueAt& r) { dma4(sptr + r.kb2 * sld, sdst + r.so + BT); };

@@ -428,7 +428,9 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows(const uint16_t* __restrict__
 // read 256 contiguous bytes of a row), and the scale bytes go through LDS so that each k-block's
 // 64 rows are written as one contiguous run. Column of row r: r (pad_off == nullptr), else
 // pad_off[g] + r - offsets[g] for r's group g. FP4: E2M1 codes packed two per byte, [M x N/2].
-template <bool SR, bool FP4 = false>
+// BLK: the codes go to that same padded position as a row of the blocked GEMM operand layout
+// (1 KB blocks of 16 rows x 64 bytes, chunk c of row r at slot c ^ ((r / 4) % 4)).
+template <bool SR, bool FP4 = false, bool BLK = false>
 __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restrict__ x, int64_t M,
                                                         int64_t N, uint64_t seed, uint32_t stream_id,
                                                         uint8_t* __restrict__ out,
@@ -437,10 +439,22 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                                                         const int64_t* __restrict__ pad_off, int64_t ld_e8m0,
                                                         const int32_t* __restrict__ gather)
 {
+    static_assert(!(BLK && FP4), "the blocked layout holds E4M3 codes");
     __shared__ uint8_t se[4][64];
     const int64_t nb = N >> 5;
     const int t = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * 64, kb0 = (int64_t)blockIdx.y * 4;
+    // padded position of slot r: pad_off[g] + r - offsets[g] for its group g (the largest g with
+    // offsets[g] <= r; empty groups are skipped)
+    auto padded_col = [&](int64_t r) {
+        if (pad_off == nullptr) return r;
+        int lo = 0, hi = G - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        return pad_off[lo] + (r - offsets[lo]);
+    };
     {
         const int64_t r = r0 + (t >> 2), kb = kb0 + (t & 3);
         if (r < M && kb < nb) {
@@ -454,36 +468,35 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
             } else {
                 uint32_t o[8];
                 e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
-                store_block32(out, r * nb + kb, o);
+                if (BLK) {
+                    // k-block kb = chunks 2 (kb % 2) and 2 (kb % 2) + 1 of 64-byte column kb / 2
+                    const int64_t pr = padded_col(r);
+                    const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
+                    uint8_t* blk = out + ((pr >> 4) * (N >> 6) + (kb >> 1)) * 1024 + r16 * 64;
+                    *reinterpret_cast<uint4*>(blk + ((c ^ x) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<uint4*>(blk + (((c + 1) ^ x) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+                } else {
+                    store_block32(out, r * nb + kb, o);
+                }
             }
             se[t & 3][t >> 2] = (uint8_t)(e + 127);
         }
     }
     __syncthreads();
     const int64_t r = r0 + (t & 63), kb = kb0 + (t >> 6);
-    if (r < M && kb < nb) {
-        int64_t col = r;
-        if (pad_off != nullptr) {
-            // group of slot r: the largest g with offsets[g] <= r (empty groups are skipped)
-            int lo = 0, hi = G - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (offsets[mid] <= r) lo = mid; else hi = mid - 1;
-            }
-            col = pad_off[lo] + (r - offsets[lo]);
-        }
-        out_e8m0[kb * ld_e8m0 + col] = se[t >> 6][t & 63];
-    }
+    if (r < M && kb < nb) out_e8m0[kb * ld_e8m0 + padded_col(r)] = se[t >> 6][t & 63];
 }
 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
-                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather, bool fp4)
+                             int64_t ld_e8m0, hipStream_t stream, const int32_t* gather, bool fp4,
+                             bool blocked)
 {
     const int64_t nb = N / 32;
     if (M * nb == 0) return hipSuccess;
-    if (fp4 && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
+    if ((fp4 || blocked) && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
+    if (blocked && (fp4 || N % 64 != 0)) return hipErrorInvalidValue;
     if (padded_offsets == nullptr && ld_e8m0 == 0) {
         const int64_t grid = (M * nb + 255) / 256;
         if (sr)
@@ -502,6 +515,15 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
         else
             hipLaunchKernelGGL((k_mxfp8_rows_kbm<false, true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id,
                                out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        return hipGetLastError();
+    }
+    if (blocked) {
+        if (sr)
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<true, false, true>), grid, dim3(256), 0, stream, x, M, N, seed,
+                               stream_id, out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        else
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<false, false, true>), grid, dim3(256), 0, stream, x, M, N, seed,
+                               stream_id, out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
         return hipGetLastError();
     }
     if (sr)

@@ -27,8 +27,10 @@ struct GroupBlock {
     bool live;    // the block lies inside the padded output
 };
 
-// Map padded block pb (32 output columns) to its slots: walk the groups, each padded to 32.
-PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t M)
+// Map padded block pb (32 output columns) to its slots: walk the groups, each padded to a
+// multiple of `unit` (32, or 64 for the blocked GEMM operands, whose last block of a group can
+// then be all padding: valid = 0).
+PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t M, int64_t unit)
 {
     GroupBlock r;
     const int64_t col = pb * 32;
@@ -42,7 +44,7 @@ PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t
     int64_t po = 0;
     for (int g = 0; g < G; g++) {
         int64_t a = offsets[g], b = offsets[g + 1];
-        int64_t P = (b - a + 31) & ~(int64_t)31;
+        int64_t P = (b - a + unit - 1) & ~(unit - 1);
         if (col < po + P) {
             r.s0 = a + (col - po);
             int64_t v = (b < M ? b : M) - r.s0;     // never past the last slot
@@ -59,18 +61,18 @@ PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t
     return r;
 }
 
-__global__ void k_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* po)
+__global__ void k_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* po, int64_t unit)
 {
     if (threadIdx.x != 0 || blockIdx.x != 0) return;
     if (offsets == nullptr) {
         po[0] = 0;
-        po[1] = (M + 31) & ~(int64_t)31;
+        po[1] = (M + unit - 1) & ~(unit - 1);
         return;
     }
     int64_t p = 0;
     po[0] = 0;
     for (int g = 0; g < G; g++) {
-        p += (offsets[g + 1] - offsets[g] + 31) & ~(int64_t)31;
+        p += (offsets[g + 1] - offsets[g] + unit - 1) & ~(unit - 1);
         po[g + 1] = p;
     }
 }
@@ -95,6 +97,9 @@ struct TransposeArgs {
     uint8_t* out_e8m0;        // [cols x ld/32], or k-block-major [ld/32 x cols] when e8m0_kb_major
     int64_t ld;
     bool e8m0_kb_major;
+    // E4M3 target only: codes in 1 KB blocks of 16 rows x 64 bytes (the GEMM operand layout; see
+    // store_blocked) and groups padded to 64 slots instead of 32
+    bool blocked;
 };
 
 // E4M3 code of v / scale (scale a power of two) by stochastic rounding with the given SR operand,
@@ -136,14 +141,18 @@ PMN_DEV void bf8(uint4 w, float (&v)[8])
 }
 
 // Output tile of a workgroup: 512 output rows (source columns) x 128 padded slots (4 blocks),
-// assembled in LDS so that global stores write whole 128-byte row segments.
-// Rows are 128 bytes (8 chunks of 16); chunk p of row r sits at position p ^ ((r / 8) % 8), so
-// the transposed writes (lane l -> rows 8l .. 8l+7) and the row-wise reads both spread over the
-// LDS banks.
+// assembled in LDS so that global stores write whole 128-byte row segments (or whole 1 KB
+// blocks). Rows are 128 bytes (8 chunks of 16); chunk p of row r sits at position
+// p ^ ((r / 8) % 8) ^ (4 ((r / 2) % 2)), so the transposed writes (lane l -> rows 8l .. 8l+7), the
+// row-wise reads (2 rows x 8 chunks per quarter-wavefront) and the block reads (4 rows x 4
+// chunks) all spread over the LDS banks.
 constexpr int TQ_ROWS = 512;
 constexpr int TQ_RS = 128;
 
-PMN_DEV int tile_chunk(int row, int chunk) { return row * TQ_RS + ((chunk ^ ((row >> 3) & 7)) << 4); }
+PMN_DEV int tile_chunk(int row, int chunk)
+{
+    return row * TQ_RS + ((chunk ^ ((row >> 3) & 7) ^ (((row >> 1) & 1) << 2)) << 4);
+}
 
 // SRC: SRC_NVFP4 or SRC_BF16. ROUND: 0 = RNE, 1 = SR. TARGET: 0 = E4M3, 1 = E2M1 (one code per
 // byte, SR only), 2 = E2M1 packed two per byte (slot 2j in the low nibble): out [cols x ld/2].
@@ -158,18 +167,21 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
     const int64_t pb = (int64_t)blockIdx.x * 4 + w;
     const int64_t cg = (int64_t)blockIdx.y * 64 + lane;   // column group of 8
     const int64_t c0 = cg * 8;
-    const GroupBlock blk = find_block(pb, a.offsets, a.G, a.M);
+    const GroupBlock blk = find_block(pb, a.offsets, a.G, a.M, a.blocked ? 64 : 32);
     if (lane == 0) block_live[w] = blk.live ? 1 : 0;
     const bool active = blk.live && c0 < a.cols;
     // lane j (mod 32) fetches slot j's source row and outer scale with one vector load each;
     // readlane later hands every slot's values to the whole wavefront, so every lane of a live
     // block computes them, whatever its columns
+    // a block that is all padding (valid = 0) re-reads slot 0; all its values become +0
     const int last = blk.valid - 1;
+    const int64_t rs0 = blk.valid > 0 ? blk.s0 : 0;
+    const int lastc = blk.valid > 0 ? last : 0;
     int rl = 0;
     float ol = 0.0f;
     if (SRC == SRC_NVFP4 && blk.live) {
         const int jl = lane & 31;
-        const int64_t sl = blk.s0 + (jl < last ? jl : last);
+        const int64_t sl = rs0 + (jl < lastc ? jl : lastc);
         rl = a.gather ? a.gather[sl] : (int)sl;
         ol = a.outer[rl / a.rows_per_outer];
     }
@@ -203,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
         } else {
 #pragma unroll
             for (int j = 0; j < 32; j++) {
-                const uint4 v = *reinterpret_cast<const uint4*>(a.x + (blk.s0 + (j < last ? j : last)) * a.cols + c0);
+                const uint4 v = *reinterpret_cast<const uint4*>(a.x + (rs0 + (j < lastc ? j : lastc)) * a.cols + c0);
                 xw[j] = j <= last ? v : make_uint4(0u, 0u, 0u, 0u);
             }
         }
@@ -339,6 +351,27 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                 *reinterpret_cast<uint4*>(a.out + col * (a.ld >> 1) + (int64_t)blockIdx.x * 64 + chunk * 16) = v;
             }
         }
+    } else if (a.blocked) {
+        // 1 KB blocks of 16 output rows x 64 bytes (32 row blocks x 2 k-blocks of this tile), one
+        // per 64 threads. Block (rb, kb) of the output sits at (rb * ld/64 + kb) * 1024 and holds
+        // row r (0..15) at bytes 64 r .. 64 r + 63 with its 16-byte chunk c at slot c ^ ((r / 4) % 4):
+        // exactly the LDS image the GEMM reads, so the GEMM copies whole blocks.
+        const int64_t nkb = a.ld >> 6;
+#pragma unroll 4
+        for (int k = 0; k < 16; k++) {
+            const int q = k * 256 + threadIdx.x;
+            const int b = q >> 6, t = q & 63;
+            const int rb = b >> 1, kb = b & 1;
+            const int r16 = t >> 2;
+            const int c = (t & 3) ^ ((r16 >> 2) & 3);
+            const int row = rb * 16 + r16;
+            const int64_t col = col_base + row;
+            if (col < a.cols && block_live[kb * 2 + (c >> 1)]) {
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, kb * 4 + c));
+                *reinterpret_cast<uint4*>(a.out + (((col_base >> 4) + rb) * nkb + (int64_t)blockIdx.x * 2 + kb) * 1024 +
+                                          t * 16) = v;
+            }
+        }
     } else {
 #pragma unroll 4
         for (int k = 0; k < 16; k++) {
@@ -367,9 +400,9 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
 }
 
 hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
-                                 hipStream_t stream)
+                                 hipStream_t stream, int64_t unit)
 {
-    hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, offsets, G, M, padded_offsets);
+    hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, offsets, G, M, padded_offsets, unit);
     return hipGetLastError();
 }
 
@@ -377,7 +410,8 @@ static hipError_t launch_transpose(const TransposeArgs& a, int src, int round, i
                                    int64_t* padded_offsets, hipStream_t stream)
 {
     if (padded_offsets)
-        hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, a.offsets, a.G, a.M, padded_offsets);
+        hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, a.offsets, a.G, a.M, padded_offsets,
+                           (int64_t)(a.blocked ? 64 : 32));
     const int64_t nblk = a.ld / 32;
     if (nblk == 0 || a.cols == 0) return hipGetLastError();
     dim3 grid((unsigned)((nblk + 3) / 4), (unsigned)((a.cols / 8 + 63) / 64));
@@ -404,10 +438,11 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t cols, int64_t rows_per_outer, const int32_t* gather, int64_t M,
                           const int64_t* offsets, int G, int target, uint64_t seed,
                           uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0, int64_t ld,
-                          bool e8m0_kb_major, int64_t* padded_offsets, hipStream_t stream)
+                          bool e8m0_kb_major, int64_t* padded_offsets, hipStream_t stream, bool blocked)
 {
     TransposeArgs a{};
     a.e8m0_kb_major = e8m0_kb_major;
+    a.blocked = blocked && target == PMN_TARGET_E4M3;
     a.codes = codes; a.scales = scales; a.outer = outer; a.rows_per_outer = rows_per_outer;
     a.x = nullptr; a.cols = cols; a.gather = gather; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
@@ -417,10 +452,11 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
                              uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,
-                             int64_t* padded_offsets, hipStream_t stream, int target)
+                             int64_t* padded_offsets, hipStream_t stream, int target, bool blocked)
 {
     TransposeArgs a{};
     a.e8m0_kb_major = e8m0_kb_major;
+    a.blocked = blocked && target == PMN_TARGET_E4M3;
     a.codes = nullptr; a.scales = nullptr; a.outer = nullptr; a.rows_per_outer = 1;
     a.x = x; a.cols = N; a.gather = nullptr; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;

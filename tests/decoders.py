@@ -21,3 +21,16 @@ def decode_s2f6_rows(codes, e8m0, mask: int):
     R, C = codes.shape
     z = codes.astype(np.float64).reshape(R, C // 32, 32) * 2.0 ** (np.asarray(e8m0, np.float64) - 133)[..., None]
     return ((z @ Hm.T) / 32 * D).reshape(R, C)
+
+
+def unblock(raw, rows: int, cols: int):
+    """Row-major [rows x cols] bytes of a code matrix held in the backward's blocked operand
+    layout: 1 KB blocks of 16 rows x 64 bytes, block (rb, kb) at byte (rb * cols/64 + kb) * 1024,
+    row r of a block at its bytes 64 r .. 64 r + 63 with the row's 16-byte chunk c at position
+    c ^ ((r / 4) % 4)."""
+    b = np.ascontiguousarray(np.asarray(raw, dtype=np.uint8)).reshape(rows // 16, cols // 64, 16, 4, 16)
+    r = np.arange(16)
+    out = np.empty_like(b)
+    for c in range(4):
+        out[:, :, :, c, :] = b[:, :, r, c ^ ((r >> 2) & 3), :]
+    return out.transpose(0, 2, 1, 3, 4).reshape(rows, cols)

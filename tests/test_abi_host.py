@@ -87,3 +87,21 @@ def test_argument_errors_without_launch(lib):
 def test_zero_size_calls_are_no_ops(lib):
     assert lib.nvfp4_quantize(None, 0, 32, 1, 1, None, None, None, None, None) == 0
     assert lib.rht32_s2f6_quantize(None, 0, 0, 64, 0, None, None, None) == 0
+
+
+def test_blocked_layout_reader_matches_the_documented_offsets():
+    """The test-side reader of the backward's blocked code parts against the byte offset the
+    header states, element by element: (rb * C/64 + kb) * 1024 + 64 r + 16 (c ^ ((r/4) % 4)) + b
+    for row 16 rb + r and column 64 kb + 16 c + b."""
+    import numpy as np
+    from decoders import unblock
+    R, Cc = 48, 192
+    m = np.random.default_rng(5).integers(0, 256, (R, Cc), dtype=np.uint8)
+    raw = np.zeros(R * Cc, dtype=np.uint8)
+    for i in range(R):
+        for j in range(Cc):
+            rb, r = divmod(i, 16)
+            kb, within = divmod(j, 64)
+            c, b = divmod(within, 16)
+            raw[(rb * (Cc // 64) + kb) * 1024 + 64 * r + 16 * (c ^ ((r // 4) % 4)) + b] = m[i, j]
+    assert np.array_equal(unblock(raw, R, Cc), m)

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from decoders import decode_s2f6_rows, fp4_value
+from decoders import decode_s2f6_rows, fp4_value, unblock
 
 pytestmark = pytest.mark.gpu
 
@@ -305,21 +305,33 @@ def test_gemm_bwd_intermediates_and_gradients(P, I):
     da, db, ws = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
                                         seed=9, rng_stream_a=4, rng_stream_b=1, rng_stream_dy=6)
     v = P.bwd_workspace_views(ws, M, G, N, K)
-    # E8M0 parts are k-block-major; the row-wise dY scales sit at padded slot columns
+    # The library pads each group to 64 slots and keeps the code parts blocked; the oracle pads
+    # to 32 and is row-major. E8M0 parts are k-block-major; the row-wise dY codes and scales sit
+    # at padded slot rows / columns.
     off = np.asarray(d["offsets"], dtype=np.int64)
-    po = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
+    cnt = np.diff(off)
+    po32 = np.concatenate([[0], np.cumsum((cnt + 31) // 32 * 32)])
+    po = np.concatenate([[0], np.cumsum((cnt + 63) // 64 * 64)])
     assert np.array_equal(npy(v["po"]), po)
+    Pb = v["de"].shape[1]
     grp = np.searchsorted(off, np.arange(M), side="right") - 1
     pcol = po[grp] + np.arange(M) - off[grp]
     rq, re = O.mxfp8_quantize_rows(dy)
-    assert np.array_equal(npy(v["dq"]), rq) and np.array_equal(npy(v["de"])[:, pcol].T, re)
+    assert np.array_equal(unblock(npy(v["dq"]), Pb, N)[pcol], rq)
+    assert np.array_equal(npy(v["de"])[:, pcol].T, re)
     rwt, rwte = O.requant_transpose_sr(d["rwq"], seed=9, stream=1)
-    assert np.array_equal(npy(v["wt"]), rwt) and np.array_equal(npy(v["wte"]).T, rwte)
+    assert np.array_equal(unblock(npy(v["wt"]), K, G * N), rwt) and np.array_equal(npy(v["wte"]).T, rwte)
     rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], stream=7)
-    Pt = rt.shape[1]
-    assert np.array_equal(npy(v["dt"])[:, :Pt], rt) and np.array_equal(npy(v["dte"]).T[:, :Pt // 32], rte)
     rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=d["offsets"], seed=9, stream=4)
-    assert np.array_equal(npy(v["xt"])[:, :Pt], rxt) and np.array_equal(npy(v["xte"]).T[:, :Pt // 32], rxte)
+    for name, ref, ref_e in (("dt", rt, rte), ("xt", rxt, rxte)):
+        got = unblock(npy(v[name]), ref.shape[0], Pb)
+        got_e = npy(v[name + "e"]).T
+        for g in range(G):
+            n32 = po32[g + 1] - po32[g]
+            a, a32 = po[g], po32[g]
+            assert np.array_equal(got[:, a:a + n32], ref[:, a32:a32 + n32]), (name, g)
+            assert np.array_equal(got_e[:, a // 32:(a + n32) // 32], ref_e[:, a32 // 32:(a32 + n32) // 32]), (name, g)
+            assert np.all(got[:, a + n32:po[g + 1]] == 0), (name, g)   # a block of padding only
     da_ref = O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K)
     db_ref = O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K)
     assert rel_fro(npy(da), da_ref) <= 2e-3
