@@ -110,8 +110,12 @@ class Layer:
         self.mask = I.sign_mask(shape.seeds["rht"])
         self.seed = shape.seeds["sr"]
         M = self.M
-        self.ws13 = torch.empty(P.moe_grouped_gemm_bwd_workspace_size(M, E, 2 * F, H, 3), dtype=torch.uint8, device=dev)
-        self.ws2 = torch.empty(P.moe_grouped_gemm_bwd_workspace_size(M, E, H, F, 3), dtype=torch.uint8, device=dev)
+        # one workspace per matrix, large enough for the MXFP8 and the FP4 backward layouts
+        def ws(N, K):
+            n = max(P.moe_grouped_gemm_bwd_workspace_size(M, E, N, K, f) for f in (3, 3 | P.BWD_FP4))
+            return torch.empty(n, dtype=torch.uint8, device=dev)
+        self.ws13 = ws(2 * F, H)
+        self.ws2 = ws(H, F)
         torch.cuda.synchronize()
 
     def flops(self):

@@ -256,8 +256,8 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * part rounded up to 256 bytes: dY row-wise codes [Pb x N] and E8M0 [N/32 x Pb]; W^T codes
  * [K x G*N] and E8M0 [G*N/32 x K]; dY^T codes [N x Pb] and E8M0 [Pb/32 x N]; A^T codes [K x Pb]
  * and E8M0 [Pb/32 x K]; padded offsets int64 [G+1]. Each group's slots are padded with zeros to
- * a multiple of 64 (padded_offsets[g] is group g's first padded slot) and Pb = roundup(M, 64) +
- * 64 G. Slot s of group g is padded slot padded_offsets[g] + s - offsets[g]: the row of the
+ * a multiple of U = 64 (padded_offsets[g] is group g's first padded slot) and Pb = roundup(M, U)
+ * + U G. Slot s of group g is padded slot padded_offsets[g] + s - offsets[g]: the row of the
  * row-wise dY codes and the column of their E8M0. The E8M0 parts are k-block-major (entry
  * [b, r] is the scale of k-block b of row r). The code parts are blocked: a [R x C] part is a
  * grid of 1 KB blocks of 16 rows x 64 bytes, block (rb, kb) at byte (rb * C/64 + kb) * 1024,
@@ -269,9 +269,8 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * section's worked example rounds onto the E2M1 grid by SR): every operand goes to MXFP4 instead
  * of MXFP8 -- E2M1 codes (W^T, A^T by SR; dY by dy_rounding) with one E8M0 per 32 values chosen
  * so that nothing saturates (amax <= 6 * 2^e) -- and dgrad / wgrad run on the block-scaled FP4
- * MFMA. Its workspace has the same parts, with groups padded to 32 (Pb = pmn_padded_bound(M, G)),
- * dY row-wise codes [M x N/2] in slot order, and row-major code parts of E2M1 codes packed two
- * per byte (element 2j in the low nibble), rows of half the bytes.
+ * MFMA. Its workspace has the same parts and the same blocked layout, with U = 128 and code
+ * parts of E2M1 codes packed two per byte (element 2j in the low nibble): rows of half the bytes.
  */
 int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
                          const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,

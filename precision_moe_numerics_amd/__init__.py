@@ -281,16 +281,17 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
 
 
 def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int, fp4: bool = False):
-    """Views of the backward workspace parts, in the order include/pmn.h documents them. E4M3:
-    groups padded to 64 slots and the code parts (dq [Pb x N] at padded slot rows, wt, dt, xt) in
-    the blocked layout, viewed here as raw bytes of the matrix's shape. FP4: groups padded to 32,
-    row-major code parts with E2M1 codes packed two per byte (rows of half the bytes)."""
-    Pb = padded_bound(M, G) if fp4 else (M + 63) // 64 * 64 + 64 * G
+    """Views of the backward workspace parts, in the order include/pmn.h documents them: groups
+    padded to U = 64 slots (E4M3) or 128 (FP4: E2M1 codes packed two per byte, rows of half the
+    bytes) and the code parts (dq at padded slot rows, wt, dt, xt) in the blocked layout, viewed
+    here as raw bytes of the matrix's shape."""
+    U = 128 if fp4 else 64
+    Pb = (M + U - 1) // U * U + U * G
     h = 2 if fp4 else 1
-    dq_rows = M if fp4 else Pb
-    sizes = [("dq", dq_rows * N, (dq_rows, N // h)), ("de", N // 32 * Pb, (N // 32, Pb)), ("wt", K * G * N, (K, G * N // h)),
-             ("wte", K * G * N // 32, (G * N // 32, K)), ("dt", N * Pb, (N, Pb // h)), ("dte", N * Pb // 32, (Pb // 32, N)),
-             ("xt", K * Pb, (K, Pb // h)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
+    sizes = [("dq", Pb * N // h, (Pb, N // h)), ("de", N // 32 * Pb, (N // 32, Pb)),
+             ("wt", K * G * N // h, (K, G * N // h)), ("wte", K * G * N // 32, (G * N // 32, K)),
+             ("dt", N * Pb // h, (N, Pb // h)), ("dte", N * Pb // 32, (Pb // 32, N)),
+             ("xt", K * Pb // h, (K, Pb // h)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
     off, views = 0, {}
     for name, nbytes, shape in sizes:
         used = nbytes if shape is None else shape[0] * shape[1]

@@ -18,27 +18,28 @@ struct BwdLayout {
     int64_t Pb;
 };
 
-// Bound on the padded slot count when every group is padded to 64 (the blocked operands).
-static int64_t padded_bound64(int64_t M, int G)
+// Bound on the padded slot count when every group is padded to a multiple of `unit`.
+static int64_t padded_bound_unit(int64_t M, int G, int64_t unit)
 {
-    return ((M + 63) & ~(int64_t)63) + 64 * (int64_t)(G > 0 ? G : 0);
+    return ((M + unit - 1) & ~(unit - 1)) + unit * (int64_t)(G > 0 ? G : 0);
 }
 
-// The E4M3 backward keeps its operands in the blocked layout with groups padded to 64 slots
-// (dY row-wise codes at padded rows); the FP4 backward keeps row-major operands padded to 32.
+// The backward keeps its operands in the blocked layout with groups padded to 64 slots (E4M3) or
+// 128 slots (packed E2M1); the row-wise dY codes sit at padded rows.
 BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K, bool fp4 = false)
 {
     BwdLayout L{};
-    L.Pb = fp4 ? pmn_padded_bound(M, G) : padded_bound64(M, G);
+    L.Pb = padded_bound_unit(M, G, pmn::blocked_unit(fp4));
+    const int64_t vpb = fp4 ? 2 : 1;   // code values per byte
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
-    L.dq = take((size_t)((fp4 ? M : L.Pb) * N));
+    L.dq = take((size_t)(L.Pb * N / vpb));
     L.de = take((size_t)(N / 32 * L.Pb));
-    L.wt = take((size_t)(K * G * N));
+    L.wt = take((size_t)(K * G * N / vpb));
     L.wte = take((size_t)(K * G * N / 32));
-    L.dt = take((size_t)(N * L.Pb));
+    L.dt = take((size_t)(N * L.Pb / vpb));
     L.dte = take((size_t)(N * L.Pb / 32));
-    L.xt = take((size_t)(K * L.Pb));
+    L.xt = take((size_t)(K * L.Pb / vpb));
     L.xte = take((size_t)(K * L.Pb / 32));
     L.po = take((size_t)(G + 1) * sizeof(int64_t));
     L.total = off;
@@ -220,10 +221,10 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const hipStream_t s = hs(stream);
     const bool sr = dy_rounding == PMN_SR;
-    const bool blocked = !fp4;
+    const bool blocked = true;
     const int target = fp4 ? pmn::TARGET_E2M1_PACKED : PMN_TARGET_E4M3;
     int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
-    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, blocked ? pmn::BLOCKED_UNIT : 32);
+    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, pmn::blocked_unit(fp4));
     if (e != hipSuccess) return PMN_ELAUNCH;
     if (dgrad) {
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,

@@ -146,9 +146,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     constexpr int LDSBk = NSTAGE * STAGEBk;
     constexpr int LPS = FP4 ? LOADS_PER_STAGE + 1 : LOADS_PER_STAGE;
     constexpr int KS = FP4 ? 2 * BK : BK;           // values (k) per stage
-    // dgrad and wgrad on E4M3 operands read the blocked layout: a stage piece (16 rows x 64 bytes)
-    // is one contiguous 1 KB block, already in the LDS image's order
-    constexpr bool BLK = MODE != MODE_FWD && !FP4;
+    // dgrad and wgrad read the blocked layout: a stage piece (16 rows x 64 bytes) is one
+    // contiguous 1 KB block, already in the LDS image's order
+    constexpr bool BLK = MODE != MODE_FWD;
     typedef typename FragsOf<FP4>::type Frags;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSBk];
     // An AGPR operand marks the kernel as using AGPRs, so the compiler keeps the 256 accumulator
@@ -205,11 +205,11 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         rvalid = u.s1 - r0 < BT ? u.s1 - r0 : BT;
         klen = p.Nf;
         // blocked: slot rows sit at their padded positions, whole 1 KB blocks of the stage
-        acode = BLK ? p.a + ((p0 >> 4) * (p.Nf >> 6)) * 1024 : p.a + r0 * p.lda;
+        acode = BLK ? p.a + ((p0 >> 4) * (p.lda >> 6)) * 1024 : p.a + r0 * p.lda;
         asc = p.ae + p0;
         asld = p.Pb;
         asrows = p.Pb - p0;                      // scale columns of this tile inside the array
-        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (int64_t)g * (p.Nf >> 6)) * 1024
+        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (int64_t)g * ((FP4 ? p.Nf / 2 : p.Nf) >> 6)) * 1024
                     : p.b + c0 * p.ldb + (int64_t)g * (FP4 ? p.Nf / 2 : p.Nf);
         bsc = p.be + (int64_t)g * (p.Nf / 32) * p.Kf + c0;
         bsld = p.Kf;
@@ -219,10 +219,11 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         r0 = tile.row * BT;
         const int64_t kbeg = p.po[g];
         klen = p.po[g + 1] - kbeg;
-        acode = BLK ? p.a + ((r0 >> 4) * (p.lda >> 6) + (kbeg >> 6)) * 1024 : p.a + r0 * p.lda + (FP4 ? kbeg / 2 : kbeg);
+        const int64_t kbyte = FP4 ? kbeg / 2 : kbeg;   // first code byte of the group in a row
+        acode = BLK ? p.a + ((r0 >> 4) * (p.lda >> 6) + (kbyte >> 6)) * 1024 : p.a + r0 * p.lda + kbyte;
         asc = p.ae + (kbeg / 32) * p.Nf + r0;
         asld = p.Nf;
-        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (kbeg >> 6)) * 1024 : p.b + c0 * p.ldb + (FP4 ? kbeg / 2 : kbeg);
+        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (kbyte >> 6)) * 1024 : p.b + c0 * p.ldb + kbyte;
         bsc = p.be + (kbeg / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
@@ -271,10 +272,11 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         IssueAt r;
         if (FP4) {
             // 16-byte chunk c of a stage row is k-block 4 kt + c; chunks past the last k-block
-            // re-read the last valid one (FP4 codes are always finite; their scale is 2^-127)
+            // re-read the last valid one (FP4 codes are always finite; their scale is 2^-127).
+            // Blocked: stage kt is block column kt (every k length is a multiple of 128).
             const int64_t vch = kblocks - 4 * (int64_t)kt;
             const int64_t cc = chunk < vch ? chunk : vch - 1;
-            r.kc = (int64_t)kt * BK + cc * 16;
+            r.kc = BLK ? (int64_t)kt * 1024 + lane * 16 : (int64_t)kt * BK + cc * 16;
             r.kb = 4 * (int64_t)kt + 2 * half;
             r.kb2 = r.kb + 1 < kblocks ? r.kb + 1 : kblocks - 1;
             r.kb = r.kb < kblocks ? r.kb : kblocks - 1;

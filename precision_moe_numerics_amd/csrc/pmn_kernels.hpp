@@ -21,8 +21,9 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 // Row-wise MXFP8. With padded_offsets null the E8M0 scales are row-major [M x N/32]; otherwise
 // they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column
 // padded_offsets[g] + s - offsets[g] (the layout the grouped dgrad GEMM streams). `blocked`
-// (E4M3, k-block-major only) writes the codes in the blocked layout below with slot s of group g
-// at row padded_offsets[g] + s - offsets[g] ([ld_e8m0 x N] rows; padding rows are not written).
+// (k-block-major only) writes the codes in the blocked layout below with slot s of group g at row
+// padded_offsets[g] + s - offsets[g] ([ld_e8m0 rows x N or N/2 bytes]; padding rows are not
+// written).
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
@@ -34,12 +35,13 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
 hipError_t launch_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* padded_offsets,
                                  hipStream_t stream, int64_t unit = 32);
 
-// The blocked operand layout of the MXFP8 backward GEMMs: a [R x C] code matrix (R % 16 == 0,
+// The blocked operand layout of the backward GEMMs: a [R x C] code matrix (R % 16 == 0, C bytes,
 // C % 64 == 0) is stored as 1 KB blocks of 16 rows x 64 bytes, block (rb, kb) at byte
 // (rb * C/64 + kb) * 1024; inside a block row r occupies bytes 64 r .. 64 r + 63 and its 16-byte
 // chunk c (bytes 16 c .. 16 c + 15 of the row's 64) sits at slot c ^ ((r / 4) % 4). Groups of
-// slots are padded to 64 so that every 64-slot GEMM stage is one block column.
-constexpr int64_t BLOCKED_UNIT = 64;
+// slots are padded so that every GEMM stage (64 bytes of a row: 64 E4M3 codes or 128 packed E2M1
+// codes) is one block column.
+inline int64_t blocked_unit(bool fp4) { return fp4 ? 128 : 64; }
 
 hipError_t launch_rht32_s2f6(const void* x, bool f32, int64_t rows, int64_t cols, uint32_t mask,
                              int8_t* codes, uint8_t* e8m0, hipStream_t stream);

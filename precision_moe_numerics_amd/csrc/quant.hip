@@ -439,7 +439,6 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                                                         const int64_t* __restrict__ pad_off, int64_t ld_e8m0,
                                                         const int32_t* __restrict__ gather)
 {
-    static_assert(!(BLK && FP4), "the blocked layout holds E4M3 codes");
     __shared__ uint8_t se[4][64];
     const int64_t nb = N >> 5;
     const int t = threadIdx.x;
@@ -464,7 +463,15 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
             if (FP4) {
                 uint32_t o[4];
                 e = mxfp4_block<SR>(w, r, kb, N, seed, stream_id, o);
-                reinterpret_cast<uint4*>(out)[r * nb + kb] = make_uint4(o[0], o[1], o[2], o[3]);
+                if (BLK) {
+                    // k-block kb = chunk kb % 4 of 64-byte column kb / 4
+                    const int64_t pr = padded_col(r);
+                    const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = (int)(kb & 3);
+                    *reinterpret_cast<uint4*>(out + ((pr >> 4) * (N >> 7) + (kb >> 2)) * 1024 + r16 * 64 + ((c ^ x) << 4)) =
+                        make_uint4(o[0], o[1], o[2], o[3]);
+                } else {
+                    reinterpret_cast<uint4*>(out)[r * nb + kb] = make_uint4(o[0], o[1], o[2], o[3]);
+                }
             } else {
                 uint32_t o[8];
                 e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
@@ -496,7 +503,7 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
     const int64_t nb = N / 32;
     if (M * nb == 0) return hipSuccess;
     if ((fp4 || blocked) && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
-    if (blocked && (fp4 || N % 64 != 0)) return hipErrorInvalidValue;
+    if (blocked && N % (fp4 ? 128 : 64) != 0) return hipErrorInvalidValue;
     if (padded_offsets == nullptr && ld_e8m0 == 0) {
         const int64_t grid = (M * nb + 255) / 256;
         if (sr)
@@ -508,6 +515,15 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
         return hipGetLastError();
     }
     const dim3 grid((unsigned)((M + 63) / 64), (unsigned)((nb + 3) / 4));
+    if (fp4 && blocked) {
+        if (sr)
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<true, true, true>), grid, dim3(256), 0, stream, x, M, N, seed,
+                               stream_id, out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        else
+            hipLaunchKernelGGL((k_mxfp8_rows_kbm<false, true, true>), grid, dim3(256), 0, stream, x, M, N, seed,
+                               stream_id, out, out_e8m0, offsets, G, padded_offsets, ld_e8m0, gather);
+        return hipGetLastError();
+    }
     if (fp4) {
         if (sr)
             hipLaunchKernelGGL((k_mxfp8_rows_kbm<true, true>), grid, dim3(256), 0, stream, x, M, N, seed, stream_id,

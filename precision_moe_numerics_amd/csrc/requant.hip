@@ -28,8 +28,8 @@ struct GroupBlock {
 };
 
 // Map padded block pb (32 output columns) to its slots: walk the groups, each padded to a
-// multiple of `unit` (32, or 64 for the blocked GEMM operands, whose last block of a group can
-// then be all padding: valid = 0).
+// multiple of `unit` (32, or 64 / 128 for the blocked GEMM operands, whose last blocks of a group
+// can then be all padding: valid = 0).
 PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t M, int64_t unit)
 {
     GroupBlock r;
@@ -97,9 +97,10 @@ struct TransposeArgs {
     uint8_t* out_e8m0;        // [cols x ld/32], or k-block-major [ld/32 x cols] when e8m0_kb_major
     int64_t ld;
     bool e8m0_kb_major;
-    // E4M3 target only: codes in 1 KB blocks of 16 rows x 64 bytes (the GEMM operand layout; see
-    // store_blocked) and groups padded to 64 slots instead of 32
+    // codes in 1 KB blocks of 16 rows x 64 bytes (the GEMM operand layout) and groups padded to
+    // `unit` slots (64 for E4M3, 128 for packed E2M1: one 64-byte block column) instead of 32
     bool blocked;
+    int64_t unit;
 };
 
 // E4M3 code of v / scale (scale a power of two) by stochastic rounding with the given SR operand,
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
     const int64_t pb = (int64_t)blockIdx.x * 4 + w;
     const int64_t cg = (int64_t)blockIdx.y * 64 + lane;   // column group of 8
     const int64_t c0 = cg * 8;
-    const GroupBlock blk = find_block(pb, a.offsets, a.G, a.M, a.blocked ? 64 : 32);
+    const GroupBlock blk = find_block(pb, a.offsets, a.G, a.M, a.unit);
     if (lane == 0) block_live[w] = blk.live ? 1 : 0;
     const bool active = blk.live && c0 < a.cols;
     // lane j (mod 32) fetches slot j's source row and outer scale with one vector load each;
@@ -339,7 +340,23 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
     // ---- store: 512 rows x 8 chunks of 16 bytes; a chunk is written if its column exists and its
     // 32-slot block lies inside the padded output.
     const int64_t col_base = (int64_t)blockIdx.y * 512;
-    if (TARGET == 2) {
+    if (TARGET == 2 && a.blocked) {
+        // 1 KB blocks of 16 output rows x 64 bytes: this tile's 128 slots are one block column
+        const int64_t nkb = a.ld >> 7;
+#pragma unroll 4
+        for (int k = 0; k < 8; k++) {
+            const int q = k * 256 + threadIdx.x;
+            const int b = q >> 6, t = q & 63;
+            const int r16 = t >> 2;
+            const int c = (t & 3) ^ ((r16 >> 2) & 3);
+            const int row = b * 16 + r16;
+            const int64_t col = col_base + row;
+            if (col < a.cols && block_live[c]) {
+                const uint4 v = *reinterpret_cast<const uint4*>(tile + tile_chunk(row, c));
+                *reinterpret_cast<uint4*>(a.out + (((col_base >> 4) + b) * nkb + (int64_t)blockIdx.x) * 1024 + t * 16) = v;
+            }
+        }
+    } else if (TARGET == 2) {
         // packed: 512 rows x 4 chunks of 16 bytes (one 32-slot block each)
 #pragma unroll 4
         for (int k = 0; k < 8; k++) {
@@ -411,7 +428,7 @@ static hipError_t launch_transpose(const TransposeArgs& a, int src, int round, i
 {
     if (padded_offsets)
         hipLaunchKernelGGL(k_padded_offsets, dim3(1), dim3(64), 0, stream, a.offsets, a.G, a.M, padded_offsets,
-                           (int64_t)(a.blocked ? 64 : 32));
+                           a.unit);
     const int64_t nblk = a.ld / 32;
     if (nblk == 0 || a.cols == 0) return hipGetLastError();
     dim3 grid((unsigned)((nblk + 3) / 4), (unsigned)((a.cols / 8 + 63) / 64));
@@ -442,7 +459,8 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 {
     TransposeArgs a{};
     a.e8m0_kb_major = e8m0_kb_major;
-    a.blocked = blocked && target == PMN_TARGET_E4M3;
+    a.blocked = blocked && (target == PMN_TARGET_E4M3 || target == TARGET_E2M1_PACKED);
+    a.unit = a.blocked ? (target == PMN_TARGET_E4M3 ? 64 : 128) : 32;
     a.codes = codes; a.scales = scales; a.outer = outer; a.rows_per_outer = rows_per_outer;
     a.x = nullptr; a.cols = cols; a.gather = gather; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;
@@ -456,7 +474,8 @@ hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int6
 {
     TransposeArgs a{};
     a.e8m0_kb_major = e8m0_kb_major;
-    a.blocked = blocked && target == PMN_TARGET_E4M3;
+    a.blocked = blocked && (target == PMN_TARGET_E4M3 || target == TARGET_E2M1_PACKED);
+    a.unit = a.blocked ? (target == PMN_TARGET_E4M3 ? 64 : 128) : 32;
     a.codes = nullptr; a.scales = nullptr; a.outer = nullptr; a.rows_per_outer = 1;
     a.x = x; a.cols = N; a.gather = nullptr; a.M = M; a.offsets = offsets; a.G = G;
     a.seed = seed; a.stream_id = stream_id; a.out = out; a.out_e8m0 = out_e8m0; a.ld = ld;

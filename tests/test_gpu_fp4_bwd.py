@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle as O
+from decoders import unblock
 
 pytestmark = pytest.mark.gpu
 
@@ -73,21 +74,35 @@ def test_fp4_backward_operands_and_gradients(P, counts, N, K, gather_rows, sr):
                                         dy_rounding=P.SR if sr else P.RNE, seed=seed, rng_stream_a=sa,
                                         rng_stream_b=sb, rng_stream_dy=sdy)
     v = P.bwd_workspace_views(ws, M, G, N, K, fp4=True)
+    # The library pads each group to 128 slots (one 64-byte block column of packed codes) and
+    # keeps the code parts blocked; the oracle pads to 32 and is row-major.
     off = d["offsets"]
-    po = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
+    cnt = np.diff(off)
+    po32 = np.concatenate([[0], np.cumsum((cnt + 31) // 32 * 32)])
+    po = np.concatenate([[0], np.cumsum((cnt + 127) // 128 * 128)])
+    assert np.array_equal(npy(v["po"]), po)
+    Pb = v["de"].shape[1]
     grp = np.searchsorted(off, np.arange(M), side="right") - 1
     pcol = po[grp] + np.arange(M) - off[grp]
-    Pt = int(po[-1])
     # dY row-wise (the dgrad's A) and column-wise per group (the wgrad's A)
     rq, re = O.mxfp8_quantize_rows(d["dy"], sr=sr, seed=seed, stream=sdy, target=E2M1)
-    assert np.array_equal(npy(v["dq"]), pack(rq)) and np.array_equal(npy(v["de"])[:, pcol].T, re)
+    assert np.array_equal(unblock(npy(v["dq"]), Pb, N // 2)[pcol], pack(rq))
+    assert np.array_equal(npy(v["de"])[:, pcol].T, re)
     rt, rte = O.mxfp8_quantize_cols(d["dy"], offsets=off, sr=sr, seed=seed, stream=sdy + 1, target=E2M1)
-    assert np.array_equal(npy(v["dt"])[:, :Pt // 2], pack(rt)) and np.array_equal(npy(v["dte"]).T[:, :Pt // 32], rte)
     # W^T and A^T requantized by SR onto the E2M1 grid
     rwt, rwte = O.requant_transpose_sr(d["rwq"], target=E2M1, seed=seed, stream=sb)
-    assert np.array_equal(npy(v["wt"]), pack(rwt)) and np.array_equal(npy(v["wte"]).T, rwte)
+    assert np.array_equal(unblock(npy(v["wt"]), K, G * N // 2), pack(rwt)) and np.array_equal(npy(v["wte"]).T, rwte)
     rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=off, target=E2M1, seed=seed, stream=sa)
-    assert np.array_equal(npy(v["xt"])[:, :Pt // 2], pack(rxt)) and np.array_equal(npy(v["xte"]).T[:, :Pt // 32], rxte)
+    for name, ref, ref_e in (("dt", rt, rte), ("xt", rxt, rxte)):
+        got = unblock(npy(v[name]), ref.shape[0], Pb // 2)
+        got_e = npy(v[name + "e"]).T
+        pref = pack(ref)
+        for g in range(G):
+            n32 = po32[g + 1] - po32[g]
+            a, a32 = po[g], po32[g]
+            assert np.array_equal(got[:, a // 2:(a + n32) // 2], pref[:, a32 // 2:(a32 + n32) // 2]), (name, g)
+            assert np.array_equal(got_e[:, a // 32:(a + n32) // 32], ref_e[:, a32 // 32:(a32 + n32) // 32]), (name, g)
+            assert np.all(got[:, (a + n32) // 2:po[g + 1] // 2] == 0), (name, g)   # blocks of padding only
     # gradients on the FP4 MFMA
     da_ref = O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, off, N, K, target=E2M1)
     db_ref = O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, off, N, K, target=E2M1)
