@@ -223,9 +223,12 @@ size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, in
  * moe_grouped_gemm_fwd (SWIGLU: rows 0..F-1 of each expert are w1, F..2F-1 are w3). N % 256 == 0,
  * K % 32 == 0. x, w, out, out_aux and the workspace 16-byte aligned, out_e8m0 8-byte aligned
  * (PMN_EALIGN). Workspace (>= moe_grouped_gemm_fwd_mxfp8_workspace_size) holds, in order, each
- * part rounded up to 256 bytes: X8 codes [M x K] in slot order and E8M0 [K/32 x Pb] (slot s of
- * group g at column padded_offsets[g] + s - offsets[g]); W8 codes [G*N x K] and E8M0
- * [K/32 x G*N]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M, G).
+ * part rounded up to 256 bytes: X8 codes [Pb x Kp] and E8M0 [K/32 x Pb], slot s of group g at
+ * row / column padded_offsets[g] + s - offsets[g] (groups padded to 32 slots); W8 codes
+ * [G*N x Kp] and E8M0 [K/32 x G*N]; padded offsets int64 [G+1] -- with Pb = pmn_padded_bound(M,
+ * G) and Kp = K rounded up to a multiple of 64 (bytes K .. Kp-1 of a row hold zero codes). The
+ * code parts are blocked as described for moe_grouped_gemm_bwd; rows of padding slots are left
+ * unwritten.
  */
 int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gather, const void* w,
                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int epilogue,

@@ -55,11 +55,12 @@ FwdMx8Layout fwd_mx8_layout(int64_t M, int G, int64_t N, int64_t K)
 {
     FwdMx8Layout L{};
     L.Pb = pmn_padded_bound(M, G);
+    const int64_t Kp = (K + 63) & ~(int64_t)63;   // blocked rows: whole 64-byte block columns
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
-    L.xq = take((size_t)(M * K));
+    L.xq = take((size_t)(L.Pb * Kp));
     L.xe = take((size_t)(K / 32 * L.Pb));
-    L.wq = take((size_t)((int64_t)G * N * K));
+    L.wq = take((size_t)((int64_t)G * N * Kp));
     L.we = take((size_t)(K / 32 * (int64_t)G * N));
     L.po = take((size_t)(G + 1) * sizeof(int64_t));
     L.total = off;
@@ -279,11 +280,12 @@ int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gat
     if (e != hipSuccess) return PMN_ELAUNCH;
     // W row-wise (RNE), E8M0 k-block-major [K/32 x G*N]
     e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(w), (int64_t)G * N, K, false, 0, 0, ws + L.wq,
-                               ws + L.we, nullptr, 0, nullptr, (int64_t)G * N, s);
+                               ws + L.we, nullptr, 0, nullptr, (int64_t)G * N, s, nullptr, false, true);
     if (e != hipSuccess) return PMN_ELAUNCH;
-    // X in slot order (row s = x[gather[s]]), E8M0 k-block-major at padded slot columns
+    // X in slot order (row s = x[gather[s]]) at padded slot rows, E8M0 k-block-major at padded
+    // slot columns
     e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(x), M, K, false, 0, 0, ws + L.xq, ws + L.xe, offsets, G,
-                               po, L.Pb, s, gather);
+                               po, L.Pb, s, gather, false, true);
     if (e != hipSuccess) return PMN_ELAUNCH;
     e = pmn::launch_mxfp8_fwd(ws + L.wq, ws + L.we, ws + L.xq, ws + L.xe, offsets, po, L.Pb, G, M, N, K, epilogue,
                               rht_sign_mask, out, out_e8m0, out_aux, s);

@@ -28,9 +28,10 @@
 //
 // LDS stage: A codes [256 rows x 64 B], B codes [256 x 64 B], A scales [2 k-blocks x 256 rows],
 // B scales [2 x 256]. Chunk c (16 B) of row r sits at slot c ^ ((r / 4) % 4): the 16 rows a
-// quarter-wavefront reads cover all 16 bank groups (the load side applies the same permutation
-// when it picks which chunk each lane fetches). Scales are streamed from k-block-major arrays, so
-// one k-block of 256 rows is 256 contiguous bytes.
+// quarter-wavefront reads cover all 16 bank groups. The operands arrive in that order: the
+// quantizers write them in 1 KB blocks of 16 rows x 64 bytes with the same permutation (the
+// blocked layout), so every copy moves one whole contiguous block. Scales are streamed from
+// k-block-major arrays, so one k-block of 256 rows is 256 contiguous bytes.
 #include "pmn_dev.hpp"
 #include "pmn_kernels.hpp"
 
@@ -146,9 +147,6 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     constexpr int LDSBk = NSTAGE * STAGEBk;
     constexpr int LPS = FP4 ? LOADS_PER_STAGE + 1 : LOADS_PER_STAGE;
     constexpr int KS = FP4 ? 2 * BK : BK;           // values (k) per stage
-    // dgrad and wgrad read the blocked layout: a stage piece (16 rows x 64 bytes) is one
-    // contiguous 1 KB block, already in the LDS image's order
-    constexpr bool BLK = MODE != MODE_FWD;
     typedef typename FragsOf<FP4>::type Frags;
     __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSBk];
     // An AGPR operand marks the kernel as using AGPRs, so the compiler keeps the 256 accumulator
@@ -161,7 +159,10 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
 
     int g = -1;
     int64_t r0 = 0, rvalid = BT, c0 = 0, klen = 0, cvalid = BT;
+    // operands in the blocked layout: acode / bcode point at block column 0 of the tile's k range,
+    // arb0 / brb0 are the tile's first row blocks
     const uint8_t *acode, *bcode, *asc, *bsc;
+    int64_t arb0 = 0, brb0 = 0;
     int64_t asld, bsld, asrows = BT, bsrows = BT;
     float* obase;
     TileXY tile;
@@ -188,10 +189,12 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         klen = p.Nf;
         r0 = tile.row * BT;                      // first feature row (plain order)
         const int64_t wrow0 = (int64_t)g * p.Kf + (EPI == PMN_EPI_SWIGLU ? 0 : r0);
-        acode = p.a + wrow0 * p.lda;
+        acode = p.a;
+        arb0 = wrow0 >> 4;                       // (the SwiGLU tile maps each piece itself)
         asc = p.ae + wrow0;
         asld = (int64_t)p.G * p.Kf;
-        bcode = p.b + c0 * p.ldb;
+        bcode = p.b;
+        brb0 = p0 >> 4;                          // slot rows sit at their padded positions
         bsc = p.be + p0;
         bsld = p.Pb;
         bsrows = p.Pb - p0;
@@ -204,13 +207,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         const int64_t p0 = p.po[g] + u.index * BT;
         rvalid = u.s1 - r0 < BT ? u.s1 - r0 : BT;
         klen = p.Nf;
-        // blocked: slot rows sit at their padded positions, whole 1 KB blocks of the stage
-        acode = BLK ? p.a + ((p0 >> 4) * (p.lda >> 6)) * 1024 : p.a + r0 * p.lda;
+        acode = p.a;
+        arb0 = p0 >> 4;                          // slot rows sit at their padded positions
         asc = p.ae + p0;
         asld = p.Pb;
         asrows = p.Pb - p0;                      // scale columns of this tile inside the array
-        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (int64_t)g * ((FP4 ? p.Nf / 2 : p.Nf) >> 6)) * 1024
-                    : p.b + c0 * p.ldb + (int64_t)g * (FP4 ? p.Nf / 2 : p.Nf);
+        bcode = p.b + (int64_t)g * ((FP4 ? p.Nf / 2 : p.Nf) >> 6) * 1024;   // expert g's columns
+        brb0 = c0 >> 4;
         bsc = p.be + (int64_t)g * (p.Nf / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + r0 * p.Kf;
@@ -220,26 +223,28 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         const int64_t kbeg = p.po[g];
         klen = p.po[g + 1] - kbeg;
         const int64_t kbyte = FP4 ? kbeg / 2 : kbeg;   // first code byte of the group in a row
-        acode = BLK ? p.a + ((r0 >> 4) * (p.lda >> 6) + (kbyte >> 6)) * 1024 : p.a + r0 * p.lda + kbyte;
+        acode = p.a + (kbyte >> 6) * 1024;
+        arb0 = r0 >> 4;
         asc = p.ae + (kbeg / 32) * p.Nf + r0;
         asld = p.Nf;
-        bcode = BLK ? p.b + ((c0 >> 4) * (p.ldb >> 6) + (kbyte >> 6)) * 1024 : p.b + c0 * p.ldb + kbyte;
+        bcode = p.b + (kbyte >> 6) * 1024;
+        brb0 = c0 >> 4;
         bsc = p.be + (kbeg / 32) * p.Kf + c0;
         bsld = p.Kf;
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
     }
 
     // Load schedule. Wavefronts 0-1 load A, 2-3 load B. Codes: wavefront w issues the 1 KB
-    // pieces 8 (w % 2) .. 8 (w % 2) + 7 of its operand (16 rows each); lane l of piece n lands at
-    // row 16 n + l / 4, slot l % 4, and so fetches chunk (l % 4) ^ ((l / 16) % 4). Rows outside the
-    // tile (dgrad's last tile of a group) fetch row 0 instead: their outputs are never stored.
+    // pieces 8 (w % 2) .. 8 (w % 2) + 7 of its operand (16 rows each). A piece of a stage is one
+    // block of the blocked operand layout, copied whole (lane l moves its bytes 16 l .. 16 l + 15),
+    // so it lands in the order the fragment reads expect. Pieces past the tile's valid rows (the
+    // last tile of a group) re-read the tile's first block: their outputs are never stored.
     // Scales: wavefront w loads k-block w % 2 of the stage, rows 4 l .. 4 l + 3 in lane l.
     const int op = wave >> 1, half = wave & 1;
     const uint8_t* cbase = op ? bcode : acode;
-    // row stride (row-major) or row-block stride (blocked: 16 rows = ld / 64 blocks of 1 KB)
-    const int64_t cld = BLK ? ((op ? p.ldb : p.lda) >> 6) * 1024 : (op ? p.ldb : p.lda);
+    const int64_t crb0 = op ? brb0 : arb0;
+    const int64_t cld = ((op ? p.ldb : p.lda) >> 6) * 1024;   // bytes per row block (ld / 64 blocks)
     const int crows = (int)(op ? cvalid : rvalid);
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
     const uint8_t* sbase = op ? bsc : asc;
     const int64_t sld = op ? bsld : asld;
     const int64_t srows = op ? bsrows : asrows;
@@ -253,8 +258,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
 
     const int64_t kblocks = klen / 32;
     const int KT = (int)((klen + KS - 1) / KS);
-    const bool half_tail = (klen & (BK - 1)) != 0;   // last stage holds one k-block (wgrad)
-    const int tail_back = chunk >= 2 ? 32 : 0;        // that stage's missing chunks re-read valid k
+    // last stage holds one k-block (the forward with K = 32 mod 64; the other half of its block
+    // column holds zero codes)
+    const bool half_tail = (klen & (BK - 1)) != 0;
 
     // Steps v = 0 .. KV-1 walk the stages; when KT is odd a leading step (v = 0) re-reads stage 0
     // with every scale forced to 2^-127 on both operands, so it adds nothing and the step count
@@ -270,27 +276,15 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     auto issue_at = [&](int v) {
         const int kt = stage_of(v);
         IssueAt r;
+        // stage kt of a piece is block column kt; this lane's 16 bytes of it
+        r.kc = (int64_t)kt * 1024 + lane * 16;
         if (FP4) {
-            // 16-byte chunk c of a stage row is k-block 4 kt + c; chunks past the last k-block
-            // re-read the last valid one (FP4 codes are always finite; their scale is 2^-127).
-            // Blocked: stage kt is block column kt (every k length is a multiple of 128).
-            const int64_t vch = kblocks - 4 * (int64_t)kt;
-            const int64_t cc = chunk < vch ? chunk : vch - 1;
-            r.kc = BLK ? (int64_t)kt * 1024 + lane * 16 : (int64_t)kt * BK + cc * 16;
+            // FP4: k-blocks 4 kt .. 4 kt + 3 (every k length is a multiple of 128)
             r.kb = 4 * (int64_t)kt + 2 * half;
             r.kb2 = r.kb + 1 < kblocks ? r.kb + 1 : kblocks - 1;
             r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
-        } else if (BLK) {
-            // stage kt of a piece is block column kt (every k length is a multiple of 64)
-            const int64_t k0 = (int64_t)kt * BK;
-            r.kc = (int64_t)kt * 1024 + lane * 16;
-            r.kb = (k0 >> 5) + half;
-            r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
-            r.kb2 = 0;
         } else {
-            const int64_t k0 = (int64_t)kt * BK;
-            r.kc = ((half_tail && kt == KT - 1) ? k0 - tail_back : k0) + chunk * 16;
-            r.kb = (k0 >> 5) + half;
+            r.kb = 2 * (int64_t)kt + half;
             r.kb = r.kb < kblocks ? r.kb : kblocks - 1;
             r.kb2 = 0;
         }
@@ -298,16 +292,12 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         return r;
     };
     auto issue_piece = [&](const IssueAt& r, int i) {
-        if (BLK) {
-            // row block half * 8 + i of the tile; blocks past the tile's valid rows (dgrad's last
-            // tile of a group) re-read its first block: their outputs are never stored
-            const int pb = half * 8 + i;
-            dma16(cbase + (int64_t)(16 * pb < crows ? pb : 0) * cld + r.kc, cdst + r.so + i * 1024);
-        } else {
-            const int row = (half * 8 + i) * 16 + (lane >> 2);
-            const int64_t src = remap ? swiglu_a_row(row, tile.row, Fh) : (int64_t)(row < crows ? row : 0);
-            dma16(cbase + src * cld + r.kc, cdst + r.so + i * 1024);
-        }
+        // row block of piece pb = half * 8 + i: the SwiGLU tile's A rows come from w1 and w3 in
+        // 32-row runs, so each 16-row piece is still one block
+        const int pb = half * 8 + i;
+        const int64_t rb = remap ? (((int64_t)g * p.Kf + swiglu_a_row(16 * pb, tile.row, Fh)) >> 4)
+                                 : crb0 + (16 * pb < crows ? pb : 0);
+        dma16(cbase + rb * cld + r.kc, cdst + r.so + i * 1024);
     };
     auto issue_scales = [&](const IssueAt& r) { dma4(sptr + r.kb * sld, sdst + r.so); };
     auto issue_scales2 = [&](const IssueAt& r) { dma4(sptr + r.kb2 * sld, sdst + r.so + BT); };
@@ -604,7 +594,8 @@ hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t*
     const int64_t rt = N / bwd::BT, ct = (M + bwd::BT - 1) / bwd::BT + G;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
-    Mx8Args p{wq, we, K, xq, xe, K, offsets, po, Pb, G, K, N, nullptr, rt, ct, SM, SN, out, out_e8m0, out_aux, mask};
+    const int64_t Kp = (K + 63) & ~(int64_t)63;   // blocked rows: K rounded up to whole 64-byte blocks
+    Mx8Args p{wq, we, Kp, xq, xe, Kp, offsets, po, Pb, G, K, N, nullptr, rt, ct, SM, SN, out, out_e8m0, out_aux, mask};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
     switch (epilogue) {
     case PMN_EPI_F32:

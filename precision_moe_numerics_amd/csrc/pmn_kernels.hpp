@@ -22,8 +22,9 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
 // they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column
 // padded_offsets[g] + s - offsets[g] (the layout the grouped dgrad GEMM streams). `blocked`
 // (k-block-major only) writes the codes in the blocked layout below with slot s of group g at row
-// padded_offsets[g] + s - offsets[g] ([ld_e8m0 rows x N or N/2 bytes]; padding rows are not
-// written).
+// padded_offsets[g] + s - offsets[g] (without padded_offsets: row s), in rows of N rounded up to
+// 64 bytes (E4M3; the rounding bytes hold zero codes) or N/2 bytes (packed E2M1, N % 128 == 0);
+// padding rows are not written.
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
                              uint32_t stream_id, uint8_t* out, uint8_t* out_e8m0,
                              const int64_t* offsets, int G, const int64_t* padded_offsets,
@@ -64,8 +65,9 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
                            void* out_aux, hipStream_t stream);
 
-// Grouped MXFP8 GEMMs. All E8M0 operands are k-block-major: de [Nf/32 x Pb] (padded slot
-// columns, po), wte [G*Nf/32 x Kf], dte [Pb/32 x Nf], xte [Pb/32 x Kf].
+// Grouped MXFP8 GEMMs. Code operands are in the blocked layout; all E8M0 operands are
+// k-block-major: de [Nf/32 x Pb] (padded slot columns, po), wte [G*Nf/32 x Kf], dte [Pb/32 x Nf],
+// xte [Pb/32 x Kf]. The forward takes W8 [G*N rows x roundup(K, 64)] and X8 at padded slot rows.
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,

@@ -476,12 +476,18 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                 uint32_t o[8];
                 e = mxfp8_block<SR>(w, r, kb, N, seed, stream_id, o);
                 if (BLK) {
-                    // k-block kb = chunks 2 (kb % 2) and 2 (kb % 2) + 1 of 64-byte column kb / 2
+                    // k-block kb = chunks 2 (kb % 2) and 2 (kb % 2) + 1 of 64-byte column kb / 2; rows
+                    // are whole columns (N rounded up to 64 bytes), and with an odd k-block count the
+                    // last column's second half holds zero codes
                     const int64_t pr = padded_col(r);
                     const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
-                    uint8_t* blk = out + ((pr >> 4) * (N >> 6) + (kb >> 1)) * 1024 + r16 * 64;
+                    uint8_t* blk = out + ((pr >> 4) * ((N + 63) >> 6) + (kb >> 1)) * 1024 + r16 * 64;
                     *reinterpret_cast<uint4*>(blk + ((c ^ x) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
                     *reinterpret_cast<uint4*>(blk + (((c + 1) ^ x) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+                    if ((nb & 1) && kb == nb - 1) {
+                        *reinterpret_cast<uint4*>(blk + (((c + 2) ^ x) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                        *reinterpret_cast<uint4*>(blk + (((c + 3) ^ x) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                    }
                 } else {
                     store_block32(out, r * nb + kb, o);
                 }
@@ -503,7 +509,7 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
     const int64_t nb = N / 32;
     if (M * nb == 0) return hipSuccess;
     if ((fp4 || blocked) && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
-    if (blocked && N % (fp4 ? 128 : 64) != 0) return hipErrorInvalidValue;
+    if (blocked && fp4 && N % 128 != 0) return hipErrorInvalidValue;
     if (padded_offsets == nullptr && ld_e8m0 == 0) {
         const int64_t grid = (M * nb + 255) / 256;
         if (sr)

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle as O
-from decoders import decode_s2f6_rows
+from decoders import decode_s2f6_rows, unblock
 
 pytestmark = pytest.mark.gpu
 
@@ -80,21 +80,25 @@ def test_mxfp8_fwd_f32_bf16_and_operands(P, counts, N, K, gather_rows):
     yb = P.moe_grouped_gemm_fwd_mxfp8(d["x"].to(DEV), d["w"].to(DEV), d["goff"], M, N, P.EPI_BF16,
                                       gather=d["ggather"])
     assert torch.equal(yb, y.to(torch.bfloat16))
-    # the quantized operands in the workspace: X in slot order, W row-wise; E8M0 k-block-major
+    # the quantized operands in the workspace: X in slot order at padded rows, W row-wise, both
+    # blocked with rows of K rounded up to 64 bytes (zero codes past K); E8M0 k-block-major
     w8 = npy(ws)
     Pb = P.padded_bound(M, G)
+    Kp = (K + 63) // 64 * 64
     r256 = lambda b: (b + 255) // 256 * 256
-    o_xq, o_xe = 0, r256(M * K)
+    o_xq, o_xe = 0, r256(Pb * Kp)
     o_wq = o_xe + r256(K // 32 * Pb)
-    o_we = o_wq + r256(G * N * K)
-    rows = d["gather"] if d["gather"] is not None else np.arange(M)
-    assert np.array_equal(w8[o_xq:o_xq + M * K].reshape(M, K), d["xq"][rows])
-    assert np.array_equal(w8[o_wq:o_wq + G * N * K].reshape(G * N, K), d["wq"])
-    assert np.array_equal(w8[o_we:o_we + K // 32 * G * N].reshape(K // 32, G * N).T, d["we"])
+    o_we = o_wq + r256(G * N * Kp)
     off = d["offsets"]
     po = np.concatenate([[0], np.cumsum((np.diff(off) + 31) // 32 * 32)])
     grp = np.searchsorted(off, np.arange(M), side="right") - 1
     pcol = po[grp] + np.arange(M) - off[grp]
+    rows = d["gather"] if d["gather"] is not None else np.arange(M)
+    xb = unblock(w8[o_xq:o_xq + Pb * Kp], Pb, Kp)[pcol]
+    wb = unblock(w8[o_wq:o_wq + G * N * Kp], G * N, Kp)
+    assert np.array_equal(xb[:, :K], d["xq"][rows]) and np.all(xb[:, K:] == 0)
+    assert np.array_equal(wb[:, :K], d["wq"]) and np.all(wb[:, K:] == 0)
+    assert np.array_equal(w8[o_we:o_we + K // 32 * G * N].reshape(K // 32, G * N).T, d["we"])
     assert np.array_equal(w8[o_xe:o_xe + K // 32 * Pb].reshape(K // 32, Pb)[:, pcol].T, d["xe"][rows])
 
 
