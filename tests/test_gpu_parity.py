@@ -297,13 +297,17 @@ def test_gemm_fwd_rht_epilogue_bit_exact(P, I):
     assert rel_fro(decode_s2f6_rows(npy(c), npy(e), mask), ref) < 0.02
 
 
-def test_gemm_bwd_intermediates_and_gradients(P, I):
+@pytest.mark.parametrize("sr", [False, True])
+def test_gemm_bwd_intermediates_and_gradients(P, I, sr):
+    """Both gradients in one call: dY's row-wise and column-wise MXFP8 (RNE, or SR on streams 6
+    and 7), W^T and A^T from the SR requant, and the two gradients."""
     counts, N, K = [40, 0, 333, 227], 256, 512
     d = _moe_small(P, I, counts, N, K, gather_rows=400, seed=80)
     M, G = d["M"], len(counts)
     dy = I.normal((M, N), 1e-3, 81)
     da, db, ws = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
-                                        seed=9, rng_stream_a=4, rng_stream_b=1, rng_stream_dy=6)
+                                        dy_rounding=P.SR if sr else P.RNE, seed=9, rng_stream_a=4, rng_stream_b=1,
+                                        rng_stream_dy=6)
     v = P.bwd_workspace_views(ws, M, G, N, K)
     # The library pads each group to 64 slots and keeps the code parts blocked; the oracle pads
     # to 32 and is row-major. E8M0 parts are k-block-major; the row-wise dY codes and scales sit
@@ -316,12 +320,12 @@ def test_gemm_bwd_intermediates_and_gradients(P, I):
     Pb = v["de"].shape[1]
     grp = np.searchsorted(off, np.arange(M), side="right") - 1
     pcol = po[grp] + np.arange(M) - off[grp]
-    rq, re = O.mxfp8_quantize_rows(dy)
+    rq, re = O.mxfp8_quantize_rows(dy, sr=sr, seed=9, stream=6)
     assert np.array_equal(unblock(npy(v["dq"]), Pb, N)[pcol], rq)
     assert np.array_equal(npy(v["de"])[:, pcol].T, re)
     rwt, rwte = O.requant_transpose_sr(d["rwq"], seed=9, stream=1)
     assert np.array_equal(unblock(npy(v["wt"]), K, G * N), rwt) and np.array_equal(npy(v["wte"]).T, rwte)
-    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], stream=7)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], sr=sr, seed=9, stream=7)
     rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=d["offsets"], seed=9, stream=4)
     for name, ref, ref_e in (("dt", rt, rte), ("xt", rxt, rxte)):
         got = unblock(npy(v[name]), ref.shape[0], Pb)
