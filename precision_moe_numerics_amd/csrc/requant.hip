@@ -306,7 +306,9 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                             asm volatile("" : "+v"(cwj));   // recompute rather than keep the amax pass's values
                             deq8(cwj, dsc[j], v);
                         } else {
-                            bf8(xw[j], v);
+                            uint4 xj = xw[j];
+                            asm volatile("" : "+v"(xj.x), "+v"(xj.y), "+v"(xj.z), "+v"(xj.w));
+                            bf8(xj, v);
                         }
                         uint32_t rw[4] = {0u, 0u, 0u, 0u};
                         if (ROUND == 1)
