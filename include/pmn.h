@@ -197,8 +197,9 @@ int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, ui
  * A: NVFP4 [a_rows x K] with a_rows_per_outer; B: NVFP4 [G*N x K] with b_rows_per_outer.
  * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (for SWIGLU also F % b_rows_per_outer == 0
  * or b_rows_per_outer % N == 0, so w1 and w3 rows keep their own outer scales). M is the number of
- * slots (host value). Codes, out and out_aux 16-byte aligned, scales 4-byte aligned, out_e8m0
- * (RHT32_S2F6) 8-byte aligned; PMN_EALIGN otherwise.
+ * slots (host value); with M == 0 nothing is computed and a_*, out, out_e8m0 may be null.
+ * Codes, out and out_aux 16-byte aligned, scales 4-byte aligned, out_e8m0 (RHT32_S2F6) 8-byte
+ * aligned; PMN_EALIGN otherwise.
  */
 int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                          int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather,
@@ -221,7 +222,8 @@ size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, in
  * PMN_ROWWISE and PMN_RNE) of x bf16 [x_rows x K] and w bf16 [G*N x K], s a slot of group g
  * (offsets, device int64 [G+1]) and row_s = gather[s] (or s). The epilogues are those of
  * moe_grouped_gemm_fwd (SWIGLU: rows 0..F-1 of each expert are w1, F..2F-1 are w3). N % 256 == 0,
- * K % 32 == 0. x, w, out, out_aux and the workspace 16-byte aligned, out_e8m0 8-byte aligned
+ * K % 32 == 0 (M == 0: only w is quantized; x, out, out_e8m0 may be null). x, w, out, out_aux
+ * and the workspace 16-byte aligned, out_e8m0 8-byte aligned
  * (PMN_EALIGN). Workspace (>= moe_grouped_gemm_fwd_mxfp8_workspace_size) holds, in order, each
  * part rounded up to 256 bytes: X8 codes [Pb x Kp] and E8M0 [K/32 x Pb], slot s of group g at
  * row / column padded_offsets[g] + s - offsets[g] (groups padded to 32 slots); W8 codes
@@ -255,6 +257,7 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * dy: bf16 [M x N]; a_*: NVFP4 [a_rows x K] (+ gather); b_*: NVFP4 [G*N x K]; offsets device
  * int64 [G+1]. N % 256 == 0, K % 256 == 0. Outputs fp32: da [M x K], db [G*N x K].
  * dY quantized with SR uses rng_stream_dy (row-wise) and rng_stream_dy + 1 (column-wise).
+ * M == 0 (no routed slots) is valid: dy, da and a_* may then be null, and db is set to zero.
  * Workspace (16-byte aligned, >= moe_grouped_gemm_bwd_workspace_size) holds, in order, each
  * part rounded up to 256 bytes: dY row-wise codes [Pb x N] and E8M0 [N/32 x Pb]; W^T codes
  * [K x G*N] and E8M0 [G*N/32 x K]; dY^T codes [N x Pb] and E8M0 [Pb/32 x N]; A^T codes [K x Pb]

@@ -174,9 +174,10 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const 
     if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 64 != 0) return PMN_ESHAPE;
     if (a_rows_per_outer < 1 || b_rows_per_outer < 32 || b_rows_per_outer % 32 != 0) return PMN_ESHAPE;
     if (!gather && M > a_rows) return PMN_ESHAPE;
-    if (!offsets || !a_codes || !a_scales || !a_outer || !b_codes || !b_scales || !b_outer || !out)
+    if (!offsets || !b_codes || !b_scales || !b_outer) return PMN_EINVAL;
+    // with no slots (M == 0) the row-sized buffers (activations, outputs) may be null
+    if (M > 0 && (!a_codes || !a_scales || !a_outer || !out || (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0)))
         return PMN_EINVAL;
-    if (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0) return PMN_EINVAL;
     if (!aligned(a_codes, 16) || !aligned(b_codes, 16) || !aligned(a_scales, 4) || !aligned(b_scales, 4) ||
         !aligned(out, 16) || (out_aux && !aligned(out_aux, 16)) ||
         (epilogue == PMN_EPI_RHT32_S2F6 && !aligned(out_e8m0, 8)))
@@ -209,10 +210,12 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
     if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
     if (!gather && M > a_rows) return PMN_ESHAPE;
-    if (!offsets || !dy) return PMN_EINVAL;
+    // with no slots (M == 0) dy, da and the activations may be null: dgrad has no rows and
+    // wgrad writes zero gradients
+    if (!offsets || (M > 0 && !dy)) return PMN_EINVAL;
     const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
-    if (dgrad && (!b_codes || !b_scales || !b_outer || !da)) return PMN_EINVAL;
-    if (wgrad && (!a_codes || !a_scales || !a_outer || !db)) return PMN_EINVAL;
+    if (dgrad && (!b_codes || !b_scales || !b_outer || (M > 0 && !da))) return PMN_EINVAL;
+    if (wgrad && (!db || (M > 0 && (!a_codes || !a_scales || !a_outer)))) return PMN_EINVAL;
     const bool fp4 = flags & PMN_BWD_FP4;
     const BwdLayout L = bwd_layout(M, G, N, K, fp4);
     if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
@@ -227,7 +230,7 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
     int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
     hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, pmn::blocked_unit(fp4));
     if (e != hipSuccess) return PMN_ELAUNCH;
-    if (dgrad) {
+    if (dgrad && M > 0) {
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
                                    ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
@@ -266,8 +269,8 @@ int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gat
     if (epilogue < PMN_EPI_F32 || epilogue > PMN_EPI_RHT32_S2F6) return PMN_EINVAL;
     if (G < 1 || M < 0 || x_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 32 != 0) return PMN_ESHAPE;
     if (!gather && M > x_rows) return PMN_ESHAPE;
-    if (!offsets || !w || !out || (M > 0 && !x)) return PMN_EINVAL;
-    if (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0) return PMN_EINVAL;
+    if (!offsets || !w || (M > 0 && (!x || !out || (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0))))
+        return PMN_EINVAL;
     const FwdMx8Layout L = fwd_mx8_layout(M, G, N, K);
     if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
     if (!aligned(workspace, 16) || !aligned(w, 16) || (x && !aligned(x, 16)) || !aligned(out, 16) ||

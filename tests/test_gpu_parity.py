@@ -391,3 +391,25 @@ def test_gemm_bwd_odd_stage_counts_and_half_stages(P, I):
     rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=d["offsets"], seed=4, stream=2)
     assert rel_fro(npy(da), O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K)) <= 2e-3
     assert rel_fro(npy(db), O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K)) <= 2e-3
+
+
+def test_empty_layer_gemms(P, I):
+    """A layer with no routed slots (M = 0, three experts): the forward GEMMs return empty outputs
+    and the backward gives an empty dgrad and zero weight gradients, in MXFP8 and in FP4."""
+    G, N, K = 3, 256, 256
+    offsets = torch.zeros(G + 1, dtype=torch.int64, device=DEV)
+    w = I.normal((G * N, K), 0.02, 5).to(DEV)
+    wq = P.nvfp4_quantize(w, P.NVFP4_WEIGHT, N // 2)
+    x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    xq = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    assert P.moe_grouped_gemm_fwd(xq, wq, offsets, 0, N, P.EPI_F32).shape == (0, N)
+    a, h13 = P.moe_grouped_gemm_fwd(xq, wq, offsets, 0, N, P.EPI_SWIGLU, save_h13=True)
+    assert a.shape == (0, N // 2) and h13.shape == (0, N)
+    assert P.moe_grouped_gemm_fwd_mxfp8(x, w, offsets, 0, N, P.EPI_F32).shape == (0, N)
+    dy = torch.empty((0, N), dtype=torch.bfloat16, device=DEV)
+    for flags in (P.BWD_DGRAD | P.BWD_WGRAD, P.BWD_DGRAD | P.BWD_WGRAD | P.BWD_FP4):
+        db = torch.full((G * N, K), float("nan"), dtype=torch.float32, device=DEV)
+        da, db, _ = P.moe_grouped_gemm_bwd(dy, xq, wq, offsets, 0, N, flags=flags, db=db)
+        torch.cuda.synchronize()
+        assert da.shape == (0, K)
+        assert torch.count_nonzero(db).item() == 0     # every expert's gradient written as zero
