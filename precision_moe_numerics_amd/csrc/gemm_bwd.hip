@@ -314,9 +314,9 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     const int off_lo = ((hh ^ swz) << 4), off_hi = (((2 + hh) ^ swz) << 4);
     // Fragments of step v: lane l supplies row l % 32 of each 32-row block with bytes 0..15 =
     // k 16h .. 16h+15 and bytes 16..31 = k 32+16h .. (h = l / 32), and the scale of k-block h.
-    // In a half-full last stage, k-block 1 holds re-read (finite) codes; both operands give it
-    // the E8M0 scale 2^-127, so its products are scaled by 2^-254 and vanish in fp32 (as does
-    // the whole leading step).
+    // A half-full last stage (the forward with K = 32 mod 64) holds zero codes in k-block 1, and
+    // both operands also give it the E8M0 scale 2^-127; the whole leading step is scaled by
+    // 2^-254 the same way, so its products vanish in fp32.
     auto frag_mask = [&](int v) {
         const int kt = v - pre;
         return (kt < 0 || (half_tail && kt == KT - 1 && hh)) ? 0 : 0xFF;
