@@ -343,6 +343,33 @@ def test_gemm_bwd_intermediates_and_gradients(P, I, sr):
     assert np.all(npy(db)[N:2 * N] == 0)          # the empty expert gets a zero gradient
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+def test_gemm_bwd_many_small_groups(P, I, fp4):
+    """96 experts with 0..40 slots each (many empty, most smaller than one 64- or 128-slot padded
+    stage): both gradients against the oracle, whose operands are its own quantizations."""
+    rng = np.random.default_rng(97)
+    counts = [int(c) if rng.random() > 0.25 else 0 for c in rng.integers(1, 41, 96)]
+    N, K = 256, 256
+    d = _moe_small(P, I, counts, N, K, gather_rows=900, seed=98)
+    M = d["M"]
+    dy = I.normal((M, N), 1e-3, 99)
+    flags = P.BWD_DGRAD | P.BWD_WGRAD | (P.BWD_FP4 if fp4 else 0)
+    da, db, _ = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, flags=flags,
+                                       gather=d["ggather"], seed=13, rng_stream_a=2, rng_stream_b=3, rng_stream_dy=4)
+    target = O.TARGET_E2M1 if fp4 else O.TARGET_E4M3
+    rq, re = O.mxfp8_quantize_rows(dy, target=target)
+    rwt, rwte = O.requant_transpose_sr(d["rwq"], target=target, seed=13, stream=3)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], target=target)
+    rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=d["offsets"], target=target, seed=13,
+                                       stream=2)
+    assert rel_fro(npy(da), O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K, target=target)) <= 2e-3
+    assert rel_fro(npy(db), O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K, target=target)) <= 2e-3
+    off = d["offsets"]
+    for g in range(len(counts)):
+        if off[g + 1] == off[g]:
+            assert np.all(npy(db)[g * N:(g + 1) * N] == 0)
+
+
 def test_gemm_bwd_sr_gradients_deterministic(P, I):
     counts, N, K = [200, 56], 256, 256
     d = _moe_small(P, I, counts, N, K, seed=90)
