@@ -403,9 +403,9 @@ def test_route_topk(P, I, T, E, k):
 
 
 def test_gemm_bwd_odd_stage_counts_and_half_stages(P, I):
-    """wgrad groups whose padded slot count gives an odd number of 64-slot stages, a half-full
-    last stage, or both (150 -> 160 slots: 3 stages, the last half full; 1 -> 32: 1 half stage;
-    95 -> 96: 2 stages, the last half full; 33 -> 64: 1 full stage)."""
+    """wgrad groups padded to whole 64-slot stages, with odd and even stage counts and mostly
+    padding in the last stage (150 -> 192 slots: 3 stages, 22 real slots in the last; 1 -> 64: 1
+    stage of 1 real slot; 95 -> 128: 2 stages; 33 -> 64: 1 stage)."""
     counts, N, K = [150, 1, 95, 33], 256, 256
     d = _moe_small(P, I, counts, N, K, gather_rows=300, seed=95)
     M = d["M"]
