@@ -50,25 +50,6 @@ constexpr int LOADS_PER_STAGE = 9;      // per wavefront
 static_assert(THREADS == 256 && BT == 256 && BK == 64 && NSTAGE == 4, "the load schedule below assumes these");
 }  // namespace bwd
 
-// Asynchronous global -> LDS copies. The LDS destination of lane l is m0 + 16 l (dwordx4) or
-// m0 + 4 l (dword), m0 being wavefront-uniform. They are issued from inline assembly so that the
-// compiler does not make every later LDS read wait for all of them; the kernel waits itself.
-PMN_DEV void dma16(const void* src, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
-}
-PMN_DEV void dma4(const void* src, uint32_t lds_base)
-{
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
-}
-// Wait for this wavefront's LDS reads and until at most N of its loads are outstanding, then
-// barrier: afterwards the stage those loads waited for is visible to the workgroup and every
-// wavefront has finished reading the stages it read before.
-template <int N>
-PMN_DEV void wait_loads_and_barrier()
-{
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
 enum { MODE_DGRAD = 0, MODE_WGRAD = 1, MODE_FWD = 2 };
 
 struct Mx8Args {
@@ -105,13 +86,6 @@ struct Mx8Args {
     void* yaux;
     uint32_t mask;
 };
-
-// fwd + SwiGLU: feature row (within the expert's 2F rows) of tile row t of n-tile nt: blocks i of
-// wavefront wr hold w1 (i = 0, 1) and w3 (i = 2, 3) rows of the same 64 features
-PMN_DEV int64_t swiglu_a_row(int t, int64_t nt, int64_t F)
-{
-    return ((t >> 6) & 1) * F + nt * 128 + (t >> 7) * 64 + ((t >> 5) & 1) * 32 + (t & 31);
-}
 
 // MFMA operands of one k-step for a wavefront's 128 x 128 quarter
 struct Mx8Frags {

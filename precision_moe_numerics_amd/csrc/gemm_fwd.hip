@@ -18,36 +18,32 @@
 // scales per 32 values, which cannot carry an E4M3 scale per 16, so the exact path is the fp16
 // one.
 //
-// Tiling. A workgroup of 8 wavefronts computes a 256 (weight rows n) x 256 (slots m) tile of
-// D = W X^T, i.e. Y^T, as 2 x 4 wavefront tiles of 128 x 64 (4 x 2 MFMA blocks), two wavefronts
-// per SIMD. K advances in stages of 64: each thread owns one weight row or one (gathered)
-// activation row, fetches its 32 code bytes and 4 scale bytes two stages ahead into registers,
-// and dequantizes them into 128 bytes of fp16 in LDS (rows padded to 144 bytes, so fragment
-// reads are bank-conflict free) between the MFMAs of the current stage; two LDS stages
-// alternate with one barrier per stage.
-// Groups (experts) are ragged: workgroup y walks the device offsets to find its (expert,
-// slot tile), so no host synchronization is needed.
+// Tiling. A workgroup of 4 wavefronts (one per SIMD) computes a 256 (weight rows n) x 256
+// (slots m) tile of D = W X^T, i.e. Y^T; each wavefront computes a 128 x 128 quarter (4 x 4 MFMA
+// blocks, accumulators in AGPRs). A stage is 128 k: 64 code bytes plus 8 E4M3 scale bytes per
+// row. Stages stream into a ring of 3 LDS slots with global_load_lds (global -> LDS without
+// registers), so the LDS holds FP4 codes rather than fp16 values: a fragment read moves a quarter
+// of the bytes of an fp16 fragment. Each wavefront dequantizes its own fragments in registers,
+// half a fragment after each MFMA, one substep (16 k) ahead of the MFMAs that use it.
+//
+// Fragment k order. Within a stage, lane half h (lanes 32h .. 32h+31) takes the 64 values
+// 64h .. 64h+63 of its row: substep s (0..7) feeds the MFMA the values 64h + 8s .. 64h + 8s + 7,
+// i.e. dword s of the lane's 32 code bytes, scaled by its block scale s / 2. Both operands use
+// the same order, so every MFMA multiplies matching k; only the fp32 summation order differs
+// from a k-sequential one.
+//
+// Code layout in a stage slot: row r at 64 r, its 16-byte chunk c at position c ^ ((r / 4) % 4),
+// so the 16 rows a quarter-wavefront reads cover all 16 bank groups. Each copy lane fetches the
+// chunk its destination position needs, so plain row-major codes arrive permuted.
+//
+// Groups (experts) are ragged: a workgroup finds its (expert, slot tile) from the device offsets
+// with one wavefront-parallel search, so no host synchronization is needed.
+#include <type_traits>
+
 #include "pmn_dev.hpp"
 #include "pmn_kernels.hpp"
 
 namespace pmn {
-
-namespace fwd {
-constexpr int BT = 256;                       // rows per operand tile
-constexpr int BK = 64;                        // K per stage
-constexpr int ROWB = 144;                     // LDS bytes per row: 64 fp16 + 16 pad
-constexpr int TILEB = BT * ROWB;              // one operand tile
-constexpr int STAGEB = 2 * TILEB;             // weights + activations
-constexpr int LDSB = 2 * STAGEB;              // two stages
-constexpr int THREADS = 512;                  // 8 wavefronts: 2 along weight rows x 4 along slots
-static_assert(THREADS == 2 * BT, "one staging thread per row of each operand tile");
-// Epilogue: the LDS holds output tiles of 256 slots x 256 bytes (row pitch 272, so the
-// transposed fragment writes of 32 slots fall on 16 distinct bank groups), written out as whole
-// row segments.
-constexpr int OPITCH = 272;
-constexpr int OTILE = BT * OPITCH;
-static_assert(2 * OTILE + BT * 8 <= LDSB, "two output tiles and the E8M0 tile fit in the LDS");
-}  // namespace fwd
 
 struct FwdArgs {
     const uint8_t* a_codes;   // activations NVFP4 [a_rows x K]
@@ -70,297 +66,324 @@ struct FwdArgs {
     int SM, SN;               // super-tile shape
 };
 
-// Dequantize block blk (16 FP4 values, two code words, one E4M3 scale byte) of one row's stage
-// to 16 fp16 values written as 2 x 16 bytes to LDS.
-struct RawStage {
-    uint4 c0, c1;   // 32 code bytes = 64 FP4 values
-    uint32_t s;     // 4 E4M3 block scales
-};
-
-template <int BLK>
-PMN_DEV void dequant_block_to_lds(const RawStage& r, uint8_t* dst)
-{
-    const uint32_t w0 = BLK == 0 ? r.c0.x : BLK == 1 ? r.c0.z : BLK == 2 ? r.c1.x : r.c1.z;
-    const uint32_t w1 = BLK == 0 ? r.c0.y : BLK == 1 ? r.c0.w : BLK == 2 ? r.c1.y : r.c1.w;
-    // E4M3 (OCP, bias 7) byte -> fp32 by the hardware converter (exact, subnormals included)
-    const _Float16 s = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)r.s, BLK);
-    const f16x2 ss = {s, s};
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const uint32_t word = h ? w1 : w0;
-        f16x2 p0 = PMN_FP4_TO_F16(word, 0) * ss;
-        f16x2 p1 = PMN_FP4_TO_F16(word, 1) * ss;
-        f16x2 p2 = PMN_FP4_TO_F16(word, 2) * ss;
-        f16x2 p3 = PMN_FP4_TO_F16(word, 3) * ss;
-        uint4 v;
-        __builtin_memcpy(&v.x, &p0, 4);
-        __builtin_memcpy(&v.y, &p1, 4);
-        __builtin_memcpy(&v.z, &p2, 4);
-        __builtin_memcpy(&v.w, &p3, 4);
-        *reinterpret_cast<uint4*>(dst + 16 * (2 * BLK + h)) = v;
-    }
-}
+namespace fwd {
+constexpr int BT = 256;
+constexpr int KS = 128;                       // k per stage
+constexpr int NSTAGE = 3;
+constexpr int CODEB = BT * 64;                // one operand's codes per stage
+constexpr int SCB = BT * 8;                   // one operand's E4M3 scales per stage
+constexpr int STAGEB = 2 * CODEB + 2 * SCB;
+constexpr int LDSB = NSTAGE * STAGEB;
+constexpr int THREADS = 256;
+constexpr int LPS = 12;                       // copies per wavefront per stage: 8 code pieces, 4 scale lines
+constexpr int OPITCH = 272;
+static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tile and E8M0 tile fit in the ring");
+}  // namespace fwd
 
 template <int EPI>
 __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
 {
     using namespace fwd;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[LDSB];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
+    asm volatile("; agpr in use %0" ::"a"(0));   // keep the accumulators in AGPRs
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wn = wave >> 2, wm = wave & 3;    // 2 wavefronts along weight rows, 4 along slots
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wave >> 1, wc = wave & 1;     // 2 wavefronts along weight rows, 2 along slots
 
-    // ---- which (expert, slot tile, weight tile): XCD-aware order over slot tiles x weight tiles
     TileXY tile;
     if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
     const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, BT);
     if (u.g < 0) return;
     const int g = u.g;
     const int64_t m0 = u.s0 + u.index * BT;
-    const int64_t mvalid = u.s1 - m0 < BT ? u.s1 - m0 : BT;
+    const int mvalid = (int)(u.s1 - m0 < BT ? u.s1 - m0 : BT);
     const int64_t N = p.N, K = p.K;
-    const int64_t n0 = tile.col * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
+    const int64_t nt = tile.col;
+    const int64_t n0 = nt * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
+    const int64_t cbytes = K >> 1, sbytes = K >> 4;
+    const int KT = (int)((K + KS - 1) / KS);
+    const bool half_tail = (K % KS) != 0;        // last stage holds 64 k (K = 64 mod 128)
 
-    // ---- staging: threads 0..255 stage weight row t, threads 256..511 activation row t - 256
-    const bool stage_w = tid < BT;                  // wavefront-uniform
-    const int srow = tid & (BT - 1);
-    const uint8_t* sc_codes;
-    const uint8_t* sc_scales;
-    bool svalid = true;
-    if (stage_w) {
-        int64_t wrow;
-        if (EPI == PMN_EPI_SWIGLU) {
-            const int F = (int)(N >> 1);
-            const int twn = srow >> 7, trb = (srow & 127) >> 5, tr = srow & 31;
-            wrow = (int64_t)g * N + (trb < 2 ? 0 : F) + n0 + twn * 64 + (trb & 1) * 32 + tr;
-        } else {
-            wrow = (int64_t)g * N + n0 + srow;
-        }
-        sc_codes = p.b_codes + wrow * (K >> 1);
-        sc_scales = p.b_scales + wrow * (K >> 4);
-    } else {
-        svalid = srow < mvalid;
-        const int64_t xrow = svalid ? (p.gather ? (int64_t)p.gather[m0 + srow] : m0 + srow) : 0;
-        sc_codes = p.a_codes + xrow * (K >> 1);
-        sc_scales = p.a_scales + xrow * (K >> 4);
-    }
-    uint8_t* const lds_row = lds + (stage_w ? 0 : TILEB) + srow * ROWB;
-
-    // Raw stages are fetched into registers two iterations ahead of their dequantization: three
-    // register sets rotate over an unrolled-by-3 loop. Fetches past the last stage re-read it, so
-    // every iteration issues the same loads and the compiler's load counting stays exact.
-    // A slot row past the tile's end reads activation row 0 instead: its products land only in
-    // output columns that are never stored, so the loaded values need no masking (masking them
-    // here would make every fetch wait for its data at once).
-    auto load_raw = [&](int kt, RawStage& r) {
-        const uint4* pc = reinterpret_cast<const uint4*>(sc_codes + (int64_t)kt * (BK / 2));
-        r.c0 = pc[0];
-        r.c1 = pc[1];
-        r.s = *reinterpret_cast<const uint32_t*>(sc_scales + (int64_t)kt * (BK / 16));
+    // ---- copy schedule: wavefronts 0-1 copy weight rows, 2-3 slot rows, 128 rows each.
+    // Code piece i = rows 16 i .. 16 i + 15 of the wavefront's 128 (lane l: row l / 4, position
+    // l % 4); scale line i = rows 32 i .. 32 i + 31 (lane l: row l / 2, dword l % 2).
+    // A slot row past the tile's valid slots reads the tile's first slot: its products land only
+    // in output columns that are never stored.
+    const int op = wave >> 1, half = wave & 1;
+    auto row_of = [&](int t) -> int64_t {
+        if (op == 0) return (int64_t)g * N + (EPI == PMN_EPI_SWIGLU ? swiglu_a_row(t, nt, N >> 1) : n0 + t);
+        const int64_t m = m0 + (t < mvalid ? t : 0);
+        return p.gather ? (int64_t)p.gather[m] : m;
+    };
+    const uint8_t* codes = op ? p.a_codes : p.b_codes;
+    const uint8_t* scales = op ? p.a_scales : p.b_scales;
+    const int csrc = (lane & 3) ^ ((lane >> 4) & 3);   // source chunk for this lane's position
+    // in a half-tail stage only chunks 0-1 and scale dword 0 of a row exist: the other lanes
+    // re-read those (their values are scaled by zero below)
+    const int64_t cadj = csrc >= 2 ? -32 : 0, sadj = (lane & 1) ? -4 : 0;
+    const uint8_t* cp[8];
+    const uint8_t* sp[4];
+#pragma unroll
+    for (int i = 0; i < 8; i++) cp[i] = codes + row_of(half * 128 + 16 * i + (lane >> 2)) * cbytes + csrc * 16;
+#pragma unroll
+    for (int i = 0; i < 4; i++) sp[i] = scales + row_of(half * 128 + 32 * i + (lane >> 1)) * sbytes + (lane & 1) * 4;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
+    const uint32_t cdst = lds0 + op * CODEB + half * 8192;
+    const uint32_t sdst = lds0 + 2 * CODEB + op * SCB + half * 1024;
+    // stage v of the copy stream: stages past the last re-load it (into a free slot or over
+    // identical bytes), so every stage issues the same copies
+    auto stage_src = [&](int v, int64_t& co, int64_t& so) {
+        const int kt = v < KT ? v : KT - 1;
+        const bool tail = half_tail && kt == KT - 1;
+        co = (int64_t)kt * 64 + (tail ? cadj : 0);
+        so = (int64_t)kt * 8 + (tail ? sadj : 0);
+    };
+    auto issue_piece = [&](int v, int i) {
+        int64_t co, so;
+        stage_src(v, co, so);
+        dma16(cp[i] + co, cdst + (uint32_t)(v % NSTAGE) * STAGEB + i * 1024);
+    };
+    auto issue_line = [&](int v, int i) {
+        int64_t co, so;
+        stage_src(v, co, so);
+        dma4(sp[i] + so, sdst + (uint32_t)(v % NSTAGE) * STAGEB + i * 256);
     };
 
-    f32x16 acc[4][2];
+    // ---- fragments: 4 weight blocks (f = 0..3) and 4 slot blocks (f = 4..7) per wavefront
+    const int lrow = lane & 31, hh = lane >> 5;
+    const int swz = (lrow >> 2) & 3;
+    const int offA = ((2 * hh) ^ swz) << 4, offB = ((2 * hh + 1) ^ swz) << 4;
+    auto frag_row = [&](int f) { return f < 4 ? wr * 128 + f * 32 + lrow : wc * 128 + (f - 4) * 32 + lrow; };
+    auto frag_op = [&](int f) { return f < 4 ? 0 : 1; };
+    uint4 rawA[8], rawB[8];       // code bytes 0..15 (substeps 0-3) and 16..31 (4-7) of the lane's half
+    uint32_t scA[8], scB[8];      // the lane's 4 block scales, read with each half
+    auto read_half = [&](int v, int f, bool second) {
+        const uint8_t* base = lds + (v % NSTAGE) * STAGEB;
+        const int row = frag_row(f), o = frag_op(f);
+        const uint4 c = *reinterpret_cast<const uint4*>(base + o * CODEB + row * 64 + (second ? offB : offA));
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + 2 * CODEB + o * SCB + row * 8 + hh * 4);
+        if (second) { rawB[f] = c; scB[f] = sc; } else { rawA[f] = c; scA[f] = sc; }
+    };
+    // scales of the half-tail stage's upper lane half are forced to zero
+    auto smask = [&](int kt) -> uint32_t { return (half_tail && kt >= KT - 1 && hh) ? 0u : 0xFFFFFFFFu; };
+
+    f16x8 fa[2][4], fb[2][4];
+    // Dequantize half `part` (values 4 part .. 4 part + 3) of fragment f of substep s (of stage
+    // kt) into buffer b. The two block scales of a code half convert together (E4M3 -> fp16 is
+    // exact); substep s takes scale s / 2. TAIL: the stage may be the half-tail one.
+    auto convert = [&](int kt, int s, int f, int b, int part, auto tail) {
+        const uint4 c = s < 4 ? rawA[f] : rawB[f];
+        const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
+        uint32_t sc = s < 4 ? scA[f] : scB[f];
+        if (decltype(tail)::value) sc &= smask(kt);
+        const f16x2 sp = s < 4 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false)
+                               : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
+        const _Float16 sv = ((s >> 1) & 1) ? sp[1] : sp[0];
+        const f16x2 ss = {sv, sv};
+        const f16x2 p0 = (part ? PMN_FP4_TO_F16(w, 2) : PMN_FP4_TO_F16(w, 0)) * ss;
+        const f16x2 p1 = (part ? PMN_FP4_TO_F16(w, 3) : PMN_FP4_TO_F16(w, 1)) * ss;
+        f16x8& d = f < 4 ? fa[b][f] : fb[b][f - 4];
+        d[4 * part] = p0[0];
+        d[4 * part + 1] = p0[1];
+        d[4 * part + 2] = p1[0];
+        d[4 * part + 3] = p1[1];
+    };
+
+    f32x16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int j = 0; j < 4; j++)
 #pragma unroll
             for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
-    const int KT = (int)(K / BK);
-    const int lrow = lane & 31, lk = (lane >> 5) * 16;
-    // one iteration: MFMAs on LDS stage kt % 2 while stage kt + 1 (registers `nxt`) is
-    // dequantized into the other LDS stage, one 16-value block per k-substep, and stage kt + 3 is
-    // fetched into `fut` (whose stage kt was dequantized in the previous iteration)
-    // The last iteration dequantizes a repeated stage into the LDS stage nobody reads again, so
-    // the body has no conditional work and the compiler's wait counts stay exact.
-    auto step = [&](int kt, const RawStage& nxt, RawStage& fut) {
-        const int buf = kt & 1;
-        load_raw(kt + 3 < KT ? kt + 3 : KT - 1, fut);
-        uint8_t* const dst = lds_row + (buf ^ 1) * STAGEB;
-        const uint8_t* wb = lds + buf * STAGEB + (wn * 128 + lrow) * ROWB + lk;
-        const uint8_t* xb = lds + buf * STAGEB + TILEB + (wm * 64 + lrow) * ROWB + lk;
-        // fragments of k-substep ks + 1 are read while the MFMAs of ks run
-        f16x8 af[2][4], bf[2][2];
-        auto read_frags = [&](int ks, f16x8 (&a)[4], f16x8 (&b)[2]) {
+    // One stage kt: 8 substeps of 16 MFMAs. Each MFMA is followed by one piece of side work, in
+    // an order the compiler may not regroup:
+    //   every MFMA q of substep s: dequantize half q % 2 of fragment q / 2 of substep s + 1 (for
+    //     s = 7: of the next stage's substep 0), so the VALU work is spread evenly;
+    //   substep 0, MFMAs 8-15: read the second halves (code bytes 16..31) of this stage;
+    //   substep 4, MFMA 8: wait until the next stage has landed and barrier (every wavefront is
+    //     then done reading this stage's slot), then MFMAs 8-15 copy the code pieces of stage
+    //     kt + 3 into this slot; substep 5, MFMAs 8-11: its scale lines;
+    //   substep 5, MFMAs 12-15 and substep 6, MFMAs 8-11: read the first halves of stage kt + 1.
+    auto stage = [&](int kt, auto tail) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) a[i] = *reinterpret_cast<const f16x8*>(wb + i * 32 * ROWB + ks * 32);
+        for (int s = 0; s < 8; s++) {
+            const int b = s & 1;
 #pragma unroll
-            for (int j = 0; j < 2; j++) b[j] = *reinterpret_cast<const f16x8*>(xb + j * 32 * ROWB + ks * 32);
-        };
-        read_frags(0, af[0], bf[0]);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ks++) {
-            if (ks + 1 < BK / 16) read_frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 2; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][i], bf[ks & 1][j], acc[i][j], 0, 0, 0);
-            if (ks == 0) dequant_block_to_lds<0>(nxt, dst);
-            if (ks == 1) dequant_block_to_lds<1>(nxt, dst);
-            if (ks == 2) dequant_block_to_lds<2>(nxt, dst);
-            if (ks == 3) dequant_block_to_lds<3>(nxt, dst);
+            for (int q = 0; q < 16; q++) {
+                const int i = q >> 2, j = q & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
+                if (s < 7) convert(kt, s + 1, q >> 1, b ^ 1, q & 1, tail);
+                else convert(kt + 1, 0, q >> 1, b ^ 1, q & 1, tail);
+                if (s == 0 && q >= 8) read_half(kt, q - 8, true);
+                if (s == 4 && q == 8) wait_loads_and_barrier<LPS>();
+                if (s == 4 && q >= 8) issue_piece(kt + NSTAGE, q - 8);
+                if (s == 5 && q >= 8 && q < 12) issue_line(kt + NSTAGE, q - 8);
+                if (s == 5 && q >= 12) read_half(kt + 1, q - 12, false);
+                if (s == 6 && q >= 8 && q < 12) read_half(kt + 1, q - 4, false);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
-        __syncthreads();
     };
+    typedef std::integral_constant<bool, false> Full;
+    typedef std::integral_constant<bool, true> Tail;
 
-    RawStage r0, r1, r2;
-    load_raw(0, r0);
-    load_raw(KT > 1 ? 1 : 0, r1);
-    load_raw(KT > 2 ? 2 : KT - 1, r2);
-    dequant_block_to_lds<0>(r0, lds_row);
-    dequant_block_to_lds<1>(r0, lds_row);
-    dequant_block_to_lds<2>(r0, lds_row);
-    dequant_block_to_lds<3>(r0, lds_row);
-    __syncthreads();
+    // prologue: stages 0..2 in flight, stage 0's halves read and its substep 0 dequantized
+#pragma unroll
+    for (int v = 0; v < NSTAGE; v++) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) issue_piece(v, i);
+#pragma unroll
+        for (int i = 0; i < 4; i++) issue_line(v, i);
+    }
+    wait_loads_and_barrier<(NSTAGE - 1) * LPS>();
+#pragma unroll
+    for (int f = 0; f < 8; f++) read_half(0, f, false);
+#pragma unroll
+    for (int f = 0; f < 8; f++) {
+        convert(0, 0, f, 0, 0, Tail());
+        convert(0, 0, f, 0, 1, Tail());
+    }
+    // the last two stages dequantize values of the last stage, which may be the half-tail one
     int kt = 0;
-    for (; kt + 2 < KT; kt += 3) {
-        step(kt, r1, r0);
-        step(kt + 1, r2, r1);
-        step(kt + 2, r0, r2);
-    }
-    if (kt < KT) step(kt, r1, r0);
-    if (kt + 1 < KT) step(kt + 1, r2, r1);
+    for (; kt + 2 < KT; kt++) stage(kt, Full());
+    for (; kt < KT; kt++) stage(kt, Tail());
+    // no copy may still be in flight when the LDS is reused or released
+    wait_loads_and_barrier<0>();
 
-    // ---- epilogue: lane holds slot m = (wm*64 + j*32 + lane%32), weight rows of block i
-    const int hh = lane >> 5;
-    // copy rows [0, mvalid) of an output tile (256 bytes per slot) to dst + (m0 + row) * pitch
-    auto store_tile = [&](const uint8_t* src, uint8_t* dst, int64_t pitch) {
+    // ---- epilogue. Block (i, j) of this wavefront holds, in lane l, slot m0 + wc*128 + j*32 + l%32
+    // and the 16 feature rows wr*128 + i*32 + (v/4)*8 + (l/32)*4 + v%4 of the tile.
+    float sx[4];
 #pragma unroll
-        for (int k = 0; k < (BT * 16) / THREADS; k++) {
-            const int q = k * THREADS + tid;
-            const int row = q >> 4, c = q & 15;
-            if (row < mvalid)
-                *reinterpret_cast<uint4*>(dst + (m0 + row) * pitch + c * 16) =
-                    *reinterpret_cast<const uint4*>(src + row * OPITCH + c * 16);
-        }
-    };
-    if (EPI == PMN_EPI_SWIGLU || EPI == PMN_EPI_RHT32_S2F6) {
-        __syncthreads();   // every fragment read of the main loop is done: the LDS holds output tiles
-        uint8_t* const t0 = lds;
-        uint8_t* const t1 = lds + OTILE;
-        uint8_t* const te = lds + 2 * OTILE;
-        float sxs[2];
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const int64_t ml = wm * 64 + j * 32 + (lane & 31);
-            const bool mok = ml < mvalid;
-            const int64_t m = m0 + ml;
-            const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
-            sxs[j] = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
-        }
-        if (EPI == PMN_EPI_SWIGLU) {
-            // tile 0: A = silu(h1) h3 (128 features), tile 1: h1; then tile 0 again: h3
-            const int64_t F = N >> 1;
-            const bool aux = p.out_aux != nullptr;
-#pragma unroll
-            for (int phase = 0; phase < 2; phase++) {
-                if (phase == 1 && !aux) break;
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const int ml = wm * 64 + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int i = 0; i < 2; i++) {
-                        const int64_t jbase = n0 + wn * 64 + i * 32;       // A column of row 0 of block
-                        const float s1 = sxs[j] * p.b_outer[((int64_t)g * N + jbase) / p.b_rpo];
-                        const float s3 = sxs[j] * p.b_outer[((int64_t)g * N + F + jbase) / p.b_rpo];
-#pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            uint32_t ab[4], b1[4], b3[4];
-#pragma unroll
-                            for (int u = 0; u < 4; u++) {
-                                const float h1 = acc[i][j][4 * q + u] * s1;
-                                const float h3 = acc[i + 2][j][4 * q + u] * s3;
-                                ab[u] = f32_to_bf16_bits(silu(h1) * h3);
-                                b1[u] = f32_to_bf16_bits(h1);
-                                b3[u] = f32_to_bf16_bits(h3);
-                            }
-                            const int off = ml * OPITCH + 2 * (wn * 64 + i * 32 + q * 8 + hh * 4);
-                            if (phase == 0) {
-                                *reinterpret_cast<uint2*>(t0 + off) = make_uint2(ab[0] | (ab[1] << 16), ab[2] | (ab[3] << 16));
-                                if (aux) *reinterpret_cast<uint2*>(t1 + off) = make_uint2(b1[0] | (b1[1] << 16), b1[2] | (b1[3] << 16));
-                            } else {
-                                *reinterpret_cast<uint2*>(t0 + off) = make_uint2(b3[0] | (b3[1] << 16), b3[2] | (b3[3] << 16));
-                            }
-                        }
-                    }
-                }
-                __syncthreads();
-                uint8_t* const H = reinterpret_cast<uint8_t*>(p.out_aux);
-                if (phase == 0) {
-                    store_tile(t0, reinterpret_cast<uint8_t*>(p.out) + n0 * 2, F * 2);
-                    if (aux) store_tile(t1, H + n0 * 2, N * 2);
-                } else {
-                    store_tile(t0, H + (F + n0) * 2, N * 2);
-                }
-                if (phase == 0 && aux) __syncthreads();   // tile 0 is rewritten with h3
-            }
-        } else {
-            // RHT32 + S2F6: codes into tile 0 (256 columns of int8), E8M0 into the E8M0 tile
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                const int ml = wm * 64 + j * 32 + (lane & 31);
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int nl = wn * 128 + i * 32;                  // tile column of row 0 of block
-                    const float s = sxs[j] * p.b_outer[((int64_t)g * N + n0 + nl) / p.b_rpo];
-                    f32x16 z;
-#pragma unroll
-                    for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * s;
-                    rht_block_store(z, p.rht_mask, lane, reinterpret_cast<int8_t*>(t0 + ml * OPITCH + nl),
-                                    te + ml * 8 + (nl >> 5));
-                }
-            }
-            __syncthreads();
-            store_tile(t0, reinterpret_cast<uint8_t*>(p.out) + n0, N);
-            if (tid < mvalid)
-                *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + tid) * (N >> 5) + (n0 >> 5)) =
-                    *reinterpret_cast<const uint2*>(te + tid * 8);
-        }
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int64_t ml = wm * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < 4; j++) {
+        const int ml = wc * 128 + j * 32 + lrow;
         const bool mok = ml < mvalid;
         const int64_t m = m0 + ml;
         const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
-        const float sx = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
+        sx[j] = mok ? p.a_outer[xr / p.a_rpo] : 0.0f;
+    }
+    if (EPI == PMN_EPI_F32 || EPI == PMN_EPI_BF16) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int64_t nb = n0 + wn * 128 + i * 32;           // first weight row of block
-            const float s = sx * p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
-            if (mok) {
+            const int64_t nb = n0 + wr * 128 + i * 32;            // first weight row of block i
+            const float sw = p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
 #pragma unroll
-                for (int q = 0; q < 4; q++) {
-                    const int64_t col = nb + q * 8 + hh * 4;
-                    float y0 = acc[i][j][4 * q] * s, y1 = acc[i][j][4 * q + 1] * s;
-                    float y2 = acc[i][j][4 * q + 2] * s, y3 = acc[i][j][4 * q + 3] * s;
-                    if (EPI == PMN_EPI_F32) {
-                        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
-                    } else {
-                        uint2 v = make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
-                                             f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
-                        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.out) + m * N + col) = v;
+            for (int j = 0; j < 4; j++) {
+                const int ml = wc * 128 + j * 32 + lrow;
+                if (ml < mvalid) {
+                    const float s = sx[j] * sw;
+                    const int64_t m = m0 + ml;
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const int64_t col = nb + q * 8 + hh * 4;
+                        const float y0 = acc[i][j][4 * q] * s, y1 = acc[i][j][4 * q + 1] * s;
+                        const float y2 = acc[i][j][4 * q + 2] * s, y3 = acc[i][j][4 * q + 3] * s;
+                        if (EPI == PMN_EPI_F32) {
+                            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
+                        } else {
+                            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * N + col) =
+                                make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
+                                           f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
+                        }
                     }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
+        return;
+    }
+    // SwiGLU and RHT32 + S2F6 stage a 256-slot output tile of 256 bytes per slot in the LDS and
+    // write whole 16-byte pieces of each slot's row
+    uint8_t* const t0 = lds;
+    uint8_t* const te = lds + BT * OPITCH;       // E8M0 tile: 8 bytes per slot
+    auto store_tile = [&](uint8_t* dst, int64_t pitch) {
+#pragma unroll
+        for (int k = 0; k < (BT * 16) / THREADS; k++) {
+            const int qq = k * THREADS + tid;
+            const int row = qq >> 4, c = qq & 15;
+            if (row < mvalid)
+                *reinterpret_cast<uint4*>(dst + (m0 + row) * pitch + c * 16) =
+                    *reinterpret_cast<const uint4*>(t0 + row * OPITCH + c * 16);
+        }
+    };
+    if (EPI == PMN_EPI_SWIGLU) {
+        // blocks i = 0, 1 hold h1 and i + 2 the matching h3 of features n0 + wr*64 + i*32 + ..
+        const int64_t F = N >> 1;
+        uint8_t* const A = static_cast<uint8_t*>(p.out);
+        uint8_t* const Hs = static_cast<uint8_t*>(p.out_aux);
+        float s1[2], s3[2];
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int64_t f0 = n0 + wr * 64 + i * 32;
+            s1[i] = p.b_outer[((int64_t)g * N + f0) / p.b_rpo];
+            s3[i] = p.b_outer[((int64_t)g * N + F + f0) / p.b_rpo];
+        }
+#pragma unroll
+        for (int phase = 0; phase < 3; phase++) {
+            if (phase > 0 && !Hs) break;
+            if (phase > 0) __syncthreads();     // the previous phase's tile has been stored
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int sl = wc * 128 + j * 32 + lrow;
+#pragma unroll
+                for (int i = 0; i < 2; i++) {
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        uint32_t bb[4];
+#pragma unroll
+                        for (int v = 0; v < 4; v++) {
+                            const float h1 = acc[i][j][4 * q + v] * (sx[j] * s1[i]);
+                            const float h3 = acc[i + 2][j][4 * q + v] * (sx[j] * s3[i]);
+                            bb[v] = f32_to_bf16_bits(phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3));
+                        }
+                        const int off = sl * OPITCH + 2 * (wr * 64 + i * 32 + q * 8 + hh * 4);
+                        *reinterpret_cast<uint2*>(t0 + off) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __syncthreads();
+            if (phase == 0) store_tile(A + n0 * 2, F * 2);
+            else if (phase == 1) store_tile(Hs + n0 * 2, N * 2);
+            else store_tile(Hs + (F + n0) * 2, N * 2);
+        }
+    } else {
+        // RHT32 + S2F6: each block's 32 feature rows are one aligned chunk of the slot's row
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int nl = wr * 128 + i * 32;
+            const float sw = p.b_outer[((int64_t)g * N + n0 + nl) / p.b_rpo];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const int sl = wc * 128 + j * 32 + lrow;
+                f32x16 z;
+#pragma unroll
+                for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * (sx[j] * sw);
+                rht_block_store(z, p.rht_mask, lane, reinterpret_cast<int8_t*>(t0 + sl * OPITCH + nl),
+                                te + sl * 8 + (nl >> 5));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+        store_tile(static_cast<uint8_t*>(p.out) + n0, N);
+        if (tid < mvalid)
+            *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + tid) * (N >> 5) + (n0 >> 5)) =
+                *reinterpret_cast<const uint2*>(te + tid * 8);
     }
 }
 
 hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
-                           int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
-                           const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
-                           const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
-                           int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
-                           void* out_aux, hipStream_t stream)
+                                int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
+                                const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
+                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
+                                int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
+                                void* out_aux, hipStream_t stream)
 {
     if (M == 0 || G == 0) return hipSuccess;
-    const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;   // bound on sum of ceil(m_g / 256)
-    const int64_t ntiles = N / fwd::BT;   // SWIGLU: each tile covers 128 w1 and 128 w3 rows
+    const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;
+    const int64_t ntiles = N / fwd::BT;
     int SM, SN;
     xcd_shape(mtiles, ntiles, SM, SN);
     FwdArgs p{a_codes, a_scales, a_outer, a_rpo, gather, b_codes, b_scales, b_outer, b_rpo,

@@ -279,7 +279,14 @@ PMN_DEV GroupUnit locate_group_unit(const int64_t* offsets, int G, int64_t t, in
 
 // ---- GEMM epilogues shared by the forward GEMMs -------------------------------------------
 
-PMN_DEV float silu(float h) { return h / (1.0f + expf(-h)); }
+// silu(h) = h * sigmoid(h) with the hardware exp2 and reciprocal (each within about 1 ulp in
+// fp32); the product silu(h1) * h3 is rounded to bf16 afterwards, which dwarfs that error. For
+// h -> -inf the reciprocal of +inf is 0 and the result is -0.
+PMN_DEV float silu(float h)
+{
+    const float e = __builtin_amdgcn_exp2f(-h * 1.44269504088896341f);
+    return h * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 // RHT32 + S2F6 on one 32 x 32 accumulator block whose 32 rows (n) are one aligned chunk:
 // lane l holds column m = l % 32 and rows i = (v/4)*8 + (l/32)*4 + v%4. The 32 codes of slot m
@@ -307,11 +314,20 @@ PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_
             }
         }
     }
-    // h = 4: across lane halves
+    // h = 4: across lane halves (lane l pairs with l ^ 32; the lower lane holds the first element
+    // of each pair). v_permlane32_swap exchanges the upper lane half of its first register with
+    // the lower lane half of its second. For registers (p, q) one swap gives A = [p_lo, q_lo] and
+    // B = [p_hi, q_hi], so every lane holds both elements of one pair; A + B and A - B hold p's
+    // results in their lower lanes and q's in their upper lanes, and a second swap of (A + B,
+    // A - B) puts p's and q's results back in place.
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-        float p = __shfl_xor(t[v], 32, 64);
-        t[v] = hh == 0 ? t[v] + p : p - t[v];
+    for (int v = 0; v < 16; v += 2) {
+        const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(t[v]), __float_as_uint(t[v + 1]), false, false);
+        const float A = __uint_as_float(s1[0]), B = __uint_as_float(s1[1]);
+        const float X = A + B, Y = A - B;
+        const auto s2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(X), __float_as_uint(Y), false, false);
+        t[v] = __uint_as_float(s2[0]);
+        t[v + 1] = __uint_as_float(s2[1]);
     }
     // h = 8 (v ^ 4), h = 16 (v ^ 8)
 #pragma unroll
@@ -328,7 +344,12 @@ PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_
     float amax = 0.0f;
 #pragma unroll
     for (int v = 0; v < 16; v++) amax = fmaxf(amax, fabsf(t[v]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    {
+        // max with the partner lane: the swap of (amax, amax) gives both lane halves' values to
+        // every lane
+        const auto m = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax), __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1]));
+    }
     const int e = e8m0_exponent<E8M0_S2F6>(amax);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -341,6 +362,35 @@ PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_
         *reinterpret_cast<uint32_t*>(out_row_chunk + q * 8 + hh * 4) = w;
     }
     if (hh == 0) *e8m0_ptr = (uint8_t)(e + 127);
+}
+
+// ---- shared by the ring-buffered GEMMs -----------------------------------------------------
+// Asynchronous global -> LDS copies. The LDS destination of lane l is m0 + 16 l (dwordx4) or
+// m0 + 4 l (dword), m0 being wavefront-uniform. They are issued from inline assembly so that the
+// compiler does not make every later LDS read wait for all of them; the kernel waits itself.
+PMN_DEV void dma16(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+PMN_DEV void dma4(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+// Wait for this wavefront's LDS reads and until at most N of its loads are outstanding, then
+// barrier: afterwards the stage those loads waited for is visible to the workgroup and every
+// wavefront has finished reading the stages it read before.
+template <int N>
+PMN_DEV void wait_loads_and_barrier()
+{
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+// Forward GEMMs with the SwiGLU epilogue (256 x 256 tiles of 4 wavefronts, 2 along weight rows):
+// the expert-local weight row (within its 2F rows) that tile row t of feature tile nt holds.
+// Blocks i of wavefront wr = t / 128 hold w1 (i = 0, 1) and w3 (i = 2, 3) rows of the same 64
+// features, so an accumulator lane holds h1 and h3 of one feature in blocks i and i + 2
+PMN_DEV int64_t swiglu_a_row(int t, int64_t nt, int64_t F)
+{
+    return ((t >> 6) & 1) * F + nt * 128 + (t >> 7) * 64 + ((t >> 5) & 1) * 32 + (t & 31);
 }
 
 }  // namespace pmn
