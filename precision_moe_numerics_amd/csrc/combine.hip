@@ -31,14 +31,6 @@ constexpr int THREADS = 256;
 constexpr int KB = 8;  // slots loaded per batch
 }  // namespace cmb
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 values -> two bf16 (a in the low half), round to nearest even: v_cvt_pk_bf16_f32.
-PMN_DEV uint32_t bf16x2_bits(float a, float b)
-{
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // acc[j] += gs * c_j for 16 int8 codes held in one 16-byte word.
 PMN_DEV void accumulate_codes16(const uint4 w, float gs, float (&acc)[16])

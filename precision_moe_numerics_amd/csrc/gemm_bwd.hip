@@ -435,10 +435,8 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
                                     make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                                 acc[i][j][4 * q + 3]);
                             } else {
-                                const uint32_t lo = f32_to_bf16_bits(acc[i][j][4 * q]) |
-                                                    (f32_to_bf16_bits(acc[i][j][4 * q + 1]) << 16);
-                                const uint32_t hi = f32_to_bf16_bits(acc[i][j][4 * q + 2]) |
-                                                    (f32_to_bf16_bits(acc[i][j][4 * q + 3]) << 16);
+                                const uint32_t lo = bf16x2_bits(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+                                const uint32_t hi = bf16x2_bits(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
                                 *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.yout) + o) = make_uint2(lo, hi);
                             }
                         }
@@ -480,14 +478,14 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
                     for (int i = 0; i < 2; i++) {
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
-                            uint32_t b[4];
+                            float o[4];
 #pragma unroll
                             for (int u = 0; u < 4; u++) {
                                 const float h1 = acc[i][j][4 * q + u], h3 = acc[i + 2][j][4 * q + u];
-                                b[u] = f32_to_bf16_bits(phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3));
+                                o[u] = phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3);
                             }
                             const int off = sl * OPITCH + 2 * (wr * 64 + i * 32 + q * 8 + hh * 4);
-                            *reinterpret_cast<uint2*>(t0 + off) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+                            *reinterpret_cast<uint2*>(t0 + off) = make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
                         }
                         // one block pair at a time: the accumulators stay in AGPRs until used
                         __builtin_amdgcn_sched_barrier(0);

@@ -284,8 +284,7 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
                             *reinterpret_cast<float4*>(static_cast<float*>(p.out) + m * N + col) = make_float4(y0, y1, y2, y3);
                         } else {
                             *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + m * N + col) =
-                                make_uint2(f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16),
-                                           f32_to_bf16_bits(y2) | (f32_to_bf16_bits(y3) << 16));
+                                make_uint2(bf16x2_bits(y0, y1), bf16x2_bits(y2, y3));
                         }
                     }
                 }
@@ -331,15 +330,15 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
                 for (int i = 0; i < 2; i++) {
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
-                        uint32_t bb[4];
+                        float o[4];
 #pragma unroll
                         for (int v = 0; v < 4; v++) {
                             const float h1 = acc[i][j][4 * q + v] * (sx[j] * s1[i]);
                             const float h3 = acc[i + 2][j][4 * q + v] * (sx[j] * s3[i]);
-                            bb[v] = f32_to_bf16_bits(phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3));
+                            o[v] = phase == 0 ? silu(h1) * h3 : (phase == 1 ? h1 : h3);
                         }
                         const int off = sl * OPITCH + 2 * (wr * 64 + i * 32 + q * 8 + hh * 4);
-                        *reinterpret_cast<uint2*>(t0 + off) = make_uint2(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16));
+                        *reinterpret_cast<uint2*>(t0 + off) = make_uint2(bf16x2_bits(o[0], o[1]), bf16x2_bits(o[2], o[3]));
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }

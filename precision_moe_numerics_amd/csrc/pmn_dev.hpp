@@ -48,6 +48,15 @@ PMN_DEV uint32_t f32_to_bf16_bits(float f)
     return u >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 (a in the low half), round to nearest even: v_cvt_pk_bf16_f32.
+PMN_DEV uint32_t bf16x2_bits(float a, float b)
+{
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // ---- E4M3 ---------------------------------------------------------------------------------
 
 // Value of an E4M3 byte (finite codes).
@@ -351,15 +360,17 @@ PMN_DEV void rht_block_store(f32x16 z, uint32_t mask, int lane, int8_t* out_row_
         amax = fmaxf(__uint_as_float(m[0]), __uint_as_float(m[1]));
     }
     const int e = e8m0_exponent<E8M0_S2F6>(amax);
+    // code c = RNE(t * 2^(6 - e)), |c| <= 127: the scaling is exact, and adding 1.5 * 2^23 (where
+    // the float spacing is 1) rounds to the nearest even integer; the sum's low byte is c in two's
+    // complement. Four such bytes pack with three byte permutes.
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-        uint32_t w = 0u;
+        uint32_t c[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            int c = (int)__builtin_rintf(__builtin_ldexpf(t[4 * q + j], 6 - e));
-            w |= ((uint32_t)c & 0xFFu) << (8 * j);
-        }
-        *reinterpret_cast<uint32_t*>(out_row_chunk + q * 8 + hh * 4) = w;
+        for (int j = 0; j < 4; j++) c[j] = __float_as_uint(__builtin_ldexpf(t[4 * q + j], 6 - e) + 12582912.0f);
+        const uint32_t lo = __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u);   // bytes c0, c1, 0, 0
+        const uint32_t hi = __builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u);   // bytes c2, c3, 0, 0
+        *reinterpret_cast<uint32_t*>(out_row_chunk + q * 8 + hh * 4) = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
     }
     if (hh == 0) *e8m0_ptr = (uint8_t)(e + 127);
 }
