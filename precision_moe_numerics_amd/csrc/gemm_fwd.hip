@@ -37,7 +37,9 @@
 // chunk its destination position needs, so plain row-major codes arrive permuted.
 //
 // Groups (experts) are ragged: a workgroup finds its (expert, slot tile) from the device offsets
-// with one wavefront-parallel search, so no host synchronization is needed.
+// with one wavefront-parallel search, so no host synchronization is needed. An expert's last
+// unit of at most 128 slots runs as 512 weight rows x 128 slots (two weight tiles), so fewer
+// MFMAs fall on padded slots.
 #include <type_traits>
 
 #include "pmn_dev.hpp"
@@ -70,67 +72,74 @@ namespace fwd {
 constexpr int BT = 256;
 constexpr int KS = 128;                       // k per stage
 constexpr int NSTAGE = 3;
-constexpr int CODEB = BT * 64;                // one operand's codes per stage
-constexpr int SCB = BT * 8;                   // one operand's E4M3 scales per stage
-constexpr int STAGEB = 2 * CODEB + 2 * SCB;
+constexpr int ROWS_MAX = 640;                 // weight + slot rows of a stage (the 512 x 128 shape)
+constexpr int STAGEB = ROWS_MAX * 72;         // 64 code bytes + 8 scale bytes per row
 constexpr int LDSB = NSTAGE * STAGEB;
 constexpr int THREADS = 256;
-constexpr int LPS = 12;                       // copies per wavefront per stage: 8 code pieces, 4 scale lines
 constexpr int OPITCH = 272;
-static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tile and E8M0 tile fit in the ring");
+static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tiles and E8M0 tiles fit in the ring");
 }  // namespace fwd
 
-template <int EPI>
-__global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
+// One workgroup tile. SHAPE false: 256 weight rows x 256 slots, wavefront w computes weight rows
+// (w / 2) * 128 .. and slots (w % 2) * 128 ... SHAPE true (the last unit of an expert's slots
+// when it holds at most 128 of them): 512 weight rows (weight tiles nt0 and nt0 + 1) x 128 slots,
+// wavefront w computes weight rows w * 128 .. and all 128 slots. Each wavefront's work (a
+// 128 x 128 quarter) and inner loop are the same in both.
+template <int EPI, bool SHAPE>
+PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, int mvalid, int64_t nt0)
 {
     using namespace fwd;
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[LDSB];
-    asm volatile("; agpr in use %0" ::"a"(0));   // keep the accumulators in AGPRs
+    constexpr int RW = SHAPE ? 512 : 256, RX = SHAPE ? 128 : 256;   // weight and slot rows
+    constexpr int XOFF = RW * 64, SOFF = (RW + RX) * 64, XSOFF = SOFF + RW * 8;   // stage layout
+    constexpr int NP = SHAPE ? 10 : 8, NL = SHAPE ? 5 : 4;   // code pieces and scale lines per wavefront
+    constexpr int LPS = NP + NL;                             // copies per wavefront per stage
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wr = wave >> 1, wc = wave & 1;     // 2 wavefronts along weight rows, 2 along slots
-
-    TileXY tile;
-    if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
-    const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, BT);
-    if (u.g < 0) return;
-    const int g = u.g;
-    const int64_t m0 = u.s0 + u.index * BT;
-    const int mvalid = (int)(u.s1 - m0 < BT ? u.s1 - m0 : BT);
     const int64_t N = p.N, K = p.K;
-    const int64_t nt = tile.col;
-    const int64_t n0 = nt * (EPI == PMN_EPI_SWIGLU ? BT / 2 : BT);
     const int64_t cbytes = K >> 1, sbytes = K >> 4;
     const int KT = (int)((K + KS - 1) / KS);
     const bool half_tail = (K % KS) != 0;        // last stage holds 64 k (K = 64 mod 128)
 
-    // ---- copy schedule: wavefronts 0-1 copy weight rows, 2-3 slot rows, 128 rows each.
-    // Code piece i = rows 16 i .. 16 i + 15 of the wavefront's 128 (lane l: row l / 4, position
-    // l % 4); scale line i = rows 32 i .. 32 i + 31 (lane l: row l / 2, dword l % 2).
+    // ---- copy schedule. Code piece = 16 rows (lane l: row l / 4, position l % 4), scale line =
+    // 32 rows (lane l: row l / 2, dword l % 2). SHAPE false: wavefronts 0-1 copy weight rows, 2-3
+    // slot rows, 128 rows each (8 pieces, 4 lines). SHAPE true: wavefront w copies weight rows
+    // 128 w .. (8 pieces, 4 lines) and slot rows 32 w .. (2 pieces, 1 line).
     // A slot row past the tile's valid slots reads the tile's first slot: its products land only
     // in output columns that are never stored.
-    const int op = wave >> 1, half = wave & 1;
-    auto row_of = [&](int t) -> int64_t {
-        if (op == 0) return (int64_t)g * N + (EPI == PMN_EPI_SWIGLU ? swiglu_a_row(t, nt, N >> 1) : n0 + t);
+    auto piece_op = [&](int i) { return SHAPE ? (i < 8 ? 0 : 1) : (wave >> 1); };
+    auto piece_row = [&](int i) { return SHAPE ? (i < 8 ? wave * 128 + 16 * i : wave * 32 + 16 * (i - 8)) : (wave & 1) * 128 + 16 * i; };
+    auto line_op = [&](int i) { return SHAPE ? (i < 4 ? 0 : 1) : (wave >> 1); };
+    auto line_row = [&](int i) { return SHAPE ? (i < 4 ? wave * 128 + 32 * i : wave * 32) : (wave & 1) * 128 + 32 * i; };
+    auto row_of = [&](int op, int t) -> int64_t {
+        if (op == 0) {
+            const int64_t nt = nt0 + (t >> 8);
+            const int tt = t & 255;
+            return (int64_t)g * N + (EPI == PMN_EPI_SWIGLU ? swiglu_a_row(tt, nt, N >> 1) : nt * BT + tt);
+        }
         const int64_t m = m0 + (t < mvalid ? t : 0);
         return p.gather ? (int64_t)p.gather[m] : m;
     };
-    const uint8_t* codes = op ? p.a_codes : p.b_codes;
-    const uint8_t* scales = op ? p.a_scales : p.b_scales;
     const int csrc = (lane & 3) ^ ((lane >> 4) & 3);   // source chunk for this lane's position
     // in a half-tail stage only chunks 0-1 and scale dword 0 of a row exist: the other lanes
     // re-read those (their values are scaled by zero below)
     const int64_t cadj = csrc >= 2 ? -32 : 0, sadj = (lane & 1) ? -4 : 0;
-    const uint8_t* cp[8];
-    const uint8_t* sp[4];
+    const uint8_t* cp[NP];
+    const uint8_t* sp[NL];
+    uint32_t cd[NP], sd[NL];                     // LDS offsets within a stage slot
 #pragma unroll
-    for (int i = 0; i < 8; i++) cp[i] = codes + row_of(half * 128 + 16 * i + (lane >> 2)) * cbytes + csrc * 16;
+    for (int i = 0; i < NP; i++) {
+        const int op = piece_op(i), r = piece_row(i);
+        cp[i] = (op ? p.a_codes : p.b_codes) + row_of(op, r + (lane >> 2)) * cbytes + csrc * 16;
+        cd[i] = (op ? XOFF : 0) + r * 64;
+    }
 #pragma unroll
-    for (int i = 0; i < 4; i++) sp[i] = scales + row_of(half * 128 + 32 * i + (lane >> 1)) * sbytes + (lane & 1) * 4;
+    for (int i = 0; i < NL; i++) {
+        const int op = line_op(i), r = line_row(i);
+        sp[i] = (op ? p.a_scales : p.b_scales) + row_of(op, r + (lane >> 1)) * sbytes + (lane & 1) * 4;
+        sd[i] = (op ? XSOFF : SOFF) + r * 8;
+    }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
-    const uint32_t cdst = lds0 + op * CODEB + half * 8192;
-    const uint32_t sdst = lds0 + 2 * CODEB + op * SCB + half * 1024;
     // stage v of the copy stream: stages past the last re-load it (into a free slot or over
     // identical bytes), so every stage issues the same copies
     auto stage_src = [&](int v, int64_t& co, int64_t& so) {
@@ -142,27 +151,27 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     auto issue_piece = [&](int v, int i) {
         int64_t co, so;
         stage_src(v, co, so);
-        dma16(cp[i] + co, cdst + (uint32_t)(v % NSTAGE) * STAGEB + i * 1024);
+        dma16(cp[i] + co, lds0 + (uint32_t)(v % NSTAGE) * STAGEB + cd[i]);
     };
     auto issue_line = [&](int v, int i) {
         int64_t co, so;
         stage_src(v, co, so);
-        dma4(sp[i] + so, sdst + (uint32_t)(v % NSTAGE) * STAGEB + i * 256);
+        dma4(sp[i] + so, lds0 + (uint32_t)(v % NSTAGE) * STAGEB + sd[i]);
     };
 
     // ---- fragments: 4 weight blocks (f = 0..3) and 4 slot blocks (f = 4..7) per wavefront
+    const int wrow0 = SHAPE ? wave * 128 : (wave >> 1) * 128;   // first weight row of the wavefront
+    const int xrow0 = SHAPE ? 0 : (wave & 1) * 128;             // first slot row
     const int lrow = lane & 31, hh = lane >> 5;
     const int swz = (lrow >> 2) & 3;
     const int offA = ((2 * hh) ^ swz) << 4, offB = ((2 * hh + 1) ^ swz) << 4;
-    auto frag_row = [&](int f) { return f < 4 ? wr * 128 + f * 32 + lrow : wc * 128 + (f - 4) * 32 + lrow; };
-    auto frag_op = [&](int f) { return f < 4 ? 0 : 1; };
     uint4 rawA[8], rawB[8];       // code bytes 0..15 (substeps 0-3) and 16..31 (4-7) of the lane's half
     uint32_t scA[8], scB[8];      // the lane's 4 block scales, read with each half
     auto read_half = [&](int v, int f, bool second) {
         const uint8_t* base = lds + (v % NSTAGE) * STAGEB;
-        const int row = frag_row(f), o = frag_op(f);
-        const uint4 c = *reinterpret_cast<const uint4*>(base + o * CODEB + row * 64 + (second ? offB : offA));
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + 2 * CODEB + o * SCB + row * 8 + hh * 4);
+        const int row = f < 4 ? wrow0 + f * 32 + lrow : xrow0 + (f - 4) * 32 + lrow;
+        const uint4 c = *reinterpret_cast<const uint4*>(base + (f < 4 ? 0 : XOFF) + row * 64 + (second ? offB : offA));
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + (f < 4 ? SOFF : XSOFF) + row * 8 + hh * 4);
         if (second) { rawB[f] = c; scB[f] = sc; } else { rawA[f] = c; scA[f] = sc; }
     };
     // scales of the half-tail stage's upper lane half are forced to zero
@@ -177,9 +186,9 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
         const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
         uint32_t sc = s < 4 ? scA[f] : scB[f];
         if (decltype(tail)::value) sc &= smask(kt);
-        const f16x2 sp = s < 4 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false)
-                               : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
-        const _Float16 sv = ((s >> 1) & 1) ? sp[1] : sp[0];
+        const f16x2 sp2 = s < 4 ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false)
+                                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
+        const _Float16 sv = ((s >> 1) & 1) ? sp2[1] : sp2[0];
         const f16x2 ss = {sv, sv};
         const f16x2 p0 = (part ? PMN_FP4_TO_F16(w, 2) : PMN_FP4_TO_F16(w, 0)) * ss;
         const f16x2 p1 = (part ? PMN_FP4_TO_F16(w, 3) : PMN_FP4_TO_F16(w, 1)) * ss;
@@ -204,8 +213,9 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     //     s = 7: of the next stage's substep 0), so the VALU work is spread evenly;
     //   substep 0, MFMAs 8-15: read the second halves (code bytes 16..31) of this stage;
     //   substep 4, MFMA 8: wait until the next stage has landed and barrier (every wavefront is
-    //     then done reading this stage's slot), then MFMAs 8-15 copy the code pieces of stage
-    //     kt + 3 into this slot; substep 5, MFMAs 8-11: its scale lines;
+    //     then done reading this stage's slot), then MFMAs 8-15 copy code pieces 0-7 of stage
+    //     kt + 3 into this slot; substep 5, MFMAs 8-11: scale lines 0-3; substep 6, MFMAs 12-14:
+    //     the 512 x 128 shape's further two pieces and one line;
     //   substep 5, MFMAs 12-15 and substep 6, MFMAs 8-11: read the first halves of stage kt + 1.
     auto stage = [&](int kt, auto tail) {
 #pragma unroll
@@ -221,6 +231,8 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
                 if (s == 4 && q == 8) wait_loads_and_barrier<LPS>();
                 if (s == 4 && q >= 8) issue_piece(kt + NSTAGE, q - 8);
                 if (s == 5 && q >= 8 && q < 12) issue_line(kt + NSTAGE, q - 8);
+                if (SHAPE && s == 6 && q >= 12 && q < 14) issue_piece(kt + NSTAGE, q - 4);
+                if (SHAPE && s == 6 && q == 14) issue_line(kt + NSTAGE, 4);
                 if (s == 5 && q >= 12) read_half(kt + 1, q - 12, false);
                 if (s == 6 && q >= 8 && q < 12) read_half(kt + 1, q - 4, false);
                 __builtin_amdgcn_sched_barrier(0);
@@ -234,9 +246,9 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
 #pragma unroll
     for (int v = 0; v < NSTAGE; v++) {
 #pragma unroll
-        for (int i = 0; i < 8; i++) issue_piece(v, i);
+        for (int i = 0; i < NP; i++) issue_piece(v, i);
 #pragma unroll
-        for (int i = 0; i < 4; i++) issue_line(v, i);
+        for (int i = 0; i < NL; i++) issue_line(v, i);
     }
     wait_loads_and_barrier<(NSTAGE - 1) * LPS>();
 #pragma unroll
@@ -253,12 +265,17 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     // no copy may still be in flight when the LDS is reused or released
     wait_loads_and_barrier<0>();
 
-    // ---- epilogue. Block (i, j) of this wavefront holds, in lane l, slot m0 + wc*128 + j*32 + l%32
-    // and the 16 feature rows wr*128 + i*32 + (v/4)*8 + (l/32)*4 + v%4 of the tile.
+    // ---- epilogue. Block (i, j) of this wavefront holds, in lane l, slot m0 + xrow0 + j*32 + l%32
+    // and the 16 rows wr*128 + i*32 + (v/4)*8 + (l/32)*4 + v%4 of weight tile nt (wr = the
+    // wavefront's 128-row half of that tile). The staged outputs (SwiGLU, RHT32 + S2F6) of weight
+    // tile nt0 + rg sit in staging rows rg * 128 + slot (SHAPE true) or slot (SHAPE false).
+    const int64_t nt = SHAPE ? nt0 + (wave >> 1) : nt0;
+    const int wr = SHAPE ? (wave & 1) : (wave >> 1);
+    const int srow0 = SHAPE ? (wave >> 1) * 128 : xrow0;        // staging row of slot xrow0
     float sx[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int ml = wc * 128 + j * 32 + lrow;
+        const int ml = xrow0 + j * 32 + lrow;
         const bool mok = ml < mvalid;
         const int64_t m = m0 + ml;
         const int64_t xr = mok ? (p.gather ? (int64_t)p.gather[m] : m) : 0;
@@ -267,11 +284,11 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     if (EPI == PMN_EPI_F32 || EPI == PMN_EPI_BF16) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int64_t nb = n0 + wr * 128 + i * 32;            // first weight row of block i
+            const int64_t nb = nt * BT + wr * 128 + i * 32;       // first weight row of block i
             const float sw = p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int ml = wc * 128 + j * 32 + lrow;
+                const int ml = xrow0 + j * 32 + lrow;
                 if (ml < mvalid) {
                     const float s = sx[j] * sw;
                     const int64_t m = m0 + ml;
@@ -293,29 +310,38 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
         }
         return;
     }
-    // SwiGLU and RHT32 + S2F6 stage a 256-slot output tile of 256 bytes per slot in the LDS and
-    // write whole 16-byte pieces of each slot's row
+    // SwiGLU and RHT32 + S2F6 stage 256 rows of 256 bytes (one per slot of a weight tile) in the
+    // LDS and write whole 16-byte pieces of each slot's row. Staging row r holds slot r of weight
+    // tile nt0 (SHAPE false) or slot r % 128 of weight tile nt0 + r / 128 (SHAPE true).
     uint8_t* const t0 = lds;
-    uint8_t* const te = lds + BT * OPITCH;       // E8M0 tile: 8 bytes per slot
-    auto store_tile = [&](uint8_t* dst, int64_t pitch) {
+    uint8_t* const te = lds + BT * OPITCH;       // E8M0 tile: 8 bytes per staging row
+    auto staged = [&](int r, int& slot, int64_t& ntr) {
+        slot = SHAPE ? (r & 127) : r;
+        ntr = SHAPE ? nt0 + (r >> 7) : nt0;
+    };
+    // dst(ntr) = the output row base of weight tile ntr for slot 0, rows pitch bytes apart
+    auto store_tile = [&](auto dst, int64_t pitch) {
 #pragma unroll
         for (int k = 0; k < (BT * 16) / THREADS; k++) {
             const int qq = k * THREADS + tid;
-            const int row = qq >> 4, c = qq & 15;
-            if (row < mvalid)
-                *reinterpret_cast<uint4*>(dst + (m0 + row) * pitch + c * 16) =
-                    *reinterpret_cast<const uint4*>(t0 + row * OPITCH + c * 16);
+            const int r = qq >> 4, c = qq & 15;
+            int slot;
+            int64_t ntr;
+            staged(r, slot, ntr);
+            if (slot < mvalid)
+                *reinterpret_cast<uint4*>(dst(ntr) + (m0 + slot) * pitch + c * 16) =
+                    *reinterpret_cast<const uint4*>(t0 + r * OPITCH + c * 16);
         }
     };
     if (EPI == PMN_EPI_SWIGLU) {
-        // blocks i = 0, 1 hold h1 and i + 2 the matching h3 of features n0 + wr*64 + i*32 + ..
+        // blocks i = 0, 1 hold h1 and i + 2 the matching h3 of features nt*128 + wr*64 + i*32 + ..
         const int64_t F = N >> 1;
         uint8_t* const A = static_cast<uint8_t*>(p.out);
         uint8_t* const Hs = static_cast<uint8_t*>(p.out_aux);
         float s1[2], s3[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
-            const int64_t f0 = n0 + wr * 64 + i * 32;
+            const int64_t f0 = nt * 128 + wr * 64 + i * 32;
             s1[i] = p.b_outer[((int64_t)g * N + f0) / p.b_rpo];
             s3[i] = p.b_outer[((int64_t)g * N + F + f0) / p.b_rpo];
         }
@@ -325,7 +351,7 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
             if (phase > 0) __syncthreads();     // the previous phase's tile has been stored
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int sl = wc * 128 + j * 32 + lrow;
+                const int sl = srow0 + j * 32 + lrow;
 #pragma unroll
                 for (int i = 0; i < 2; i++) {
 #pragma unroll
@@ -344,19 +370,19 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
                 }
             }
             __syncthreads();
-            if (phase == 0) store_tile(A + n0 * 2, F * 2);
-            else if (phase == 1) store_tile(Hs + n0 * 2, N * 2);
-            else store_tile(Hs + (F + n0) * 2, N * 2);
+            if (phase == 0) store_tile([&](int64_t ntr) { return A + ntr * 128 * 2; }, F * 2);
+            else if (phase == 1) store_tile([&](int64_t ntr) { return Hs + ntr * 128 * 2; }, N * 2);
+            else store_tile([&](int64_t ntr) { return Hs + (F + ntr * 128) * 2; }, N * 2);
         }
     } else {
-        // RHT32 + S2F6: each block's 32 feature rows are one aligned chunk of the slot's row
+        // RHT32 + S2F6: each block's 32 weight rows are one aligned chunk of the slot's row
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int nl = wr * 128 + i * 32;
-            const float sw = p.b_outer[((int64_t)g * N + n0 + nl) / p.b_rpo];
+            const float sw = p.b_outer[((int64_t)g * N + nt * BT + nl) / p.b_rpo];
 #pragma unroll
             for (int j = 0; j < 4; j++) {
-                const int sl = wc * 128 + j * 32 + lrow;
+                const int sl = srow0 + j * 32 + lrow;
                 f32x16 z;
 #pragma unroll
                 for (int v = 0; v < 16; v++) z[v] = acc[i][j][v] * (sx[j] * sw);
@@ -366,19 +392,45 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
             }
         }
         __syncthreads();
-        store_tile(static_cast<uint8_t*>(p.out) + n0, N);
-        if (tid < mvalid)
-            *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + tid) * (N >> 5) + (n0 >> 5)) =
-                *reinterpret_cast<const uint2*>(te + tid * 8);
+        store_tile([&](int64_t ntr) { return static_cast<uint8_t*>(p.out) + ntr * BT; }, N);
+        {
+            int slot;
+            int64_t ntr;
+            staged(tid, slot, ntr);
+            if (slot < mvalid)
+                *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + slot) * (N >> 5) + ((ntr * BT) >> 5)) =
+                    *reinterpret_cast<const uint2*>(te + tid * 8);
+        }
     }
 }
 
+template <int EPI>
+__global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[fwd::LDSB];
+    asm volatile("; agpr in use %0" ::"a"(0));   // keep the accumulators in AGPRs
+    TileXY tile;
+    if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
+    const GroupUnit u = locate_group_unit(p.offsets, p.G, tile.row, fwd::BT);
+    if (u.g < 0) return;
+    const int64_t m0 = u.s0 + u.index * fwd::BT;
+    const int mvalid = (int)(u.s1 - m0 < fwd::BT ? u.s1 - m0 : fwd::BT);
+    // a unit of at most 128 slots is computed as 512 weight rows x 128 slots by the workgroup of
+    // the even weight tile of each pair (the odd one has nothing to do); an unpaired last weight
+    // tile keeps the 256 x 256 shape
+    if (mvalid <= 128 && (tile.col & 1)) return;
+    if (mvalid <= 128 && tile.col + 1 < p.ntiles)
+        nvfp4_gemm_tile<EPI, true>(p, lds, u.g, m0, mvalid, tile.col);
+    else
+        nvfp4_gemm_tile<EPI, false>(p, lds, u.g, m0, mvalid, tile.col);
+}
+
 hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
-                                int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
-                                const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
-                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
-                                int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
-                                void* out_aux, hipStream_t stream)
+                           int64_t a_rpo, const int32_t* gather, const uint8_t* b_codes,
+                           const uint8_t* b_scales, const float* b_outer, int64_t b_rpo,
+                           const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K,
+                           int epilogue, uint32_t rht_mask, void* out, uint8_t* out_e8m0,
+                           void* out_aux, hipStream_t stream)
 {
     if (M == 0 || G == 0) return hipSuccess;
     const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;
