@@ -203,6 +203,30 @@ def test_requant_full_size_windows_and_unbiased(P, I):
     assert abs(z.item()) < 5
 
 
+@pytest.mark.parametrize("counts,N,K,gather_rows", [([70, 300, 129, 128, 1], 768, 320, None),
+                                                    ([5, 0, 600], 512, 448, 700)])
+def test_gemm_fwd_short_units(P, I, counts, N, K, gather_rows):
+    """Slot units of at most 128 slots (an expert's last) run as 512 weight rows x 128 slots,
+    covering two weight tiles; with an odd number of weight tiles the last one keeps the
+    256 x 256 shape. K = 64 mod 128 leaves a half-full last k-stage. All four epilogues."""
+    d = _moe_small(P, I, counts, N, K, gather_rows, seed=80)
+    F = N // 2
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_F32, gather=d["ggather"])
+    ref = O.gemm_nvfp4_grouped(d["rxq"], d["rwq"], d["offsets"], N, K, gather=d["gather"])
+    assert rel_fro(npy(y), ref) <= 1e-5          # exact products, fp32 accumulation
+    yb = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_BF16, gather=d["ggather"])
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    a, h13 = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_SWIGLU, gather=d["ggather"],
+                                    save_h13=True)
+    assert rel_fro(npy(a.float()), O.swiglu(ref, F)) <= 2e-3
+    assert torch.equal(h13, y.to(torch.bfloat16))
+    mask = I.sign_mask(3)
+    c, e = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_RHT32_S2F6, gather=d["ggather"],
+                                  rht_sign_mask=mask)
+    sc, se = P.rht32_s2f6_quantize(y, mask)
+    assert torch.equal(c, sc) and torch.equal(e, se)
+
+
 @pytest.mark.parametrize("sr", [False, True])
 def test_mxfp8_quantize_rows_and_cols(P, I, sr):
     dy = I.normal((600, 512), 1e-3, 31)
