@@ -29,6 +29,11 @@
  *     whatever the stream, launch order or launch configuration. Random bits are keyed by the
  *     element's index in the logical source matrix, never by thread or block id.
  *   - bf16 data is passed as `const void*` (raw 16-bit bf16 words).
+ *   - Index arrays that live on the device are the caller's contract, because the host cannot
+ *     read them without synchronizing: offsets non-decreasing from offsets[0] = 0 to
+ *     offsets[G] = M, and gather values in [0, rows of the gathered matrix). Other values make
+ *     the kernels read outside the operands (moe_combine_s2f6, whose slot ids come from the
+ *     caller, skips ids outside [0, M) instead).
  *
  * Formats:
  *   NVFP4 matrix [R x C] (C % 16 == 0):
@@ -195,8 +200,8 @@ int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, ui
  * sum runs over exact products of dequantized values fp4 * e4m3 scale (fp32 accumulation), s is
  * a slot of group g (offsets, device int64 [G+1], offsets[G] = M) and row_s = gather[s] (or s).
  * A: NVFP4 [a_rows x K] with a_rows_per_outer; B: NVFP4 [G*N x K] with b_rows_per_outer.
- * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (for SWIGLU also F % b_rows_per_outer == 0
- * or b_rows_per_outer % N == 0, so w1 and w3 rows keep their own outer scales). M is the number of
+ * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (each aligned run of 32 weight rows shares
+ * one outer scale; for SWIGLU, F % b_rows_per_outer == 0 keeps w1 and w3 apart). M is the number of
  * slots (host value); with M == 0 nothing is computed and a_*, out, out_e8m0 may be null.
  * Codes, out and out_aux 16-byte aligned, scales 4-byte aligned, out_e8m0 (RHT32_S2F6) 8-byte
  * aligned; PMN_EALIGN otherwise.
