@@ -88,6 +88,32 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+# ---- argument checks of the binding: the C ABI takes sizes as integers and cannot see the
+# tensors, so tensors whose shape or dtype disagrees with those integers are refused here
+def _need(cond: bool, what: str):
+    if not cond:
+        raise PmnError(what)
+
+
+def _tensor(t: Optional[torch.Tensor], shape, dtype, name: str):
+    _need(t is not None and t.dtype == dtype and tuple(t.shape) == tuple(shape),
+          f"{name} must be {dtype} of shape {tuple(shape)}"
+          + ("" if t is None else f", got {t.dtype} of shape {tuple(t.shape)}"))
+
+
+def _index(t: Optional[torch.Tensor], n: int, dtype, name: str):
+    if t is not None:
+        _need(t.dtype == dtype and t.numel() == n, f"{name} must hold {n} values of {dtype}")
+
+
+def _nvfp4(q: "NVFP4", name: str):
+    _need(q.codes.dtype == torch.uint8 and q.codes.dim() == 2, f"{name}.codes must be uint8 [rows, cols/2]")
+    R, C = q.rows, q.cols
+    _tensor(q.scales, (R, C // 16), torch.uint8, f"{name}.scales")
+    _need(q.rows_per_outer >= 1 and q.outer.dtype == torch.float32 and q.outer.numel() * q.rows_per_outer >= R,
+          f"{name}.outer must be fp32 with one value per {q.rows_per_outer} rows")
+
+
 def version() -> int:
     return _lib.pmn_version()
 
@@ -116,7 +142,7 @@ class NVFP4:
 
 def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int = 1,
                    outer_in: Optional[torch.Tensor] = None) -> NVFP4:
-    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [rows, cols]")
     R, Cc = x.shape
     dev = x.device
     codes = torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev)
@@ -140,8 +166,13 @@ def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
     if ld is None:
         ld = padded_bound(M, G)
     dev = q.codes.device
+    _nvfp4(q, "q")
+    _index(gather, M, torch.int32, "gather")
+    _index(offsets, G + 1, torch.int64, "offsets")
     out = torch.empty((q.cols, ld), dtype=torch.uint8, device=dev) if out is None else out
     oe = torch.empty((q.cols, ld // 32), dtype=torch.uint8, device=dev) if out_e8m0 is None else out_e8m0
+    _tensor(out, (q.cols, ld), torch.uint8, "out")
+    _tensor(oe, (q.cols, ld // 32), torch.uint8, "out_e8m0")
     po = torch.zeros((max(G, 1) + 1,), dtype=torch.int64, device=dev) if want_padded_offsets else None
     _check(_lib.requant_transpose_sr_mxfp8(_ptr(q.codes), _ptr(q.scales), _ptr(q.outer), q.rows, q.cols,
                                            q.rows_per_outer, _ptr(gather), M, _ptr(offsets), G, target, seed,
@@ -153,10 +184,11 @@ def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
 def mxfp8_quantize(x: torch.Tensor, layout: int = ROWWISE, offsets: Optional[torch.Tensor] = None,
                    rounding: int = RNE, seed: int = 0, rng_stream: int = 0, ld: Optional[int] = None,
                    want_padded_offsets: bool = False):
-    assert x.dtype == torch.bfloat16 and x.dim() == 2
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [M, N]")
     M, N = x.shape
     dev = x.device
     G = 0 if offsets is None else offsets.numel() - 1
+    _index(offsets, G + 1, torch.int64, "offsets")
     po = None
     if layout == ROWWISE:
         out = torch.empty((M, N), dtype=torch.uint8, device=dev)
@@ -174,7 +206,7 @@ def mxfp8_quantize(x: torch.Tensor, layout: int = ROWWISE, offsets: Optional[tor
 
 
 def rht32_s2f6_quantize(x: torch.Tensor, sign_mask: int):
-    assert x.dim() == 2 and x.dtype in (torch.bfloat16, torch.float32)
+    _need(x.dim() == 2 and x.dtype in (torch.bfloat16, torch.float32), "x must be bf16 or fp32 [rows, cols]")
     R, Cc = x.shape
     codes = torch.empty((R, Cc), dtype=torch.int8, device=x.device)
     e = torch.empty((R, Cc // 32), dtype=torch.uint8, device=x.device)
@@ -191,6 +223,11 @@ def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N:
     K = xq.cols
     G = offsets.numel() - 1
     dev = xq.codes.device
+    _nvfp4(xq, "xq")
+    _nvfp4(wq, "wq")
+    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    _index(offsets, G + 1, torch.int64, "offsets")
+    _index(gather, M, torch.int32, "gather")
     if out is None:
         if epilogue == EPI_F32:
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -204,6 +241,7 @@ def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N:
         out_e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
     if epilogue == EPI_SWIGLU and save_h13 and out_aux is None:
         out_aux = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _epilogue_outputs(epilogue, M, N, out, out_e8m0, out_aux)
     _check(_lib.moe_grouped_gemm_fwd(_ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows, xq.rows_per_outer,
                                      _ptr(gather), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer),
                                      wq.rows_per_outer, _ptr(offsets), G, M, N, K, epilogue,
@@ -216,6 +254,16 @@ def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N:
     return out
 
 
+def _epilogue_outputs(epilogue: int, M: int, N: int, out, out_e8m0, out_aux):
+    shape, dtype = {EPI_F32: ((M, N), torch.float32), EPI_BF16: ((M, N), torch.bfloat16),
+                    EPI_SWIGLU: ((M, N // 2), torch.bfloat16)}.get(epilogue, ((M, N), torch.int8))
+    _tensor(out, shape, dtype, "out")
+    if epilogue == EPI_RHT32_S2F6:
+        _tensor(out_e8m0, (M, N // 32), torch.uint8, "out_e8m0")
+    if epilogue == EPI_SWIGLU and out_aux is not None:
+        _tensor(out_aux, (M, N), torch.bfloat16, "out_aux")
+
+
 def moe_grouped_gemm_bwd_workspace_size(M: int, G: int, N: int, K: int, flags: int) -> int:
     return _lib.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
 
@@ -226,10 +274,13 @@ def moe_grouped_gemm_fwd_mxfp8(x: torch.Tensor, w: torch.Tensor, offsets: torch.
                                out_e8m0=None, out_aux=None):
     """MXFP8 forward (row-wise RNE quantization of x and w inside the call); returns the
     epilogue's outputs as moe_grouped_gemm_fwd does."""
-    assert x.dtype == torch.bfloat16 and w.dtype == torch.bfloat16
     K = x.shape[1]
     G = offsets.numel() - 1
     dev = w.device
+    _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [rows, K]")
+    _tensor(w, (G * N, K), torch.bfloat16, "w")
+    _index(offsets, G + 1, torch.int64, "offsets")
+    _index(gather, M, torch.int32, "gather")
     if workspace is None:
         workspace = torch.empty((_lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, G, N, K),), dtype=torch.uint8,
                                 device=dev)
@@ -246,6 +297,8 @@ def moe_grouped_gemm_fwd_mxfp8(x: torch.Tensor, w: torch.Tensor, offsets: torch.
         out_e8m0 = torch.empty((M, N // 32), dtype=torch.uint8, device=dev)
     if epilogue == EPI_SWIGLU and save_h13 and out_aux is None:
         out_aux = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    _epilogue_outputs(epilogue, M, N, out, out_e8m0, out_aux)
+    _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
     _check(_lib.moe_grouped_gemm_fwd_mxfp8(_ptr(x), x.shape[0], _ptr(gather), _ptr(w), _ptr(offsets), G, M, N, K,
                                            epilogue, rht_sign_mask & 0xFFFFFFFF, _ptr(out), _ptr(out_e8m0),
                                            _ptr(out_aux), _ptr(workspace), workspace.numel(), _stream()),
@@ -265,6 +318,12 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
     K = xq.cols
     G = offsets.numel() - 1
     dev = dy.device
+    _tensor(dy, (M, N), torch.bfloat16, "dy")
+    _nvfp4(xq, "xq")
+    _nvfp4(wq, "wq")
+    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    _index(offsets, G + 1, torch.int64, "offsets")
+    _index(gather, M, torch.int32, "gather")
     ws_bytes = moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
     if workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
@@ -272,6 +331,11 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
         da = torch.empty((M, K), dtype=torch.float32, device=dev)
     if db is None and flags & BWD_WGRAD:
         db = torch.empty((G * N, K), dtype=torch.float32, device=dev)
+    if flags & BWD_DGRAD:
+        _tensor(da, (M, K), torch.float32, "da")
+    if flags & BWD_WGRAD:
+        _tensor(db, (G * N, K), torch.float32, "db")
+    _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
     _check(_lib.moe_grouped_gemm_bwd(_ptr(dy), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows,
                                      xq.rows_per_outer, _ptr(gather), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer),
                                      wq.rows_per_outer, _ptr(offsets), G, M, N, K, flags, dy_rounding, seed,
@@ -302,7 +366,9 @@ def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int,
 
 
 def swiglu_bwd(da: torch.Tensor, h13: torch.Tensor) -> torch.Tensor:
+    _need(da.dtype == torch.float32 and da.dim() == 2, "da must be fp32 [M, F]")
     M, F = da.shape
+    _tensor(h13, (M, 2 * F), torch.bfloat16, "h13")
     out = torch.empty((M, 2 * F), dtype=torch.bfloat16, device=da.device)
     _check(_lib.swiglu_bwd(_ptr(da), _ptr(h13), M, F, _ptr(out), _stream()), "swiglu_bwd")
     return out
@@ -310,6 +376,7 @@ def swiglu_bwd(da: torch.Tensor, h13: torch.Tensor) -> torch.Tensor:
 
 def moe_route_topk(logits: torch.Tensor, k: int):
     """Returns dict(ids, gates, offsets, gather, slot_of) on the device."""
+    _need(logits.dtype == torch.float32 and logits.dim() == 2, "logits must be fp32 [T, E]")
     T, E = logits.shape
     dev = logits.device
     ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -325,14 +392,16 @@ def moe_route_topk(logits: torch.Tensor, k: int):
 def moe_combine_s2f6(codes: torch.Tensor, e8m0: torch.Tensor, sign_mask: int, slot_of: torch.Tensor,
                      gates: torch.Tensor, out=None):
     """Receiver side of the combine: bf16 [T x H], row t = sum_j gates[t, j] * decode(codes[slot_of[t, j]])."""
+    _need(codes.dtype == torch.int8 and codes.dim() == 2, "codes must be int8 [M, H]")
     M, H = codes.shape
-    assert codes.dtype == torch.int8 and e8m0.dtype == torch.uint8 and tuple(e8m0.shape) == (M, H // 32)
-    assert slot_of.dtype == torch.int32 and gates.dtype == torch.float32
-    assert codes.is_contiguous() and e8m0.is_contiguous() and slot_of.is_contiguous() and gates.is_contiguous()
+    _tensor(e8m0, (M, H // 32), torch.uint8, "e8m0")
+    _need(gates.dtype == torch.float32 and gates.dim() == 2, "gates must be fp32 [T, k]")
     T, k = gates.shape
-    assert slot_of.numel() == T * k
+    _index(slot_of, T * k, torch.int32, "slot_of")
+    _need(slot_of is not None, "slot_of is required")
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=codes.device)
+    _tensor(out, (T, H), torch.bfloat16, "out")
     _check(_lib.moe_combine_s2f6(_ptr(codes), _ptr(e8m0), M, H, sign_mask & 0xFFFFFFFF, _ptr(slot_of), _ptr(gates),
                                  T, k, _ptr(out), _stream()), "moe_combine_s2f6")
     return out

@@ -464,3 +464,39 @@ def test_empty_layer_gemms(P, I):
         torch.cuda.synchronize()
         assert da.shape == (0, K)
         assert torch.count_nonzero(db).item() == 0     # every expert's gradient written as zero
+
+
+def test_binding_rejects_mismatched_tensors(P, I):
+    """The C ABI takes sizes as integers; the binding refuses tensors whose shape or dtype
+    disagrees with them (PmnError), before anything is launched."""
+    G, N, K, M = 2, 256, 256, 64
+    x = I.normal((M, K), 1.0, 90).to(DEV)
+    w = I.normal((G * N, K), 0.02, 91).to(DEV)
+    xq = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    wq = P.nvfp4_quantize(w, P.NVFP4_WEIGHT, rows_per_outer=N)
+    off = torch.tensor([0, 30, M], dtype=torch.int64, device=DEV)
+    bad = [
+        lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, 2 * N),                                   # wq rows != G*N
+        lambda: P.moe_grouped_gemm_fwd(xq, P.nvfp4_quantize(w[:, :128].contiguous(), P.NVFP4_WEIGHT, N),
+                                       off, M, N),                                               # K differs
+        lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, N, out=torch.empty((M, N - 1), device=DEV)),
+        lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, N, gather=torch.zeros(M, dtype=torch.int64, device=DEV)),
+        lambda: P.moe_grouped_gemm_fwd(xq, wq, off.to(torch.int32), M, N),
+        lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, N, P.EPI_RHT32_S2F6,
+                                       out_e8m0=torch.empty((M, N // 16), dtype=torch.uint8, device=DEV)),
+        lambda: P.moe_grouped_gemm_bwd(torch.zeros((M, N + 32), dtype=torch.bfloat16, device=DEV), xq, wq, off, M, N),
+        lambda: P.moe_grouped_gemm_bwd(torch.zeros((M, N), dtype=torch.bfloat16, device=DEV), xq, wq, off, M, N,
+                                       db=torch.empty((G * N, K - 1), device=DEV)),
+        lambda: P.requant_transpose_sr_mxfp8(xq, out=torch.empty((K, 32), dtype=torch.uint8, device=DEV)),
+        lambda: P.swiglu_bwd(torch.zeros((M, N), device=DEV), torch.zeros((M, N), dtype=torch.bfloat16, device=DEV)),
+        lambda: P.moe_combine_s2f6(torch.zeros((M, N), dtype=torch.int8, device=DEV),
+                                   torch.zeros((M, N // 16), dtype=torch.uint8, device=DEV), 0,
+                                   torch.zeros(M, dtype=torch.int32, device=DEV), torch.ones((M, 1), device=DEV)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises(P.PmnError):
+            call()
+    # a well-formed call still runs
+    y = P.moe_grouped_gemm_fwd(xq, wq, off, M, N)
+    torch.cuda.synchronize()
+    assert y.shape == (M, N)
