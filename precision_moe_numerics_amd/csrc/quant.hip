@@ -440,6 +440,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                                                         const int32_t* __restrict__ gather)
 {
     __shared__ uint8_t se[4][64];
+    __shared__ int64_t pcol[64];
     const int64_t nb = N >> 5;
     const int t = threadIdx.x;
     const int64_t r0 = (int64_t)blockIdx.x * 64, kb0 = (int64_t)blockIdx.y * 4;
@@ -454,18 +455,22 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
         }
         return pad_off[lo] + (r - offsets[lo]);
     };
+    const int64_t r = r0 + (t >> 2), kb = kb0 + (t & 3);
+    const bool live = r < M && kb < nb;
+    uint32_t w[16];
+    if (live) load_block32(x, (gather ? (int64_t)gather[r] : r) * nb + kb, w);
+    // the workgroup's 64 rows look their padded positions up once, while the loads are in flight
+    if (t < 64) pcol[t] = r0 + t < M ? padded_col(r0 + t) : 0;
+    __syncthreads();
     {
-        const int64_t r = r0 + (t >> 2), kb = kb0 + (t & 3);
-        if (r < M && kb < nb) {
-            uint32_t w[16];
-            load_block32(x, (gather ? (int64_t)gather[r] : r) * nb + kb, w);
+        if (live) {
             int e;
             if (FP4) {
                 uint32_t o[4];
                 e = mxfp4_block<SR>(w, r, kb, N, seed, stream_id, o);
                 if (BLK) {
                     // k-block kb = chunk kb % 4 of 64-byte column kb / 4
-                    const int64_t pr = padded_col(r);
+                    const int64_t pr = pcol[t >> 2];
                     const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = (int)(kb & 3);
                     *reinterpret_cast<uint4*>(out + ((pr >> 4) * (N >> 7) + (kb >> 2)) * 1024 + r16 * 64 + ((c ^ x) << 4)) =
                         make_uint4(o[0], o[1], o[2], o[3]);
@@ -479,7 +484,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                     // k-block kb = chunks 2 (kb % 2) and 2 (kb % 2) + 1 of 64-byte column kb / 2; rows
                     // are whole columns (N rounded up to 64 bytes), and with an odd k-block count the
                     // last column's second half holds zero codes
-                    const int64_t pr = padded_col(r);
+                    const int64_t pr = pcol[t >> 2];
                     const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
                     uint8_t* blk = out + ((pr >> 4) * ((N + 63) >> 6) + (kb >> 1)) * 1024 + r16 * 64;
                     *reinterpret_cast<uint4*>(blk + ((c ^ x) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -496,8 +501,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
         }
     }
     __syncthreads();
-    const int64_t r = r0 + (t & 63), kb = kb0 + (t >> 6);
-    if (r < M && kb < nb) out_e8m0[kb * ld_e8m0 + padded_col(r)] = se[t >> 6][t & 63];
+    const int64_t re = r0 + (t & 63), kbe = kb0 + (t >> 6);
+    if (re < M && kbe < nb) out_e8m0[kbe * ld_e8m0 + pcol[t & 63]] = se[t >> 6][t & 63];
 }
 
 hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, uint64_t seed,
