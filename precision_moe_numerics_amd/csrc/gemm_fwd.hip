@@ -32,9 +32,10 @@
 // the same order, so every MFMA multiplies matching k; only the fp32 summation order differs
 // from a k-sequential one.
 //
-// Code layout in a stage slot: row r at 64 r, its 16-byte chunk c at position c ^ ((r / 4) % 4),
-// so the 16 rows a quarter-wavefront reads cover all 16 bank groups. Each copy lane fetches the
-// chunk its destination position needs, so plain row-major codes arrive permuted.
+// Code layout in a stage slot: the weight rows, then the slot rows, then their scale bytes (8 per
+// row). Row r of an operand's region holds its 64 code bytes at 64 r, 16-byte chunk c at position
+// c ^ ((r / 4) % 4), so the 16 rows a quarter-wavefront reads cover all 16 bank groups. Each copy
+// lane fetches the chunk its destination position needs, so plain row-major codes arrive permuted.
 //
 // Groups (experts) are ragged: a workgroup finds its (expert, slot tile) from the device offsets
 // with one wavefront-parallel search, so no host synchronization is needed. An expert's last
@@ -77,7 +78,7 @@ constexpr int STAGEB = ROWS_MAX * 72;         // 64 code bytes + 8 scale bytes p
 constexpr int LDSB = NSTAGE * STAGEB;
 constexpr int THREADS = 256;
 constexpr int OPITCH = 272;
-static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tiles and E8M0 tiles fit in the ring");
+static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tile and E8M0 tile fit in the ring");
 }  // namespace fwd
 
 // One workgroup tile. SHAPE false: 256 weight rows x 256 slots, wavefront w computes weight rows
