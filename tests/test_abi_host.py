@@ -105,3 +105,33 @@ def test_blocked_layout_reader_matches_the_documented_offsets():
             c, b = divmod(within, 16)
             raw[(rb * (Cc // 64) + kb) * 1024 + 64 * r + 16 * (c ^ ((r // 4) % 4)) + b] = m[i, j]
     assert np.array_equal(unblock(raw, R, Cc), m)
+
+
+def test_binding_refuses_mismatched_tensors_on_the_host():
+    """The Python binding checks tensor shapes and dtypes against the sizes it passes to the C
+    ABI before it takes any pointer, so the checks run (and fail) without a GPU."""
+    import torch
+    import precision_moe_numerics_amd as P
+    G, N, K, M = 2, 256, 256, 64
+
+    def nv(rows, cols, rpo=1):
+        return P.NVFP4(torch.zeros((rows, cols // 2), dtype=torch.uint8), torch.zeros((rows, cols // 16), dtype=torch.uint8),
+                       torch.ones((rows // rpo,), dtype=torch.float32), rpo)
+
+    xq, wq = nv(M, K), nv(G * N, K, N)
+    off = torch.tensor([0, 30, M], dtype=torch.int64)
+    cases = [
+        (lambda: P.moe_grouped_gemm_fwd(xq, nv(G * N, K - 64, N), off, M, N), "wq must be"),
+        (lambda: P.moe_grouped_gemm_fwd(xq, nv(G * N + 256, K, N), off, M, N), "wq must be"),
+        (lambda: P.moe_grouped_gemm_fwd(xq, wq, off.to(torch.int32), M, N), "offsets"),
+        (lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, N, gather=torch.zeros(M, dtype=torch.int64)), "gather"),
+        (lambda: P.moe_grouped_gemm_fwd(xq, wq, off, M, N, out=torch.empty((M, N), dtype=torch.bfloat16)), "out"),
+        (lambda: P.moe_grouped_gemm_fwd(P.NVFP4(xq.codes, xq.scales[:, :8].contiguous(), xq.outer, 1), wq, off, M, N),
+         "xq.scales"),
+        (lambda: P.moe_grouped_gemm_bwd(torch.zeros((M, N + 1), dtype=torch.bfloat16), xq, wq, off, M, N), "dy"),
+        (lambda: P.swiglu_bwd(torch.zeros((M, N)), torch.zeros((M, N), dtype=torch.bfloat16)), "h13"),
+        (lambda: P.requant_transpose_sr_mxfp8(xq, out=torch.empty((K, 32), dtype=torch.uint8)), "out"),
+    ]
+    for call, what in cases:
+        with pytest.raises(P.PmnError, match=what):
+            call()
