@@ -61,19 +61,32 @@ PMN_DEV GroupBlock find_block(int64_t pb, const int64_t* offsets, int G, int64_t
     return r;
 }
 
+// po[0] = 0, po[g + 1] = sum over h <= g of the group sizes rounded up to `unit`: one wavefront,
+// an inclusive prefix sum over 64 groups at a time
 __global__ void k_padded_offsets(const int64_t* offsets, int G, int64_t M, int64_t* po, int64_t unit)
 {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    const int lane = threadIdx.x;
+    if (blockIdx.x != 0 || lane >= 64) return;
     if (offsets == nullptr) {
-        po[0] = 0;
-        po[1] = (M + unit - 1) & ~(unit - 1);
+        if (lane == 0) {
+            po[0] = 0;
+            po[1] = (M + unit - 1) & ~(unit - 1);
+        }
         return;
     }
-    int64_t p = 0;
-    po[0] = 0;
-    for (int g = 0; g < G; g++) {
-        p += (offsets[g + 1] - offsets[g] + unit - 1) & ~(unit - 1);
-        po[g + 1] = p;
+    if (lane == 0) po[0] = 0;
+    int64_t base = 0;
+    for (int g0 = 0; g0 < G; g0 += 64) {
+        const int g = g0 + lane;
+        const int64_t P = g < G ? (offsets[g + 1] - offsets[g] + unit - 1) & ~(unit - 1) : 0;
+        int64_t cum = P;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t y = __shfl_up(cum, d, 64);
+            if (lane >= d) cum += y;
+        }
+        if (g < G) po[g + 1] = base + cum;
+        base += __shfl(cum, 63, 64);
     }
 }
 
