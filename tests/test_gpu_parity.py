@@ -203,6 +203,22 @@ def test_requant_full_size_windows_and_unbiased(P, I):
     assert abs(z.item()) < 5
 
 
+def test_gemm_fwd_many_groups(P, I):
+    """200 experts (the group lookup scans them 64 at a time), most with 0..40 slots and a few
+    with several tiles; F32 against the oracle, SwiGLU's h13 against it."""
+    rng = np.random.default_rng(31)
+    counts = [int(c) for c in rng.integers(0, 41, 200)]
+    counts[7], counts[150], counts[199] = 300, 0, 513
+    N, K = 256, 128
+    d = _moe_small(P, I, counts, N, K, gather_rows=None, seed=90)
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_F32)
+    ref = O.gemm_nvfp4_grouped(d["rxq"], d["rwq"], d["offsets"], N, K)
+    assert rel_fro(npy(y), ref) <= 1e-5
+    a, h13 = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_SWIGLU, save_h13=True)
+    assert torch.equal(h13, y.to(torch.bfloat16))
+    assert rel_fro(npy(a.float()), O.swiglu(ref, N // 2)) <= 2e-3
+
+
 @pytest.mark.parametrize("counts,N,K,gather_rows", [([70, 300, 129, 128, 1], 768, 320, None),
                                                     ([5, 0, 600], 512, 448, 700)])
 def test_gemm_fwd_short_units(P, I, counts, N, K, gather_rows):
