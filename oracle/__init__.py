@@ -26,23 +26,40 @@ TARGET_E4M3 = 0
 TARGET_E2M1 = 1
 
 
-def build() -> str:
-    """Compile the oracle with strict IEEE semantics (no contraction, no fast-math)."""
+# Sanitizer flags of the checking build: AddressSanitizer (every out-of-bounds or use-after-free
+# access aborts) and UndefinedBehaviorSanitizer (signed overflow, bad shifts, misaligned or null
+# accesses, float-to-int overflow abort: nothing recovers).
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fsanitize=float-cast-overflow",
+                  "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with strict IEEE semantics (no contraction, no fast-math).
+
+    ``sanitize`` adds ASan + UBSan (a checking build; the process that loads it needs the ASan
+    runtime first in LD_PRELOAD). ``out`` is the library path (default: next to the source).
+    """
+    out = out or _LIB
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-           "-shared", "-fPIC", "-Wall", "-o", _LIB, _SRC, "-lm"]
+           "-shared", "-fPIC", "-Wall"] + (SANITIZE_FLAGS if sanitize else []) + ["-o", out, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    return _LIB
+    return out
 
 
 _lib = None
 
 
 def lib():
+    """The loaded oracle library: PMN_ORACLE_LIB if set (e.g. a sanitizer build), else the
+    default build, rebuilt when the source is newer."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        _lib = C.CDLL(_LIB)
+        path = os.environ.get("PMN_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        _lib = C.CDLL(path)
         _declare(_lib)
     return _lib
 

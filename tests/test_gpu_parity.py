@@ -102,6 +102,24 @@ def test_nvfp4_edge_values(P):
         assert_nvfp4_equal(q, O.nvfp4_quantize(xb, 1, four_six))
 
 
+@pytest.mark.parametrize("cols", [32, 1024, 2048, 4096, 8192, 8208])
+def test_nvfp4_four_over_six_exact_tie_keeps_six(P, cols):
+    """[2688, 0 x 15 | 6, 0 x 15]: both candidates of the second block are exact, the tie keeps 6
+    (scale byte 0x38; a '<=' rule would store 0x3C). Checked through the one-wavefront row kernel
+    (every row-length instantiation and the long-row fallback) and through the outer-scale hook."""
+    x = np.zeros((3, cols), np.float32)
+    for r in range(3):
+        x[r, 0], x[r, 16] = 2688.0, 6.0
+        x[r, cols - 16] = 6.0 if cols > 32 else x[r, cols - 16]     # a tie in the row's last block
+    xb = bf16_np(x)
+    ref = O.nvfp4_quantize(xb, 1, True)
+    assert ref["scales"][0, 1] == 0x38
+    for outer_in in (None, torch.ones(3, device=DEV)):
+        q = P.nvfp4_quantize(xb.to(DEV), P.NVFP4_ACT, outer_in=outer_in)
+        assert_nvfp4_equal(q, ref)
+        assert npy(q.scales)[0, 1] == 0x38 and npy(q.scales)[2, cols // 16 - 1] == 0x38
+
+
 def test_nvfp4_empty(P):
     q = P.nvfp4_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV))
     assert q.codes.shape == (0, 32)

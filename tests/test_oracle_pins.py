@@ -205,6 +205,30 @@ def test_four_over_six_hand_case():
     assert qy["chose4"][0, 0] == 0 and np.array_equal(O.nvfp4_dequantize(qy), y)
 
 
+def test_four_over_six_exact_tie_keeps_six():
+    """An exact tie between the two candidates keeps candidate 6 (the strict '<' of the rule).
+
+    Row [2688, 0 x 15 | 6, 0 x 15] in activation mode: the row amax 2688 = 6 * 448 gives the
+    outer scale exactly 1. In the second block candidate 6 takes scale 1 (E4M3 0x38) and stores 6
+    as code 6; candidate 4 takes scale 1.5 (0x3C) and stores 6 as code 4 (4 * 1.5 = 6). Both
+    reproduce the block with zero error, so only the tie rule decides: 0x38 under '<', 0x3C under
+    '<='. The first block saturates both candidates to 448 (0x7E), an identical pair.
+    """
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0], x[0, 16] = 2688.0, 6.0
+    # the tie is real: both candidates' dequantized blocks equal the input, computed here from
+    # the FP4 grid and the E4M3 values 1 and 1.5 alone
+    grid = FACTS["fp4_grid"]["magnitudes"]
+    assert 6.0 in grid and 4.0 in grid and grid[grid.index(6.0)] * 1.0 == 6.0 and 4.0 * 1.5 == 6.0
+    for outer_in in (None, [1.0]):
+        q = O.nvfp4_quantize(bf16(x), four_six=True, outer_in=outer_in)
+        assert q["outer"][0] == 1.0
+        assert list(q["scales"][0]) == [0x7E, 0x38]
+        assert list(q["chose4"][0]) == [0, 0]
+        assert q["codes"][0, 0] == 0x07 and q["codes"][0, 8] == 0x07      # code 6 = magnitude index 7
+        assert np.array_equal(O.nvfp4_dequantize(q), x)
+
+
 def _dequant_block_fp64(codes, scale_byte, s_o):
     """Independent decode: the pages' grid and the OCP E4M3 layout, written out here."""
     mags = FACTS["fp4_grid"]["magnitudes"]
