@@ -12,20 +12,25 @@ FFN 2048, SwiGLU):
 Inputs are generated on the GPU from fixed seeds before the timed region and stay resident in
 HBM. Per-call device time comes from HIP events on the stream the kernels run on.
 
-Also reported: the memory-bound quantizer workload (8192 x 7168 activations, 0.5 * StudentT(3)):
-nvfp4_quantize with 4/6 and requant_transpose_sr_mxfp8 of its output, each timed over rotating
-input buffers larger than the 256 MB Infinity Cache, as GB/s of algorithmic bytes.
-
-Also reported: the MXFP8 forward of the layers that keep MXFP8, on the same layer shape (w13 with
-SwiGLU, w2 with RHT32 + S2F6, each call including its MXFP8 quantization), as TFLOP/s.
-
-Also reported: the FP4 backward variant on the same layer (every backward operand in MXFP4, the
-GEMMs on the block-scaled FP4 MFMA), as TFLOP/s.
-
-Also reported: the receiver side of the combine (moe_combine_s2f6) on the routed shape, 16384
-tokens with top-8 of 32 experts gathered back from 131072 S2F6 rows of hidden 4096, as GB/s.
+Also reported, each in its own object of the JSON line:
+  moe32              the same step on the routed 32-expert layer (16384 tokens, top-8 of 32
+                     experts, hidden 4096, FFN 1536), activations gathered through the routing
+  hw_measured        roofs measured in this run on this chip: HBM bandwidth of a streaming kernel
+                     for each kernel's read:write byte mix (nontemporal 16-byte accesses, buffers
+                     larger than the 256 MB Infinity Cache) and the throughput of every MFMA
+                     instruction the grouped GEMMs issue
+  memory_kernels     every memory-bound call (layer and workloads) as GB/s of algorithmic bytes,
+                     against 8 TB/s and against the measured roof of its own mix
+  quantizer_workload nvfp4_quantize with 4/6 and requant_transpose_sr_mxfp8 on 8192 x 7168
+                     activations (0.5 * StudentT(3)), rotating inputs larger than the cache
+  mxfp8_forward      the forward of the layers that keep MXFP8 (w13 + SwiGLU, w2 + RHT32/S2F6)
+  fp4_backward       the FP4 backward variant (every backward operand in MXFP4)
+  combine_workload   the combine's receiver, 16384 tokens x top-8 of 131072 S2F6 rows of 4096
+  cpu_baseline       the CPU oracle on a bounded sample of the layer, and on the full 8192 x 7168
+                     quantizer workload with all host threads and with one
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ep48|moe32]
+       python bench.py --summarize-profiles DIR   (writes profiles/*.md from rocprofv3 CSVs in DIR)
 """
 from __future__ import annotations
 
@@ -44,6 +49,19 @@ PEAK_F16_TFLOPS = 2500.0       # MI355X dense MFMA fp16/bf16
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense MFMA fp8
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MFMA fp4
 
+# Read:write byte mixes of the memory-bound kernels, as KB read : KB written per streamed unit.
+STREAM_MIXES = {
+    "read": (1, 0),
+    "write": (0, 1),
+    "copy": (1, 1),
+    "nvfp4_quantize": (32, 9),      # bf16 in (2 B) : codes + E4M3 scales out (0.5 + 1/16 B) per element
+    "requant": (6, 11),             # codes + scales in (0.5 + 1/16 B) : E4M3 + E8M0 out (1 + 1/32 B)
+    "mxfp8_quantize": (64, 33),     # bf16 in (2 B) : E4M3 + E8M0 out (1 + 1/32 B); also bf16 RHT32 + S2F6
+    "combine": (33, 8),             # 8 slots x (4096 + 128) B + 64 B of index/gate in : 8192 B out per token
+    "swiglu_bwd": (2, 1),           # da fp32 + h13 bf16 in (8 B) : dh13 bf16 out (4 B) per FFN element
+}
+CALIB_GRID = 4097                   # grid of the one calibration copy (1 GiB read + 1 GiB written)
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -51,8 +69,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="ep48", choices=["ep48", "moe32"])
+    ap.add_argument("--moe32-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quant-iters", type=int, default=20)
+    ap.add_argument("--summarize-profiles", metavar="DIR", default=None)
     return ap.parse_args()
 
 
@@ -144,6 +164,62 @@ class Layer:
         return yc, dx, dw13, dw2
 
 
+def _time_ms(torch, fn, reps):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def hardware_roofs(P, torch, dev):
+    """Roofs measured in this run: the streaming kernel's HBM bandwidth for each read:write mix
+    (best of three grid sizes; 2 GiB read, or written when nothing is read, so every buffer is far
+    larger than the 256 MB Infinity Cache), torch's
+    1 GiB device-to-device copy, and each MFMA instruction's throughput at 1 and 2 wavefronts per
+    SIMD (one workgroup per compute unit). One copy launch with the grid CALIB_GRID moves exactly
+    1 GiB each way: the profile summaries calibrate the PMC byte counters on it."""
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev).fill_(7)
+    dst = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    hbm = {}
+    for name, (rv, wv) in STREAM_MIXES.items():
+        units = (2 << 20) // (rv if rv else wv)          # 2 GiB read (or written)
+        nbytes = units * (rv + wv) * 1024.0
+        best = 0.0
+        for grid in (1024, 4096, 16384):
+            def run(g=grid):
+                P.probe_stream(src, dst, units, rv, wv, grid=g)
+            run()
+            best = max(best, nbytes / (_time_ms(torch, run, 3) * 1e-3) / 1e9)
+        hbm[name] = dict(gbs=best, read_kb=rv, write_kb=wv)
+    P.probe_stream(src, dst, 1 << 20, 1, 1, grid=CALIB_GRID)      # the calibration copy
+    src1, dst1 = src[: 1 << 30], dst[: 1 << 30]
+    dst1.copy_(src1)
+    torch_copy = 2.0 * (1 << 30) / (_time_ms(torch, lambda: dst1.copy_(src1), 3) * 1e-3) / 1e9
+    del src, dst, src1, dst1
+    sink = torch.empty(P._lib.pmn_probe_mfma_sink_floats(2, 256), dtype=torch.float32, device=dev)
+    guess = {0: 2.0e15, 1: 2.2e15, 2: 4.5e15, 3: 4.5e15, 4: 9.0e15}       # only sizes the launches
+    mfma = {}
+    for kind, name in P.PROBE_MFMA_KINDS.items():
+        for wps in (1, 2):
+            per_iter = P.probe_mfma(kind, wps, 256, 1, sink)
+            iters = max(200, int(4e-3 * guess[kind] / per_iter))
+            P.probe_mfma(kind, wps, 256, 50, sink)
+            fl = [0.0]
+
+            def run(k=kind, w=wps, it=iters):
+                fl[0] = P.probe_mfma(k, w, 256, it, sink)
+            ms = _time_ms(torch, run, 2)
+            mfma.setdefault(name, {})[f"{wps}_wave_per_simd"] = fl[0] / (ms * 1e-3) / 1e12
+    del sink
+    return dict(hbm_gbs=hbm, torch_copy_gbs=torch_copy, mfma_tflops=mfma,
+                note="streaming kernel: nontemporal 16-byte loads/stores, one contiguous KB per instruction; "
+                     "MFMA: independent accumulator chains on constant operands, no memory traffic")
+
+
 def quantizer_workload(P, I, torch, dev, iters):
     """GB/s of nvfp4_quantize (4/6, per-token outer) and requant_transpose_sr_mxfp8 on the
     8192 x 7168 activation workload, rotating inputs so the Infinity Cache cannot serve them."""
@@ -191,20 +267,6 @@ def quantizer_workload(P, I, torch, dev, iters):
     ms = e0.elapsed_time(e1) / iters
     nbytes = R * Cc * (0.5 + 1 / 16 + 1 + 1 / 32) + R * 4
     res["requant_transpose_sr_mxfp8"] = dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
-    # measured copy bandwidth (device-to-device copy of 1 GiB, read + write)
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(2):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(5):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
-    res["hbm_copy_gbs"] = 2 * (1 << 30) / (ms * 1e-3) / 1e9
-    del src, dst
     return res
 
 
@@ -318,12 +380,16 @@ def fp4_backward_workload(P, torch, layer, iters):
 
 
 def cpu_baseline(I, shape):
-    """The CPU oracle (as it stands) on a bounded sample of the same step: 16 slots of one expert
-    through the whole layer, forward and backward. Returns TFLOP/s of that sample."""
-    import numpy as np
+    """The CPU oracle (as it stands, never tuned for speed) on bounded samples of the same work:
+    16 slots of one expert through the whole layer, forward and backward (the `value`, TFLOP/s of
+    the sample's GEMM work), and the full 8192 x 7168 quantizer workload (nvfp4_quantize with 4/6
+    and requant_transpose_sr_mxfp8 of its output) with all host threads and with one thread, as
+    GB/s of the same algorithmic bytes the GPU is rated on."""
+    import numpy as np  # noqa: F401
     import torch
 
     import oracle as O
+    threads = O.threads()
     S, H, F = 16, shape.hidden, shape.ffn
     x = I.moe_activations(shape, "cpu", rows=S)
     w13 = I.normal((2 * F, H), 0.02, shape.seeds["w"])
@@ -356,10 +422,64 @@ def cpu_baseline(I, shape):
     O.gemm_mxfp8_wgrad(gt, gte, xt, xte, off, 2 * F, H)
     dt_s = time.perf_counter() - t0
     flops = 3 * 2.0 * S * (2 * F * H + H * F)
-    return dict(value=flops / dt_s / 1e12, unit="TFLOP/s", cores=O.threads(), kind="oracle", seconds=dt_s,
+    # the memory-bound workload at full size
+    base = I.quantizer("cpu")
+    R, Cc = base["x"].shape
+    qbytes = R * Cc * (2 + 0.5 + 1 / 16) + R * 4
+    rbytes = R * Cc * (0.5 + 1 / 16 + 1 + 1 / 32) + R * 4
+    quant = {}
+    for nt in (threads, 1):
+        O.set_threads(nt)
+        t1 = time.perf_counter()
+        q = O.nvfp4_quantize(base["x"], 1, True)
+        t2 = time.perf_counter()
+        O.requant_transpose_sr(q, seed=base["seed"], stream=base["stream"])
+        t3 = time.perf_counter()
+        quant[f"threads_{nt}"] = dict(nvfp4_quantize_s=t2 - t1, nvfp4_quantize_gbs=qbytes / (t2 - t1) / 1e9,
+                                      requant_s=t3 - t2, requant_gbs=rbytes / (t3 - t2) / 1e9)
+    O.set_threads(threads)
+    return dict(value=flops / dt_s / 1e12, unit="TFLOP/s", cores=threads, kind="oracle", seconds=dt_s,
                 sample=f"{S} routed slots of one expert through the whole layer (NVFP4 quantize of X, w13, w2; "
                        f"w13 GEMM + SwiGLU; A quantize; w2 GEMM; RHT32+S2F6; MXFP8 dY quantize; SR requant of "
-                       f"W2^T, A^T, W13^T, X^T; dgrad and wgrad of both GEMMs), H={H}, F={F}")
+                       f"W2^T, A^T, W13^T, X^T; dgrad and wgrad of both GEMMs), H={H}, F={F}",
+                quantizer_workload=dict(shape=[R, Cc], **quant,
+                                        note="full size, the same inputs and algorithmic bytes as the GPU's "
+                                             "quantizer_workload"))
+
+
+def moe32_workload(P, I, torch, dev, steps, warmup=2):
+    """The layer step on the routed 32-expert layer (16384 tokens, top-8 of 32 experts, hidden
+    4096, FFN 1536; routing on the device from the seeded logits, activations gathered)."""
+    layer = Layer(P, I, torch, I.MOE32, dev)
+    T = Timer(torch)
+    for _ in range(warmup):
+        layer.step(T)
+    torch.cuda.synchronize()
+    T.collect()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        layer.step(T)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per_call = T.collect()
+    fl = layer.flops()
+    kern = {name: {"ms": v} for name, v in per_call.items()}
+    for nm, f, pk in (("moe_grouped_gemm_fwd[w13+swiglu]", fl["fwd13"], PEAK_F16_TFLOPS),
+                      ("moe_grouped_gemm_fwd[w2+rht32_s2f6]", fl["fwd2"], PEAK_F16_TFLOPS),
+                      ("moe_grouped_gemm_bwd[w2]", 2 * fl["fwd2"], PEAK_FP8_TFLOPS),
+                      ("moe_grouped_gemm_bwd[w13]", 2 * fl["fwd13"], PEAK_FP8_TFLOPS)):
+        t = f / (per_call[nm] * 1e-3) / 1e12
+        kern[nm].update(tflops=t, frac_of_dtype_peak=t / pk)
+    fwd_ms = sum(per_call[k] for k in per_call if "fwd" in k or k in ("nvfp4_quantize[x]", "nvfp4_quantize[a]"))
+    bwd_ms = sum(per_call[k] for k in per_call if "bwd" in k)
+    res = dict(workload=f"moe32: 32 experts, {layer.M} routed slots (top-8 of 16384 tokens), hidden 4096, FFN 1536",
+               steps=steps, ms_per_step=ms, tflops=fl["step"] / (ms * 1e-3) / 1e12, step_tflop=fl["step"] / 1e12,
+               forward_ms=fwd_ms, forward_tflops=fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
+               backward_ms=bwd_ms, backward_tflops=fl["bwd"] / (bwd_ms * 1e-3) / 1e12, kernels=kern)
+    del layer
+    return res
 
 
 def measured_traffic():
@@ -377,10 +497,182 @@ def measured_traffic():
     return rec["traffic_bytes_per_launch"]
 
 
+# ---- profile summaries ---------------------------------------------------------------------
+
+PROFILE_COMMANDS = {
+    "kernel_trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof/kt -o ep48 -- "
+                     "python3 bench.py --steps 10 --warmup 3 --no-cpu-baseline"),
+    "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/prof/fetch -o ep48 -- "
+              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --quant-iters 2 --moe32-steps 1"),
+    "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/prof/write -o ep48 -- "
+              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --quant-iters 2 --moe32-steps 1"),
+    "clock": ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA "
+              "SQ_ACTIVE_INST_VALU --output-format csv -d gpurun_out/prof/clock -o ep48 -- "
+              "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --quant-iters 1 --moe32-steps 1"),
+    "bench": "python3 bench.py --no-cpu-baseline > gpurun_out/prof/bench.json",
+}
+TRAFFIC_SOURCES = ["precision_moe_numerics_amd/csrc/gemm_fwd.hip", "precision_moe_numerics_amd/csrc/pmn_dev.hpp"]
+
+
+def _kname(n):
+    return n.split("(")[0].replace("void ", "").strip()
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def summarize_profiles(d):
+    """Write profiles/*.md (and the forward GEMM's traffic record) from the rocprofv3 CSVs of the
+    PROFILE_COMMANDS runs under d (subfolders kt, fetch, write, clock, and bench.json: the
+    benchmark line of the same lease)."""
+    import csv
+    import hashlib
+    from collections import defaultdict
+    out_dir = os.path.join(ROOT, "profiles")
+    bench = None
+    bp = os.path.join(d, "bench.json")
+    if os.path.exists(bp):
+        lines = [l for l in open(bp) if l.strip().startswith("{")]
+        bench = json.loads(lines[-1]) if lines else None
+    # kernel trace + stats
+    stats = list(csv.DictReader(open(_find_csv(os.path.join(d, "kt"), "kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(_find_csv(os.path.join(d, "kt"), "kernel_trace.csv"))))
+    md = ["# Kernel time of the 48-expert layer step and the workloads bench.py reports", "",
+          "Command (from the repository root, one MI355X; the bench line below ran in the same lease):", "",
+          "```", PROFILE_COMMANDS["kernel_trace"], PROFILE_COMMANDS["bench"], "```", "",
+          "rocprofv3 `--stats` summary (every kernel of the profiled run, input generation included):", "",
+          "| kernel | calls | avg us | min us | max us | % time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in stats:
+        n = _kname(r["Name"])
+        n = n if len(n) <= 70 else n[:67] + "..."
+        md.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                  f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    agg = defaultdict(list)
+    for r in trace:
+        n = r["Kernel_Name"]
+        if "pmn::" not in n and "k_stream_mix" not in n and "k_mfma_probe" not in n:
+            continue
+        key = (_kname(n), r.get("Grid_Size_X", r.get("Grid_Size", "")), r.get("Grid_Size_Y", "1"))
+        agg[key].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    md += ["", "Library kernels by launch shape (grid in work-items x, y):", "",
+           "| kernel | grid | launches | avg us |", "|---|---|---:|---:|"]
+    for k, v in sorted(agg.items(), key=lambda kv: -sum(kv[1]) / len(kv[1])):
+        md.append(f"| `{k[0]}` | {k[1]},{k[2]} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} |")
+    if bench:
+        r = bench["roofline"]
+        gem = [v for k, v in agg.items() if k[0].startswith("pmn::k_nvfp4_grouped_gemm<2>")]
+        if gem:
+            v = max(gem, key=len)
+            avg = sum(v) / len(v) / 1e6
+            md += ["", f"Dominant kernel: `k_nvfp4_grouped_gemm<2>` (w13 forward + SwiGLU) averages {avg:.3f} ms per "
+                       f"launch in this trace; bench.py in the same lease measured {r['ms_per_launch']:.3f} ms by HIP "
+                       f"events ({r['achieved']:.0f} TFLOP/s, frac {r['frac']:.3f} of {r['peak']:.0f}); from the "
+                       f"trace: {r['flops_per_launch'] / (avg * 1e-3) / 1e12:.0f} TFLOP/s, frac "
+                       f"{r['flops_per_launch'] / (avg * 1e-3) / 1e12 / r['peak']:.3f}.",
+                   "", f"Bench line of the same lease: {bench['ms_per_step']:.2f} ms per step, {bench['value']:.0f} "
+                       f"TFLOP/s."]
+    open(os.path.join(out_dir, "ep48_layer_step_kernel_stats.md"), "w").write("\n".join(md) + "\n")
+
+    # HBM traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), calibrated on the probe's copy
+    def load(sub):
+        dd = defaultdict(list)
+        for r in csv.DictReader(open(_find_csv(os.path.join(d, sub), "counter_collection.csv"))):
+            dd[(_kname(r["Kernel_Name"]), r["Grid_Size"])].append(float(r["Counter_Value"]))
+        return dd
+    fe, wr = load("fetch"), load("write")
+    cal = str(CALIB_GRID * 256)
+    ck = [k for k in fe if "k_stream_mix" in k[0] and k[1] == cal]
+    assert ck, "the calibration copy (k_stream_mix, grid CALIB_GRID) is missing from the PMC runs"
+    gib_kib = float(1 << 20)
+    ff = gib_kib / (sum(fe[ck[0]]) / len(fe[ck[0]]))
+    fw = gib_kib / (sum(wr[ck[0]]) / len(wr[ck[0]]))
+    tc = [k for k in fe if "copyBuffer" in k[0]]
+    tmd = ["# HBM traffic per kernel launch (48-expert layer step and the workloads)", "",
+           "Commands (from the repository root, one MI355X, one counter per run):", "", "```",
+           PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"], "```", "",
+           f"Calibration: the probe copy `k_stream_mix` launched with grid {CALIB_GRID} x 256 reads and writes exactly "
+           f"1 GiB (1048576 KiB) with nontemporal 16-byte accesses; it reads FETCH_SIZE = {gib_kib / ff:.1f} KiB and "
+           f"WRITE_SIZE = {gib_kib / fw:.1f} KiB, so HBM bytes = FETCH_SIZE x {ff:.3f} KiB and WRITE_SIZE x {fw:.3f} KiB."
+           + (f" (torch's 1 GiB copy reads FETCH_SIZE = {max(max(fe[k]) for k in tc):.1f} KiB.)" if tc else ""), "",
+           "| kernel | grid | launches | read GB (scaled) | written GB (scaled) |", "|---|---:|---:|---:|---:|"]
+    for k in sorted(fe, key=lambda k: -max(fe[k])):
+        if "pmn::" not in k[0]:
+            continue
+        f = sum(fe[k]) / len(fe[k]) * ff * 1024 / 1e9
+        w = sum(wr.get(k, [0.0])) / max(len(wr.get(k, [])), 1) * fw * 1024 / 1e9
+        tmd.append(f"| `{k[0]}` | {k[1]} | {len(fe[k])} | {f:.3f} | {w:.3f} |")
+    open(os.path.join(out_dir, "ep48_layer_step_hbm_traffic.md"), "w").write("\n".join(tmd) + "\n")
+    key = [k for k in fe if k[0].startswith("pmn::k_nvfp4_grouped_gemm<2>")]
+    key = max(key, key=lambda k: int(k[1]))
+    fetch = sum(fe[key]) / len(fe[key]) * ff * 1024
+    write = sum(wr[key]) / len(wr[key]) * fw * 1024
+    M, E, H, F = 65536, 48, 7168, 2048
+    alg = M * H * (0.5 + 1 / 16) + E * 2 * F * H * (0.5 + 1 / 16) + M * F * 2 + M * 2 * F * 2
+    h = hashlib.sha256(b"".join(open(os.path.join(ROOT, f), "rb").read() for f in TRAFFIC_SOURCES)).hexdigest()
+    rec = {"kernel": f"k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU> (w13 forward of the 48-expert layer step, "
+                     f"{int(key[1]) // 256} workgroups)",
+           "source_sha256": h, "sources": TRAFFIC_SOURCES, "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "traffic_bytes_per_launch": fetch + write,
+           "algorithmic_bytes_per_launch": alg,
+           "calibration": f"FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {fw:.3f} (probe copy of 1 GiB each way)",
+           "commands": [PROFILE_COMMANDS["fetch"], PROFILE_COMMANDS["write"]]}
+    json.dump(rec, open(os.path.join(out_dir, "traffic_gemm_fwd.json"), "w"), indent=1)
+
+    # clock, MFMA and VALU busy
+    rows = list(csv.DictReader(open(_find_csv(os.path.join(d, "clock"), "counter_collection.csv"))))
+    ag = defaultdict(dict)
+    for r in rows:
+        n = _kname(r["Kernel_Name"])
+        if "pmn::" not in n:
+            continue
+        v = ag[(int(r["Dispatch_Id"]), n, r["Grid_Size"])]
+        v[r["Counter_Name"]] = float(r["Counter_Value"])
+        v["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+    cmd = ["# Clock and matrix-core / VALU utilisation per kernel (48-expert layer step and workloads)", "",
+           "Command (from the repository root, one MI355X):", "", "```", PROFILE_COMMANDS["clock"], "```", "",
+           "GRBM_GUI_ACTIVE sums the 8 XCDs, so the clock is GRBM_GUI_ACTIVE / 8 / kernel time. "
+           "SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of the 1024 SIMDs, so MFMA busy = MFMA_BUSY / 1024 / "
+           "(GRBM_GUI_ACTIVE / 8) at the running clock. SQ_ACTIVE_INST_VALU counts quad-cycles issuing VALU work "
+           "(MFMA included): VALU busy = 4 x ACTIVE_INST_VALU / 1024 / (GRBM_GUI_ACTIVE / 8). Kernels under "
+           "0.02 ms are omitted.", "",
+           "| kernel | grid | ms | clock GHz | MFMA busy (at that clock) | MFMA busy vs 2.4 GHz | VALU busy |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    for k, v in sorted(ag.items()):
+        if v["dur"] < 2e-5 or "GRBM_GUI_ACTIVE" not in v:
+            continue
+        clk = v["GRBM_GUI_ACTIVE"] / 8 / v["dur"]
+        busy = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / (v["GRBM_GUI_ACTIVE"] / 8)
+        busy24 = v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / 1024 / (2.4e9 * v["dur"])
+        valu = 4 * v.get("SQ_ACTIVE_INST_VALU", 0.0) / 1024 / (v["GRBM_GUI_ACTIVE"] / 8)
+        cmd.append(f"| `{k[1]}` | {k[2]} | {v['dur'] * 1e3:.3f} | {clk / 1e9:.2f} | {busy:.2f} | {busy24:.2f} | "
+                   f"{valu:.2f} |")
+    open(os.path.join(out_dir, "ep48_layer_step_clock_mfma.md"), "w").write("\n".join(cmd) + "\n")
+    print(f"wrote profiles/ from {d}: forward w13 traffic {(fetch + write) / 1e9:.3f} GB per launch "
+          f"(algorithmic {alg / 1e9:.3f} GB)")
+
+
+# ---- the benchmark ---------------------------------------------------------------------------
+
+def _mem(nbytes, ms, mix, roofs):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    roof = roofs["hbm_gbs"][mix]["gbs"]
+    return dict(ms=ms, bytes=nbytes, gbs=gbs, frac_of_8TBs=gbs / PEAK_HBM_GBS, mix=mix, measured_roof_gbs=roof,
+                frac_of_measured_roof=gbs / roof)
+
+
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (every box here has one "
+                                   "GPU; the multi-GPU design is expert parallelism over RCCL all-to-alls)"}))
         sys.exit(2)
     import torch
 
@@ -413,15 +705,20 @@ def main():
     fl = layer.flops()
     value = fl["step"] / (ms_step * 1e-3) / 1e12
 
+    roofs = hardware_roofs(P, torch, dev)
+    f16_ceiling = roofs["mfma_tflops"][P.PROBE_MFMA_KINDS[0]]["1_wave_per_simd"]
     k13 = per_call["moe_grouped_gemm_fwd[w13+swiglu]"]
     k2 = per_call["moe_grouped_gemm_fwd[w2+rht32_s2f6]"]
     ach = fl["fwd13"] / (k13 * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": "k_nvfp4_grouped_gemm<SWIGLU> (w13 forward, fp16 MFMA after exact "
-                                           "NVFP4 dequant)",
+    roofline = {"bound": "mfma",
+                "kernel": "k_nvfp4_grouped_gemm<SWIGLU> (w13 forward: NVFP4 operands dequantized exactly to fp16, "
+                          "products on the fp16 matrix cores)",
                 "achieved": ach, "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_F16_TFLOPS,
                 "traffic": measured_traffic() if args.workload == "ep48" else None,
+                "peak_basis": "MI355X dense fp16 MFMA (2.5 PFLOP/s), the dtype this exact path computes in; "
+                              "frac_fp4_class rates the same kernel against the 10.1 PFLOP/s FP4-class peak",
                 "flops_per_launch": fl["fwd13"], "ms_per_launch": k13,
-                # the same rate against the FP4-class peak, above this exact path's own roof
+                "frac_of_measured_f16_ceiling": ach / f16_ceiling,
                 "frac_fp4_class": ach / PEAK_FP4_TFLOPS}
     kernels = {name: {"ms": ms} for name, ms in per_call.items()}
     kernels["moe_grouped_gemm_fwd[w13+swiglu]"].update(tflops=ach, frac_f16_peak=ach / PEAK_F16_TFLOPS)
@@ -432,27 +729,44 @@ def main():
         kernels[nm].update(tflops_incl_quant=t, frac_fp8_peak=t / PEAK_FP8_TFLOPS)
 
     quant = quantizer_workload(P, I, torch, dev, args.quant_iters)
-    for k in ("nvfp4_quantize", "requant_transpose_sr_mxfp8"):
-        quant[k]["frac_of_8TBs"] = quant[k]["gbs"] / PEAK_HBM_GBS
-        quant[k]["frac_of_measured_copy"] = quant[k]["gbs"] / quant["hbm_copy_gbs"]
-
     # 16 x 16 square-block NVFP4 of the w13 weights, beside the 1D weight mode of the same call
     sq = {}
     for name, mode in (("weight_1d", P.NVFP4_WEIGHT), ("weight_16x16", P.NVFP4_WEIGHT_2D)):
         for _ in range(2):
             P.nvfp4_quantize(layer.w13, mode, layer.F)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(5):
-            P.nvfp4_quantize(layer.w13, mode, layer.F)
-        e1.record()
-        torch.cuda.synchronize()
-        sq[name] = dict(ms=e0.elapsed_time(e1) / 5)
+        sq[name] = dict(ms=_time_ms(torch, lambda m=mode: P.nvfp4_quantize(layer.w13, m, layer.F), 5))
     mx8 = mxfp8_forward_workload(P, I, torch, layer, max(args.quant_iters // 4, 3))
     fp4b = fp4_backward_workload(P, torch, layer, max(args.quant_iters // 4, 3))
     comb = combine_workload(P, I, torch, dev, args.quant_iters)
-    comb["frac_of_measured_copy"] = comb["gbs"] / quant["hbm_copy_gbs"]
+
+    # memory-bound calls, each against 8 TB/s and the measured roof of its read:write mix
+    M, E, H, F = layer.M, layer.E, layer.H, layer.F
+    w13_el, w2_el = E * 2 * F * H, E * H * F
+    mem = {
+        "nvfp4_quantize[w13]": _mem(w13_el * 2.5625 + E * 2 * 4, per_call["nvfp4_quantize[w13]"],
+                                    "nvfp4_quantize", roofs),
+        "nvfp4_quantize[w2]": _mem(w2_el * 2.5625 + E * 4, per_call["nvfp4_quantize[w2]"], "nvfp4_quantize",
+                                   roofs),
+        "nvfp4_quantize[x]": _mem(layer.x.numel() * 2.5625 + layer.x.shape[0] * 4,
+                                  per_call["nvfp4_quantize[x]"], "nvfp4_quantize", roofs),
+        "nvfp4_quantize[a]": _mem(M * F * 2.5625 + M * 4, per_call["nvfp4_quantize[a]"], "nvfp4_quantize",
+                                  roofs),
+        "swiglu_bwd": _mem(M * F * 12.0, per_call["swiglu_bwd"], "swiglu_bwd", roofs),
+        "quantizer_workload.nvfp4_quantize": _mem(quant["nvfp4_quantize"]["bytes"],
+                                                  quant["nvfp4_quantize"]["us"] * 1e-3, "nvfp4_quantize", roofs),
+        "quantizer_workload.requant_transpose_sr_mxfp8": _mem(
+            quant["requant_transpose_sr_mxfp8"]["bytes"], quant["requant_transpose_sr_mxfp8"]["us"] * 1e-3,
+            "requant", roofs),
+        "combine_workload.moe_combine_s2f6": _mem(comb["bytes"], comb["us"] * 1e-3, "combine", roofs),
+    }
+    for k in ("nvfp4_quantize", "requant_transpose_sr_mxfp8"):
+        quant[k].update({kk: mem[f"quantizer_workload.{k}"][kk] for kk in
+                         ("frac_of_8TBs", "measured_roof_gbs", "frac_of_measured_roof")})
+    comb.update({kk: mem["combine_workload.moe_combine_s2f6"][kk] for kk in ("measured_roof_gbs",
+                                                                             "frac_of_measured_roof")})
+    over = [k for k, v in mem.items() if v["frac_of_measured_roof"] > 1.0]
+
+    moe32 = moe32_workload(P, I, torch, dev, args.moe32_steps) if args.moe32_steps > 0 else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -471,8 +785,10 @@ def main():
             "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "nvfp4->f16 MFMA fwd, e4m3 MFMA bwd, fp32 accumulate",
             "data": "synthetic (seeded, generated on the GPU)", "config": cfg, "roofline": roofline,
-            "cpu_baseline": cpu, "kernels": kernels, "quantizer_workload": quant, "combine_workload": comb,
-            "mxfp8_forward": mx8, "fp4_backward": fp4b, "nvfp4_w13_blocking": sq,
+            "cpu_baseline": cpu, "kernels": kernels, "memory_kernels": mem,
+            "memory_roof_check": "ok" if not over else f"above the measured roof: {over}",
+            "hw_measured": roofs, "quantizer_workload": quant, "combine_workload": comb,
+            "moe32": moe32, "mxfp8_forward": mx8, "fp4_backward": fp4b, "nvfp4_w13_blocking": sq,
             "wall_s_timed": wall}
     print(json.dumps(line))
 

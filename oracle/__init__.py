@@ -65,9 +65,13 @@ def lib():
 
 
 def threads() -> int:
-    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
-    v = os.environ.get("OMP_NUM_THREADS")
-    return int(v) if v else (os.cpu_count() or 1)
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().orc_get_threads())
+
+
+def set_threads(n: int) -> None:
+    """Set the OpenMP threads of the oracle's parallel loops (timing only; results do not change)."""
+    lib().orc_set_threads(int(n))
 
 
 P = C.c_void_p
@@ -120,6 +124,8 @@ def _declare(L):
         "orc_fp4_encode_array": (None, [P, I64, I32, P, P]),
         "orc_rand16_array": (None, [U64, U32, P, I64, P]),
         "orc_requant_window": (None, [P, P, P, I64, I64, I64, I64, I64, I32, U64, U32, P, P]),
+        "orc_set_threads": (None, [I32]),
+        "orc_get_threads": (I32, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -37,6 +37,10 @@ _SIGS = {
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
     "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
+    # measurement kernels (include/pmn_probe.h)
+    "pmn_probe_stream": (I32, [P, P, I64, I32, I32, I32, P]),
+    "pmn_probe_mfma_sink_floats": (SZ, [I32, I32]),
+    "pmn_probe_mfma": (I32, [I32, I32, I32, I32, P, P, P]),
 }
 
 ABI_FUNCTIONS = tuple(n for n in _SIGS if not n.startswith("pmn_"))
@@ -405,3 +409,31 @@ def moe_combine_s2f6(codes: torch.Tensor, e8m0: torch.Tensor, sign_mask: int, sl
     _check(_lib.moe_combine_s2f6(_ptr(codes), _ptr(e8m0), M, H, sign_mask & 0xFFFFFFFF, _ptr(slot_of), _ptr(gates),
                                  T, k, _ptr(out), _stream()), "moe_combine_s2f6")
     return out
+
+
+# ---- measurement kernels of include/pmn_probe.h ---------------------------------------------
+
+PROBE_MFMA_KINDS = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_16x16x32_f16",
+                    2: "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 3: "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)",
+                    4: "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1)"}
+
+
+def probe_stream(src: Optional[torch.Tensor], dst: Optional[torch.Tensor], units: int, read_kb: int, write_kb: int,
+                 grid: int = 8192):
+    """Stream `units` units of read_kb KB read from src and write_kb KB written to dst."""
+    if read_kb:
+        _need(src is not None and src.numel() * src.element_size() >= units * read_kb * 1024, "src too small")
+    if write_kb:
+        _need(dst is not None and dst.numel() * dst.element_size() >= units * write_kb * 1024, "dst too small")
+    _check(_lib.pmn_probe_stream(_ptr(src) if read_kb else None, _ptr(dst) if write_kb else None, units, read_kb,
+                                 write_kb, grid, _stream()), "pmn_probe_stream")
+
+
+def probe_mfma(kind: int, waves_per_simd: int, workgroups: int, iters: int, sink: torch.Tensor) -> float:
+    """Launch the MFMA throughput probe; returns the launch's FLOPs (time it on the current stream)."""
+    n = _lib.pmn_probe_mfma_sink_floats(waves_per_simd, workgroups)
+    _need(sink.dtype == torch.float32 and sink.numel() >= n, f"sink must hold {n} floats")
+    fl = C.c_double(0.0)
+    _check(_lib.pmn_probe_mfma(kind, waves_per_simd, workgroups, iters, _ptr(sink), C.byref(fl), _stream()),
+           "pmn_probe_mfma")
+    return fl.value

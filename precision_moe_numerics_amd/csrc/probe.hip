@@ -1,0 +1,152 @@
+// probe.hip -- measurement kernels: the HBM roof for a given read:write mix and the matrix-core
+// ceilings of the MFMA instructions the grouped GEMMs issue. They compute nothing of the layer;
+// the benchmark runs them in the same process as the kernels it rates, so every fraction of a
+// measured roof is taken against a roof measured on the same chip, clock and run.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pmn_probe.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One wavefront streams units of `rv` 1 KB read rows and `wv` 1 KB write rows: each 16-byte
+// load or store instruction covers 64 consecutive vectors (one contiguous KB). Loads and stores
+// are nontemporal, as in the quantizers. The stored value depends on every loaded vector so that
+// no load can be dropped.
+__global__ __launch_bounds__(256) void k_stream_mix(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                    int64_t units, int rv, int wv)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nwaves) {
+        const u32x4* s = src + u * rv * 64 + lane;
+        u32x4 acc = {(uint32_t)lane, (uint32_t)u, 0u, 0u};
+        int r = 0;
+        for (; r + 4 <= rv; r += 4) {
+            const u32x4 a = __builtin_nontemporal_load(s + (r + 0) * 64);
+            const u32x4 b = __builtin_nontemporal_load(s + (r + 1) * 64);
+            const u32x4 c = __builtin_nontemporal_load(s + (r + 2) * 64);
+            const u32x4 d = __builtin_nontemporal_load(s + (r + 3) * 64);
+            acc ^= (a ^ b) ^ (c ^ d);
+        }
+        for (; r < rv; r++) acc ^= __builtin_nontemporal_load(s + r * 64);
+        u32x4* d = dst + u * wv * 64 + lane;
+        for (int w = 0; w < wv; w++) {
+            u32x4 v = acc;
+            v.x += (uint32_t)w;
+            __builtin_nontemporal_store(v, d + w * 64);
+        }
+    }
+}
+
+// Independent accumulator chains per wavefront, constant operands, no memory traffic in the loop.
+// KIND: 0 fp16 32x32x16, 1 fp16 16x16x32, 2 E4M3 block-scaled 32x32x64, 3 E4M3 block-scaled
+// 16x16x128, 4 E2M1 block-scaled 32x32x64.
+template <int KIND>
+__global__ __launch_bounds__(512) void k_mfma_probe(float* __restrict__ sink, int iters)
+{
+    const int lane = threadIdx.x & 63;
+    f32x16 acc[8];
+    f32x4 acc4[16];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc4[i] = f32x4{};
+    f16x8 a, b;
+    i32x8 ia, ib;
+#pragma unroll
+    for (int v = 0; v < 8; v++) {
+        a[v] = (_Float16)(lane * 0.001f + v);
+        b[v] = (_Float16)(v * 0.5f);
+        ia[v] = lane * 0x01030507 + v * 0x11111111;
+        ib[v] = v * 0x07050301 + 0x22222222;
+    }
+    for (int it = 0; it < iters; it++) {
+        if (KIND == 0 || KIND == 2 || KIND == 4) {
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                if (KIND == 0) acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[i], 0, 0, 0);
+                if (KIND == 2)
+                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ia, ib, acc[i], 0, 0, 0, 127, 0, 127);
+                if (KIND == 4)
+                    acc[i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ia, ib, acc[i], 4, 4, 0, 127, 0, 127);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+                if (KIND == 1) acc4[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc4[i], 0, 0, 0);
+                if (KIND == 3)
+                    acc4[i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ia, ib, acc4[i], 0, 0, 0, 127, 0, 127);
+            }
+        }
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; i++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) s += acc[i][v];
+#pragma unroll
+    for (int i = 0; i < 16; i++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) s += acc4[i][v];
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// FLOPs one wavefront does per loop iteration of k_mfma_probe<KIND>.
+double mfma_flops_per_iter(int kind)
+{
+    switch (kind) {
+    case 0: return 8.0 * 2 * 32 * 32 * 16;
+    case 1: return 16.0 * 2 * 16 * 16 * 32;
+    case 2: return 8.0 * 2 * 32 * 32 * 64;
+    case 3: return 16.0 * 2 * 16 * 16 * 128;
+    default: return 8.0 * 2 * 32 * 32 * 64;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+int pmn_probe_stream(const void* src, void* dst, int64_t units, int read_kb, int write_kb, int grid,
+                     pmn_stream_t stream)
+{
+    if (units < 0 || read_kb < 0 || write_kb < 0 || read_kb + write_kb == 0 || grid < 1) return PMN_ESHAPE;
+    if (units == 0) return PMN_OK;
+    if ((read_kb > 0 && !src) || (write_kb > 0 && !dst)) return PMN_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return PMN_EALIGN;
+    hipLaunchKernelGGL(k_stream_mix, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), units, read_kb, write_kb);
+    return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;
+}
+
+size_t pmn_probe_mfma_sink_floats(int waves_per_simd, int workgroups)
+{
+    return (size_t)workgroups * 256 * (size_t)waves_per_simd;
+}
+
+int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, float* sink, double* flops,
+                   pmn_stream_t stream)
+{
+    if (kind < 0 || kind > 4 || !sink || !flops) return PMN_EINVAL;
+    if (waves_per_simd < 1 || waves_per_simd > 2 || workgroups < 1 || iters < 1) return PMN_ESHAPE;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 g(workgroups), b(256 * waves_per_simd);
+    switch (kind) {
+    case 0: hipLaunchKernelGGL(k_mfma_probe<0>, g, b, 0, s, sink, iters); break;
+    case 1: hipLaunchKernelGGL(k_mfma_probe<1>, g, b, 0, s, sink, iters); break;
+    case 2: hipLaunchKernelGGL(k_mfma_probe<2>, g, b, 0, s, sink, iters); break;
+    case 3: hipLaunchKernelGGL(k_mfma_probe<3>, g, b, 0, s, sink, iters); break;
+    default: hipLaunchKernelGGL(k_mfma_probe<4>, g, b, 0, s, sink, iters); break;
+    }
+    *flops = mfma_flops_per_iter(kind) * iters * 4.0 * waves_per_simd * workgroups;
+    return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;
+}
+
+}  // extern "C"

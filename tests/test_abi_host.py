@@ -7,14 +7,16 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pmn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
-                       text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?(?:int|int64_t|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                            text, flags=re.M)
     return sorted(set(names))
 
 

@@ -164,3 +164,59 @@ def test_ep48_backward_w13_sampled(layer):
                 ref.append(O.mxfp8_dot(dt, dte, xt, xte, n, k, 0, Pg))
                 got.append(float(db[g * N + n, k]))
     assert rel_fro(got, ref) <= 2e-3
+
+
+@pytest.mark.parametrize("fp4", [False, True], ids=["mxfp8", "fp4"])
+def test_ep48_backward_w2_sampled(layer, fp4):
+    """The w2 backward as the bench runs it: dY [65536 x 7168] N(0, 1e-3) (the bench's gradient),
+    the saved NVFP4 A of a synthetic Student-t(4) x 0.05 activation, contraction N = 7168 in dgrad,
+    RNG streams a = 5 (A^T), b = 3 (W2^T), dY = 6, in MXFP8 and in the FP4 variant. dA samples
+    use the oracle's own W2_g^T windows (from its quantization of W2_g in a full-size array); dW2
+    samples use its A^T windows and column-wise dY of the sampled group (sampled feature columns,
+    each column quantizes on its own). Samples take in the first and last slot of the largest and
+    the smallest group and the first and last column of both gradients."""
+    P, I, L = layer["P"], layer["I"], layer
+    M, H, F, E = L["M"], L["H"], L["F"], L["E"]
+    N, K = H, F
+    tgt = O.TARGET_E2M1 if fp4 else O.TARGET_E4M3
+    A = I.student_t((M, F), 4, 0.05, 611, DEV)
+    aq = P.nvfp4_quantize(A, P.NVFP4_ACT)
+    dy = I.moe_grad(I.EP48, M, DEV)
+    flags = P.BWD_DGRAD | P.BWD_WGRAD | (P.BWD_FP4 if fp4 else 0)
+    da, db, _ = P.moe_grouped_gemm_bwd(dy, aq, L["w2q"], L["goff"], M, N, flags=flags, seed=L["seed"],
+                                       rng_stream_a=5, rng_stream_b=3, rng_stream_dy=6)
+    off, seed = L["offsets"], L["seed"]
+    rng = np.random.default_rng(14 + fp4)
+
+    def at(t, rows, cols):
+        return npy(t[torch.as_tensor(rows, device=DEV), torch.as_tensor(cols, device=DEV)]).astype(np.float64)
+    # dgrad: da[s, k] = sum_n dq[s, n] W2_g^T[k, n] over all 7168 n
+    ij, ref = [], []
+    for g in (0, E - 1):
+        wh = oracle_quant_rows(host_bf16(L["w2"][g]), E * N, g * N, N, False)
+        wt, wte = O.requant_window(wh, g * N, N, target=tgt, seed=seed, stream=3)
+        for s in _sample_slots(off, [g], 4, rng):
+            dq, de = O.mxfp8_quantize_rows(host_bf16(dy[int(s):int(s) + 1]), target=tgt)
+            for k in (0, K - 1, int(rng.integers(0, K))):
+                ref.append(O.mxfp8_dot(dq, de, wt, wte, 0, k, 0, N, target=tgt))
+                ij.append((int(s), k))
+    got = at(da, [i for i, _ in ij], [j for _, j in ij])
+    assert rel_fro(got, ref) <= 2e-3
+    # wgrad: db[g N + n, k] = sum over the group's padded slots of dt[n, s] at[k, s]
+    ncols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 30)]))
+    ij, ref = [], []
+    for g in (0, E - 1, 20):
+        a, b = int(off[g]), int(off[g + 1])
+        dt, dte = O.mxfp8_quantize_cols(host_bf16(dy[a:b][:, torch.as_tensor(ncols, device=DEV)]), target=tgt)
+        ah = oracle_quant_rows(host_bf16(A[a:b]), M, a, 1, True)
+        xt, xte = O.requant_window(ah, a, b - a, target=tgt, seed=seed, stream=5)
+        Pg = dt.shape[1]
+        for jj, n in enumerate(ncols.tolist()):
+            for k in (0, K - 1, int(rng.integers(0, K))):
+                ref.append(O.mxfp8_dot(dt, dte, xt, xte, jj, k, 0, Pg, target=tgt))
+                ij.append((g * N + n, k))
+    got = at(db, [i for i, _ in ij], [j for _, j in ij])
+    assert rel_fro(got, ref) <= 2e-3
+    # the largest group's first and last slot rows of dA are finite and not all zero
+    edge = npy(da[torch.as_tensor([0, int(off[1]) - 1], device=DEV)])
+    assert np.all(np.isfinite(edge)) and np.any(edge[0] != 0)

@@ -352,7 +352,15 @@ def test_gemm_fwd_rht_epilogue_bit_exact(P, I):
     sc, se = P.rht32_s2f6_quantize(y, mask)
     assert torch.equal(c, sc) and torch.equal(e, se)
     ref = O.gemm_nvfp4_grouped(d["rxq"], d["rwq"], d["offsets"], N, K, gather=d["gather"])
-    assert rel_fro(decode_s2f6_rows(npy(c), npy(e), mask), ref) < 0.02
+    # per 32-chunk: the S2F6 bound ||x_hat - x||_2 <= 2^(e-127)/128 around the fp32 result, which
+    # is itself within the GEMM tolerance of the oracle's fp64 product
+    M = d["M"]
+    dec = decode_s2f6_rows(npy(c), npy(e), mask)
+    ee = npy(e).astype(np.float64)
+    err = np.sqrt(((dec - ref) ** 2).reshape(M, N // 32, 32).sum(-1))
+    nrm = np.sqrt((ref ** 2).reshape(M, N // 32, 32).sum(-1))
+    assert np.all(err <= 2.0 ** (ee - 127) / 128 * (1 + 1e-6) + 2e-3 * nrm)
+    assert rel_fro(npy(y), ref) <= 1e-5
 
 
 @pytest.mark.parametrize("sr", [False, True])
