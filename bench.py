@@ -177,8 +177,8 @@ def _time_ms(torch, fn, reps):
 
 def hardware_roofs(P, torch, dev):
     """Roofs measured in this run: the streaming kernel's HBM bandwidth for each read:write mix
-    (best of three grid sizes; 2 GiB read, or written when nothing is read, so every buffer is far
-    larger than the 256 MB Infinity Cache), torch's
+    (best of three grid sizes and the four load/store cache hints; 2 GiB read, or written when
+    nothing is read, so every buffer is far larger than the 256 MB Infinity Cache), torch's
     1 GiB device-to-device copy, and each MFMA instruction's throughput at 1 and 2 wavefronts per
     SIMD (one workgroup per compute unit). One copy launch with the grid CALIB_GRID moves exactly
     1 GiB each way: the profile summaries calibrate the PMC byte counters on it."""
@@ -188,14 +188,18 @@ def hardware_roofs(P, torch, dev):
     for name, (rv, wv) in STREAM_MIXES.items():
         units = (2 << 20) // (rv if rv else wv)          # 2 GiB read (or written)
         nbytes = units * (rv + wv) * 1024.0
-        best = 0.0
-        for grid in (1024, 4096, 16384):
-            def run(g=grid):
-                P.probe_stream(src, dst, units, rv, wv, grid=g)
-            run()
-            best = max(best, nbytes / (_time_ms(torch, run, 3) * 1e-3) / 1e9)
-        hbm[name] = dict(gbs=best, read_kb=rv, write_kb=wv)
-    P.probe_stream(src, dst, 1 << 20, 1, 1, grid=CALIB_GRID)      # the calibration copy
+        best, how = 0.0, None
+        for hints in (0, 1, 2, 3):
+            for grid in (1024, 4096, 16384):
+                def run(g=grid, h=hints):
+                    P.probe_stream(src, dst, units, rv, wv, grid=g, hints=h)
+                run()
+                gbs = nbytes / (_time_ms(torch, run, 3) * 1e-3) / 1e9
+                if gbs > best:
+                    best, how = gbs, dict(grid=grid, nontemporal_loads=bool(hints & 1),
+                                          nontemporal_stores=bool(hints & 2))
+        hbm[name] = dict(gbs=best, read_kb=rv, write_kb=wv, best_launch=how)
+    P.probe_stream(src, dst, 1 << 20, 1, 1, grid=CALIB_GRID, hints=3)      # the calibration copy
     src1, dst1 = src[: 1 << 30], dst[: 1 << 30]
     dst1.copy_(src1)
     torch_copy = 2.0 * (1 << 30) / (_time_ms(torch, lambda: dst1.copy_(src1), 3) * 1e-3) / 1e9
@@ -216,55 +220,48 @@ def hardware_roofs(P, torch, dev):
             mfma.setdefault(name, {})[f"{wps}_wave_per_simd"] = fl[0] / (ms * 1e-3) / 1e12
     del sink
     return dict(hbm_gbs=hbm, torch_copy_gbs=torch_copy, mfma_tflops=mfma,
-                note="streaming kernel: nontemporal 16-byte loads/stores, one contiguous KB per instruction; "
+                note="streaming kernel: 16-byte loads/stores, one contiguous KB per instruction, best of "
+                     "ordinary and nontemporal accesses; "
                      "MFMA: independent accumulator chains on constant operands, no memory traffic")
 
 
 def quantizer_workload(P, I, torch, dev, iters):
     """GB/s of nvfp4_quantize (4/6, per-token outer) and requant_transpose_sr_mxfp8 on the
-    8192 x 7168 activation workload, rotating inputs so the Infinity Cache cannot serve them."""
+    8192 x 7168 activation workload. Inputs and outputs both rotate over buffer sets larger than the
+    256 MB Infinity Cache, so neither the reads nor the writes can be served or absorbed by it."""
     R, Cc = 8192, 7168
     base = I.quantizer(dev)
     nbuf = 4
     xs = [base["x"]] + [base["x"].roll(shifts=97 * i, dims=1).contiguous() for i in range(1, nbuf)]
-    qs = [P.nvfp4_quantize(x, P.NVFP4_ACT) for x in xs]
     nq = 12
-    qs = [qs[i % nbuf] for i in range(nq)]
-    qbuf = []
-    for i in range(nq):     # distinct copies of the quantized tensors (> 256 MB in total)
-        q = qs[i]
-        qbuf.append(P.NVFP4(q.codes.clone(), q.scales.clone(), q.outer.clone(), q.rows_per_outer))
+    qbuf = [P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT) for i in range(nq)]   # 12 x 33 MB of outputs
     ld = P.padded_bound(R, 0)
-    out = torch.empty((Cc, ld), dtype=torch.uint8, device=dev)
-    oe = torch.empty((Cc, ld // 32), dtype=torch.uint8, device=dev)
+    nr = 8
+    outs = [(torch.empty((Cc, ld), dtype=torch.uint8, device=dev),
+             torch.empty((Cc, ld // 32), dtype=torch.uint8, device=dev)) for _ in range(nr)]   # 8 x 61 MB
     torch.cuda.synchronize()
     res = {}
-    # nvfp4_quantize
-    for i in range(3):
-        P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(iters):
-        P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    it = [0]
+
+    def quant():
+        i = it[0]
+        it[0] += 1
+        P.nvfp4_quantize(xs[i % nbuf], P.NVFP4_ACT, out=qbuf[i % nq])
+    for _ in range(3):
+        quant()
+    ms = _time_ms(torch, quant, iters)
     nbytes = R * Cc * (2 + 0.5 + 1 / 16) + R * 4
     res["nvfp4_quantize"] = dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
-    # requant
-    def rq(q):
-        P.requant_transpose_sr_mxfp8(q, seed=base["seed"], rng_stream=base["stream"], ld=ld, out=out, out_e8m0=oe)
 
-    for i in range(3):
-        rq(qbuf[i])
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(iters):
-        rq(qbuf[i % nq])
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    def rq():
+        i = it[0]
+        it[0] += 1
+        o, oe = outs[i % nr]
+        P.requant_transpose_sr_mxfp8(qbuf[i % nq], seed=base["seed"], rng_stream=base["stream"], ld=ld, out=o,
+                                     out_e8m0=oe)
+    for _ in range(3):
+        rq()
+    ms = _time_ms(torch, rq, iters)
     nbytes = R * Cc * (0.5 + 1 / 16 + 1 + 1 / 32) + R * 4
     res["requant_transpose_sr_mxfp8"] = dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9)
     return res
@@ -273,7 +270,8 @@ def quantizer_workload(P, I, torch, dev, iters):
 def combine_workload(P, I, torch, dev, iters):
     """GB/s of moe_combine_s2f6 on the routed shape (16384 tokens, top-8 of 32 experts, 131072 slot
     rows of hidden 4096): routing on the device from the seeded logits, two S2F6 payloads of
-    553 MB each used in turn so the Infinity Cache cannot serve them."""
+    553 MB each used in turn and four 134 MB outputs in turn, so the Infinity Cache can neither
+    serve the reads nor absorb the writes."""
     sh = I.MOE32
     T, k, H = sh.tokens, sh.top_k, sh.hidden
     M = T * k
@@ -281,21 +279,19 @@ def combine_workload(P, I, torch, dev, iters):
     so, gates = r["slot_of"], r["gates"]
     mask = I.sign_mask(sh.seeds["rht"])
     pay = [I.s2f6_payload(M, H, sh.seeds["payload"] + i, dev) for i in range(2)]
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    torch.cuda.synchronize()
-    for i in range(3):
-        P.moe_combine_s2f6(*pay[i % 2], mask, so, gates, out=out)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(iters):
-        P.moe_combine_s2f6(*pay[i % 2], mask, so, gates, out=out)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
+    outs = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    it = [0]
+
+    def run():
+        i = it[0]
+        it[0] += 1
+        P.moe_combine_s2f6(*pay[i % 2], mask, so, gates, out=outs[i % 4])
+    for _ in range(3):
+        run()
+    ms = _time_ms(torch, run, iters)
     # per token: k rows of H codes + H/32 E8M0 bytes, k slot indices and gates; H bf16 out
     nbytes = T * (k * (H + H // 32) + 8 * k + 2 * H)
-    del pay
+    del pay, outs
     return dict(us=ms * 1e3, bytes=nbytes, gbs=nbytes / (ms * 1e-3) / 1e9, tokens=T, top_k=k, hidden=H,
                 slots=M, frac_of_8TBs=nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS)
 
@@ -515,7 +511,9 @@ TRAFFIC_SOURCES = ["precision_moe_numerics_amd/csrc/gemm_fwd.hip", "precision_mo
 
 
 def _kname(n):
-    return n.split("(")[0].replace("void ", "").strip()
+    n = n.replace("(anonymous namespace)::", "").strip()
+    n = n[5:] if n.startswith("void ") else n
+    return n.split("(")[0].strip()
 
 
 def _find_csv(d, suffix):

@@ -20,11 +20,12 @@ extern "C" {
 /*
  * Streams `units` units through HBM. A unit reads read_kb contiguous KB of src and writes
  * write_kb contiguous KB of dst (src holds units * read_kb KB, dst units * write_kb KB; both
- * 16-byte aligned). Every load and store is a nontemporal 16-byte access and one wavefront
- * handles one unit at a time; `grid` workgroups of 256 threads stride over the units. The written
- * bytes are a function of every byte read. read_kb + write_kb > 0 (PMN_ESHAPE).
+ * 16-byte aligned). Every access is 16 bytes wide and one wavefront handles one unit at a time;
+ * `grid` workgroups of 256 threads stride over the units. hints: bit 0 = nontemporal loads, bit 1
+ * = nontemporal stores (0..3, else PMN_EINVAL). The written bytes are a function of every byte
+ * read. read_kb + write_kb > 0 (PMN_ESHAPE).
  */
-int pmn_probe_stream(const void* src, void* dst, int64_t units, int read_kb, int write_kb, int grid,
+int pmn_probe_stream(const void* src, void* dst, int64_t units, int read_kb, int write_kb, int grid, int hints,
                      pmn_stream_t stream);
 
 /* Floats pmn_probe_mfma writes to `sink` (one per thread of the launch). */

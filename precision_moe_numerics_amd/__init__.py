@@ -38,7 +38,7 @@ _SIGS = {
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
     "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
     # measurement kernels (include/pmn_probe.h)
-    "pmn_probe_stream": (I32, [P, P, I64, I32, I32, I32, P]),
+    "pmn_probe_stream": (I32, [P, P, I64, I32, I32, I32, I32, P]),
     "pmn_probe_mfma_sink_floats": (SZ, [I32, I32]),
     "pmn_probe_mfma": (I32, [I32, I32, I32, I32, P, P, P]),
 }
@@ -145,13 +145,21 @@ class NVFP4:
 
 
 def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int = 1,
-                   outer_in: Optional[torch.Tensor] = None) -> NVFP4:
+                   outer_in: Optional[torch.Tensor] = None, out: Optional[NVFP4] = None) -> NVFP4:
+    """NVFP4 of x; `out` (optional) supplies the output tensors to write into."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [rows, cols]")
     R, Cc = x.shape
     dev = x.device
-    codes = torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev)
-    outer = torch.empty((max(R // max(rows_per_outer, 1), 0),), dtype=torch.float32, device=dev)
+    n_outer = max(R // max(rows_per_outer, 1), 0)
+    if out is None:
+        codes = torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev)
+        outer = torch.empty((n_outer,), dtype=torch.float32, device=dev)
+    else:
+        codes, scales, outer = out.codes, out.scales, out.outer
+        _tensor(codes, (R, Cc // 2), torch.uint8, "out.codes")
+        _tensor(scales, (R, Cc // 16), torch.uint8, "out.scales")
+        _tensor(outer, (n_outer,), torch.float32, "out.outer")
     _check(_lib.nvfp4_quantize(_ptr(x), R, Cc, mode, rows_per_outer, _ptr(outer_in), _ptr(codes), _ptr(scales),
                                _ptr(outer), _stream()), "nvfp4_quantize")
     return NVFP4(codes, scales, outer, rows_per_outer)
@@ -419,14 +427,15 @@ PROBE_MFMA_KINDS = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_16x16x32_f16",
 
 
 def probe_stream(src: Optional[torch.Tensor], dst: Optional[torch.Tensor], units: int, read_kb: int, write_kb: int,
-                 grid: int = 8192):
-    """Stream `units` units of read_kb KB read from src and write_kb KB written to dst."""
+                 grid: int = 8192, hints: int = 3):
+    """Stream `units` units of read_kb KB read from src and write_kb KB written to dst (hints: bit 0
+    nontemporal loads, bit 1 nontemporal stores)."""
     if read_kb:
         _need(src is not None and src.numel() * src.element_size() >= units * read_kb * 1024, "src too small")
     if write_kb:
         _need(dst is not None and dst.numel() * dst.element_size() >= units * write_kb * 1024, "dst too small")
     _check(_lib.pmn_probe_stream(_ptr(src) if read_kb else None, _ptr(dst) if write_kb else None, units, read_kb,
-                                 write_kb, grid, _stream()), "pmn_probe_stream")
+                                 write_kb, grid, hints, _stream()), "pmn_probe_stream")
 
 
 def probe_mfma(kind: int, waves_per_simd: int, workgroups: int, iters: int, sink: torch.Tensor) -> float:

@@ -16,31 +16,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One wavefront streams units of `rv` 1 KB read rows and `wv` 1 KB write rows: each 16-byte
-// load or store instruction covers 64 consecutive vectors (one contiguous KB). Loads and stores
-// are nontemporal, as in the quantizers. The stored value depends on every loaded vector so that
-// no load can be dropped.
+// load or store instruction covers 64 consecutive vectors (one contiguous KB). NT_LOAD / NT_STORE
+// choose nontemporal or ordinary accesses. The stored value depends on every loaded vector so
+// that no load can be dropped.
+template <bool NT_LOAD, bool NT_STORE>
 __global__ __launch_bounds__(256) void k_stream_mix(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                     int64_t units, int rv, int wv)
 {
     const int lane = threadIdx.x & 63;
     const int64_t nwaves = (int64_t)gridDim.x * 4;
+    auto ld = [](const u32x4* p) { return NT_LOAD ? __builtin_nontemporal_load(p) : *p; };
     for (int64_t u = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nwaves) {
         const u32x4* s = src + u * rv * 64 + lane;
         u32x4 acc = {(uint32_t)lane, (uint32_t)u, 0u, 0u};
         int r = 0;
-        for (; r + 4 <= rv; r += 4) {
-            const u32x4 a = __builtin_nontemporal_load(s + (r + 0) * 64);
-            const u32x4 b = __builtin_nontemporal_load(s + (r + 1) * 64);
-            const u32x4 c = __builtin_nontemporal_load(s + (r + 2) * 64);
-            const u32x4 d = __builtin_nontemporal_load(s + (r + 3) * 64);
-            acc ^= (a ^ b) ^ (c ^ d);
+        for (; r + 8 <= rv; r += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) v[i] = ld(s + (r + i) * 64);
+            acc ^= ((v[0] ^ v[1]) ^ (v[2] ^ v[3])) ^ ((v[4] ^ v[5]) ^ (v[6] ^ v[7]));
         }
-        for (; r < rv; r++) acc ^= __builtin_nontemporal_load(s + r * 64);
+        for (; r < rv; r++) acc ^= ld(s + r * 64);
         u32x4* d = dst + u * wv * 64 + lane;
         for (int w = 0; w < wv; w++) {
             u32x4 v = acc;
             v.x += (uint32_t)w;
-            __builtin_nontemporal_store(v, d + w * 64);
+            if (NT_STORE)
+                __builtin_nontemporal_store(v, d + w * 64);
+            else
+                d[w * 64] = v;
         }
     }
 }
@@ -114,15 +118,23 @@ double mfma_flops_per_iter(int kind)
 
 extern "C" {
 
-int pmn_probe_stream(const void* src, void* dst, int64_t units, int read_kb, int write_kb, int grid,
+int pmn_probe_stream(const void* src, void* dst, int64_t units, int read_kb, int write_kb, int grid, int hints,
                      pmn_stream_t stream)
 {
+    if (hints < 0 || hints > 3) return PMN_EINVAL;
     if (units < 0 || read_kb < 0 || write_kb < 0 || read_kb + write_kb == 0 || grid < 1) return PMN_ESHAPE;
     if (units == 0) return PMN_OK;
     if ((read_kb > 0 && !src) || (write_kb > 0 && !dst)) return PMN_EINVAL;
     if ((reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(dst) & 15)) return PMN_EALIGN;
-    hipLaunchKernelGGL(k_stream_mix, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), units, read_kb, write_kb);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const u32x4* a = static_cast<const u32x4*>(src);
+    u32x4* b = static_cast<u32x4*>(dst);
+    switch (hints) {
+    case 0: hipLaunchKernelGGL((k_stream_mix<false, false>), dim3(grid), dim3(256), 0, s, a, b, units, read_kb, write_kb); break;
+    case 1: hipLaunchKernelGGL((k_stream_mix<true, false>), dim3(grid), dim3(256), 0, s, a, b, units, read_kb, write_kb); break;
+    case 2: hipLaunchKernelGGL((k_stream_mix<false, true>), dim3(grid), dim3(256), 0, s, a, b, units, read_kb, write_kb); break;
+    default: hipLaunchKernelGGL((k_stream_mix<true, true>), dim3(grid), dim3(256), 0, s, a, b, units, read_kb, write_kb); break;
+    }
     return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;
 }
 
