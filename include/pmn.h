@@ -70,6 +70,7 @@ typedef void* pmn_stream_t; /* hipStream_t */
 #define PMN_EALIGN     -3  /* a pointer is not aligned as the call requires (16 bytes) */
 #define PMN_EWORKSPACE -4  /* the workspace is missing or smaller than *_workspace_size() */
 #define PMN_ELAUNCH    -5  /* the HIP runtime refused a launch (hipGetLastError after launch) */
+#define PMN_ESCRATCH   -6  /* the sizes need more than the static scratch of moe_grouped_gemm_bwd_noalloc */
 
 /* Text for a status code (static storage, never NULL). */
 const char* pmn_strerror(int status);
@@ -291,6 +292,27 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b,
                          uint32_t rng_stream_dy, float* da, float* db, void* workspace,
                          size_t workspace_bytes, pmn_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): moe_grouped_gemm_bwd with its workspace taken from a static
+ * device array of the library, PMN_NOALLOC_SCRATCH_BYTES per device, held by each device the
+ * library runs on until the process ends. Arguments, results and errors are those of
+ * moe_grouped_gemm_bwd without the workspace; sizes whose workspace
+ * (moe_grouped_gemm_bwd_workspace_size) exceeds the array return PMN_ESCRATCH and launch nothing.
+ * The call allocates and frees nothing. Every call on a device uses that device's one array, which
+ * keeps the last call's contents (nothing in it needs to start at zero): calls that overlap on one
+ * device (concurrent streams, several host threads) race and must be serialized by the caller.
+ */
+#define PMN_NOALLOC_SCRATCH_BYTES (256ull << 20)
+size_t pmn_noalloc_scratch_bytes(void);
+int moe_grouped_gemm_bwd_noalloc(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* a_outer, int64_t a_rows, int64_t a_rows_per_outer,
+                                 const int32_t* gather, const uint8_t* b_codes, const uint8_t* b_scales,
+                                 const float* b_outer, int64_t b_rows_per_outer, const int64_t* offsets, int G,
+                                 int64_t M, int64_t N, int64_t K, int flags, int dy_rounding, uint64_t seed,
+                                 uint32_t rng_stream_a, uint32_t rng_stream_b, uint32_t rng_stream_dy, float* da,
+                                 float* db, pmn_stream_t stream);
 
 /*
  * SwiGLU backward (the layer's activation between w1/w3 and w2): da fp32 [M x F] and the saved

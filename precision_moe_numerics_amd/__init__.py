@@ -37,6 +37,9 @@ _SIGS = {
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
     "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
+    "pmn_noalloc_scratch_bytes": (SZ, []),
+    "moe_grouped_gemm_bwd_noalloc": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32,
+                                           U64, U32, U32, U32, P, P, P]),
     # measurement kernels (include/pmn_probe.h)
     "pmn_probe_stream": (I32, [P, P, I64, I32, I32, I32, I32, P]),
     "pmn_probe_mfma_sink_floats": (SZ, [I32, I32]),
@@ -354,6 +357,37 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
                                      rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da), _ptr(db),
                                      _ptr(workspace), workspace.numel(), _stream()), "moe_grouped_gemm_bwd")
     return da, db, workspace
+
+
+def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", offsets: torch.Tensor, M: int, N: int,
+                                 flags: int = BWD_DGRAD | BWD_WGRAD, gather: Optional[torch.Tensor] = None,
+                                 dy_rounding: int = RNE, seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
+                                 rng_stream_dy: int = 3, da=None, db=None):
+    """moe_grouped_gemm_bwd with the library's static scratch as its workspace (no workspace
+    argument; the C call allocates nothing). Returns (da or None, db or None)."""
+    K = xq.cols
+    G = offsets.numel() - 1
+    dev = dy.device
+    _tensor(dy, (M, N), torch.bfloat16, "dy")
+    _nvfp4(xq, "xq")
+    _nvfp4(wq, "wq")
+    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    _index(offsets, G + 1, torch.int64, "offsets")
+    _index(gather, M, torch.int32, "gather")
+    if da is None and flags & BWD_DGRAD:
+        da = torch.empty((M, K), dtype=torch.float32, device=dev)
+    if db is None and flags & BWD_WGRAD:
+        db = torch.empty((G * N, K), dtype=torch.float32, device=dev)
+    if flags & BWD_DGRAD:
+        _tensor(da, (M, K), torch.float32, "da")
+    if flags & BWD_WGRAD:
+        _tensor(db, (G * N, K), torch.float32, "db")
+    _check(_lib.moe_grouped_gemm_bwd_noalloc(_ptr(dy), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows,
+                                             xq.rows_per_outer, _ptr(gather), _ptr(wq.codes), _ptr(wq.scales),
+                                             _ptr(wq.outer), wq.rows_per_outer, _ptr(offsets), G, M, N, K, flags,
+                                             dy_rounding, seed, rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da),
+                                             _ptr(db), _stream()), "moe_grouped_gemm_bwd_noalloc")
+    return da, db
 
 
 def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int, fp4: bool = False):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpmn.so")
-SOURCES = ["abi.hip", "quant.hip", "requant.hip", "gemm_fwd.hip", "gemm_bwd.hip", "route.hip", "combine.hip", "probe.hip"]
+SOURCES = ["abi.hip", "quant.hip", "requant.hip", "gemm_fwd.hip", "gemm_bwd.hip", "route.hip", "combine.hip", "probe.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

@@ -69,6 +69,74 @@ FwdMx8Layout fwd_mx8_layout(int64_t M, int G, int64_t N, int64_t K)
 
 }  // namespace
 
+namespace pmn {
+
+int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                         int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
+                         const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
+                         const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
+                         uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, uint32_t rng_stream_dy,
+                         float* da, float* db, void* workspace, size_t workspace_bytes, pmn_stream_t stream,
+                         size_t* workspace_needed)
+{
+    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
+        return PMN_EINVAL;
+    if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
+    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
+    if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
+    if (!gather && M > a_rows) return PMN_ESHAPE;
+    // with no slots (M == 0) dy, da and the activations may be null: dgrad has no rows and
+    // wgrad writes zero gradients
+    if (!offsets || (M > 0 && !dy)) return PMN_EINVAL;
+    const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
+    if (dgrad && (!b_codes || !b_scales || !b_outer || (M > 0 && !da))) return PMN_EINVAL;
+    if (wgrad && (!db || (M > 0 && (!a_codes || !a_scales || !a_outer)))) return PMN_EINVAL;
+    const bool fp4 = flags & PMN_BWD_FP4;
+    const BwdLayout L = bwd_layout(M, G, N, K, fp4);
+    if (workspace_needed) {
+        // the caller supplies the workspace once it knows the size (the scratch-free entry point)
+        *workspace_needed = L.total;
+        return PMN_OK;
+    }
+    if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
+    if (!aligned(workspace, 16) || !aligned(dy, 16) || (da && !aligned(da, 16)) || (db && !aligned(db, 16)) ||
+        (a_codes && !aligned(a_codes, 16)) || (b_codes && !aligned(b_codes, 16)))
+        return PMN_EALIGN;
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const hipStream_t s = hs(stream);
+    const bool sr = dy_rounding == PMN_SR;
+    const bool blocked = true;
+    const int target = fp4 ? pmn::TARGET_E2M1_PACKED : PMN_TARGET_E4M3;
+    int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
+    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, pmn::blocked_unit(fp4));
+    if (e != hipSuccess) return PMN_ELAUNCH;
+    if (dgrad && M > 0) {
+        e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
+                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
+                                0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true, nullptr,
+                                s, blocked);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
+                                    s, fp4);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+    }
+    if (wgrad) {
+        e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
+                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target, blocked);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G, target, seed,
+                                rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s, blocked);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+        e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s, fp4);
+        if (e != hipSuccess) return PMN_ELAUNCH;
+    }
+    return PMN_OK;
+}
+
+}  // namespace pmn
+
 extern "C" {
 
 const char* pmn_strerror(int s)
@@ -80,6 +148,7 @@ const char* pmn_strerror(int s)
     case PMN_EALIGN: return "pointer not aligned as required";
     case PMN_EWORKSPACE: return "workspace missing or too small";
     case PMN_ELAUNCH: return "kernel launch failed";
+    case PMN_ESCRATCH: return "the sizes need more scratch than the library's static scratch array holds";
     default: return "unknown status";
     }
 }
@@ -204,55 +273,10 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          uint32_t rng_stream_dy, float* da, float* db, void* workspace,
                          size_t workspace_bytes, pmn_stream_t stream)
 {
-    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
-        return PMN_EINVAL;
-    if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
-    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
-    if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
-    if (!gather && M > a_rows) return PMN_ESHAPE;
-    // with no slots (M == 0) dy, da and the activations may be null: dgrad has no rows and
-    // wgrad writes zero gradients
-    if (!offsets || (M > 0 && !dy)) return PMN_EINVAL;
-    const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
-    if (dgrad && (!b_codes || !b_scales || !b_outer || (M > 0 && !da))) return PMN_EINVAL;
-    if (wgrad && (!db || (M > 0 && (!a_codes || !a_scales || !a_outer)))) return PMN_EINVAL;
-    const bool fp4 = flags & PMN_BWD_FP4;
-    const BwdLayout L = bwd_layout(M, G, N, K, fp4);
-    if (!workspace || workspace_bytes < L.total) return PMN_EWORKSPACE;
-    if (!aligned(workspace, 16) || !aligned(dy, 16) || (da && !aligned(da, 16)) || (db && !aligned(db, 16)) ||
-        (a_codes && !aligned(a_codes, 16)) || (b_codes && !aligned(b_codes, 16)))
-        return PMN_EALIGN;
-    uint8_t* ws = static_cast<uint8_t*>(workspace);
-    const hipStream_t s = hs(stream);
-    const bool sr = dy_rounding == PMN_SR;
-    const bool blocked = true;
-    const int target = fp4 ? pmn::TARGET_E2M1_PACKED : PMN_TARGET_E4M3;
-    int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
-    hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, pmn::blocked_unit(fp4));
-    if (e != hipSuccess) return PMN_ELAUNCH;
-    if (dgrad && M > 0) {
-        e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
-                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
-                                0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true, nullptr,
-                                s, blocked);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
-                                    s, fp4);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-    }
-    if (wgrad) {
-        e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
-                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target, blocked);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G, target, seed,
-                                rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s, blocked);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_mxfp8_wgrad(ws + L.dt, ws + L.dte, ws + L.xt, ws + L.xte, L.Pb, po, G, N, K, db, s, fp4);
-        if (e != hipSuccess) return PMN_ELAUNCH;
-    }
-    return PMN_OK;
+    return pmn::grouped_gemm_bwd_run(dy, a_codes, a_scales, a_outer, a_rows, a_rows_per_outer, gather, b_codes,
+                                     b_scales, b_outer, b_rows_per_outer, offsets, G, M, N, K, flags, dy_rounding,
+                                     seed, rng_stream_a, rng_stream_b, rng_stream_dy, da, db, workspace,
+                                     workspace_bytes, stream, nullptr);
 }
 
 size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, int64_t K)

@@ -92,4 +92,15 @@ hipError_t launch_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t
                                const int32_t* slot_of, const float* gates, int64_t T, int k, uint16_t* out,
                                hipStream_t stream);
 
+// The whole moe_grouped_gemm_bwd call (argument checks, workspace layout, launches) on a given
+// workspace. With workspace_needed non-null it only checks the arguments and stores the workspace
+// bytes the sizes need (nothing is launched).
+int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
+                         int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
+                         const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
+                         const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
+                         uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, uint32_t rng_stream_dy,
+                         float* da, float* db, void* workspace, size_t workspace_bytes, pmn_stream_t stream,
+                         size_t* workspace_needed);
+
 }  // namespace pmn

@@ -137,3 +137,19 @@ def test_binding_refuses_mismatched_tensors_on_the_host():
     for call, what in cases:
         with pytest.raises(P.PmnError, match=what):
             call()
+
+
+def test_noalloc_entry_rejects_sizes_beyond_its_scratch_on_the_host(lib):
+    """moe_grouped_gemm_bwd_noalloc checks its sizes against the static scratch before touching the
+    device: the 48-expert w2 backward (far above 256 MiB of workspace) returns PMN_ESCRATCH."""
+    fake = C.c_void_p(0x1000)     # never dereferenced
+    M, G, N, K = 65536, 48, 7168, 2048
+    lib.moe_grouped_gemm_bwd_noalloc.restype = C.c_int
+    assert lib.pmn_noalloc_scratch_bytes() == 256 << 20
+    assert lib.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, 3) > 256 << 20
+    st = lib.moe_grouped_gemm_bwd_noalloc(fake, fake, fake, fake, M, 1, None, fake, fake, fake, N, fake, G, M, N, K,
+                                          3, 0, 0, 1, 2, 3, fake, fake, None)
+    assert st == -6 and b"scratch" in lib.pmn_strerror(st)
+    # argument errors come first, as in moe_grouped_gemm_bwd
+    assert lib.moe_grouped_gemm_bwd_noalloc(fake, fake, fake, fake, 64, 1, None, fake, fake, fake, 256, fake, 1, 64,
+                                            250, 256, 3, 0, 0, 1, 2, 3, fake, fake, None) == -2
