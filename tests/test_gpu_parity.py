@@ -78,6 +78,23 @@ def test_nvfp4_quantize_weight_groups(P, I, rpo):
     assert_nvfp4_equal(q, ref)
 
 
+@pytest.mark.parametrize("four_six", [False, True])
+def test_nvfp4_large_weight_groups(P, I, four_six):
+    """13 groups of 2048 x 7168 (29.4 MB of bf16 each, the size of one expert's w1 or w3): the
+    group amax pass spreads each group over many workgroups that fold into one atomic max, so a
+    group whose amax is one isolated value checks the fold. Sampled groups, bit-exact."""
+    G, R, Cc = 13, 2048, 7168
+    w = I.normal((G * R, Cc), 0.02, 31, DEV)
+    w[4 * R + 17, 5] = 0.75                              # a group whose amax is an isolated outlier
+    q = P.nvfp4_quantize(w, P.NVFP4_ACT if four_six else P.NVFP4_WEIGHT, rows_per_outer=R)
+    codes, scales, outer = npy(q.codes), npy(q.scales), npy(q.outer)
+    for g in (0, 4, 5, 9, 10, 12):
+        ref = O.nvfp4_quantize(w[g * R:(g + 1) * R].cpu(), R, four_six)
+        assert np.array_equal(scales[g * R:(g + 1) * R], ref["scales"]), g
+        assert np.array_equal(codes[g * R:(g + 1) * R], ref["codes"]), g
+        assert outer[g] == ref["outer"][0], g
+
+
 def test_nvfp4_worked_example_with_outer_hook(P):
     x = np.zeros((1, 16), np.float32)
     x[0, :5] = [-54.0, 5.4, 1.0, -2.0, 0.3]
