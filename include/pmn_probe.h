@@ -43,6 +43,15 @@ size_t pmn_probe_mfma_sink_floats(int waves_per_simd, int workgroups);
 int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, float* sink, double* flops,
                    pmn_stream_t stream);
 
+/*
+ * Verification of the activation quantizer's division-free reciprocal: adds to *mismatches (a
+ * device counter the caller zeroes) the number of fp32 values d whose bit patterns lie in
+ * [first_bits, last_bits] for which that reciprocal differs in any bit from the IEEE quotient
+ * 1.0f / d. first_bits <= last_bits (PMN_ESHAPE).
+ */
+int pmn_probe_recip_check(uint32_t first_bits, uint32_t last_bits, unsigned long long* mismatches,
+                          pmn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ _SIGS = {
     "pmn_probe_stream": (I32, [P, P, I64, I32, I32, I32, I32, P]),
     "pmn_probe_mfma_sink_floats": (SZ, [I32, I32]),
     "pmn_probe_mfma": (I32, [I32, I32, I32, I32, P, P, P]),
+    "pmn_probe_recip_check": (I32, [U32, U32, P, P]),
 }
 
 ABI_FUNCTIONS = tuple(n for n in _SIGS if not n.startswith("pmn_"))
@@ -480,3 +481,11 @@ def probe_mfma(kind: int, waves_per_simd: int, workgroups: int, iters: int, sink
     _check(_lib.pmn_probe_mfma(kind, waves_per_simd, workgroups, iters, _ptr(sink), C.byref(fl), _stream()),
            "pmn_probe_mfma")
     return fl.value
+
+
+def probe_recip_check(first_bits: int, last_bits: int) -> int:
+    """Number of fp32 values with bit patterns in [first_bits, last_bits] whose division-free
+    reciprocal (the activation quantizer's) differs from the IEEE quotient 1/d."""
+    count = torch.zeros(1, dtype=torch.int64, device=torch.device("cuda", torch.cuda.current_device()))
+    _check(_lib.pmn_probe_recip_check(first_bits, last_bits, _ptr(count), _stream()), "pmn_probe_recip_check")
+    return int(count.item())

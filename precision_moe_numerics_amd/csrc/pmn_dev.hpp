@@ -74,6 +74,42 @@ PMN_DEV uint32_t e4m3_rne_sat(float t)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(t, t, 0, false) & 0xFFu;
 }
 
+// ---- correctly rounded quotients without a division sequence ------------------------------
+//
+// The activation quantizer needs RN(ab / 6), RN(q / s_o) and RN(1 / d) per 16-value block. The
+// IEEE division sequence costs about ten instructions each; these replacements give the same
+// bits on the domains where the quantizer uses them, which are finite and were checked
+// exhaustively (the first two with IEEE fp32 arithmetic on the host, the third on the device).
+
+// RN(a / 6) for every non-negative bf16 value a (widened to fp32): one product by RN(1/6) and one
+// correction with the exact fma residual.
+PMN_DEV float div6_rn(float a)
+{
+    const float y = 0x1.555556p-3f;   // RN(1/6)
+    const float q = a * y;
+    const float r = __builtin_fmaf(-q, 6.0f, a);
+    return __builtin_fmaf(r, y, q);
+}
+
+// RN(q / s) given ys = RN(1 / s): one product and one fma correction. Exact whenever
+// s = RN(A / 2688) >= 2^-96 for a bf16 amax A and q = RN(ab / 6) or ab / 4 for a bf16 block max
+// ab <= A, except where the quotient is below 2^-11 (both results then encode as E4M3 zero).
+PMN_DEV float div_rn(float q, float s, float ys)
+{
+    const float t = q * ys;
+    const float r = __builtin_fmaf(-t, s, q);
+    return __builtin_fmaf(r, ys, t);
+}
+
+// RN(1 / d) for every fp32 d in [2^-105, 2^126): the hardware reciprocal (within one ulp) and one
+// Newton step with the exact fma residual.
+PMN_DEV float recip_rn(float d)
+{
+    const float y = __builtin_amdgcn_rcpf(d);
+    const float e = __builtin_fmaf(-d, y, 1.0f);
+    return __builtin_fmaf(e, y, y);
+}
+
 // ---- FP4 ----------------------------------------------------------------------------------
 
 // Two fp32 values -> one byte of two FP4 nibbles (a low, b high), placed at byte `sel` of old.

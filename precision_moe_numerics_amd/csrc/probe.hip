@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pmn_dev.hpp"
 #include "pmn_probe.h"
 
 namespace {
@@ -114,6 +115,21 @@ double mfma_flops_per_iter(int kind)
     }
 }
 
+// Counts the fp32 values d with bit patterns in [first, last] for which the quantizer's reciprocal
+// recip_rn(d) differs from the IEEE quotient 1.0f / d.
+__global__ __launch_bounds__(256) void k_recip_check(uint32_t first, uint32_t last,
+                                                     unsigned long long* __restrict__ mismatches)
+{
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    unsigned long long bad = 0;
+    for (uint64_t u = (uint64_t)first + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; u <= last; u += stride) {
+        const float d = __uint_as_float((uint32_t)u);
+        const float ieee = 1.0f / d;
+        bad += __float_as_uint(pmn::recip_rn(d)) != __float_as_uint(ieee) ? 1u : 0u;
+    }
+    if (bad) atomicAdd(mismatches, bad);
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +174,16 @@ int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, floa
     default: hipLaunchKernelGGL(k_mfma_probe<4>, g, b, 0, s, sink, iters); break;
     }
     *flops = mfma_flops_per_iter(kind) * iters * 4.0 * waves_per_simd * workgroups;
+    return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;
+}
+
+int pmn_probe_recip_check(uint32_t first_bits, uint32_t last_bits, unsigned long long* mismatches,
+                          pmn_stream_t stream)
+{
+    if (!mismatches) return PMN_EINVAL;
+    if (first_bits > last_bits) return PMN_ESHAPE;
+    hipLaunchKernelGGL(k_recip_check, dim3(8192), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), first_bits,
+                       last_bits, mismatches);
     return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;
 }
 

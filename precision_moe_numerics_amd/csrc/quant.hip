@@ -42,15 +42,21 @@ PMN_DEV float block_absmax(const Block16& b)
     return m;
 }
 
-// One candidate: scale byte, 16 nibbles (2 words) and the effective scale d.
-template <int CAND>
+// One candidate: scale byte, 16 nibbles (2 words) and the effective scale d. FAST (rows whose
+// outer scale s_o >= 2^-96, with ys = RN(1 / s_o)) forms the same correctly rounded quotients
+// without division sequences (div6_rn, div_rn, recip_rn: d then lies in [2^-105, 2^126)).
+template <int CAND, bool FAST = false>
 PMN_DEV void quant_candidate(const Block16& b, float ab, float s_o, uint32_t& sb, uint32_t& w0,
-                             uint32_t& w1, float& d)
+                             uint32_t& w1, float& d, float ys = 0.0f)
 {
-    float t = (ab / (float)CAND) / s_o;
+    float t;
+    if (FAST) t = div_rn(CAND == 4 ? ab * 0.25f : div6_rn(ab), s_o, ys);
+    else t = (ab / (float)CAND) / s_o;
     sb = e4m3_rne_sat(t);
     d = e4m3_value(sb) * s_o;
-    float r = (d != 0.0f) ? fminf(1.0f / d, 3.402823466e38f) : 0.0f;
+    float r;
+    if (FAST) r = (d != 0.0f) ? recip_rn(d) : 0.0f;
+    else r = (d != 0.0f) ? fminf(1.0f / d, 3.402823466e38f) : 0.0f;
     w0 = 0u;
     w1 = 0u;
     w0 = PMN_CVT_FP4(w0, b.x[0] * r, b.x[1] * r, 0);
@@ -80,19 +86,19 @@ PMN_DEV float candidate_error(const Block16& b, uint32_t w0, uint32_t w1, float 
     return e;
 }
 
-template <bool FOUR_SIX>
-PMN_DEV void quant_block(const Block16& b, float s_o, uint32_t& sb, uint2& q)
+// ab: the block's max |x| (block_absmax(b)).
+template <bool FOUR_SIX, bool FAST = false>
+PMN_DEV void quant_block_ab(const Block16& b, float ab, float s_o, uint32_t& sb, uint2& q, float ys = 0.0f)
 {
-    float ab = block_absmax(b);
     uint32_t sb6, a0, a1;
     float d6;
-    quant_candidate<6>(b, ab, s_o, sb6, a0, a1, d6);
+    quant_candidate<6, FAST>(b, ab, s_o, sb6, a0, a1, d6, ys);
     sb = sb6;
     q = make_uint2(a0, a1);
     if (FOUR_SIX) {
         uint32_t sb4, c0, c1;
         float d4;
-        quant_candidate<4>(b, ab, s_o, sb4, c0, c1, d4);
+        quant_candidate<4, FAST>(b, ab, s_o, sb4, c0, c1, d4, ys);
         float e6 = candidate_error(b, a0, a1, d6);
         float e4 = candidate_error(b, c0, c1, d4);
         if (e4 < e6) {
@@ -100,6 +106,12 @@ PMN_DEV void quant_block(const Block16& b, float s_o, uint32_t& sb, uint2& q)
             q = make_uint2(c0, c1);
         }
     }
+}
+
+template <bool FOUR_SIX>
+PMN_DEV void quant_block(const Block16& b, float s_o, uint32_t& sb, uint2& q)
+{
+    quant_block_ab<FOUR_SIX>(b, block_absmax(b), s_o, sb, q);
 }
 
 PMN_DEV float outer_from_amax(float amax) { return amax > 0.0f ? amax / 2688.0f : 1.0f; }
@@ -118,13 +130,16 @@ __global__ __launch_bounds__(256) void k_nvfp4_rows(const uint16_t* __restrict__
     const int nb = (int)(cols >> 4);
     const uint4* xr = reinterpret_cast<const uint4*>(x + r * cols);
     Block16 blk[NBL];
+    float ab[NBL];
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < NBL; j++) {
         int b = lane + 64 * j;
+        ab[j] = 0.0f;
         if (b < nb) {
             load_block(xr + 2 * b, blk[j]);
-            amax = fmaxf(amax, block_absmax(blk[j]));
+            ab[j] = block_absmax(blk[j]);
+            amax = fmaxf(amax, ab[j]);
         }
     }
     amax = wave_max(amax);
@@ -132,13 +147,69 @@ __global__ __launch_bounds__(256) void k_nvfp4_rows(const uint16_t* __restrict__
     if (lane == 0) outer_out[r] = s_o;
     uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
     uint8_t* sr = scales + r * nb;
+    // the row's quotients take the division-free path when its outer scale allows (uniform per row)
+    const bool fast = s_o >= 0x1p-96f;
+    const float ys = fast ? 1.0f / s_o : 0.0f;
 #pragma unroll
     for (int j = 0; j < NBL; j++) {
         int b = lane + 64 * j;
         if (b < nb) {
             uint32_t sb;
             uint2 q;
-            quant_block<FOUR_SIX>(blk[j], s_o, sb, q);
+            if (fast) quant_block_ab<FOUR_SIX, true>(blk[j], ab[j], s_o, sb, q, ys);
+            else quant_block_ab<FOUR_SIX, false>(blk[j], ab[j], s_o, sb, q);
+            cr[b] = q;
+            sr[b] = (uint8_t)sb;
+        }
+    }
+}
+
+// Rows of 129 .. 512 blocks (up to 8192 values): the 4 wavefronts of a workgroup share one row,
+// lane l of wavefront w holding blocks 256 j + 64 w + l (j < NBL), so each lane keeps at most
+// NBL blocks in registers (more wavefronts fit per SIMD) and every load instruction reads 2 KB
+// of contiguous row. The row amax is combined across the wavefronts through LDS.
+template <int NBL, bool FOUR_SIX>
+__global__ __launch_bounds__(256) void k_nvfp4_row_split(const uint16_t* __restrict__ x, int64_t rows,
+                                                         int64_t cols, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales,
+                                                         float* __restrict__ outer_out)
+{
+    __shared__ float wmax[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t r = blockIdx.x;
+    const int nb = (int)(cols >> 4);
+    const uint4* xr = reinterpret_cast<const uint4*>(x + r * cols);
+    Block16 blk[NBL];
+    float ab[NBL];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBL; j++) {
+        const int b = 256 * j + 64 * w + lane;
+        ab[j] = 0.0f;
+        if (b < nb) {
+            load_block(xr + 2 * b, blk[j]);
+            ab[j] = block_absmax(blk[j]);
+            amax = fmaxf(amax, ab[j]);
+        }
+    }
+    amax = wave_max(amax);
+    if (lane == 0) wmax[w] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float s_o = outer_from_amax(amax);
+    if (threadIdx.x == 0) outer_out[r] = s_o;
+    uint2* cr = reinterpret_cast<uint2*>(codes + r * (cols >> 1));
+    uint8_t* sr = scales + r * nb;
+    const bool fast = s_o >= 0x1p-96f;   // uniform per row, as in k_nvfp4_rows
+    const float ys = fast ? 1.0f / s_o : 0.0f;
+#pragma unroll
+    for (int j = 0; j < NBL; j++) {
+        const int b = 256 * j + 64 * w + lane;
+        if (b < nb) {
+            uint32_t sb;
+            uint2 q;
+            if (fast) quant_block_ab<FOUR_SIX, true>(blk[j], ab[j], s_o, sb, q, ys);
+            else quant_block_ab<FOUR_SIX, false>(blk[j], ab[j], s_o, sb, q);
             cr[b] = q;
             sr[b] = (uint8_t)sb;
         }
@@ -268,6 +339,15 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
     if (rows == 0) return hipSuccess;
     const int64_t nb = cols / 16;
     const int64_t ngroups = rows / rows_per_outer;
+    if (!square && outer_in == nullptr && rows_per_outer == 1 && nb > 128 && nb <= 512) {
+        if (four_six)
+            hipLaunchKernelGGL((k_nvfp4_row_split<2, true>), dim3((unsigned)rows), dim3(256), 0, stream, x, rows, cols,
+                               codes, scales, outer_out);
+        else
+            hipLaunchKernelGGL((k_nvfp4_row_split<2, false>), dim3((unsigned)rows), dim3(256), 0, stream, x, rows, cols,
+                               codes, scales, outer_out);
+        return hipGetLastError();
+    }
     if (!square && outer_in == nullptr && rows_per_outer == 1 && nb <= 64 * 8) {
         const int64_t grid = (rows + 3) / 4;
         int nbl = nb <= 64 ? 1 : (nb <= 128 ? 2 : (nb <= 256 ? 4 : 8));

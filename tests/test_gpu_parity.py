@@ -137,6 +137,27 @@ def test_nvfp4_four_over_six_exact_tie_keeps_six(P, cols):
         assert npy(q.scales)[0, 1] == 0x38 and npy(q.scales)[2, cols // 16 - 1] == 0x38
 
 
+def test_nvfp4_division_free_reciprocal_is_exact(P):
+    """The activation quantizer forms 1/d as the hardware reciprocal plus one Newton step on rows
+    whose outer scale is at least 2^-96; d then lies in [2^-105, 2^126). Over every fp32 value of
+    that range the result equals the IEEE quotient 1.0f / d bit for bit."""
+    assert P.probe_recip_check(0x0B000000, 0x7E7FFFFF) == 0
+
+
+@pytest.mark.parametrize("four_six", [True, False])
+def test_nvfp4_rows_on_both_sides_of_the_exact_division_switch(P, I, four_six):
+    """Rows scaled by powers of two from 2^-120 to 2^100: outer scales below 2^-96 take the IEEE
+    division sequences, the others the division-free quotients; all bit-exact with the oracle."""
+    x = I.normal((16, 7168), 1.0, 41).float()
+    pw = [-120, -100, -90, -86, -85, -84, -83, -60, -20, 0, 0, 20, 60, 90, 100, -127]
+    x = (x * torch.tensor([2.0 ** p for p in pw])[:, None]).to(torch.bfloat16)
+    q = P.nvfp4_quantize(x.to(DEV), P.NVFP4_ACT if four_six else P.NVFP4_WEIGHT)
+    ref = O.nvfp4_quantize(x, 1, four_six)
+    assert_nvfp4_equal(q, ref)
+    so = ref["outer"]
+    assert (so < 2.0 ** -96).sum() >= 4 and (so >= 2.0 ** -96).sum() >= 8
+
+
 def test_nvfp4_empty(P):
     q = P.nvfp4_quantize(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV))
     assert q.codes.shape == (0, 32)
