@@ -225,6 +225,37 @@ def hardware_roofs(P, torch, dev):
                      "MFMA: independent accumulator chains on constant operands, no memory traffic")
 
 
+def library_reference(torch, dev, shape):
+    """The vendor library's dense GEMM on this chip, as a calibration of what the matrix cores reach
+    on plain operands of the layer's sizes (not a path of this library): hipBLASLt through torch,
+    fp16 for the forward shapes and fp8 E4M3 with unit per-tensor scales and fp32 output for the
+    backward shapes, M = all routed slots in one group. TFLOP/s per shape."""
+    M, H, F = shape.slots or shape.tokens * shape.top_k, shape.hidden, shape.ffn
+    res = {}
+
+    def rate(fn, flops, it=5):
+        fn()
+        ms = _time_ms(torch, fn, it)
+        return flops / (ms * 1e-3) / 1e12
+    for name, (m, n, k) in (("fwd_w13 fp16", (M, 2 * F, H)), ("fwd_w2 fp16", (M, H, F))):
+        a = torch.randn(m, k, device=dev, dtype=torch.float16)
+        b = torch.randn(k, n, device=dev, dtype=torch.float16)
+        res[name] = rate(lambda: torch.matmul(a, b), 2.0 * m * n * k)
+        del a, b
+    one = torch.ones((), device=dev)
+    for name, (m, n, k) in (("dgrad_w13 fp8", (M, H, 2 * F)), ("wgrad_w13 fp8", (2 * F, H, M))):
+        try:
+            a = torch.randn(m, k, device=dev).to(torch.float8_e4m3fn)
+            b = torch.randn(n, k, device=dev).to(torch.float8_e4m3fn)
+            res[name] = rate(lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.float32),
+                             2.0 * m * n * k)
+            del a, b
+        except Exception as ex:   # the library may not offer this fp8 product
+            res[name] = None
+            res[name + " error"] = type(ex).__name__
+    return res
+
+
 def quantizer_workload(P, I, torch, dev, iters):
     """GB/s of nvfp4_quantize (4/6, per-token outer) and requant_transpose_sr_mxfp8 on the
     8192 x 7168 activation workload. Inputs and outputs both rotate over buffer sets larger than the
@@ -505,6 +536,9 @@ PROFILE_COMMANDS = {
     "clock": ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA "
               "SQ_ACTIVE_INST_VALU --output-format csv -d gpurun_out/prof/clock -o ep48 -- "
               "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --quant-iters 1 --moe32-steps 1"),
+    "valu": ("rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_WAVES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_VALU_CVT "
+             "SQ_INSTS_LDS SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_INSTS_SALU --output-format csv -d gpurun_out/prof/valu "
+             "-o ep48 -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --quant-iters 1 --moe32-steps 1"),
     "bench": "python3 bench.py --no-cpu-baseline > gpurun_out/prof/bench.json",
 }
 TRAFFIC_SOURCES = ["precision_moe_numerics_amd/csrc/gemm_fwd.hip", "precision_moe_numerics_amd/csrc/pmn_dev.hpp"]
@@ -650,6 +684,39 @@ def summarize_profiles(d):
         cmd.append(f"| `{k[1]}` | {k[2]} | {v['dur'] * 1e3:.3f} | {clk / 1e9:.2f} | {busy:.2f} | {busy24:.2f} | "
                    f"{valu:.2f} |")
     open(os.path.join(out_dir, "ep48_layer_step_clock_mfma.md"), "w").write("\n".join(cmd) + "\n")
+
+    # VALU instruction counts: what the VALU-bound kernels spend their issue cycles on
+    vd = os.path.join(d, "valu")
+    if os.path.isdir(vd):
+        rows = list(csv.DictReader(open(_find_csv(vd, "counter_collection.csv"))))
+        ag = defaultdict(dict)
+        for r in rows:
+            n = _kname(r["Kernel_Name"])
+            if "pmn::" not in n:
+                continue
+            v = ag[(int(r["Dispatch_Id"]), n, r["Grid_Size"])]
+            v[r["Counter_Name"]] = float(r["Counter_Value"])
+            v["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+        md = ["# VALU instructions per kernel (48-expert layer step and workloads)", "",
+              "Command (from the repository root, one MI355X):", "", "```", PROFILE_COMMANDS["valu"], "```", "",
+              "SQ_INSTS_VALU counts wavefront VALU instructions (MFMA included) and SQ_ACTIVE_INST_VALU the "
+              "quad-cycles spent issuing them, so 4 x ACTIVE / INSTS is the SIMD cycles per VALU instruction and "
+              "4 x ACTIVE / 1024 / (GRBM_GUI_ACTIVE / 8) the share of SIMD cycles issuing VALU work (VALU busy). "
+              "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES is the share of wavefront time spent waiting on a dependency "
+              "(s_waitcnt). Kernels under 0.02 ms are omitted.", "",
+              "| kernel | grid | ms | waves | VALU instr (M) | per wave | cycles / instr | VALU busy | converts (M) | "
+              "LDS instr (M) | waiting |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for k, v in sorted(ag.items()):
+            if v["dur"] < 2e-5 or "GRBM_GUI_ACTIVE" not in v or not v.get("SQ_INSTS_VALU"):
+                continue
+            cyc = v["GRBM_GUI_ACTIVE"] / 8
+            md.append(f"| `{k[1]}` | {k[2]} | {v['dur'] * 1e3:.3f} | {v.get('SQ_WAVES', 0):.0f} | "
+                      f"{v['SQ_INSTS_VALU'] / 1e6:.1f} | {v['SQ_INSTS_VALU'] / max(v.get('SQ_WAVES', 1), 1):.0f} | "
+                      f"{4 * v['SQ_ACTIVE_INST_VALU'] / v['SQ_INSTS_VALU']:.2f} | "
+                      f"{4 * v['SQ_ACTIVE_INST_VALU'] / 1024 / cyc:.2f} | {v.get('SQ_INSTS_VALU_CVT', 0) / 1e6:.1f} | "
+                      f"{v.get('SQ_INSTS_LDS', 0) / 1e6:.1f} | "
+                      f"{v.get('SQ_WAIT_INST_ANY', 0) / max(v.get('SQ_WAVE_CYCLES', 1), 1):.2f} |")
+        open(os.path.join(out_dir, "ep48_layer_step_valu_instructions.md"), "w").write("\n".join(md) + "\n")
     print(f"wrote profiles/ from {d}: forward w13 traffic {(fetch + write) / 1e9:.3f} GB per launch "
           f"(algorithmic {alg / 1e9:.3f} GB)")
 
@@ -765,6 +832,14 @@ def main():
     over = [k for k, v in mem.items() if v["frac_of_measured_roof"] > 1.0]
 
     moe32 = moe32_workload(P, I, torch, dev, args.moe32_steps) if args.moe32_steps > 0 else None
+    lib = library_reference(torch, dev, shape)
+    roofs["library_gemm_tflops"] = lib
+    for nm, ln in (("moe_grouped_gemm_fwd[w13+swiglu]", "fwd_w13 fp16"),
+                   ("moe_grouped_gemm_fwd[w2+rht32_s2f6]", "fwd_w2 fp16")):
+        if lib.get(ln):
+            kernels[nm]["frac_of_library_dense_gemm"] = kernels[nm]["tflops"] / lib[ln]
+    if lib.get("fwd_w13 fp16"):
+        roofline["frac_of_library_dense_gemm"] = ach / lib["fwd_w13 fp16"]
 
     cpu = None
     if not args.no_cpu_baseline:
