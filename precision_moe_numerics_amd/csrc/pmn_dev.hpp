@@ -163,34 +163,53 @@ PMN_DEV int e8m0_exponent(float amax)
 }
 
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) -------------------------------------
-
-PMN_DEV void philox4x32_10(uint32_t c[4], uint32_t k0, uint32_t k1)
+// Ten rounds on a four-word counter under a two-word key. A round multiplies words 0 and 2 by the
+// two Philox multipliers; the new words 0 and 2 are the high halves of the products of words 2
+// and 0, xor'ed with words 1 and 3 and the round key; the new words 1 and 3 are the low halves of
+// those products; the key then advances by the two Weyl constants.
+//
+// The 8 random 16-bit values of elements 8*blk .. 8*blk+7 under (seed, stream), returned as
+// four words: element 8*blk + j uses half (j & 1) of word j >> 1 (low half first). The counter is
+// (blk lo, blk hi, stream, 0) and the key (seed lo, seed hi). The stream word, the zero word and
+// the key are the same for every lane of a launch, so the first two rounds are written out to keep
+// their products and xors on the scalar unit: round 0 costs one vector multiply, and each of the
+// first two rounds two single vector xors.
+PMN_DEV void rand16x8(uint64_t seed, uint32_t stream, uint64_t blk, uint32_t w[4])
 {
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+    // round 0 on (lo, hi, stream, 0)
+    const uint64_t p0 = (uint64_t)0xD2511F53u * (uint32_t)blk;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * stream;
+    // (readfirstlane keeps the lane-independent xor on the scalar unit)
+    uint32_t c0 = __builtin_amdgcn_readfirstlane((uint32_t)(p1 >> 32) ^ k0) ^ (uint32_t)(blk >> 32);
+    uint32_t c1 = (uint32_t)p1;
+    uint32_t c2 = (uint32_t)(p0 >> 32) ^ k1;
+    uint32_t c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+    // round 1: c1 is still lane-independent
+    const uint64_t q0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t q1 = (uint64_t)0xCD9E8D57u * c2;
+    w[0] = (uint32_t)(q1 >> 32) ^ (c1 ^ k0);
+    w[1] = (uint32_t)q1;
+    w[2] = __builtin_amdgcn_bitop3_b32((uint32_t)(q0 >> 32), c3, k1, 0x96);
+    w[3] = (uint32_t)q0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+    // rounds 2 .. 9
 #pragma unroll
-    for (int r = 0; r < 10; r++) {
-        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
-        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
-        // three-way xor in one gfx950 v_bitop3_b32 (truth table 0x96)
-        uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c[1], k0, 0x96);
-        uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c[3], k1, 0x96);
-        c[1] = (uint32_t)p1;
-        c[3] = (uint32_t)p0;
-        c[0] = n0;
-        c[2] = n2;
+    for (int r = 2; r < 10; r++) {
+        const uint64_t m0 = (uint64_t)0xD2511F53u * w[0];
+        const uint64_t m1 = (uint64_t)0xCD9E8D57u * w[2];
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32((uint32_t)(m1 >> 32), w[1], k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32((uint32_t)(m0 >> 32), w[3], k1, 0x96);
+        w[1] = (uint32_t)m1;
+        w[3] = (uint32_t)m0;
+        w[0] = n0;
+        w[2] = n2;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
     }
-}
-
-// The 8 random 16-bit values of elements 8*blk .. 8*blk+7 under (seed, stream), returned as
-// four words: element 8*blk + j uses half (j & 1) of word j >> 1 (low half first).
-PMN_DEV void rand16x8(uint64_t seed, uint32_t stream, uint64_t blk, uint32_t w[4])
-{
-    w[0] = (uint32_t)blk;
-    w[1] = (uint32_t)(blk >> 32);
-    w[2] = stream;
-    w[3] = 0u;
-    philox4x32_10(w, (uint32_t)seed, (uint32_t)(seed >> 32));
 }
 
 // SR operand of the hardware converter for the element that owns 16-bit half `hi` of word w.

@@ -139,6 +139,26 @@ PMN_DEV uint32_t e4m3_rne_pair_scaled_into(uint32_t word, float a, float b, floa
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// a + b for a per-lane a and a wavefront-uniform b: one 64-bit vector add. Written as asm so that
+// the compiler keeps it an add instead of re-deriving each slot's counter with a 64-bit multiply.
+PMN_DEV uint64_t add_uniform64(uint64_t a, uint64_t b)
+{
+    uint64_t r;
+    asm("v_lshl_add_u64 %0, %1, 0, %2" : "=v"(r) : "v"(a), "s"(b));
+    return r;
+}
+
+// p, a wavefront-uniform pointer, pinned to scalar registers: a load from p + (32-bit lane offset)
+// then takes the scalar-base addressing form and needs no per-lane 64-bit address arithmetic.
+typedef const __attribute__((address_space(1))) uint8_t gbyte;   // global memory
+PMN_DEV gbyte* uniform_ptr(const uint8_t* p)
+{
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<gbyte*>(((uint64_t)hi << 32) | lo);
+}
+
 // Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
 PMN_DEV void deq8(uint32_t cw, float d, float (&v)[8])
 {
@@ -197,7 +217,9 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
         const int jl = lane & 31;
         const int64_t sl = rs0 + (jl < lastc ? jl : lastc);
         rl = a.gather ? a.gather[sl] : (int)sl;
-        ol = a.outer[rl / a.rows_per_outer];
+        // rl is a 32-bit row index, so a 32-bit division serves whenever the divisor fits
+        ol = a.outer[a.rows_per_outer <= 0x7FFFFFFF ? (int64_t)((uint32_t)rl / (uint32_t)a.rows_per_outer)
+                                                    : (int64_t)rl / a.rows_per_outer];
     }
 
     if (active) {
@@ -215,16 +237,18 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
             for (int j = 0; j < 32; j++) {
                 const int64_t r = __builtin_amdgcn_readlane(rl, j);
                 so[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ol), j));
-                const uint8_t* crow = a.codes + r * (a.cols >> 1);
-                const uint8_t* srow = a.scales + r * (a.cols >> 4);
-                cw[j] = *reinterpret_cast<const uint32_t*>(crow + coff);
+                gbyte* crow = uniform_ptr(a.codes + r * (a.cols >> 1));
+                gbyte* srow = uniform_ptr(a.scales + r * (a.cols >> 4));
+                cw[j] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(crow + coff);
                 sbyte[j] = srow[soff];
             }
-            // slots past the group's end become +0 (code word 0, scale 0), so they need no branch
+            // slots past the group's end become +0 (code word 0, scale 0), so they need no branch:
+            // a wavefront-uniform mask clears both
 #pragma unroll
             for (int j = 0; j < 32; j++) {
-                dsc[j] = j <= last ? e4m3_value(sbyte[j]) * so[j] : 0.0f;
-                cw[j] = j <= last ? cw[j] : 0u;
+                const uint32_t keep = j <= last ? 0xFFFFFFFFu : 0u;
+                dsc[j] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, e4m3_value(sbyte[j]) * so[j]) & keep);
+                cw[j] &= keep;
             }
         } else {
 #pragma unroll
@@ -246,8 +270,9 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                 bf8(xw[j], v0);
                 bf8(xw[j + 1], v1);
             }
+            // one running maximum per column, two slots per step (one three-input max)
 #pragma unroll
-            for (int c = 0; c < 8; c++) amax[c] = fmaxf(amax[c], fmaxf(fabsf(v0[c]), fabsf(v1[c])));
+            for (int c = 0; c < 8; c++) amax[c] = fmaxf(fmaxf(amax[c], fabsf(v0[c])), fabsf(v1[c]));
         }
         int e[8];
         float escale[8];   // 2^e: the scaled converter divides by it exactly
@@ -259,13 +284,22 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
         }
 
         // ---- pass 2: convert 16 slots at a time (4 words per column) into the LDS tile
+        // Philox counter of slot s0 + j: (s * cols + c0) / 8 = ctr0 + j * cols / 8 (cols and c0 are
+        // multiples of 8), so consecutive slots add a wavefront-uniform step
+        const uint64_t ctr0 = ((uint64_t)blk.s0 * (uint64_t)a.cols + (uint64_t)c0) >> 3;
+        const uint64_t cstep = (uint64_t)a.cols >> 3;
 #pragma unroll
         for (int half = 0; half < 2; half++) {
             uint32_t o[8][4];
 #pragma unroll
             for (int c = 0; c < 8; c++)
 #pragma unroll
-                for (int q = 0; q < 4; q++) o[c][q] = 0u;
+                for (int q = 0; q < 4; q++) {
+                    // the E4M3 target writes all four bytes of every word below, so the words need
+                    // no initial value; the packed E2M1 targets OR nibbles into zero
+                    if (TARGET == 0) o[c][q] = __builtin_nondeterministic_value(o[c][q]);
+                    else o[c][q] = 0u;
+                }
             if (TARGET == 0) {
                 // E4M3 target: every slot runs (padding slots are +0 and convert to 0 whatever the
                 // random bits). The scaled converters compute the conversion of v / 2^e exactly and
@@ -292,9 +326,8 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                     if (ROUND == 1) {
 #pragma unroll
                         for (int u = 0; u < 2; u++) {
-                            const int64_t s = blk.s0 + half * 16 + jj + u;
                             uint32_t rw[4];
-                            rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+                            rand16x8(a.seed, a.stream_id, add_uniform64(ctr0, (uint64_t)(half * 16 + jj + u) * cstep), rw);
 #pragma unroll
                             for (int c = 0; c < 8; c++)
                                 o[c][jj >> 2] = e4m3_sr_scaled_into(o[c][jj >> 2], v[u][c], sr_operand(rw[c >> 1], c & 1),
@@ -312,7 +345,6 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                 for (int jj = 0; jj < 16; jj++) {
                     const int j = half * 16 + jj;
                     if (j < blk.valid) {
-                        const int64_t s = blk.s0 + j;
                         float v[8];
                         if (SRC == SRC_NVFP4) {
                             uint32_t cwj = cw[j];
@@ -325,7 +357,7 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                         }
                         uint32_t rw[4] = {0u, 0u, 0u, 0u};
                         if (ROUND == 1)
-                            rand16x8(a.seed, a.stream_id, ((uint64_t)s * (uint64_t)a.cols + (uint64_t)c0) >> 3, rw);
+                            rand16x8(a.seed, a.stream_id, add_uniform64(ctr0, (uint64_t)j * cstep), rw);
 #pragma unroll
                         for (int c = 0; c < 8; c++) {
                             const float y = __builtin_ldexpf(v[c], -e[c]);
