@@ -240,7 +240,8 @@ int moe_grouped_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const 
                          uint8_t* out_e8m0, void* out_aux, pmn_stream_t stream)
 {
     if (epilogue < PMN_EPI_F32 || epilogue > PMN_EPI_RHT32_S2F6) return PMN_EINVAL;
-    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 64 != 0) return PMN_ESHAPE;
+    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return PMN_ESHAPE;
+    if (epilogue == PMN_EPI_SWIGLU && N % 64 != 0) return PMN_ESHAPE;   // F = N / 2 features, a multiple of 32
     if (a_rows_per_outer < 1 || b_rows_per_outer < 32 || b_rows_per_outer % 32 != 0) return PMN_ESHAPE;
     if (!gather && M > a_rows) return PMN_ESHAPE;
     if (!offsets || !b_codes || !b_scales || !b_outer) return PMN_EINVAL;

@@ -74,25 +74,41 @@ constexpr int BT = 256;
 constexpr int KS = 128;                       // k per stage
 constexpr int NSTAGE = 3;
 constexpr int ROWS_MAX = 640;                 // weight + slot rows of a stage (the 512 x 128 shape)
-constexpr int STAGEB = ROWS_MAX * 72;         // 64 code bytes + 8 scale bytes per row
-constexpr int LDSB = NSTAGE * STAGEB;
+// Per row and stage: 64 code bytes, then the 8 E4M3 scale bytes, copied as two 4-byte words
+// (8 LDS bytes) or, when K = 32 mod 64 leaves rows of scales only 2-byte aligned (SC2), as four
+// 2-byte pieces that each land in the low half of a 4-byte LDS word (16 LDS bytes).
+constexpr int srow_bytes(bool sc2) { return sc2 ? 16 : 8; }
+constexpr int stage_bytes(bool sc2) { return ROWS_MAX * (64 + srow_bytes(sc2)); }
+constexpr int lds_bytes(bool sc2) { return NSTAGE * stage_bytes(sc2); }
 constexpr int THREADS = 256;
 constexpr int OPITCH = 272;
-static_assert(BT * OPITCH + BT * 8 <= LDSB, "the epilogue's output tile and E8M0 tile fit in the ring");
+static_assert(BT * OPITCH + BT * 8 <= lds_bytes(false), "the epilogue's output tile and E8M0 tile fit in the ring");
+static_assert(lds_bytes(true) <= 160 * 1024, "the 2-byte scale layout fits the LDS");
 }  // namespace fwd
 
 // One workgroup tile. SHAPE false: 256 weight rows x 256 slots, wavefront w computes weight rows
 // (w / 2) * 128 .. and slots (w % 2) * 128 ... SHAPE true (the last unit of an expert's slots
 // when it holds at most 128 of them): 512 weight rows (weight tiles nt0 and nt0 + 1) x 128 slots,
 // wavefront w computes weight rows w * 128 .. and all 128 slots. Each wavefront's work (a
-// 128 x 128 quarter) and inner loop are the same in both.
-template <int EPI, bool SHAPE>
+// 128 x 128 quarter) and inner loop are the same in both. SC2: scales copied as 2-byte pieces
+// (K = 32 mod 64).
+//
+// Edges. N (weight rows per expert; 2F for SwiGLU) need only be a multiple of 32 (64 for
+// SwiGLU): weight rows past the expert's last re-read one of its first 32 rows, and the outputs
+// of those rows are never stored. K need only be a multiple of 32: the last stage may hold 32,
+// 64 or 96 valid k; its other 32-k chunks re-read the stage's first chunk and their block scales
+// are forced to zero, so they add nothing.
+template <int EPI, bool SHAPE, bool SC2>
 PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, int mvalid, int64_t nt0)
 {
     using namespace fwd;
+    constexpr int SROW = srow_bytes(SC2);                    // LDS bytes of a row's scales per stage
+    constexpr int STAGEB = stage_bytes(SC2);
     constexpr int RW = SHAPE ? 512 : 256, RX = SHAPE ? 128 : 256;   // weight and slot rows
-    constexpr int XOFF = RW * 64, SOFF = (RW + RX) * 64, XSOFF = SOFF + RW * 8;   // stage layout
-    constexpr int NP = SHAPE ? 10 : 8, NL = SHAPE ? 5 : 4;   // code pieces and scale lines per wavefront
+    constexpr int XOFF = RW * 64, SOFF = (RW + RX) * 64, XSOFF = SOFF + RW * SROW;   // stage layout
+    constexpr int RL = SC2 ? 16 : 32;                        // rows per scale line
+    constexpr int NLW = 128 / RL;                            // scale lines of 128 rows
+    constexpr int NP = SHAPE ? 10 : 8, NL = SHAPE ? NLW + 32 / RL : NLW;   // code pieces, scale lines per wavefront
     constexpr int LPS = NP + NL;                             // copies per wavefront per stage
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -100,31 +116,41 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
     const int64_t N = p.N, K = p.K;
     const int64_t cbytes = K >> 1, sbytes = K >> 4;
     const int KT = (int)((K + KS - 1) / KS);
-    const bool half_tail = (K % KS) != 0;        // last stage holds 64 k (K = 64 mod 128)
+    const int tailv = (int)(K % KS);             // valid k of the last stage (0: a full stage)
 
     // ---- copy schedule. Code piece = 16 rows (lane l: row l / 4, position l % 4), scale line =
-    // 32 rows (lane l: row l / 2, dword l % 2). SHAPE false: wavefronts 0-1 copy weight rows, 2-3
-    // slot rows, 128 rows each (8 pieces, 4 lines). SHAPE true: wavefront w copies weight rows
-    // 128 w .. (8 pieces, 4 lines) and slot rows 32 w .. (2 pieces, 1 line).
+    // 32 rows (lane l: row l / 2, dword l % 2) or, with SC2, 16 rows (lane l: row l / 4, 2-byte
+    // piece l % 4). SHAPE false: wavefronts 0-1 copy weight rows, 2-3 slot rows, 128 rows each
+    // (8 pieces, NLW lines). SHAPE true: wavefront w copies weight rows 128 w .. (8 pieces, NLW
+    // lines) and slot rows 32 w .. (2 pieces, 32 / RL lines).
     // A slot row past the tile's valid slots reads the tile's first slot: its products land only
     // in output columns that are never stored.
     auto piece_op = [&](int i) { return SHAPE ? (i < 8 ? 0 : 1) : (wave >> 1); };
     auto piece_row = [&](int i) { return SHAPE ? (i < 8 ? wave * 128 + 16 * i : wave * 32 + 16 * (i - 8)) : (wave & 1) * 128 + 16 * i; };
-    auto line_op = [&](int i) { return SHAPE ? (i < 4 ? 0 : 1) : (wave >> 1); };
-    auto line_row = [&](int i) { return SHAPE ? (i < 4 ? wave * 128 + 32 * i : wave * 32) : (wave & 1) * 128 + 32 * i; };
+    auto line_op = [&](int i) { return SHAPE ? (i < NLW ? 0 : 1) : (wave >> 1); };
+    auto line_row = [&](int i) { return SHAPE ? (i < NLW ? wave * 128 + RL * i : wave * 32 + RL * (i - NLW)) : (wave & 1) * 128 + RL * i; };
     auto row_of = [&](int op, int t) -> int64_t {
         if (op == 0) {
             const int64_t nt = nt0 + (t >> 8);
             const int tt = t & 255;
-            return (int64_t)g * N + (EPI == PMN_EPI_SWIGLU ? swiglu_a_row(tt, nt, N >> 1) : nt * BT + tt);
+            int64_t r;
+            if (EPI == PMN_EPI_SWIGLU) {
+                r = swiglu_a_row_clamped(tt, nt, N >> 1);
+            } else {
+                r = nt * BT + tt;
+                r = r < N ? r : (int64_t)(tt & 31);
+            }
+            return (int64_t)g * N + r;
         }
         const int64_t m = m0 + (t < mvalid ? t : 0);
         return p.gather ? (int64_t)p.gather[m] : m;
     };
     const int csrc = (lane & 3) ^ ((lane >> 4) & 3);   // source chunk for this lane's position
-    // in a half-tail stage only chunks 0-1 and scale dword 0 of a row exist: the other lanes
-    // re-read those (their values are scaled by zero below)
-    const int64_t cadj = csrc >= 2 ? -32 : 0, sadj = (lane & 1) ? -4 : 0;
+    // in the last stage only its first tailv / 32 chunks and tailv / 16 scales of a row exist: the
+    // other lanes re-read the stage's first chunk or scales (their values are scaled by zero below)
+    const int64_t cadj = tailv && csrc >= tailv / 32 ? -16 * csrc : 0;
+    const int sidx = SC2 ? (lane & 3) : (lane & 1);   // this lane's scale piece of a row
+    const int64_t sadj = tailv && sidx >= tailv / (SC2 ? 32 : 64) ? -(SC2 ? 2 : 4) * sidx : 0;
     const uint8_t* cp[NP];
     const uint8_t* sp[NL];
     uint32_t cd[NP], sd[NL];                     // LDS offsets within a stage slot
@@ -137,15 +163,15 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
 #pragma unroll
     for (int i = 0; i < NL; i++) {
         const int op = line_op(i), r = line_row(i);
-        sp[i] = (op ? p.a_scales : p.b_scales) + row_of(op, r + (lane >> 1)) * sbytes + (lane & 1) * 4;
-        sd[i] = (op ? XSOFF : SOFF) + r * 8;
+        sp[i] = (op ? p.a_scales : p.b_scales) + row_of(op, r + lane / (64 / RL)) * sbytes + sidx * (SC2 ? 2 : 4);
+        sd[i] = (op ? XSOFF : SOFF) + r * SROW;
     }
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);
     // stage v of the copy stream: stages past the last re-load it (into a free slot or over
     // identical bytes), so every stage issues the same copies
     auto stage_src = [&](int v, int64_t& co, int64_t& so) {
         const int kt = v < KT ? v : KT - 1;
-        const bool tail = half_tail && kt == KT - 1;
+        const bool tail = tailv && kt == KT - 1;
         co = (int64_t)kt * 64 + (tail ? cadj : 0);
         so = (int64_t)kt * 8 + (tail ? sadj : 0);
     };
@@ -157,7 +183,8 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
     auto issue_line = [&](int v, int i) {
         int64_t co, so;
         stage_src(v, co, so);
-        dma4(sp[i] + so, lds0 + (uint32_t)(v % NSTAGE) * STAGEB + sd[i]);
+        if (SC2) dma2(sp[i] + so, lds0 + (uint32_t)(v % NSTAGE) * STAGEB + sd[i]);
+        else dma4(sp[i] + so, lds0 + (uint32_t)(v % NSTAGE) * STAGEB + sd[i]);
     };
 
     // ---- fragments: 4 weight blocks (f = 0..3) and 4 slot blocks (f = 4..7) per wavefront
@@ -172,11 +199,21 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
         const uint8_t* base = lds + (v % NSTAGE) * STAGEB;
         const int row = f < 4 ? wrow0 + f * 32 + lrow : xrow0 + (f - 4) * 32 + lrow;
         const uint4 c = *reinterpret_cast<const uint4*>(base + (f < 4 ? 0 : XOFF) + row * 64 + (second ? offB : offA));
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(base + (f < 4 ? SOFF : XSOFF) + row * 8 + hh * 4);
+        uint32_t sc;
+        if (SC2) {
+            // the lane half's two 2-byte pieces sit in the low halves of two LDS words
+            const uint2 t = *reinterpret_cast<const uint2*>(base + (f < 4 ? SOFF : XSOFF) + row * 16 + hh * 8);
+            sc = __builtin_amdgcn_perm(t.y, t.x, 0x05040100u);
+        } else {
+            sc = *reinterpret_cast<const uint32_t*>(base + (f < 4 ? SOFF : XSOFF) + row * 8 + hh * 4);
+        }
         if (second) { rawB[f] = c; scB[f] = sc; } else { rawA[f] = c; scA[f] = sc; }
     };
-    // scales of the half-tail stage's upper lane half are forced to zero
-    auto smask = [&](int kt) -> uint32_t { return (half_tail && kt >= KT - 1 && hh) ? 0u : 0xFFFFFFFFu; };
+    // in the last stage, the scales of blocks past its tailv valid k are forced to zero: lane half
+    // hh holds blocks 4 hh .. 4 hh + 3
+    const int tcnt = tailv / 16 - 4 * hh;
+    const uint32_t tmask = tcnt >= 4 ? 0xFFFFFFFFu : (tcnt <= 0 ? 0u : (1u << (8 * tcnt)) - 1u);
+    auto smask = [&](int kt) -> uint32_t { return (tailv && kt >= KT - 1) ? tmask : 0xFFFFFFFFu; };
 
     f16x8 fa[2][4], fb[2][4];
     // Dequantize half `part` (values 4 part .. 4 part + 3) of fragment f of substep s (of stage
@@ -215,8 +252,9 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
     //   substep 0, MFMAs 8-15: read the second halves (code bytes 16..31) of this stage;
     //   substep 4, MFMA 8: wait until the next stage has landed and barrier (every wavefront is
     //     then done reading this stage's slot), then MFMAs 8-15 copy code pieces 0-7 of stage
-    //     kt + 3 into this slot; substep 5, MFMAs 8-11: scale lines 0-3; substep 6, MFMAs 12-14:
-    //     the 512 x 128 shape's further two pieces and one line;
+    //     kt + 3 into this slot; substep 5, MFMAs 8-11: scale lines 0-3 (SC2: and substep 7,
+    //     MFMAs 8-11, lines 4-7); substep 6, MFMAs 12-14: the 512 x 128 shape's further two pieces
+    //     and one line (SC2: substep 7, MFMAs 12-13, its two further lines);
     //   substep 5, MFMAs 12-15 and substep 6, MFMAs 8-11: read the first halves of stage kt + 1.
     auto stage = [&](int kt, auto tail) {
 #pragma unroll
@@ -232,8 +270,10 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
                 if (s == 4 && q == 8) wait_loads_and_barrier<LPS>();
                 if (s == 4 && q >= 8) issue_piece(kt + NSTAGE, q - 8);
                 if (s == 5 && q >= 8 && q < 12) issue_line(kt + NSTAGE, q - 8);
+                if (SC2 && s == 7 && q >= 8 && q < 12) issue_line(kt + NSTAGE, q - 4);
                 if (SHAPE && s == 6 && q >= 12 && q < 14) issue_piece(kt + NSTAGE, q - 4);
-                if (SHAPE && s == 6 && q == 14) issue_line(kt + NSTAGE, 4);
+                if (SHAPE && !SC2 && s == 6 && q == 14) issue_line(kt + NSTAGE, 4);
+                if (SHAPE && SC2 && s == 7 && q >= 12 && q < 14) issue_line(kt + NSTAGE, q - 4);
                 if (s == 5 && q >= 12) read_half(kt + 1, q - 12, false);
                 if (s == 6 && q >= 8 && q < 12) read_half(kt + 1, q - 4, false);
                 __builtin_amdgcn_sched_barrier(0);
@@ -286,11 +326,12 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int64_t nb = nt * BT + wr * 128 + i * 32;       // first weight row of block i
-            const float sw = p.b_outer[((int64_t)g * N + nb) / p.b_rpo];
+            const bool nok = nb < N;                              // inside the expert's rows
+            const float sw = nok ? p.b_outer[((int64_t)g * N + nb) / p.b_rpo] : 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int ml = xrow0 + j * 32 + lrow;
-                if (ml < mvalid) {
+                if (nok && ml < mvalid) {
                     const float s = sx[j] * sw;
                     const int64_t m = m0 + ml;
 #pragma unroll
@@ -320,8 +361,9 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
         slot = SHAPE ? (r & 127) : r;
         ntr = SHAPE ? nt0 + (r >> 7) : nt0;
     };
-    // dst(ntr) = the output row base of weight tile ntr for slot 0, rows pitch bytes apart
-    auto store_tile = [&](auto dst, int64_t pitch) {
+    // dst(ntr) = the output row base of weight tile ntr for slot 0, rows pitch bytes apart; piece c
+    // (16 bytes) of a staged row is stored if cvalid(ntr, c) (it lies inside the expert's N)
+    auto store_tile = [&](auto dst, int64_t pitch, auto cvalid) {
 #pragma unroll
         for (int k = 0; k < (BT * 16) / THREADS; k++) {
             const int qq = k * THREADS + tid;
@@ -329,7 +371,7 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
             int slot;
             int64_t ntr;
             staged(r, slot, ntr);
-            if (slot < mvalid)
+            if (slot < mvalid && cvalid(ntr, c))
                 *reinterpret_cast<uint4*>(dst(ntr) + (m0 + slot) * pitch + c * 16) =
                     *reinterpret_cast<const uint4*>(t0 + r * OPITCH + c * 16);
         }
@@ -342,10 +384,13 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
         float s1[2], s3[2];
 #pragma unroll
         for (int i = 0; i < 2; i++) {
+            // features past F (an F that is not a multiple of 128) get scale 0: their values are
+            // finite zeros and never stored
             const int64_t f0 = nt * 128 + wr * 64 + i * 32;
-            s1[i] = p.b_outer[((int64_t)g * N + f0) / p.b_rpo];
-            s3[i] = p.b_outer[((int64_t)g * N + F + f0) / p.b_rpo];
+            s1[i] = f0 < F ? p.b_outer[((int64_t)g * N + f0) / p.b_rpo] : 0.0f;
+            s3[i] = f0 < F ? p.b_outer[((int64_t)g * N + F + f0) / p.b_rpo] : 0.0f;
         }
+        auto fvalid = [&](int64_t ntr, int c) { return ntr * 128 + c * 8 < F; };   // 8 features per piece
 #pragma unroll
         for (int phase = 0; phase < 3; phase++) {
             if (phase > 0 && !Hs) break;
@@ -371,16 +416,17 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
                 }
             }
             __syncthreads();
-            if (phase == 0) store_tile([&](int64_t ntr) { return A + ntr * 128 * 2; }, F * 2);
-            else if (phase == 1) store_tile([&](int64_t ntr) { return Hs + ntr * 128 * 2; }, N * 2);
-            else store_tile([&](int64_t ntr) { return Hs + (F + ntr * 128) * 2; }, N * 2);
+            if (phase == 0) store_tile([&](int64_t ntr) { return A + ntr * 128 * 2; }, F * 2, fvalid);
+            else if (phase == 1) store_tile([&](int64_t ntr) { return Hs + ntr * 128 * 2; }, N * 2, fvalid);
+            else store_tile([&](int64_t ntr) { return Hs + (F + ntr * 128) * 2; }, N * 2, fvalid);
         }
     } else {
         // RHT32 + S2F6: each block's 32 weight rows are one aligned chunk of the slot's row
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int nl = wr * 128 + i * 32;
-            const float sw = p.b_outer[((int64_t)g * N + nt * BT + nl) / p.b_rpo];
+            // rows past the expert's N get scale 0 (finite zeros, never stored)
+            const float sw = nt * BT + nl < N ? p.b_outer[((int64_t)g * N + nt * BT + nl) / p.b_rpo] : 0.0f;
 #pragma unroll
             for (int j = 0; j < 4; j++) {
                 const int sl = srow0 + j * 32 + lrow;
@@ -393,22 +439,33 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
             }
         }
         __syncthreads();
-        store_tile([&](int64_t ntr) { return static_cast<uint8_t*>(p.out) + ntr * BT; }, N);
+        store_tile([&](int64_t ntr) { return static_cast<uint8_t*>(p.out) + ntr * BT; }, N,
+                   [&](int64_t ntr, int c) { return ntr * BT + c * 16 < N; });
         {
             int slot;
             int64_t ntr;
             staged(tid, slot, ntr);
-            if (slot < mvalid)
-                *reinterpret_cast<uint2*>(p.out_e8m0 + (m0 + slot) * (N >> 5) + ((ntr * BT) >> 5)) =
-                    *reinterpret_cast<const uint2*>(te + tid * 8);
+            if (slot < mvalid) {
+                // the tile's 8 chunk scales; an N that is not a multiple of 256 has fewer in its last
+                // tile, and its rows of scales are then not 8-byte aligned
+                uint8_t* const d = p.out_e8m0 + (m0 + slot) * (N >> 5) + ((ntr * BT) >> 5);
+                const int64_t nc = (N >> 5) - ntr * 8;
+                if ((N & 255) == 0) {
+                    *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(te + tid * 8);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 8; c++)
+                        if (c < nc) d[c] = te[tid * 8 + c];
+                }
+            }
         }
     }
 }
 
-template <int EPI>
+template <int EPI, bool SC2>
 __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs p)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[fwd::LDSB];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[fwd::lds_bytes(SC2)];
     asm volatile("; agpr in use %0" ::"a"(0));   // keep the accumulators in AGPRs
     TileXY tile;
     if (!xcd_tile(blockIdx.x, p.mtiles, p.ntiles, p.SM, p.SN, tile)) return;
@@ -421,9 +478,9 @@ __global__ __launch_bounds__(fwd::THREADS, 1) void k_nvfp4_grouped_gemm(FwdArgs 
     // tile keeps the 256 x 256 shape
     if (mvalid <= 128 && (tile.col & 1)) return;
     if (mvalid <= 128 && tile.col + 1 < p.ntiles)
-        nvfp4_gemm_tile<EPI, true>(p, lds, u.g, m0, mvalid, tile.col);
+        nvfp4_gemm_tile<EPI, true, SC2>(p, lds, u.g, m0, mvalid, tile.col);
     else
-        nvfp4_gemm_tile<EPI, false>(p, lds, u.g, m0, mvalid, tile.col);
+        nvfp4_gemm_tile<EPI, false, SC2>(p, lds, u.g, m0, mvalid, tile.col);
 }
 
 hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
@@ -435,17 +492,28 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
 {
     if (M == 0 || G == 0) return hipSuccess;
     const int64_t mtiles = (M + fwd::BT - 1) / fwd::BT + G;
-    const int64_t ntiles = N / fwd::BT;
+    // a weight tile is 256 rows of one expert (SwiGLU: 128 features of w1 and the same of w3)
+    const int64_t ntiles = epilogue == PMN_EPI_SWIGLU ? (N / 2 + 127) / 128 : (N + fwd::BT - 1) / fwd::BT;
     int SM, SN;
     xcd_shape(mtiles, ntiles, SM, SN);
     FwdArgs p{a_codes, a_scales, a_outer, a_rpo, gather, b_codes, b_scales, b_outer, b_rpo,
               offsets, G, N, K, rht_mask, out, out_e8m0, out_aux, mtiles, ntiles, SM, SN};
     dim3 grid((unsigned)xcd_grid(mtiles, ntiles, SM, SN));
-    switch (epilogue) {
-    case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32>), grid, dim3(fwd::THREADS), 0, stream, p); break;
-    case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16>), grid, dim3(fwd::THREADS), 0, stream, p); break;
-    case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU>), grid, dim3(fwd::THREADS), 0, stream, p); break;
-    default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6>), grid, dim3(fwd::THREADS), 0, stream, p); break;
+    const dim3 blk(fwd::THREADS);
+    if (K % 64 == 0) {
+        switch (epilogue) {
+        case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32, false>), grid, blk, 0, stream, p); break;
+        case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16, false>), grid, blk, 0, stream, p); break;
+        case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU, false>), grid, blk, 0, stream, p); break;
+        default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6, false>), grid, blk, 0, stream, p); break;
+        }
+    } else {
+        switch (epilogue) {
+        case PMN_EPI_F32: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_F32, true>), grid, blk, 0, stream, p); break;
+        case PMN_EPI_BF16: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_BF16, true>), grid, blk, 0, stream, p); break;
+        case PMN_EPI_SWIGLU: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_SWIGLU, true>), grid, blk, 0, stream, p); break;
+        default: hipLaunchKernelGGL((k_nvfp4_grouped_gemm<PMN_EPI_RHT32_S2F6, true>), grid, blk, 0, stream, p); break;
+        }
     }
     return hipGetLastError();
 }

@@ -442,6 +442,11 @@ PMN_DEV void dma4(const void* src, uint32_t lds_base)
 {
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
+// 2 bytes per lane; lane l's bytes land in the low half of the LDS dword at m0 + 4 l
+PMN_DEV void dma2(const void* src, uint32_t lds_base)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
 // Wait for this wavefront's LDS reads and until at most N of its loads are outstanding, then
 // barrier: afterwards the stage those loads waited for is visible to the workgroup and every
 // wavefront has finished reading the stages it read before.
@@ -457,6 +462,14 @@ PMN_DEV void wait_loads_and_barrier()
 PMN_DEV int64_t swiglu_a_row(int t, int64_t nt, int64_t F)
 {
     return ((t >> 6) & 1) * F + nt * 128 + (t >> 7) * 64 + ((t >> 5) & 1) * 32 + (t & 31);
+}
+// The same for an F that need not be a multiple of 128 (a multiple of 32): a 32-row run past the
+// expert's F features re-reads the first run of the same matrix (w1 or w3); its outputs are never
+// stored.
+PMN_DEV int64_t swiglu_a_row_clamped(int t, int64_t nt, int64_t F)
+{
+    const int64_t f = nt * 128 + (t >> 7) * 64 + ((t >> 5) & 1) * 32 + (t & 31);
+    return ((t >> 6) & 1) * F + (f < F ? f : (int64_t)(t & 31));
 }
 
 }  // namespace pmn

@@ -299,6 +299,37 @@ def test_gemm_fwd_short_units(P, I, counts, N, K, gather_rows):
     assert torch.equal(c, sc) and torch.equal(e, se)
 
 
+@pytest.mark.parametrize("counts,N,K,gather_rows", [([70, 300, 129, 1], 288, 96, None),
+                                                    ([5, 0, 600, 128], 352, 160, 700),
+                                                    ([300, 40], 320, 32, None),
+                                                    ([129, 257], 64, 224, 300),
+                                                    ([200, 3], 96, 320, None)])
+def test_gemm_fwd_edge_shapes(P, I, counts, N, K, gather_rows):
+    """Weight rows per expert that are not a multiple of 256 (a partial last weight tile: 32, 96
+    or 64 of its rows exist) and contractions that are not a multiple of 64 (the last k-stage
+    holds 32 or 96 values; rows of scales then sit at 2-byte alignment), with short slot units.
+    All four epilogues where the shape allows them (SwiGLU needs F = N / 2 a multiple of 32)."""
+    d = _moe_small(P, I, counts, N, K, gather_rows, seed=85)
+    y = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_F32, gather=d["ggather"])
+    ref = O.gemm_nvfp4_grouped(d["rxq"], d["rwq"], d["offsets"], N, K, gather=d["gather"])
+    assert rel_fro(npy(y), ref) <= 1e-5          # exact products, fp32 accumulation
+    yb = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_BF16, gather=d["ggather"])
+    assert torch.equal(yb, y.to(torch.bfloat16))
+    mask = I.sign_mask(3)
+    c, e = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_RHT32_S2F6, gather=d["ggather"],
+                                  rht_sign_mask=mask)
+    sc, se = P.rht32_s2f6_quantize(y, mask)
+    assert torch.equal(c, sc) and torch.equal(e, se)
+    if N % 64 == 0:
+        a, h13 = P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_SWIGLU, gather=d["ggather"],
+                                        save_h13=True)
+        assert torch.equal(h13, y.to(torch.bfloat16))
+        assert rel_fro(npy(a.float()), O.swiglu(ref, N // 2)) <= 2e-3
+    else:
+        with pytest.raises(RuntimeError):
+            P.moe_grouped_gemm_fwd(d["xq"], d["wq"], d["goff"], d["M"], N, P.EPI_SWIGLU, gather=d["ggather"])
+
+
 @pytest.mark.parametrize("sr", [False, True])
 def test_mxfp8_quantize_rows_and_cols(P, I, sr):
     dy = I.normal((600, 512), 1e-3, 31)
