@@ -66,10 +66,12 @@ def test_argument_errors_without_launch(lib):
                                           64, None, None) == -1
     # rht: cols not a multiple of 32
     assert lib.rht32_s2f6_quantize(fake, 0, 2, 48, 0, fake, fake, None) == -2
-    # gemm fwd: N not a multiple of 256, K not a multiple of 64
-    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 128, 64, 0,
+    # gemm fwd: N or K not a multiple of 32; SwiGLU with N not a multiple of 64
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 144, 64, 0,
                                     0, fake, None, None, None) == -2
-    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 256, 96, 0,
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 256, 80, 0,
+                                    0, fake, None, None, None) == -2
+    assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 96, fake, 1, 64, 96, 64, 2,
                                     0, fake, None, None, None) == -2
     assert lib.moe_grouped_gemm_fwd(fake, fake, fake, 64, 1, None, fake, fake, fake, 128, fake, 1, 64, 256, 64, 3,
                                     0, fake, None, None, None) == -1
