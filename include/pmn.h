@@ -201,7 +201,8 @@ int rht32_s2f6_quantize(const void* x, int dtype, int64_t rows, int64_t cols, ui
  * sum runs over exact products of dequantized values fp4 * e4m3 scale (fp32 accumulation), s is
  * a slot of group g (offsets, device int64 [G+1], offsets[G] = M) and row_s = gather[s] (or s).
  * A: NVFP4 [a_rows x K] with a_rows_per_outer; B: NVFP4 [G*N x K] with b_rows_per_outer.
- * K % 64 == 0, N % 256 == 0; b_rows_per_outer % 32 == 0 (each aligned run of 32 weight rows shares
+ * K % 32 == 0, N % 32 == 0 (SWIGLU: N % 64 == 0, so that F = N/2 is a multiple of 32);
+ * b_rows_per_outer % 32 == 0 (each aligned run of 32 weight rows shares
  * one outer scale; for SWIGLU, F % b_rows_per_outer == 0 keeps w1 and w3 apart). M is the number of
  * slots (host value); with M == 0 nothing is computed and a_*, out, out_e8m0 may be null.
  * Codes, out and out_aux 16-byte aligned, scales 4-byte aligned, out_e8m0 (RHT32_S2F6) 8-byte
@@ -227,8 +228,9 @@ size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, in
  * 32 values along K, the smallest scale that does not saturate -- as mxfp8_quantize with
  * PMN_ROWWISE and PMN_RNE) of x bf16 [x_rows x K] and w bf16 [G*N x K], s a slot of group g
  * (offsets, device int64 [G+1]) and row_s = gather[s] (or s). The epilogues are those of
- * moe_grouped_gemm_fwd (SWIGLU: rows 0..F-1 of each expert are w1, F..2F-1 are w3). N % 256 == 0,
- * K % 32 == 0 (M == 0: only w is quantized; x, out, out_e8m0 may be null). x, w, out, out_aux
+ * moe_grouped_gemm_fwd (SWIGLU: rows 0..F-1 of each expert are w1, F..2F-1 are w3). N % 32 == 0
+ * (SWIGLU: N % 64 == 0), K % 32 == 0 (M == 0: only w is quantized; x, out, out_e8m0 may be null).
+ * x, w, out, out_aux
  * and the workspace 16-byte aligned, out_e8m0 8-byte aligned
  * (PMN_EALIGN). Workspace (>= moe_grouped_gemm_fwd_mxfp8_workspace_size) holds, in order, each
  * part rounded up to 256 bytes: X8 codes [Pb x Kp] and E8M0 [K/32 x Pb], slot s of group g at
@@ -261,13 +263,17 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  *     quantized column-wise per group and A^T requantized (seed, rng_stream_a), contraction over
  *     the zero-padded slot dimension.
  * dy: bf16 [M x N]; a_*: NVFP4 [a_rows x K] (+ gather); b_*: NVFP4 [G*N x K]; offsets device
- * int64 [G+1]. N % 256 == 0, K % 256 == 0. Outputs fp32: da [M x K], db [G*N x K].
+ * int64 [G+1]. N % 32 == 0, K % 32 == 0. Outputs fp32: da [M x K], db [G*N x K].
  * dY quantized with SR uses rng_stream_dy (row-wise) and rng_stream_dy + 1 (column-wise).
  * M == 0 (no routed slots) is valid: dy, da and a_* may then be null, and db is set to zero.
  * Workspace (16-byte aligned, >= moe_grouped_gemm_bwd_workspace_size) holds, in order, each
- * part rounded up to 256 bytes: dY row-wise codes [Pb x N] and E8M0 [N/32 x Pb]; W^T codes
- * [K x G*N] and E8M0 [G*N/32 x K]; dY^T codes [N x Pb] and E8M0 [Pb/32 x N]; A^T codes [K x Pb]
- * and E8M0 [Pb/32 x K]; padded offsets int64 [G+1]. Each group's slots are padded with zeros to
+ * part rounded up to 256 bytes: dY row-wise codes [Pb x Nk] and E8M0 [N/32 x Pb]; W^T codes
+ * [K x G*Nk] and E8M0 [G*Nk/32 x K], expert g at columns g*Nk .. g*Nk + N - 1 (zero codes up to
+ * the next expert); dY^T codes [N x Pb] and E8M0 [Pb/32 x N]; A^T codes [K x Pb] and E8M0
+ * [Pb/32 x K]; padded offsets int64 [G+1]; the experts' row offsets g*N, int64 [G+1] (used when
+ * Nk != N). Nk is N rounded up to a multiple of 64 (128 with PMN_BWD_FP4); codes of dY's row-wise
+ * columns N .. Nk-1 are zero (E4M3) or unspecified E2M1 values whose scale the GEMM forces to
+ * 2^-127 (FP4). Each group's slots are padded with zeros to
  * a multiple of U = 64 (padded_offsets[g] is group g's first padded slot) and Pb = roundup(M, U)
  * + U G. Slot s of group g is padded slot padded_offsets[g] + s - offsets[g]: the row of the
  * row-wise dY codes and the column of their E8M0. The E8M0 parts are k-block-major (entry

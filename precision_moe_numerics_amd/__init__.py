@@ -399,10 +399,12 @@ def bwd_workspace_views(workspace: torch.Tensor, M: int, G: int, N: int, K: int,
     U = 128 if fp4 else 64
     Pb = (M + U - 1) // U * U + U * G
     h = 2 if fp4 else 1
-    sizes = [("dq", Pb * N // h, (Pb, N // h)), ("de", N // 32 * Pb, (N // 32, Pb)),
-             ("wt", K * G * N // h, (K, G * N // h)), ("wte", K * G * N // 32, (G * N // 32, K)),
+    Nk = (N + U - 1) // U * U   # dgrad's contraction: N rounded up to a whole stage (64 E4M3 / 128 E2M1 values)
+    sizes = [("dq", Pb * Nk // h, (Pb, Nk // h)), ("de", N // 32 * Pb, (N // 32, Pb)),
+             ("wt", K * G * Nk // h, (K, G * Nk // h)), ("wte", K * G * Nk // 32, (G * Nk // 32, K)),
              ("dt", N * Pb // h, (N, Pb // h)), ("dte", N * Pb // 32, (Pb // 32, N)),
-             ("xt", K * Pb // h, (K, Pb // h)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None)]
+             ("xt", K * Pb // h, (K, Pb // h)), ("xte", K * Pb // 32, (Pb // 32, K)), ("po", (G + 1) * 8, None),
+             ("woff", (G + 1) * 8, None)]
     off, views = 0, {}
     for name, nbytes, shape in sizes:
         used = nbytes if shape is None else shape[0] * shape[1]

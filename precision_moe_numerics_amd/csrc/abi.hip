@@ -14,8 +14,8 @@ inline hipStream_t hs(pmn_stream_t s) { return reinterpret_cast<hipStream_t>(s);
 inline size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 struct BwdLayout {
-    size_t dq, de, wt, wte, dt, dte, xt, xte, po, total;
-    int64_t Pb;
+    size_t dq, de, wt, wte, dt, dte, xt, xte, po, woff, total;
+    int64_t Pb, Nk;
 };
 
 // Bound on the padded slot count when every group is padded to a multiple of `unit`.
@@ -25,23 +25,28 @@ static int64_t padded_bound_unit(int64_t M, int G, int64_t unit)
 }
 
 // The backward keeps its operands in the blocked layout with groups padded to 64 slots (E4M3) or
-// 128 slots (packed E2M1); the row-wise dY codes sit at padded rows.
+// 128 slots (packed E2M1); the row-wise dY codes sit at padded rows. dgrad contracts over N in
+// stages of 64 E4M3 / 128 E2M1 values, so dY's rows and each expert's columns of W^T are Nk wide:
+// N rounded up to a whole stage (equal to N for the pages' shapes).
 BwdLayout bwd_layout(int64_t M, int G, int64_t N, int64_t K, bool fp4 = false)
 {
     BwdLayout L{};
     L.Pb = padded_bound_unit(M, G, pmn::blocked_unit(fp4));
     const int64_t vpb = fp4 ? 2 : 1;   // code values per byte
+    const int64_t stage = 64 * vpb;
+    L.Nk = (N + stage - 1) / stage * stage;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off += round256(bytes); return o; };
-    L.dq = take((size_t)(L.Pb * N / vpb));
+    L.dq = take((size_t)(L.Pb * L.Nk / vpb));
     L.de = take((size_t)(N / 32 * L.Pb));
-    L.wt = take((size_t)(K * G * N / vpb));
-    L.wte = take((size_t)(K * G * N / 32));
+    L.wt = take((size_t)(K * G * L.Nk / vpb));
+    L.wte = take((size_t)(K * G * L.Nk / 32));
     L.dt = take((size_t)(N * L.Pb / vpb));
     L.dte = take((size_t)(N * L.Pb / 32));
     L.xt = take((size_t)(K * L.Pb / vpb));
     L.xte = take((size_t)(K * L.Pb / 32));
     L.po = take((size_t)(G + 1) * sizeof(int64_t));
+    L.woff = take((size_t)(G + 1) * sizeof(int64_t));
     L.total = off;
     return L;
 }
@@ -82,7 +87,7 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
     if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
         return PMN_EINVAL;
     if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
-    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 256 != 0) return PMN_ESHAPE;
+    if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return PMN_ESHAPE;
     if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
     if (!gather && M > a_rows) return PMN_ESHAPE;
     // with no slots (M == 0) dy, da and the activations may be null: dgrad has no rows and
@@ -114,12 +119,23 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
         e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
                                    ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
-                                0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true, nullptr,
-                                s, blocked);
+        if (L.Nk == N) {
+            e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
+                                    0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true,
+                                    nullptr, s, blocked);
+        } else {
+            // every expert's N rows form a group, padded to Nk columns of W^T; the random bits and
+            // the codes of the real columns are those of the ungrouped call
+            int64_t* woff = reinterpret_cast<int64_t*>(ws + L.woff);
+            e = pmn::launch_iota_offsets(woff, G, N, s);
+            if (e != hipSuccess) return PMN_ELAUNCH;
+            e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, woff, G,
+                                    target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * L.Nk, true,
+                                    nullptr, s, blocked);
+        }
         if (e != hipSuccess) return PMN_ELAUNCH;
         e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
-                                    s, fp4);
+                                    s, fp4, L.Nk);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (wgrad) {
@@ -292,7 +308,8 @@ int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gat
                                void* workspace, size_t workspace_bytes, pmn_stream_t stream)
 {
     if (epilogue < PMN_EPI_F32 || epilogue > PMN_EPI_RHT32_S2F6) return PMN_EINVAL;
-    if (G < 1 || M < 0 || x_rows < 0 || N <= 0 || K <= 0 || N % 256 != 0 || K % 32 != 0) return PMN_ESHAPE;
+    if (G < 1 || M < 0 || x_rows < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return PMN_ESHAPE;
+    if (epilogue == PMN_EPI_SWIGLU && N % 64 != 0) return PMN_ESHAPE;   // F = N / 2 features, a multiple of 32
     if (!gather && M > x_rows) return PMN_ESHAPE;
     if (!offsets || !w || (M > 0 && (!x || !out || (epilogue == PMN_EPI_RHT32_S2F6 && !out_e8m0))))
         return PMN_EINVAL;

@@ -32,6 +32,8 @@
 // quantizers write them in 1 KB blocks of 16 rows x 64 bytes with the same permutation (the
 // blocked layout), so every copy moves one whole contiguous block. Scales are streamed from
 // k-block-major arrays, so one k-block of 256 rows is 256 contiguous bytes.
+#include <type_traits>
+
 #include "pmn_dev.hpp"
 #include "pmn_kernels.hpp"
 
@@ -85,6 +87,9 @@ struct Mx8Args {
     uint8_t* ye8m0;
     void* yaux;
     uint32_t mask;
+    // dgrad: B columns per expert (Nf rounded up to whole stages, so that every expert's columns
+    // start on a block column)
+    int64_t gstride;
 };
 
 // MFMA operands of one k-step for a wavefront's 128 x 128 quarter
@@ -162,6 +167,12 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         cvalid = u.s1 - c0 < BT ? u.s1 - c0 : BT;
         klen = p.Nf;
         r0 = tile.row * BT;                      // first feature row (plain order)
+        if (EPI != PMN_EPI_SWIGLU) {
+            // the last feature tile of an N that is not a multiple of 256: rows past it re-read
+            // the tile's first block (their outputs are not stored)
+            rvalid = p.Kf - r0 < BT ? p.Kf - r0 : BT;
+            asrows = rvalid;
+        }
         const int64_t wrow0 = (int64_t)g * p.Kf + (EPI == PMN_EPI_SWIGLU ? 0 : r0);
         acode = p.a;
         arb0 = wrow0 >> 4;                       // (the SwiGLU tile maps each piece itself)
@@ -186,10 +197,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         asc = p.ae + p0;
         asld = p.Pb;
         asrows = p.Pb - p0;                      // scale columns of this tile inside the array
-        bcode = p.b + (int64_t)g * ((FP4 ? p.Nf / 2 : p.Nf) >> 6) * 1024;   // expert g's columns
+        bcode = p.b + (int64_t)g * ((FP4 ? p.gstride / 2 : p.gstride) >> 6) * 1024;   // expert g's columns
         brb0 = c0 >> 4;
-        bsc = p.be + (int64_t)g * (p.Nf / 32) * p.Kf + c0;
+        bsc = p.be + (int64_t)g * (p.gstride / 32) * p.Kf + c0;
         bsld = p.Kf;
+        // the last column tile of a K that is not a multiple of 256
+        cvalid = p.Kf - c0 < BT ? p.Kf - c0 : BT;
+        bsrows = cvalid;
         obase = p.out + r0 * p.Kf;
     } else {
         g = (int)batch;
@@ -205,6 +219,11 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         brb0 = c0 >> 4;
         bsc = p.be + (kbeg / 32) * p.Kf + c0;
         bsld = p.Kf;
+        // the last row / column tiles of an N / K that is not a multiple of 256
+        rvalid = p.Nf - r0 < BT ? p.Nf - r0 : BT;
+        asrows = rvalid;
+        cvalid = p.Kf - c0 < BT ? p.Kf - c0 : BT;
+        bsrows = cvalid;
         obase = p.out + (int64_t)g * p.Nf * p.Kf + r0 * p.Kf;
     }
 
@@ -225,7 +244,7 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
     // the forward's SwiGLU tile takes its A rows (w1 and w3 features) through swiglu_a_row
     const bool remap = MODE == MODE_FWD && EPI == PMN_EPI_SWIGLU && op == 0;
     const int64_t Fh = p.Kf >> 1;
-    const uint8_t* sptr = sbase + (remap ? swiglu_a_row(4 * lane, tile.row, Fh) : (4 * lane < srows ? 4 * lane : 0));
+    const uint8_t* sptr = sbase + (remap ? swiglu_a_row_clamped(4 * lane, tile.row, Fh) : (4 * lane < srows ? 4 * lane : 0));
     const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)lds);   // LDS offset
     const uint32_t cdst = lds0 + op * TILEB + half * 8192;
     const uint32_t sdst = lds0 + 2 * TILEB + op * SCBk + half * (FP4 ? 2 : 1) * BT;
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         // row block of piece pb = half * 8 + i: the SwiGLU tile's A rows come from w1 and w3 in
         // 32-row runs, so each 16-row piece is still one block
         const int pb = half * 8 + i;
-        const int64_t rb = remap ? (((int64_t)g * p.Kf + swiglu_a_row(16 * pb, tile.row, Fh)) >> 4)
+        const int64_t rb = remap ? (((int64_t)g * p.Kf + swiglu_a_row_clamped(16 * pb, tile.row, Fh)) >> 4)
                                  : crb0 + (16 * pb < crows ? pb : 0);
         dma16(cbase + rb * cld + r.kc, cdst + r.so + i * 1024);
     };
@@ -426,6 +445,7 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
                 if (sl < cvalid) {
 #pragma unroll
                     for (int i = 0; i < 4; i++) {
+                        if (r0 + wr * 128 + i * 32 >= Nout) continue;   // past the expert's N
 #pragma unroll
                         for (int q = 0; q < 4; q++) {
                             const int64_t n = r0 + wr * 128 + i * 32 + q * 8 + hh * 4;
@@ -452,12 +472,13 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
         constexpr int OPITCH = 272;                 // bytes per slot row: conflict-free 8-byte writes
         uint8_t* const t0 = lds;
         uint8_t* const te = lds + BT * OPITCH;      // E8M0 tile: 8 bytes per slot
-        auto store_tile = [&](uint8_t* dst, int64_t pitch) {
+        // piece c (16 bytes) of a slot's row is stored if pvalid(c): it lies inside the expert's N
+        auto store_tile = [&](uint8_t* dst, int64_t pitch, auto pvalid) {
 #pragma unroll
             for (int k = 0; k < (BT * 16) / THREADS; k++) {
                 const int q = k * THREADS + tid;
                 const int row = q >> 4, c = q & 15;
-                if (row < cvalid)
+                if (row < cvalid && pvalid(c))
                     *reinterpret_cast<uint4*>(dst + (c0 + row) * pitch + c * 16) =
                         *reinterpret_cast<const uint4*>(t0 + row * OPITCH + c * 16);
             }
@@ -492,9 +513,10 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
                     }
                 }
                 __syncthreads();
-                if (phase == 0) store_tile(A + n0 * 2, F * 2);
-                else if (phase == 1) store_tile(Hs + n0 * 2, Nout * 2);
-                else store_tile(Hs + (F + n0) * 2, Nout * 2);
+                auto fvalid = [&](int c) { return n0 + c * 8 < F; };   // 8 features per piece
+                if (phase == 0) store_tile(A + n0 * 2, F * 2, fvalid);
+                else if (phase == 1) store_tile(Hs + n0 * 2, Nout * 2, fvalid);
+                else store_tile(Hs + (F + n0) * 2, Nout * 2, fvalid);
             }
         } else {
             // RHT32 + S2F6: each block's 32 feature rows are one aligned chunk of the slot's row
@@ -510,45 +532,65 @@ __global__ __launch_bounds__(bwd::THREADS, 1) void k_mxfp8_grouped_gemm(Mx8Args 
                 }
             }
             __syncthreads();
-            store_tile(static_cast<uint8_t*>(p.yout) + r0, Nout);
-            if (tid < cvalid)
-                *reinterpret_cast<uint2*>(p.ye8m0 + (c0 + tid) * (Nout >> 5) + (r0 >> 5)) =
-                    *reinterpret_cast<const uint2*>(te + tid * 8);
+            store_tile(static_cast<uint8_t*>(p.yout) + r0, Nout, [&](int c) { return r0 + c * 16 < Nout; });
+            if (tid < cvalid) {
+                // the tile's 8 chunk scales; an N that is not a multiple of 256 has fewer in its
+                // last tile, and its rows of scales are then not 8-byte aligned
+                uint8_t* const d = p.ye8m0 + (c0 + tid) * (Nout >> 5) + (r0 >> 5);
+                if ((Nout & 255) == 0) {
+                    *reinterpret_cast<uint2*>(d) = *reinterpret_cast<const uint2*>(te + tid * 8);
+                } else {
+                    const int64_t nc = (Nout - r0) >> 5;
+#pragma unroll
+                    for (int c = 0; c < 8; c++)
+                        if (c < nc) d[c] = te[tid * 8 + c];
+                }
+            }
         }
         return;
     }
 
     // epilogue: block (i, j): lane holds column c = c0 + wc*128 + j*32 + lane%32 and tile rows
-    // wr*128 + i*32 + (v/4)*8 + hh*4 + v%4
+    // wr*128 + i*32 + (v/4)*8 + hh*4 + v%4. Stores are nontemporal: the fp32 gradients are not
+    // read again by this pass, and streaming them past the caches measured faster. A whole tile
+    // (every tile of the pages' shapes but the last slot tile of each expert in dgrad) stores
+    // without per-value checks.
+    auto store_blocks = [&](auto masked) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+        for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int64_t col = c0 + wc * 128 + j * 32 + lrow;
+            for (int j = 0; j < 4; j++) {
+                const int64_t col = c0 + wc * 128 + j * 32 + lrow;
+                const bool cok = col < p.Kf;        // a K that is not a multiple of 256
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
-                // nontemporal: the fp32 gradients are not read again by this pass, and streaming
-                // them past the caches measured faster
-                if (rl < rvalid) __builtin_nontemporal_store(acc[i][j][v], obase + rl * p.Kf + col);
+                for (int v = 0; v < 16; v++) {
+                    const int64_t rl = wr * 128 + i * 32 + (v >> 2) * 8 + hh * 4 + (v & 3);
+                    if (!decltype(masked)::value || (cok && rl < rvalid))
+                        __builtin_nontemporal_store(acc[i][j][v], obase + rl * p.Kf + col);
+                }
+                // one block at a time: keeps the accumulators in AGPRs until they are stored
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // one block at a time: keeps the accumulators in AGPRs until they are stored
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    };
+    if (rvalid == BT && cvalid == BT)
+        store_blocks(std::integral_constant<bool, false>());
+    else
+        store_blocks(std::integral_constant<bool, true>());
 }
 
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
-                              hipStream_t stream, bool fp4)
+                              hipStream_t stream, bool fp4, int64_t Nk)
 {
     if (M == 0 || G == 0) return hipSuccess;
-    const int64_t rt = (M + bwd::BT - 1) / bwd::BT + G, ct = Kf / bwd::BT;
+    const int64_t rt = (M + bwd::BT - 1) / bwd::BT + G, ct = (Kf + bwd::BT - 1) / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
     const int64_t bpv = fp4 ? 2 : 1;   // values per byte
-    Mx8Args p{dq, de, Nf / bpv, wt, wte, (int64_t)G * Nf / bpv, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN,
-              nullptr, nullptr, nullptr, 0u};
+    // dY rows and each expert's W^T columns are Nk (Nf rounded up to whole stages) wide
+    Mx8Args p{dq, de, Nk / bpv, wt, wte, (int64_t)G * Nk / bpv, offsets, po, Pb, G, Nf, Kf, dx, rt, ct, SM, SN,
+              nullptr, nullptr, nullptr, 0u, Nk};
     dim3 grid((unsigned)xcd_grid(rt, ct, SM, SN));
     if (fp4)
         hipLaunchKernelGGL((k_mxfp8_grouped_gemm<MODE_DGRAD, PMN_EPI_F32, true>), grid, dim3(bwd::THREADS), 0, stream, p);
@@ -563,7 +605,9 @@ hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t*
                             hipStream_t stream)
 {
     if (M == 0 || G == 0) return hipSuccess;
-    const int64_t rt = N / bwd::BT, ct = (M + bwd::BT - 1) / bwd::BT + G;
+    // a feature tile is 256 rows of one expert (SwiGLU: 128 features of w1 and the same of w3)
+    const int64_t rt = epilogue == PMN_EPI_SWIGLU ? (N / 2 + 127) / 128 : (N + bwd::BT - 1) / bwd::BT;
+    const int64_t ct = (M + bwd::BT - 1) / bwd::BT + G;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
     const int64_t Kp = (K + 63) & ~(int64_t)63;   // blocked rows: K rounded up to whole 64-byte blocks
@@ -592,7 +636,7 @@ hipError_t launch_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8
                               int64_t Nf, int64_t Kf, float* dw, hipStream_t stream, bool fp4)
 {
     if (G == 0) return hipSuccess;
-    const int64_t rt = Nf / bwd::BT, ct = Kf / bwd::BT;
+    const int64_t rt = (Nf + bwd::BT - 1) / bwd::BT, ct = (Kf + bwd::BT - 1) / bwd::BT;
     int SM, SN;
     xcd_shape(rt, ct, SM, SN);
     const int64_t ldb = fp4 ? ld / 2 : ld;   // code bytes per row

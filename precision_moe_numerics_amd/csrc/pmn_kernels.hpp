@@ -66,12 +66,14 @@ hipError_t launch_gemm_fwd(const uint8_t* a_codes, const uint8_t* a_scales, cons
                            void* out_aux, hipStream_t stream);
 
 // Grouped MXFP8 GEMMs. Code operands are in the blocked layout; all E8M0 operands are
-// k-block-major: de [Nf/32 x Pb] (padded slot columns, po), wte [G*Nf/32 x Kf], dte [Pb/32 x Nf],
-// xte [Pb/32 x Kf]. The forward takes W8 [G*N rows x roundup(K, 64)] and X8 at padded slot rows.
+// k-block-major: de [Nf/32 x Pb] (padded slot columns, po), wte [G*Nk/32 x Kf] (Nk = Nf rounded up
+// to whole stages of 64 E4M3 or 128 E2M1 values), dte [Pb/32 x Nf], xte [Pb/32 x Kf]. The forward takes W8 [G*N rows x roundup(K, 64)] and X8 at padded slot rows.
 hipError_t launch_mxfp8_dgrad(const uint8_t* dq, const uint8_t* de, const uint8_t* wt,
                               const uint8_t* wte, const int64_t* offsets, const int64_t* po,
                               int64_t Pb, int G, int64_t M, int64_t Nf, int64_t Kf, float* dx,
-                              hipStream_t stream, bool fp4 = false);
+                              hipStream_t stream, bool fp4, int64_t Nk);
+// o[g] = g * step for g = 0 .. G (device), one thread per entry
+hipError_t launch_iota_offsets(int64_t* o, int G, int64_t step, hipStream_t stream);
 
 hipError_t launch_mxfp8_fwd(const uint8_t* wq, const uint8_t* we, const uint8_t* xq, const uint8_t* xe,
                             const int64_t* offsets, const int64_t* po, int64_t Pb, int G, int64_t M, int64_t N,

@@ -550,10 +550,14 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_kbm(const uint16_t* __restri
                 e = mxfp4_block<SR>(w, r, kb, N, seed, stream_id, o);
                 if (BLK) {
                     // k-block kb = chunk kb % 4 of 64-byte column kb / 4
+                    // rows are whole 64-byte columns (N rounded up to 128 values); with N not a
+                    // multiple of 128 the last column's chunks past N are not written (the GEMM
+                    // gives those k-blocks the scale 2^-127 on both operands, and every E2M1 code
+                    // is finite)
                     const int64_t pr = pcol[t >> 2];
                     const int r16 = (int)(pr & 15), x = (r16 >> 2) & 3, c = (int)(kb & 3);
-                    *reinterpret_cast<uint4*>(out + ((pr >> 4) * (N >> 7) + (kb >> 2)) * 1024 + r16 * 64 + ((c ^ x) << 4)) =
-                        make_uint4(o[0], o[1], o[2], o[3]);
+                    *reinterpret_cast<uint4*>(out + ((pr >> 4) * ((N + 127) >> 7) + (kb >> 2)) * 1024 + r16 * 64 +
+                                              ((c ^ x) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
                 } else {
                     reinterpret_cast<uint4*>(out)[r * nb + kb] = make_uint4(o[0], o[1], o[2], o[3]);
                 }
@@ -594,7 +598,6 @@ hipError_t launch_mxfp8_rows(const uint16_t* x, int64_t M, int64_t N, bool sr, u
     const int64_t nb = N / 32;
     if (M * nb == 0) return hipSuccess;
     if ((fp4 || blocked) && padded_offsets == nullptr && ld_e8m0 == 0) return hipErrorInvalidValue;   // k-block-major only
-    if (blocked && fp4 && N % 128 != 0) return hipErrorInvalidValue;
     if (padded_offsets == nullptr && ld_e8m0 == 0) {
         const int64_t grid = (M * nb + 255) / 256;
         if (sr)

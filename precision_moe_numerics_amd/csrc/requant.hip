@@ -90,6 +90,18 @@ __global__ void k_padded_offsets(const int64_t* offsets, int G, int64_t M, int64
     }
 }
 
+__global__ void k_iota_offsets(int64_t* o, int G, int64_t step)
+{
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g <= G) o[g] = (int64_t)g * step;
+}
+
+hipError_t launch_iota_offsets(int64_t* o, int G, int64_t step, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_iota_offsets, dim3((unsigned)((G + 1 + 255) / 256)), dim3(256), 0, stream, o, G, step);
+    return hipGetLastError();
+}
+
 enum { SRC_NVFP4 = 0, SRC_BF16 = 1 };
 
 struct TransposeArgs {

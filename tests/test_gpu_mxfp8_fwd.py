@@ -60,13 +60,15 @@ def swiglu_bound(h1, h3, aref):
 
 
 CASES = [([300], 256, 192, None), ([10, 0, 300, 77], 512, 256, 200), ([256, 513], 256, 1024, 1000),
-         ([37, 1, 90], 512, 96, None), ([64, 0, 5], 256, 160, 40), ([1], 256, 32, None)]
+         ([37, 1, 90], 512, 96, None), ([64, 0, 5], 256, 160, 40), ([1], 256, 32, None),
+         # N not a multiple of 256: a partial last feature tile (32 or 96 of its rows exist)
+         ([70, 300, 1], 288, 96, None), ([5, 0, 600], 352, 160, 700)]
 
 
 @pytest.mark.parametrize("counts,N,K,gather_rows", CASES)
 def test_mxfp8_fwd_f32_bf16_and_operands(P, counts, N, K, gather_rows):
     """Ragged and empty groups, a gather, K a multiple of 64 and K = 32 mod 64 (a half-full last
-    stage), one and several tiles per dimension."""
+    stage), one and several tiles per dimension, N not a multiple of 256."""
     d = _layer(counts, N, K, gather_rows)
     M, G = d["M"], d["G"]
     ws = torch.empty((P._lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, G, N, K),), dtype=torch.uint8, device=DEV)
@@ -102,7 +104,8 @@ def test_mxfp8_fwd_f32_bf16_and_operands(P, counts, N, K, gather_rows):
     assert np.array_equal(w8[o_xe:o_xe + K // 32 * Pb].reshape(K // 32, Pb)[:, pcol].T, d["xe"][rows])
 
 
-@pytest.mark.parametrize("counts,F,K,gather_rows", [([130, 0, 301], 128, 256, 250), ([40, 300], 256, 96, None)])
+@pytest.mark.parametrize("counts,F,K,gather_rows", [([130, 0, 301], 128, 256, 250), ([40, 300], 256, 96, None),
+                                                    ([40, 300], 160, 96, None)])
 def test_mxfp8_fwd_swiglu(P, counts, F, K, gather_rows):
     d = _layer(counts, 2 * F, K, gather_rows, seed=210)
     M = d["M"]
@@ -123,7 +126,7 @@ def test_mxfp8_fwd_swiglu(P, counts, F, K, gather_rows):
     assert none is None and torch.equal(a2, a)
 
 
-@pytest.mark.parametrize("counts,N,K", [([70, 256, 3], 512, 192), ([300, 1], 256, 96)])
+@pytest.mark.parametrize("counts,N,K", [([70, 256, 3], 512, 192), ([300, 1], 256, 96), ([300, 1], 288, 96)])
 def test_mxfp8_fwd_rht_epilogue(P, counts, N, K):
     from precision_moe_numerics_amd import inputs as I
     d = _layer(counts, N, K, gather_rows=120, seed=220)
@@ -154,7 +157,8 @@ def test_mxfp8_fwd_argument_errors(P):
     s = P._stream()
     call = lambda N, K, epi=0, o=None, e=None, wsb=need: lib.moe_grouped_gemm_fwd_mxfp8(
         p(x), 64, None, p(w), p(off), 1, 64, N, K, epi, 0, o if o is not None else p(out), e, None, p(ws), wsb, s)
-    assert call(128, 256) == -2                       # N % 256
+    assert call(144, 256) == -2                       # N % 32
+    assert call(96, 256, epi=2) == -2                 # SwiGLU: N % 64
     assert call(256, 48) == -2                        # K % 32
     assert call(256, 256, epi=7) == -1                # epilogue
     assert call(256, 256, epi=3) == -1                # RHT without out_e8m0

@@ -505,6 +505,38 @@ def test_gemm_bwd_many_small_groups(P, I, fp4):
             assert np.all(npy(db)[g * N:(g + 1) * N] == 0)
 
 
+@pytest.mark.parametrize("fp4", [False, True])
+@pytest.mark.parametrize("counts,N,K,gather_rows", [([40, 0, 333, 227], 288, 96, 400), ([129, 70], 96, 352, None)])
+def test_gemm_bwd_edge_shapes(P, I, counts, N, K, gather_rows, fp4):
+    """N and K that are not multiples of 256 (nor N of 64): dgrad contracts over N rounded up to a
+    whole stage (W^T re-quantized per expert, each expert's columns padded with zero codes; dY's
+    last block column half or partly empty), and the last row / column tiles of dX and dW are
+    partial. Both gradients against the oracle; the padded W^T bit-exact with the oracle's."""
+    d = _moe_small(P, I, counts, N, K, gather_rows, seed=87)
+    M, G = d["M"], len(counts)
+    dy = I.normal((M, N), 1e-3, 88)
+    flags = P.BWD_DGRAD | P.BWD_WGRAD | (P.BWD_FP4 if fp4 else 0)
+    da, db, ws = P.moe_grouped_gemm_bwd(dy.to(DEV), d["xq"], d["wq"], d["goff"], M, N, flags=flags,
+                                        gather=d["ggather"], seed=13, rng_stream_a=2, rng_stream_b=3, rng_stream_dy=4)
+    target = O.TARGET_E2M1 if fp4 else O.TARGET_E4M3
+    rq, re = O.mxfp8_quantize_rows(dy, target=target)
+    rwt, rwte = O.requant_transpose_sr(d["rwq"], target=target, seed=13, stream=3)
+    rt, rte = O.mxfp8_quantize_cols(dy, offsets=d["offsets"], target=target)
+    rxt, rxte = O.requant_transpose_sr(d["rxq"], gather=d["gather"], offsets=d["offsets"], target=target, seed=13,
+                                       stream=2)
+    assert rel_fro(npy(da), O.gemm_mxfp8_dgrad(rq, re, rwt, rwte, d["offsets"], N, K, target=target)) <= 2e-3
+    assert rel_fro(npy(db), O.gemm_mxfp8_wgrad(rt, rte, rxt, rxte, d["offsets"], N, K, target=target)) <= 2e-3
+    if not fp4:
+        Nk = (N + 63) // 64 * 64
+        v = P.bwd_workspace_views(ws, M, G, N, K)
+        wt = unblock(npy(v["wt"]), K, G * Nk)
+        wte = npy(v["wte"]).T
+        for g in range(G):
+            assert np.array_equal(wt[:, g * Nk:g * Nk + N], rwt[:, g * N:(g + 1) * N]), g
+            assert np.all(wt[:, g * Nk + N:(g + 1) * Nk] == 0), g
+            assert np.array_equal(wte[:, g * Nk // 32:(g * Nk + N) // 32], rwte[:, g * N // 32:(g + 1) * N // 32]), g
+
+
 def test_gemm_bwd_sr_gradients_deterministic(P, I):
     counts, N, K = [200, 56], 256, 256
     d = _moe_small(P, I, counts, N, K, seed=90)
