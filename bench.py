@@ -61,6 +61,8 @@ STREAM_MIXES = {
     "swiglu_bwd": (2, 1),           # da fp32 + h13 bf16 in (8 B) : dh13 bf16 out (4 B) per FFN element
 }
 CALIB_GRID = 4097                   # grid of the one calibration copy (1 GiB read + 1 GiB written)
+# the roofline kernel in the traces: the NVFP4 forward with the SwiGLU epilogue, K a multiple of 64
+ROOF_KERNEL = "pmn::k_nvfp4_grouped_gemm<2, false>"
 
 
 def parse():
@@ -597,11 +599,11 @@ def summarize_profiles(d):
         md.append(f"| `{k[0]}` | {k[1]},{k[2]} | {len(v)} | {sum(v) / len(v) / 1e3:.1f} |")
     if bench:
         r = bench["roofline"]
-        gem = [v for k, v in agg.items() if k[0].startswith("pmn::k_nvfp4_grouped_gemm<2>")]
+        gem = [v for k, v in agg.items() if k[0].startswith(ROOF_KERNEL)]
         if gem:
             v = max(gem, key=len)
             avg = sum(v) / len(v) / 1e6
-            md += ["", f"Dominant kernel: `k_nvfp4_grouped_gemm<2>` (w13 forward + SwiGLU) averages {avg:.3f} ms per "
+            md += ["", f"Dominant kernel: `{ROOF_KERNEL[5:]}` (w13 forward + SwiGLU) averages {avg:.3f} ms per "
                        f"launch in this trace; bench.py in the same lease measured {r['ms_per_launch']:.3f} ms by HIP "
                        f"events ({r['achieved']:.0f} TFLOP/s, frac {r['frac']:.3f} of {r['peak']:.0f}); from the "
                        f"trace: {r['flops_per_launch'] / (avg * 1e-3) / 1e12:.0f} TFLOP/s, frac "
@@ -639,7 +641,7 @@ def summarize_profiles(d):
         w = sum(wr.get(k, [0.0])) / max(len(wr.get(k, [])), 1) * fw * 1024 / 1e9
         tmd.append(f"| `{k[0]}` | {k[1]} | {len(fe[k])} | {f:.3f} | {w:.3f} |")
     open(os.path.join(out_dir, "ep48_layer_step_hbm_traffic.md"), "w").write("\n".join(tmd) + "\n")
-    key = [k for k in fe if k[0].startswith("pmn::k_nvfp4_grouped_gemm<2>")]
+    key = [k for k in fe if k[0].startswith(ROOF_KERNEL)]
     key = max(key, key=lambda k: int(k[1]))
     fetch = sum(fe[key]) / len(fe[key]) * ff * 1024
     write = sum(wr[key]) / len(wr[key]) * fw * 1024
