@@ -218,7 +218,7 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
     f16x8 fa[2][4], fb[2][4];
     // Dequantize half `part` (values 4 part .. 4 part + 3) of fragment f of substep s (of stage
     // kt) into buffer b. The two block scales of a code half convert together (E4M3 -> fp16 is
-    // exact); substep s takes scale s / 2. TAIL: the stage may be the half-tail one.
+    // exact); substep s takes scale s / 2. TAIL: the stage may be the last, partly filled one.
     auto convert = [&](int kt, int s, int f, int b, int part, auto tail) {
         const uint4 c = s < 4 ? rawA[f] : rawB[f];
         const uint32_t w = (s & 3) == 0 ? c.x : (s & 3) == 1 ? c.y : (s & 3) == 2 ? c.z : c.w;
@@ -299,7 +299,7 @@ PMN_DEV void nvfp4_gemm_tile(const FwdArgs& p, uint8_t* lds, int g, int64_t m0, 
         convert(0, 0, f, 0, 0, Tail());
         convert(0, 0, f, 0, 1, Tail());
     }
-    // the last two stages dequantize values of the last stage, which may be the half-tail one
+    // the last two stages dequantize values of the last stage, which may be partly filled
     int kt = 0;
     for (; kt + 2 < KT; kt++) stage(kt, Full());
     for (; kt < KT; kt++) stage(kt, Tail());
