@@ -560,14 +560,14 @@ def _find_csv(d, suffix):
     raise FileNotFoundError(f"no *{suffix} under {d}")
 
 
-def summarize_profiles(d):
+def summarize_profiles(d, out_dir=None):
     """Write profiles/*.md (and the forward GEMM's traffic record) from the rocprofv3 CSVs of the
-    PROFILE_COMMANDS runs under d (subfolders kt, fetch, write, clock, and bench.json: the
-    benchmark line of the same lease)."""
+    PROFILE_COMMANDS runs under d (subfolders kt, fetch, write, clock, valu, and bench.json: the
+    benchmark line of the same lease); out_dir defaults to the repository's profiles/."""
     import csv
     import hashlib
     from collections import defaultdict
-    out_dir = os.path.join(ROOT, "profiles")
+    out_dir = out_dir or os.path.join(ROOT, "profiles")
     bench = None
     bp = os.path.join(d, "bench.json")
     if os.path.exists(bp):
