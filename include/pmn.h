@@ -111,6 +111,24 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int mode, int64_t 
                    const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out,
                    pmn_stream_t stream);
 
+/*
+ * The same quantization with a caller-provided workspace (device memory, 16-byte aligned, at
+ * least nvfp4_quantize_ws_size() bytes; PMN_EWORKSPACE otherwise). Outputs are bit-identical to
+ * nvfp4_quantize's. In the weight mode with outer_in == NULL, the per-group amax that must
+ * precede every block ([AREX] "配方的代价:预训练约 2% 的计算效率": one outer scale per expert
+ * matrix) is then taken without a second read of x: when a group has at most 7 * 512 * (compute
+ * units) blocks of 16 (one expert matrix of 2048 x 7168 on MI355X), one cooperative launch of one
+ * 512-thread workgroup per compute unit holds each group in registers while the workgroups
+ * exchange their partial maxima through the workspace. Other modes and shapes take the two
+ * reads, as nvfp4_quantize does. The workspace's contents need no initialization (the call
+ * clears what it uses, with a kernel on the stream); calls that overlap in time must not share
+ * one workspace.
+ */
+size_t nvfp4_quantize_ws_size(void);
+int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64_t rows_per_outer,
+                      const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out, void* ws,
+                      size_t ws_bytes, pmn_stream_t stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Backward operand preparation   [AREX] "转置打散分组,随机舍入保住期望值"; [LHC] (dequantize,   */
 /* transpose in higher precision, re-quantize to MXFP8 with stochastic rounding; the           */

@@ -25,6 +25,8 @@ _SIGS = {
     "pmn_version": (I32, []),
     "pmn_padded_bound": (I64, [I64, I32]),
     "nvfp4_quantize": (I32, [P, I64, I64, I32, I64, P, P, P, P, P]),
+    "nvfp4_quantize_ws_size": (SZ, []),
+    "nvfp4_quantize_ws": (I32, [P, I64, I64, I32, I64, P, P, P, P, P, SZ, P]),
     "requant_transpose_sr_mxfp8": (I32, [P, P, P, I64, I64, I64, P, I64, P, I32, I32, U64, U32, P, P, I64, P, P]),
     "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, I32, U64, U32, P, P, I64, P, P]),
     "rht32_s2f6_quantize": (I32, [P, I32, I64, I64, U32, P, P, P]),
@@ -148,9 +150,16 @@ class NVFP4:
         return self.codes.shape[1] * 2
 
 
+def nvfp4_quantize_ws_size() -> int:
+    return _lib.nvfp4_quantize_ws_size()
+
+
 def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int = 1,
-                   outer_in: Optional[torch.Tensor] = None, out: Optional[NVFP4] = None) -> NVFP4:
-    """NVFP4 of x; `out` (optional) supplies the output tensors to write into."""
+                   outer_in: Optional[torch.Tensor] = None, out: Optional[NVFP4] = None,
+                   workspace: Optional[torch.Tensor] = None) -> NVFP4:
+    """NVFP4 of x; `out` (optional) supplies the output tensors to write into. With `workspace`
+    (uint8, at least nvfp4_quantize_ws_size() bytes) the call goes through nvfp4_quantize_ws: the
+    same outputs, weights taken in one read of x."""
     _need(x.dtype == torch.bfloat16 and x.dim() == 2, "x must be bf16 [rows, cols]")
     R, Cc = x.shape
     dev = x.device
@@ -164,8 +173,14 @@ def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int =
         _tensor(codes, (R, Cc // 2), torch.uint8, "out.codes")
         _tensor(scales, (R, Cc // 16), torch.uint8, "out.scales")
         _tensor(outer, (n_outer,), torch.float32, "out.outer")
-    _check(_lib.nvfp4_quantize(_ptr(x), R, Cc, mode, rows_per_outer, _ptr(outer_in), _ptr(codes), _ptr(scales),
-                               _ptr(outer), _stream()), "nvfp4_quantize")
+    if workspace is None:
+        _check(_lib.nvfp4_quantize(_ptr(x), R, Cc, mode, rows_per_outer, _ptr(outer_in), _ptr(codes),
+                                   _ptr(scales), _ptr(outer), _stream()), "nvfp4_quantize")
+    else:
+        _need(workspace.dtype == torch.uint8, "workspace must be uint8")
+        _check(_lib.nvfp4_quantize_ws(_ptr(x), R, Cc, mode, rows_per_outer, _ptr(outer_in), _ptr(codes),
+                                      _ptr(scales), _ptr(outer), _ptr(workspace), workspace.numel(), _stream()),
+               "nvfp4_quantize_ws")
     return NVFP4(codes, scales, outer, rows_per_outer)
 
 

@@ -190,6 +190,28 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int mode, int64_t 
                                              scales, outer_out, hs(stream), mode == PMN_NVFP4_WEIGHT_2D));
 }
 
+size_t nvfp4_quantize_ws_size(void) { return pmn::nvfp4_weight_1pass_ws_bytes(); }
+
+int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64_t rows_per_outer,
+                      const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out, void* ws,
+                      size_t ws_bytes, pmn_stream_t stream)
+{
+    if (mode != PMN_NVFP4_WEIGHT && mode != PMN_NVFP4_ACT && mode != PMN_NVFP4_WEIGHT_2D) return PMN_EINVAL;
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows_per_outer < 1 || rows % rows_per_outer != 0)
+        return PMN_ESHAPE;
+    if (mode == PMN_NVFP4_WEIGHT_2D && (rows % 16 != 0 || rows_per_outer % 16 != 0)) return PMN_ESHAPE;
+    if (rows == 0) return PMN_OK;
+    if (!x || !codes || !scales || !outer_out) return PMN_EINVAL;
+    if (!ws || ws_bytes < nvfp4_quantize_ws_size()) return PMN_EWORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(outer_out, 4) || (outer_in && !aligned(outer_in, 4)) ||
+        !aligned(ws, 16))
+        return PMN_EALIGN;
+    return status(pmn::launch_nvfp4_quantize(static_cast<const uint16_t*>(x), rows, cols,
+                                             mode == PMN_NVFP4_ACT, rows_per_outer, outer_in, codes,
+                                             scales, outer_out, hs(stream), mode == PMN_NVFP4_WEIGHT_2D, ws,
+                                             ws_bytes));
+}
+
 static int check_groups(int64_t M, const int64_t* offsets, int G, int64_t ld)
 {
     if (M < 0 || G < 0 || (offsets == nullptr) != (G == 0)) return PMN_ESHAPE;

@@ -14,9 +14,14 @@ namespace pmn {
 // per byte (slot 2j in the low nibble), the operand format of the FP4 backward GEMMs
 constexpr int TARGET_E2M1_PACKED = 2;
 
+// ws: NULL, or at least nvfp4_weight_1pass_ws_bytes() of device memory, which lets the weight
+// mode (one candidate, computed outer scales) read x once when the device holds a whole group of
+// rows in registers (cooperative launch); otherwise the group amax and the blocks take two reads.
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
-                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square = false);
+                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square = false,
+                                 void* ws = nullptr, size_t ws_bytes = 0);
+size_t nvfp4_weight_1pass_ws_bytes();
 
 // Row-wise MXFP8. With padded_offsets null the E8M0 scales are row-major [M x N/32]; otherwise
 // they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column

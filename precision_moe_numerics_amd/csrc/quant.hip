@@ -332,11 +332,240 @@ __global__ void k_copy_f32(const float* __restrict__ a, float* __restrict__ b, i
     if (i < n) b[i] = a[i];
 }
 
+// ------------------------------------------------------------------------------------------
+// Weights in one read. The per-(expert, matrix) outer scale needs the whole matrix's amax before
+// any block, and the Infinity Cache does not serve a second pass faster than HBM. Here the whole
+// chip holds one matrix at a time: one 512-thread workgroup per CU (a cooperative launch, so all
+// are resident together), thread t of T taking blocks t, t + T, .. (W1P_NBT of them).
+//
+// Round m: matrix m + 1 (copied into the LDS during the previous round) moves into registers,
+// the copies of matrix m + 2 are issued, matrix m + 1's partial amax is published, matrix m's
+// amax is gathered from every workgroup's word, and matrix m (in registers since the previous
+// round) is quantized while matrix m + 2 arrives. The copies go global -> LDS without registers
+// (each lane's 16 bytes land at its own LDS position), so the kernel waits for them with exact
+// counts: loads into registers would make the compiler wait for every outstanding load wherever
+// stores are pending too.
+//
+// A workgroup's partial amax is a max of |bf16| values, so it is one of them: a word is
+// (m + 1) << 16 | its 16 bits, published in slot m % 4 of an array in the workspace (a workgroup
+// can be at most three rounds ahead of the slowest, so four slots never overwrite a word still
+// awaited). The words are cleared before the launch. Codes, scales and outer scales are those of
+// k_nvfp4_given.
+// ------------------------------------------------------------------------------------------
+constexpr int W1P_THREADS = 512;
+constexpr int W1P_WAVES = W1P_THREADS / 64;
+constexpr int W1P_NBT = 7;          // blocks per thread per matrix
+constexpr int W1P_MAX_WG = 512;     // workspace sized for up to this many workgroups
+constexpr int64_t W1P_MAX_G = 65535;
+constexpr int W1P_SPIN_LIMIT = 1 << 22;
+
+typedef uint32_t w1p_u32x4 __attribute__((ext_vector_type(4)));
+struct RawBlock16 {
+    w1p_u32x4 lo, hi;
+};
+
+PMN_DEV Block16 unpack_block(const RawBlock16& r)
+{
+    Block16 b;
+    const uint32_t w[8] = {r.lo[0], r.lo[1], r.lo[2], r.lo[3], r.hi[0], r.hi[1], r.hi[2], r.hi[3]};
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        b.x[2 * i] = bf16_lo(w[i]);
+        b.x[2 * i + 1] = bf16_hi(w[i]);
+    }
+    return b;
+}
+
+template <int N>
+PMN_DEV void w1p_wait_loads()
+{
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uint16_t* __restrict__ x, int64_t G,
+                                                                       int64_t group_blocks, float* __restrict__ outer_out,
+                                                                       uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales,
+                                                                       uint32_t* __restrict__ words,
+                                                                       uint32_t* __restrict__ flags)
+{
+    // landing area of the copies: wavefront w, copy c (block c / 2, half c % 2) at [w][c]
+    __shared__ __attribute__((aligned(1024))) uint8_t sdata[W1P_WAVES][2 * W1P_NBT][1024];
+    __shared__ uint32_t swords[W1P_WAVES][64];
+    __shared__ float red_a[W1P_WAVES];
+    __shared__ uint32_t red_w[2][W1P_WAVES];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nwg = gridDim.x;
+    const int64_t T = (int64_t)nwg * W1P_THREADS;
+    const int64_t t0 = (int64_t)blockIdx.x * W1P_THREADS + tid;
+    const uint32_t lds_data = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)&sdata[wave][0][0]);
+    const uint32_t lds_words = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)&swords[wave][0]);
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+
+    // matrix m into the landing area: 14 copies per lane
+    auto copy_in = [&](int64_t m) {
+#pragma unroll
+        for (int k = 0; k < W1P_NBT; k++) {
+            // a thread past the matrix's last block re-reads that block (it changes no max and
+            // is not quantized)
+            const int64_t blk = t0 + k * T;
+            const uint8_t* src = xb + 32 * (m * group_blocks + (blk < group_blocks ? blk : group_blocks - 1));
+            dma16(src, lds_data + (2 * k) * 1024);
+            dma16(src + 16, lds_data + (2 * k + 1) * 1024);
+        }
+    };
+    // the landed copies into registers (the caller has waited for them)
+    auto read_in = [&](RawBlock16 (&b)[W1P_NBT]) {
+#pragma unroll
+        for (int k = 0; k < W1P_NBT; k++) {
+            b[k].lo = *reinterpret_cast<const w1p_u32x4*>(&sdata[wave][2 * k][16 * lane]);
+            b[k].hi = *reinterpret_cast<const w1p_u32x4*>(&sdata[wave][2 * k + 1][16 * lane]);
+        }
+        // every lane's reads are done before its next copies land on the same bytes
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    };
+    // publish this workgroup's max |x| of matrix m (a bf16 value: its upper 16 bits)
+    auto arrive = [&](int64_t m, const RawBlock16 (&b)[W1P_NBT]) {
+        float a = 0.0f;
+#pragma unroll
+        for (int k = 0; k < W1P_NBT; k++) a = fmaxf(a, block_absmax(unpack_block(b[k])));
+        a = wave_max(a);
+        if (lane == 0) red_a[wave] = a;
+        __syncthreads();
+        if (tid == 0) {
+            float v = red_a[0];
+#pragma unroll
+            for (int w = 1; w < W1P_WAVES; w++) v = fmaxf(v, red_a[w]);
+            const uint32_t word = ((uint32_t)(m + 1) << 16) | (__float_as_uint(v) >> 16);
+            __hip_atomic_store(words + (m & 3) * W1P_MAX_WG + blockIdx.x, word, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    // thread u < nwg reads workgroup u's word of matrix m into the LDS (every lane issues one
+    // copy, so that each wavefront's count of outstanding copies is fixed)
+    auto word_in = [&](int64_t m) {
+        dma4(words + (m & 3) * W1P_MAX_WG + (tid < nwg ? tid : 0), lds_words);
+    };
+    // matrix m's amax from the landed words; a word not yet published is read again (boundedly)
+    auto gather = [&](int64_t m) -> float {
+        uint32_t bits = 0;
+        if (tid < nwg) {
+            uint32_t word = swords[wave][lane];
+            const uint32_t tag = (uint32_t)(m + 1);
+            const uint32_t* wp = words + (m & 3) * W1P_MAX_WG + tid;
+            for (int spin = 0; (word >> 16) != tag; spin++) {
+                if (spin == W1P_SPIN_LIMIT) {
+                    // never expected with every workgroup resident; the outputs are then wrong
+                    // and flags[0] says so, but no wavefront waits forever
+                    atomicOr(flags, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                word = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            bits = word & 0xffffu;
+        }
+        // max |bf16| bits = bits of the max (non-negative values order as their bit patterns)
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) bits = max(bits, (uint32_t)__shfl_xor((int)bits, d, 64));
+        if (lane == 0) red_w[m & 1][wave] = bits;
+        __syncthreads();
+        uint32_t r = red_w[m & 1][0];
+#pragma unroll
+        for (int w = 1; w < W1P_WAVES; w++) r = max(r, red_w[m & 1][w]);
+        return __uint_as_float(r << 16);
+    };
+    auto quantize = [&](int64_t m, const RawBlock16 (&b)[W1P_NBT], float s_o) {
+        const bool fast = s_o >= 0x1p-96f;   // uniform per matrix, as in k_nvfp4_rows
+        const float ys = fast ? 1.0f / s_o : 0.0f;
+#pragma unroll
+        for (int k = 0; k < W1P_NBT; k++) {
+            const int64_t blk = t0 + k * T;
+            if (blk < group_blocks) {
+                const Block16 v = unpack_block(b[k]);
+                uint32_t sb;
+                uint2 q;
+                if (fast) quant_block_ab<false, true>(v, block_absmax(v), s_o, sb, q, ys);
+                else quant_block_ab<false, false>(v, block_absmax(v), s_o, sb, q);
+                const int64_t i = m * group_blocks + blk;
+                reinterpret_cast<uint2*>(codes)[i] = q;
+                scales[i] = (uint8_t)sb;
+            }
+        }
+    };
+    // round m: cur holds matrix m (published); matrix m + 1 sits in the landing area
+    auto round = [&](int64_t m, RawBlock16 (&cur)[W1P_NBT], RawBlock16 (&nx)[W1P_NBT]) {
+        word_in(m);
+        const bool more1 = m + 1 < G, more2 = m + 2 < G;
+        if (more1) {
+            w1p_wait_loads<1>();                       // all but the word: matrix m + 1 has landed
+            read_in(nx);
+        }
+        if (more2) copy_in(m + 2);
+        if (more1) arrive(m + 1, nx);
+        // younger than the word: matrix m + 2's copies (and wavefront 0's publishing store)
+        if (more2) w1p_wait_loads<2 * W1P_NBT>();
+        else w1p_wait_loads<0>();
+        const float s_o = outer_from_amax(gather(m));
+        if (blockIdx.x == 0 && tid == 0) outer_out[m] = s_o;
+        quantize(m, cur, s_o);
+    };
+    RawBlock16 b0[W1P_NBT], b1[W1P_NBT];
+    copy_in(0);
+    w1p_wait_loads<0>();
+    read_in(b0);
+    if (G > 1) copy_in(1);
+    arrive(0, b0);
+    for (int64_t m = 0; m < G; m += 2) {
+        round(m, b0, b1);
+        if (m + 1 < G) round(m + 1, b1, b0);
+    }
+}
+
+size_t nvfp4_weight_1pass_ws_bytes() { return (size_t)4 * W1P_MAX_WG * 4 + 256; }
+
+// The one-read path, if the device and the shape allow it; hipErrorNotSupported otherwise (the
+// caller then takes the two passes).
+static hipError_t launch_nvfp4_weight_1pass(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_outer,
+                                            uint8_t* codes, uint8_t* scales, float* outer_out, void* ws,
+                                            size_t ws_bytes, hipStream_t stream)
+{
+    if (ws == nullptr || ws_bytes < nvfp4_weight_1pass_ws_bytes()) return hipErrorNotSupported;
+    int dev = 0, ncu = 0, coop = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_nvfp4_weight_1pass, W1P_THREADS, 0) != hipSuccess)
+        return hipErrorNotSupported;
+    if (!coop || per_cu < 1 || ncu < 1 || ncu > W1P_MAX_WG) return hipErrorNotSupported;
+    int64_t G = rows / rows_per_outer;
+    int64_t group_blocks = rows_per_outer * (cols / 16);
+    if (G > W1P_MAX_G || group_blocks > (int64_t)W1P_NBT * ncu * W1P_THREADS) return hipErrorNotSupported;
+    uint32_t* words = static_cast<uint32_t*>(ws);
+    uint32_t* flags = words + 4 * W1P_MAX_WG;
+    const int64_t nfill = (int64_t)(nvfp4_weight_1pass_ws_bytes() / 4);
+    hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nfill + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(ws), nfill, 0u);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    void* args[] = {(void*)&x, (void*)&G, (void*)&group_blocks, (void*)&outer_out, (void*)&codes, (void*)&scales,
+                    (void*)&words, (void*)&flags};
+    return hipLaunchCooperativeKernel((const void*)k_nvfp4_weight_1pass, dim3((unsigned)ncu), dim3(W1P_THREADS),
+                                      args, 0, stream);
+}
+
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,
                                  int64_t rows_per_outer, const float* outer_in, uint8_t* codes,
-                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square)
+                                 uint8_t* scales, float* outer_out, hipStream_t stream, bool square,
+                                 void* ws, size_t ws_bytes)
 {
     if (rows == 0) return hipSuccess;
+    if (!four_six && !square && outer_in == nullptr && ws != nullptr) {
+        const hipError_t e = launch_nvfp4_weight_1pass(x, rows, cols, rows_per_outer, codes, scales, outer_out, ws,
+                                                       ws_bytes, stream);
+        if (e != hipErrorNotSupported) return e;
+    }
     const int64_t nb = cols / 16;
     const int64_t ngroups = rows / rows_per_outer;
     if (!square && outer_in == nullptr && rows_per_outer == 1 && nb > 128 && nb <= 512) {

@@ -88,6 +88,20 @@ def test_argument_errors_without_launch(lib):
     assert lib.pmn_padded_bound(33, 2) == 64 + 64
 
 
+def test_quantize_with_workspace_argument_errors(lib):
+    """nvfp4_quantize_ws checks its shapes like nvfp4_quantize, then its workspace (missing or
+    smaller than nvfp4_quantize_ws_size(): PMN_EWORKSPACE; not 16-byte aligned: PMN_EALIGN),
+    before any launch."""
+    fake = C.c_void_p(0x1000)     # never dereferenced
+    n = lib.nvfp4_quantize_ws_size()
+    assert n >= 4 * 512 * 4
+    assert lib.nvfp4_quantize_ws(fake, 4, 15, 0, 1, None, fake, fake, fake, fake, n, None) == -2
+    assert lib.nvfp4_quantize_ws(fake, 4096, 256, 0, 2048, None, fake, fake, fake, None, n, None) == -4
+    assert lib.nvfp4_quantize_ws(fake, 4096, 256, 0, 2048, None, fake, fake, fake, fake, n - 1, None) == -4
+    assert lib.nvfp4_quantize_ws(fake, 4096, 256, 0, 2048, None, fake, fake, fake, C.c_void_p(0x1008), n, None) == -3
+    assert lib.nvfp4_quantize_ws(None, 0, 32, 0, 1, None, None, None, None, None, 0, None) == 0
+
+
 def test_zero_size_calls_are_no_ops(lib):
     assert lib.nvfp4_quantize(None, 0, 32, 1, 1, None, None, None, None, None) == 0
     assert lib.rht32_s2f6_quantize(None, 0, 0, 64, 0, None, None, None) == 0
