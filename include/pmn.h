@@ -120,9 +120,10 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int mode, int64_t 
  * units) blocks of 16 (one expert matrix of 2048 x 7168 on MI355X), one cooperative launch of one
  * 512-thread workgroup per compute unit holds each group in registers while the workgroups
  * exchange their partial maxima through the workspace. Other modes and shapes take the two
- * reads, as nvfp4_quantize does. The workspace's contents need no initialization (the call
- * clears what it uses, with a kernel on the stream); calls that overlap in time must not share
- * one workspace.
+ * reads, as nvfp4_quantize does, and so do calls on a capturing stream (a replayed graph would
+ * not guarantee the co-residency) and calls whose cooperative launch the runtime refuses. The
+ * workspace's contents need no initialization (the call clears what it uses, with a kernel on
+ * the stream); calls that overlap in time must not share one workspace.
  */
 size_t nvfp4_quantize_ws_size(void);
 int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64_t rows_per_outer,

@@ -532,6 +532,11 @@ static hipError_t launch_nvfp4_weight_1pass(const uint16_t* x, int64_t rows, int
                                             size_t ws_bytes, hipStream_t stream)
 {
     if (ws == nullptr || ws_bytes < nvfp4_weight_1pass_ws_bytes()) return hipErrorNotSupported;
+    // a captured graph would replay the launch without the co-residency a cooperative launch
+    // guarantees, so a capturing stream takes the two reads
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
+        return hipErrorNotSupported;
     int dev = 0, ncu = 0, coop = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -551,8 +556,14 @@ static hipError_t launch_nvfp4_weight_1pass(const uint16_t* x, int64_t rows, int
     if (e != hipSuccess) return e;
     void* args[] = {(void*)&x, (void*)&G, (void*)&group_blocks, (void*)&outer_out, (void*)&codes, (void*)&scales,
                     (void*)&words, (void*)&flags};
-    return hipLaunchCooperativeKernel((const void*)k_nvfp4_weight_1pass, dim3((unsigned)ncu), dim3(W1P_THREADS),
-                                      args, 0, stream);
+    e = hipLaunchCooperativeKernel((const void*)k_nvfp4_weight_1pass, dim3((unsigned)ncu), dim3(W1P_THREADS), args, 0,
+                                   stream);
+    if (e != hipSuccess) {
+        // a runtime that refuses the cooperative launch: the two reads instead
+        (void)hipGetLastError();
+        return hipErrorNotSupported;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,

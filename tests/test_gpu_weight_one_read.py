@@ -113,3 +113,29 @@ def test_workspace_calls_of_the_other_modes_and_shapes(P, I, ws):
                      P.nvfp4_quantize(x, P.NVFP4_WEIGHT, 128, outer_in=o))
     big = I.normal((2 * 4096, 7168), 0.02, 72, DEV)
     assert identical(P.nvfp4_quantize(big, P.NVFP4_WEIGHT, 4096, workspace=ws), P.nvfp4_quantize(big, P.NVFP4_WEIGHT, 4096))
+
+
+def test_captured_call_takes_the_two_reads(P, I, ws):
+    """Under stream capture the call takes the two reads (a replayed graph would not guarantee the
+    co-residency of a cooperative launch). Each replay, with eager work between replays, gives
+    the eager outputs."""
+    x = I.normal((4 * 256, 512), 0.02, 81, DEV)
+    ref = P.nvfp4_quantize(x, P.NVFP4_WEIGHT, 256)
+    out = P.nvfp4_quantize(x, P.NVFP4_WEIGHT, 256)          # buffers the graph writes into
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                           # warm-up before capture
+        P.nvfp4_quantize(x, P.NVFP4_WEIGHT, 256, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        P.nvfp4_quantize(x, P.NVFP4_WEIGHT, 256, out=out, workspace=ws)
+    for i in range(3):
+        out.codes.zero_()
+        out.scales.zero_()
+        out.outer.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert identical(out, ref), i
+        P.nvfp4_quantize(x, P.NVFP4_ACT)                    # eager work between replays
