@@ -115,10 +115,20 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
     int64_t* po = reinterpret_cast<int64_t*>(ws + L.po);
     hipError_t e = pmn::launch_padded_offsets(offsets, G, M, po, s, pmn::blocked_unit(fp4));
     if (e != hipSuccess) return PMN_ELAUNCH;
-    if (dgrad && M > 0) {
-        e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
-                                   ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
+    // both gradients of an E4M3 backward with dY rounded to nearest: dY's row-wise and column-wise
+    // codes from one read of dY (the same bytes as the two separate quantizations)
+    const bool dy_both = dgrad && wgrad && !fp4 && !sr && M > 0;
+    if (dy_both) {
+        e = pmn::launch_mxfp8_rows_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, L.Pb, ws + L.dq, ws + L.de,
+                                        ws + L.dt, ws + L.dte, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
+    }
+    if (dgrad && M > 0) {
+        if (!dy_both) {
+            e = pmn::launch_mxfp8_rows(static_cast<const uint16_t*>(dy), M, N, sr, seed, rng_stream_dy, ws + L.dq,
+                                       ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
+            if (e != hipSuccess) return PMN_ELAUNCH;
+        }
         if (L.Nk == N) {
             e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
                                     0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true,
@@ -139,9 +149,12 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (wgrad) {
-        e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed, rng_stream_dy + 1,
-                                   ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target, blocked);
-        if (e != hipSuccess) return PMN_ELAUNCH;
+        if (!dy_both) {
+            e = pmn::launch_mxfp8_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, sr, seed,
+                                       rng_stream_dy + 1, ws + L.dt, ws + L.dte, L.Pb, true, nullptr, s, target,
+                                       blocked);
+            if (e != hipSuccess) return PMN_ELAUNCH;
+        }
         e = pmn::launch_requant(a_codes, a_scales, a_outer, K, a_rows_per_outer, gather, M, offsets, G, target, seed,
                                 rng_stream_a, ws + L.xt, ws + L.xte, L.Pb, true, nullptr, s, blocked);
         if (e != hipSuccess) return PMN_ELAUNCH;

@@ -247,6 +247,45 @@ PMN_DEV uint32_t fp4_sr(float y, uint32_t r16)
     return idx | ((__float_as_uint(y) >> 28) & 8u);
 }
 
+// One block of 32 bf16 values (16 words) of row r, k-block kb -> 32 E4M3 codes (8 words, element
+// 0 in the low byte) and the E8M0 exponent e (scale 2^e). SR draws the element index r * N + c.
+template <bool SR>
+PMN_DEV int mxfp8_block(const uint32_t (&w)[16], int64_t r, int64_t kb, int64_t N, uint64_t seed,
+                        uint32_t stream_id, uint32_t (&o)[8])
+{
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; j++) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[j])), fabsf(bf16_hi(w[j]))));
+    const int e = e8m0_exponent<E8M0_E4M3>(amax);
+    if (SR) {
+        const uint64_t idx0 = (uint64_t)r * (uint64_t)N + (uint64_t)(kb * 32);   // multiple of 8
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            uint32_t rw[4];
+            rand16x8(seed, stream_id, (idx0 >> 3) + q, rw);
+            uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                uint32_t word = w[4 * q + j / 2];
+                float v = (j & 1) ? bf16_hi(word) : bf16_lo(word);
+                uint32_t c = e4m3_sr(__builtin_ldexpf(v, -e), sr_operand(rw[j >> 1], j & 1));
+                if (j < 4) lo |= c << (8 * j); else hi |= c << (8 * (j - 4));
+            }
+            o[2 * q] = lo;
+            o[2 * q + 1] = hi;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++) {
+            float v0 = __builtin_ldexpf(bf16_lo(w[2 * q]), -e), v1 = __builtin_ldexpf(bf16_hi(w[2 * q]), -e);
+            float v2 = __builtin_ldexpf(bf16_lo(w[2 * q + 1]), -e), v3 = __builtin_ldexpf(bf16_hi(w[2 * q + 1]), -e);
+            int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+            o[q] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, lo, true);
+        }
+    }
+    return e;
+}
+
 // ---- XCD-aware tile order for the GEMMs ----------------------------------------------------
 //
 // MI355X has 8 XCDs, each with its own L2; workgroup L of a 1-D grid runs on XCD L % 8, and the

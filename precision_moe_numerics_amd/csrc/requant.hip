@@ -526,6 +526,151 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
     return launch_transpose(a, SRC_NVFP4, 1, target, padded_offsets, stream);
 }
 
+// ------------------------------------------------------------------------------------------
+// dY to MXFP8 both ways in one read (the backward's gradient operands, E4M3 by round to nearest
+// even): the row-wise codes that dgrad takes and the column-wise codes (per 32 slots of a group)
+// that wgrad takes, each in the blocked GEMM operand layout, with the same bytes as
+// k_mxfp8_rows_kbm<false, false, true> and k_transpose_quant<SRC_BF16, 0, 0> write separately.
+// A workgroup takes one 64-slot unit of the padded slot space (groups are padded to 64 slots, so
+// the unit lies in one group) and 256 columns: the 64 x 256 bf16 tile is read once into the LDS;
+// then each thread quantizes two row blocks (32 columns of one slot) and one column pair (two
+// columns over 32 slots). Padding slots read as zero.
+// ------------------------------------------------------------------------------------------
+constexpr int RC_COLS = 256;
+constexpr int RC_PITCH = RC_COLS * 2 + 16;   // bytes per tile row: 16-byte row reads of 16 rows cover all banks
+
+__global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restrict__ x, int64_t M, int64_t N,
+                                                        const int64_t* __restrict__ offsets, int G,
+                                                        int64_t Pb, uint8_t* __restrict__ rq,
+                                                        uint8_t* __restrict__ re, uint8_t* __restrict__ cq,
+                                                        uint8_t* __restrict__ ce)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * RC_PITCH];
+    const int t = threadIdx.x;
+    const int64_t p0 = (int64_t)blockIdx.x * 64;          // first padded slot of the unit
+    const int64_t c0 = (int64_t)blockIdx.y * RC_COLS;     // first column
+    const GroupBlock blk = find_block(p0 / 32, offsets, G, M, 64);
+    if (!blk.live) return;                                // workgroup-uniform
+    // slots of the unit that exist: s0 .. s0 + nv - 1
+    int64_t nv = 0;
+    {
+        int64_t end = M;
+        if (offsets) {
+            // the group holding slot s0 ends at the first offset past it
+            int lo = 0, hi = G - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (offsets[mid] <= blk.s0) lo = mid; else hi = mid - 1;
+            }
+            end = offsets[lo + 1] < M ? offsets[lo + 1] : M;
+        }
+        nv = blk.valid == 0 ? 0 : (end - blk.s0 < 64 ? end - blk.s0 : 64);
+    }
+    // ---- the tile: 8 loads of 16 bytes per thread (row t / 32 + 8 i, chunk t % 32)
+    {
+        uint4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int row = (t >> 5) + 8 * i;
+            const int64_t col = c0 + (t & 31) * 8;
+            v[i] = (row < nv && col < N) ? *reinterpret_cast<const uint4*>(x + (blk.s0 + row) * N + col)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+            *reinterpret_cast<uint4*>(tile + ((t >> 5) + 8 * i) * RC_PITCH + (t & 31) * 16) = v[i];
+    }
+    __syncthreads();
+    const int64_t nb = N >> 5;
+
+    // ---- row-wise: unit u = t + 256 i is slot row u % 64, k-block u / 64 of the tile
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int u = t + 256 * i;
+        const int row = u & 63, kbl = u >> 6;
+        const int64_t kb = (c0 >> 5) + kbl;
+        if (row < nv && kb < nb) {
+            uint32_t w[16];
+            const uint4* src = reinterpret_cast<const uint4*>(tile + row * RC_PITCH + kbl * 64);
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint4 a4 = src[q];
+                w[4 * q] = a4.x; w[4 * q + 1] = a4.y; w[4 * q + 2] = a4.z; w[4 * q + 3] = a4.w;
+            }
+            uint32_t o[8];
+            const int e = mxfp8_block<false>(w, 0, kb, N, 0, 0, o);
+            // padded row pr: k-block kb = chunks 2 (kb % 2), 2 (kb % 2) + 1 of 64-byte column kb / 2
+            // of its 1 KB block (16 rows x 64 bytes, chunk c of row r16 at slot c ^ ((r16 / 4) % 4));
+            // with an odd k-block count the last column's second half holds zero codes
+            const int64_t pr = p0 + row;
+            const int r16 = (int)(pr & 15), xs = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
+            uint8_t* b = rq + ((pr >> 4) * ((N + 63) >> 6) + (kb >> 1)) * 1024 + r16 * 64;
+            *reinterpret_cast<uint4*>(b + ((c ^ xs) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<uint4*>(b + (((c + 1) ^ xs) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+            if ((nb & 1) && kb == nb - 1) {
+                *reinterpret_cast<uint4*>(b + (((c + 2) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                *reinterpret_cast<uint4*>(b + (((c + 3) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+            }
+            re[kb * Pb + pr] = (uint8_t)(e + 127);
+        }
+    }
+
+    // ---- column-wise: thread t takes columns 2 (t % 128) and 2 (t % 128) + 1 over slots
+    // 32 (t / 128) .. + 31 of the unit (padding slots are +0)
+    {
+        const int cp = t & 127, sb = t >> 7;
+        const int64_t col = c0 + 2 * cp;
+        if (col < N) {
+            uint32_t pw[32];
+#pragma unroll
+            for (int j = 0; j < 32; j++) pw[j] = *reinterpret_cast<const uint32_t*>(tile + (sb * 32 + j) * RC_PITCH + cp * 4);
+            float amax0 = 0.0f, amax1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; j++) {
+                amax0 = fmaxf(amax0, fabsf(bf16_lo(pw[j])));
+                amax1 = fmaxf(amax1, fabsf(bf16_hi(pw[j])));
+            }
+            const int e0 = e8m0_exponent<E8M0_E4M3>(amax0), e1 = e8m0_exponent<E8M0_E4M3>(amax1);
+            const float s0 = __builtin_ldexpf(1.0f, e0), s1 = __builtin_ldexpf(1.0f, e1);
+            uint32_t o0[8], o1[8];
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                // slots 4q .. 4q + 3 of each column into one word (slot 4q in the low byte)
+                o0[q] = e4m3_rne_pair_scaled_into(0u, bf16_lo(pw[4 * q]), bf16_lo(pw[4 * q + 1]), s0, false);
+                o0[q] = e4m3_rne_pair_scaled_into(o0[q], bf16_lo(pw[4 * q + 2]), bf16_lo(pw[4 * q + 3]), s0, true);
+                o1[q] = e4m3_rne_pair_scaled_into(0u, bf16_hi(pw[4 * q]), bf16_hi(pw[4 * q + 1]), s1, false);
+                o1[q] = e4m3_rne_pair_scaled_into(o1[q], bf16_hi(pw[4 * q + 2]), bf16_hi(pw[4 * q + 3]), s1, true);
+            }
+            // output row c (one per column): 1 KB blocks of 16 rows x 64 bytes, the unit's 64 slots
+            // one block column; this 32-slot block is chunks 2 sb and 2 sb + 1 of the row
+            const int64_t kbo = p0 >> 6, nkb = Pb >> 6;
+#pragma unroll
+            for (int h = 0; h < 2; h++) {
+                const int64_t c = col + h;
+                const uint32_t* o = h ? o1 : o0;
+                const int r16 = (int)(c & 15), xs = (r16 >> 2) & 3;
+                uint8_t* b = cq + ((c >> 4) * nkb + kbo) * 1024 + r16 * 64;
+                *reinterpret_cast<uint4*>(b + (((2 * sb) ^ xs) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(b + (((2 * sb + 1) ^ xs) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+            // E8M0 k-block-major: [Pb/32 x N], 32-slot block (p0 / 32 + sb) at row kb
+            uint8_t* eo = ce + (p0 / 32 + sb) * N + col;
+            eo[0] = (uint8_t)(e0 + 127);
+            eo[1] = (uint8_t)(e1 + 127);
+        }
+    }
+}
+
+hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets, int G,
+                                  int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce,
+                                  hipStream_t stream)
+{
+    if (M == 0 || N == 0 || Pb == 0) return hipSuccess;
+    const dim3 grid((unsigned)(Pb / 64), (unsigned)((N + RC_COLS - 1) / RC_COLS));
+    hipLaunchKernelGGL(k_mxfp8_rows_cols, grid, dim3(256), 0, stream, x, M, N, offsets, G, Pb, rq, re, cq, ce);
+    return hipGetLastError();
+}
+
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
                              uint8_t* out_e8m0, int64_t ld, bool e8m0_kb_major,

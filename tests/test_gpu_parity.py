@@ -432,6 +432,28 @@ def test_gemm_fwd_rht_epilogue_bit_exact(P, I):
     assert rel_fro(npy(y), ref) <= 1e-5
 
 
+@pytest.mark.parametrize("counts,N,K", [([40, 0, 333, 227], 256, 128), ([1, 64, 65, 0, 130], 288, 96),
+                                         ([300, 5, 700], 1024, 64), ([0, 129], 7168, 32)])
+def test_gemm_bwd_dy_both_ways_in_one_read(P, I, counts, N, K):
+    """With both gradients (E4M3, dY by RNE) the call quantizes dY row-wise and column-wise from
+    one read of dY. Its workspace parts equal those of the one-gradient calls, which quantize each
+    orientation separately, byte for byte (the parts the one-gradient call does not write aside):
+    N of 288 (an odd k-block count and a partial last column tile), groups of 1, 64, 65 and 129
+    slots (a padded unit of padding only), empty groups, and 7168 columns."""
+    d = _moe_small(P, I, counts, N, K, seed=90)
+    M, G = d["M"], len(counts)
+    dy = I.normal((M, N), 1e-3, 91).to(DEV)
+    size = P.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, 3)
+    views = {}
+    for flags in (3, 1, 2):
+        ws = torch.zeros((size,), dtype=torch.uint8, device=DEV)
+        P.moe_grouped_gemm_bwd(dy, d["xq"], d["wq"], d["goff"], M, N, flags=flags, seed=3, workspace=ws)
+        views[flags] = P.bwd_workspace_views(ws, M, G, N, K)
+    torch.cuda.synchronize()
+    for name, flags in (("dq", 1), ("de", 1), ("dt", 2), ("dte", 2)):
+        assert torch.equal(views[3][name], views[flags][name]), name
+
+
 @pytest.mark.parametrize("sr", [False, True])
 def test_gemm_bwd_intermediates_and_gradients(P, I, sr):
     """Both gradients in one call: dY's row-wise and column-wise MXFP8 (RNE, or SR on streams 6
