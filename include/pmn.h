@@ -319,6 +319,24 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          size_t workspace_bytes, pmn_stream_t stream);
 
 /*
+ * The w1||w3 backward of a SwiGLU layer with the SwiGLU backward folded into dY's quantization:
+ * moe_grouped_gemm_bwd with both gradients (dgrad -> dx [M x K], wgrad -> dw [G*N x K]) and dY
+ * rounded to nearest, where dY = dh13 [M x N] is not passed but formed from the gradient of the
+ * SwiGLU output da_act (fp32 [M x F], F = N / 2) and the saved pre-activations h13 (bf16
+ * [M x N], h1 in columns 0 .. F-1, h3 in F .. N-1) exactly as swiglu_bwd forms it, and never
+ * written out. N % 64 == 0. The results and the workspace contents equal those of swiglu_bwd
+ * followed by moe_grouped_gemm_bwd(PMN_BWD_DGRAD | PMN_BWD_WGRAD, PMN_RNE). The rounding of dY
+ * is fixed to RNE and there is no FP4 variant; other configurations call the two separately.
+ */
+int moe_grouped_gemm_bwd_swiglu(const float* da_act, const void* h13, const uint8_t* a_codes,
+                                const uint8_t* a_scales, const float* a_outer, int64_t a_rows,
+                                int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
+                                const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
+                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, uint64_t seed,
+                                uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
+                                void* workspace, size_t workspace_bytes, pmn_stream_t stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): moe_grouped_gemm_bwd with its workspace taken from a static
  * device array of the library, PMN_NOALLOC_SCRATCH_BYTES per device, held by each device the

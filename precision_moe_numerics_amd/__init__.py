@@ -34,6 +34,8 @@ _SIGS = {
     "moe_grouped_gemm_bwd_workspace_size": (SZ, [I64, I32, I64, I64, I32]),
     "moe_grouped_gemm_bwd": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32, U64,
                                    U32, U32, U32, P, P, P, SZ, P]),
+    "moe_grouped_gemm_bwd_swiglu": (I32, [P, P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, U64, U32,
+                                          U32, P, P, P, SZ, P]),
     "moe_grouped_gemm_fwd_mxfp8_workspace_size": (SZ, [I64, I32, I64, I64]),
     "moe_grouped_gemm_fwd_mxfp8": (I32, [P, I64, P, P, P, I32, I64, I64, I64, I32, U32, P, P, P, P, SZ, P]),
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
@@ -373,6 +375,40 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
                                      rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da), _ptr(db),
                                      _ptr(workspace), workspace.numel(), _stream()), "moe_grouped_gemm_bwd")
     return da, db, workspace
+
+
+def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVFP4, wq: NVFP4,
+                                offsets: torch.Tensor, M: int, N: int, gather: Optional[torch.Tensor] = None,
+                                seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
+                                workspace: Optional[torch.Tensor] = None, dx=None, dw=None):
+    """The w1||w3 backward with the SwiGLU backward folded into dY's quantization: the results of
+    swiglu_bwd(da_act, h13) followed by moe_grouped_gemm_bwd(..., both gradients, RNE).
+    Returns (dx [M, K] fp32, dw [G*N, K] fp32, workspace)."""
+    K = xq.cols
+    G = offsets.numel() - 1
+    dev = h13.device
+    _tensor(da_act, (M, N // 2), torch.float32, "da_act")
+    _tensor(h13, (M, N), torch.bfloat16, "h13")
+    _nvfp4(xq, "xq")
+    _nvfp4(wq, "wq")
+    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    _index(offsets, G + 1, torch.int64, "offsets")
+    _index(gather, M, torch.int32, "gather")
+    ws_bytes = moe_grouped_gemm_bwd_workspace_size(M, G, N, K, BWD_DGRAD | BWD_WGRAD)
+    if workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    dx = torch.empty((M, K), dtype=torch.float32, device=dev) if dx is None else dx
+    dw = torch.empty((G * N, K), dtype=torch.float32, device=dev) if dw is None else dw
+    _tensor(dx, (M, K), torch.float32, "dx")
+    _tensor(dw, (G * N, K), torch.float32, "dw")
+    _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
+    _check(_lib.moe_grouped_gemm_bwd_swiglu(_ptr(da_act), _ptr(h13), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer),
+                                            xq.rows, xq.rows_per_outer, _ptr(gather), _ptr(wq.codes),
+                                            _ptr(wq.scales), _ptr(wq.outer), wq.rows_per_outer, _ptr(offsets), G, M,
+                                            N, K, seed, rng_stream_a, rng_stream_b, _ptr(dx), _ptr(dw),
+                                            _ptr(workspace), workspace.numel(), _stream()),
+           "moe_grouped_gemm_bwd_swiglu")
+    return dx, dw, workspace
 
 
 def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", offsets: torch.Tensor, M: int, N: int,

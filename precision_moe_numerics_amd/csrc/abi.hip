@@ -82,8 +82,17 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
                          uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, uint32_t rng_stream_dy,
                          float* da, float* db, void* workspace, size_t workspace_bytes, pmn_stream_t stream,
-                         size_t* workspace_needed)
+                         size_t* workspace_needed, bool swiglu, const float* swi_da, const void* swi_h13)
 {
+    const bool swi = swiglu;
+    if (swi) {
+        // dY formed from the SwiGLU backward inside the fused dY quantization only
+        if (flags != (PMN_BWD_DGRAD | PMN_BWD_WGRAD) || dy_rounding != PMN_RNE) return PMN_EINVAL;
+        if (N % 64 != 0) return PMN_ESHAPE;
+        if (M > 0 && (!swi_da || !swi_h13)) return PMN_EINVAL;
+        if (M > 0 && (!aligned(swi_da, 16) || !aligned(swi_h13, 16))) return PMN_EALIGN;
+        dy = swi_h13;   // stands in for dY in the checks below (not read as dY)
+    }
     if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
         return PMN_EINVAL;
     if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
@@ -119,8 +128,11 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
     // codes from one read of dY (the same bytes as the two separate quantizations)
     const bool dy_both = dgrad && wgrad && !fp4 && !sr && M > 0;
     if (dy_both) {
-        e = pmn::launch_mxfp8_rows_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, L.Pb, ws + L.dq, ws + L.de,
-                                        ws + L.dt, ws + L.dte, s);
+        e = swi ? pmn::launch_swiglu_bwd_mxfp8_rows_cols(swi_da, static_cast<const uint16_t*>(swi_h13), M, N / 2,
+                                                         offsets, G, L.Pb, ws + L.dq, ws + L.de, ws + L.dt,
+                                                         ws + L.dte, s)
+                : pmn::launch_mxfp8_rows_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, L.Pb, ws + L.dq,
+                                              ws + L.de, ws + L.dt, ws + L.dte, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (dgrad && M > 0) {
@@ -329,6 +341,20 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
                                      b_scales, b_outer, b_rows_per_outer, offsets, G, M, N, K, flags, dy_rounding,
                                      seed, rng_stream_a, rng_stream_b, rng_stream_dy, da, db, workspace,
                                      workspace_bytes, stream, nullptr);
+}
+
+int moe_grouped_gemm_bwd_swiglu(const float* da_act, const void* h13, const uint8_t* a_codes,
+                                const uint8_t* a_scales, const float* a_outer, int64_t a_rows,
+                                int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
+                                const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
+                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, uint64_t seed,
+                                uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
+                                void* workspace, size_t workspace_bytes, pmn_stream_t stream)
+{
+    return pmn::grouped_gemm_bwd_run(nullptr, a_codes, a_scales, a_outer, a_rows, a_rows_per_outer, gather, b_codes,
+                                     b_scales, b_outer, b_rows_per_outer, offsets, G, M, N, K,
+                                     PMN_BWD_DGRAD | PMN_BWD_WGRAD, PMN_RNE, seed, rng_stream_a, rng_stream_b, 0, dx,
+                                     dw, workspace, workspace_bytes, stream, nullptr, true, da_act, h13);
 }
 
 size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, int64_t K)

@@ -672,14 +672,9 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(const float* __restrict__ da
     for (int q = 0; q < 4; q++) {
         uint32_t r1[2], r3[2];
 #pragma unroll
-        for (int u = 0; u < 2; u++) {
-            float h1 = u ? bf16_hi(a1[q]) : bf16_lo(a1[q]);
-            float h3 = u ? bf16_hi(a3[q]) : bf16_lo(a3[q]);
-            float s = 1.0f / (1.0f + expf(-h1));
-            float g = d[2 * q + u];
-            r1[u] = f32_to_bf16_bits(g * h3 * (s * (1.0f + h1 * (1.0f - s))));
-            r3[u] = f32_to_bf16_bits(g * h1 * s);
-        }
+        for (int u = 0; u < 2; u++)
+            swiglu_bwd_elem(d[2 * q + u], u ? bf16_hi(a1[q]) : bf16_lo(a1[q]), u ? bf16_hi(a3[q]) : bf16_lo(a3[q]),
+                            r1[u], r3[u]);
         o1[q] = r1[0] | (r1[1] << 16);
         o3[q] = r3[0] | (r3[1] << 16);
     }

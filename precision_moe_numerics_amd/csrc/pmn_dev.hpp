@@ -286,6 +286,15 @@ PMN_DEV int mxfp8_block(const uint32_t (&w)[16], int64_t r, int64_t kb, int64_t 
     return e;
 }
 
+// SwiGLU backward of one element, as bf16 bits: dh1 = g h3 silu'(h1), dh3 = g silu(h1), with
+// silu'(h) = s (1 + h (1 - s)) and s = sigmoid(h)
+PMN_DEV void swiglu_bwd_elem(float g, float h1, float h3, uint32_t& d1, uint32_t& d3)
+{
+    const float s = 1.0f / (1.0f + expf(-h1));
+    d1 = f32_to_bf16_bits(g * h3 * (s * (1.0f + h1 * (1.0f - s))));
+    d3 = f32_to_bf16_bits(g * h1 * s);
+}
+
 // ---- XCD-aware tile order for the GEMMs ----------------------------------------------------
 //
 // MI355X has 8 XCDs, each with its own L2; workgroup L of a 1-D grid runs on XCD L % 8, and the

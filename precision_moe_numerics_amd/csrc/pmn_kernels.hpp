@@ -66,6 +66,11 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets, int G,
                                   int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce,
                                   hipStream_t stream);
+// The same for dY = the SwiGLU backward's dh13 [M x 2F], formed from da [M x F] (fp32) and h13
+// [M x 2F] (bf16) as launch_swiglu_bwd forms it, without writing it.
+hipError_t launch_swiglu_bwd_mxfp8_rows_cols(const float* da, const uint16_t* h13, int64_t M, int64_t F,
+                                             const int64_t* offsets, int G, int64_t Pb, uint8_t* rq, uint8_t* re,
+                                             uint8_t* cq, uint8_t* ce, hipStream_t stream);
 
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,
@@ -110,13 +115,16 @@ hipError_t launch_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t
 
 // The whole moe_grouped_gemm_bwd call (argument checks, workspace layout, launches) on a given
 // workspace. With workspace_needed non-null it only checks the arguments and stores the workspace
-// bytes the sizes need (nothing is launched).
+// bytes the sizes need (nothing is launched). With swiglu, dy is instead the SwiGLU backward of
+// (swi_da [M x N/2] fp32, swi_h13 [M x N] bf16), formed inside the dY quantization (both
+// gradients, E4M3, RNE only).
 int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* a_scales, const float* a_outer,
                          int64_t a_rows, int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
                          const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
                          const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags, int dy_rounding,
                          uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, uint32_t rng_stream_dy,
                          float* da, float* db, void* workspace, size_t workspace_bytes, pmn_stream_t stream,
-                         size_t* workspace_needed);
+                         size_t* workspace_needed, bool swiglu = false, const float* swi_da = nullptr,
+                         const void* swi_h13 = nullptr);
 
 }  // namespace pmn

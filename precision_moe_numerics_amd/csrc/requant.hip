@@ -535,20 +535,27 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 // the unit lies in one group) and 256 columns: the 64 x 256 bf16 tile is read once into the LDS;
 // then each thread quantizes two row blocks (32 columns of one slot) and one column pair (two
 // columns over 32 slots). Padding slots read as zero.
+//
+// SWI: dY is the SwiGLU backward's dh13 = [dh1 | dh3] (N = 2F), formed on the fly from
+// da [M x F] (fp32) and h13 [M x 2F] (bf16) exactly as k_swiglu_bwd forms it; the workgroup's
+// 256 features give a dh1 tile and a dh3 tile, both quantized both ways.
 // ------------------------------------------------------------------------------------------
 constexpr int RC_COLS = 256;
 constexpr int RC_PITCH = RC_COLS * 2 + 16;   // bytes per tile row: 16-byte row reads of 16 rows cover all banks
 
-__global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restrict__ x, int64_t M, int64_t N,
-                                                        const int64_t* __restrict__ offsets, int G,
-                                                        int64_t Pb, uint8_t* __restrict__ rq,
+template <bool SWI>
+__global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restrict__ x, const float* __restrict__ da,
+                                                        int64_t M, int64_t N, const int64_t* __restrict__ offsets,
+                                                        int G, int64_t Pb, uint8_t* __restrict__ rq,
                                                         uint8_t* __restrict__ re, uint8_t* __restrict__ cq,
                                                         uint8_t* __restrict__ ce)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t tile[64 * RC_PITCH];
+    constexpr int NT = SWI ? 2 : 1;   // tiles per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t tile[NT][64 * RC_PITCH];
     const int t = threadIdx.x;
     const int64_t p0 = (int64_t)blockIdx.x * 64;          // first padded slot of the unit
-    const int64_t c0 = (int64_t)blockIdx.y * RC_COLS;     // first column
+    const int64_t c0 = (int64_t)blockIdx.y * RC_COLS;     // first column (SWI: first feature)
+    const int64_t W = SWI ? N / 2 : N;                    // columns the grid spans (SWI: F)
     const GroupBlock blk = find_block(p0 / 32, offsets, G, M, 64);
     if (!blk.live) return;                                // workgroup-uniform
     // slots of the unit that exist: s0 .. s0 + nv - 1
@@ -566,8 +573,37 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
         }
         nv = blk.valid == 0 ? 0 : (end - blk.s0 < 64 ? end - blk.s0 : 64);
     }
-    // ---- the tile: 8 loads of 16 bytes per thread (row t / 32 + 8 i, chunk t % 32)
-    {
+    // ---- the tile(s): 8 chunks of 8 columns per thread (row t / 32 + 8 i, chunk t % 32)
+    if (SWI) {
+        const uint16_t* h13 = x;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int row = (t >> 5) + 8 * i;
+            const int64_t f = c0 + (t & 31) * 8;
+            uint32_t o1[4] = {0u, 0u, 0u, 0u}, o3[4] = {0u, 0u, 0u, 0u};
+            if (row < nv && f < W) {
+                const int64_t s = blk.s0 + row;
+                const float4 g0 = *reinterpret_cast<const float4*>(da + s * W + f);
+                const float4 g1 = *reinterpret_cast<const float4*>(da + s * W + f + 4);
+                const uint4 w1 = *reinterpret_cast<const uint4*>(h13 + s * N + f);
+                const uint4 w3 = *reinterpret_cast<const uint4*>(h13 + s * N + W + f);
+                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w}, a3[4] = {w3.x, w3.y, w3.z, w3.w};
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    uint32_t r1[2], r3[2];
+#pragma unroll
+                    for (int u = 0; u < 2; u++)
+                        swiglu_bwd_elem(g[2 * q + u], u ? bf16_hi(a1[q]) : bf16_lo(a1[q]),
+                                        u ? bf16_hi(a3[q]) : bf16_lo(a3[q]), r1[u], r3[u]);
+                    o1[q] = r1[0] | (r1[1] << 16);
+                    o3[q] = r3[0] | (r3[1] << 16);
+                }
+            }
+            *reinterpret_cast<uint4*>(tile[0] + row * RC_PITCH + (t & 31) * 16) = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+            *reinterpret_cast<uint4*>(tile[NT - 1] + row * RC_PITCH + (t & 31) * 16) = make_uint4(o3[0], o3[1], o3[2], o3[3]);
+        }
+    } else {
         uint4 v[8];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
@@ -578,52 +614,57 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
         }
 #pragma unroll
         for (int i = 0; i < 8; i++)
-            *reinterpret_cast<uint4*>(tile + ((t >> 5) + 8 * i) * RC_PITCH + (t & 31) * 16) = v[i];
+            *reinterpret_cast<uint4*>(tile[0] + ((t >> 5) + 8 * i) * RC_PITCH + (t & 31) * 16) = v[i];
     }
     __syncthreads();
     const int64_t nb = N >> 5;
 
-    // ---- row-wise: unit u = t + 256 i is slot row u % 64, k-block u / 64 of the tile
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int u = t + 256 * i;
-        const int row = u & 63, kbl = u >> 6;
-        const int64_t kb = (c0 >> 5) + kbl;
-        if (row < nv && kb < nb) {
-            uint32_t w[16];
-            const uint4* src = reinterpret_cast<const uint4*>(tile + row * RC_PITCH + kbl * 64);
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const uint4 a4 = src[q];
-                w[4 * q] = a4.x; w[4 * q + 1] = a4.y; w[4 * q + 2] = a4.z; w[4 * q + 3] = a4.w;
-            }
-            uint32_t o[8];
-            const int e = mxfp8_block<false>(w, 0, kb, N, 0, 0, o);
-            // padded row pr: k-block kb = chunks 2 (kb % 2), 2 (kb % 2) + 1 of 64-byte column kb / 2
-            // of its 1 KB block (16 rows x 64 bytes, chunk c of row r16 at slot c ^ ((r16 / 4) % 4));
-            // with an odd k-block count the last column's second half holds zero codes
-            const int64_t pr = p0 + row;
-            const int r16 = (int)(pr & 15), xs = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
-            uint8_t* b = rq + ((pr >> 4) * ((N + 63) >> 6) + (kb >> 1)) * 1024 + r16 * 64;
-            *reinterpret_cast<uint4*>(b + ((c ^ xs) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<uint4*>(b + (((c + 1) ^ xs) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
-            if ((nb & 1) && kb == nb - 1) {
-                *reinterpret_cast<uint4*>(b + (((c + 2) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
-                *reinterpret_cast<uint4*>(b + (((c + 3) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
-            }
-            re[kb * Pb + pr] = (uint8_t)(e + 127);
-        }
-    }
+    for (int h = 0; h < NT; h++) {
+        const uint8_t* tl = tile[h];
+        const int64_t cb = c0 + h * W;   // the tile's first column of dY
 
-    // ---- column-wise: thread t takes columns 2 (t % 128) and 2 (t % 128) + 1 over slots
-    // 32 (t / 128) .. + 31 of the unit (padding slots are +0)
-    {
+        // ---- row-wise: unit u = t + 256 i is slot row u % 64, k-block u / 64 of the tile
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            const int u = t + 256 * i;
+            const int row = u & 63, kbl = u >> 6;
+            const int64_t kb = (cb >> 5) + kbl;
+            if (row < nv && c0 + 32 * kbl < W) {
+                uint32_t w[16];
+                const uint4* src = reinterpret_cast<const uint4*>(tl + row * RC_PITCH + kbl * 64);
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const uint4 a4 = src[q];
+                    w[4 * q] = a4.x; w[4 * q + 1] = a4.y; w[4 * q + 2] = a4.z; w[4 * q + 3] = a4.w;
+                }
+                uint32_t o[8];
+                const int e = mxfp8_block<false>(w, 0, kb, N, 0, 0, o);
+                // padded row pr: k-block kb = chunks 2 (kb % 2), 2 (kb % 2) + 1 of 64-byte column
+                // kb / 2 of its 1 KB block (16 rows x 64 bytes, chunk c of row r16 at slot
+                // c ^ ((r16 / 4) % 4)); with an odd k-block count the last column's second half
+                // holds zero codes
+                const int64_t pr = p0 + row;
+                const int r16 = (int)(pr & 15), xs = (r16 >> 2) & 3, c = 2 * (int)(kb & 1);
+                uint8_t* b = rq + ((pr >> 4) * ((N + 63) >> 6) + (kb >> 1)) * 1024 + r16 * 64;
+                *reinterpret_cast<uint4*>(b + ((c ^ xs) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
+                *reinterpret_cast<uint4*>(b + (((c + 1) ^ xs) << 4)) = make_uint4(o[4], o[5], o[6], o[7]);
+                if ((nb & 1) && kb == nb - 1) {
+                    *reinterpret_cast<uint4*>(b + (((c + 2) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                    *reinterpret_cast<uint4*>(b + (((c + 3) ^ xs) << 4)) = make_uint4(0u, 0u, 0u, 0u);
+                }
+                re[kb * Pb + pr] = (uint8_t)(e + 127);
+            }
+        }
+
+        // ---- column-wise: thread t takes columns 2 (t % 128) and 2 (t % 128) + 1 over slots
+        // 32 (t / 128) .. + 31 of the unit (padding slots are +0)
         const int cp = t & 127, sb = t >> 7;
-        const int64_t col = c0 + 2 * cp;
-        if (col < N) {
+        if (c0 + 2 * cp < W) {
+            const int64_t col = cb + 2 * cp;
             uint32_t pw[32];
 #pragma unroll
-            for (int j = 0; j < 32; j++) pw[j] = *reinterpret_cast<const uint32_t*>(tile + (sb * 32 + j) * RC_PITCH + cp * 4);
+            for (int j = 0; j < 32; j++) pw[j] = *reinterpret_cast<const uint32_t*>(tl + (sb * 32 + j) * RC_PITCH + cp * 4);
             float amax0 = 0.0f, amax1 = 0.0f;
 #pragma unroll
             for (int j = 0; j < 32; j++) {
@@ -641,13 +682,13 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
                 o1[q] = e4m3_rne_pair_scaled_into(0u, bf16_hi(pw[4 * q]), bf16_hi(pw[4 * q + 1]), s1, false);
                 o1[q] = e4m3_rne_pair_scaled_into(o1[q], bf16_hi(pw[4 * q + 2]), bf16_hi(pw[4 * q + 3]), s1, true);
             }
-            // output row c (one per column): 1 KB blocks of 16 rows x 64 bytes, the unit's 64 slots
-            // one block column; this 32-slot block is chunks 2 sb and 2 sb + 1 of the row
+            // output row c (one per column): 1 KB blocks of 16 rows x 64 bytes, the unit's 64
+            // slots one block column; this 32-slot block is chunks 2 sb and 2 sb + 1 of the row
             const int64_t kbo = p0 >> 6, nkb = Pb >> 6;
 #pragma unroll
-            for (int h = 0; h < 2; h++) {
-                const int64_t c = col + h;
-                const uint32_t* o = h ? o1 : o0;
+            for (int hc = 0; hc < 2; hc++) {
+                const int64_t c = col + hc;
+                const uint32_t* o = hc ? o1 : o0;
                 const int r16 = (int)(c & 15), xs = (r16 >> 2) & 3;
                 uint8_t* b = cq + ((c >> 4) * nkb + kbo) * 1024 + r16 * 64;
                 *reinterpret_cast<uint4*>(b + (((2 * sb) ^ xs) << 4)) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -667,7 +708,19 @@ hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const
 {
     if (M == 0 || N == 0 || Pb == 0) return hipSuccess;
     const dim3 grid((unsigned)(Pb / 64), (unsigned)((N + RC_COLS - 1) / RC_COLS));
-    hipLaunchKernelGGL(k_mxfp8_rows_cols, grid, dim3(256), 0, stream, x, M, N, offsets, G, Pb, rq, re, cq, ce);
+    hipLaunchKernelGGL(k_mxfp8_rows_cols<false>, grid, dim3(256), 0, stream, x, nullptr, M, N, offsets, G, Pb, rq,
+                       re, cq, ce);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd_mxfp8_rows_cols(const float* da, const uint16_t* h13, int64_t M, int64_t F,
+                                             const int64_t* offsets, int G, int64_t Pb, uint8_t* rq, uint8_t* re,
+                                             uint8_t* cq, uint8_t* ce, hipStream_t stream)
+{
+    if (M == 0 || F == 0 || Pb == 0) return hipSuccess;
+    const dim3 grid((unsigned)(Pb / 64), (unsigned)((F + RC_COLS - 1) / RC_COLS));
+    hipLaunchKernelGGL(k_mxfp8_rows_cols<true>, grid, dim3(256), 0, stream, h13, da, M, 2 * F, offsets, G, Pb, rq,
+                       re, cq, ce);
     return hipGetLastError();
 }
 

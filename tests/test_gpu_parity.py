@@ -454,6 +454,30 @@ def test_gemm_bwd_dy_both_ways_in_one_read(P, I, counts, N, K):
         assert torch.equal(views[3][name], views[flags][name]), name
 
 
+@pytest.mark.parametrize("counts,N,K,gather_rows", [([40, 0, 333, 227], 256, 128, 400), ([1, 64, 65, 0, 130], 320, 96, None)])
+def test_gemm_bwd_swiglu_equals_swiglu_then_bwd(P, I, counts, N, K, gather_rows):
+    """moe_grouped_gemm_bwd_swiglu (dh13 formed inside dY's quantization, never written) gives the
+    gradients and workspace parts of swiglu_bwd followed by moe_grouped_gemm_bwd, bit for bit; F
+    of 160 leaves the last 256-feature tile partial."""
+    d = _moe_small(P, I, counts, N, K, gather_rows=gather_rows, seed=95)
+    M, G, F = d["M"], len(counts), N // 2
+    da = I.normal((M, F), 1e-3, 96, DEV, dtype=torch.float32)
+    h13 = I.student_t((M, N), 4, 1.0, 97, DEV)
+    size = P.moe_grouped_gemm_bwd_workspace_size(M, G, N, K, 3)
+    ws1 = torch.zeros((size,), dtype=torch.uint8, device=DEV)
+    ws2 = torch.zeros((size,), dtype=torch.uint8, device=DEV)
+    dh13 = P.swiglu_bwd(da, h13)
+    dx1, dw1, _ = P.moe_grouped_gemm_bwd(dh13, d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"], seed=4,
+                                         workspace=ws1)
+    dx2, dw2, _ = P.moe_grouped_gemm_bwd_swiglu(da, h13, d["xq"], d["wq"], d["goff"], M, N, gather=d["ggather"],
+                                                seed=4, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2) and torch.equal(dw1, dw2)
+    v1, v2 = P.bwd_workspace_views(ws1, M, G, N, K), P.bwd_workspace_views(ws2, M, G, N, K)
+    for name in ("dq", "de", "dt", "dte", "wt", "wte", "xt", "xte"):
+        assert torch.equal(v1[name], v2[name]), name
+
+
 @pytest.mark.parametrize("sr", [False, True])
 def test_gemm_bwd_intermediates_and_gradients(P, I, sr):
     """Both gradients in one call: dY's row-wise and column-wise MXFP8 (RNE, or SR on streams 6
