@@ -33,7 +33,8 @@
  *     read them without synchronizing: offsets non-decreasing from offsets[0] = 0 to
  *     offsets[G] = M, and gather values in [0, rows of the gathered matrix). Other values make
  *     the kernels read outside the operands (moe_combine_s2f6, whose slot ids come from the
- *     caller, skips ids outside [0, M) instead).
+ *     caller, skips ids outside [0, M) instead). pmn_check_indices (at the end) checks these
+ *     rules on the device, for debugging a caller.
  *
  * Formats:
  *   NVFP4 matrix [R x C] (C % 16 == 0):
@@ -399,6 +400,28 @@ int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, f
 int moe_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t rht_sign_mask,
                      const int32_t* slot_of, const float* gates, int64_t T, int k, void* out,
                      pmn_stream_t stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Checking the device index contract (a debugging aid for callers; no other call runs it).   */
+/* ------------------------------------------------------------------------------------------ */
+
+#define PMN_CHECK_OFFSETS_START 1u  /* offsets[0] != 0 */
+#define PMN_CHECK_OFFSETS_END   2u  /* offsets[G] != M */
+#define PMN_CHECK_OFFSETS_ORDER 4u  /* offsets[g] > offsets[g + 1] for some g */
+#define PMN_CHECK_OFFSETS_RANGE 8u  /* offsets[g] outside [0, M] for some g */
+#define PMN_CHECK_GATHER_RANGE 16u  /* gather[i] outside [0, src_rows) for some i */
+
+/*
+ * The rules the grouped calls assume of their device index arrays (Conventions above), which they
+ * cannot check without synchronizing: offsets int64 [G+1] and gather int32 [n_gather] (either may
+ * be NULL, not both; G >= 1 and M >= 0 with offsets, n_gather >= 0 and src_rows >= 0 with gather),
+ * src_rows being the rows of the matrix gather indexes. One small launch on `stream` writes to
+ * result (device, uint32, 4-byte aligned) the OR of the PMN_CHECK_* bits of every violated rule,
+ * 0 when all hold; the caller synchronizes the stream before reading it. Only offsets[0..G] and
+ * gather[0..n_gather) are read, so the check itself is safe on any values.
+ */
+int pmn_check_indices(const int64_t* offsets, int G, int64_t M, const int32_t* gather, int64_t n_gather,
+                      int64_t src_rows, uint32_t* result, pmn_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -41,6 +41,7 @@ _SIGS = {
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
     "moe_route_topk": (I32, [P, I64, I32, I32, P, P, P, P, P, P]),
     "moe_combine_s2f6": (I32, [P, P, I64, I64, U32, P, P, I64, I32, P, P]),
+    "pmn_check_indices": (I32, [P, I32, I64, P, I64, I64, P, P]),
     "pmn_noalloc_scratch_bytes": (SZ, []),
     "moe_grouped_gemm_bwd_noalloc": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32,
                                            U64, U32, U32, U32, P, P, P]),
@@ -75,6 +76,16 @@ RNE, SR = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 EPI_F32, EPI_BF16, EPI_SWIGLU, EPI_RHT32_S2F6 = 0, 1, 2, 3
 BWD_DGRAD, BWD_WGRAD, BWD_FP4 = 1, 2, 4
+
+
+CHECK_OFFSETS_START, CHECK_OFFSETS_END, CHECK_OFFSETS_ORDER, CHECK_OFFSETS_RANGE, CHECK_GATHER_RANGE = 1, 2, 4, 8, 16
+_CHECK_RULES = ((CHECK_OFFSETS_START, "offsets[0] != 0"), (CHECK_OFFSETS_END, "offsets[G] != M"),
+                (CHECK_OFFSETS_ORDER, "offsets decrease"), (CHECK_OFFSETS_RANGE, "an offset outside [0, M]"),
+                (CHECK_GATHER_RANGE, "a gather index outside the gathered matrix"))
+
+# PMN_CHECK_INDICES=1 in the environment: every grouped call first checks its device index arrays
+# with pmn_check_indices (one small launch and a synchronization) and refuses bad ones
+CHECK_INDICES = os.environ.get("PMN_CHECK_INDICES", "") not in ("", "0")
 
 
 class PmnError(RuntimeError):
@@ -124,6 +135,31 @@ def _nvfp4(q: "NVFP4", name: str):
     _tensor(q.scales, (R, C // 16), torch.uint8, f"{name}.scales")
     _need(q.rows_per_outer >= 1 and q.outer.dtype == torch.float32 and q.outer.numel() * q.rows_per_outer >= R,
           f"{name}.outer must be fp32 with one value per {q.rows_per_outer} rows")
+
+
+def check_indices(offsets: Optional[torch.Tensor] = None, M: int = 0, gather: Optional[torch.Tensor] = None,
+                  src_rows: int = 0) -> int:
+    """pmn_check_indices: the mask of CHECK_* rules that the device arrays offsets [G+1] (int64)
+    and gather (int32, indexing a matrix of src_rows rows) break, 0 if none. Synchronizes."""
+    _need(offsets is not None or gather is not None, "check_indices needs offsets or gather")
+    _need(offsets is None or (offsets.dtype == torch.int64 and offsets.numel() >= 2), "offsets must be int64 [G+1]")
+    _need(gather is None or gather.dtype == torch.int32, "gather must be int32")
+    dev = (offsets if offsets is not None else gather).device
+    res = torch.empty(1, dtype=torch.int32, device=dev)
+    G = offsets.numel() - 1 if offsets is not None else 0
+    n = gather.numel() if gather is not None else 0
+    _check(_lib.pmn_check_indices(_ptr(offsets), G, M, _ptr(gather), n, src_rows, _ptr(res), _stream()),
+           "pmn_check_indices")
+    return int(res.item()) & 0xFFFFFFFF
+
+
+def _debug_indices(what: str, offsets, M: int, gather=None, src_rows: int = 0):
+    if not CHECK_INDICES or (offsets is None and gather is None):
+        return
+    bad = check_indices(offsets, M, gather, src_rows)
+    if bad:
+        raise PmnError(f"{what}: the device index arrays break the contract: "
+                       + ", ".join(t for b, t in _CHECK_RULES if bad & b))
 
 
 def version() -> int:
@@ -202,6 +238,7 @@ def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
     _nvfp4(q, "q")
     _index(gather, M, torch.int32, "gather")
     _index(offsets, G + 1, torch.int64, "offsets")
+    _debug_indices("requant_transpose_sr_mxfp8", offsets, M, gather, q.rows)
     out = torch.empty((q.cols, ld), dtype=torch.uint8, device=dev) if out is None else out
     oe = torch.empty((q.cols, ld // 32), dtype=torch.uint8, device=dev) if out_e8m0 is None else out_e8m0
     _tensor(out, (q.cols, ld), torch.uint8, "out")
@@ -222,6 +259,7 @@ def mxfp8_quantize(x: torch.Tensor, layout: int = ROWWISE, offsets: Optional[tor
     dev = x.device
     G = 0 if offsets is None else offsets.numel() - 1
     _index(offsets, G + 1, torch.int64, "offsets")
+    _debug_indices("mxfp8_quantize", offsets, M)
     po = None
     if layout == ROWWISE:
         out = torch.empty((M, N), dtype=torch.uint8, device=dev)
@@ -261,6 +299,7 @@ def moe_grouped_gemm_fwd(xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N:
     _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
+    _debug_indices("moe_grouped_gemm_fwd", offsets, M, gather, xq.rows)
     if out is None:
         if epilogue == EPI_F32:
             out = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -314,6 +353,7 @@ def moe_grouped_gemm_fwd_mxfp8(x: torch.Tensor, w: torch.Tensor, offsets: torch.
     _tensor(w, (G * N, K), torch.bfloat16, "w")
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
+    _debug_indices("moe_grouped_gemm_fwd_mxfp8", offsets, M, gather, x.shape[0])
     if workspace is None:
         workspace = torch.empty((_lib.moe_grouped_gemm_fwd_mxfp8_workspace_size(M, G, N, K),), dtype=torch.uint8,
                                 device=dev)
@@ -357,6 +397,7 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
     _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
+    _debug_indices("moe_grouped_gemm_bwd", offsets, M, gather, xq.rows)
     ws_bytes = moe_grouped_gemm_bwd_workspace_size(M, G, N, K, flags)
     if workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
@@ -394,6 +435,7 @@ def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVF
     _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
+    _debug_indices("moe_grouped_gemm_bwd_swiglu", offsets, M, gather, xq.rows)
     ws_bytes = moe_grouped_gemm_bwd_workspace_size(M, G, N, K, BWD_DGRAD | BWD_WGRAD)
     if workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
@@ -426,6 +468,7 @@ def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", off
     _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
+    _debug_indices("moe_grouped_gemm_bwd_noalloc", offsets, M, gather, xq.rows)
     if da is None and flags & BWD_DGRAD:
         da = torch.empty((M, K), dtype=torch.float32, device=dev)
     if db is None and flags & BWD_WGRAD:

@@ -416,6 +416,16 @@ int moe_route_topk(const float* logits, int64_t T, int E, int k, int32_t* ids, f
     return status(pmn::launch_route(logits, T, E, k, ids, gates, offsets, gather_token, slot_of, hs(stream)));
 }
 
+int pmn_check_indices(const int64_t* offsets, int G, int64_t M, const int32_t* gather, int64_t n_gather,
+                      int64_t src_rows, uint32_t* result, pmn_stream_t stream)
+{
+    if (!result || (!offsets && !gather)) return PMN_EINVAL;
+    if ((offsets && (G < 1 || M < 0)) || (gather && (n_gather < 0 || src_rows < 0))) return PMN_ESHAPE;
+    if (!aligned(result, 4)) return PMN_EALIGN;
+    return status(pmn::launch_check_indices(offsets, offsets ? G : 0, M, gather, gather ? n_gather : 0, src_rows,
+                                            result, hs(stream)));
+}
+
 int moe_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t rht_sign_mask,
                      const int32_t* slot_of, const float* gates, int64_t T, int k, void* out,
                      pmn_stream_t stream)

@@ -109,6 +109,10 @@ hipError_t launch_swiglu_bwd(const float* da, const uint16_t* h13, int64_t M, in
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
                         int64_t* offsets, int32_t* gather_token, int32_t* slot_of, hipStream_t stream);
 
+// Violations of the device index contract as a PMN_CHECK_* mask written to result[0].
+hipError_t launch_check_indices(const int64_t* offsets, int G, int64_t M, const int32_t* gather, int64_t n,
+                                int64_t src_rows, uint32_t* result, hipStream_t stream);
+
 hipError_t launch_combine_s2f6(const int8_t* codes, const uint8_t* e8m0, int64_t M, int64_t H, uint32_t mask,
                                const int32_t* slot_of, const float* gates, int64_t T, int k, uint16_t* out,
                                hipStream_t stream);

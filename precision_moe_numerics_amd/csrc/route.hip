@@ -99,6 +99,44 @@ __global__ __launch_bounds__(256) void k_route_scatter(const int32_t* __restrict
     }
 }
 
+// The device index contract of the grouped calls, checked by one workgroup (for debugging a
+// caller; nothing on the hot path runs it): each violated rule sets its PMN_CHECK_* bit, and the
+// mask is written to *result, 0 when every rule holds. Reads offsets[0..G] and gather[0..n) only.
+__global__ __launch_bounds__(1024) void k_check_indices(const int64_t* __restrict__ offsets, int G, int64_t M,
+                                                        const int32_t* __restrict__ gather, int64_t n,
+                                                        int64_t src_rows, uint32_t* __restrict__ result)
+{
+    __shared__ uint32_t bad;
+    if (threadIdx.x == 0) bad = 0u;
+    __syncthreads();
+    uint32_t b = 0u;
+    if (offsets) {
+        for (int64_t g = threadIdx.x; g <= G; g += blockDim.x) {
+            const int64_t o = offsets[g];
+            if (g == 0 && o != 0) b |= PMN_CHECK_OFFSETS_START;
+            if (g == G && o != M) b |= PMN_CHECK_OFFSETS_END;
+            if (o < 0 || o > M) b |= PMN_CHECK_OFFSETS_RANGE;
+            if (g > 0 && offsets[g - 1] > o) b |= PMN_CHECK_OFFSETS_ORDER;
+        }
+    }
+    if (gather) {
+        for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+            const int64_t r = gather[i];
+            if (r < 0 || r >= src_rows) b |= PMN_CHECK_GATHER_RANGE;
+        }
+    }
+    if (b) atomicOr(&bad, b);
+    __syncthreads();
+    if (threadIdx.x == 0) result[0] = bad;
+}
+
+hipError_t launch_check_indices(const int64_t* offsets, int G, int64_t M, const int32_t* gather, int64_t n,
+                                int64_t src_rows, uint32_t* result, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_check_indices, dim3(1), dim3(1024), 0, stream, offsets, G, M, gather, n, src_rows, result);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids, float* gates,
                         int64_t* offsets, int32_t* gather_token, int32_t* slot_of, hipStream_t stream)
 {

@@ -102,6 +102,20 @@ def test_quantize_with_workspace_argument_errors(lib):
     assert lib.nvfp4_quantize_ws(None, 0, 32, 0, 1, None, None, None, None, None, 0, None) == 0
 
 
+def test_check_indices_argument_errors(lib):
+    """pmn_check_indices refuses, before any launch: no result or neither array (PMN_EINVAL), no
+    groups or a negative M with offsets, a negative count or row bound with gather (PMN_ESHAPE),
+    and a result not 4-byte aligned (PMN_EALIGN)."""
+    fake = C.c_void_p(0x1000)     # never dereferenced
+    assert lib.pmn_check_indices(None, 0, 0, None, 0, 0, fake, None) == -1
+    assert lib.pmn_check_indices(fake, 1, 4, None, 0, 0, None, None) == -1
+    assert lib.pmn_check_indices(fake, 0, 4, None, 0, 0, fake, None) == -2
+    assert lib.pmn_check_indices(fake, 2, -1, None, 0, 0, fake, None) == -2
+    assert lib.pmn_check_indices(None, 0, 0, fake, -1, 8, fake, None) == -2
+    assert lib.pmn_check_indices(None, 0, 0, fake, 4, -8, fake, None) == -2
+    assert lib.pmn_check_indices(fake, 1, 4, fake, 4, 8, C.c_void_p(0x1002), None) == -3
+
+
 def test_zero_size_calls_are_no_ops(lib):
     assert lib.nvfp4_quantize(None, 0, 32, 1, 1, None, None, None, None, None) == 0
     assert lib.rht32_s2f6_quantize(None, 0, 0, 64, 0, None, None, None) == 0
