@@ -131,6 +131,32 @@ int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64
                       const float* outer_in, uint8_t* codes, uint8_t* scales, float* outer_out, void* ws,
                       size_t ws_bytes, pmn_stream_t stream);
 
+/*
+ * Weights for both passes ([AREX] "转置打散分组,随机舍入保住期望值": the backward multiplies by the
+ * transposed weights, re-quantized from the NVFP4 ones by SR; the weights do not change between
+ * a step's forward and backward): nvfp4_quantize_ws(x, rows, cols, PMN_NVFP4_WEIGHT,
+ * rows_per_outer, NULL, codes, scales, outer_out) and, from the same codes, the W^T operand that
+ * moe_grouped_gemm_bwd's dgrad would requantize for weights of G*N = rows rows:
+ *   wt_codes  uint8 [cols x rows]   E4M3 codes of W^T, in the backward workspace's blocked layout
+ *                                   (1 KB blocks of 16 rows x 64 bytes, see moe_grouped_gemm_bwd)
+ *   wt_e8m0   uint8 [rows/32 x cols] E8M0 per 32 rows of W, k-block-major
+ * i.e. the bytes of requant_transpose_sr_mxfp8(codes, scales, outer_out, rows, cols,
+ * rows_per_outer, NULL, rows, NULL, 0, PMN_TARGET_E4M3, seed, rng_stream, ...) with ld = rows,
+ * blocked. Pass them to moe_grouped_gemm_bwd with PMN_BWD_W_PREPARED as b_codes / b_scales; the
+ * gradients then equal those of a call with the NVFP4 weights and rng_stream_b = rng_stream.
+ * rows % 64 == 0, cols % 16 == 0, rows % rows_per_outer == 0 (PMN_ESHAPE); x, codes, wt_codes,
+ * wt_e8m0 and the workspace 16-byte aligned (PMN_EALIGN). Workspace as nvfp4_quantize_ws.
+ * When every matrix of rows_per_outer rows (a multiple of 64) splits into at most one tile per
+ * compute unit (tiles of TH <= 512 rows, a multiple of 64, by TW columns, a multiple of 16, with
+ * TH * TW <= 57344), x is read once and the codes are re-quantized while the matrix is on chip;
+ * otherwise (and on a capturing stream, or when the cooperative launch is refused) the call runs
+ * the two steps. The results are the same.
+ */
+int nvfp4_quantize_weights_bwd(const void* x, int64_t rows, int64_t cols, int64_t rows_per_outer,
+                               uint8_t* codes, uint8_t* scales, float* outer_out, uint8_t* wt_codes,
+                               uint8_t* wt_e8m0, uint64_t seed, uint32_t rng_stream, void* ws,
+                               size_t ws_bytes, pmn_stream_t stream);
+
 /* ------------------------------------------------------------------------------------------ */
 /* Backward operand preparation   [AREX] "转置打散分组,随机舍入保住期望值"; [LHC] (dequantize,   */
 /* transpose in higher precision, re-quantize to MXFP8 with stochastic rounding; the           */
@@ -268,6 +294,7 @@ int moe_grouped_gemm_fwd_mxfp8(const void* x, int64_t x_rows, const int32_t* gat
 #define PMN_BWD_DGRAD 1
 #define PMN_BWD_WGRAD 2
 #define PMN_BWD_FP4   4  /* with DGRAD and/or WGRAD: the FP4 backward variant (see below) */
+#define PMN_BWD_W_PREPARED 8 /* b_codes / b_scales are nvfp4_quantize_weights_bwd's W^T operand */
 
 /*
  * Workspace bytes moe_grouped_gemm_bwd needs for these sizes and flags (host call).
@@ -303,6 +330,10 @@ size_t moe_grouped_gemm_bwd_workspace_size(int64_t M, int G, int64_t N, int64_t 
  * 16 c .. 16 c + 15 of those 64) at position c ^ ((r / 4) % 4). Rows of padding slots in the
  * dY row-wise codes are left unwritten. The parts of a gradient not requested are still
  * reserved.
+ * PMN_BWD_W_PREPARED (not with PMN_BWD_FP4; N % 64 == 0): b_codes and b_scales are the W^T codes
+ * and E8M0 scales nvfp4_quantize_weights_bwd wrote for the G*N x K weights; b_outer and
+ * b_rows_per_outer are not used, rng_stream_b neither, and the workspace's W^T parts are reserved
+ * but not written.
  * PMN_BWD_FP4 ([AREX], closing section: FP4 in the backward pass is the next step; the transpose
  * section's worked example rounds onto the E2M1 grid by SR): every operand goes to MXFP4 instead
  * of MXFP8 -- E2M1 codes (W^T, A^T by SR; dY by dy_rounding) with one E8M0 per 32 values chosen
@@ -326,15 +357,16 @@ int moe_grouped_gemm_bwd(const void* dy, const uint8_t* a_codes, const uint8_t* 
  * SwiGLU output da_act (fp32 [M x F], F = N / 2) and the saved pre-activations h13 (bf16
  * [M x N], h1 in columns 0 .. F-1, h3 in F .. N-1) exactly as swiglu_bwd forms it, and never
  * written out. N % 64 == 0. The results and the workspace contents equal those of swiglu_bwd
- * followed by moe_grouped_gemm_bwd(PMN_BWD_DGRAD | PMN_BWD_WGRAD, PMN_RNE). The rounding of dY
- * is fixed to RNE and there is no FP4 variant; other configurations call the two separately.
+ * followed by moe_grouped_gemm_bwd(PMN_BWD_DGRAD | PMN_BWD_WGRAD | flags, PMN_RNE), flags being 0
+ * or PMN_BWD_W_PREPARED (PMN_EINVAL otherwise). The rounding of dY is fixed to RNE and there is no
+ * FP4 variant; other configurations call the two separately.
  */
 int moe_grouped_gemm_bwd_swiglu(const float* da_act, const void* h13, const uint8_t* a_codes,
                                 const uint8_t* a_scales, const float* a_outer, int64_t a_rows,
                                 int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
                                 const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
-                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, uint64_t seed,
-                                uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
+                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags,
+                                uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
                                 void* workspace, size_t workspace_bytes, pmn_stream_t stream);
 
 /*

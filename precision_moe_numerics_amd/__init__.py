@@ -27,6 +27,7 @@ _SIGS = {
     "nvfp4_quantize": (I32, [P, I64, I64, I32, I64, P, P, P, P, P]),
     "nvfp4_quantize_ws_size": (SZ, []),
     "nvfp4_quantize_ws": (I32, [P, I64, I64, I32, I64, P, P, P, P, P, SZ, P]),
+    "nvfp4_quantize_weights_bwd": (I32, [P, I64, I64, I64, P, P, P, P, P, U64, U32, P, SZ, P]),
     "requant_transpose_sr_mxfp8": (I32, [P, P, P, I64, I64, I64, P, I64, P, I32, I32, U64, U32, P, P, I64, P, P]),
     "mxfp8_quantize": (I32, [P, I64, I64, I32, P, I32, I32, U64, U32, P, P, I64, P, P]),
     "rht32_s2f6_quantize": (I32, [P, I32, I64, I64, U32, P, P, P]),
@@ -34,8 +35,8 @@ _SIGS = {
     "moe_grouped_gemm_bwd_workspace_size": (SZ, [I64, I32, I64, I64, I32]),
     "moe_grouped_gemm_bwd": (I32, [P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, I32, U64,
                                    U32, U32, U32, P, P, P, SZ, P]),
-    "moe_grouped_gemm_bwd_swiglu": (I32, [P, P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, U64, U32,
-                                          U32, P, P, P, SZ, P]),
+    "moe_grouped_gemm_bwd_swiglu": (I32, [P, P, P, P, P, I64, I64, P, P, P, P, I64, P, I32, I64, I64, I64, I32, U64,
+                                          U32, U32, P, P, P, SZ, P]),
     "moe_grouped_gemm_fwd_mxfp8_workspace_size": (SZ, [I64, I32, I64, I64]),
     "moe_grouped_gemm_fwd_mxfp8": (I32, [P, I64, P, P, P, I32, I64, I64, I64, I32, U32, P, P, P, P, SZ, P]),
     "swiglu_bwd": (I32, [P, P, I64, I64, P, P]),
@@ -75,7 +76,7 @@ ROWWISE, COLWISE = 0, 1
 RNE, SR = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 EPI_F32, EPI_BF16, EPI_SWIGLU, EPI_RHT32_S2F6 = 0, 1, 2, 3
-BWD_DGRAD, BWD_WGRAD, BWD_FP4 = 1, 2, 4
+BWD_DGRAD, BWD_WGRAD, BWD_FP4, BWD_W_PREPARED = 1, 2, 4, 8
 
 
 CHECK_OFFSETS_START, CHECK_OFFSETS_END, CHECK_OFFSETS_ORDER, CHECK_OFFSETS_RANGE, CHECK_GATHER_RANGE = 1, 2, 4, 8, 16
@@ -220,6 +221,53 @@ def nvfp4_quantize(x: torch.Tensor, mode: int = NVFP4_ACT, rows_per_outer: int =
                                       _ptr(scales), _ptr(outer), _ptr(workspace), workspace.numel(), _stream()),
                "nvfp4_quantize_ws")
     return NVFP4(codes, scales, outer, rows_per_outer)
+
+
+@dataclass
+class WeightsBwd:
+    """Weights quantized for both passes (nvfp4_quantize_weights_bwd): q, the NVFP4 matrix for
+    the forward, and the backward's W^T operand, wt u8 [cols, rows] (E4M3 codes, blocked layout)
+    with wte u8 [rows/32, cols] (E8M0), drawn with (seed, rng_stream). The backward calls take it
+    in place of the NVFP4 weights."""
+    q: NVFP4
+    wt: torch.Tensor
+    wte: torch.Tensor
+    seed: int
+    rng_stream: int
+
+
+def nvfp4_quantize_weights_bwd(w: torch.Tensor, rows_per_outer: int, seed: int = 0, rng_stream: int = 2,
+                               workspace: Optional[torch.Tensor] = None) -> WeightsBwd:
+    """nvfp4_quantize_weights_bwd: w bf16 [rows, cols] (rows % 64 == 0) in weight mode with one
+    outer scale per rows_per_outer rows, and its W^T operand for the backward's dgrad."""
+    _need(w.dtype == torch.bfloat16 and w.dim() == 2, "w must be bf16 [rows, cols]")
+    R, Cc = w.shape
+    dev = w.device
+    if workspace is None:
+        workspace = torch.empty((nvfp4_quantize_ws_size(),), dtype=torch.uint8, device=dev)
+    _need(workspace.dtype == torch.uint8, "workspace must be uint8")
+    codes = torch.empty((R, Cc // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((R, Cc // 16), dtype=torch.uint8, device=dev)
+    outer = torch.empty((R // max(rows_per_outer, 1),), dtype=torch.float32, device=dev)
+    wt = torch.empty((Cc, R), dtype=torch.uint8, device=dev)
+    wte = torch.empty((R // 32, Cc), dtype=torch.uint8, device=dev)
+    _check(_lib.nvfp4_quantize_weights_bwd(_ptr(w), R, Cc, rows_per_outer, _ptr(codes), _ptr(scales), _ptr(outer),
+                                           _ptr(wt), _ptr(wte), seed, rng_stream, _ptr(workspace),
+                                           workspace.numel(), _stream()), "nvfp4_quantize_weights_bwd")
+    return WeightsBwd(NVFP4(codes, scales, outer, rows_per_outer), wt, wte, seed, rng_stream)
+
+
+def _bwd_weights(wq, G: int, N: int, K: int):
+    """(codes, scales, outer, rows_per_outer, extra flags) of the backward's weight operand: the
+    NVFP4 weights, or a WeightsBwd's prepared W^T (PMN_BWD_W_PREPARED)."""
+    if isinstance(wq, WeightsBwd):
+        _need(wq.q.cols == K and wq.q.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}]")
+        _tensor(wq.wt, (K, G * N), torch.uint8, "wq.wt")
+        _tensor(wq.wte, (G * N // 32, K), torch.uint8, "wq.wte")
+        return _ptr(wq.wt), _ptr(wq.wte), None, 1, BWD_W_PREPARED
+    _nvfp4(wq, "wq")
+    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    return _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer), wq.rows_per_outer, 0
 
 
 def requant_transpose_sr_mxfp8(q: NVFP4, gather: Optional[torch.Tensor] = None,
@@ -383,18 +431,19 @@ def moe_grouped_gemm_fwd_mxfp8(x: torch.Tensor, w: torch.Tensor, offsets: torch.
     return out
 
 
-def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.Tensor, M: int, N: int,
+def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq, offsets: torch.Tensor, M: int, N: int,
                          flags: int = BWD_DGRAD | BWD_WGRAD, gather: Optional[torch.Tensor] = None,
                          dy_rounding: int = RNE, seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
                          rng_stream_dy: int = 3, workspace: Optional[torch.Tensor] = None, da=None, db=None):
-    """Returns (da [M, K] fp32 or None, db [G*N, K] fp32 or None, workspace)."""
+    """wq: the NVFP4 weights [G*N, K], or a WeightsBwd (its prepared W^T, PMN_BWD_W_PREPARED).
+    Returns (da [M, K] fp32 or None, db [G*N, K] fp32 or None, workspace)."""
     K = xq.cols
     G = offsets.numel() - 1
     dev = dy.device
     _tensor(dy, (M, N), torch.bfloat16, "dy")
     _nvfp4(xq, "xq")
-    _nvfp4(wq, "wq")
-    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    bc, bs, bo, brpo, wflag = _bwd_weights(wq, G, N, K)
+    flags |= wflag
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
     _debug_indices("moe_grouped_gemm_bwd", offsets, M, gather, xq.rows)
@@ -411,14 +460,14 @@ def moe_grouped_gemm_bwd(dy: torch.Tensor, xq: NVFP4, wq: NVFP4, offsets: torch.
         _tensor(db, (G * N, K), torch.float32, "db")
     _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
     _check(_lib.moe_grouped_gemm_bwd(_ptr(dy), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows,
-                                     xq.rows_per_outer, _ptr(gather), _ptr(wq.codes), _ptr(wq.scales), _ptr(wq.outer),
-                                     wq.rows_per_outer, _ptr(offsets), G, M, N, K, flags, dy_rounding, seed,
+                                     xq.rows_per_outer, _ptr(gather), bc, bs, bo, brpo, _ptr(offsets), G, M, N, K,
+                                     flags, dy_rounding, seed,
                                      rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da), _ptr(db),
                                      _ptr(workspace), workspace.numel(), _stream()), "moe_grouped_gemm_bwd")
     return da, db, workspace
 
 
-def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVFP4, wq: NVFP4,
+def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVFP4, wq,
                                 offsets: torch.Tensor, M: int, N: int, gather: Optional[torch.Tensor] = None,
                                 seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
                                 workspace: Optional[torch.Tensor] = None, dx=None, dw=None):
@@ -431,8 +480,7 @@ def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVF
     _tensor(da_act, (M, N // 2), torch.float32, "da_act")
     _tensor(h13, (M, N), torch.bfloat16, "h13")
     _nvfp4(xq, "xq")
-    _nvfp4(wq, "wq")
-    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    bc, bs, bo, brpo, wflag = _bwd_weights(wq, G, N, K)
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
     _debug_indices("moe_grouped_gemm_bwd_swiglu", offsets, M, gather, xq.rows)
@@ -445,15 +493,15 @@ def moe_grouped_gemm_bwd_swiglu(da_act: torch.Tensor, h13: torch.Tensor, xq: NVF
     _tensor(dw, (G * N, K), torch.float32, "dw")
     _need(workspace.dtype == torch.uint8 and workspace.dim() == 1, "workspace must be a 1-D uint8 tensor")
     _check(_lib.moe_grouped_gemm_bwd_swiglu(_ptr(da_act), _ptr(h13), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer),
-                                            xq.rows, xq.rows_per_outer, _ptr(gather), _ptr(wq.codes),
-                                            _ptr(wq.scales), _ptr(wq.outer), wq.rows_per_outer, _ptr(offsets), G, M,
-                                            N, K, seed, rng_stream_a, rng_stream_b, _ptr(dx), _ptr(dw),
+                                            xq.rows, xq.rows_per_outer, _ptr(gather), bc, bs, bo, brpo,
+                                            _ptr(offsets), G, M, N, K, wflag, seed, rng_stream_a, rng_stream_b,
+                                            _ptr(dx), _ptr(dw),
                                             _ptr(workspace), workspace.numel(), _stream()),
            "moe_grouped_gemm_bwd_swiglu")
     return dx, dw, workspace
 
 
-def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", offsets: torch.Tensor, M: int, N: int,
+def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq, offsets: torch.Tensor, M: int, N: int,
                                  flags: int = BWD_DGRAD | BWD_WGRAD, gather: Optional[torch.Tensor] = None,
                                  dy_rounding: int = RNE, seed: int = 0, rng_stream_a: int = 1, rng_stream_b: int = 2,
                                  rng_stream_dy: int = 3, da=None, db=None):
@@ -464,8 +512,8 @@ def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", off
     dev = dy.device
     _tensor(dy, (M, N), torch.bfloat16, "dy")
     _nvfp4(xq, "xq")
-    _nvfp4(wq, "wq")
-    _need(wq.cols == K and wq.rows == G * N, f"wq must be [G*N, K] = [{G * N}, {K}], got [{wq.rows}, {wq.cols}]")
+    bc, bs, bo, brpo, wflag = _bwd_weights(wq, G, N, K)
+    flags |= wflag
     _index(offsets, G + 1, torch.int64, "offsets")
     _index(gather, M, torch.int32, "gather")
     _debug_indices("moe_grouped_gemm_bwd_noalloc", offsets, M, gather, xq.rows)
@@ -478,8 +526,8 @@ def moe_grouped_gemm_bwd_noalloc(dy: torch.Tensor, xq: "NVFP4", wq: "NVFP4", off
     if flags & BWD_WGRAD:
         _tensor(db, (G * N, K), torch.float32, "db")
     _check(_lib.moe_grouped_gemm_bwd_noalloc(_ptr(dy), _ptr(xq.codes), _ptr(xq.scales), _ptr(xq.outer), xq.rows,
-                                             xq.rows_per_outer, _ptr(gather), _ptr(wq.codes), _ptr(wq.scales),
-                                             _ptr(wq.outer), wq.rows_per_outer, _ptr(offsets), G, M, N, K, flags,
+                                             xq.rows_per_outer, _ptr(gather), bc, bs, bo, brpo, _ptr(offsets), G, M,
+                                             N, K, flags,
                                              dy_rounding, seed, rng_stream_a, rng_stream_b, rng_stream_dy, _ptr(da),
                                              _ptr(db), _stream()), "moe_grouped_gemm_bwd_noalloc")
     return da, db

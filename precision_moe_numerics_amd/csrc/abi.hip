@@ -85,25 +85,32 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
                          size_t* workspace_needed, bool swiglu, const float* swi_da, const void* swi_h13)
 {
     const bool swi = swiglu;
+    // W^T operand prepared by nvfp4_quantize_weights_bwd: b_codes / b_scales are its E4M3 codes
+    // and E8M0 scales, and no requant of the weights runs here
+    const bool prepared = flags & PMN_BWD_W_PREPARED;
     if (swi) {
         // dY formed from the SwiGLU backward inside the fused dY quantization only
-        if (flags != (PMN_BWD_DGRAD | PMN_BWD_WGRAD) || dy_rounding != PMN_RNE) return PMN_EINVAL;
+        if ((flags & ~PMN_BWD_W_PREPARED) != (PMN_BWD_DGRAD | PMN_BWD_WGRAD) || dy_rounding != PMN_RNE)
+            return PMN_EINVAL;
         if (N % 64 != 0) return PMN_ESHAPE;
         if (M > 0 && (!swi_da || !swi_h13)) return PMN_EINVAL;
         if (M > 0 && (!aligned(swi_da, 16) || !aligned(swi_h13, 16))) return PMN_EALIGN;
         dy = swi_h13;   // stands in for dY in the checks below (not read as dY)
     }
-    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4)) != 0 || (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
+    if ((flags & ~(PMN_BWD_DGRAD | PMN_BWD_WGRAD | PMN_BWD_FP4 | PMN_BWD_W_PREPARED)) != 0 ||
+        (flags & (PMN_BWD_DGRAD | PMN_BWD_WGRAD)) == 0)
         return PMN_EINVAL;
+    if (prepared && (flags & PMN_BWD_FP4)) return PMN_EINVAL;
+    if (prepared && N % 64 != 0) return PMN_ESHAPE;
     if (dy_rounding != PMN_RNE && dy_rounding != PMN_SR) return PMN_EINVAL;
     if (G < 1 || M < 0 || a_rows < 0 || N <= 0 || K <= 0 || N % 32 != 0 || K % 32 != 0) return PMN_ESHAPE;
-    if (a_rows_per_outer < 1 || b_rows_per_outer < 1) return PMN_ESHAPE;
+    if (a_rows_per_outer < 1 || (!prepared && b_rows_per_outer < 1)) return PMN_ESHAPE;
     if (!gather && M > a_rows) return PMN_ESHAPE;
     // with no slots (M == 0) dy, da and the activations may be null: dgrad has no rows and
     // wgrad writes zero gradients
     if (!offsets || (M > 0 && !dy)) return PMN_EINVAL;
     const bool dgrad = flags & PMN_BWD_DGRAD, wgrad = flags & PMN_BWD_WGRAD;
-    if (dgrad && (!b_codes || !b_scales || !b_outer || (M > 0 && !da))) return PMN_EINVAL;
+    if (dgrad && (!b_codes || !b_scales || (!prepared && !b_outer) || (M > 0 && !da))) return PMN_EINVAL;
     if (wgrad && (!db || (M > 0 && (!a_codes || !a_scales || !a_outer)))) return PMN_EINVAL;
     const bool fp4 = flags & PMN_BWD_FP4;
     const BwdLayout L = bwd_layout(M, G, N, K, fp4);
@@ -141,7 +148,12 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
                                        ws + L.de, offsets, G, po, L.Pb, s, nullptr, fp4, blocked);
             if (e != hipSuccess) return PMN_ELAUNCH;
         }
-        if (L.Nk == N) {
+        const uint8_t* wt = ws + L.wt;
+        const uint8_t* wte = ws + L.wte;
+        if (prepared) {
+            wt = b_codes;
+            wte = b_scales;
+        } else if (L.Nk == N) {
             e = pmn::launch_requant(b_codes, b_scales, b_outer, K, b_rows_per_outer, nullptr, (int64_t)G * N, nullptr,
                                     0, target, seed, rng_stream_b, ws + L.wt, ws + L.wte, (int64_t)G * N, true,
                                     nullptr, s, blocked);
@@ -156,8 +168,7 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
                                     nullptr, s, blocked);
         }
         if (e != hipSuccess) return PMN_ELAUNCH;
-        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, ws + L.wt, ws + L.wte, offsets, po, L.Pb, G, M, N, K, da,
-                                    s, fp4, L.Nk);
+        e = pmn::launch_mxfp8_dgrad(ws + L.dq, ws + L.de, wt, wte, offsets, po, L.Pb, G, M, N, K, da, s, fp4, L.Nk);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (wgrad) {
@@ -235,6 +246,24 @@ int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64
                                              mode == PMN_NVFP4_ACT, rows_per_outer, outer_in, codes,
                                              scales, outer_out, hs(stream), mode == PMN_NVFP4_WEIGHT_2D, ws,
                                              ws_bytes));
+}
+
+int nvfp4_quantize_weights_bwd(const void* x, int64_t rows, int64_t cols, int64_t rows_per_outer, uint8_t* codes,
+                               uint8_t* scales, float* outer_out, uint8_t* wt_codes, uint8_t* wt_e8m0, uint64_t seed,
+                               uint32_t rng_stream, void* ws, size_t ws_bytes, pmn_stream_t stream)
+{
+    if (rows < 0 || cols <= 0 || cols % 16 != 0 || rows_per_outer < 1 || rows % rows_per_outer != 0 ||
+        rows % 64 != 0)
+        return PMN_ESHAPE;
+    if (rows == 0) return PMN_OK;
+    if (!x || !codes || !scales || !outer_out || !wt_codes || !wt_e8m0) return PMN_EINVAL;
+    if (!ws || ws_bytes < nvfp4_quantize_ws_size()) return PMN_EWORKSPACE;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(outer_out, 4) || !aligned(wt_codes, 16) ||
+        !aligned(wt_e8m0, 16) || !aligned(ws, 16))
+        return PMN_EALIGN;
+    return status(pmn::launch_nvfp4_quantize_weights_bwd(static_cast<const uint16_t*>(x), rows, cols, rows_per_outer,
+                                                         codes, scales, outer_out, wt_codes, wt_e8m0, seed,
+                                                         rng_stream, ws, ws_bytes, hs(stream)));
 }
 
 static int check_groups(int64_t M, const int64_t* offsets, int G, int64_t ld)
@@ -347,14 +376,15 @@ int moe_grouped_gemm_bwd_swiglu(const float* da_act, const void* h13, const uint
                                 const uint8_t* a_scales, const float* a_outer, int64_t a_rows,
                                 int64_t a_rows_per_outer, const int32_t* gather, const uint8_t* b_codes,
                                 const uint8_t* b_scales, const float* b_outer, int64_t b_rows_per_outer,
-                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, uint64_t seed,
-                                uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
+                                const int64_t* offsets, int G, int64_t M, int64_t N, int64_t K, int flags,
+                                uint64_t seed, uint32_t rng_stream_a, uint32_t rng_stream_b, float* dx, float* dw,
                                 void* workspace, size_t workspace_bytes, pmn_stream_t stream)
 {
+    if ((flags & ~PMN_BWD_W_PREPARED) != 0) return PMN_EINVAL;
     return pmn::grouped_gemm_bwd_run(nullptr, a_codes, a_scales, a_outer, a_rows, a_rows_per_outer, gather, b_codes,
                                      b_scales, b_outer, b_rows_per_outer, offsets, G, M, N, K,
-                                     PMN_BWD_DGRAD | PMN_BWD_WGRAD, PMN_RNE, seed, rng_stream_a, rng_stream_b, 0, dx,
-                                     dw, workspace, workspace_bytes, stream, nullptr, true, da_act, h13);
+                                     PMN_BWD_DGRAD | PMN_BWD_WGRAD | flags, PMN_RNE, seed, rng_stream_a, rng_stream_b,
+                                     0, dx, dw, workspace, workspace_bytes, stream, nullptr, true, da_act, h13);
 }
 
 size_t moe_grouped_gemm_fwd_mxfp8_workspace_size(int64_t M, int G, int64_t N, int64_t K)

@@ -225,6 +225,36 @@ PMN_DEV uint32_t e4m3_sr(float y, uint32_t rng)
     return (uint32_t)__builtin_amdgcn_cvt_sr_fp8_f32(y, (int)rng, 0, 0) & 0xFFu;
 }
 
+// E4M3 code of v / scale (scale a power of two) by stochastic rounding with the given SR operand,
+// written into byte `sel` (0..3) of `word`.
+PMN_DEV uint32_t e4m3_sr_scaled_into(uint32_t word, float v, uint32_t rng, float scale, int sel)
+{
+    switch (sel) {
+    case 0: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 0);
+    case 1: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 1);
+    case 2: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 2);
+    default: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 3);
+    }
+}
+
+// Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
+PMN_DEV void deq8(uint32_t cw, float d, float (&v)[8])
+{
+    float q[8];
+    fp4x8_to_f32(cw, q);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = q[i] * d;
+}
+
+// a + b for a per-lane a and a wavefront-uniform b: one 64-bit vector add. Written as asm so that
+// the compiler keeps it an add instead of re-deriving each slot's counter with a 64-bit multiply.
+PMN_DEV uint64_t add_uniform64(uint64_t a, uint64_t b)
+{
+    uint64_t r;
+    asm("v_lshl_add_u64 %0, %1, 0, %2" : "=v"(r) : "v"(a), "s"(b));
+    return r;
+}
+
 // y (|y| <= 448) -> E4M3 byte, round to nearest even.
 PMN_DEV uint32_t e4m3_rne(float y)
 {

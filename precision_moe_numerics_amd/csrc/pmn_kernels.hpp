@@ -22,6 +22,14 @@ hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, 
                                  uint8_t* scales, float* outer_out, hipStream_t stream, bool square = false,
                                  void* ws = nullptr, size_t ws_bytes = 0);
 size_t nvfp4_weight_1pass_ws_bytes();
+// Weights (weight mode, computed outer scales) and the backward's W^T operand from them: wt E4M3
+// [cols x rows] in the blocked layout below (rows % 64 == 0) and wte E8M0 [rows/32 x cols], the
+// bytes of launch_requant(ungrouped, E4M3, SR with (seed, stream_id), k-block-major, blocked).
+// One read of x when the device holds a tile of every matrix per CU, else the two steps.
+hipError_t launch_nvfp4_quantize_weights_bwd(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_outer,
+                                             uint8_t* codes, uint8_t* scales, float* outer_out, uint8_t* wt,
+                                             uint8_t* wte, uint64_t seed, uint32_t stream_id, void* ws,
+                                             size_t ws_bytes, hipStream_t stream);
 
 // Row-wise MXFP8. With padded_offsets null the E8M0 scales are row-major [M x N/32]; otherwise
 // they are k-block-major [N/32 x ld_e8m0] with slot s of group g at column

@@ -382,35 +382,86 @@ PMN_DEV void w1p_wait_loads()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-__global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uint16_t* __restrict__ x, int64_t G,
-                                                                       int64_t group_blocks, float* __restrict__ outer_out,
-                                                                       uint8_t* __restrict__ codes,
-                                                                       uint8_t* __restrict__ scales,
-                                                                       uint32_t* __restrict__ words,
-                                                                       uint32_t* __restrict__ flags)
+// The backward's operand from the same read (RQ). [AREX] "转置打散分组,随机舍入保住期望值": the
+// backward multiplies by the transposed weights, whose blocks run along the other axis, so the
+// NVFP4 weights are dequantized, transposed and re-quantized to MXFP8 (E8M0 per 32 values, SR).
+// Weights do not change between a step's forward and backward, so the RQ kernel produces that
+// operand while each matrix is on chip. Its workgroups own rectangular tiles instead of
+// interleaved blocks: tile (band, q) is rows band * TH .. and columns q * TW .. of every matrix
+// (TH a multiple of 64, TW of 16, one tile per workgroup), thread t holding blocks t + 512 k of
+// the tile in row-major order. After quantizing matrix m a workgroup stages the tile's codes and
+// scales in the LDS; thread pairs then take 8 columns x 32 rows (16 rows per lane, the pair's
+// maxima meet by one exchange), dequantize, reduce the per-column amax and convert by SR (one
+// Philox4x32-10 call per 8 columns of a row, keyed by the element's index in the [rows x cols]
+// source) into one 16-byte chunk per column of the backward's blocked W^T layout. The bytes are
+// those of requant_transpose_sr_mxfp8 on the quantized weights (ungrouped, E4M3, blocked).
+constexpr int W1R_STG_CODES = 32768;   // TH * (TW / 2 + 8) bytes with TH <= 512, TH * TW <= 57344
+constexpr int W1R_STG_SCALES = 3584;   // TH * TW / 16
+constexpr int W1R_TH_MAX = 512;
+
+struct W1PArgs {
+    const uint16_t* x;
+    int64_t G;              // matrices (rows_per_outer rows each)
+    int64_t group_blocks;   // 16-value blocks per matrix
+    float* outer_out;
+    uint8_t* codes;
+    uint8_t* scales;
+    uint32_t* words;
+    uint32_t* flags;
+    // RQ: the matrix shape, the tile and the W^T outputs
+    int64_t R, C;
+    int TH, TW;
+    uint8_t* wt;            // E4M3 [C x G*R], blocked (1 KB blocks of 16 rows x 64 bytes)
+    uint8_t* wte;           // E8M0 [G*R/32 x C]
+    uint64_t seed;
+    uint32_t stream_id;
+};
+
+template <bool RQ>
+__global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(W1PArgs a)
 {
     // landing area of the copies: wavefront w, copy c (block c / 2, half c % 2) at [w][c]
     __shared__ __attribute__((aligned(1024))) uint8_t sdata[W1P_WAVES][2 * W1P_NBT][1024];
+    __shared__ __attribute__((aligned(16))) uint8_t stg_c[RQ ? W1R_STG_CODES : 16];   // RQ: staged codes
+    __shared__ uint8_t stg_s[RQ ? W1R_STG_SCALES : 16];                               // RQ: staged scales
     __shared__ uint32_t swords[W1P_WAVES][64];
     __shared__ float red_a[W1P_WAVES];
     __shared__ uint32_t red_w[2][W1P_WAVES];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nwg = gridDim.x;
-    const int64_t T = (int64_t)nwg * W1P_THREADS;
-    const int64_t t0 = (int64_t)blockIdx.x * W1P_THREADS + tid;
+    const int64_t G = a.G, group_blocks = a.group_blocks;
     const uint32_t lds_data = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)&sdata[wave][0][0]);
     const uint32_t lds_words = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)&swords[wave][0]);
-    const uint8_t* xb = reinterpret_cast<const uint8_t*>(x);
+    const uint8_t* xb = reinterpret_cast<const uint8_t*>(a.x);
+
+    // block k of this thread: its index within the matrix and whether it exists (a thread past
+    // the last block re-reads an existing one, which changes no max and is not quantized)
+    int bidx[W1P_NBT];   // fewer than 2^31 blocks per matrix (one matrix fits on chip)
+    bool bok[W1P_NBT];
+    const int bpr = RQ ? a.TW >> 4 : 0;                  // RQ: blocks per tile row
+    const int pitch = RQ ? (a.TW >> 1) + 8 : 0;          // RQ: staged code bytes per tile row
+    const int64_t row0 = RQ ? (int64_t)(blockIdx.x / (int)(a.C / a.TW)) * a.TH : 0;
+    const int64_t col0 = RQ ? (int64_t)(blockIdx.x % (int)(a.C / a.TW)) * a.TW : 0;
+#pragma unroll
+    for (int k = 0; k < W1P_NBT; k++) {
+        if (RQ) {
+            const int beta = tid + W1P_THREADS * k, nblk = (a.TH * a.TW) >> 4;
+            bok[k] = beta < nblk;
+            const int b = bok[k] ? beta : 0;
+            bidx[k] = (int)(((row0 + b / bpr) * a.C + col0) / 16 + b % bpr);
+        } else {
+            const int64_t blk = (int64_t)blockIdx.x * W1P_THREADS + tid + (int64_t)k * nwg * W1P_THREADS;
+            bok[k] = blk < group_blocks;
+            bidx[k] = (int)(bok[k] ? blk : group_blocks - 1);
+        }
+    }
 
     // matrix m into the landing area: 14 copies per lane
     auto copy_in = [&](int64_t m) {
 #pragma unroll
         for (int k = 0; k < W1P_NBT; k++) {
-            // a thread past the matrix's last block re-reads that block (it changes no max and
-            // is not quantized)
-            const int64_t blk = t0 + k * T;
-            const uint8_t* src = xb + 32 * (m * group_blocks + (blk < group_blocks ? blk : group_blocks - 1));
+            const uint8_t* src = xb + 32 * (m * group_blocks + bidx[k]);
             dma16(src, lds_data + (2 * k) * 1024);
             dma16(src + 16, lds_data + (2 * k + 1) * 1024);
         }
@@ -427,25 +478,25 @@ __global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uin
     };
     // publish this workgroup's max |x| of matrix m (a bf16 value: its upper 16 bits)
     auto arrive = [&](int64_t m, const RawBlock16 (&b)[W1P_NBT]) {
-        float a = 0.0f;
+        float v = 0.0f;
 #pragma unroll
-        for (int k = 0; k < W1P_NBT; k++) a = fmaxf(a, block_absmax(unpack_block(b[k])));
-        a = wave_max(a);
-        if (lane == 0) red_a[wave] = a;
+        for (int k = 0; k < W1P_NBT; k++) v = fmaxf(v, block_absmax(unpack_block(b[k])));
+        v = wave_max(v);
+        if (lane == 0) red_a[wave] = v;
         __syncthreads();
         if (tid == 0) {
-            float v = red_a[0];
+            float r = red_a[0];
 #pragma unroll
-            for (int w = 1; w < W1P_WAVES; w++) v = fmaxf(v, red_a[w]);
-            const uint32_t word = ((uint32_t)(m + 1) << 16) | (__float_as_uint(v) >> 16);
-            __hip_atomic_store(words + (m & 3) * W1P_MAX_WG + blockIdx.x, word, __ATOMIC_RELAXED,
+            for (int w = 1; w < W1P_WAVES; w++) r = fmaxf(r, red_a[w]);
+            const uint32_t word = ((uint32_t)(m + 1) << 16) | (__float_as_uint(r) >> 16);
+            __hip_atomic_store(a.words + (m & 3) * W1P_MAX_WG + blockIdx.x, word, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
     };
     // thread u < nwg reads workgroup u's word of matrix m into the LDS (every lane issues one
     // copy, so that each wavefront's count of outstanding copies is fixed)
     auto word_in = [&](int64_t m) {
-        dma4(words + (m & 3) * W1P_MAX_WG + (tid < nwg ? tid : 0), lds_words);
+        dma4(a.words + (m & 3) * W1P_MAX_WG + (tid < nwg ? tid : 0), lds_words);
     };
     // matrix m's amax from the landed words; a word not yet published is read again (boundedly)
     auto gather = [&](int64_t m) -> float {
@@ -453,12 +504,12 @@ __global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uin
         if (tid < nwg) {
             uint32_t word = swords[wave][lane];
             const uint32_t tag = (uint32_t)(m + 1);
-            const uint32_t* wp = words + (m & 3) * W1P_MAX_WG + tid;
+            const uint32_t* wp = a.words + (m & 3) * W1P_MAX_WG + tid;
             for (int spin = 0; (word >> 16) != tag; spin++) {
                 if (spin == W1P_SPIN_LIMIT) {
                     // never expected with every workgroup resident; the outputs are then wrong
                     // and flags[0] says so, but no wavefront waits forever
-                    atomicOr(flags, 1u);
+                    atomicOr(a.flags, 1u);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
@@ -481,17 +532,101 @@ __global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uin
         const float ys = fast ? 1.0f / s_o : 0.0f;
 #pragma unroll
         for (int k = 0; k < W1P_NBT; k++) {
-            const int64_t blk = t0 + k * T;
-            if (blk < group_blocks) {
+            if (bok[k]) {
                 const Block16 v = unpack_block(b[k]);
                 uint32_t sb;
                 uint2 q;
                 if (fast) quant_block_ab<false, true>(v, block_absmax(v), s_o, sb, q, ys);
                 else quant_block_ab<false, false>(v, block_absmax(v), s_o, sb, q);
-                const int64_t i = m * group_blocks + blk;
-                reinterpret_cast<uint2*>(codes)[i] = q;
-                scales[i] = (uint8_t)sb;
+                const int64_t i = m * group_blocks + bidx[k];
+                reinterpret_cast<uint2*>(a.codes)[i] = q;
+                a.scales[i] = (uint8_t)sb;
+                if (RQ) {
+                    // (the laundered sizes keep these offsets from being hoisted out of the
+                    // matrix loop, where they would hold registers for the whole kernel)
+                    int bp = bpr, pt = pitch;
+                    asm volatile("" : "+s"(bp), "+s"(pt));
+                    const int beta = tid + W1P_THREADS * k;
+                    const int r = beta / bp, c = beta - r * bp;
+                    *reinterpret_cast<uint2*>(&stg_c[r * pt + 8 * c]) = q;
+                    stg_s[r * bp + c] = (uint8_t)sb;
+                }
             }
+        }
+    };
+    // RQ: matrix m's tile, staged by quantize, to E4M3 codes of W^T by SR
+    auto requant = [&](int64_t m, float s_o) {
+        __syncthreads();   // every thread's codes and scales are staged
+        // (sizes laundered as in quantize: every address below is formed inside this call)
+        int pt = pitch, bp = bpr, cpr = a.TW >> 3;        // cpr: column octets per tile row
+        asm volatile("" : "+s"(pt), "+s"(bp), "+s"(cpr));
+        const int p = tid >> 1, h = tid & 1;
+        if (p >= cpr * (a.TH >> 5)) return;
+        const int rb = p / cpr, co = p - rb * cpr;
+        const int r0 = 32 * rb + 16 * h;                  // the lane's first tile row
+        const uint8_t* cb = &stg_c[r0 * pt + 4 * co];
+        const uint8_t* sbp = &stg_s[r0 * bp + (co >> 1)];
+        // pass 1: per-column amax over the lane's 16 rows (codes and scales read from the LDS in
+        // both passes, so that neither pass keeps them in registers)
+        float amax[8];
+#pragma unroll
+        for (int c = 0; c < 8; c++) amax[c] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+            float v0[8], v1[8];
+            deq8(*reinterpret_cast<const uint32_t*>(cb + j * pt), e4m3_value(sbp[j * bp]) * s_o, v0);
+            deq8(*reinterpret_cast<const uint32_t*>(cb + (j + 1) * pt), e4m3_value(sbp[(j + 1) * bp]) * s_o, v1);
+#pragma unroll
+            for (int c = 0; c < 8; c++) amax[c] = fmaxf(fmaxf(amax[c], fabsf(v0[c])), fabsf(v1[c]));
+        }
+        // the other 16 rows of the 32-row block sit in the partner lane
+        float escale[8];   // 2^e: the scaled converter divides by it exactly
+        uint32_t elo = 0u, ehi = 0u;
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            amax[c] = fmaxf(amax[c], __shfl_xor(amax[c], 1, 64));
+            const int e = e8m0_exponent<E8M0_E4M3>(amax[c]);
+            escale[c] = __builtin_ldexpf(1.0f, e);
+            if (c < 4) elo |= (uint32_t)(e + 127) << (8 * c);
+            else ehi |= (uint32_t)(e + 127) << (8 * (c - 4));
+        }
+        const int64_t n0 = m * a.R + row0 + r0;           // W row (W^T column) of the lane's first row
+        const int64_t k0 = col0 + 8 * co;                 // first W column (W^T row)
+        if (h == 0) *reinterpret_cast<uint2*>(a.wte + (n0 >> 5) * a.C + k0) = make_uint2(elo, ehi);
+        asm volatile("" ::: "memory");   // pass 2 reads the LDS again
+        // pass 2: element (n, k) of the [G*R x C] source draws from Philox block (n * C + k) / 8;
+        // consecutive rows are C / 8 blocks apart. (The laundered key makes the scalar unit
+        // derive the round keys here rather than hold them for the whole kernel.)
+        uint32_t seed_lo = (uint32_t)a.seed, seed_hi = (uint32_t)(a.seed >> 32), sid = a.stream_id;
+        asm volatile("" : "+s"(seed_lo), "+s"(seed_hi), "+s"(sid));
+        const uint64_t seed = ((uint64_t)seed_hi << 32) | seed_lo;
+        uint64_t ctr = ((uint64_t)n0 * (uint64_t)a.C + (uint64_t)k0) >> 3;
+        const uint64_t cstep = (uint64_t)a.C >> 3;
+        uint32_t o[8][4];
+#pragma unroll
+        for (int c = 0; c < 8; c++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) o[c][q] = __builtin_nondeterministic_value(o[c][q]);   // every byte is written below
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            float v[8];
+            deq8(*reinterpret_cast<const uint32_t*>(cb + j * pt), e4m3_value(sbp[j * bp]) * s_o, v);
+            uint32_t rw[4];
+            rand16x8(seed, sid, ctr, rw);
+            ctr = add_uniform64(ctr, cstep);
+#pragma unroll
+            for (int c = 0; c < 8; c++)
+                o[c][j >> 2] = e4m3_sr_scaled_into(o[c][j >> 2], v[c], sr_operand(rw[c >> 1], c & 1), escale[c], j & 3);
+        }
+        // the lane's 16 slots of column k are one 16-byte chunk of W^T row k
+        const int64_t ldb = (G * a.R) >> 6;               // 64-slot block columns of W^T
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+            const int64_t k = k0 + c;
+            const int r16 = (int)(k & 15);
+            const int pos = (int)((n0 & 63) >> 4) ^ ((r16 >> 2) & 3);
+            *reinterpret_cast<uint4*>(a.wt + ((k >> 4) * ldb + (n0 >> 6)) * 1024 + 64 * r16 + 16 * pos) =
+                make_uint4(o[c][0], o[c][1], o[c][2], o[c][3]);
         }
     };
     // round m: cur holds matrix m (published); matrix m + 1 sits in the landing area
@@ -508,8 +643,9 @@ __global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uin
         if (more2) w1p_wait_loads<2 * W1P_NBT>();
         else w1p_wait_loads<0>();
         const float s_o = outer_from_amax(gather(m));
-        if (blockIdx.x == 0 && tid == 0) outer_out[m] = s_o;
+        if (blockIdx.x == 0 && tid == 0) a.outer_out[m] = s_o;
         quantize(m, cur, s_o);
+        if (RQ) requant(m, s_o);
     };
     RawBlock16 b0[W1P_NBT], b1[W1P_NBT];
     copy_in(0);
@@ -521,15 +657,39 @@ __global__ __launch_bounds__(W1P_THREADS, 1) void k_nvfp4_weight_1pass(const uin
         round(m, b0, b1);
         if (m + 1 < G) round(m + 1, b1, b0);
     }
+    // flags[0] bit 1: the W^T operand came from this kernel (bit 0: a wait was abandoned)
+    if (RQ && blockIdx.x == 0 && tid == 0) atomicOr(a.flags, 2u);
 }
 
 size_t nvfp4_weight_1pass_ws_bytes() { return (size_t)4 * W1P_MAX_WG * 4 + 256; }
 
+// RQ tile of an R x C matrix for at most ncu workgroups: TH a multiple of 64 dividing R (at most
+// W1R_TH_MAX), TW a multiple of 16 dividing C, TH * TW <= the blocks a workgroup holds; the most
+// tiles, then the widest. False if none exists.
+static bool w1r_tile(int64_t R, int64_t C, int ncu, int& TH, int& TW)
+{
+    int64_t best = 0;
+    for (int64_t th = 64; th <= W1R_TH_MAX && th <= R; th += 64) {
+        if (R % th != 0) continue;
+        for (int64_t tw = 16; tw <= C; tw += 16) {
+            if (C % tw != 0 || th * tw > (int64_t)W1P_NBT * W1P_THREADS * 16) continue;
+            const int64_t tiles = (R / th) * (C / tw);
+            if (tiles > ncu || tiles < best || (tiles == best && tw <= TW)) continue;
+            best = tiles;
+            TH = (int)th;
+            TW = (int)tw;
+        }
+    }
+    return best > 0;
+}
+
 // The one-read path, if the device and the shape allow it; hipErrorNotSupported otherwise (the
-// caller then takes the two passes).
+// caller then takes the two passes). wt != nullptr: also the backward's W^T operand (RQ), which
+// needs rows_per_outer % 64 == 0 and a tile (w1r_tile).
 static hipError_t launch_nvfp4_weight_1pass(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_outer,
                                             uint8_t* codes, uint8_t* scales, float* outer_out, void* ws,
-                                            size_t ws_bytes, hipStream_t stream)
+                                            size_t ws_bytes, hipStream_t stream, uint8_t* wt = nullptr,
+                                            uint8_t* wte = nullptr, uint64_t seed = 0, uint32_t stream_id = 0)
 {
     if (ws == nullptr || ws_bytes < nvfp4_weight_1pass_ws_bytes()) return hipErrorNotSupported;
     // a captured graph would replay the launch without the co-residency a cooperative launch
@@ -537,33 +697,67 @@ static hipError_t launch_nvfp4_weight_1pass(const uint16_t* x, int64_t rows, int
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone)
         return hipErrorNotSupported;
+    const bool rq = wt != nullptr;
+    const void* kern = rq ? (const void*)k_nvfp4_weight_1pass<true> : (const void*)k_nvfp4_weight_1pass<false>;
     int dev = 0, ncu = 0, coop = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_nvfp4_weight_1pass, W1P_THREADS, 0) != hipSuccess)
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, W1P_THREADS, 0) != hipSuccess)
         return hipErrorNotSupported;
     if (!coop || per_cu < 1 || ncu < 1 || ncu > W1P_MAX_WG) return hipErrorNotSupported;
-    int64_t G = rows / rows_per_outer;
-    int64_t group_blocks = rows_per_outer * (cols / 16);
-    if (G > W1P_MAX_G || group_blocks > (int64_t)W1P_NBT * ncu * W1P_THREADS) return hipErrorNotSupported;
-    uint32_t* words = static_cast<uint32_t*>(ws);
-    uint32_t* flags = words + 4 * W1P_MAX_WG;
+    W1PArgs a{};
+    a.x = x;
+    a.G = rows / rows_per_outer;
+    a.group_blocks = rows_per_outer * (cols / 16);
+    a.outer_out = outer_out;
+    a.codes = codes;
+    a.scales = scales;
+    a.words = static_cast<uint32_t*>(ws);
+    a.flags = a.words + 4 * W1P_MAX_WG;
+    int nwg = ncu;
+    if (a.G > W1P_MAX_G) return hipErrorNotSupported;
+    if (rq) {
+        if (rows_per_outer % 64 != 0 || !w1r_tile(rows_per_outer, cols, ncu, a.TH, a.TW)) return hipErrorNotSupported;
+        a.R = rows_per_outer;
+        a.C = cols;
+        a.wt = wt;
+        a.wte = wte;
+        a.seed = seed;
+        a.stream_id = stream_id;
+        nwg = (int)((a.R / a.TH) * (a.C / a.TW));
+    } else if (a.group_blocks > (int64_t)W1P_NBT * ncu * W1P_THREADS) {
+        return hipErrorNotSupported;
+    }
     const int64_t nfill = (int64_t)(nvfp4_weight_1pass_ws_bytes() / 4);
     hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((nfill + 255) / 256)), dim3(256), 0, stream,
                        static_cast<uint32_t*>(ws), nfill, 0u);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    void* args[] = {(void*)&x, (void*)&G, (void*)&group_blocks, (void*)&outer_out, (void*)&codes, (void*)&scales,
-                    (void*)&words, (void*)&flags};
-    e = hipLaunchCooperativeKernel((const void*)k_nvfp4_weight_1pass, dim3((unsigned)ncu), dim3(W1P_THREADS), args, 0,
-                                   stream);
+    void* args[] = {(void*)&a};
+    e = hipLaunchCooperativeKernel(kern, dim3((unsigned)nwg), dim3(W1P_THREADS), args, 0, stream);
     if (e != hipSuccess) {
         // a runtime that refuses the cooperative launch: the two reads instead
         (void)hipGetLastError();
         return hipErrorNotSupported;
     }
     return hipSuccess;
+}
+
+hipError_t launch_nvfp4_quantize_weights_bwd(const uint16_t* x, int64_t rows, int64_t cols, int64_t rows_per_outer,
+                                             uint8_t* codes, uint8_t* scales, float* outer_out, uint8_t* wt,
+                                             uint8_t* wte, uint64_t seed, uint32_t stream_id, void* ws,
+                                             size_t ws_bytes, hipStream_t stream)
+{
+    if (rows == 0) return hipSuccess;
+    hipError_t e = launch_nvfp4_weight_1pass(x, rows, cols, rows_per_outer, codes, scales, outer_out, ws, ws_bytes,
+                                             stream, wt, wte, seed, stream_id);
+    if (e != hipErrorNotSupported) return e;
+    e = launch_nvfp4_quantize(x, rows, cols, false, rows_per_outer, nullptr, codes, scales, outer_out, stream, false,
+                              ws, ws_bytes);
+    if (e != hipSuccess) return e;
+    return launch_requant(codes, scales, outer_out, cols, rows_per_outer, nullptr, rows, nullptr, 0, PMN_TARGET_E4M3,
+                          seed, stream_id, wt, wte, rows, true, nullptr, stream, true);
 }
 
 hipError_t launch_nvfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, bool four_six,

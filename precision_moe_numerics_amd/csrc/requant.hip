@@ -128,18 +128,6 @@ struct TransposeArgs {
     int64_t unit;
 };
 
-// E4M3 code of v / scale (scale a power of two) by stochastic rounding with the given SR operand,
-// written into byte `sel` (0..3) of `word`.
-PMN_DEV uint32_t e4m3_sr_scaled_into(uint32_t word, float v, uint32_t rng, float scale, int sel)
-{
-    switch (sel) {
-    case 0: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 0);
-    case 1: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 1);
-    case 2: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 2);
-    default: return (uint32_t)__builtin_amdgcn_cvt_scalef32_sr_fp8_f32((int)word, v, rng, scale, 3);
-    }
-}
-
 // E4M3 codes of a / scale and b / scale (scale a power of two), round to nearest even, written
 // into the low (hi = false) or high 16 bits of `word`.
 PMN_DEV uint32_t e4m3_rne_pair_scaled_into(uint32_t word, float a, float b, float scale, bool hi)
@@ -151,15 +139,6 @@ PMN_DEV uint32_t e4m3_rne_pair_scaled_into(uint32_t word, float a, float b, floa
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// a + b for a per-lane a and a wavefront-uniform b: one 64-bit vector add. Written as asm so that
-// the compiler keeps it an add instead of re-deriving each slot's counter with a 64-bit multiply.
-PMN_DEV uint64_t add_uniform64(uint64_t a, uint64_t b)
-{
-    uint64_t r;
-    asm("v_lshl_add_u64 %0, %1, 0, %2" : "=v"(r) : "v"(a), "s"(b));
-    return r;
-}
-
 // p, a wavefront-uniform pointer, pinned to scalar registers: a load from p + (32-bit lane offset)
 // then takes the scalar-base addressing form and needs no per-lane 64-bit address arithmetic.
 typedef const __attribute__((address_space(1))) uint8_t gbyte;   // global memory
@@ -169,15 +148,6 @@ PMN_DEV gbyte* uniform_ptr(const uint8_t* p)
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
     return reinterpret_cast<gbyte*>(((uint64_t)hi << 32) | lo);
-}
-
-// Dequantize 8 consecutive NVFP4 values (one code word, one effective scale d) to fp32.
-PMN_DEV void deq8(uint32_t cw, float d, float (&v)[8])
-{
-    float q[8];
-    fp4x8_to_f32(cw, q);
-#pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = q[i] * d;
 }
 
 PMN_DEV void bf8(uint4 w, float (&v)[8])

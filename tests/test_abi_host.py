@@ -102,6 +102,35 @@ def test_quantize_with_workspace_argument_errors(lib):
     assert lib.nvfp4_quantize_ws(None, 0, 32, 0, 1, None, None, None, None, None, 0, None) == 0
 
 
+def test_weights_bwd_argument_errors(lib):
+    """nvfp4_quantize_weights_bwd checks shapes (rows a multiple of 64 and of rows_per_outer, cols
+    of 16), pointers, the workspace and alignment before any launch; the backward refuses the
+    prepared operand with the FP4 variant or an N that is not a multiple of 64, and the SwiGLU
+    backward any flag but PMN_BWD_W_PREPARED."""
+    fake = C.c_void_p(0x1000)     # never dereferenced
+    n = lib.nvfp4_quantize_ws_size()
+    args = lambda rows, cols, rpo, wt=fake, ws=fake, nb=n: (fake, rows, cols, rpo, fake, fake, fake, wt, fake, 0, 0, ws,
+                                                         nb, None)
+    assert lib.nvfp4_quantize_weights_bwd(*args(96, 64, 32)) == -2
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 40, 64)) == -2
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 64, 48)) == -2
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 64, 64, wt=None)) == -1
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 64, 64, ws=None)) == -4
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 64, 64, nb=n - 1)) == -4
+    assert lib.nvfp4_quantize_weights_bwd(*args(128, 64, 64, wt=C.c_void_p(0x1008))) == -3
+    assert lib.nvfp4_quantize_weights_bwd(*args(0, 64, 64)) == 0
+    ws = lib.moe_grouped_gemm_bwd_workspace_size(64, 1, 256, 256, 3)
+    bwd = lambda flags, N: lib.moe_grouped_gemm_bwd(fake, fake, fake, fake, 64, 1, None, fake, fake, None, 1, fake, 1,
+                                                   64, N, 256, flags, 0, 0, 0, 0, 0, fake, fake, fake, ws, None)
+    assert bwd(1 | 8 | 4, 256) == -1
+    assert bwd(1 | 8, 288) == -2
+    assert bwd(1 | 16, 256) == -1
+    swi = lambda flags: lib.moe_grouped_gemm_bwd_swiglu(fake, fake, fake, fake, fake, 64, 1, None, fake, fake, fake,
+                                                        1, fake, 1, 64, 256, 256, flags, 0, 0, 0, fake, fake, fake,
+                                                        ws, None)
+    assert swi(1) == -1 and swi(4) == -1
+
+
 def test_check_indices_argument_errors(lib):
     """pmn_check_indices refuses, before any launch: no result or neither array (PMN_EINVAL), no
     groups or a negative M with offsets, a negative count or row bound with gather (PMN_ESHAPE),

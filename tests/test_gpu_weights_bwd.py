@@ -1,0 +1,150 @@
+"""nvfp4_quantize_weights_bwd: the weights' NVFP4 codes for the forward and, from the same read,
+the backward's transposed SR requant of them (W^T E4M3 codes in the blocked layout, E8M0
+k-block-major). Checked bit for bit against the oracle (its NVFP4 quantizer and its transposed SR
+requant, [AREX] "转置打散分组,随机舍入保住期望值") on tile shapes the one-read kernel takes (tiny
+tiles with idle threads, the 48-expert layer's w13 and w2 tiles, several rounds) and on ones that
+fall back to the two steps; against the backward's own workspace at the layer's full w13 and w2
+sizes; and through the backward, whose gradients with the prepared operand equal those with the
+NVFP4 weights. The workspace's status word tells which path ran: the one-read kernel that also
+requantizes sets its bit 1 (bit 0 would mean an abandoned wait); the two steps leave it clear."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from decoders import unblock
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def P():
+    import precision_moe_numerics_amd as P
+    return P
+
+
+@pytest.fixture(scope="module")
+def I():
+    from precision_moe_numerics_amd import inputs as I
+    return I
+
+
+def npy(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def fresh_ws(P):
+    return torch.zeros((P.nvfp4_quantize_ws_size(),), dtype=torch.uint8, device=DEV)
+
+
+def one_read_ran(ws):
+    """The status word after the word slots of the one-read kernels: bit 1 if the weights and
+    their W^T operand came from one read; bit 0 (a wait abandoned) must stay clear."""
+    torch.cuda.synchronize()
+    st = int(ws.view(torch.int32)[4 * 512].item())
+    assert st & 1 == 0
+    return bool(st & 2)
+
+
+@pytest.mark.parametrize("G,R,C,one_read", [
+    (2, 128, 896, True),      # 64 x 16 tiles: 64 of 512 threads hold a block, 4 thread pairs requantize
+    (5, 64, 256, True),       # five rounds of small matrices
+    (3, 256, 512, True),
+    (2, 2048, 7168, True),    # one expert's w1 and w3 (64 x 896 tiles, 256 workgroups)
+    (1, 7168, 2048, True),    # one expert's w2 (448 x 128 tiles)
+    (4, 32, 128, False),      # 32-row matrices: no 64-row tiles, the two steps
+])
+def test_matches_oracle(P, I, G, R, C, one_read):
+    w = I.normal((G * R, C), 0.02, 300 + G)
+    if G >= 2:
+        w[R:2 * R] *= 1e-3
+        w[R + 3, 5] = 0.25                                  # one isolated value sets that amax
+    seed, stream = 77 + G, 4
+    ws = fresh_ws(P)
+    wb = P.nvfp4_quantize_weights_bwd(w.to(DEV), R, seed=seed, rng_stream=stream, workspace=ws)
+    assert one_read_ran(ws) == one_read
+    ref = O.nvfp4_quantize(w, R, False)
+    assert np.array_equal(npy(wb.q.codes), ref["codes"])
+    assert np.array_equal(npy(wb.q.scales), ref["scales"])
+    assert np.array_equal(npy(wb.q.outer).view(np.uint32), np.asarray(ref["outer"], np.float32).view(np.uint32))
+    ro, roe = O.requant_transpose_sr(ref, seed=seed, stream=stream)
+    assert ro.shape == (C, G * R)
+    assert np.array_equal(unblock(npy(wb.wt), C, G * R), ro)
+    assert np.array_equal(npy(wb.wte).T, roe)
+
+
+def test_capturing_stream_takes_the_two_steps(P, I):
+    """Under graph capture the call records the two steps; replays give the eager bytes."""
+    G, R, C = 2, 128, 512
+    w = I.normal((G * R, C), 0.02, 310).to(DEV)
+    eager = P.nvfp4_quantize_weights_bwd(w, R, seed=3, rng_stream=2)
+    ws = fresh_ws(P)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            captured = P.nvfp4_quantize_weights_bwd(w, R, seed=3, rng_stream=2, workspace=ws)
+    for _ in range(3):
+        for t in (captured.q.codes, captured.wt, captured.wte):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in ((captured.q.codes, eager.q.codes), (captured.q.scales, eager.q.scales),
+                     (captured.wt, eager.wt), (captured.wte, eager.wte)):
+            assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("G,N,K,counts", [(3, 256, 192, [70, 0, 130]), (2, 512, 896, [129, 64])])
+def test_backward_with_the_prepared_operand(P, I, G, N, K, counts):
+    """moe_grouped_gemm_bwd and moe_grouped_gemm_bwd_swiglu with a WeightsBwd give the gradients
+    of the same calls with its NVFP4 weights and rng_stream_b = its stream, bit for bit; the
+    call with the NVFP4 weights also writes the same W^T bytes into its workspace."""
+    M = sum(counts)
+    offsets = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int64), device=DEV)
+    x = I.normal((M, K), 1.0, 320, DEV)
+    xq = P.nvfp4_quantize(x, P.NVFP4_ACT)
+    wb = P.nvfp4_quantize_weights_bwd(I.normal((G * N, K), 0.02, 321, DEV), N // 2, seed=9, rng_stream=6)
+    dy = I.normal((M, N), 1e-3, 322, DEV)
+    da0, db0, ws0 = P.moe_grouped_gemm_bwd(dy, xq, wb.q, offsets, M, N, seed=9, rng_stream_b=6)
+    da1, db1, _ = P.moe_grouped_gemm_bwd(dy, xq, wb, offsets, M, N, seed=9, rng_stream_b=123)
+    assert torch.equal(da0, da1) and torch.equal(db0, db1)
+    v = P.bwd_workspace_views(ws0, M, G, N, K)
+    assert torch.equal(v["wt"], wb.wt) and torch.equal(v["wte"], wb.wte)
+    da_act = I.normal((M, N // 2), 1e-3, 323, DEV).float()
+    h13 = I.normal((M, N), 1.0, 324, DEV)
+    dx0, dw0, _ = P.moe_grouped_gemm_bwd_swiglu(da_act, h13, xq, wb.q, offsets, M, N, seed=9, rng_stream_b=6)
+    dx1, dw1, _ = P.moe_grouped_gemm_bwd_swiglu(da_act, h13, xq, wb, offsets, M, N, seed=9, rng_stream_b=6)
+    assert torch.equal(dx0, dx1) and torch.equal(dw0, dw1)
+
+
+@pytest.mark.parametrize("which", ["w13", "w2"])
+def test_full_size_equals_the_backward_workspace(P, I, which):
+    """The 48-expert layer's w13 (48 x 4096 x 7168, one outer scale per 2048 rows) and w2 (48 x
+    7168 x 2048): the one-read kernel's W^T bytes equal those the backward requantizes into its
+    workspace from the NVFP4 weights, and its NVFP4 bytes those of nvfp4_quantize_ws."""
+    G = 48
+    N, K, rpo = (4096, 7168, 2048) if which == "w13" else (7168, 2048, 7168)
+    torch.manual_seed(5)
+    w = (torch.randn((G * N, K), device=DEV) * 0.02).to(torch.bfloat16)
+    ws = fresh_ws(P)
+    wb = P.nvfp4_quantize_weights_bwd(w, rpo, seed=11, rng_stream=1, workspace=ws)
+    assert one_read_ran(ws)
+    q = P.nvfp4_quantize(w, P.NVFP4_WEIGHT, rows_per_outer=rpo)
+    assert torch.equal(wb.q.codes, q.codes) and torch.equal(wb.q.scales, q.scales)
+    assert torch.equal(wb.q.outer.view(torch.int32), q.outer.view(torch.int32))
+    del w
+    M = 64
+    counts = [M] + [0] * (G - 1)
+    offsets = torch.as_tensor(np.concatenate([[0], np.cumsum(counts)]).astype(np.int64), device=DEV)
+    xq = P.nvfp4_quantize(I.normal((M, K), 1.0, 330, DEV), P.NVFP4_ACT)
+    dy = I.normal((M, N), 1e-3, 331, DEV)
+    da0, _, ws0 = P.moe_grouped_gemm_bwd(dy, xq, q, offsets, M, N, flags=P.BWD_DGRAD, seed=11, rng_stream_b=1)
+    v = P.bwd_workspace_views(ws0, M, G, N, K)
+    assert torch.equal(v["wt"], wb.wt) and torch.equal(v["wte"], wb.wte)
+    da1, _, _ = P.moe_grouped_gemm_bwd(dy, xq, wb, offsets, M, N, flags=P.BWD_DGRAD, seed=11)
+    assert torch.equal(da0, da1)
