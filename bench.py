@@ -3,12 +3,14 @@
 A step is one pass of the whole hot path over one batch of synthetic input, by default the
 one-GPU expert share (48 local experts, 65536 routed slots with Zipf(1.1) loads, hidden 7168,
 FFN 2048, SwiGLU):
-  weights:  NVFP4 quantization of w13 and w2 (one outer scale per expert and matrix)
+  weights:  NVFP4 quantization of w13 and w2 (one outer scale per expert and matrix) and, from
+            the same read, the SR requantization of W13^T and W2^T for the backward's dgrad
   forward:  NVFP4 quantization of X (per-token outer scale, 4/6) -> grouped GEMM w13 with the
             SwiGLU epilogue (h13 saved) -> NVFP4 quantization of A -> grouped GEMM w2 with the
             fused RHT32 + S2F6 epilogue (the combine payload)
-  backward: w2 backward (dY MXFP8 row/column quantization, SR requantization of W2^T and A^T,
-            MXFP8 dgrad and wgrad) -> SwiGLU backward -> w13 backward (same steps with X^T, W13^T)
+  backward: w2 backward (dY MXFP8 row/column quantization, SR requantization of A^T, MXFP8 dgrad
+            and wgrad) -> w13 backward (the same with X^T, its dY the SwiGLU backward formed
+            inside the dY quantization)
 Inputs are generated on the GPU from fixed seeds before the timed region and stay resident in
 HBM. Per-call device time comes from HIP events on the stream the kernels run on.
 
@@ -57,6 +59,7 @@ STREAM_MIXES = {
     "nvfp4_quantize": (32, 9),      # bf16 in (2 B) : codes + E4M3 scales out (0.5 + 1/16 B) per element
     "requant": (6, 11),             # codes + scales in (0.5 + 1/16 B) : E4M3 + E8M0 out (1 + 1/32 B)
     "mxfp8_quantize": (64, 33),     # bf16 in (2 B) : E4M3 + E8M0 out (1 + 1/32 B); also bf16 RHT32 + S2F6
+    "weights_bwd": (64, 51),        # bf16 in (2 B) : NVFP4 codes + scales and W^T E4M3 + E8M0 out (1.59375 B)
     "combine": (33, 8),             # 8 slots x (4096 + 128) B + 64 B of index/gate in : 8192 B out per token
     "swiglu_bwd": (2, 1),           # da fp32 + h13 bf16 in (8 B) : dh13 bf16 out (4 B) per FFN element
 }
@@ -151,18 +154,22 @@ class Layer:
     def step(self, T):
         P = self.P
         E, H, F, M = self.E, self.H, self.F, self.M
-        w13q = T.run("nvfp4_quantize[w13]", P.nvfp4_quantize, self.w13, P.NVFP4_WEIGHT, F, workspace=self.wsq)
-        w2q = T.run("nvfp4_quantize[w2]", P.nvfp4_quantize, self.w2, P.NVFP4_WEIGHT, H, workspace=self.wsq)
+        # weights for both passes: NVFP4 for the forward, W^T requantized by SR for the dgrad
+        w13b = T.run("nvfp4_quantize_weights_bwd[w13]", P.nvfp4_quantize_weights_bwd, self.w13, F, seed=self.seed,
+                     rng_stream=1, workspace=self.wsq)
+        w2b = T.run("nvfp4_quantize_weights_bwd[w2]", P.nvfp4_quantize_weights_bwd, self.w2, H, seed=self.seed,
+                    rng_stream=3, workspace=self.wsq)
+        w13q, w2q = w13b.q, w2b.q
         xq = T.run("nvfp4_quantize[x]", P.nvfp4_quantize, self.x, P.NVFP4_ACT)
         a, h13 = T.run("moe_grouped_gemm_fwd[w13+swiglu]", P.moe_grouped_gemm_fwd, xq, w13q, self.offsets, M, 2 * F,
                        P.EPI_SWIGLU, gather=self.gather, save_h13=True)
         aq = T.run("nvfp4_quantize[a]", P.nvfp4_quantize, a, P.NVFP4_ACT)
         yc, ye = T.run("moe_grouped_gemm_fwd[w2+rht32_s2f6]", P.moe_grouped_gemm_fwd, aq, w2q, self.offsets, M, H,
                        P.EPI_RHT32_S2F6, rht_sign_mask=self.mask)
-        da, dw2, _ = T.run("moe_grouped_gemm_bwd[w2]", P.moe_grouped_gemm_bwd, self.dy, aq, w2q, self.offsets, M, H,
+        da, dw2, _ = T.run("moe_grouped_gemm_bwd[w2]", P.moe_grouped_gemm_bwd, self.dy, aq, w2b, self.offsets, M, H,
                            seed=self.seed, rng_stream_a=5, rng_stream_b=3, rng_stream_dy=6, workspace=self.ws2)
         # the SwiGLU backward runs inside the w13 backward's dY quantization (dh13 is not written)
-        dx, dw13, _ = T.run("moe_grouped_gemm_bwd_swiglu[w13]", P.moe_grouped_gemm_bwd_swiglu, da, h13, xq, w13q,
+        dx, dw13, _ = T.run("moe_grouped_gemm_bwd_swiglu[w13]", P.moe_grouped_gemm_bwd_swiglu, da, h13, xq, w13b,
                             self.offsets, M, 2 * F, gather=self.gather, seed=self.seed, rng_stream_a=4,
                             rng_stream_b=1, workspace=self.ws13)
         return yc, dx, dw13, dw2
@@ -516,7 +523,7 @@ def moe32_workload(P, I, torch, dev, steps, warmup=2):
         t = f / (per_call[nm] * 1e-3) / 1e12
         kern[nm].update(tflops=t, frac_of_dtype_peak=t / pk)
     fwd_ms = sum(per_call[k] for k in per_call if "fwd" in k or k in ("nvfp4_quantize[x]", "nvfp4_quantize[a]"))
-    bwd_ms = sum(per_call[k] for k in per_call if "bwd" in k)
+    bwd_ms = sum(per_call[k] for k in per_call if k.startswith("moe_grouped_gemm_bwd"))
     res = dict(workload=f"moe32: 32 experts, {layer.M} routed slots (top-8 of 16384 tokens), hidden 4096, FFN 1536",
                steps=steps, ms_per_step=ms, tflops=fl["step"] / (ms * 1e-3) / 1e12, step_tflop=fl["step"] / 1e12,
                forward_ms=fwd_ms, forward_tflops=fl["fwd"] / (fwd_ms * 1e-3) / 1e12,
@@ -819,6 +826,10 @@ def main():
         for _ in range(2):
             P.nvfp4_quantize(layer.w13, mode, layer.F, **kw)
         sq[name] = dict(ms=_time_ms(torch, lambda m=mode, k=kw: P.nvfp4_quantize(layer.w13, m, layer.F, **k), 5))
+    # the step's call: the same one read, also writing the backward's W13^T operand
+    sq["weight_1d_one_read_with_wt"] = dict(ms=_time_ms(
+        torch, lambda: P.nvfp4_quantize_weights_bwd(layer.w13, layer.F, seed=layer.seed, rng_stream=1,
+                                                    workspace=layer.wsq), 5))
     mx8 = mxfp8_forward_workload(P, I, torch, layer, max(args.quant_iters // 4, 3))
     fp4b = fp4_backward_workload(P, torch, layer, max(args.quant_iters // 4, 3))
     comb = combine_workload(P, I, torch, dev, args.quant_iters)
@@ -827,10 +838,10 @@ def main():
     M, E, H, F = layer.M, layer.E, layer.H, layer.F
     w13_el, w2_el = E * 2 * F * H, E * H * F
     mem = {
-        "nvfp4_quantize[w13]": _mem(w13_el * 2.5625 + E * 2 * 4, per_call["nvfp4_quantize[w13]"],
-                                    "nvfp4_quantize", roofs),
-        "nvfp4_quantize[w2]": _mem(w2_el * 2.5625 + E * 4, per_call["nvfp4_quantize[w2]"], "nvfp4_quantize",
-                                   roofs),
+        "nvfp4_quantize_weights_bwd[w13]": _mem(w13_el * (2.5625 + 1.03125) + E * 2 * 4,
+                                                per_call["nvfp4_quantize_weights_bwd[w13]"], "weights_bwd", roofs),
+        "nvfp4_quantize_weights_bwd[w2]": _mem(w2_el * (2.5625 + 1.03125) + E * 4,
+                                               per_call["nvfp4_quantize_weights_bwd[w2]"], "weights_bwd", roofs),
         "nvfp4_quantize[x]": _mem(layer.x.numel() * 2.5625 + layer.x.shape[0] * 4,
                                   per_call["nvfp4_quantize[x]"], "nvfp4_quantize", roofs),
         "nvfp4_quantize[a]": _mem(M * F * 2.5625 + M * 4, per_call["nvfp4_quantize[a]"], "nvfp4_quantize",
