@@ -136,10 +136,10 @@ int grouped_gemm_bwd_run(const void* dy, const uint8_t* a_codes, const uint8_t* 
     const bool dy_both = dgrad && wgrad && !fp4 && !sr && M > 0;
     if (dy_both) {
         e = swi ? pmn::launch_swiglu_bwd_mxfp8_rows_cols(swi_da, static_cast<const uint16_t*>(swi_h13), M, N / 2,
-                                                         offsets, G, L.Pb, ws + L.dq, ws + L.de, ws + L.dt,
+                                                         offsets, po, G, L.Pb, ws + L.dq, ws + L.de, ws + L.dt,
                                                          ws + L.dte, s)
-                : pmn::launch_mxfp8_rows_cols(static_cast<const uint16_t*>(dy), M, N, offsets, G, L.Pb, ws + L.dq,
-                                              ws + L.de, ws + L.dt, ws + L.dte, s);
+                : pmn::launch_mxfp8_rows_cols(static_cast<const uint16_t*>(dy), M, N, offsets, po, G, L.Pb,
+                                              ws + L.dq, ws + L.de, ws + L.dt, ws + L.dte, s);
         if (e != hipSuccess) return PMN_ELAUNCH;
     }
     if (dgrad && M > 0) {

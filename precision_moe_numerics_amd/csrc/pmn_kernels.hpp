@@ -69,16 +69,17 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 // dY [M x N] bf16 to MXFP8 (E4M3, round to nearest even) both ways in one read, in the blocked
 // layouts of the backward's workspace: row-wise codes rq at padded rows ([Pb x N rounded to 64]
 // in 1 KB blocks) with E8M0 re [N/32 x Pb], and column-wise codes cq ([N x Pb] in 1 KB blocks)
-// with E8M0 ce [Pb/32 x N]; groups padded to 64 slots. The same bytes as launch_mxfp8_rows and
-// launch_mxfp8_cols with those layouts.
-hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets, int G,
-                                  int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce,
-                                  hipStream_t stream);
+// with E8M0 ce [Pb/32 x N]; groups padded to 64 slots, po [G+1] their padded offsets (from
+// launch_padded_offsets with unit 64, earlier on the stream). The same bytes as launch_mxfp8_rows
+// and launch_mxfp8_cols with those layouts.
+hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                                  const int64_t* po, int G, int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq,
+                                  uint8_t* ce, hipStream_t stream);
 // The same for dY = the SwiGLU backward's dh13 [M x 2F], formed from da [M x F] (fp32) and h13
 // [M x 2F] (bf16) as launch_swiglu_bwd forms it, without writing it.
 hipError_t launch_swiglu_bwd_mxfp8_rows_cols(const float* da, const uint16_t* h13, int64_t M, int64_t F,
-                                             const int64_t* offsets, int G, int64_t Pb, uint8_t* rq, uint8_t* re,
-                                             uint8_t* cq, uint8_t* ce, hipStream_t stream);
+                                             const int64_t* offsets, const int64_t* po, int G, int64_t Pb,
+                                             uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce, hipStream_t stream);
 
 hipError_t launch_mxfp8_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
                              int G, bool sr, uint64_t seed, uint32_t stream_id, uint8_t* out,

@@ -513,12 +513,36 @@ hipError_t launch_requant(const uint8_t* codes, const uint8_t* scales, const flo
 constexpr int RC_COLS = 256;
 constexpr int RC_PITCH = RC_COLS * 2 + 16;   // bytes per tile row: 16-byte row reads of 16 rows cover all banks
 
+// The 64-slot unit at padded slot p0 (a multiple of 64): its first slot s0 and how many of its
+// slots exist (nv), from the groups' 64-slot padded offsets po [G+1] by one binary search (the
+// largest g with po[g] <= p0 is the group holding p0; empty groups have po[g] == po[g+1]). False
+// past the last group's padding.
+PMN_DEV bool unit_of(int64_t p0, const int64_t* __restrict__ offsets, const int64_t* __restrict__ po, int G,
+                     int64_t M, int64_t& s0, int64_t& nv)
+{
+    if (offsets == nullptr) {
+        s0 = p0;
+        nv = M - p0 < 64 ? M - p0 : 64;
+        return p0 < M;
+    }
+    if (p0 >= po[G]) return false;
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (po[mid] <= p0) lo = mid; else hi = mid - 1;
+    }
+    s0 = offsets[lo] + (p0 - po[lo]);
+    const int64_t end = offsets[lo + 1] < M ? offsets[lo + 1] : M;
+    nv = end - s0 < 0 ? 0 : (end - s0 < 64 ? end - s0 : 64);
+    return true;
+}
+
 template <bool SWI>
 __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restrict__ x, const float* __restrict__ da,
                                                         int64_t M, int64_t N, const int64_t* __restrict__ offsets,
-                                                        int G, int64_t Pb, uint8_t* __restrict__ rq,
-                                                        uint8_t* __restrict__ re, uint8_t* __restrict__ cq,
-                                                        uint8_t* __restrict__ ce)
+                                                        const int64_t* __restrict__ po, int G, int64_t Pb,
+                                                        uint8_t* __restrict__ rq, uint8_t* __restrict__ re,
+                                                        uint8_t* __restrict__ cq, uint8_t* __restrict__ ce)
 {
     constexpr int NT = SWI ? 2 : 1;   // tiles per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t tile[NT][64 * RC_PITCH];
@@ -526,23 +550,9 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
     const int64_t p0 = (int64_t)blockIdx.x * 64;          // first padded slot of the unit
     const int64_t c0 = (int64_t)blockIdx.y * RC_COLS;     // first column (SWI: first feature)
     const int64_t W = SWI ? N / 2 : N;                    // columns the grid spans (SWI: F)
-    const GroupBlock blk = find_block(p0 / 32, offsets, G, M, 64);
-    if (!blk.live) return;                                // workgroup-uniform
     // slots of the unit that exist: s0 .. s0 + nv - 1
-    int64_t nv = 0;
-    {
-        int64_t end = M;
-        if (offsets) {
-            // the group holding slot s0 ends at the first offset past it
-            int lo = 0, hi = G - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (offsets[mid] <= blk.s0) lo = mid; else hi = mid - 1;
-            }
-            end = offsets[lo + 1] < M ? offsets[lo + 1] : M;
-        }
-        nv = blk.valid == 0 ? 0 : (end - blk.s0 < 64 ? end - blk.s0 : 64);
-    }
+    int64_t s0 = 0, nv = 0;
+    if (!unit_of(p0, offsets, po, G, M, s0, nv)) return;   // workgroup-uniform
     // ---- the tile(s): 8 chunks of 8 columns per thread (row t / 32 + 8 i, chunk t % 32)
     if (SWI) {
         const uint16_t* h13 = x;
@@ -552,7 +562,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
             const int64_t f = c0 + (t & 31) * 8;
             uint32_t o1[4] = {0u, 0u, 0u, 0u}, o3[4] = {0u, 0u, 0u, 0u};
             if (row < nv && f < W) {
-                const int64_t s = blk.s0 + row;
+                const int64_t s = s0 + row;
                 const float4 g0 = *reinterpret_cast<const float4*>(da + s * W + f);
                 const float4 g1 = *reinterpret_cast<const float4*>(da + s * W + f + 4);
                 const uint4 w1 = *reinterpret_cast<const uint4*>(h13 + s * N + f);
@@ -579,7 +589,7 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
         for (int i = 0; i < 8; i++) {
             const int row = (t >> 5) + 8 * i;
             const int64_t col = c0 + (t & 31) * 8;
-            v[i] = (row < nv && col < N) ? *reinterpret_cast<const uint4*>(x + (blk.s0 + row) * N + col)
+            v[i] = (row < nv && col < N) ? *reinterpret_cast<const uint4*>(x + (s0 + row) * N + col)
                                         : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
@@ -672,25 +682,25 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
     }
 }
 
-hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets, int G,
-                                  int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce,
-                                  hipStream_t stream)
+hipError_t launch_mxfp8_rows_cols(const uint16_t* x, int64_t M, int64_t N, const int64_t* offsets,
+                                  const int64_t* po, int G, int64_t Pb, uint8_t* rq, uint8_t* re, uint8_t* cq,
+                                  uint8_t* ce, hipStream_t stream)
 {
     if (M == 0 || N == 0 || Pb == 0) return hipSuccess;
     const dim3 grid((unsigned)(Pb / 64), (unsigned)((N + RC_COLS - 1) / RC_COLS));
-    hipLaunchKernelGGL(k_mxfp8_rows_cols<false>, grid, dim3(256), 0, stream, x, nullptr, M, N, offsets, G, Pb, rq,
-                       re, cq, ce);
+    hipLaunchKernelGGL(k_mxfp8_rows_cols<false>, grid, dim3(256), 0, stream, x, nullptr, M, N, offsets, po, G, Pb,
+                       rq, re, cq, ce);
     return hipGetLastError();
 }
 
 hipError_t launch_swiglu_bwd_mxfp8_rows_cols(const float* da, const uint16_t* h13, int64_t M, int64_t F,
-                                             const int64_t* offsets, int G, int64_t Pb, uint8_t* rq, uint8_t* re,
-                                             uint8_t* cq, uint8_t* ce, hipStream_t stream)
+                                             const int64_t* offsets, const int64_t* po, int G, int64_t Pb,
+                                             uint8_t* rq, uint8_t* re, uint8_t* cq, uint8_t* ce, hipStream_t stream)
 {
     if (M == 0 || F == 0 || Pb == 0) return hipSuccess;
     const dim3 grid((unsigned)(Pb / 64), (unsigned)((F + RC_COLS - 1) / RC_COLS));
-    hipLaunchKernelGGL(k_mxfp8_rows_cols<true>, grid, dim3(256), 0, stream, h13, da, M, 2 * F, offsets, G, Pb, rq,
-                       re, cq, ce);
+    hipLaunchKernelGGL(k_mxfp8_rows_cols<true>, grid, dim3(256), 0, stream, h13, da, M, 2 * F, offsets, po, G, Pb,
+                       rq, re, cq, ce);
     return hipGetLastError();
 }
 
