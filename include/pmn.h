@@ -148,7 +148,8 @@ int nvfp4_quantize_ws(const void* x, int64_t rows, int64_t cols, int mode, int64
  * wt_e8m0 and the workspace 16-byte aligned (PMN_EALIGN). Workspace as nvfp4_quantize_ws.
  * When every matrix of rows_per_outer rows (a multiple of 64) splits into at most one tile per
  * compute unit (tiles of TH <= 512 rows, a multiple of 64, by TW columns, a multiple of 16, with
- * TH * TW <= 57344), x is read once and the codes are re-quantized while the matrix is on chip;
+ * 49152 <= TH * TW <= 57344), x is read once and the codes are re-quantized while the matrix is on
+ * chip;
  * otherwise (and on a capturing stream, or when the cooperative launch is refused) the call runs
  * the two steps. The results are the same.
  */

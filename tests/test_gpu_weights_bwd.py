@@ -50,12 +50,14 @@ def one_read_ran(ws):
 
 
 @pytest.mark.parametrize("G,R,C,one_read", [
-    (2, 128, 896, True),      # 64 x 16 tiles: 64 of 512 threads hold a block, 4 thread pairs requantize
-    (5, 64, 256, True),       # five rounds of small matrices
-    (3, 256, 512, True),
     (2, 2048, 7168, True),    # one expert's w1 and w3 (64 x 896 tiles, 256 workgroups)
     (1, 7168, 2048, True),    # one expert's w2 (448 x 128 tiles)
-    (4, 32, 128, False),      # 32-row matrices: no 64-row tiles, the two steps
+    (3, 1024, 13312, True),   # 64 x 832 tiles: 3328 blocks, so half the threads hold six, and
+                              # 416 of 512 threads requantize; three rounds
+    (2, 1536, 4096, False),   # the 32-expert layer's w1 / w3: tiles of 24576 values keep too few
+    (1, 4096, 1536, False),   # wavefronts busy in the requant, so the two steps run
+    (5, 64, 256, False),      # small matrices (1024-value tiles)
+    (4, 32, 128, False),      # 32-row matrices: no 64-row tiles
 ])
 def test_matches_oracle(P, I, G, R, C, one_read):
     w = I.normal((G * R, C), 0.02, 300 + G)
