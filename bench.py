@@ -228,12 +228,12 @@ def hardware_roofs(P, torch, dev):
     torch_copy = 2.0 * (1 << 30) / (_time_ms(torch, lambda: dst1.copy_(src1), 3) * 1e-3) / 1e9
     del src, dst, src1, dst1
     sink = torch.empty(P._lib.pmn_probe_mfma_sink_floats(2, 256), dtype=torch.float32, device=dev)
-    guess = {0: 2.0e15, 1: 2.2e15, 2: 4.5e15, 3: 4.5e15, 4: 9.0e15}       # only sizes the launches
+    guess = {0: 2.0e15, 1: 2.2e15, 2: 4.5e15, 3: 4.5e15, 4: 9.0e15, 5: 1.8e15, 6: 1.5e15}   # only sizes the launches
     mfma = {}
     for kind, name in P.PROBE_MFMA_KINDS.items():
-        for wps in (1, 2):
-            per_iter = P.probe_mfma(kind, wps, 256, 1, sink)
-            iters = max(200, int(4e-3 * guess[kind] / per_iter))
+        for wps in ((1,) if kind >= 5 else (1, 2)):   # kinds 5, 6: the GEMM's register budget, one wave per SIMD
+            per_iter = P.probe_mfma(kind, wps, 256, 2, sink) / 2
+            iters = max(200, int(4e-3 * guess[kind] / per_iter)) // 2 * 2
             P.probe_mfma(kind, wps, 256, 50, sink)
             fl = [0.0]
 
@@ -795,6 +795,8 @@ def main():
 
     roofs = hardware_roofs(P, torch, dev)
     f16_ceiling = roofs["mfma_tflops"][P.PROBE_MFMA_KINDS[0]]["1_wave_per_simd"]
+    # the same instruction with the kernel's dequantization interleaved, without memory traffic
+    dequant_ceiling = roofs["mfma_tflops"][P.PROBE_MFMA_KINDS[5]]["1_wave_per_simd"]
     k13 = per_call["moe_grouped_gemm_fwd[w13+swiglu]"]
     k2 = per_call["moe_grouped_gemm_fwd[w2+rht32_s2f6]"]
     ach = fl["fwd13"] / (k13 * 1e-3) / 1e12
@@ -807,6 +809,7 @@ def main():
                               "frac_fp4_class rates the same kernel against the 10.1 PFLOP/s FP4-class peak",
                 "flops_per_launch": fl["fwd13"], "ms_per_launch": k13,
                 "frac_of_measured_f16_ceiling": ach / f16_ceiling,
+                "frac_of_measured_dequant_ceiling": ach / dequant_ceiling,
                 "frac_fp4_class": ach / PEAK_FP4_TFLOPS}
     kernels = {name: {"ms": ms} for name, ms in per_call.items()}
     kernels["moe_grouped_gemm_fwd[w13+swiglu]"].update(tflops=ach, frac_f16_peak=ach / PEAK_F16_TFLOPS)

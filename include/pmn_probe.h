@@ -36,9 +36,12 @@ size_t pmn_probe_mfma_sink_floats(int waves_per_simd, int workgroups);
  * wavefronts (1 or 2) each run `iters` iterations of independent accumulator chains on constant
  * operands, with no memory traffic. kind: 0 v_mfma_f32_32x32x16_f16, 1 v_mfma_f32_16x16x32_f16,
  * 2 block-scaled 32x32x64 on E4M3, 3 block-scaled 16x16x128 on E4M3, 4 block-scaled 32x32x64 on
- * E2M1. *flops (host) receives the launch's floating-point operations; time the launch on
- * `stream` to get the rate. With one workgroup per compute unit (workgroups = 256) the kernel
- * runs exactly waves_per_simd wavefronts on every SIMD.
+ * E2M1; 5 and 6: v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 on a 128 x 128 tile per
+ * wavefront with the forward GEMM's dequantization interleaved (one FP4 -> fp16 conversion and
+ * one packed multiply per two operand values, the same per flop for both), one wavefront per
+ * SIMD only and an even iters (PMN_ESHAPE otherwise). *flops (host) receives the launch's
+ * floating-point operations; time the launch on `stream` to get the rate. With one workgroup per
+ * compute unit (workgroups = 256) the kernel runs exactly waves_per_simd wavefronts on every SIMD.
  */
 int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, float* sink, double* flops,
                    pmn_stream_t stream);

@@ -602,7 +602,8 @@ def moe_combine_s2f6(codes: torch.Tensor, e8m0: torch.Tensor, sign_mask: int, sl
 
 PROBE_MFMA_KINDS = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_16x16x32_f16",
                     2: "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 3: "v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3)",
-                    4: "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1)"}
+                    4: "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1)",
+                    5: "v_mfma_f32_32x32x16_f16 + FP4 dequantization", 6: "v_mfma_f32_16x16x32_f16 + FP4 dequantization"}
 
 
 def probe_stream(src: Optional[torch.Tensor], dst: Optional[torch.Tensor], units: int, read_kb: int, write_kb: int,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pmn_dev.hpp"
 #include "pmn_probe.h"
 
@@ -103,7 +105,113 @@ __global__ __launch_bounds__(512) void k_mfma_probe(float* __restrict__ sink, in
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// FLOPs one wavefront does per loop iteration of k_mfma_probe<KIND>.
+// The forward GEMM's inner loop without its memory traffic: one wavefront per SIMD computes a
+// 128 x 128 tile with fp16 MFMAs while it dequantizes the operand fragments of the next k-step
+// from FP4 codes (one FP4 -> fp16 conversion and one packed multiply by the block scale per two
+// values of each operand, the same vector work per flop for either instruction), interleaved with
+// the MFMAs. KIND 0: v_mfma_f32_32x32x16_f16 on 4 x 4 blocks, two 16-k substeps per iteration,
+// every MFMA followed by half a fragment of the next substep (double-buffered fragments). KIND 1:
+// v_mfma_f32_16x16x32_f16 on 8 x 8 blocks, one 32-k substep per half iteration; each row of 8
+// MFMAs carries the next B fragment of that row (double-buffered) and the next A fragment
+// (written once the row's MFMAs are issued).
+__device__ __forceinline__ void dequant_half(f16x8& r, uint32_t w, _Float16 s, int part)
+{
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ss = {s, s};
+    const f16x2 p0 = (part ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * ss;
+    const f16x2 p1 = (part ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)
+                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * ss;
+    r[4 * part] = p0[0];
+    r[4 * part + 1] = p0[1];
+    r[4 * part + 2] = p1[0];
+    r[4 * part + 3] = p1[1];
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256, 1) void k_mfma_dequant_probe(float* __restrict__ sink, int iters)
+{
+    const int lane = threadIdx.x & 63;
+    uint32_t raw[16];   // FP4 code words (magnitudes only, so the values stay small)
+#pragma unroll
+    for (int f = 0; f < 16; f++) raw[f] = (lane * 0x9E3779B1u + f * 0x85EBCA77u + 7u) & 0x77777777u;
+    const _Float16 sc = (_Float16)(1.0f + (lane & 7) * 0.125f);
+    float t = 0.0f;
+    if (KIND == 0) {
+        f32x16 acc[4][4];
+        f16x8 fa[2][4], fb[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) acc[i][j] = f32x16{};
+            dequant_half(fa[0][i], raw[i], sc, 0);
+            dequant_half(fa[0][i], raw[i], sc, 1);
+            dequant_half(fb[0][i], raw[4 + i], sc, 0);
+            dequant_half(fb[0][i], raw[4 + i], sc, 1);
+        }
+        for (int it = 0; it < iters; it++) {
+#pragma unroll
+            for (int b = 0; b < 2; b++) {
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int i = q >> 2, j = q & 3, f = q >> 1;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[b][i], fb[b][j], acc[i][j], 0, 0, 0);
+                    const uint32_t w = raw[f + 8 * b] ^ (uint32_t)it;
+                    if (f < 4) dequant_half(fa[b ^ 1][f], w, sc, q & 1);
+                    else dequant_half(fb[b ^ 1][f - 4], w, sc, q & 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) t += acc[i][j][v];
+    } else {
+        f32x4 acc[8][8];
+        f16x8 fa[8], fb[2][8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+#pragma unroll
+            for (int j = 0; j < 8; j++) acc[i][j] = f32x4{};
+            dequant_half(fa[i], raw[i], sc, 0);
+            dequant_half(fa[i], raw[i], sc, 1);
+            dequant_half(fb[0][i], raw[8 + i], sc, 0);
+            dequant_half(fb[0][i], raw[8 + i], sc, 1);
+        }
+        auto substep = [&](int it, auto bc) {
+            constexpr int b = decltype(bc)::value;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                f16x8 na = fa[i];
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fa[i], fb[b][j], acc[i][j], 0, 0, 0);
+                    if (j == 1 || j == 3) dequant_half(fb[b ^ 1][i], raw[8 + i] ^ (uint32_t)it, sc, j == 3);
+                    if (j == 5 || j == 7) dequant_half(na, raw[i] ^ (uint32_t)it, sc, j == 7);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                fa[i] = na;
+            }
+        };
+        for (int it = 0; it < iters; it += 2) {
+            substep(it, std::integral_constant<int, 0>());
+            substep(it + 1, std::integral_constant<int, 1>());
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) t += acc[i][j][v];
+    }
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
+// FLOPs one wavefront does per loop iteration of k_mfma_probe<KIND> (kinds 5 and 6: of
+// k_mfma_dequant_probe, 32 k of a 128 x 128 tile per iteration).
 double mfma_flops_per_iter(int kind)
 {
     switch (kind) {
@@ -111,6 +219,8 @@ double mfma_flops_per_iter(int kind)
     case 1: return 16.0 * 2 * 16 * 16 * 32;
     case 2: return 8.0 * 2 * 32 * 32 * 64;
     case 3: return 16.0 * 2 * 16 * 16 * 128;
+    case 5:
+    case 6: return 2.0 * 128 * 128 * 32;
     default: return 8.0 * 2 * 32 * 32 * 64;
     }
 }
@@ -162,8 +272,9 @@ size_t pmn_probe_mfma_sink_floats(int waves_per_simd, int workgroups)
 int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, float* sink, double* flops,
                    pmn_stream_t stream)
 {
-    if (kind < 0 || kind > 4 || !sink || !flops) return PMN_EINVAL;
+    if (kind < 0 || kind > 6 || !sink || !flops) return PMN_EINVAL;
     if (waves_per_simd < 1 || waves_per_simd > 2 || workgroups < 1 || iters < 1) return PMN_ESHAPE;
+    if (kind >= 5 && (waves_per_simd != 1 || iters % 2 != 0)) return PMN_ESHAPE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 g(workgroups), b(256 * waves_per_simd);
     switch (kind) {
@@ -171,7 +282,9 @@ int pmn_probe_mfma(int kind, int waves_per_simd, int workgroups, int iters, floa
     case 1: hipLaunchKernelGGL(k_mfma_probe<1>, g, b, 0, s, sink, iters); break;
     case 2: hipLaunchKernelGGL(k_mfma_probe<2>, g, b, 0, s, sink, iters); break;
     case 3: hipLaunchKernelGGL(k_mfma_probe<3>, g, b, 0, s, sink, iters); break;
-    default: hipLaunchKernelGGL(k_mfma_probe<4>, g, b, 0, s, sink, iters); break;
+    case 4: hipLaunchKernelGGL(k_mfma_probe<4>, g, b, 0, s, sink, iters); break;
+    case 5: hipLaunchKernelGGL(k_mfma_dequant_probe<0>, g, b, 0, s, sink, iters); break;
+    default: hipLaunchKernelGGL(k_mfma_dequant_probe<1>, g, b, 0, s, sink, iters); break;
     }
     *flops = mfma_flops_per_iter(kind) * iters * 4.0 * waves_per_simd * workgroups;
     return hipGetLastError() == hipSuccess ? PMN_OK : PMN_ELAUNCH;

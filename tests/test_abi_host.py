@@ -131,6 +131,17 @@ def test_weights_bwd_argument_errors(lib):
     assert swi(1) == -1 and swi(4) == -1
 
 
+def test_probe_argument_errors(lib):
+    """The MFMA probe refuses unknown kinds (PMN_EINVAL), and the dequantization kinds 5 and 6 at
+    two wavefronts per SIMD or with an odd iteration count (PMN_ESHAPE), before any launch."""
+    fake = C.c_void_p(0x1000)     # never dereferenced
+    fl = C.c_double(0.0)
+    assert lib.pmn_probe_mfma(7, 1, 256, 10, fake, C.byref(fl), None) == -1
+    assert lib.pmn_probe_mfma(5, 2, 256, 10, fake, C.byref(fl), None) == -2
+    assert lib.pmn_probe_mfma(6, 1, 256, 11, fake, C.byref(fl), None) == -2
+    assert lib.pmn_probe_mfma(0, 3, 256, 10, fake, C.byref(fl), None) == -2
+
+
 def test_check_indices_argument_errors(lib):
     """pmn_check_indices refuses, before any launch: no result or neither array (PMN_EINVAL), no
     groups or a negative M with offsets, a negative count or row bound with gather (PMN_ESHAPE),
