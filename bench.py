@@ -759,8 +759,8 @@ def main():
         summarize_profiles(args.summarize_profiles)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (every box here has one "
-                                   "GPU; the multi-GPU design is expert parallelism over RCCL all-to-alls)"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1 (the multi-GPU design, expert "
+                                   "parallelism over RCCL all-to-alls, is not implemented here)"}))
         sys.exit(2)
     import torch
 

@@ -870,7 +870,7 @@ void orc_gemm_mxfp8_wgrad(const uint8_t* dt, const uint8_t* dte, const uint8_t* 
 }
 
 /* ------------------------------------------------------------------------------------------ */
-/* SwiGLU and its backward (BASELINE layer shape: w1, w3 then w2), fp64                        */
+/* SwiGLU and its backward (the expert layer's shape: w1, w3 then w2), fp64                    */
 /* ------------------------------------------------------------------------------------------ */
 
 /* h13 [M x 2F] fp32 (h1 = columns 0..F-1, h3 = F..2F-1) -> a = silu(h1) * h3. */
