@@ -694,7 +694,10 @@ def summarize_profiles(d, out_dir=None):
            "SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of the 1024 SIMDs, so MFMA busy = MFMA_BUSY / 1024 / "
            "(GRBM_GUI_ACTIVE / 8) at the running clock. SQ_ACTIVE_INST_VALU counts quad-cycles issuing VALU work "
            "(MFMA included): VALU busy = 4 x ACTIVE_INST_VALU / 1024 / (GRBM_GUI_ACTIVE / 8). Kernels under "
-           "0.02 ms are omitted.", "",
+           "0.02 ms are omitted. Two limits of these figures: launches shorter than about 0.05 ms read clocks "
+           "above the 2.4 GHz maximum, because the counters run over a longer window than the dispatch's "
+           "timestamps; and SQ_ACTIVE_INST_VALU is accumulated per wavefront, so a kernel whose wavefronts "
+           "share a SIMD can read a VALU busy above 1, which means its vector units are saturated.", "",
            "| kernel | grid | ms | clock GHz | MFMA busy (at that clock) | MFMA busy vs 2.4 GHz | VALU busy |",
            "|---|---:|---:|---:|---:|---:|---:|"]
     for k, v in sorted(ag.items()):
