@@ -359,6 +359,14 @@ def test_rht32_s2f6(P, I, dtype):
     assert np.array_equal(npy(c), rc) and np.array_equal(npy(e), re)
     xh = decode_s2f6_rows(npy(c), npy(e), mask)
     assert rel_fro(xh, x.float().numpy()) < 0.02
+    # per 32-chunk: the transform is orthogonal up to its factor 32, so the decoded chunk lies within
+    # half a code step, 2^(e-127)/128, of the input in the 2-norm (up to the fp32 transform's rounding)
+    xr = x.float().numpy().astype(np.float64)
+    R, Cc = xr.shape
+    ee = npy(e).astype(np.float64)
+    err = np.sqrt(((xh - xr) ** 2).reshape(R, Cc // 32, 32).sum(-1))
+    nrm = np.sqrt((xr ** 2).reshape(R, Cc // 32, 32).sum(-1))
+    assert np.all(err <= 2.0 ** (ee - 127) / 128 * (1 + 1e-6) + 1e-6 * nrm)
 
 
 # ------------------------------------------------------------------------------------------
