@@ -20,6 +20,7 @@
 #include "pmn_kernels.hpp"
 
 namespace pmn {
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct GroupBlock {
     int64_t s0;   // first slot of the block
@@ -213,7 +214,9 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
         if (SRC == SRC_NVFP4) {
             uint32_t sbyte[32];
             float so[32];
-            // row bases are wavefront-uniform (scalar registers); each lane adds a 32-bit offset
+            // row bases are wavefront-uniform (scalar registers); each lane adds a 32-bit offset.
+            // The loads are nontemporal: the source is read once (measured 4% faster than cached
+            // loads on the 8192 x 7168 workload and on the layer's X^T)
             const uint32_t coff = (uint32_t)(c0 >> 1), soff = (uint32_t)(c0 >> 4);
 #pragma unroll
             for (int j = 0; j < 32; j++) {
@@ -221,8 +224,8 @@ __global__ __launch_bounds__(256, 2) void k_transpose_quant(TransposeArgs a)
                 so[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ol), j));
                 gbyte* crow = uniform_ptr(a.codes + r * (a.cols >> 1));
                 gbyte* srow = uniform_ptr(a.scales + r * (a.cols >> 4));
-                cw[j] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(crow + coff);
-                sbyte[j] = srow[soff];
+                cw[j] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(crow + coff));
+                sbyte[j] = __builtin_nontemporal_load(srow + soff);
             }
             // slots past the group's end become +0 (code word 0, scale 0), so they need no branch:
             // a wavefront-uniform mask clears both
@@ -563,10 +566,15 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
             uint32_t o1[4] = {0u, 0u, 0u, 0u}, o3[4] = {0u, 0u, 0u, 0u};
             if (row < nv && f < W) {
                 const int64_t s = s0 + row;
-                const float4 g0 = *reinterpret_cast<const float4*>(da + s * W + f);
-                const float4 g1 = *reinterpret_cast<const float4*>(da + s * W + f + 4);
-                const uint4 w1 = *reinterpret_cast<const uint4*>(h13 + s * N + f);
-                const uint4 w3 = *reinterpret_cast<const uint4*>(h13 + s * N + W + f);
+                // nontemporal: dA and h13 are read once
+                const f32x4 g0v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(da + s * W + f));
+                const f32x4 g1v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(da + s * W + f + 4));
+                const u32x4 w1v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(h13 + s * N + f));
+                const u32x4 w3v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(h13 + s * N + W + f));
+                const float4 g0 = make_float4(g0v[0], g0v[1], g0v[2], g0v[3]);
+                const float4 g1 = make_float4(g1v[0], g1v[1], g1v[2], g1v[3]);
+                const uint4 w1 = make_uint4(w1v[0], w1v[1], w1v[2], w1v[3]);
+                const uint4 w3 = make_uint4(w3v[0], w3v[1], w3v[2], w3v[3]);
                 const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
                 const uint32_t a1[4] = {w1.x, w1.y, w1.z, w1.w}, a3[4] = {w3.x, w3.y, w3.z, w3.w};
 #pragma unroll
@@ -589,8 +597,12 @@ __global__ __launch_bounds__(256) void k_mxfp8_rows_cols(const uint16_t* __restr
         for (int i = 0; i < 8; i++) {
             const int row = (t >> 5) + 8 * i;
             const int64_t col = c0 + (t & 31) * 8;
-            v[i] = (row < nv && col < N) ? *reinterpret_cast<const uint4*>(x + (s0 + row) * N + col)
-                                        : make_uint4(0u, 0u, 0u, 0u);
+            if (row < nv && col < N) {   // nontemporal: dY is read once
+                const u32x4 t4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (s0 + row) * N + col));
+                v[i] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+            } else {
+                v[i] = make_uint4(0u, 0u, 0u, 0u);
+            }
         }
 #pragma unroll
         for (int i = 0; i < 8; i++)
